@@ -1,0 +1,78 @@
+"""Attention over gathered candidate keys (window ++ selected blocks), fp64 on the CPU.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Follows ``faiss_block_attention`` of the "AnnAttention" page ("Core code"):
+  * heads are flattened into one joint embedding E = H * D per token;
+  * every token t attends to a candidate list made of
+      - a sliding window of ``window`` keys ending at t (inclusive), padded with
+        zero vectors before the start of the sequence, then
+      - for each of its selected block indices (in the stored ascending order) the
+        ``block_size`` rows of that block; an index of -1 is clamped to token 0 for
+        every row, as the page clamps negative item indices to 0;
+    duplicates are kept;
+  * logits = q_t . k_slot / sqrt(E); softmax over all slots with no mask (zero
+    padding slots take part with logit 0 and value 0); o_t = sum p * v_slot.
+
+The window helper and the block-to-item helper are not shown on the page; the
+readings above (window ends at t inclusive, zero padding; block c -> rows c*bs ..
+c*bs+bs-1) are pinned only to themselves -- parity unpinned against the originals.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .dense import as_f64
+
+
+def _flat(x):
+    x = as_f64(x)
+    if x.ndim == 4:
+        x = x.reshape(x.shape[0], x.shape[1], -1)
+    return x
+
+
+def candidate_positions(t: int, sel_row, *, window: int, block_size: int):
+    """(positions, is_zero_pad) of token t's candidate slots, in list order."""
+    pos, pad = [], []
+    for w in range(window):
+        p = t - window + 1 + w
+        pos.append(max(p, 0))
+        pad.append(p < 0)
+    for c in sel_row:
+        for r in range(block_size):
+            p = int(c) * block_size + r
+            pos.append(p if p >= 0 else 0)
+            pad.append(False)
+    return np.asarray(pos, dtype=np.int64), np.asarray(pad, dtype=bool)
+
+
+def sparse_attention(q, k, v, sel, *, window: int, block_size: int, scale=None, tokens=None):
+    """o [B, S, E], m [B, S], l [B, S] in fp64 (m, l: max logit and sum of exp(logit - m)).
+
+    ``tokens`` restricts the evaluation to sampled token indices (others are NaN).
+    """
+    q, k, v = _flat(q), _flat(k), _flat(v)
+    sel = np.asarray(sel.cpu() if hasattr(sel, "cpu") else sel)
+    B, S, E = q.shape
+    sc = 1.0 / math.sqrt(E) if (scale is None or scale <= 0) else float(scale)
+    fill = np.nan if tokens is not None else 0.0
+    o = np.full((B, S, E), fill)
+    m = np.full((B, S), fill)
+    l = np.full((B, S), fill)
+    toks = range(S) if tokens is None else tokens
+    for b in range(B):
+        for t in toks:
+            pos, pad = candidate_positions(t, sel[b, t], window=window, block_size=block_size)
+            K = np.where(pad[:, None], 0.0, k[b, pos])
+            V = np.where(pad[:, None], 0.0, v[b, pos])
+            s = sc * (K @ q[b, t])
+            mt = s.max()
+            p = np.exp(s - mt)
+            lt = p.sum()
+            o[b, t] = (p @ V) / lt
+            m[b, t] = mt
+            l[b, t] = lt
+    return o, m, l

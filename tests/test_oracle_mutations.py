@@ -1,0 +1,107 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+Each mutation replaces one small oracle helper through monkeypatching; the named pin
+test must then fail.  This shows the pins are not vacuous: a dropped term, a wrong
+index or sign, a transposed operand or a wrong tie rule anywhere in the oracle turns
+at least one of them red.
+"""
+import numpy as np
+import pytest
+
+from oracle import blockwise, dense, select, sparse
+import test_oracle_backward as tb
+import test_oracle_blockwise as tw
+import test_oracle_dense as td
+import test_oracle_select_sparse as ts
+
+
+def _mut_gqa_modulo(monkeypatch):
+    monkeypatch.setattr(dense, "kv_head_of", lambda hq, G: hq % G)
+    monkeypatch.setattr(blockwise, "kv_head_of", lambda hq, G: hq % G)
+
+
+def _mut_drop_scale(monkeypatch):
+    monkeypatch.setattr(dense, "scores", lambda q, k, scale: q @ k.T)
+
+
+def _mut_transposed_scores(monkeypatch):
+    monkeypatch.setattr(dense, "scores", lambda q, k, scale: scale * (k @ q.T).T[::-1, ::-1])
+
+
+def _mut_strict_causal(monkeypatch):
+    orig = dense.visible
+
+    def vis(q_pos, k_pos, causal, wl=-1, wr=-1):
+        ok = orig(q_pos, k_pos, False, wl, wr)
+        if causal:
+            ok &= np.asarray(k_pos)[None, :] < np.asarray(q_pos)[:, None]
+        return ok
+    monkeypatch.setattr(dense, "visible", vis)
+
+
+def _mut_window_exclusive(monkeypatch):
+    orig = dense.visible
+
+    def vis(q_pos, k_pos, causal, wl=-1, wr=-1):
+        return orig(q_pos, k_pos, causal, wl - 1 if wl > 0 else wl, wr)
+    monkeypatch.setattr(dense, "visible", vis)
+
+
+def _mut_grad_sign(monkeypatch):
+    monkeypatch.setattr(dense, "grad_scores", lambda P, dP, Di: P * (dP + Di[:, None]))
+
+
+def _mut_grad_drop_d(monkeypatch):
+    monkeypatch.setattr(dense, "grad_scores", lambda P, dP, Di: P * dP)
+
+
+def _mut_correction_inverted(monkeypatch):
+    monkeypatch.setattr(blockwise, "correction_factor", lambda prev, new: np.exp(new - prev))
+
+
+def _mut_ties_to_higher_index(monkeypatch):
+    monkeypatch.setattr(select, "rank_candidates",
+                        lambda sc: sc.shape[1] - 1 - np.argsort(-sc[:, ::-1], axis=1, kind="stable"))
+
+
+def _mut_window_off_by_one(monkeypatch):
+    orig = sparse.candidate_positions
+
+    def cand(t, sel_row, *, window, block_size):
+        return orig(t - 1, sel_row, window=window, block_size=block_size)
+    monkeypatch.setattr(sparse, "candidate_positions", cand)
+
+
+def _mut_clamp_to_last(monkeypatch):
+    orig = sparse.candidate_positions
+
+    def cand(t, sel_row, *, window, block_size):
+        pos, pad = orig(t, sel_row, window=window, block_size=block_size)
+        n_w = window
+        fixed = [p if (i < n_w or c >= 0) else block_size - 1
+                 for i, (p, c) in enumerate(zip(pos, [0] * n_w + [c for c in sel_row for _ in range(block_size)]))]
+        return np.asarray(fixed), pad
+    monkeypatch.setattr(sparse, "candidate_positions", cand)
+
+
+MUTATIONS = [
+    (_mut_gqa_modulo, lambda: td.test_forward_matches_torch_sdpa(td.CASES[0])),
+    (_mut_drop_scale, lambda: td.test_forward_matches_torch_sdpa(td.CASES[1])),
+    (_mut_transposed_scores, lambda: td.test_forward_matches_torch_sdpa(td.CASES[1])),
+    (_mut_strict_causal, td.test_window_zero_left_returns_own_value),
+    (_mut_window_exclusive, td.test_zero_queries_average_visible_values),
+    (_mut_grad_sign, lambda: tb.test_finite_differences(True, (-1, -1), 0, 0)),
+    (_mut_grad_drop_d, tb.test_gradient_sums),
+    (_mut_correction_inverted, lambda: tw.test_ring_carry_equals_definition(4, 8, 8, True, (-1, -1))),
+    (_mut_ties_to_higher_index, ts.test_select_ties_go_to_lower_index),
+    (_mut_window_off_by_one, ts.test_sparse_equals_materialised_candidate_list),
+    (_mut_clamp_to_last, ts.test_sparse_zero_keys_closed_form),
+]
+
+
+@pytest.mark.parametrize("mutate,pin", MUTATIONS, ids=[m.__name__ for m, _ in MUTATIONS])
+def test_pin_catches_mutation(monkeypatch, mutate, pin):
+    pin()                                   # green before the mutation
+    mutate(monkeypatch)
+    with pytest.raises(AssertionError):
+        pin()
