@@ -1,0 +1,192 @@
+/*
+ * attn.h -- C ABI of libattn.so: blockwise exact softmax attention for gfx950 (MI355X).
+ *
+ * The operation (sources are web pages, cited by title and section):
+ *   * "bpt.py" (llm_large_context): ring attention over blockwise attention.  Query
+ *     and key chunks are scored, masked with global chunk offsets, and folded into a
+ *     carried running max / numerator / denominator (``_blockwise_attention_fwd``,
+ *     ``_ring_attention_fwd``); the backward pass recomputes the probabilities from the
+ *     saved max and denominator (``_blockwise_attention_bwd``, ``_ring_attention_bwd``).
+ *   * "JAX: Single-GPU Attention with TransformerEngine", section 1: BSHD layout, grouped
+ *     query heads (q head h reads kv head h / (Hq/Hkv)), and the causal sliding-window
+ *     mask ``_make_causal_swa_mask``; "Other attention knobs": ``scale_factor``.
+ *   * "AnnAttention" (StudyExchange), "Core code": per-token top-n selection of earlier
+ *     key blocks by their mean (``select_block``) and attention over the gathered
+ *     window ++ selected blocks (``faiss_block_attention``).
+ *
+ * Conventions shared by every entry point:
+ *   * All tensor arguments are DEVICE pointers (memory of the current HIP device),
+ *     dense and row-major, allocated and owned by the caller.  The library allocates
+ *     no device memory and keeps no pointer after a call returns.
+ *   * BSHD layout: q, o, dout, dq are [B, Sq, Hq, D]; k, v, dk, dv are [B, Skv, Hkv, D].
+ *     Statistics m, l are fp32 [B, Hq, Sq].  The carry ``acc`` is fp32 [B, Sq, Hq, D].
+ *   * ``stream`` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; nothing is synchronised.  Buffers must stay alive until the
+ *     stream work completes.
+ *   * Arguments are checked on the host before anything is launched.  A failed check
+ *     returns ATTN_ERR_INVALID_ARG / ATTN_ERR_UNSUPPORTED / ATTN_ERR_WORKSPACE and
+ *     launches nothing; a failed launch returns ATTN_ERR_HIP.  attn_last_error() then
+ *     describes the problem.  A batch of 0 (or Sq = 0) is a successful no-op.
+ */
+#ifndef RING_EXACT_ATTENTION_ATTN_H_
+#define RING_EXACT_ATTENTION_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,   /* malformed arguments (NULL pointer, bad size, ...) */
+  ATTN_ERR_UNSUPPORTED = -2,   /* well-formed but not built (head_dim, dtype, ...)  */
+  ATTN_ERR_WORKSPACE = -3,     /* workspace NULL or smaller than required           */
+  ATTN_ERR_HIP = -4            /* the HIP runtime reported an error                  */
+} attn_status;
+
+typedef enum {
+  ATTN_BF16 = 0,               /* q, k, v, o, dout, dq, dk, dv are bfloat16 */
+  ATTN_F32 = 1                 /* ... are float32                           */
+} attn_dtype;
+
+/* attn_params.flags */
+enum {
+  /* Read m, l, acc as the incoming carry instead of starting from
+   * m = -inf, l = 0, acc = 0 (one ring step resumes where the previous one stopped;
+   * "bpt.py", ``_ring_attention_fwd`` threads (max, numerator, denominator) through
+   * its scan). */
+  ATTN_CARRY_IN = 1u,
+  /* Leave the carry unnormalised in m, l, acc and do not write o (a ring step that is
+   * not the last one). */
+  ATTN_NO_FINALIZE = 2u
+};
+
+#define ATTN_PARAMS_VERSION 1u
+
+typedef struct attn_params {
+  uint32_t struct_size;        /* = sizeof(attn_params); versioning of the ABI        */
+  int32_t dtype;               /* attn_dtype                                           */
+  int32_t batch;               /* B >= 0                                               */
+  int32_t seqlen_q;            /* Sq >= 0 (rows of q in this call)                     */
+  int32_t seqlen_kv;           /* Skv >= 0 (rows of k, v in this call)                 */
+  int32_t num_q_heads;         /* Hq > 0                                               */
+  int32_t num_kv_heads;        /* Hkv > 0, Hq % Hkv == 0 (GQA group G = Hq / Hkv)      */
+  int32_t head_dim;            /* D: 32, 64 or 128 (dense); 512 (sparse mode)         */
+  int64_t q_pos0;              /* global position of q row 0 (chunk index start times
+                                  chunk size in "bpt.py")                              */
+  int64_t kv_pos0;             /* global position of k/v row 0                         */
+  int32_t causal;              /* 1: key position <= query position                    */
+  int32_t window_left;         /* -1 = unbounded, else key >= query - left (inclusive) */
+  int32_t window_right;        /* -1 = unbounded, else key <= query + right; with
+                                  causal only -1 or 0 is accepted                      */
+  float scale;                 /* logit scale; <= 0 selects 1/sqrt(head_dim)          */
+  int32_t query_chunk;         /* 0 = Sq; otherwise must divide Sq                     */
+  int32_t key_chunk;           /* 0 = Skv; otherwise must divide Skv                   */
+  int32_t kv_block;            /* virtual ring block: 0 = Skv (one block); otherwise
+                                  must divide Skv.  Key blocks are visited in ring
+                                  order starting at the block holding the query tile's
+                                  own position and descending (mod the block count).  */
+  uint32_t flags;              /* ATTN_CARRY_IN | ATTN_NO_FINALIZE (attn_fwd only)     */
+  /* Gathered block-sparse mode ("AnnAttention", faiss_block_attention): when sel_idx
+   * is non-NULL, attn_fwd attends each token to a zero-padded window of
+   * sparse_window keys ending at the token, followed by the sel_block rows of each of
+   * its top_n selected blocks (an index of -1 reads token 0 for every row), with one
+   * softmax over all slots and no mask.  Requires bf16, Hq = Hkv = 1, head_dim = the
+   * joint embedding (512), Sq = Skv, causal/window/flags/kv_block unused.           */
+  const int32_t* sel_idx;      /* [B, Sq, top_n] device, from block_select             */
+  int32_t top_n;               /* 1..16                                                */
+  int32_t sel_block;           /* rows per selected block (32)                         */
+  int32_t sparse_window;       /* 1..64                                                */
+  int32_t reserved;            /* must be 0                                            */
+} attn_params;
+
+typedef struct select_params {
+  uint32_t struct_size;        /* = sizeof(select_params)                              */
+  int32_t dtype;               /* ATTN_BF16                                            */
+  int32_t batch;               /* B >= 0                                               */
+  int32_t seqlen;              /* S >= 0                                               */
+  int32_t embed;               /* E = heads * head_dim, multiple of 64, <= 1024        */
+  int32_t block_size;          /* 16, 32 or 64                                         */
+  int32_t top_n;               /* 1..16                                                */
+  int32_t reserved;            /* must be 0                                            */
+} select_params;
+
+/*
+ * attn_fwd -- exact softmax attention forward, one GPU's share of the ring.
+ * ("bpt.py": _ring_attention_fwd / _blockwise_attention_fwd; masking as in
+ * _chunk_attention_bias and the TransformerEngine page's _make_causal_swa_mask.)
+ *
+ *   s_ij = scale * q_i . k_j over visible pairs, where query row i sits at q_pos0 + i,
+ *   key row j at kv_pos0 + j, and (i, j) is visible iff
+ *   (causal => kpos <= qpos) and (right >= 0 => kpos <= qpos + right) and
+ *   (left >= 0 => kpos >= qpos - left).
+ *   Writes m_i = max_j s_ij (natural-log units), l_i = sum_j exp(s_ij - m_i), and
+ *   o_i = sum_j exp(s_ij - m_i) v_j / l_i rounded to the element type.  A row with no
+ *   visible key gets o = 0, m = -inf, l = 0.
+ *
+ *   q, k, v   [in]  element type per params->dtype, BSHD.
+ *   o         [out] [B, Sq, Hq, D]; may be NULL only with ATTN_NO_FINALIZE.
+ *   m, l      [in/out] fp32 [B, Hq, Sq]; inputs only with ATTN_CARRY_IN.
+ *   acc       [in/out] fp32 [B, Sq, Hq, D] unnormalised numerator; required (and only
+ *             used) with ATTN_CARRY_IN or ATTN_NO_FINALIZE, else may be NULL.
+ *             With ATTN_NO_FINALIZE the stored (m, l, acc) satisfy
+ *             acc_i = sum_j exp(s_ij - m_i) v_j over all blocks seen so far.
+ * In sparse mode (sel_idx != NULL) m and l hold the max logit and the softmax sum
+ * over the token's slots.
+ */
+int attn_fwd(const attn_params* params, const void* q, const void* k, const void* v,
+             void* o, float* m, float* l, float* acc, void* stream);
+
+/*
+ * attn_bwd -- gradients of attn_fwd's output, recomputing the probabilities from the
+ * saved statistics ("bpt.py": _blockwise_attention_bwd / _ring_attention_bwd):
+ *   D_i = dO_i . o_i,  P_ij = exp(s_ij - m_i) / l_i,  dS_ij = P_ij (dO_i . v_j - D_i),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dO_i,
+ * with dk, dv summed over the q heads that share a kv head.
+ *
+ *   q, k, v, o, dout [in] as in attn_fwd (o = attn_fwd's output, dout = dL/do).
+ *   m, l             [in] fp32 [B, Hq, Sq] written by attn_fwd.
+ *   dq [out] [B, Sq, Hq, D]; dk, dv [out] [B, Skv, Hkv, D] (element type of q).
+ *   workspace        device scratch of at least attn_bwd_workspace_bytes(params)
+ *                    bytes (256-byte aligned); its contents are overwritten.
+ * flags must be 0 and sel_idx NULL.  The result is bitwise reproducible run to run.
+ */
+int attn_bwd(const attn_params* params, const void* q, const void* k, const void* v,
+             const void* o, const void* dout, const float* m, const float* l,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* Bytes of device workspace attn_bwd needs for these params (0 if params invalid). */
+size_t attn_bwd_workspace_bytes(const attn_params* params);
+
+/*
+ * block_select -- exact top-n block selection ("AnnAttention", select_block, with the
+ * approximate index replaced by exact inner products):
+ *   mean_c = average of key rows c*bs .. c*bs+bs-1 (full blocks), in fp64;
+ *   a token t in block i = t / bs scores the blocks c < i by q_t . mean_c (fp64),
+ *   keeps the top min(top_n, i) by (score descending, block index ascending), pads
+ *   with -1 and sorts ascending (so -1 entries come first).
+ *
+ *   q, k       [in]  bf16 [B, S, E] (BSHD with the heads flattened: E = H * D).
+ *   idx        [out] int32 [B, S, top_n].
+ *   workspace  device scratch of at least block_select_workspace_bytes(params) bytes.
+ */
+int block_select(const select_params* params, const void* q, const void* k, int32_t* idx,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace block_select needs (0 if params invalid). */
+size_t block_select_workspace_bytes(const select_params* params);
+
+/* Message of the last failed call on this thread ("" after a success). */
+const char* attn_last_error(void);
+
+/* ATTN_PARAMS_VERSION the library was built with. */
+uint32_t attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_EXACT_ATTENTION_ATTN_H_ */

@@ -165,11 +165,14 @@ def probs(q, k, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0, k
 
 
 def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0,
-             kv_pos0: int = 0, row_block: int = 256):
+             kv_pos0: int = 0, row_block: int = 256, heads=None, batches=None):
     """Analytic gradient of ``forward`` contracted with dO.
 
     Returns (dq [B, Sq, Hq, D], dk [B, Skv, Hkv, D], dv [B, Skv, Hkv, D]) in fp64.
-    D_i uses this function's own fp64 output O.
+    D_i uses this function's own fp64 output O.  ``heads`` / ``batches`` restrict the
+    evaluation to some q heads / batch entries: dq of the others is NaN, and dk, dv
+    only collect the contributions of the evaluated q heads (complete for a kv head
+    when all q heads of its group are listed).
     """
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, Sq, Hq, D = q.shape
@@ -177,14 +180,16 @@ def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: 
     G = Hq // Hkv
     sc = _default_scale(D, scale)
     wl, wr = window
-    dq = np.zeros_like(q)
+    partial = heads is not None or batches is not None
+    dq = np.full_like(q, np.nan) if partial else np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     rows = np.arange(Sq)
     kpos = kv_pos0 + np.arange(Skv)
-    for b in range(B):
-        for hq in range(Hq):
+    for b in (range(B) if batches is None else batches):
+        for hq in (range(Hq) if heads is None else heads):
             g = kv_head_of(hq, G)
+            dq[b, :, hq] = 0.0
             K, V = k[b, :, g, :], v[b, :, g, :]
             for r in _row_slices(rows, row_block):
                 vis = visible(q_pos0 + r, kpos, causal, wl, wr)

@@ -1,0 +1,290 @@
+"""Blockwise exact softmax attention for MI355X (gfx950): Python binding of libattn.so.
+
+This module only marshals arguments: it checks tensor shapes/dtypes, allocates the
+outputs with torch on the tensors' device, and calls the C ABI declared in
+``include/attn.h`` on the current torch stream.  Every step of the computation runs
+in the HIP kernels of ``libattn.so``; there is no fallback.  If the library has not
+been built (``python -m ring_exact_attention_amd.build``), importing works but every
+call raises.
+
+Entry points (names as in the C ABI):
+  attn_fwd(q, k, v, ...)                 -> (o, m, l)      or (acc, m, l) without finalize
+  attn_bwd(q, k, v, o, dout, m, l, ...)  -> (dq, dk, dv)
+  block_select(q, k, block_size, top_n)  -> idx int32 [B, S, top_n]
+  attn_fwd_sparse(q, k, v, idx, ...)     -> (o, m, l)      (attn_fwd with sel_idx)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, -1, -2, -3, -4
+ATTN_BF16, ATTN_F32 = 0, 1
+ATTN_CARRY_IN, ATTN_NO_FINALIZE = 1, 2
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("seqlen_q", ctypes.c_int32),
+        ("seqlen_kv", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("q_pos0", ctypes.c_int64),
+        ("kv_pos0", ctypes.c_int64),
+        ("causal", ctypes.c_int32),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("query_chunk", ctypes.c_int32),
+        ("key_chunk", ctypes.c_int32),
+        ("kv_block", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("sel_idx", ctypes.c_void_p),
+        ("top_n", ctypes.c_int32),
+        ("sel_block", ctypes.c_int32),
+        ("sparse_window", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class SelectParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("embed", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("top_n", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libattn status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "attn_fwd": (ctypes.c_int, [ctypes.POINTER(AttnParams), _P, _P, _P, _P, _P, _P, _P, _P]),
+    "attn_bwd": (ctypes.c_int, [ctypes.POINTER(AttnParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _P, ctypes.c_size_t, _P]),
+    "attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AttnParams)]),
+    "block_select": (ctypes.c_int, [ctypes.POINTER(SelectParams), _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "block_select_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SelectParams)]),
+    "attn_last_error": (ctypes.c_char_p, []),
+    "attn_abi_version": (ctypes.c_uint32, []),
+}
+
+
+def lib():
+    """The loaded libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m ring_exact_attention_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, lib().attn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _need(t, name, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
+                kv_block=0, q_pos0=0, kv_pos0=0, flags=0) -> AttnParams:
+    B, Sq, Hq, D = q.shape
+    Bk, Skv, Hkv, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on batch or head_dim")
+    p = AttnParams()
+    p.struct_size = ctypes.sizeof(AttnParams)
+    p.dtype = _dtype_code(q)
+    p.batch, p.seqlen_q, p.seqlen_kv = B, Sq, Skv
+    p.num_q_heads, p.num_kv_heads, p.head_dim = Hq, Hkv, D
+    p.q_pos0, p.kv_pos0 = int(q_pos0), int(kv_pos0)
+    p.causal = 1 if causal else 0
+    p.window_left, p.window_right = int(window[0]), int(window[1])
+    p.scale = 0.0 if scale is None else float(scale)
+    p.query_chunk, p.key_chunk, p.kv_block = int(query_chunk), int(key_chunk), int(kv_block)
+    p.flags = int(flags)
+    return p
+
+
+def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
+             kv_block=0, q_pos0=0, kv_pos0=0, m=None, l=None, acc=None, carry_in=False,
+             finalize=True, out=None):
+    """Forward attention.  q [B, Sq, Hq, D], k/v [B, Skv, Hkv, D] on the GPU.
+
+    Returns (o, m, l); with ``finalize=False`` returns (acc, m, l) where acc is the
+    fp32 unnormalised numerator.  ``carry_in=True`` resumes from the given m, l, acc.
+    """
+    _need(q, "q")
+    _need(k, "k", q.dtype, q.device)
+    _need(v, "v", q.dtype, q.device)
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape")
+    B, Sq, Hq, D = q.shape
+    flags = (ATTN_CARRY_IN if carry_in else 0) | (0 if finalize else ATTN_NO_FINALIZE)
+    p = make_params(q, k, causal=causal, window=window, scale=scale, query_chunk=query_chunk,
+                    key_chunk=key_chunk, kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, flags=flags)
+    dev = q.device
+    if m is None:
+        m = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    if l is None:
+        l = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    _need(m, "m", torch.float32, dev)
+    _need(l, "l", torch.float32, dev)
+    if (carry_in or not finalize) and acc is None:
+        acc = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=dev)
+    if acc is not None:
+        _need(acc, "acc", torch.float32, dev)
+    o = None
+    if finalize:
+        o = out if out is not None else torch.empty_like(q)
+        _need(o, "o", q.dtype, dev)
+    _check(lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l),
+                          _ptr(acc), _stream(q)))
+    return (o, m, l) if finalize else (acc, m, l)
+
+
+def bwd_workspace_bytes(q, k, **kw) -> int:
+    p = make_params(q, k, **kw)
+    return int(lib().attn_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None, query_chunk=0,
+             key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, workspace=None, out=None):
+    """Gradients (dq, dk, dv) of attn_fwd's output for upstream gradient dout."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, q.dtype, q.device)
+    _need(m, "m", torch.float32, q.device)
+    _need(l, "l", torch.float32, q.device)
+    kw = dict(causal=causal, window=window, scale=scale, query_chunk=query_chunk, key_chunk=key_chunk,
+              kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0)
+    p = make_params(q, k, **kw)
+    need = int(lib().attn_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    _check(lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(m),
+                          _ptr(l), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq, dk, dv
+
+
+def _joint(x):
+    """[B, S, H, D] or [B, S, E] -> [B, S, E] view (heads flattened into one embedding)."""
+    return x.reshape(x.shape[0], x.shape[1], -1) if x.dim() == 4 else x
+
+
+def block_select(q, k, *, block_size=32, top_n=8, workspace=None, out=None):
+    """Exact top-n earlier-block selection by block-mean inner product -> int32 [B, S, top_n]."""
+    q, k = _joint(q), _joint(k)
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, q.device)
+    B, S, E = q.shape
+    p = SelectParams()
+    p.struct_size = ctypes.sizeof(SelectParams)
+    p.dtype = ATTN_BF16
+    p.batch, p.seqlen, p.embed = B, S, E
+    p.block_size, p.top_n = int(block_size), int(top_n)
+    need = int(lib().block_select_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    idx = out if out is not None else torch.empty((B, S, top_n), dtype=torch.int32, device=q.device)
+    _check(lib().block_select(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(idx), _ptr(workspace),
+                              workspace.numel(), _stream(q)))
+    return idx
+
+
+def attn_fwd_sparse(q, k, v, idx, *, window=32, block_size=32, scale=None, out=None):
+    """Attention of every token over its zero-padded window ++ selected blocks."""
+    q, k, v = _joint(q), _joint(k), _joint(v)
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, q.device)
+    _need(v, "v", torch.bfloat16, q.device)
+    _need(idx, "idx", torch.int32, q.device)
+    B, S, E = q.shape
+    top_n = idx.shape[-1]
+    if idx.shape != (B, S, top_n):
+        raise ValueError("idx must be [B, S, top_n]")
+    p = AttnParams()
+    p.struct_size = ctypes.sizeof(AttnParams)
+    p.dtype = ATTN_BF16
+    p.batch, p.seqlen_q, p.seqlen_kv = B, S, S
+    p.num_q_heads = p.num_kv_heads = 1
+    p.head_dim = E
+    p.scale = 0.0 if scale is None else float(scale)
+    p.sel_idx = idx.data_ptr()
+    p.top_n, p.sel_block, p.sparse_window = int(top_n), int(block_size), int(window)
+    o = out if out is not None else torch.empty_like(q)
+    m = torch.empty((B, S), dtype=torch.float32, device=q.device)
+    l = torch.empty((B, S), dtype=torch.float32, device=q.device)
+    _check(lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l), None,
+                          _stream(q)))
+    return o, m, l
+
+
+def flops_fwd(visible_pairs_per_head: int, heads: int, batch: int, head_dim: int) -> float:
+    """Algorithmic forward flops: 4*D per visible (query, key) pair per q head."""
+    return 4.0 * head_dim * visible_pairs_per_head * heads * batch
+
+
+def flops_bwd(visible_pairs_per_head: int, heads: int, batch: int, head_dim: int) -> float:
+    """Algorithmic backward flops: 10*D per visible pair (recompute S, dP, dV, dQ, dK)."""
+    return 10.0 * head_dim * visible_pairs_per_head * heads * batch
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

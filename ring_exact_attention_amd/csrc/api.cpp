@@ -1,0 +1,344 @@
+// C-ABI entry points of libattn.so (declared in include/attn.h).
+//
+// Every argument is validated here, on the host, before anything is launched; a
+// failed check returns a status code and leaves a thread-local message.  Nothing in
+// this file allocates device memory: scratch comes in through the caller's workspace.
+#include "attn.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+int ok() {
+  g_err.clear();
+  return ATTN_OK;
+}
+
+constexpr long long kMaxLen = 1LL << 28;    // rows per call
+constexpr long long kMaxPos = 1LL << 27;    // |global position of row 0|
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+std::string fmt(const char* f, long long a, long long b = 0) {
+  char buf[256];
+  snprintf(buf, sizeof buf, f, a, b);
+  return buf;
+}
+
+// A validated dense (or sparse) problem.
+struct Problem {
+  int dtype = 0, B = 0, Sq = 0, Skv = 0, Hq = 0, Hkv = 0, D = 0, G = 1;
+  int delta = 0, lo_off = -rea::kPosInf, hi_off = rea::kPosInf;
+  float scale = 1.f;
+  int kv_block = 1, n_vblocks = 0, q_vblock = 1, n_qvblocks = 0;
+  bool carry_in = false, finalize = true;
+};
+
+int check_dense(const attn_params* p, bool bwd, Problem& r) {
+  if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size != sizeof(attn_params))
+    return fail(ATTN_ERR_INVALID_ARG, fmt("params->struct_size is %lld, this library expects %lld",
+                                          (long long)p->struct_size, (long long)sizeof(attn_params)));
+  if (p->reserved != 0) return fail(ATTN_ERR_INVALID_ARG, "params->reserved must be 0");
+  if (p->dtype != ATTN_BF16 && p->dtype != ATTN_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, fmt("dtype %lld is not supported (ATTN_BF16 or ATTN_F32)", p->dtype));
+  if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_kv < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "batch, seqlen_q and seqlen_kv must be >= 0");
+  if (p->seqlen_q > kMaxLen || p->seqlen_kv > kMaxLen)
+    return fail(ATTN_ERR_UNSUPPORTED, fmt("sequence lengths above %lld are not supported", kMaxLen));
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0)
+    return fail(ATTN_ERR_INVALID_ARG, "num_q_heads and num_kv_heads must be > 0");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fmt("num_q_heads (%lld) must be a multiple of num_kv_heads (%lld)",
+                                          p->num_q_heads, p->num_kv_heads));
+  const int D = p->head_dim;
+  const bool d_ok = p->dtype == ATTN_BF16 ? (D == 32 || D == 64 || D == 128) : (D == 32 || D == 64);
+  if (!d_ok)
+    return fail(ATTN_ERR_UNSUPPORTED, fmt("head_dim %lld is not supported for this dtype "
+                                          "(bf16: 32, 64, 128; f32: 32, 64)", D));
+  if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->window_left < -1 || p->window_right < -1)
+    return fail(ATTN_ERR_INVALID_ARG, "window_left and window_right must be >= -1 (-1 = unbounded)");
+  if (p->causal && p->window_right > 0)
+    return fail(ATTN_ERR_INVALID_ARG, "a causal mask accepts window_right of -1 or 0 only");
+  if (p->q_pos0 < -kMaxPos || p->q_pos0 > kMaxPos || p->kv_pos0 < -kMaxPos || p->kv_pos0 > kMaxPos)
+    return fail(ATTN_ERR_UNSUPPORTED, fmt("|q_pos0|, |kv_pos0| above %lld are not supported", kMaxPos));
+  if (std::isinf(p->scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  if (p->query_chunk < 0 || p->key_chunk < 0 || p->kv_block < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "query_chunk, key_chunk and kv_block must be >= 0");
+  if (p->query_chunk > 0 && p->seqlen_q % p->query_chunk != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fmt("query_chunk (%lld) must divide seqlen_q (%lld)",
+                                          p->query_chunk, p->seqlen_q));
+  if (p->key_chunk > 0 && p->seqlen_kv % p->key_chunk != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fmt("key_chunk (%lld) must divide seqlen_kv (%lld)",
+                                          p->key_chunk, p->seqlen_kv));
+  if (p->kv_block > 0 && p->seqlen_kv % p->kv_block != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fmt("kv_block (%lld) must divide seqlen_kv (%lld)",
+                                          p->kv_block, p->seqlen_kv));
+  const uint32_t known = ATTN_CARRY_IN | ATTN_NO_FINALIZE;
+  if (p->flags & ~known) return fail(ATTN_ERR_INVALID_ARG, "unknown bits in flags");
+  if (bwd && p->flags) return fail(ATTN_ERR_INVALID_ARG, "attn_bwd takes no flags");
+
+  r.dtype = p->dtype;
+  r.B = p->batch;
+  r.Sq = p->seqlen_q;
+  r.Skv = p->seqlen_kv;
+  r.Hq = p->num_q_heads;
+  r.Hkv = p->num_kv_heads;
+  r.D = D;
+  r.G = r.Hq / r.Hkv;
+  r.delta = (int)(p->kv_pos0 - p->q_pos0);
+  // A window wider than any distance between rows is the same as no window.
+  const long long wl = p->window_left > kMaxLen * 2 ? -1 : p->window_left;
+  const long long wr = p->window_right > kMaxLen * 2 ? -1 : p->window_right;
+  r.lo_off = wl >= 0 ? -(int)wl : -rea::kPosInf;
+  int hi = rea::kPosInf;
+  if (p->causal) hi = 0;
+  if (wr >= 0 && wr < hi) hi = (int)wr;
+  r.hi_off = hi;
+  r.scale = (p->scale > 0.f) ? p->scale : 1.f / std::sqrt((float)D);
+  r.kv_block = p->kv_block > 0 ? p->kv_block : (r.Skv > 0 ? r.Skv : 1);
+  r.n_vblocks = r.Skv / r.kv_block;
+  r.q_vblock = (r.Sq > 0 && r.Sq % r.kv_block == 0) ? r.kv_block : (r.Sq > 0 ? r.Sq : 1);
+  r.n_qvblocks = r.Sq / r.q_vblock;
+  r.carry_in = (p->flags & ATTN_CARRY_IN) != 0;
+  r.finalize = (p->flags & ATTN_NO_FINALIZE) == 0;
+  return ATTN_OK;
+}
+
+int check_ptr(const void* ptr, const char* name) {
+  if (!ptr) return fail(ATTN_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, std::string(name) + " must be 16-byte aligned");
+  return ATTN_OK;
+}
+
+int xcd_groups(int B, int Hkv) { return ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0; }
+
+int hip_status(hipError_t e) {
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, std::string("HIP error: ") + hipGetErrorString(e));
+  return ok();
+}
+
+// Gathered block-sparse forward (sel_idx != NULL).
+int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o, float* m,
+               float* l, void* stream) {
+  if (p->struct_size != sizeof(attn_params))
+    return fail(ATTN_ERR_INVALID_ARG, "params->struct_size does not match this library");
+  if (p->reserved != 0) return fail(ATTN_ERR_INVALID_ARG, "params->reserved must be 0");
+  if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode supports bf16 only");
+  if (p->num_q_heads != 1 || p->num_kv_heads != 1)
+    return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes the joint embedding: num_q_heads = num_kv_heads = 1");
+  if (p->head_dim != 512) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode supports head_dim (embed) 512");
+  if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_kv != p->seqlen_q)
+    return fail(ATTN_ERR_INVALID_ARG, "sparse mode needs seqlen_q == seqlen_kv >= 0");
+  if (p->seqlen_q > kMaxLen) return fail(ATTN_ERR_UNSUPPORTED, "sequence too long");
+  if (p->top_n < 1 || p->top_n > 16) return fail(ATTN_ERR_INVALID_ARG, "top_n must be in 1..16");
+  if (p->sel_block < 1 || p->sel_block > 64) return fail(ATTN_ERR_INVALID_ARG, "sel_block must be in 1..64");
+  if (p->sparse_window < 1 || p->sparse_window > 64)
+    return fail(ATTN_ERR_INVALID_ARG, "sparse_window must be in 1..64");
+  if (p->flags) return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes no flags");
+  if (std::isinf(p->scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  if (p->batch == 0 || p->seqlen_q == 0) return ok();
+  int st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")) || (st = check_ptr(m, "m")) || (st = check_ptr(l, "l")))
+    return st;
+  rea::SparseArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sel = p->sel_idx;
+  a.o = o;
+  a.m = m;
+  a.l = l;
+  a.B = p->batch;
+  a.S = p->seqlen_q;
+  a.E = p->head_dim;
+  a.top_n = p->top_n;
+  a.sel_block = p->sel_block;
+  a.window = p->sparse_window;
+  a.scale = p->scale > 0.f ? p->scale : 1.f / std::sqrt((float)a.E);
+  a.scale_log2 = a.scale * rea::kLog2e;
+  return hip_status(rea::launch_sparse(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+uint32_t attn_abi_version(void) { return ATTN_PARAMS_VERSION; }
+
+int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o, float* m,
+             float* l, float* acc, void* stream) {
+  if (p && p->sel_idx) return sparse_fwd(p, q, k, v, o, m, l, stream);
+  Problem r;
+  int st = check_dense(p, false, r);
+  if (st) return st;
+  if (r.B == 0 || r.Sq == 0) return ok();
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(m, "m")) || (st = check_ptr(l, "l"))) return st;
+  if (r.Skv > 0 && ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")))) return st;
+  if (r.finalize && (st = check_ptr(o, "o"))) return st;
+  if ((r.carry_in || !r.finalize) && (st = check_ptr(acc, "acc (needed by ATTN_CARRY_IN / ATTN_NO_FINALIZE)")))
+    return st;
+  rea::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.m = m;
+  a.l = l;
+  a.acc = acc;
+  a.B = r.B;
+  a.Sq = r.Sq;
+  a.Skv = r.Skv;
+  a.Hq = r.Hq;
+  a.Hkv = r.Hkv;
+  a.G = r.G;
+  a.D = r.D;
+  a.delta = r.delta;
+  a.lo_off = r.lo_off;
+  a.hi_off = r.hi_off;
+  a.scale = r.scale;
+  a.scale_log2 = r.scale * rea::kLog2e;
+  a.kv_block = r.kv_block;
+  a.n_vblocks = r.n_vblocks;
+  a.carry_in = r.carry_in;
+  a.finalize = r.finalize;
+  const int bm = rea::fwd_tile_rows(r.dtype);
+  a.n_qtiles = (r.Sq + bm - 1) / bm;
+  a.xcd_groups = r.dtype == ATTN_BF16 ? xcd_groups(r.B, r.Hkv) : 0;
+  if ((long long)a.n_qtiles * r.B * r.Hq >= (1LL << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+  return hip_status(rea::launch_fwd(r.dtype, a, (hipStream_t)stream));
+}
+
+size_t attn_bwd_workspace_bytes(const attn_params* p) {
+  Problem r;
+  const std::string saved = g_err;
+  if (!p || check_dense(p, true, r) != ATTN_OK) return 0;
+  g_err = saved;
+  const size_t n = (size_t)r.B * r.Hq * r.Sq * sizeof(float);
+  return 2 * align_up(n > 0 ? n : 1);
+}
+
+int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const float* m, const float* l, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  if (p && p->sel_idx) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd has no sparse mode");
+  Problem r;
+  int st = check_dense(p, true, r);
+  if (st) return st;
+  if (r.B == 0 || (r.Sq == 0 && r.Skv == 0)) return ok();
+  const size_t need = attn_bwd_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
+                                        (long long)(workspace ? workspace_bytes : 0)));
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (r.Sq > 0 && ((st = check_ptr(q, "q")) || (st = check_ptr(o, "o")) || (st = check_ptr(dout, "dout")) ||
+                   (st = check_ptr(m, "m")) || (st = check_ptr(l, "l")) || (st = check_ptr(dq, "dq"))))
+    return st;
+  if (r.Skv > 0 && ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(dk, "dk")) ||
+                    (st = check_ptr(dv, "dv"))))
+    return st;
+  rea::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.m = m;
+  a.l = l;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const size_t n = (size_t)r.B * r.Hq * r.Sq * sizeof(float);
+  a.Dvec = (float*)workspace;
+  a.lse2 = (float*)((char*)workspace + align_up(n > 0 ? n : 1));
+  a.B = r.B;
+  a.Sq = r.Sq;
+  a.Skv = r.Skv;
+  a.Hq = r.Hq;
+  a.Hkv = r.Hkv;
+  a.G = r.G;
+  a.D = r.D;
+  a.delta = r.delta;
+  a.lo_off = r.lo_off;
+  a.hi_off = r.hi_off;
+  a.scale = r.scale;
+  a.scale_log2 = r.scale * rea::kLog2e;
+  a.kv_block = r.kv_block;
+  a.n_vblocks = r.n_vblocks;
+  a.q_vblock = r.q_vblock;
+  a.n_qvblocks = r.n_qvblocks;
+  const int bq = rea::bwd_q_tile_rows(r.dtype), bk = rea::bwd_k_tile_rows(r.dtype);
+  a.n_qtiles = (r.Sq + bq - 1) / bq;
+  a.n_ktiles = (r.Skv + bk - 1) / bk;
+  a.xcd_groups = r.dtype == ATTN_BF16 ? xcd_groups(r.B, r.Hkv) : 0;
+  a.xcd_kv_groups = a.xcd_groups;
+  if ((long long)a.n_qtiles * r.B * r.Hq >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large");
+  return hip_status(rea::launch_bwd(r.dtype, a, (hipStream_t)stream));
+}
+
+size_t block_select_workspace_bytes(const select_params* p) {
+  if (!p || p->struct_size != sizeof(select_params) || p->batch < 0 || p->seqlen < 0 || p->embed <= 0 ||
+      p->block_size <= 0)
+    return 0;
+  const size_t nblk = (size_t)(p->seqlen / p->block_size);
+  const size_t n = (size_t)p->batch * nblk * p->embed * sizeof(double);
+  return align_up(n > 0 ? n : 1);
+}
+
+int block_select(const select_params* p, const void* q, const void* k, int32_t* idx, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size != sizeof(select_params))
+    return fail(ATTN_ERR_INVALID_ARG, "params->struct_size does not match this library");
+  if (p->reserved != 0) return fail(ATTN_ERR_INVALID_ARG, "params->reserved must be 0");
+  if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "block_select supports bf16 inputs");
+  if (p->batch < 0 || p->seqlen < 0) return fail(ATTN_ERR_INVALID_ARG, "batch and seqlen must be >= 0");
+  if (p->seqlen > kMaxLen) return fail(ATTN_ERR_UNSUPPORTED, "sequence too long");
+  if (p->embed <= 0 || p->embed % 64 != 0 || p->embed > 1024)
+    return fail(ATTN_ERR_UNSUPPORTED, "embed must be a multiple of 64 up to 1024");
+  if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
+    return fail(ATTN_ERR_UNSUPPORTED, "block_size must be 16, 32 or 64");
+  if (p->top_n < 1 || p->top_n > 16) return fail(ATTN_ERR_INVALID_ARG, "top_n must be in 1..16");
+  if (p->batch == 0 || p->seqlen == 0) return ok();
+  int st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(idx, "idx"))) return st;
+  const size_t need = block_select_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
+                                        (long long)(workspace ? workspace_bytes : 0)));
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  rea::SelectArgs a{};
+  a.q = q;
+  a.k = k;
+  a.idx = idx;
+  a.means = (double*)workspace;
+  a.B = p->batch;
+  a.S = p->seqlen;
+  a.E = p->embed;
+  a.bs = p->block_size;
+  a.top_n = p->top_n;
+  a.nblk = p->seqlen / p->block_size;
+  return hip_status(rea::launch_select(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// Shared device-side definitions for the gfx950 attention kernels.
+//
+// Everything here is plain HIP for CDNA4: 64-wide wavefronts, bf16 MFMA with fp32
+// accumulation, LDS staging.  The kernel argument structs are filled by the host
+// layer (api.cpp) after it has validated the C-ABI parameters.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+namespace rea {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPosInf = 1 << 30;   // "unbounded" key offset (positions are validated < 2^29)
+
+// Forward kernel arguments (dense path).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* m;
+  float* l;
+  float* acc;
+  int B, Sq, Skv, Hq, Hkv, G, D;
+  // Visibility of (row i, key j): lo_off <= (j - i) + delta <= hi_off, with
+  // delta = kv_pos0 - q_pos0 and j < Skv.
+  int delta;
+  int lo_off;
+  int hi_off;
+  float scale;        // natural-units logit scale
+  float scale_log2;   // scale * log2(e)
+  int kv_block;       // rows per virtual ring block (>= 1)
+  int n_vblocks;      // Skv / kv_block
+  int carry_in;
+  int finalize;
+  int n_qtiles;       // ceil(Sq / BM)
+  int xcd_groups;     // (B*Hkv) / 8 when the XCD-aware order applies, else 0
+};
+
+// Backward kernel arguments (dense path).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* m;
+  const float* l;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* Dvec;        // [B, Hq, Sq] workspace: rowsum(dO * o)
+  float* lse2;        // [B, Hq, Sq] workspace: m*log2(e) + log2(l)  (log2 units)
+  int B, Sq, Skv, Hq, Hkv, G, D;
+  int delta, lo_off, hi_off;
+  float scale, scale_log2;
+  int kv_block, n_vblocks;     // virtual key blocks (ring order of the dq pass)
+  int q_vblock, n_qvblocks;    // virtual query blocks (ring order of the dk/dv pass)
+  int n_qtiles, n_ktiles;      // grid sizes: query tiles (dq), key tiles (dk/dv)
+  int xcd_groups;              // (B*Hkv)/8 for the XCD-aware dq order, else 0
+  int xcd_kv_groups;           // same for the dk/dv grid
+};
+
+struct SelectArgs {
+  const void* q;
+  const void* k;
+  int32_t* idx;
+  double* means;      // [B, nblk, E] workspace
+  int B, S, E, bs, top_n, nblk;
+};
+
+struct SparseArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* sel;
+  void* o;
+  float* m;
+  float* l;
+  int B, S, E, top_n, sel_block, window;
+  float scale_log2, scale;
+};
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by the lane in the other half of the wavefront (lane ^ 32).
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const bool lo = (threadIdx.x & 63) < 32;
+  return __uint_as_float(lo ? r[1] : r[0]);
+}
+
+// Two floats -> two bf16 (round to nearest even) packed in one dword.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __hip_bfloat162 p = __float22bfloat162_rn(make_float2(a, b));
+  uint32_t u;
+  __builtin_memcpy(&u, &p, 4);
+  return u;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
+
+// Clamp an int64 to the int32 range used for key offsets.
+__host__ __device__ inline int clamp_i32(long long x) {
+  return x > kPosInf ? kPosInf : (x < -kPosInf ? -kPosInf : (int)x);
+}
+
+}  // namespace rea

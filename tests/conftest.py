@@ -21,3 +21,12 @@ def gpu():
         pytest.skip("no GPU")
     import ring_exact_attention_amd as rea
     return rea
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_test(request):
+    """Name each GPU test on the real stderr before it runs (survives a lost box)."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"[gpu-test] start {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

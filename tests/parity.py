@@ -1,0 +1,62 @@
+"""Tolerances for comparing GPU results with the fp64 oracle.
+
+bf16 outputs / gradients: |gpu - ref| <= 2e-2 + 2^-8 |ref| element-wise (the second
+term is one bf16 rounding of the stored value, needed where |ref| >= 8 since the bf16
+half-ulp there exceeds 2e-2), plus a relative Frobenius error <= 1e-2 so that the
+absolute bound cannot pass vacuously on small outputs.
+fp32: |gpu - ref| <= 1e-4 + 2^-24 |ref| and relative Frobenius <= 1e-5.
+Statistics: m within 1e-3 (bf16) / 1e-4 (fp32) absolute, l within 1e-3 / 1e-4 relative;
+rows without any visible key must read m = -inf, l = 0 on both sides.
+"""
+import numpy as np
+import torch
+
+
+def to_np(x):
+    if isinstance(x, torch.Tensor):
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def tol(dtype):
+    bf16 = dtype in ("bf16", torch.bfloat16)
+    return (2e-2, 2.0 ** -8, 1e-2) if bf16 else (1e-4, 2.0 ** -24, 1e-5)
+
+
+def check_close(name, gpu, ref, dtype, sel=None):
+    g, r = to_np(gpu), to_np(ref)
+    if sel is not None:
+        g, r = g[sel], r[sel]
+    keep = ~np.isnan(r)
+    g, r = g[keep], r[keep]
+    assert g.size > 0, f"{name}: nothing to compare"
+    assert np.isfinite(g).all(), f"{name}: non-finite GPU values"
+    atol, rt, frob = tol(dtype)
+    err = np.abs(g - r)
+    bound = atol + rt * np.abs(r)
+    bad = err > bound
+    denom = np.linalg.norm(r)
+    rel = np.linalg.norm(g - r) / denom if denom > 0 else np.linalg.norm(g - r)
+    assert not bad.any(), (f"{name}: {int(bad.sum())} of {g.size} outside tolerance; max abs err "
+                           f"{err.max():.3e}, max |ref| {np.abs(r).max():.3e}, rel frob {rel:.3e}")
+    assert rel <= frob, f"{name}: relative Frobenius error {rel:.3e} > {frob}"
+    return float(err.max()), float(rel)
+
+
+def check_stats(m_gpu, l_gpu, m_ref, l_ref, dtype, sel=None):
+    mg, lg, mr, lr = to_np(m_gpu), to_np(l_gpu), to_np(m_ref), to_np(l_ref)
+    if sel is not None:
+        mg, lg, mr, lr = mg[sel], lg[sel], mr[sel], lr[sel]
+    keep = ~np.isnan(mr)
+    mg, lg, mr, lr = mg[keep], lg[keep], mr[keep], lr[keep]
+    bf16 = dtype in ("bf16", torch.bfloat16)
+    m_tol, l_tol = (1e-3, 1e-3) if bf16 else (1e-4, 1e-4)
+    empty = np.isneginf(mr)
+    assert np.array_equal(np.isneginf(mg), empty), "rows without visible keys differ"
+    assert np.all(lg[empty] == 0)
+    full = ~empty
+    if full.any():
+        dm = np.abs(mg[full] - mr[full]).max()
+        dl = (np.abs(lg[full] - lr[full]) / lr[full]).max()
+        assert dm <= m_tol, f"m: max abs err {dm:.3e}"
+        assert dl <= l_tol, f"l: max rel err {dl:.3e}"

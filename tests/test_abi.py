@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: libattn.so loads, exports every function include/attn.h
+declares, the ctypes structs match the C layout, and every argument check returns its
+status before anything touches the device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ring_exact_attention_amd as rea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rea.LIB_PATH):
+        from ring_exact_attention_amd import build
+        build.build()
+    return rea.lib()
+
+
+def declared_functions():
+    names = []
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?(?:int|size_t|uint32_t|char\s*\*|void)\s*\*?\s*(\w+)\s*\(",
+                            text, flags=re.M)
+    return names
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "block_select",
+            "block_select_workspace_bytes", "attn_last_error", "attn_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert lib.attn_abi_version() == 1
+
+
+def params(**kw):
+    p = rea.AttnParams()
+    p.struct_size = ctypes.sizeof(rea.AttnParams)
+    base = dict(dtype=rea.ATTN_BF16, batch=1, seqlen_q=128, seqlen_kv=128, num_q_heads=4,
+                num_kv_heads=2, head_dim=128, causal=1, window_left=-1, window_right=-1)
+    base.update(kw)
+    for k_, v_ in base.items():
+        setattr(p, k_, v_)
+    return p
+
+
+def fwd_status(lib, p, ptr=None):
+    dummy = ctypes.c_void_p(ptr)
+    return lib.attn_fwd(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, None, None)
+
+
+def test_struct_layout(lib):
+    assert ctypes.sizeof(rea.AttnParams) == 104
+    assert ctypes.sizeof(rea.SelectParams) == 32
+    # a zero batch is a successful no-op only when the struct size matches
+    assert fwd_status(lib, params(batch=0)) == rea.ATTN_OK
+    p = params(batch=0)
+    p.struct_size = 100
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG
+    assert b"struct_size" in lib.attn_last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(num_q_heads=6, num_kv_heads=4), rea.ATTN_ERR_INVALID_ARG, b"multiple"),
+    (dict(num_q_heads=0), rea.ATTN_ERR_INVALID_ARG, b"> 0"),
+    (dict(head_dim=48), rea.ATTN_ERR_UNSUPPORTED, b"head_dim"),
+    (dict(dtype=rea.ATTN_F32, head_dim=128), rea.ATTN_ERR_UNSUPPORTED, b"head_dim"),
+    (dict(dtype=7), rea.ATTN_ERR_UNSUPPORTED, b"dtype"),
+    (dict(seqlen_q=-1), rea.ATTN_ERR_INVALID_ARG, b">= 0"),
+    (dict(causal=1, window_right=3), rea.ATTN_ERR_INVALID_ARG, b"window_right"),
+    (dict(window_left=-2), rea.ATTN_ERR_INVALID_ARG, b"-1"),
+    (dict(query_chunk=48), rea.ATTN_ERR_INVALID_ARG, b"query_chunk"),
+    (dict(key_chunk=96), rea.ATTN_ERR_INVALID_ARG, b"key_chunk"),
+    (dict(kv_block=100), rea.ATTN_ERR_INVALID_ARG, b"kv_block"),
+    (dict(flags=8), rea.ATTN_ERR_INVALID_ARG, b"flags"),
+    (dict(causal=2), rea.ATTN_ERR_INVALID_ARG, b"causal"),
+    (dict(q_pos0=1 << 40), rea.ATTN_ERR_UNSUPPORTED, b"q_pos0"),
+    (dict(scale=float("inf")), rea.ATTN_ERR_INVALID_ARG, b"scale"),
+    (dict(reserved=1), rea.ATTN_ERR_INVALID_ARG, b"reserved"),
+])
+def test_forward_argument_checks(lib, kw, status, msg):
+    assert fwd_status(lib, params(**kw)) == status
+    assert msg in lib.attn_last_error()
+
+
+def test_null_and_misaligned_pointers(lib):
+    assert fwd_status(lib, params()) == rea.ATTN_ERR_INVALID_ARG
+    assert b"q is NULL" in lib.attn_last_error()
+    assert fwd_status(lib, params(), ptr=0x1008) == rea.ATTN_ERR_INVALID_ARG
+    assert b"aligned" in lib.attn_last_error()
+
+
+def test_no_finalize_needs_acc(lib):
+    p = params(flags=rea.ATTN_NO_FINALIZE)
+    d = ctypes.c_void_p(0x1000)
+    st = lib.attn_fwd(ctypes.byref(p), d, d, d, None, d, d, None, None)
+    assert st == rea.ATTN_ERR_INVALID_ARG and b"acc" in lib.attn_last_error()
+
+
+def test_backward_checks(lib):
+    p = params()
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(p))
+    assert need == 2 * 2048                           # D and LSE: 4*128 floats each, 256-aligned
+    d = ctypes.c_void_p(0x1000)
+    st = lib.attn_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, need - 1, None)
+    assert st == rea.ATTN_ERR_WORKSPACE
+    st = lib.attn_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, None, need, None)
+    assert st == rea.ATTN_ERR_WORKSPACE
+    p2 = params(flags=rea.ATTN_CARRY_IN)
+    st = lib.attn_bwd(ctypes.byref(p2), d, d, d, d, d, d, d, d, d, d, d, need, None)
+    assert st == rea.ATTN_ERR_INVALID_ARG and b"flags" in lib.attn_last_error()
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(params(head_dim=48))) == 0
+
+
+def test_sparse_mode_checks(lib):
+    d = ctypes.c_void_p(0x1000)
+    p = params(num_q_heads=1, num_kv_heads=1, head_dim=512, seqlen_q=64, seqlen_kv=64, causal=0)
+    p.sel_idx = 0x1000
+    p.top_n, p.sel_block, p.sparse_window = 8, 32, 32
+    p.num_q_heads = 8
+    assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_ERR_INVALID_ARG
+    p.num_q_heads = 1
+    p.top_n = 17
+    assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_ERR_INVALID_ARG
+    p.top_n = 8
+    p.batch = 0
+    assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_OK
+
+
+def test_select_checks(lib):
+    p = rea.SelectParams()
+    p.struct_size = ctypes.sizeof(rea.SelectParams)
+    p.dtype, p.batch, p.seqlen, p.embed, p.block_size, p.top_n = rea.ATTN_BF16, 2, 256, 512, 32, 8
+    need = lib.block_select_workspace_bytes(ctypes.byref(p))
+    assert need == 2 * 8 * 512 * 8
+    d = ctypes.c_void_p(0x1000)
+    assert lib.block_select(ctypes.byref(p), d, d, d, d, need - 8, None) == rea.ATTN_ERR_WORKSPACE
+    p.block_size = 24
+    assert lib.block_select(ctypes.byref(p), d, d, d, d, need, None) == rea.ATTN_ERR_UNSUPPORTED
+    p.block_size, p.embed = 32, 100
+    assert lib.block_select(ctypes.byref(p), d, d, d, d, need, None) == rea.ATTN_ERR_UNSUPPORTED
+    p.embed, p.batch = 512, 0
+    assert lib.block_select(ctypes.byref(p), d, d, d, d, need, None) == rea.ATTN_OK
+
+
+def test_success_clears_error(lib):
+    fwd_status(lib, params(head_dim=48))
+    assert lib.attn_last_error() != b""
+    assert fwd_status(lib, params(batch=0)) == rea.ATTN_OK
+    assert lib.attn_last_error() == b""

@@ -1,0 +1,240 @@
+"""GPU parity of the dense path (attn_fwd / attn_bwd through the C ABI) against the
+fp64 oracle, on seeded inputs.
+
+* small shapes that span several tiles and end in a ragged tail, for every mask kind
+  (causal, sliding window, right window, none), GQA, position offsets, Sq != Skv,
+  virtual ring blocks, bf16 head dims 32/64/128 and the fp32 path;
+* every workload at its full size, in the launch configuration bench.py times, checked
+  on sampled heads / rows the oracle can compute;
+* the step API (carry in / no finalize), determinism and the degenerate cases.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import dense
+from parity import check_close, check_stats
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def rnd(shape, seed, dtype):
+    return workloads.random_tensor(shape, seed, dtype=dtype)
+
+
+def tdtype(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+SMALL = [
+    # id, dtype, B, Sq, Skv, Hq, Hkv, D, causal, window, q_pos0, kv_pos0, kv_block
+    ("bf16_d128_causal_gqa2_ragged", "bf16", 2, 300, 300, 4, 2, 128, True, (-1, -1), 0, 0, 0),
+    ("bf16_d64_full_ragged", "bf16", 1, 333, 333, 2, 1, 64, False, (-1, -1), 0, 0, 0),
+    ("bf16_d128_swa37_gqa4", "bf16", 1, 515, 515, 8, 2, 128, True, (37, 0), 0, 0, 0),
+    ("bf16_d32_window_offsets", "bf16", 1, 200, 260, 2, 2, 32, False, (5, 7), 60, 0, 0),
+    ("bf16_d128_ring4", "bf16", 1, 1024, 1024, 2, 2, 128, True, (-1, -1), 0, 0, 256),
+    ("bf16_d128_ring_swa", "bf16", 1, 768, 768, 4, 1, 128, True, (100, 0), 0, 0, 128),
+    ("bf16_d128_right_window", "bf16", 1, 190, 190, 2, 1, 128, False, (-1, 20), 0, 0, 0),
+    ("bf16_d64_ring_tiny_blocks", "bf16", 1, 256, 256, 2, 2, 64, True, (-1, -1), 0, 0, 32),
+    ("f32_d32_causal_gqa2", "f32", 1, 256, 256, 4, 2, 32, True, (-1, -1), 0, 0, 64),
+    ("f32_d64_swa_ragged", "f32", 2, 77, 77, 2, 1, 64, True, (9, 0), 0, 0, 0),
+]
+
+
+def small_inputs(case):
+    _, dt, B, Sq, Skv, Hq, Hkv, D, *_ = case
+    t = tdtype(dt)
+    seed = zlib.crc32(case[0].encode()) % 10000
+    return (rnd((B, Sq, Hq, D), seed, t), rnd((B, Skv, Hkv, D), seed + 1, t),
+            rnd((B, Skv, Hkv, D), seed + 2, t), rnd((B, Sq, Hq, D), seed + 3, t))
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_forward(gpu, case):
+    name, dt, B, Sq, Skv, Hq, Hkv, D, causal, window, qp0, kp0, kvb = case
+    q, k, v, _ = small_inputs(case)
+    o, m, l = gpu.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window=window,
+                           q_pos0=qp0, kv_pos0=kp0, kv_block=kvb)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=causal, window=window, q_pos0=qp0, kv_pos0=kp0)
+    check_close("o", o, o_r, dt)
+    check_stats(m, l, m_r, l_r, dt)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_backward(gpu, case):
+    name, dt, B, Sq, Skv, Hq, Hkv, D, causal, window, qp0, kp0, kvb = case
+    q, k, v, do = small_inputs(case)
+    kw = dict(causal=causal, window=window, q_pos0=qp0, kv_pos0=kp0, kv_block=kvb)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **kw)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **kw)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, causal=causal, window=window, q_pos0=qp0, kv_pos0=kp0)
+    check_close("dq", dq, dq_r, dt)
+    check_close("dk", dk, dk_r, dt)
+    check_close("dv", dv, dv_r, dt)
+
+
+def full_inputs(name, with_dout=True):
+    w = workloads.WORKLOADS[name]
+    q, k, v, do = workloads.generate(w, with_dout=with_dout)
+    return w, q, k, v, do
+
+
+def launch_kw(w):
+    return dict(causal=w.causal, window=w.window, query_chunk=w.query_chunk, key_chunk=w.key_chunk,
+                kv_block=w.kv_block)
+
+
+def oracle_kw(w):
+    return dict(causal=w.causal, window=w.window)
+
+
+def test_tiny_fp32_workload(gpu):
+    w, q, k, v, do = full_inputs("tiny_causal_gqa_fp32")
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, scale=w.scale, **launch_kw(w))
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, scale=w.scale, **launch_kw(w))
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, scale=w.scale, **oracle_kw(w))
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, scale=w.scale, **oracle_kw(w))
+    for nm, a, b in (("o", o, o_r), ("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r)):
+        check_close(nm, a, b, "f32")
+    check_stats(m, l, m_r, l_r, "f32")
+
+
+def test_ring_sim_full_size(gpu):
+    """B1 S8192 H16 D128 causal, 8 virtual blocks: all rows of 3 heads (fwd), 2 heads (bwd)."""
+    w, q, k, v, do = full_inputs("ring_sim_causal_s8192")
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **launch_kw(w))
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **launch_kw(w))
+    torch.cuda.synchronize()
+    heads = [0, 7, 15]
+    o_r, m_r, l_r = dense.forward(q, k, v, heads=heads, **oracle_kw(w))
+    check_close("o", o[:, :, heads], o_r[:, :, heads], "bf16")
+    check_stats(m[:, heads], l[:, heads], m_r[:, heads], l_r[:, heads], "bf16")
+    bh = [3, 12]
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, heads=bh, **oracle_kw(w))
+    check_close("dq", dq[:, :, bh], dq_r[:, :, bh], "bf16")
+    check_close("dk", dk[:, :, bh], dk_r[:, :, bh], "bf16")      # G = 1: kv head = q head
+    check_close("dv", dv[:, :, bh], dv_r[:, :, bh], "bf16")
+
+
+def test_gqa_swa_full_size(gpu):
+    """B2 S4096 Hq128 Hkv8 D128, window (128, 0): one full GQA group checked fwd and bwd."""
+    w, q, k, v, do = full_inputs("gqa16_swa128_s4096")
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **launch_kw(w))
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **launch_kw(w))
+    torch.cuda.synchronize()
+    group = 5
+    heads = list(range(16 * group, 16 * group + 16))
+    b = 1
+    qs, ks, vs, dos = q[b:b + 1], k[b:b + 1], v[b:b + 1], do[b:b + 1]
+    o_r, m_r, l_r = dense.forward(qs, ks, vs, heads=heads, **oracle_kw(w))
+    check_close("o", o[b:b + 1, :, heads], o_r[:, :, heads], "bf16")
+    check_stats(m[b:b + 1, heads], l[b:b + 1, heads], m_r[:, heads], l_r[:, heads], "bf16")
+    dq_r, dk_r, dv_r = dense.backward(qs, ks, vs, dos, heads=heads, **oracle_kw(w))
+    check_close("dq", dq[b:b + 1, :, heads], dq_r[:, :, heads], "bf16")
+    check_close("dk", dk[b:b + 1, :, group], dk_r[:, :, group], "bf16")
+    check_close("dv", dv[b:b + 1, :, group], dv_r[:, :, group], "bf16")
+
+
+def test_long_context_sampled_rows(gpu):
+    """B1 S131072 Hq32 Hkv8 D128 causal, 32 virtual blocks of 4096: sampled rows."""
+    w, q, k, v, _ = full_inputs("long_causal_s131072", with_dout=False)
+    o, m, l = gpu.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), **launch_kw(w))
+    torch.cuda.synchronize()
+    g = np.random.default_rng(3)
+    blk = w.kv_block
+    rows = sorted(set([0, 1, blk - 1, blk, 17 * blk + 5, w.seqlen - 1] +
+                      list(g.integers(0, w.seqlen, 10))))
+    heads = [0, 13, 31]
+    o_r, m_r, l_r = dense.forward(q, k, v, rows=rows, heads=heads, **oracle_kw(w))
+    check_close("o", o[:, rows][:, :, heads], o_r[:, rows][:, :, heads], "bf16")
+    check_stats(m[:, heads][:, :, rows], l[:, heads][:, :, rows], m_r[:, heads][:, :, rows],
+                l_r[:, heads][:, :, rows], "bf16")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_step_api_carry_equals_single_call(gpu, dt):
+    """Two ring steps (the later kv block first, as the ring visits them) with the carry
+    handed over through m, l, acc equal one call over both blocks."""
+    t = tdtype(dt)
+    B, S, Hq, Hkv, D = 1, 512, 4, 2, (128 if dt == "bf16" else 32)
+    q, k, v = rnd((B, S, Hq, D), 11, t), rnd((B, 2 * S, Hkv, D), 12, t), rnd((B, 2 * S, Hkv, D), 13, t)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    # queries occupy positions S..2S-1 (ring member 1), keys 0..2S-1 in two blocks
+    acc, m, l = gpu.attn_fwd(qd, kd[:, S:].contiguous(), vd[:, S:].contiguous(), causal=True,
+                             q_pos0=S, kv_pos0=S, finalize=False)
+    o, m, l = gpu.attn_fwd(qd, kd[:, :S].contiguous(), vd[:, :S].contiguous(), causal=True,
+                           q_pos0=S, kv_pos0=0, carry_in=True, m=m, l=l, acc=acc)
+    o1, m1, l1 = gpu.attn_fwd(qd, kd, vd, causal=True, q_pos0=S, kv_pos0=0)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=True, q_pos0=S, kv_pos0=0)
+    check_close("o (two steps)", o, o_r, dt)
+    check_stats(m, l, m_r, l_r, dt)
+    check_close("o (one call)", o1, o_r, dt)
+
+
+def test_no_finalize_carry_matches_oracle(gpu):
+    B, S, H, D = 1, 256, 2, 64
+    q, k, v = rnd((B, S, H, D), 21, torch.bfloat16), rnd((B, S, H, D), 22, torch.bfloat16), \
+        rnd((B, S, H, D), 23, torch.bfloat16)
+    acc, m, l = gpu.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, finalize=False)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=True)
+    check_stats(m, l, m_r, l_r, "bf16")
+    # acc is the unnormalised numerator: acc / l must be the attention output
+    check_close("acc/l", acc / l.transpose(1, 2)[..., None], o_r, "bf16")
+
+
+def test_backward_is_deterministic(gpu):
+    B, S, Hq, Hkv, D = 1, 640, 8, 2, 128
+    q, k, v, do = (rnd((B, S, Hq, D), 31, torch.bfloat16).to(DEV), rnd((B, S, Hkv, D), 32, torch.bfloat16).to(DEV),
+                   rnd((B, S, Hkv, D), 33, torch.bfloat16).to(DEV), rnd((B, S, Hq, D), 34, torch.bfloat16).to(DEV))
+    o, m, l = gpu.attn_fwd(q, k, v, causal=True, window=(200, 0))
+    a = gpu.attn_bwd(q, k, v, o, do, m, l, causal=True, window=(200, 0))
+    b = gpu.attn_bwd(q, k, v, o, do, m, l, causal=True, window=(200, 0))
+    o2, _, _ = gpu.attn_fwd(q, k, v, causal=True, window=(200, 0))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert torch.equal(o, o2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_rows_without_visible_keys(gpu, dt):
+    t = tdtype(dt)
+    B, Sq, Skv, H, D = 1, 200, 150, 2, 64
+    q, k, v, do = rnd((B, Sq, H, D), 41, t), rnd((B, Skv, H, D), 42, t), rnd((B, Skv, H, D), 43, t), \
+        rnd((B, Sq, H, D), 44, t)
+    kw = dict(causal=True, q_pos0=0, kv_pos0=100)      # queries 0..99 precede every key
+    o, m, l = gpu.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), **kw)
+    dq, dk, dv = gpu.attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), o, do.to(DEV), m, l, **kw)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, **kw)
+    check_close("o", o, o_r, dt)
+    check_stats(m, l, m_r, l_r, dt)
+    assert torch.all(o[:, :100] == 0) and torch.all(dq[:, :100] == 0)
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, **kw)
+    check_close("dk", dk, dk_r, dt)
+    check_close("dv", dv, dv_r, dt)
+
+
+def test_empty_key_set_and_zero_sizes(gpu):
+    q = rnd((1, 64, 2, 64), 51, torch.bfloat16).to(DEV)
+    k = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, device=DEV)
+    o, m, l = gpu.attn_fwd(q, k, k, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(m)) and torch.all(l == 0)
+    q0 = torch.empty((0, 64, 2, 64), dtype=torch.bfloat16, device=DEV)
+    o0, _, _ = gpu.attn_fwd(q0, q0, q0)
+    assert o0.shape == q0.shape
