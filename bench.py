@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Throughput of blockwise exact attention (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward and one backward pass of the whole attention over one batch of
+synthetic seeded input resident in HBM.  The default workload is one GPU's share of a
+causal ring: B1, S8192, 16 heads of 128, bf16, 8 virtual key blocks of 1024 visited
+in ring order.  Prints ONE JSON line: whole-step TFLOP/s over the algorithmic flops
+(4*D per visible pair forward, 10*D backward), per-kernel HIP-event timings, the
+roofline of the dominant kernel, and the oracle timed on a bounded sample on the host
+cores as a CPU baseline.
+
+Only one GPU is used: a run asking for more exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 + % of MFMA peak at 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+
+
+def visible_pairs(Sq, Skv, causal, window, q_pos0=0, kv_pos0=0):
+    """Visible (query, key) pairs per (batch, q head) for the causal / window mask."""
+    import numpy as np
+    i = np.arange(Sq, dtype=np.int64) + q_pos0
+    lo = np.full(Sq, kv_pos0, dtype=np.int64)
+    hi = np.full(Sq, kv_pos0 + Skv - 1, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, i)
+    if window[1] >= 0:
+        hi = np.minimum(hi, i + window[1])
+    if window[0] >= 0:
+        lo = np.maximum(lo, i - window[0])
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def cpu_baseline(w, q, k, v, do, budget_s):
+    """The oracle (numpy fp64) on whole heads of the same workload until ~budget_s."""
+    import numpy as np
+    from oracle import dense
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    pairs = visible_pairs(w.seqlen, w.seqlen, w.causal, w.window)
+    heads_done, flops, t0 = 0, 0.0, time.perf_counter()
+    for h in range(w.num_q_heads):
+        dense.forward(q[:1], k[:1], v[:1], causal=w.causal, window=w.window, heads=[h])
+        if w.backward:
+            dense.backward(q[:1], k[:1], v[:1], do[:1], causal=w.causal, window=w.window, heads=[h])
+        heads_done += 1
+        flops += (14.0 if w.backward else 4.0) * w.head_dim * pairs
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    what = "fwd+bwd" if w.backward else "fwd"
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "host_cpus": os.cpu_count(), "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"oracle {what} (numpy fp64) of {heads_done} of {w.num_q_heads} q heads of batch 0 "
+                      f"at full length S={w.seqlen}; TFLOP/s over the same algorithmic flops as the GPU"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ring_sim_causal_s8192")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import ring_exact_attention_amd as rea
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    rea.lib()                                         # fail loudly if libattn.so is missing
+    w = workloads.WORKLOADS[args.workload]
+    if w.sparse:
+        print("use --workload with a dense workload; the block-sparse path is benchmarked by "
+              "its own tests", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    q, k, v, do = workloads.generate(w, with_dout=w.backward)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    dod = do.to(dev) if do is not None else None
+    kw = dict(causal=w.causal, window=w.window, query_chunk=w.query_chunk, key_chunk=w.key_chunk,
+              kv_block=w.kv_block)
+    B, S, Hq, Hkv, D = w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim
+    o = torch.empty_like(qd)
+    m = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
+    ws = torch.empty(max(rea.bwd_workspace_bytes(qd, kd, **kw), 256), dtype=torch.uint8, device=dev)
+
+    # One step, split into its kernels so each can be timed on the launch stream:
+    # forward | D/LSE pre-pass | dq | dk,dv.
+    def segments():
+        yield "attn_fwd", lambda: rea.attn_fwd(qd, kd, vd, out=o, m=m, l=l, **kw)
+        if w.backward:
+            yield "bwd_pre", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
+                                                  skip_dq=True, skip_dkdv=True, **kw)
+            yield "bwd_dq", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
+                                                 skip_dkdv=True, reuse_stats=True, **kw)
+            yield "bwd_dkdv", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
+                                                   skip_dq=True, reuse_stats=True, **kw)
+
+    segs = list(segments())
+    for _ in range(args.warmup):
+        for _, fn in segs:
+            fn()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(segs) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev = events[s]
+        ev[0].record(stream)
+        for i, (_, fn) in enumerate(segs):
+            fn()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg_ms = {name: 0.0 for name, _ in segs}
+    for ev in events:
+        for i, (name, _) in enumerate(segs):
+            seg_ms[name] += ev[i].elapsed_time(ev[i + 1])
+    seg_ms = {n: t / args.steps for n, t in seg_ms.items()}
+
+    pairs = visible_pairs(S, S, w.causal, w.window) * B * Hq
+    f_fwd = 4.0 * D * pairs
+    f_bwd = 10.0 * D * pairs if w.backward else 0.0
+    # Algorithmic flops per kernel launch: the dk/dv kernel does the recompute of S and
+    # dP plus dV and dK (8D per pair); the dq kernel's share is dQ (2D per pair), its own
+    # recompute being the cost of computing dq without atomics.
+    alg = {"attn_fwd": f_fwd, "bwd_dq": 2.0 * D * pairs, "bwd_dkdv": 8.0 * D * pairs, "bwd_pre": 0.0}
+    # Compulsory HBM bytes per launch (bf16 tensors read or written once, fp32 stats).
+    esz = 2 if w.dtype == "bf16" else 4
+    qbytes, kvbytes, stat = B * S * Hq * D * esz, B * S * Hkv * D * esz, B * Hq * S * 4
+    hbm = {"attn_fwd": 2 * qbytes + 2 * kvbytes + 2 * stat,
+           "bwd_pre": 2 * qbytes + 4 * stat,
+           "bwd_dq": 3 * qbytes + 2 * kvbytes + 2 * stat,
+           "bwd_dkdv": 2 * qbytes + 4 * kvbytes + 2 * stat}
+    kernels = {}
+    for n, t in seg_ms.items():
+        kernels[n] = {"avg_us": round(t * 1e3, 2), "alg_gflop": round(alg[n] / 1e9, 3),
+                      "tflops": round(alg[n] / (t * 1e-3) / 1e12, 2),
+                      "hbm_gbs": round(hbm[n] / (t * 1e-3) / 1e9, 1)}
+    step_ms = sum(seg_ms.values())
+    ms_per_step = wall / args.steps * 1e3
+    total = f_fwd + f_bwd
+    value = total / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = f_fwd / (seg_ms["attn_fwd"] * 1e-3) / 1e12
+    bwd_ms = step_ms - seg_ms["attn_fwd"]
+    bwd_tflops = f_bwd / (bwd_ms * 1e-3) / 1e12 if w.backward else None
+
+    dom = max(seg_ms, key=seg_ms.get)
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(alg[dom] / (seg_ms[dom] * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(alg[dom] / (seg_ms[dom] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "avg_us": round(seg_ms[dom] * 1e3, 2), "alg_flop_per_launch": alg[dom], "traffic": None}
+    if w.window[0] >= 0:        # sliding window: the kernels are HBM-bound
+        roof.update({"bound": "hbm", "achieved": round(hbm[dom] / (seg_ms[dom] * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(hbm[dom] / (seg_ms[dom] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "alg_bytes_per_launch": hbm[dom]})
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "causal": w.causal, "window": list(w.window),
+                   "virtual_blocks": (S // w.kv_block) if w.kv_block else 1,
+                   "query_chunk": w.query_chunk, "key_chunk": w.key_chunk, "parallelism": "none (1 GPU)"},
+        "fwd_tflops": round(fwd_tflops, 2),
+        "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
+        "fwd_bwd_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_mfma_frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -60,7 +60,15 @@ enum {
   ATTN_CARRY_IN = 1u,
   /* Leave the carry unnormalised in m, l, acc and do not write o (a ring step that is
    * not the last one). */
-  ATTN_NO_FINALIZE = 2u
+  ATTN_NO_FINALIZE = 2u,
+  /* attn_bwd only: compute part of the backward pass.  dq is owned by the query
+   * block and dk/dv by the key block ("bpt.py", _ring_attention_bwd keeps dq local
+   * and passes dk, dv along the ring), so an owner may want only its share. */
+  ATTN_BWD_SKIP_DQ = 8u,       /* do not compute dq (dq may be NULL)                  */
+  ATTN_BWD_SKIP_DKDV = 16u,    /* do not compute dk, dv (both may be NULL)            */
+  ATTN_BWD_REUSE_STATS = 32u   /* the workspace already holds D and the log-sum-exp
+                                  written by an earlier attn_bwd call with the same
+                                  params, o, dout, m and l: do not recompute them     */
 };
 
 #define ATTN_PARAMS_VERSION 1u
@@ -88,7 +96,9 @@ typedef struct attn_params {
                                   must divide Skv.  Key blocks are visited in ring
                                   order starting at the block holding the query tile's
                                   own position and descending (mod the block count).  */
-  uint32_t flags;              /* ATTN_CARRY_IN | ATTN_NO_FINALIZE (attn_fwd only)     */
+  uint32_t flags;              /* attn_fwd: ATTN_CARRY_IN | ATTN_NO_FINALIZE;
+                                  attn_bwd: ATTN_BWD_SKIP_DQ | ATTN_BWD_SKIP_DKDV |
+                                  ATTN_BWD_REUSE_STATS                                  */
   /* Gathered block-sparse mode ("AnnAttention", faiss_block_attention): when sel_idx
    * is non-NULL, attn_fwd attends each token to a zero-padded window of
    * sparse_window keys ending at the token, followed by the sel_block rows of each of
@@ -151,7 +161,8 @@ int attn_fwd(const attn_params* params, const void* q, const void* k, const void
  *   dq [out] [B, Sq, Hq, D]; dk, dv [out] [B, Skv, Hkv, D] (element type of q).
  *   workspace        device scratch of at least attn_bwd_workspace_bytes(params)
  *                    bytes (256-byte aligned); its contents are overwritten.
- * flags must be 0 and sel_idx NULL.  The result is bitwise reproducible run to run.
+ * flags: 0 or a combination of the ATTN_BWD_* flags; sel_idx must be NULL.  The
+ * result is bitwise reproducible run to run.
  */
 int attn_bwd(const attn_params* params, const void* q, const void* k, const void* v,
              const void* o, const void* dout, const float* m, const float* l,

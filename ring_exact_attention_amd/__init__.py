@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, -1, -2, -3, -4
 ATTN_BF16, ATTN_F32 = 0, 1
 ATTN_CARRY_IN, ATTN_NO_FINALIZE = 1, 2
+ATTN_BWD_SKIP_DQ, ATTN_BWD_SKIP_DKDV, ATTN_BWD_REUSE_STATS = 8, 16, 32
 
 
 class AttnParams(ctypes.Structure):
@@ -204,17 +205,27 @@ def bwd_workspace_bytes(q, k, **kw) -> int:
 
 
 def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None, query_chunk=0,
-             key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, workspace=None, out=None):
-    """Gradients (dq, dk, dv) of attn_fwd's output for upstream gradient dout."""
+             key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, workspace=None, out=None,
+             skip_dq=False, skip_dkdv=False, reuse_stats=False):
+    """Gradients (dq, dk, dv) of attn_fwd's output for upstream gradient dout.
+
+    ``skip_dq`` / ``skip_dkdv`` compute only part of them (the skipped outputs are left
+    untouched); ``reuse_stats`` takes D and the log-sum-exp from ``workspace`` as left
+    by an earlier call with the same inputs.
+    """
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _need(t, n, q.dtype, q.device)
     _need(m, "m", torch.float32, q.device)
     _need(l, "l", torch.float32, q.device)
     kw = dict(causal=causal, window=window, scale=scale, query_chunk=query_chunk, key_chunk=key_chunk,
               kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0)
-    p = make_params(q, k, **kw)
+    flags = ((ATTN_BWD_SKIP_DQ if skip_dq else 0) | (ATTN_BWD_SKIP_DKDV if skip_dkdv else 0) |
+             (ATTN_BWD_REUSE_STATS if reuse_stats else 0))
+    p = make_params(q, k, flags=flags, **kw)
     need = int(lib().attn_bwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
+        if reuse_stats:
+            raise ValueError("reuse_stats needs the workspace of the earlier call")
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     _check(lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(m),

@@ -88,9 +88,13 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   if (p->kv_block > 0 && p->seqlen_kv % p->kv_block != 0)
     return fail(ATTN_ERR_INVALID_ARG, fmt("kv_block (%lld) must divide seqlen_kv (%lld)",
                                           p->kv_block, p->seqlen_kv));
-  const uint32_t known = ATTN_CARRY_IN | ATTN_NO_FINALIZE;
-  if (p->flags & ~known) return fail(ATTN_ERR_INVALID_ARG, "unknown bits in flags");
-  if (bwd && p->flags) return fail(ATTN_ERR_INVALID_ARG, "attn_bwd takes no flags");
+  const uint32_t fwd_flags = ATTN_CARRY_IN | ATTN_NO_FINALIZE;
+  const uint32_t bwd_flags = ATTN_BWD_SKIP_DQ | ATTN_BWD_SKIP_DKDV | ATTN_BWD_REUSE_STATS;
+  if (p->flags & ~(fwd_flags | bwd_flags)) return fail(ATTN_ERR_INVALID_ARG, "unknown bits in flags");
+  if (bwd && (p->flags & fwd_flags))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_bwd flags: only the ATTN_BWD_* flags apply");
+  if (!bwd && (p->flags & bwd_flags))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_fwd flags: the ATTN_BWD_* flags do not apply");
 
   r.dtype = p->dtype;
   r.B = p->batch;
@@ -146,7 +150,8 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
     return fail(ATTN_ERR_INVALID_ARG, "sparse mode needs seqlen_q == seqlen_kv >= 0");
   if (p->seqlen_q > kMaxLen) return fail(ATTN_ERR_UNSUPPORTED, "sequence too long");
   if (p->top_n < 1 || p->top_n > 16) return fail(ATTN_ERR_INVALID_ARG, "top_n must be in 1..16");
-  if (p->sel_block < 1 || p->sel_block > 64) return fail(ATTN_ERR_INVALID_ARG, "sel_block must be in 1..64");
+  if (p->sel_block != 16 && p->sel_block != 32 && p->sel_block != 64)
+    return fail(ATTN_ERR_UNSUPPORTED, "sel_block must be 16, 32 or 64");
   if (p->sparse_window < 1 || p->sparse_window > 64)
     return fail(ATTN_ERR_INVALID_ARG, "sparse_window must be in 1..64");
   if (p->flags) return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes no flags");
@@ -250,12 +255,16 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
                                         (long long)(workspace ? workspace_bytes : 0)));
   if (((uintptr_t)workspace & (kAlign - 1)) != 0)
     return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (r.Sq > 0 && ((st = check_ptr(q, "q")) || (st = check_ptr(o, "o")) || (st = check_ptr(dout, "dout")) ||
-                   (st = check_ptr(m, "m")) || (st = check_ptr(l, "l")) || (st = check_ptr(dq, "dq"))))
+  const bool do_pre = !(p->flags & ATTN_BWD_REUSE_STATS);
+  const bool do_dq = !(p->flags & ATTN_BWD_SKIP_DQ);
+  const bool do_dkdv = !(p->flags & ATTN_BWD_SKIP_DKDV);
+  if (r.Sq > 0 && ((st = check_ptr(q, "q")) || (st = check_ptr(dout, "dout"))))
     return st;
-  if (r.Skv > 0 && ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(dk, "dk")) ||
-                    (st = check_ptr(dv, "dv"))))
+  if (r.Sq > 0 && do_pre && ((st = check_ptr(o, "o")) || (st = check_ptr(m, "m")) || (st = check_ptr(l, "l"))))
     return st;
+  if (r.Sq > 0 && do_dq && (st = check_ptr(dq, "dq"))) return st;
+  if (r.Skv > 0 && ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")))) return st;
+  if (r.Skv > 0 && do_dkdv && ((st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))) return st;
   rea::BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -291,6 +300,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.n_ktiles = (r.Skv + bk - 1) / bk;
   a.xcd_groups = r.dtype == ATTN_BF16 ? xcd_groups(r.B, r.Hkv) : 0;
   a.xcd_kv_groups = a.xcd_groups;
+  a.stages = (do_pre ? 1 : 0) | (do_dq ? 2 : 0) | (do_dkdv ? 4 : 0);
   if ((long long)a.n_qtiles * r.B * r.Hq >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large");
   return hip_status(rea::launch_bwd(r.dtype, a, (hipStream_t)stream));
 }
@@ -317,6 +327,8 @@ int block_select(const select_params* p, const void* q, const void* k, int32_t* 
     return fail(ATTN_ERR_UNSUPPORTED, "embed must be a multiple of 64 up to 1024");
   if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
     return fail(ATTN_ERR_UNSUPPORTED, "block_size must be 16, 32 or 64");
+  if ((long long)p->embed * p->block_size > 32768)
+    return fail(ATTN_ERR_UNSUPPORTED, "embed * block_size above 32768 is not supported");
   if (p->top_n < 1 || p->top_n > 16) return fail(ATTN_ERR_INVALID_ARG, "top_n must be in 1..16");
   if (p->batch == 0 || p->seqlen == 0) return ok();
   int st;

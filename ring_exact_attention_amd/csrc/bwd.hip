@@ -626,12 +626,13 @@ static void launch_pre(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd(int dtype, const BwdArgs& a, hipStream_t stream) {
   const dim3 gq((unsigned)a.n_qtiles * a.B * a.Hq), gk((unsigned)a.n_ktiles * a.B * a.Hkv);
   const bool has_q = gq.x > 0, has_k = gk.x > 0;
+  const bool pre = has_q && (a.stages & 1), dq = has_q && (a.stages & 2), dkdv = has_k && (a.stages & 4);
   const dim3 bb(dtype == 0 ? 256 : 128);
 #define REA_BWD(T, DD, DQ, DKV)                                                  \
   do {                                                                          \
-    if (has_q) launch_pre<T, DD>(a, stream);                                    \
-    if (has_q) hipLaunchKernelGGL(DQ<DD>, gq, bb, 0, stream, a);                \
-    if (has_k) hipLaunchKernelGGL(DKV<DD>, gk, bb, 0, stream, a);               \
+    if (pre) launch_pre<T, DD>(a, stream);                                      \
+    if (dq) hipLaunchKernelGGL(DQ<DD>, gq, bb, 0, stream, a);                   \
+    if (dkdv) hipLaunchKernelGGL(DKV<DD>, gk, bb, 0, stream, a);                \
   } while (0)
   if (dtype == 0) {
     switch (a.D) {

@@ -69,6 +69,7 @@ struct BwdArgs {
   int n_qtiles, n_ktiles;      // grid sizes: query tiles (dq), key tiles (dk/dv)
   int xcd_groups;              // (B*Hkv)/8 for the XCD-aware dq order, else 0
   int xcd_kv_groups;           // same for the dk/dv grid
+  int stages;                  // bit 0: D/LSE pre-pass, bit 1: dq, bit 2: dk/dv
 };
 
 struct SelectArgs {

@@ -121,6 +121,14 @@ def test_backward_checks(lib):
     st = lib.attn_bwd(ctypes.byref(p2), d, d, d, d, d, d, d, d, d, d, d, need, None)
     assert st == rea.ATTN_ERR_INVALID_ARG and b"flags" in lib.attn_last_error()
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(params(head_dim=48))) == 0
+    # partial backward: dq may be NULL when skipped, not otherwise
+    p3 = params(flags=rea.ATTN_BWD_SKIP_DQ | rea.ATTN_BWD_SKIP_DKDV | rea.ATTN_BWD_REUSE_STATS, batch=0)
+    assert lib.attn_bwd(ctypes.byref(p3), d, d, d, d, d, d, d, None, None, None, d, need, None) == rea.ATTN_OK
+    p4 = params(flags=rea.ATTN_BWD_SKIP_DKDV)
+    st = lib.attn_bwd(ctypes.byref(p4), d, d, d, d, d, d, d, None, d, d, d, need, None)
+    assert st == rea.ATTN_ERR_INVALID_ARG and b"dq is NULL" in lib.attn_last_error()
+    p5 = params(flags=rea.ATTN_BWD_SKIP_DQ)
+    assert lib.attn_fwd(ctypes.byref(p5), d, d, d, d, d, d, None, None) == rea.ATTN_ERR_INVALID_ARG
 
 
 def test_sparse_mode_checks(lib):

@@ -1,0 +1,102 @@
+"""GPU parity of block_select (bit-exact indices) and the gathered block-sparse forward
+(attn_fwd with sel_idx) against the fp64 oracle, on seeded inputs: small ragged shapes,
+engineered exact ties, the degenerate first blocks, and the full-size workload
+(B4 S8192, 8 heads x 64 as a joint embedding of 512, top-8 of 32-token blocks, window 32)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import select, sparse
+from parity import check_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def rnd(shape, seed):
+    return workloads.random_tensor(shape, seed, dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("B,S,E,bs,n", [(2, 256, 64, 16, 3), (1, 300, 512, 32, 8), (2, 200, 128, 64, 2),
+                                         (1, 1000, 512, 32, 16), (3, 64, 64, 32, 1)])
+def test_select_small(gpu, B, S, E, bs, n):
+    q, k = rnd((B, S, E), S + E), rnd((B, S, E), S + E + 1)
+    idx = gpu.block_select(q.to(DEV), k.to(DEV), block_size=bs, top_n=n)
+    torch.cuda.synchronize()
+    ref = select.block_select(q, k, block_size=bs, top_n=n)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+
+
+def test_select_exact_ties(gpu):
+    """Integer-valued inputs with duplicated key blocks: every tie must go to the lower index."""
+    B, S, E, bs, n = 2, 512, 64, 32, 3
+    g = torch.Generator().manual_seed(5)
+    k = torch.randint(-2, 3, (B, S, E), generator=g).to(torch.bfloat16)
+    for b in range(B):
+        for c in range(4, S // bs, 3):
+            k[b, c * bs:(c + 1) * bs] = k[b, (c - 3) * bs:(c - 2) * bs]     # block c repeats block c-3
+    q = torch.randint(-2, 3, (B, S, E), generator=g).to(torch.bfloat16)
+    idx = gpu.block_select(q.to(DEV), k.to(DEV), block_size=bs, top_n=n)
+    torch.cuda.synchronize()
+    ref = select.block_select(q, k, block_size=bs, top_n=n)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+
+
+def test_select_full_size(gpu):
+    w = workloads.WORKLOADS["block_sparse_top8_s8192"]
+    q, k, v, _ = workloads.generate(w)
+    idx = gpu.block_select(q.to(DEV), k.to(DEV), block_size=w.block_size, top_n=w.top_n)
+    torch.cuda.synchronize()
+    ref, gap = select.block_select(q, k, block_size=w.block_size, top_n=w.top_n, return_gap=True)
+    print(f"smallest gap between the 8th and 9th score: {gap:.3e}")
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("B,S,bs,n,W", [(1, 200, 32, 4, 32), (2, 160, 16, 8, 7), (1, 256, 64, 2, 64),
+                                        (1, 96, 32, 8, 1)])
+def test_sparse_small(gpu, B, S, bs, n, W):
+    E = 512
+    q, k, v = rnd((B, S, E), 7 + S), rnd((B, S, E), 8 + S), rnd((B, S, E), 9 + S)
+    sel = select.block_select(q, k, block_size=bs, top_n=n)
+    o, m, l = gpu.attn_fwd_sparse(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(sel).to(DEV),
+                                  window=W, block_size=bs)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = sparse.sparse_attention(q, k, v, sel, window=W, block_size=bs)
+    check_close("o", o, o_r, "bf16")
+    np.testing.assert_allclose(m.cpu().numpy(), m_r, atol=1e-3, rtol=0)
+    np.testing.assert_allclose(l.cpu().numpy(), l_r, rtol=1e-3, atol=0)
+
+
+def test_sparse_zero_keys_uniform_weights(gpu):
+    """K = 0: all logits 0, so o is the plain mean over all slots (zero pads, duplicate
+    clamped rows of token 0 and all)."""
+    B, S, E, bs, n, W = 1, 160, 512, 32, 8, 32
+    q, v = rnd((B, S, E), 11), rnd((B, S, E), 12)
+    k = torch.zeros((B, S, E), dtype=torch.bfloat16)
+    sel = select.block_select(q, k, block_size=bs, top_n=n)
+    o, m, l = gpu.attn_fwd_sparse(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(sel).to(DEV),
+                                  window=W, block_size=bs)
+    torch.cuda.synchronize()
+    o_r, _, _ = sparse.sparse_attention(q, k, v, sel, window=W, block_size=bs)
+    check_close("o", o, o_r, "bf16")
+    assert torch.all(l == W + n * bs)
+
+
+def test_sparse_full_size_sampled(gpu):
+    w = workloads.WORKLOADS["block_sparse_top8_s8192"]
+    q, k, v, _ = workloads.generate(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    idx = gpu.block_select(qd, kd, block_size=w.block_size, top_n=w.top_n)
+    o, m, l = gpu.attn_fwd_sparse(qd, kd, vd, idx, window=w.sparse_window, block_size=w.block_size)
+    torch.cuda.synchronize()
+    sel = idx.cpu().numpy()
+    g = np.random.default_rng(4)
+    toks = sorted(set([0, 1, 31, 32, 255, 256, 4095, w.seqlen - 1] + list(g.integers(0, w.seqlen, 24))))
+    o_r, m_r, l_r = sparse.sparse_attention(q, k, v, sel, window=w.sparse_window, block_size=w.block_size,
+                                            tokens=toks)
+    oo = o.view(w.batch, w.seqlen, -1)
+    check_close("o", oo[:, toks], o_r[:, toks], "bf16")
+    np.testing.assert_allclose(m.cpu().numpy()[:, toks], m_r[:, toks], atol=1e-3, rtol=0)
+    np.testing.assert_allclose(l.cpu().numpy()[:, toks], l_r[:, toks], rtol=1e-3, atol=0)
