@@ -72,6 +72,109 @@ def cpu_baseline(w, q, k, v, do, budget_s):
                       f"at full length S={w.seqlen}; TFLOP/s over the same algorithmic flops as the GPU"}
 
 
+def time_segments(torch, segs, steps, warmup, stream):
+    """Run warmup + timed steps of the segment list; per-segment mean ms from HIP events."""
+    for _ in range(warmup):
+        for _, fn in segs:
+            fn()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(segs) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev = events[s]
+        ev[0].record(stream)
+        for i, (_, fn) in enumerate(segs):
+            fn()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg_ms = {name: 0.0 for name, _ in segs}
+    for ev in events:
+        for i, (name, _) in enumerate(segs):
+            seg_ms[name] += ev[i].elapsed_time(ev[i + 1])
+    return {n: t / steps for n, t in seg_ms.items()}, wall
+
+
+def copy_calibration(torch, dev, args):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    n = args.copy_bytes
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    seg_ms, _ = time_segments(torch, [("copy", lambda: b.copy_(a))], args.steps, args.warmup,
+                              torch.cuda.current_stream(dev))
+    print(json.dumps({"copy_bytes": n, "avg_us": round(seg_ms["copy"] * 1e3, 2),
+                      "gbs": round(2 * n / (seg_ms["copy"] * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def sparse_cpu_baseline(w, q, k, v, sel, budget_s):
+    import numpy as np
+    from oracle import select, sparse
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    E = w.head_dim
+    t0 = time.perf_counter()
+    select.block_select(q[:1], k[:1], block_size=w.block_size, top_n=w.top_n)
+    t_sel = time.perf_counter() - t0
+    sel_flops = 2.0 * E * w.block_size * sum(range(w.seqlen // w.block_size))
+    slots = w.sparse_window + w.top_n * w.block_size
+    toks, t1 = 0, time.perf_counter()
+    step = 64
+    while time.perf_counter() - t1 < budget_s and toks < w.seqlen:
+        sparse.sparse_attention(q[:1], k[:1], v[:1], sel[:1], window=w.sparse_window,
+                                block_size=w.block_size, tokens=range(toks, min(toks + step, w.seqlen)))
+        toks = min(toks + step, w.seqlen)
+    t_sp = time.perf_counter() - t1
+    gathered = toks * slots * E * 2 * 2
+    return {"value": round(gathered / t_sp / 1e9, 4), "unit": "GB/s gathered", "cores": int(threads),
+            "host_cpus": os.cpu_count(), "kind": "oracle", "seconds": round(t_sel + t_sp, 2),
+            "select_tflops": round(sel_flops / t_sel / 1e12, 6),
+            "sample": f"oracle block_select of batch 0 (full S={w.seqlen}) and oracle sparse attention of "
+                      f"its first {toks} tokens (numpy fp64)"}
+
+
+def bench_sparse(torch, rea, workloads, w, dev, args):
+    """Block selection + gathered sparse attention (one step = both)."""
+    q, k, v, _ = workloads.generate(w, with_dout=False)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    B, S, E = w.batch, w.seqlen, w.head_dim
+    idx = torch.empty((B, S, w.top_n), dtype=torch.int32, device=dev)
+    o = torch.empty_like(qd)
+    segs = [("block_select", lambda: rea.block_select(qd, kd, block_size=w.block_size, top_n=w.top_n, out=idx)),
+            ("attn_fwd_sparse", lambda: rea.attn_fwd_sparse(qd, kd, vd, idx, window=w.sparse_window,
+                                                            block_size=w.block_size, out=o))]
+    seg_ms, wall = time_segments(torch, segs, args.steps, args.warmup, torch.cuda.current_stream(dev))
+    slots = w.sparse_window + w.top_n * w.block_size
+    gathered = B * S * slots * E * 2 * 2
+    f_sparse = B * S * slots * E * 4.0
+    f_select = B * 2.0 * E * w.block_size * sum(range(S // w.block_size))
+    ms = wall / args.steps * 1e3
+    kernels = {"block_select": {"avg_us": round(seg_ms["block_select"] * 1e3, 2),
+                                "fp64_gflop": round(f_select / 1e9, 3),
+                                "fp64_tflops": round(f_select / (seg_ms["block_select"] * 1e-3) / 1e12, 3)},
+               "attn_fwd_sparse": {"avg_us": round(seg_ms["attn_fwd_sparse"] * 1e3, 2),
+                                   "gathered_gb": round(gathered / 1e9, 3),
+                                   "gathered_gbs": round(gathered / (seg_ms["attn_fwd_sparse"] * 1e-3) / 1e9, 1),
+                                   "tflops": round(f_sparse / (seg_ms["attn_fwd_sparse"] * 1e-3) / 1e12, 2)}}
+    ach = gathered / (seg_ms["attn_fwd_sparse"] * 1e-3) / 1e9
+    out = {"metric": METRIC, "value": round((f_sparse + f_select) / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": w.name, "batch": B, "seq_len": S, "embed": E, "block_size": w.block_size,
+                      "top_n": w.top_n, "window": w.sparse_window, "parallelism": "none (1 GPU)"},
+           "kernels": kernels,
+           "roofline": {"kernel": "attn_fwd_sparse", "bound": "hbm", "achieved": round(ach, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                        "avg_us": round(seg_ms["attn_fwd_sparse"] * 1e3, 2), "alg_bytes_per_launch": gathered,
+                        "traffic": None}}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = sparse_cpu_baseline(w, q, k, v, idx.cpu().numpy(), args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,6 +183,8 @@ def main():
     ap.add_argument("--workload", default="ring_sim_causal_s8192")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -97,11 +202,11 @@ def main():
         sys.exit(1)
     rea.lib()                                         # fail loudly if libattn.so is missing
     w = workloads.WORKLOADS[args.workload]
-    if w.sparse:
-        print("use --workload with a dense workload; the block-sparse path is benchmarked by "
-              "its own tests", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.copy_bytes:
+        return copy_calibration(torch, dev, args)
+    if w.sparse:
+        return bench_sparse(torch, rea, workloads, w, dev, args)
     q, k, v, do = workloads.generate(w, with_dout=w.backward)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     dod = do.to(dev) if do is not None else None
@@ -127,28 +232,7 @@ def main():
                                                    skip_dq=True, reuse_stats=True, **kw)
 
     segs = list(segments())
-    for _ in range(args.warmup):
-        for _, fn in segs:
-            fn()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(segs) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev = events[s]
-        ev[0].record(stream)
-        for i, (_, fn) in enumerate(segs):
-            fn()
-            ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    seg_ms = {name: 0.0 for name, _ in segs}
-    for ev in events:
-        for i, (name, _) in enumerate(segs):
-            seg_ms[name] += ev[i].elapsed_time(ev[i + 1])
-    seg_ms = {n: t / args.steps for n, t in seg_ms.items()}
+    seg_ms, wall = time_segments(torch, segs, args.steps, args.warmup, torch.cuda.current_stream(dev))
 
     pairs = visible_pairs(S, S, w.causal, w.window) * B * Hq
     f_fwd = 4.0 * D * pairs
