@@ -124,6 +124,32 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) {
   return r;
 }
 
+// Raw buffer resource over `bytes` bytes at `base`: loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte load at base + voffset + soffset (bytes); zero when out of range.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j points at 4 consecutive
+// 16-bit values (row j of a 16 x 4 block); lane i receives column i % 4 of rows
+// i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12.
+typedef short short4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
+  typedef __attribute__((address_space(3))) short4v lds_s4;
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s4*)((__attribute__((address_space(3))) char*)((uintptr_t)p)));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ bf16x8 join_bf16x8(u32x2 lo, u32x2 hi) {
+  const u32x4 u = {lo[0], lo[1], hi[0], hi[1]};
+  return as_bf16x8(u);
+}
+
 // Clamp an int64 to the int32 range used for key offsets.
 __host__ __device__ inline int clamp_i32(long long x) {
   return x > kPosInf ? kPosInf : (x < -kPosInf ? -kPosInf : (int)x);

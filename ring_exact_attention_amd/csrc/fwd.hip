@@ -12,9 +12,14 @@
 // S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so that each lane owns one query row
 // (column of the accumulator): the row max / sum need one cross-half exchange, and
 // the probabilities P^T are already in the B-operand layout of O^T = V^T P^T.
-// K tiles are staged row-major in LDS (A operand of S^T), V tiles transposed with a
-// key permutation (A operand of O^T), both double-buffered through registers.
-// Accumulation is fp32; exp uses v_exp_f32 on logits pre-scaled by scale*log2(e).
+// K and V tiles are fetched with raw buffer loads (rows past the end read as zero) and
+// staged row-major in LDS at a pitch of D + 32 elements, double-buffered through
+// registers.  K feeds S^T with 16-byte reads; the transposed V operand of O^T is read
+// with ds_read_b64_tr_b16, in the key order of the score accumulator.  Both read
+// patterns are free of LDS bank conflicts at that pitch.
+// Accumulation is fp32; exp uses v_exp_f32 on logits pre-scaled by scale*log2(e).  The
+// carry is rescaled only when a row max grows by more than 2^8 (exact: numerator and
+// denominator share the stale reference), and the stored statistics use the exact max.
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
@@ -27,18 +32,19 @@ struct FwdCfg {
   static constexpr int BN = 64;                    // keys per tile
   static constexpr int KS = D / 16;                // k-steps of S^T over d
   static constexpr int DB = D / 32;                // 32-row blocks of O^T
-  static constexpr int KROW = D + 8;               // K tile row pitch (elements)
-  static constexpr int VROW = BN + 8;              // V^T tile row pitch (elements)
-  static constexpr int KCH = BN * D / 8 / 256;     // 16-byte K chunks per thread
-  static constexpr int KG = BN * D / 2048;         // keys per thread in the V transpose
+  static constexpr int PITCH = D + 32;             // LDS row pitch (elements); 320 B at D = 128
   static constexpr int DC = D / 8;                 // 16-byte chunks per row
+  static constexpr int LPT = BN * DC / 256;        // 16-byte chunks per thread per tile and tensor
 };
+
+// Rows of the scores may grow by this much (log2 units) before the carry is rescaled.
+constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::BN * C::KROW];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][D * C::VROW];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::BN * C::PITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::BN * C::PITCH];
 
   int b, hq, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, a.xcd_groups, a.hi_off < kPosInf, b, hq, qt);
@@ -51,10 +57,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const bool row_ok = row < a.Sq;
 
   const size_t q_rs = (size_t)a.Hq * D;
-  const size_t kv_rs = (size_t)a.Hkv * D;
+  const uint32_t kv_rs_b = (uint32_t)a.Hkv * D * 2;           // bytes between key rows
   const __bf16* qp = (const __bf16*)a.q + (size_t)b * a.Sq * q_rs + (size_t)hq * D;
-  const __bf16* kp = (const __bf16*)a.k + (size_t)b * a.Skv * kv_rs + (size_t)hkv * D;
-  const __bf16* vp = (const __bf16*)a.v + (size_t)b * a.Skv * kv_rs + (size_t)hkv * D;
+  const size_t kv_base = ((size_t)b * a.Skv * a.Hkv + hkv) * D;
+  const uint32_t kv_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * kv_rs_b + D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + kv_base, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + kv_base, kv_bytes);
 
   // Q^T as B operands: lane (li, lh) holds q[row][16kk + 8lh .. +7].
   bf16x8 qreg[C::KS];
@@ -65,19 +73,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     qreg[kk] = as_bf16x8(u);
   }
 
-  // O^T accumulators: acc[db][r] = O[row][32db + 8(r>>2) + 4lh + (r&3)].
+  // O^T accumulators: acc[db][r] = O[row][32db + 8(r>>2) + 4lh + (r&3)], unnormalised,
+  // relative to m_used.  m_true is the exact running max.
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m_run = -INFINITY;   // running max, log2 units of the scaled logits
-  float l_part = 0.f;        // this lane's half of the running denominator
+  float m_used = -INFINITY, m_true = -INFINITY;   // log2 units of the scaled logits
+  float l_part = 0.f;                              // this lane's half of the denominator
   const size_t stat = ((size_t)b * a.Hq + hq) * a.Sq + row;
   float* accp = a.acc ? a.acc + ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D : nullptr;
   if (a.carry_in && row_ok) {
     const float mi = a.m[stat];
-    m_run = mi * kLog2e;
+    m_used = m_true = mi * kLog2e;
     l_part = lh == 0 ? a.l[stat] : 0.f;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -99,61 +108,45 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   KeyTileIter<C::BN> it;
   it.init(a.n_vblocks, a.kv_block, diag, jlo, jhi);
 
-  // This wave's rows and their visible key bounds.
   const bool wave_on = row0 < a.Sq;
   const int w_last = min(row0 + 31, a.Sq - 1);
-  const int w_jmin_lo = row0 - a.delta + a.lo_off;     // smallest key any wave row sees
-  const int w_jmin_hi = w_last - a.delta + a.lo_off;   // largest lower bound
-  const int w_jmax_lo = row0 - a.delta + a.hi_off;     // smallest upper bound
-  const int w_jmax_hi = w_last - a.delta + a.hi_off;   // largest key any wave row sees
+  const int w_jmin_lo = row0 - a.delta + a.lo_off;
+  const int w_jmin_hi = w_last - a.delta + a.lo_off;
+  const int w_jmax_lo = row0 - a.delta + a.hi_off;
+  const int w_jmax_hi = w_last - a.delta + a.hi_off;
   const int my_jmin = row - a.delta + a.lo_off;
   const int my_jmax = row - a.delta + a.hi_off;
 
-  // Staging registers for the next tile.
-  u32x4 kbuf[C::KCH];
-  u32x4 vbuf[C::KG];
-  const int v_dc = tid % C::DC, v_kg = tid / C::DC;
-
+  // Staging: thread t moves 16-byte chunks c = t + 256u (row c / DC, chunk c % DC).
+  u32x4 kbuf[C::LPT], vbuf[C::LPT];
+  uint32_t goff[C::LPT];
+  int loff[C::LPT];
+#pragma unroll
+  for (int u = 0; u < C::LPT; ++u) {
+    const int c = tid + 256 * u, r = c / C::DC, ch = c % C::DC;
+    goff[u] = (uint32_t)r * kv_rs_b + 16u * ch;
+    loff[u] = r * C::PITCH + 8 * ch;
+  }
   auto load_tile = [&](int ts) {
+    const uint32_t so = (uint32_t)ts * kv_rs_b;
 #pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / C::DC, col = (c % C::DC) * 8;
-      const int j = ts + r;
-      kbuf[u] = (j < a.Skv) ? *(const u32x4*)(kp + (size_t)j * kv_rs + col) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int r = 0; r < C::KG; ++r) {
-      const int j = ts + C::KG * v_kg + r;
-      vbuf[r] = (j < a.Skv) ? *(const u32x4*)(vp + (size_t)j * kv_rs + 8 * v_dc) : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < C::LPT; ++u) {
+      kbuf[u] = buf_load16(rk, goff[u], so);
+      vbuf[u] = buf_load16(rv, goff[u], so);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / C::DC, col = (c % C::DC) * 8;
-      *(u32x4*)&sK[buf][r * C::KROW + col] = kbuf[u];
-    }
-    const int slot = perm_slot(C::KG * v_kg);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {               // element e of the 8 d values
-      __bf16* dst = &sV[buf][(8 * v_dc + e) * C::VROW + slot];
-      const int w = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      if constexpr (C::KG == 4) {
-        u32x2 pr;
-        pr[0] = __builtin_amdgcn_perm(vbuf[1][w], vbuf[0][w], sel);
-        pr[1] = __builtin_amdgcn_perm(vbuf[3][w], vbuf[2][w], sel);
-        *(u32x2*)dst = pr;
-      } else if constexpr (C::KG == 2) {
-        *(uint32_t*)dst = __builtin_amdgcn_perm(vbuf[1][w], vbuf[0][w], sel);
-      } else {
-        const uint32_t x = (e & 1) ? (vbuf[0][w] >> 16) : (vbuf[0][w] & 0xffffu);
-        *(uint16_t*)dst = (uint16_t)x;
-      }
+    for (int u = 0; u < C::LPT; ++u) {
+      *(u32x4*)&sK[buf][loff[u]] = kbuf[u];
+      *(u32x4*)&sV[buf][loff[u]] = vbuf[u];
     }
   };
+  // Transposed V operand: lane (group g = lane/16, j = lane%16) points at
+  // V[16c + 4(g>>1) + j/4 (+8)][32db + 16(g&1) + 4(j%4) ..+3].
+  const int tg = lane >> 4, tj = lane & 15;
+  const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * C::PITCH + 16 * (tg & 1) + 4 * (tj & 3);
+  const int k_off = li * C::PITCH + 8 * lh;
 
   int ts = 0, kend = 0;
   bool have = it.next(ts, kend);
@@ -172,6 +165,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     const bool empty = !wave_on || ts > w_jmax_hi || tend - 1 < w_jmin_lo;
     if (!empty) {
       const bool full = ts >= w_jmin_hi && ts + C::BN - 1 <= w_jmax_lo && ts + C::BN <= tend;
+      const __bf16* kt = sK[cur];
+      const __bf16* vt = sV[cur];
       f32x16 s[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -179,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) {
-          const bf16x8 ka = *(const bf16x8*)&sK[cur][(32 * mb + li) * C::KROW + 16 * kk + 8 * lh];
+          const bf16x8 ka = *(const bf16x8*)&kt[k_off + 32 * mb * C::PITCH + 16 * kk];
           s[mb] = mfma32(ka, qreg[kk], s[mb]);
         }
       }
@@ -198,9 +193,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
       mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_ref);
+      const float mt = mx * a.scale_log2;          // this tile's row max (log2 units)
+      m_true = fmaxf(m_true, mt);
+      if (__ballot(mt > m_used + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_used, mt);
+        const float alpha = fast_exp2(m_used - (m_new == -INFINITY ? 0.f : m_new));
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        m_used = m_new;
+      }
+      const float m_ref = (m_used == -INFINITY) ? 0.f : m_used;
       float rs = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -210,12 +215,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
           s[mb][r] = p;
           rs += p;
         }
-      l_part = fmaf(l_part, alpha, rs);
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      l_part += rs;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -227,7 +227,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
           const int c = 2 * mb + ks;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
-            const bf16x8 va = *(const bf16x8*)&sV[cur][(32 * db + li) * C::VROW + 16 * c + 8 * lh];
+            const __bf16* vp0 = &vt[tr_off + 16 * c * C::PITCH + 32 * db];
+            const bf16x8 va = join_bf16x8(lds_read_tr16(vp0), lds_read_tr16(vp0 + 8 * C::PITCH));
             acc[db] = mfma32(va, pbf, acc[db]);
           }
         }
@@ -241,10 +242,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     have = nhave;
   }
 
-  const float l_tot = l_part + other_half(l_part);
+  // Normalise the statistics to the exact max: l_true = l_used * 2^(m_used - m_true).
+  const float l_used = l_part + other_half(l_part);
+  const float corr = (m_true == -INFINITY) ? 0.f : fast_exp2(m_used - m_true);
   if (row_ok) {
     if (a.finalize) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float inv = l_used > 0.f ? 1.f / l_used : 0.f;
       __bf16* op = (__bf16*)a.o + ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -262,13 +265,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
         for (int g = 0; g < 4; ++g) {
           f32x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e];
+          for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * corr;
           *(f32x4*)(accp + 32 * db + 8 * g + 4 * lh) = v4;
         }
     }
     if (lh == 0) {
-      a.m[stat] = (m_run == -INFINITY) ? -INFINITY : m_run * kLn2;
-      a.l[stat] = l_tot;
+      a.m[stat] = (m_true == -INFINITY) ? -INFINITY : m_true * kLn2;
+      a.l[stat] = l_used * corr;
     }
   }
 }
