@@ -13,7 +13,9 @@
 // Kernels: bwd_pre (D and the log2-domain LSE), bwd_dq (per 128-row query tile:
 // S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T) and bwd_dkdv (per 128-key tile:
 // S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS), all on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Tiles are fetched with raw buffer
+// loads (rows past the end read as zero) into row-major LDS tiles at a pitch of D + 32
+// elements; transposed operands come from the same tiles through ds_read_b64_tr_b16.
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
@@ -58,24 +60,27 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ dq (bf16)
+// One workgroup = 128 query rows of one (batch, q head), 32 per wavefront, walking the
+// key tiles in ring order.  Transposed form, so each lane owns one query row:
+//   S^T = K Q^T, dP^T = V dO^T (A operands: row-major K, V tiles; B: Q, dO in registers),
+//   P^T = exp2(S^T scale log2e - lse2_i), dS^T = P^T (dP^T - D_i) (lane-local stats),
+//   dQ^T += K^T dS^T with the transposed K operand read by ds_read_b64_tr_b16.
 template <int D>
 struct BwdQCfg {
   static constexpr int BM = 128;
   static constexpr int BN = 64;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int KROW = D + 8;
-  static constexpr int TROW = BN + 8;
-  static constexpr int KG = BN * D / 2048;
+  static constexpr int PITCH = D + 32;
   static constexpr int DC = D / 8;
+  static constexpr int LPT = BN * DC / 256;
 };
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   using C = BwdQCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::BN * C::KROW];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::BN * C::KROW];
-  __shared__ __attribute__((aligned(16))) __bf16 sKt[2][D * C::TROW];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::BN * C::PITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::BN * C::PITCH];
 
   int b, hq, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, a.xcd_groups, a.hi_off < kPosInf, b, hq, qt);
@@ -86,10 +91,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   const int row0 = wg_row0 + wave * 32;
   const int row = row0 + li;
   const bool row_ok = row < a.Sq;
-  const size_t q_rs = (size_t)a.Hq * D, kv_rs = (size_t)a.Hkv * D;
+  const size_t q_rs = (size_t)a.Hq * D;
+  const uint32_t kv_rs_b = (uint32_t)a.Hkv * D * 2;
   const size_t qoff = ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D;
-  const __bf16* kp = (const __bf16*)a.k + (size_t)b * a.Skv * kv_rs + (size_t)hkv * D;
-  const __bf16* vp = (const __bf16*)a.v + (size_t)b * a.Skv * kv_rs + (size_t)hkv * D;
+  const size_t kv_base = ((size_t)b * a.Skv * a.Hkv + hkv) * D;
+  const uint32_t kv_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * kv_rs_b + D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + kv_base, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + kv_base, kv_bytes);
 
   bf16x8 qreg[C::KS], doreg[C::KS];
 #pragma unroll
@@ -127,43 +135,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   const int w_jmax_lo = row0 - a.delta + a.hi_off, w_jmax_hi = w_last - a.delta + a.hi_off;
   const int my_jmin = row - a.delta + a.lo_off, my_jmax = row - a.delta + a.hi_off;
 
-  u32x4 kbuf[C::KG], vbuf[C::KG];
-  const int t_dc = tid % C::DC, t_kg = tid / C::DC;
-  auto load_tile = [&](int ts) {
+  u32x4 kbuf[C::LPT], vbuf[C::LPT];
+  uint32_t goff[C::LPT];
+  int loff[C::LPT];
 #pragma unroll
-    for (int r = 0; r < C::KG; ++r) {
-      const int j = ts + C::KG * t_kg + r;
-      const bool ok = j < a.Skv;
-      kbuf[r] = ok ? *(const u32x4*)(kp + (size_t)j * kv_rs + 8 * t_dc) : u32x4{0u, 0u, 0u, 0u};
-      vbuf[r] = ok ? *(const u32x4*)(vp + (size_t)j * kv_rs + 8 * t_dc) : u32x4{0u, 0u, 0u, 0u};
+  for (int u = 0; u < C::LPT; ++u) {
+    const int c = tid + 256 * u, r = c / C::DC, ch = c % C::DC;
+    goff[u] = (uint32_t)r * kv_rs_b + 16u * ch;
+    loff[u] = r * C::PITCH + 8 * ch;
+  }
+  auto load_tile = [&](int ts) {
+    const uint32_t so = (uint32_t)ts * kv_rs_b;
+#pragma unroll
+    for (int u = 0; u < C::LPT; ++u) {
+      kbuf[u] = buf_load16(rk, goff[u], so);
+      vbuf[u] = buf_load16(rv, goff[u], so);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < C::KG; ++r) {
-      const int j = C::KG * t_kg + r;
-      *(u32x4*)&sK[buf][j * C::KROW + 8 * t_dc] = kbuf[r];
-      *(u32x4*)&sV[buf][j * C::KROW + 8 * t_dc] = vbuf[r];
-    }
-    const int slot = perm_slot(C::KG * t_kg);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      __bf16* dst = &sKt[buf][(8 * t_dc + e) * C::TROW + slot];
-      const int w = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      if constexpr (C::KG == 4) {
-        u32x2 pr;
-        pr[0] = __builtin_amdgcn_perm(kbuf[1][w], kbuf[0][w], sel);
-        pr[1] = __builtin_amdgcn_perm(kbuf[3][w], kbuf[2][w], sel);
-        *(u32x2*)dst = pr;
-      } else if constexpr (C::KG == 2) {
-        *(uint32_t*)dst = __builtin_amdgcn_perm(kbuf[1][w], kbuf[0][w], sel);
-      } else {
-        const uint32_t x = (e & 1) ? (kbuf[0][w] >> 16) : (kbuf[0][w] & 0xffffu);
-        *(uint16_t*)dst = (uint16_t)x;
-      }
+    for (int u = 0; u < C::LPT; ++u) {
+      *(u32x4*)&sK[buf][loff[u]] = kbuf[u];
+      *(u32x4*)&sV[buf][loff[u]] = vbuf[u];
     }
   };
+  const int tg = lane >> 4, tj = lane & 15;
+  const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * C::PITCH + 16 * (tg & 1) + 4 * (tj & 3);
+  const int k_off = li * C::PITCH + 8 * lh;
 
   int ts = 0, kend = 0;
   bool have = it.next(ts, kend);
@@ -181,6 +179,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
     const bool empty = !wave_on || ts > w_jmax_hi || tend - 1 < w_jmin_lo;
     if (!empty) {
       const bool full = ts >= w_jmin_hi && ts + C::BN - 1 <= w_jmax_lo && ts + C::BN <= tend;
+      const __bf16* kt = sK[cur];
+      const __bf16* vt = sV[cur];
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -191,9 +191,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) {
-          const int off = (32 * mb + li) * C::KROW + 16 * kk + 8 * lh;
-          s[mb] = mfma32(*(const bf16x8*)&sK[cur][off], qreg[kk], s[mb]);
-          dp[mb] = mfma32(*(const bf16x8*)&sV[cur][off], doreg[kk], dp[mb]);
+          const int off = k_off + 32 * mb * C::PITCH + 16 * kk;
+          s[mb] = mfma32(*(const bf16x8*)&kt[off], qreg[kk], s[mb]);
+          dp[mb] = mfma32(*(const bf16x8*)&vt[off], doreg[kk], dp[mb]);
         }
       }
       if (!full) {
@@ -221,7 +221,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
         const bf16x8 pbf = as_bf16x8(pb);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 ka = *(const bf16x8*)&sKt[cur][(32 * db + li) * C::TROW + 16 * c + 8 * lh];
+          const __bf16* kp0 = &kt[tr_off + 16 * c * C::PITCH + 32 * db];
+          const bf16x8 ka = join_bf16x8(lds_read_tr16(kp0), lds_read_tr16(kp0 + 8 * C::PITCH));
           acc[db] = mfma32(ka, pbf, acc[db]);
         }
       }
@@ -249,14 +250,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ dk, dv (bf16)
+// One workgroup = 128 keys of one (batch, kv head), 32 per wavefront, with K and V in
+// registers.  It walks every q head of the GQA group and, for each, the 32-row query
+// steps that can see its keys (ring order over the virtual query blocks).  Per step:
+//   S = Q K^T, dP = dO V^T (A operands: row-major Q, dO tiles; B: K, V in registers),
+//   P = exp2(S scale log2e - lse2_i), dS = P (dP - D_i),
+//   dV^T += dO^T P, dK^T += Q^T dS with transposed dO / Q operands via ds_read_b64_tr_b16.
 template <int D>
 struct BwdKVCfg {
   static constexpr int BK = 128;                  // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 32;                   // query rows per step
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int QROW = D + 8;
-  static constexpr int TROW = BQ + 8;
+  static constexpr int PITCH = D + 32;
   static constexpr int DC = D / 8;
   static constexpr int NCH = BQ * DC;             // 16-byte chunks per tensor per step
   static constexpr int CPT = (NCH + 255) / 256;   // chunks per thread
@@ -265,10 +271,8 @@ struct BwdKVCfg {
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdKVCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][C::BQ * C::QROW];
-  __shared__ __attribute__((aligned(16))) __bf16 sG[2][C::BQ * C::QROW];
-  __shared__ __attribute__((aligned(16))) __bf16 sQt[2][D * C::TROW];
-  __shared__ __attribute__((aligned(16))) __bf16 sGt[2][D * C::TROW];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][C::BQ * C::PITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 sG[2][C::BQ * C::PITCH];
   __shared__ __attribute__((aligned(16))) float sLse[2][C::BQ];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BQ];
 
@@ -280,8 +284,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + li;
   const bool key_ok = key < a.Skv;
-  const size_t q_rs = (size_t)a.Hq * D, kv_rs = (size_t)a.Hkv * D;
+  const size_t kv_rs = (size_t)a.Hkv * D;
+  const uint32_t q_rs_b = (uint32_t)a.Hq * D * 2;
   const size_t koff = ((size_t)b * a.Skv + key) * kv_rs + (size_t)hkv * D;
+  const size_t q_base = (size_t)b * a.Sq * a.Hq * D;
+  const uint32_t q_bytes = a.Sq > 0 ? (uint32_t)a.Sq * q_rs_b : 0;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)a.q + q_base, q_bytes);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const __bf16*)a.dout + q_base, q_bytes);
 
   bf16x8 kreg[C::KS], vreg[C::KS];
 #pragma unroll
@@ -330,18 +339,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int w_klast = kw0 + 31;
 
   u32x4 qbuf[C::CPT], gbuf[C::CPT];
+  uint32_t goff[C::CPT];
+  int loff[C::CPT];
+#pragma unroll
+  for (int u = 0; u < C::CPT; ++u) {
+    const int c = min(tid + 256 * u, C::NCH - 1), i = c / C::DC, ch = c % C::DC;
+    goff[u] = (uint32_t)i * q_rs_b + 16u * ch;
+    loff[u] = i * C::PITCH + 8 * ch;
+  }
   float lbuf = 0.f;
   auto load_step = [&](int hq_, int qs) {
-    const __bf16* qp = (const __bf16*)a.q + (size_t)b * a.Sq * q_rs + (size_t)hq_ * D;
-    const __bf16* gp = (const __bf16*)a.dout + (size_t)b * a.Sq * q_rs + (size_t)hq_ * D;
+    const uint32_t so = (uint32_t)qs * q_rs_b + (uint32_t)hq_ * D * 2;
 #pragma unroll
     for (int u = 0; u < C::CPT; ++u) {
-      const int c = tid + 256 * u;
-      const int i = c / C::DC, col = (c % C::DC) * 8;
-      const int row = qs + i;
-      const bool ok = c < C::NCH && row < a.Sq;
-      qbuf[u] = ok ? *(const u32x4*)(qp + (size_t)row * q_rs + col) : u32x4{0u, 0u, 0u, 0u};
-      gbuf[u] = ok ? *(const u32x4*)(gp + (size_t)row * q_rs + col) : u32x4{0u, 0u, 0u, 0u};
+      qbuf[u] = buf_load16(rq, goff[u], so);
+      gbuf[u] = buf_load16(rg, goff[u], so);
     }
     if (tid < 2 * C::BQ) {
       const int i = tid & (C::BQ - 1), row = qs + i;
@@ -352,25 +364,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   auto store_step = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < C::CPT; ++u) {
-      const int c = tid + 256 * u;
-      if (c < C::NCH) {
-        const int i = c / C::DC, col = (c % C::DC) * 8;
-        *(u32x4*)&sQ[buf][i * C::QROW + col] = qbuf[u];
-        *(u32x4*)&sG[buf][i * C::QROW + col] = gbuf[u];
-        const int slot = perm_slot(i);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          const uint32_t qv = (e & 1) ? (qbuf[u][w] >> 16) : (qbuf[u][w] & 0xffffu);
-          const uint32_t gv = (e & 1) ? (gbuf[u][w] >> 16) : (gbuf[u][w] & 0xffffu);
-          *(uint16_t*)&sQt[buf][(col + e) * C::TROW + slot] = (uint16_t)qv;
-          *(uint16_t*)&sGt[buf][(col + e) * C::TROW + slot] = (uint16_t)gv;
-        }
+      if (tid + 256 * u < C::NCH) {
+        *(u32x4*)&sQ[buf][loff[u]] = qbuf[u];
+        *(u32x4*)&sG[buf][loff[u]] = gbuf[u];
       }
     }
     if (tid < C::BQ) sLse[buf][tid] = lbuf;
     else if (tid < 2 * C::BQ) sD[buf][tid - C::BQ] = lbuf;
   };
+  const int tg = lane >> 4, tj = lane & 15;
+  const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * C::PITCH + 16 * (tg & 1) + 4 * (tj & 3);
+  const int q_off = li * C::PITCH + 8 * lh;
 
   int hq = 0, qs = 0, rend = 0;
   bool have = next_step(hq, qs, rend);
@@ -392,6 +396,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     const bool empty = !wave_on || dmax < a.lo_off || dmin > a.hi_off || qs >= qe;
     if (!empty) {
       const bool full = dmin >= a.lo_off && dmax <= a.hi_off && qs + C::BQ <= qe;
+      const __bf16* qt_ = sQ[cur];
+      const __bf16* gt_ = sG[cur];
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -400,9 +406,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk) {
-        const int off = li * C::QROW + 16 * kk + 8 * lh;
-        s = mfma32(*(const bf16x8*)&sQ[cur][off], kreg[kk], s);
-        dp = mfma32(*(const bf16x8*)&sG[cur][off], vreg[kk], dp);
+        const int off = q_off + 16 * kk;
+        s = mfma32(*(const bf16x8*)&qt_[off], kreg[kk], s);
+        dp = mfma32(*(const bf16x8*)&gt_[off], vreg[kk], dp);
       }
       // lane (key li) holds query rows i = 8g + 4lh + e, r = 4g + e
 #pragma unroll
@@ -434,9 +440,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         const bf16x8 pbf = as_bf16x8(pb), sbf = as_bf16x8(sb);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const int off = (32 * db + li) * C::TROW + 16 * ks + 8 * lh;
-          dv[db] = mfma32(*(const bf16x8*)&sGt[cur][off], pbf, dv[db]);
-          dk[db] = mfma32(*(const bf16x8*)&sQt[cur][off], sbf, dk[db]);
+          const int off = tr_off + 16 * ks * C::PITCH + 32 * db;
+          const bf16x8 ga = join_bf16x8(lds_read_tr16(&gt_[off]), lds_read_tr16(&gt_[off + 8 * C::PITCH]));
+          const bf16x8 qa = join_bf16x8(lds_read_tr16(&qt_[off]), lds_read_tr16(&qt_[off + 8 * C::PITCH]));
+          dv[db] = mfma32(ga, pbf, dv[db]);
+          dk[db] = mfma32(qa, sbf, dk[db]);
         }
       }
     }
