@@ -25,6 +25,9 @@ COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep fp32 arithmetic off the packed (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: otherwise loop-carried accumulators are copied
+    # between VGPRs and AGPRs around every MFMA of the backward kernels
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-result", "-Wno-unused-variable",
 ]
