@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   int b, hq, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, a.xcd_groups, a.hi_off < kPosInf, b, hq, qt);
   const int hkv = hq / a.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int wg_row0 = qt * C::BM;
   const int row0 = wg_row0 + wave * 32;
@@ -183,26 +183,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
       const __bf16* vt = sV[cur];
       f32x16 s[2], dp[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           s[mb][r] = 0.f;
           dp[mb][r] = 0.f;
         }
 #pragma unroll
-        for (int kk = 0; kk < C::KS; ++kk) {
+      for (int kk = 0; kk < C::KS; ++kk)        // four independent accumulation chains
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
           const int off = k_off + 32 * mb * C::PITCH + 16 * kk;
           s[mb] = mfma32(*(const bf16x8*)&kt[off], qreg[kk], s[mb]);
           dp[mb] = mfma32(*(const bf16x8*)&vt[off], doreg[kk], dp[mb]);
         }
-      }
       if (!full) {
+        cold_path();
+        const int jlo_v = max(my_jmin, ts), jhi_v = min(my_jmax, tend - 1);
+        const uint32_t span = (uint32_t)(jhi_v - jlo_v);
+        const int base = ts + 4 * lh - jlo_v;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = ts + 32 * mb + 8 * (r >> 2) + 4 * lh + (r & 3);
-            if (j < my_jmin || j > my_jmax || j >= tend) s[mb][r] = -INFINITY;
+            const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
+            if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
           }
       }
 #pragma unroll
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 
   int b, hkv, kt;
   map_kv_task(blockIdx.x, a.n_ktiles, a.B, a.Hkv, a.xcd_kv_groups, false, b, hkv, kt);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int k0 = kt * C::BK;
   const int kw0 = k0 + wave * 32;
@@ -410,6 +415,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         s = mfma32(*(const bf16x8*)&qt_[off], kreg[kk], s);
         dp = mfma32(*(const bf16x8*)&gt_[off], vreg[kk], dp);
       }
+      if (!full) {
+        cold_path();
+        // row i = qs + 4lh + ioff is visible iff ilo_v <= i <= ihi_v (rows that see key)
+        const int ilo_v = max(key + a.delta - a.hi_off, qs);
+        const int ihi_v = min(key + a.delta - a.lo_off, qe - 1);
+        const uint32_t span = (uint32_t)(ihi_v - ilo_v);
+        const int base = qs + 4 * lh - ilo_v;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ioff = 8 * (r >> 2) + (r & 3);
+          if (ihi_v < ilo_v || (uint32_t)(base + ioff) > span) s[r] = -INFINITY;
+        }
+      }
       // lane (key li) holds query rows i = 8g + 4lh + e, r = 4g + e
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -418,13 +436,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float x = s[r];
-          if (!full) {
-            const int i = qs + 8 * g + 4 * lh + e;
-            const int dd = key - i + a.delta;
-            if (dd < a.lo_off || dd > a.hi_off || i >= qe) x = -INFINITY;
-          }
-          const float p = fast_exp2(fmaf(x, a.scale_log2, -lse4[e]));
+          const float p = fast_exp2(fmaf(s[r], a.scale_log2, -lse4[e]));
           s[r] = p;
           dp[r] = p * (dp[r] - d4[e]);
         }

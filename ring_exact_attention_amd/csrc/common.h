@@ -107,13 +107,20 @@ __device__ __forceinline__ float other_half(float x) {
   return __uint_as_float(lo ? r[1] : r[0]);
 }
 
-// Two floats -> two bf16 (round to nearest even) packed in one dword.
+// Two floats -> two bf16 (round to nearest even) packed in one dword; a single
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __hip_bfloat162 p = __float22bfloat162_rn(make_float2(a, b));
-  uint32_t u;
-  __builtin_memcpy(&u, &p, 4);
-  return u;
+  const bf16x2v p = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
 }
+
+// Marks a rarely taken branch: an opaque statement cannot be speculated, so the
+// compiler keeps the branch instead of computing its body unconditionally.
+__device__ __forceinline__ void cold_path() { asm volatile(""); }
+
+// Index of this thread's wavefront in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }

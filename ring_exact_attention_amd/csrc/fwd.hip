@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   int b, hq, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, a.xcd_groups, a.hi_off < kPosInf, b, hq, qt);
   const int hkv = hq / a.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int wg_row0 = qt * C::BM;
   const int row0 = wg_row0 + wave * 32;
@@ -169,22 +169,28 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       const __bf16* vt = sV[cur];
       f32x16 s[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < C::KS; ++kk) {
+      for (int kk = 0; kk < C::KS; ++kk)        // two independent accumulation chains
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
           const bf16x8 ka = *(const bf16x8*)&kt[k_off + 32 * mb * C::PITCH + 16 * kk];
           s[mb] = mfma32(ka, qreg[kk], s[mb]);
         }
-      }
       if (!full) {
+        cold_path();
+        // key j = ts + 4lh + koff is visible iff jlo_v <= j <= jhi_v: one unsigned compare
+        const int jlo_v = max(my_jmin, ts), jhi_v = min(my_jmax, tend - 1);
+        const uint32_t span = (uint32_t)(jhi_v - jlo_v);
+        const int base = ts + 4 * lh - jlo_v;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = ts + 32 * mb + 8 * (r >> 2) + 4 * lh + (r & 3);
-            if (j < my_jmin || j > my_jmax || j >= tend) s[mb][r] = -INFINITY;
+            const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
+            if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -196,6 +202,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       const float mt = mx * a.scale_log2;          // this tile's row max (log2 units)
       m_true = fmaxf(m_true, mt);
       if (__ballot(mt > m_used + kRescaleThreshold)) {
+        cold_path();
         const float m_new = fmaxf(m_used, mt);
         const float alpha = fast_exp2(m_used - (m_new == -INFINITY ? 0.f : m_new));
         l_part *= alpha;
