@@ -271,13 +271,16 @@ struct BwdKVCfg {
   static constexpr int DC = D / 8;
   static constexpr int NCH = BQ * DC;             // 16-byte chunks per tensor per step
   static constexpr int CPT = (NCH + 255) / 256;   // chunks per thread
+  static constexpr int VPITCH = D + 8;            // V tile pitch: row reads only (272 B at D = 128)
+  static constexpr int VCPT = BK * DC / 256;      // 16-byte chunks of the V tile per thread
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdKVCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 sQ[2][C::BQ * C::PITCH];
   __shared__ __attribute__((aligned(16))) __bf16 sG[2][C::BQ * C::PITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 sVk[C::BK * C::VPITCH];   // this workgroup's V rows
   __shared__ __attribute__((aligned(16))) float sLse[2][C::BQ];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BQ];
 
@@ -297,16 +300,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)a.q + q_base, q_bytes);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc((const __bf16*)a.dout + q_base, q_bytes);
 
-  bf16x8 kreg[C::KS], vreg[C::KS];
+  // K stays in registers (B operand of S = Q K^T); V goes to LDS once (B operand of
+  // dP = dO V^T, re-read every step) to keep the register count within two waves per SIMD.
+  bf16x8 kreg[C::KS];
 #pragma unroll
   for (int kk = 0; kk < C::KS; ++kk) {
-    u32x4 u = {0u, 0u, 0u, 0u}, w = {0u, 0u, 0u, 0u};
-    if (key_ok) {
-      u = *(const u32x4*)((const __bf16*)a.k + koff + 16 * kk + 8 * lh);
-      w = *(const u32x4*)((const __bf16*)a.v + koff + 16 * kk + 8 * lh);
-    }
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (key_ok) u = *(const u32x4*)((const __bf16*)a.k + koff + 16 * kk + 8 * lh);
     kreg[kk] = as_bf16x8(u);
-    vreg[kk] = as_bf16x8(w);
+  }
+  {
+    const uint32_t kv_rs_b = (uint32_t)kv_rs * 2;
+    const size_t v_base = ((size_t)b * a.Skv + k0) * kv_rs + (size_t)hkv * D;
+    const int rows = min(C::BK, a.Skv - k0);
+    const __amdgpu_buffer_rsrc_t rvk =
+        make_rsrc((const __bf16*)a.v + v_base, (uint32_t)(rows - 1) * kv_rs_b + D * 2);
+#pragma unroll
+    for (int u = 0; u < C::VCPT; ++u) {
+      const int c = tid + 256 * u, r = c / C::DC, ch = c % C::DC;
+      *(u32x4*)&sVk[r * C::VPITCH + 8 * ch] = buf_load16(rvk, (uint32_t)r * kv_rs_b + 16u * ch, 0);
+    }
   }
   f32x16 dk[C::DB], dv[C::DB];
 #pragma unroll
@@ -380,6 +393,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int tg = lane >> 4, tj = lane & 15;
   const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * C::PITCH + 16 * (tg & 1) + 4 * (tj & 3);
   const int q_off = li * C::PITCH + 8 * lh;
+  const int v_off = (wave * 32 + li) * C::VPITCH + 8 * lh;
 
   int hq = 0, qs = 0, rend = 0;
   bool have = next_step(hq, qs, rend);
@@ -412,8 +426,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk) {
         const int off = q_off + 16 * kk;
+        const bf16x8 vb = *(const bf16x8*)&sVk[v_off + 16 * kk];
         s = mfma32(*(const bf16x8*)&qt_[off], kreg[kk], s);
-        dp = mfma32(*(const bf16x8*)&gt_[off], vreg[kk], dp);
+        dp = mfma32(*(const bf16x8*)&gt_[off], vb, dp);
       }
       if (!full) {
         cold_path();
