@@ -5,152 +5,274 @@
 // (block index -1 reads token 0 for every row, as the page clamps negative item
 // indices).  One softmax over all slots, no mask; logits are q . k / sqrt(E).
 //
-// gfx950 mapping: one wavefront per token, each lane owning 8 of the E = 512
-// embedding values (16 bytes of every row, so a row load is one coalesced 1 KB
-// access per wave).  Rows are taken 32 at a time: each lane keeps 32 partial dots and
-// a butterfly reduce-scatter over the 64 lanes (halving the values at every exchange)
-// leaves row r's full dot in lanes 2r and 2r+1 after 32 exchanges.  Logits go to LDS;
-// the max / exp / sum run over LDS; a second pass accumulates p * v in fp32.
 #include "common.h"
 #include "launch.h"
 
 namespace rea {
 
 constexpr int kSpE = 512;            // joint embedding (8 bf16 per lane)
-constexpr int kSpMaxSlots = 64 + 16 * 64;
-constexpr int kSpWaves = 4;
+// ---------------------------------------------------------------------------------
+// Block-shared form (E = 512, bs in {16, 32, 64}): one workgroup per 32 consecutive
+// tokens.  The tokens' selected block indices are sorted and deduplicated in LDS; each
+// distinct block u gets a per-token multiplicity cnt(u, t) (a token lists a block at
+// most once in a valid selection; -1 entries are one block whose rows are all token 0,
+// counted once per entry).  The window is covered by up to three 32-row blocks with a
+// per-token mask.  Every 32-row block is then attended with MFMA like a dense tile:
+//   S^T = K Q^T (split over the embedding: wave w owns e in [128w, 128w + 128), the
+//   four partial score tiles are summed through LDS), weights w(t, row) = multiplicity
+//   or window mask, online softmax with weights (p = w * exp(s - m)), and
+//   O^T += V^T P^T on the wave's embedding slice (V staged row-major in LDS, read
+//   transposed with ds_read_b64_tr_b16).
+// A block shared by several tokens is read once for all of them.
+constexpr int kUQ = 32;              // tokens per workgroup
+constexpr int kUDW = 128;            // embedding slice per wavefront
+constexpr int kUPITCH = kUDW + 32;   // V slice row pitch (elements): conflict-free tr reads
+constexpr int kUMaxEnt = 512;        // 32 tokens x top_n (<= 16)
+constexpr int kUSentinel = 0x7fffffff;
 
-__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m); }
+__global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
+  // LDS: partial scores 16 KiB | V slices 40 KiB (setup scratch reuses it) | counts 16 KiB
+  __shared__ __attribute__((aligned(16))) float sS[4][64 * 16];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[4][32 * kUPITCH];
+  __shared__ uint32_t ucnt[kUMaxEnt][kUQ / 4];
+  __shared__ int ublk[kUMaxEnt];
+  __shared__ int s_nu;
 
-__global__ __launch_bounds__(256) void sparse_fwd_kernel(SparseArgs a) {
-  __shared__ int spos[kSpWaves][kSpMaxSlots];
-  __shared__ float sdot[kSpWaves][kSpMaxSlots];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int li = lane & 31, lh = lane >> 5;
+  const int nqb = (a.S + kUQ - 1) / kUQ;
+  const int b = blockIdx.x / nqb, t0 = (blockIdx.x % nqb) * kUQ;
+  const int n = a.top_n, bs = a.sel_block, W = a.window;
+  const int ne = kUQ * n;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long long tok_raw = (long long)blockIdx.x * kSpWaves + wave;   // b * S + t
-  const bool valid = tok_raw < (long long)a.B * a.S;                   // tail waves compute token 0
-  const long long tok = valid ? tok_raw : 0;                          // and store nothing
-  const int b = (int)(tok / a.S), t = (int)(tok % a.S);
-  const int W = a.window, bs = a.sel_block, n = a.top_n;
-  const int nslots = W + n * bs;
+  // ---- setup: sort (block, token) pairs, deduplicate, count per token
+  int* skey = (int*)&sV[0][0];
+  int* stok = skey + kUMaxEnt;
+  for (int k = tid; k < kUMaxEnt; k += 256) {
+    int key = kUSentinel, tok = 0;
+    if (k < ne) {
+      const int t = k / n, j = k % n;
+      if (t0 + t < a.S) {
+        const int c = a.sel[((size_t)b * a.S + t0 + t) * n + j];
+        key = c < 0 ? -1 : c;
+        tok = t;
+      }
+    }
+    skey[k] = key;
+    stok[k] = tok;
+  }
+  __syncthreads();
+  for (int size = 2; size <= kUMaxEnt; size <<= 1) {          // bitonic sort by key
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int k = tid; k < kUMaxEnt / 2; k += 256) {
+        const int lo = 2 * k - (k & (stride - 1)), hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const int ka = skey[lo], kb = skey[hi];
+        if ((ka > kb) == up) {
+          skey[lo] = kb;
+          skey[hi] = ka;
+          const int ta = stok[lo];
+          stok[lo] = stok[hi];
+          stok[hi] = ta;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (wave == 0) {                                             // union index of each entry
+    int* suid = stok + kUMaxEnt;
+    int running = 0;
+    for (int c0 = 0; c0 < kUMaxEnt; c0 += 64) {
+      const int k = c0 + lane;
+      const int key = skey[k];
+      const bool first = key != kUSentinel && (k == 0 || skey[k - 1] != key);
+      const uint64_t mask = __ballot(first);
+      const int before = __popcll(mask & ((1ull << lane) - 1));
+      suid[k] = running + before + (first ? 0 : -1);
+      if (first) ublk[running + before] = key;
+      running += __popcll(mask);
+    }
+    if (lane == 0) s_nu = running;
+  }
+  for (int k = tid; k < kUMaxEnt * (kUQ / 4); k += 256) ((uint32_t*)ucnt)[k] = 0u;
+  __syncthreads();
+  {
+    const int* suid = stok + kUMaxEnt;
+    for (int k = tid; k < kUMaxEnt; k += 256)
+      if (skey[k] != kUSentinel) atomicAdd(&ucnt[suid[k]][stok[k] >> 2], 1u << (8 * (stok[k] & 3)));
+  }
+  __syncthreads();
+  const int nu = s_nu;
 
-  // slot positions (-1 = zero padding)
-  const int32_t* sel = a.sel + tok * n;
-  for (int s = lane; s < nslots; s += 64) {
-    int p;
-    if (s < W) {
-      p = t - W + 1 + s;
-      if (p < 0) p = -1;
+  // ---- main loop over 32-row blocks: window blocks, then union blocks
+  const int nwin = (W + kUQ - 1 + 31) / 32;
+  const int nsub = (bs + 31) / 32;
+  const int nsteps = nwin + nu * nsub;
+  const int wstart = t0 - W + 1;
+  const uint32_t row_b = (uint32_t)kSpE * 2;
+  const size_t bbase = (size_t)b * a.S * kSpE;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + bbase, (uint32_t)a.S * row_b);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + bbase, (uint32_t)a.S * row_b);
+  const int e0 = kUDW * wave;                                  // this wave's embedding slice
+  const int tok = t0 + li;                                     // this lane's token (B / C column)
+
+  bf16x8 qreg[kUDW / 16];
+#pragma unroll
+  for (int kk = 0; kk < kUDW / 16; ++kk) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (tok < a.S) u = *(const u32x4*)((const __bf16*)a.q + bbase + (size_t)tok * kSpE + e0 + 16 * kk + 8 * lh);
+    qreg[kk] = as_bf16x8(u);
+  }
+
+  auto row_pos = [&](int step, int r, bool& valid) -> int {   // position of row r of a step
+    valid = true;
+    if (step < nwin) return wstart + 32 * step + r;
+    const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;
+    const int c = ublk[u];
+    valid = 32 * h + r < bs;
+    return c < 0 ? 0 : c * bs + 32 * h + r;
+  };
+  u32x4 kbuf[kUDW / 16], vbuf[8];
+  auto load_step = [&](int step) {
+    bool ok;
+    const int pk = row_pos(step, li, ok);                      // K operand row of this lane
+#pragma unroll
+    for (int kk = 0; kk < kUDW / 16; ++kk)
+      kbuf[kk] = buf_load16(rk, (uint32_t)pk * row_b + 2u * (e0 + 16 * kk + 8 * lh), 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {                              // V slice: row (lane + 64u) / 16
+      const int qc = lane + 64 * u, r = qc >> 4, ch = qc & 15;
+      const int pv = row_pos(step, r, ok);
+      vbuf[u] = buf_load16(rv, (uint32_t)pv * row_b + 2u * (e0 + 8 * ch), 0);
+    }
+  };
+
+  f32x16 acc[kUDW / 32];
+#pragma unroll
+  for (int db = 0; db < kUDW / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m_used = -INFINITY, m_true = -INFINITY, l_part = 0.f;
+  const int tg = lane >> 4, tj = lane & 15;
+  const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * kUPITCH + 16 * (tg & 1) + 4 * (tj & 3);
+
+  if (nsteps > 0) load_step(0);
+  for (int step = 0; step < nsteps; ++step) {
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kUDW / 16; ++kk) s = mfma32(as_bf16x8(kbuf[kk]), qreg[kk], s);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 v4 = {s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
+      *(f32x4*)&sS[wave][lane * 16 + 4 * g] = v4;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int qc = lane + 64 * u, r = qc >> 4, ch = qc & 15;
+      *(u32x4*)&sV[wave][r * kUPITCH + 8 * ch] = vbuf[u];
+    }
+    __syncthreads();
+    if (step + 1 < nsteps) load_step(step + 1);              // registers are free again
+
+    // full scores (sum of the four embedding slices), identical in every wave
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v4 = *(const f32x4*)&sS[w2][lane * 16 + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * g + e] += v4[e];
+      }
+    // weights of (token li, row 8(r>>2) + 4lh + (r&3))
+    float wt[16];
+    if (step < nwin) {
+      const int p0 = wstart + 32 * step + 4 * lh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = p0 + 8 * (r >> 2) + (r & 3);
+        wt[r] = (tok < a.S && p >= tok - W + 1 && p <= tok) ? 1.f : 0.f;
+      }
     } else {
-      const int j = (s - W) / bs, r = (s - W) % bs;
-      const int c = sel[j];
-      p = c < 0 ? 0 : c * bs + r;
-      if (p >= a.S) p = a.S - 1;        // indices are < S/bs by contract; keep reads in bounds
-    }
-    spos[wave][s] = p;
-  }
-  __syncthreads();
-
-  const __bf16* kb = (const __bf16*)a.k + (size_t)b * a.S * kSpE + 8 * lane;
-  const __bf16* vb = (const __bf16*)a.v + (size_t)b * a.S * kSpE + 8 * lane;
-  const u32x4 qu = *(const u32x4*)((const __bf16*)a.q + (size_t)tok * kSpE + 8 * lane);
-  float qf[8];
+      const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;
+      const float cnt = (float)((ucnt[u][li >> 2] >> (8 * (li & 3))) & 0xffu);
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    qf[2 * w] = bf16_lo(qu[w]);
-    qf[2 * w + 1] = bf16_hi(qu[w]);
-  }
-
-  // pass 1: dots of q with every slot row, 32 rows at a time
-  for (int g = 0; g < nslots; g += 32) {
-    float part[32];
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      const int s = g + r;
-      const int p = s < nslots ? spos[wave][s] : -1;
-      float acc = 0.f;
-      if (p >= 0) {
-        const u32x4 ku = *(const u32x4*)(kb + (size_t)p * kSpE);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          acc = fmaf(qf[2 * w], bf16_lo(ku[w]), acc);
-          acc = fmaf(qf[2 * w + 1], bf16_hi(ku[w]), acc);
-        }
-      }
-      part[r] = acc;
-    }
-    // butterfly reduce-scatter: after the exchange at distance m (32, 16, 8, 4, 2)
-    // each lane keeps the half of its values selected by its lane bit, summed with
-    // the partner's; lane L ends with row L >> 1, then one more exchange at distance 1.
-#pragma unroll
-    for (int half = 16, m = 32; half >= 1; half >>= 1, m >>= 1) {
-      const bool upper = (lane & m) != 0;
-#pragma unroll
-      for (int r = 0; r < half; ++r) {
-        const float keep = upper ? part[r + half] : part[r];
-        const float send = upper ? part[r] : part[r + half];
-        part[r] = keep + shfl_xor_f(send, m);
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * h + 8 * (r >> 2) + 4 * lh + (r & 3);
+        wt[r] = row < bs ? cnt : 0.f;
       }
     }
-    const float dot = part[0] + shfl_xor_f(part[0], 1);
-    const int s = g + (lane >> 1);
-    if ((lane & 1) == 0 && s < nslots) sdot[wave][s] = dot;
-  }
-  __syncthreads();
-
-  // softmax statistics over all slots
-  float mx = -INFINITY;
-  for (int s = lane; s < nslots; s += 64) mx = fmaxf(mx, sdot[wave][s]);
+    float mx = -INFINITY;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
-  float sum = 0.f;
-  for (int s = lane; s < nslots; s += 64) {
-    const float p = fast_exp2((sdot[wave][s] - mx) * a.scale_log2);
-    sdot[wave][s] = p;
-    sum += p;
-  }
+    for (int r = 0; r < 16; ++r) {
+      s[r] = wt[r] > 0.f ? s[r] : -INFINITY;
+      mx = fmaxf(mx, s[r]);
+    }
+    mx = fmaxf(mx, other_half(mx));
+    const float mt = mx * a.scale_log2;
+    m_true = fmaxf(m_true, mt);
+    if (__ballot(mt > m_used + 8.0f)) {
+      cold_path();
+      const float m_new = fmaxf(m_used, mt);
+      const float alpha = fast_exp2(m_used - (m_new == -INFINITY ? 0.f : m_new));
+      l_part *= alpha;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) sum += shfl_xor_f(sum, m);
-  __syncthreads();
-
-  // pass 2: o = sum_s p_s v_s / sum
-  float o[8];
+      for (int db = 0; db < kUDW / 32; ++db)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = 0.f;
-  for (int g = 0; g < nslots; g += 8) {
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m_used = m_new;
+    }
+    const float m_ref = (m_used == -INFINITY) ? 0.f : m_used;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int s = g + r;
-      if (s < nslots) {
-        const int p = spos[wave][s];
-        if (p >= 0) {
-          const float ps = sdot[wave][s];
-          const u32x4 vu = *(const u32x4*)(vb + (size_t)p * kSpE);
+    for (int r = 0; r < 16; ++r) {
+      const float p = wt[r] * fast_exp2(fmaf(s[r], a.scale_log2, -m_ref));
+      s[r] = p;
+      l_part += p;
+    }
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            o[2 * w] = fmaf(ps, bf16_lo(vu[w]), o[2 * w]);
-            o[2 * w + 1] = fmaf(ps, bf16_hi(vu[w]), o[2 * w + 1]);
-          }
-        }
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 pb;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(s[8 * ks + 2 * w], s[8 * ks + 2 * w + 1]);
+      const bf16x8 pbf = as_bf16x8(pb);
+#pragma unroll
+      for (int db = 0; db < kUDW / 32; ++db) {
+        const __bf16* vp0 = &sV[wave][tr_off + 16 * ks * kUPITCH + 32 * db];
+        const bf16x8 va = join_bf16x8(lds_read_tr16(vp0), lds_read_tr16(vp0 + 8 * kUPITCH));
+        acc[db] = mfma32(va, pbf, acc[db]);
       }
     }
+    __syncthreads();                                           // sS / sV are rewritten next step
   }
-  const float inv = 1.f / sum;
-  u32x4 ou;
+
+  const float l_used = l_part + other_half(l_part);
+  const float corr = (m_true == -INFINITY) ? 0.f : fast_exp2(m_used - m_true);
+  if (tok < a.S) {
+    const float inv = l_used > 0.f ? 1.f / l_used : 0.f;
+    __bf16* op = (__bf16*)a.o + bbase + (size_t)tok * kSpE + e0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) ou[w] = pack_bf16x2(o[2 * w] * inv, o[2 * w + 1] * inv);
-  if (!valid) return;
-  *(u32x4*)((__bf16*)a.o + (size_t)tok * kSpE + 8 * lane) = ou;
-  if (lane == 0) {
-    a.m[tok] = mx * a.scale;
-    a.l[tok] = sum;
+    for (int db = 0; db < kUDW / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+        *(u32x2*)(op + 32 * db + 8 * g + 4 * lh) = w;
+      }
+    if (wave == 0 && lh == 0) {
+      const size_t st = (size_t)b * a.S + tok;
+      a.m[st] = (m_true == -INFINITY) ? -INFINITY : m_true * kLn2;
+      a.l[st] = l_used * corr;
+    }
   }
 }
 
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
-  const long long ntok = (long long)a.B * a.S;
-  const unsigned blocks = (unsigned)((ntok + kSpWaves - 1) / kSpWaves);
-  hipLaunchKernelGGL(sparse_fwd_kernel, dim3(blocks), dim3(64 * kSpWaves), 0, stream, a);
+  const long long nqb = (a.S + kUQ - 1) / kUQ;
+  hipLaunchKernelGGL(sparse_union_kernel, dim3((unsigned)(a.B * nqb)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
