@@ -27,6 +27,9 @@
  *     returns ATTN_ERR_INVALID_ARG / ATTN_ERR_UNSUPPORTED / ATTN_ERR_WORKSPACE and
  *     launches nothing; a failed launch returns ATTN_ERR_HIP.  attn_last_error() then
  *     describes the problem.  A batch of 0 (or Sq = 0) is a successful no-op.
+ *   * One batch element's slice of any tensor (S x H x D elements) must stay under
+ *     4 GiB: the kernels address each slice with 32-bit byte offsets.  Larger slices
+ *     return ATTN_ERR_UNSUPPORTED.
  */
 #ifndef RING_EXACT_ATTENTION_ATTN_H_
 #define RING_EXACT_ATTENTION_ATTN_H_

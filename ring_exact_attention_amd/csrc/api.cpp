@@ -27,6 +27,7 @@ int ok() {
 
 constexpr long long kMaxLen = 1LL << 28;    // rows per call
 constexpr long long kMaxPos = 1LL << 27;    // |global position of row 0|
+constexpr long long kMaxSlice = (1LL << 32) - 256;   // bytes of one batch element of a tensor
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -118,6 +119,9 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   r.n_vblocks = r.Skv / r.kv_block;
   r.q_vblock = (r.Sq > 0 && r.Sq % r.kv_block == 0) ? r.kv_block : (r.Sq > 0 ? r.Sq : 1);
   r.n_qvblocks = r.Sq / r.q_vblock;
+  const long long esize = r.dtype == ATTN_BF16 ? 2 : 4;
+  if ((long long)r.Sq * r.Hq * D * esize > kMaxSlice || (long long)r.Skv * r.Hkv * D * esize > kMaxSlice)
+    return fail(ATTN_ERR_UNSUPPORTED, fmt("one batch element of q or k/v exceeds %lld bytes", kMaxSlice));
   r.carry_in = (p->flags & ATTN_CARRY_IN) != 0;
   r.finalize = (p->flags & ATTN_NO_FINALIZE) == 0;
   return ATTN_OK;
@@ -148,7 +152,8 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
   if (p->head_dim != 512) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode supports head_dim (embed) 512");
   if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_kv != p->seqlen_q)
     return fail(ATTN_ERR_INVALID_ARG, "sparse mode needs seqlen_q == seqlen_kv >= 0");
-  if (p->seqlen_q > kMaxLen) return fail(ATTN_ERR_UNSUPPORTED, "sequence too long");
+  if (p->seqlen_q > kMaxLen || (long long)p->seqlen_q * 512 * 2 > kMaxSlice)
+    return fail(ATTN_ERR_UNSUPPORTED, "sequence too long");
   if (p->top_n < 1 || p->top_n > 16) return fail(ATTN_ERR_INVALID_ARG, "top_n must be in 1..16");
   if (p->sel_block != 16 && p->sel_block != 32 && p->sel_block != 64)
     return fail(ATTN_ERR_UNSUPPORTED, "sel_block must be 16, 32 or 64");

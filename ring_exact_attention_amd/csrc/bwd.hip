@@ -71,16 +71,17 @@ struct BwdQCfg {
   static constexpr int BN = 64;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int PITCH = D + 32;
+  using KL = TileLayout<D, kBothRead>;             // K tile: row operands and transposed
+  using VL = TileLayout<D, kRowRead>;              // V tile: row operands
   static constexpr int DC = D / 8;
   static constexpr int LPT = BN * DC / 256;
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   using C = BwdQCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::BN * C::PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::BN * C::PITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::KL::elems(C::BN)];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::VL::elems(C::BN)];
 
   int b, hq, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, a.xcd_groups, a.hi_off < kPosInf, b, hq, qt);
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   const size_t qoff = ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D;
   const size_t kv_base = ((size_t)b * a.Skv * a.Hkv + hkv) * D;
   const uint32_t kv_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * kv_rs_b + D * 2 : 0;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + kv_base, kv_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + kv_base, kv_bytes);
+  const __bf16* kbase = (const __bf16*)a.k + kv_base;
+  const __bf16* vbase = (const __bf16*)a.v + kv_base;
 
   bf16x8 qreg[C::KS], doreg[C::KS];
 #pragma unroll
@@ -137,31 +138,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
 
   u32x4 kbuf[C::LPT], vbuf[C::LPT];
   uint32_t goff[C::LPT];
-  int loff[C::LPT];
+  constexpr int RPU = 256 / C::DC;                  // rows per staging round (multiple of 4)
 #pragma unroll
-  for (int u = 0; u < C::LPT; ++u) {
-    const int c = tid + 256 * u, r = c / C::DC, ch = c % C::DC;
-    goff[u] = (uint32_t)r * kv_rs_b + 16u * ch;
-    loff[u] = r * C::PITCH + 8 * ch;
-  }
+  for (int u = 0; u < C::LPT; ++u) goff[u] = (uint32_t)(tid / C::DC + RPU * u) * kv_rs_b + 16u * (tid % C::DC);
+  const int kl0 = C::KL::idx(tid / C::DC, 8 * (tid % C::DC));
+  const int vl0 = C::VL::idx(tid / C::DC, 8 * (tid % C::DC));
   auto load_tile = [&](int ts) {
-    const uint32_t so = (uint32_t)ts * kv_rs_b;
+    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)ts * kv_rs_b);   // uniform
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc_at(kbase, kv_bytes, so);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc_at(vbase, kv_bytes, so);
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
-      kbuf[u] = buf_load16(rk, goff[u], so);
-      vbuf[u] = buf_load16(rv, goff[u], so);
+      kbuf[u] = buf_load16(rk, goff[u], 0);
+      vbuf[u] = buf_load16(rv, goff[u], 0);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
-      *(u32x4*)&sK[buf][loff[u]] = kbuf[u];
-      *(u32x4*)&sV[buf][loff[u]] = vbuf[u];
+      *(u32x4*)&sK[buf][kl0 + C::KL::rows(RPU * u)] = kbuf[u];
+      *(u32x4*)&sV[buf][vl0 + C::VL::rows(RPU * u)] = vbuf[u];
     }
   };
+  // Operand offsets: per-lane base + constants.  Transposed reads: lane (g = lane/16,
+  // j = lane%16) points at K[16c + 4(g>>1) + j/4 (+8)][32db + 16(g&1) + 4(j%4) ..+3].
   const int tg = lane >> 4, tj = lane & 15;
-  const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * C::PITCH + 16 * (tg & 1) + 4 * (tj & 3);
-  const int k_off = li * C::PITCH + 8 * lh;
+  const int tr_off = C::KL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
+  const int k_off = C::KL::idx(li, 8 * lh);
+  const int v_off = C::VL::idx(li, 8 * lh);
 
   int ts = 0, kend = 0;
   bool have = it.next(ts, kend);
@@ -193,9 +197,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
       for (int kk = 0; kk < C::KS; ++kk)        // four independent accumulation chains
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const int off = k_off + 32 * mb * C::PITCH + 16 * kk;
-          s[mb] = mfma32(*(const bf16x8*)&kt[off], qreg[kk], s[mb]);
-          dp[mb] = mfma32(*(const bf16x8*)&vt[off], doreg[kk], dp[mb]);
+          s[mb] = mfma32(*(const bf16x8*)&kt[k_off + C::KL::rows(32 * mb) + 16 * kk], qreg[kk], s[mb]);
+          dp[mb] = mfma32(*(const bf16x8*)&vt[v_off + C::VL::rows(32 * mb) + 16 * kk], doreg[kk], dp[mb]);
         }
       if (!full) {
         cold_path();
@@ -226,8 +229,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
         const bf16x8 pbf = as_bf16x8(pb);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const __bf16* kp0 = &kt[tr_off + 16 * c * C::PITCH + 32 * db];
-          const bf16x8 ka = join_bf16x8(lds_read_tr16(kp0), lds_read_tr16(kp0 + 8 * C::PITCH));
+          const __bf16* kp0 = &kt[tr_off + C::KL::rows(16 * c) + 32 * db];
+          const bf16x8 ka = join_bf16x8(lds_read_tr16(kp0), lds_read_tr16(kp0 + C::KL::rows(8)));
           acc[db] = mfma32(ka, pbf, acc[db]);
         }
       }
@@ -267,20 +270,20 @@ struct BwdKVCfg {
   static constexpr int BQ = 32;                   // query rows per step
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int PITCH = D + 32;
+  using QL = TileLayout<D, kBothRead>;            // Q, dO tiles: row operands and transposed
+  using VL = TileLayout<D, kRowRead>;             // V tile: row operands
   static constexpr int DC = D / 8;
   static constexpr int NCH = BQ * DC;             // 16-byte chunks per tensor per step
   static constexpr int CPT = (NCH + 255) / 256;   // chunks per thread
-  static constexpr int VPITCH = D + 8;            // V tile pitch: row reads only (272 B at D = 128)
   static constexpr int VCPT = BK * DC / 256;      // 16-byte chunks of the V tile per thread
 };
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdKVCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][C::BQ * C::PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 sG[2][C::BQ * C::PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 sVk[C::BK * C::VPITCH];   // this workgroup's V rows
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][C::QL::elems(C::BQ)];
+  __shared__ __attribute__((aligned(16))) __bf16 sG[2][C::QL::elems(C::BQ)];
+  __shared__ __attribute__((aligned(16))) __bf16 sVk[C::VL::elems(C::BK)];   // this workgroup's V rows
   __shared__ __attribute__((aligned(16))) float sLse[2][C::BQ];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BQ];
 
@@ -297,8 +300,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const size_t koff = ((size_t)b * a.Skv + key) * kv_rs + (size_t)hkv * D;
   const size_t q_base = (size_t)b * a.Sq * a.Hq * D;
   const uint32_t q_bytes = a.Sq > 0 ? (uint32_t)a.Sq * q_rs_b : 0;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)a.q + q_base, q_bytes);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const __bf16*)a.dout + q_base, q_bytes);
+  const __bf16* qbase = (const __bf16*)a.q + q_base;
+  const __bf16* gbase = (const __bf16*)a.dout + q_base;
 
   // K stays in registers (B operand of S = Q K^T); V goes to LDS once (B operand of
   // dP = dO V^T, re-read every step) to keep the register count within two waves per SIMD.
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < C::VCPT; ++u) {
       const int c = tid + 256 * u, r = c / C::DC, ch = c % C::DC;
-      *(u32x4*)&sVk[r * C::VPITCH + 8 * ch] = buf_load16(rvk, (uint32_t)r * kv_rs_b + 16u * ch, 0);
+      *(u32x4*)&sVk[C::VL::idx(r, 8 * ch)] = buf_load16(rvk, (uint32_t)r * kv_rs_b + 16u * ch, 0);
     }
   }
   f32x16 dk[C::DB], dv[C::DB];
@@ -363,15 +366,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   for (int u = 0; u < C::CPT; ++u) {
     const int c = min(tid + 256 * u, C::NCH - 1), i = c / C::DC, ch = c % C::DC;
     goff[u] = (uint32_t)i * q_rs_b + 16u * ch;
-    loff[u] = i * C::PITCH + 8 * ch;
+    loff[u] = C::QL::idx(i, 8 * ch);
   }
   float lbuf = 0.f;
   auto load_step = [&](int hq_, int qs) {
-    const uint32_t so = (uint32_t)qs * q_rs_b + (uint32_t)hq_ * D * 2;
+    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)qs * q_rs_b + (uint32_t)hq_ * D * 2);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc_at(qbase, q_bytes, so);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc_at(gbase, q_bytes, so);
 #pragma unroll
     for (int u = 0; u < C::CPT; ++u) {
-      qbuf[u] = buf_load16(rq, goff[u], so);
-      gbuf[u] = buf_load16(rg, goff[u], so);
+      qbuf[u] = buf_load16(rq, goff[u], 0);
+      gbuf[u] = buf_load16(rg, goff[u], 0);
     }
     if (tid < 2 * C::BQ) {
       const int i = tid & (C::BQ - 1), row = qs + i;
@@ -391,9 +396,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     else if (tid < 2 * C::BQ) sD[buf][tid - C::BQ] = lbuf;
   };
   const int tg = lane >> 4, tj = lane & 15;
-  const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * C::PITCH + 16 * (tg & 1) + 4 * (tj & 3);
-  const int q_off = li * C::PITCH + 8 * lh;
-  const int v_off = (wave * 32 + li) * C::VPITCH + 8 * lh;
+  const int tr_off = C::QL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
+  const int q_off = C::QL::idx(li, 8 * lh);
+  const int v_off = C::VL::idx(wave * 32 + li, 8 * lh);
 
   int hq = 0, qs = 0, rend = 0;
   bool have = next_step(hq, qs, rend);
@@ -425,10 +430,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk) {
-        const int off = q_off + 16 * kk;
         const bf16x8 vb = *(const bf16x8*)&sVk[v_off + 16 * kk];
-        s = mfma32(*(const bf16x8*)&qt_[off], kreg[kk], s);
-        dp = mfma32(*(const bf16x8*)&gt_[off], vb, dp);
+        s = mfma32(*(const bf16x8*)&qt_[q_off + 16 * kk], kreg[kk], s);
+        dp = mfma32(*(const bf16x8*)&gt_[q_off + 16 * kk], vb, dp);
       }
       if (!full) {
         cold_path();
@@ -467,9 +471,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         const bf16x8 pbf = as_bf16x8(pb), sbf = as_bf16x8(sb);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const int off = tr_off + 16 * ks * C::PITCH + 32 * db;
-          const bf16x8 ga = join_bf16x8(lds_read_tr16(&gt_[off]), lds_read_tr16(&gt_[off + 8 * C::PITCH]));
-          const bf16x8 qa = join_bf16x8(lds_read_tr16(&qt_[off]), lds_read_tr16(&qt_[off + 8 * C::PITCH]));
+          const int o0 = tr_off + C::QL::rows(16 * ks) + 32 * db, o1 = o0 + C::QL::rows(8);
+          const bf16x8 ga = join_bf16x8(lds_read_tr16(&gt_[o0]), lds_read_tr16(&gt_[o1]));
+          const bf16x8 qa = join_bf16x8(lds_read_tr16(&qt_[o0]), lds_read_tr16(&qt_[o1]));
           dv[db] = mfma32(ga, pbf, dv[db]);
           dk[db] = mfma32(qa, sbf, dk[db]);
         }

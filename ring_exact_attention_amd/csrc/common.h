@@ -136,7 +136,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
-// 16-byte load at base + voffset + soffset (bytes); zero when out of range.
+// Resource for the bytes [start, total) of a region: offsets used with it are relative
+// to `start` and range-checked against the rest of the region.  All arguments must be
+// the same on every lane; they are moved to scalar registers explicitly, since a
+// resource the compiler cannot prove uniform makes it loop over lanes at every load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_at(const void* base, uint32_t total,
+                                                               uint32_t start) {
+  const uint64_t addr = (uint64_t)(uintptr_t)base + start;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(total > start ? total - start : 0u);
+  return make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), n);
+}
+
+// 16-byte load at base + voffset + soffset (bytes); zero when voffset is out of range.
+// The range check covers voffset only, so callers keep soffset at zero and move a tile's
+// start into the resource (make_rsrc_at).
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }

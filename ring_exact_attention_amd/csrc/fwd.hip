@@ -32,7 +32,8 @@ struct FwdCfg {
   static constexpr int BN = 64;                    // keys per tile
   static constexpr int KS = D / 16;                // k-steps of S^T over d
   static constexpr int DB = D / 32;                // 32-row blocks of O^T
-  static constexpr int PITCH = D + 32;             // LDS row pitch (elements); 320 B at D = 128
+  using KL = TileLayout<D, kRowRead>;              // K tile: read as row operands
+  using VL = TileLayout<D, kTrRead>;               // V tile: read transposed
   static constexpr int DC = D / 8;                 // 16-byte chunks per row
   static constexpr int LPT = BN * DC / 256;        // 16-byte chunks per thread per tile and tensor
 };
@@ -43,8 +44,8 @@ constexpr float kRescaleThreshold = 8.0f;
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::BN * C::PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::BN * C::PITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::KL::elems(C::BN)];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::VL::elems(C::BN)];
 
   int b, hq, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, a.xcd_groups, a.hi_off < kPosInf, b, hq, qt);
@@ -61,8 +62,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const __bf16* qp = (const __bf16*)a.q + (size_t)b * a.Sq * q_rs + (size_t)hq * D;
   const size_t kv_base = ((size_t)b * a.Skv * a.Hkv + hkv) * D;
   const uint32_t kv_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * kv_rs_b + D * 2 : 0;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + kv_base, kv_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + kv_base, kv_bytes);
+  const __bf16* kbase = (const __bf16*)a.k + kv_base;
+  const __bf16* vbase = (const __bf16*)a.v + kv_base;
 
   // Q^T as B operands: lane (li, lh) holds q[row][16kk + 8lh .. +7].
   bf16x8 qreg[C::KS];
@@ -120,33 +121,33 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Staging: thread t moves 16-byte chunks c = t + 256u (row c / DC, chunk c % DC).
   u32x4 kbuf[C::LPT], vbuf[C::LPT];
   uint32_t goff[C::LPT];
-  int loff[C::LPT];
+  constexpr int RPU = 256 / C::DC;                  // rows per staging round (multiple of 4)
 #pragma unroll
-  for (int u = 0; u < C::LPT; ++u) {
-    const int c = tid + 256 * u, r = c / C::DC, ch = c % C::DC;
-    goff[u] = (uint32_t)r * kv_rs_b + 16u * ch;
-    loff[u] = r * C::PITCH + 8 * ch;
-  }
+  for (int u = 0; u < C::LPT; ++u) goff[u] = (uint32_t)(tid / C::DC + RPU * u) * kv_rs_b + 16u * (tid % C::DC);
+  const int kl0 = C::KL::idx(tid / C::DC, 8 * (tid % C::DC));
+  const int vl0 = C::VL::idx(tid / C::DC, 8 * (tid % C::DC));
   auto load_tile = [&](int ts) {
-    const uint32_t so = (uint32_t)ts * kv_rs_b;
+    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)ts * kv_rs_b);   // uniform
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc_at(kbase, kv_bytes, so);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc_at(vbase, kv_bytes, so);
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
-      kbuf[u] = buf_load16(rk, goff[u], so);
-      vbuf[u] = buf_load16(rv, goff[u], so);
+      kbuf[u] = buf_load16(rk, goff[u], 0);
+      vbuf[u] = buf_load16(rv, goff[u], 0);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < C::LPT; ++u) {
-      *(u32x4*)&sK[buf][loff[u]] = kbuf[u];
-      *(u32x4*)&sV[buf][loff[u]] = vbuf[u];
+      *(u32x4*)&sK[buf][kl0 + C::KL::rows(RPU * u)] = kbuf[u];
+      *(u32x4*)&sV[buf][vl0 + C::VL::rows(RPU * u)] = vbuf[u];
     }
   };
   // Transposed V operand: lane (group g = lane/16, j = lane%16) points at
   // V[16c + 4(g>>1) + j/4 (+8)][32db + 16(g&1) + 4(j%4) ..+3].
   const int tg = lane >> 4, tj = lane & 15;
-  const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * C::PITCH + 16 * (tg & 1) + 4 * (tj & 3);
-  const int k_off = li * C::PITCH + 8 * lh;
+  const int tr_off = C::VL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
+  const int k_off = C::KL::idx(li, 8 * lh);
 
   int ts = 0, kend = 0;
   bool have = it.next(ts, kend);
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       for (int kk = 0; kk < C::KS; ++kk)        // two independent accumulation chains
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 ka = *(const bf16x8*)&kt[k_off + 32 * mb * C::PITCH + 16 * kk];
+          const bf16x8 ka = *(const bf16x8*)&kt[k_off + C::KL::rows(32 * mb) + 16 * kk];
           s[mb] = mfma32(ka, qreg[kk], s[mb]);
         }
       if (!full) {
@@ -234,8 +235,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
           const int c = 2 * mb + ks;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
-            const __bf16* vp0 = &vt[tr_off + 16 * c * C::PITCH + 32 * db];
-            const bf16x8 va = join_bf16x8(lds_read_tr16(vp0), lds_read_tr16(vp0 + 8 * C::PITCH));
+            const __bf16* vp0 = &vt[tr_off + C::VL::rows(16 * c) + 32 * db];
+            const bf16x8 va = join_bf16x8(lds_read_tr16(vp0), lds_read_tr16(vp0 + C::VL::rows(8)));
             acc[db] = mfma32(va, pbf, acc[db]);
           }
         }

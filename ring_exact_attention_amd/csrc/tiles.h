@@ -150,4 +150,31 @@ __device__ __forceinline__ int perm_slot(int kk) {
   return c | (h << 3) | pos;
 }
 
+// LDS layouts of a row-major bf16 tile with D columns, chosen per access pattern so that
+// no pattern has bank conflicts (64 banks x 4 bytes; measured on gfx950):
+//   kRowRead:  rows read as 16-byte MFMA operands (16 lanes = 16 rows, same column) ->
+//              pitch D + 8 elements (272 B at D = 128: 16 rows land on 16 distinct 16-byte
+//              bank groups);
+//   kTrRead:   rows read with ds_read_b64_tr_b16 (32 lanes = 4 rows x 64 bytes) -> pitch
+//              D + 32 (320 B: 4 consecutive rows start 64 bytes apart modulo 256);
+//   kBothRead: both patterns.  At D = 128, rows go in groups of four at a 320-byte pitch
+//              and each group starts 16 bytes further round the banks (group pitch 1296 B),
+//              which satisfies both conditions with offsets that stay linear in the row
+//              for row steps that are multiples of 4.  Otherwise pitch D + 32.
+// Row stores of 16-byte chunks (16 lanes per row) are conflict-free in all three.
+enum TileKind { kRowRead = 0, kTrRead = 1, kBothRead = 2 };
+
+template <int D, int KIND>
+struct TileLayout {
+  static constexpr bool kGrouped = (KIND == kBothRead && D == 128);
+  static constexpr int PITCH = kGrouped ? 160 : (KIND == kRowRead ? D + 8 : D + 32);
+  static constexpr int GROUP = kGrouped ? 4 * PITCH + 8 : 4 * PITCH;   // elements per 4 rows
+  static constexpr int elems(int rows) { return (rows / 4) * GROUP; }  // rows % 4 == 0
+  // element offset of (row, col); row steps that are multiples of 4 add (step / 4) * GROUP
+  __device__ static __forceinline__ int idx(int row, int col) {
+    return (row >> 2) * GROUP + (row & 3) * PITCH + col;
+  }
+  static constexpr int rows(int step) { return (step / 4) * GROUP; }   // step % 4 == 0
+};
+
 }  // namespace rea
