@@ -45,6 +45,9 @@ struct FwdArgs {
   int finalize;
   int n_qtiles;       // ceil(Sq / BM)
   int xcd_groups;     // (B*Hkv) / 8 when the XCD-aware order applies, else 0
+  // bf16 workgroup shape (set by the launcher): gh q heads of one GQA group x
+  // rows_wg query rows, gh * rows_wg = 256; n_hg = Hq / gh head groups.
+  int gh, gh_shift, rows_wg, n_hg;
 };
 
 // Backward kernel arguments (dense path).
@@ -148,6 +151,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_at(const void* base,
   const uint32_t n = __builtin_amdgcn_readfirstlane(total > start ? total - start : 0u);
   return make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), n);
 }
+
+// Direct global -> LDS copy (gfx950 buffer_load_dwordx4 ... lds): each active lane
+// reads 16 bytes at voff and writes them to lds + 16 * lane.  `lds` must be the same on
+// every lane.  Completion is tracked by vmcnt (wait_vmcnt0 before the data is read).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0,
+                                           0, 0);
+}
+// s_waitcnt vmcnt(0), leaving the other counters alone.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // 16-byte load at base + voffset + soffset (bytes); zero when voffset is out of range.
 // The range check covers voffset only, so callers keep soffset at zero and move a tile's

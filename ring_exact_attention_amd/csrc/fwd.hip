@@ -7,16 +7,25 @@
 // follow _chunk_attention_bias (causal) and the TransformerEngine page's
 // _make_causal_swa_mask (window), on global positions.
 //
-// gfx950 mapping (bf16): one workgroup = 4 wavefronts = 128 query rows of one
-// (batch, q head); each wave owns 32 rows.  Scores are computed transposed,
-// S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so that each lane owns one query row
-// (column of the accumulator): the row max / sum need one cross-half exchange, and
-// the probabilities P^T are already in the B-operand layout of O^T = V^T P^T.
-// K and V tiles are fetched with raw buffer loads (rows past the end read as zero) and
-// staged row-major in LDS at a pitch of D + 32 elements, double-buffered through
-// registers.  K feeds S^T with 16-byte reads; the transposed V operand of O^T is read
-// with ds_read_b64_tr_b16, in the key order of the score accumulator.  Both read
-// patterns are free of LDS bank conflicts at that pitch.
+// gfx950 mapping (bf16): one workgroup = 8 wavefronts (one per CU, two per SIMD); each
+// wave owns 32 query rows of one q head, and the workgroup covers gh heads of one GQA
+// group x 256/gh rows, so all eight waves read the same K/V tiles.  Scores are computed
+// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane owns one query row
+// (a column of the accumulator), the row max / sum need one cross-half exchange, and
+// P^T is already the B operand of O^T = V^T P^T.
+//
+// K and V tiles of 64 keys are copied straight from HBM/L2 into LDS (buffer loads with
+// an LDS destination, rows past the end read as zero), three stages deep, with layouts
+// chosen so that neither operand read has bank conflicts: K rows at an odd number of
+// 16-byte slots (row-operand reads), V rows at 20 slots (ds_read_b64_tr_b16 reads, four
+// rows cover all banks).
+//
+// The two waves of a SIMD alternate between an MFMA block (S of tile t and O += P V of
+// tile t-1) and a VALU block (mask, row max, exp, row sum of tile t): waves 0-3 run the
+// MFMA block while waves 4-7 run the VALU block, and the roles swap at every workgroup
+// barrier, so the matrix unit of each SIMD is fed by one wave while the other does its
+// softmax arithmetic.
+//
 // Accumulation is fp32; exp uses v_exp_f32 on logits pre-scaled by scale*log2(e).  The
 // carry is rescaled only when a row max grows by more than 2^8 (exact: numerator and
 // denominator share the stale reference), and the stored statistics use the exact max.
@@ -28,32 +37,38 @@ namespace rea {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 128;                   // query rows per workgroup
+  static constexpr int NW = 8;                     // wavefronts per workgroup
   static constexpr int BN = 64;                    // keys per tile
+  static constexpr int NS = 3;                     // LDS stages
   static constexpr int KS = D / 16;                // k-steps of S^T over d
   static constexpr int DB = D / 32;                // 32-row blocks of O^T
-  using KL = TileLayout<D, kRowRead>;              // K tile: read as row operands
-  using VL = TileLayout<D, kTrRead>;               // V tile: read transposed
   static constexpr int DC = D / 8;                 // 16-byte chunks per row
-  static constexpr int LPT = BN * DC / 256;        // 16-byte chunks per thread per tile and tensor
+  static constexpr int KRS = DC + 1;               // K row pitch in 16-byte slots (odd)
+  static constexpr int VRS = DC == 4 ? 4 : (DC == 8 ? 12 : 20);   // V row pitch, slots
+  static constexpr int KI = (BN * KRS + 63) / 64;  // 64-lane copy instructions per K tile
+  static constexpr int VI = (BN * VRS + 63) / 64;  // ... per V tile
+  static constexpr int NI = (KI + VI + NW - 1) / NW;   // per wave per tile
+  static constexpr int STAGE = (KI + VI) * 1024;   // bytes per stage (K then V)
 };
 
 // Rows of the scores may grow by this much (log2 units) before the carry is rescaled.
 constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::KL::elems(C::BN)];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::VL::elems(C::BN)];
+  __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE];
 
-  int b, hq, qt;
-  map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, a.xcd_groups, a.hi_off < kPosInf, b, hq, qt);
-  const int hkv = hq / a.G;
+  int b, hg, qt;
+  map_task(blockIdx.x, a.n_qtiles, a.B, a.n_hg, a.Hkv, a.G >> a.gh_shift, a.xcd_groups, a.hi_off < kPosInf,
+           b, hg, qt);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
-  const int wg_row0 = qt * C::BM;
-  const int row0 = wg_row0 + wave * 32;
+  const int grp = wave >> 2;                       // 0: MFMA block in the first half-step
+  const int hq = (hg << a.gh_shift) + (wave & (a.gh - 1));
+  const int hkv = hq / a.G;
+  const int wg_row0 = qt * a.rows_wg;
+  const int row0 = wg_row0 + 32 * (wave >> a.gh_shift);
   const int row = row0 + li;
   const bool row_ok = row < a.Sq;
 
@@ -100,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // Keys visible to any row of this workgroup: j in [i - delta + lo_off, i - delta + hi_off].
-  const int r_last_wg = min(wg_row0 + C::BM, a.Sq) - 1;
+  const int r_last_wg = min(wg_row0 + a.rows_wg, a.Sq) - 1;
   const int jlo = max(0, wg_row0 - a.delta + a.lo_off);
   const int jhi = min(a.Skv - 1, r_last_wg - a.delta + a.hi_off);
   int diag = (wg_row0 - a.delta);
@@ -118,136 +133,179 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int my_jmin = row - a.delta + a.lo_off;
   const int my_jmax = row - a.delta + a.hi_off;
 
-  // Staging: thread t moves 16-byte chunks c = t + 256u (row c / DC, chunk c % DC).
-  u32x4 kbuf[C::LPT], vbuf[C::LPT];
-  uint32_t goff[C::LPT];
-  constexpr int RPU = 256 / C::DC;                  // rows per staging round (multiple of 4)
+  // Tile copies: instruction n (0 <= n < KI + VI) of a stage fills bytes [1024n, 1024n+1024);
+  // lane l of it carries 16-byte slot 64n' + l of the K (n' = n) or V (n' = n - KI) tile,
+  // i.e. row slot / pitch, chunk slot % pitch (padding slots are skipped).  Wave w issues
+  // instructions w, w + 8, ...
+  uint32_t voff[C::NI];
+  bool vld[C::NI];
 #pragma unroll
-  for (int u = 0; u < C::LPT; ++u) goff[u] = (uint32_t)(tid / C::DC + RPU * u) * kv_rs_b + 16u * (tid % C::DC);
-  const int kl0 = C::KL::idx(tid / C::DC, 8 * (tid % C::DC));
-  const int vl0 = C::VL::idx(tid / C::DC, 8 * (tid % C::DC));
-  auto load_tile = [&](int ts) {
-    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)ts * kv_rs_b);   // uniform
+  for (int i = 0; i < C::NI; ++i) {
+    const int n = wave + C::NW * i;
+    const bool is_k = n < C::KI;
+    const int pitch = is_k ? C::KRS : C::VRS;
+    const int slot = 64 * (is_k ? n : n - C::KI) + lane;
+    const int r = slot / pitch, ch = slot - r * pitch;
+    vld[i] = n < C::KI + C::VI && ch < C::DC && r < C::BN;
+    voff[i] = (uint32_t)r * kv_rs_b + 16u * ch;
+  }
+  auto issue = [&](int ts, int stage) {
+    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)ts * kv_rs_b);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc_at(kbase, kv_bytes, so);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc_at(vbase, kv_bytes, so);
+    char* sb = lds + stage * C::STAGE;
 #pragma unroll
-    for (int u = 0; u < C::LPT; ++u) {
-      kbuf[u] = buf_load16(rk, goff[u], 0);
-      vbuf[u] = buf_load16(rv, goff[u], 0);
+    for (int i = 0; i < C::NI; ++i) {
+      const int n = wave + C::NW * i;
+      if (n < C::KI + C::VI) {
+        if (vld[i]) dma16(n < C::KI ? rk : rv, sb + 1024 * n, voff[i]);
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::LPT; ++u) {
-      *(u32x4*)&sK[buf][kl0 + C::KL::rows(RPU * u)] = kbuf[u];
-      *(u32x4*)&sV[buf][vl0 + C::VL::rows(RPU * u)] = vbuf[u];
-    }
-  };
-  // Transposed V operand: lane (group g = lane/16, j = lane%16) points at
+
+  // Operand offsets (bytes within a stage).  K rows as A operands of S^T; V^T by
+  // transposed reads: lane (g = lane/16, j = lane%16) points at
   // V[16c + 4(g>>1) + j/4 (+8)][32db + 16(g&1) + 4(j%4) ..+3].
   const int tg = lane >> 4, tj = lane & 15;
-  const int tr_off = C::VL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
-  const int k_off = C::KL::idx(li, 8 * lh);
+  const int k_off = li * (16 * C::KRS) + 16 * lh;
+  const int v_off = C::KI * 1024 + (4 * (tg >> 1) + (tj >> 2)) * (16 * C::VRS) + 32 * (tg & 1) + 8 * (tj & 3);
 
-  int ts = 0, kend = 0;
-  bool have = it.next(ts, kend);
-  if (have) {
-    load_tile(ts);
-    store_tile(0);
-  }
-  __syncthreads();
-  int cur = 0;
-  while (have) {
-    int nts = 0, nkend = 0;
-    const bool nhave = it.next(nts, nkend);
-    if (nhave) load_tile(nts);
+  f32x16 s[2];
+  bf16x8 pb[4];                                    // P^T of the last softmax, B operands
+  bool s_valid = false, p_valid = false;
 
-    const int tend = min(kend, a.Skv);            // keys >= tend are not in this visit
-    const bool empty = !wave_on || ts > w_jmax_hi || tend - 1 < w_jmin_lo;
-    if (!empty) {
-      const bool full = ts >= w_jmin_hi && ts + C::BN - 1 <= w_jmax_lo && ts + C::BN <= tend;
-      const __bf16* kt = sK[cur];
-      const __bf16* vt = sV[cur];
-      f32x16 s[2];
+  // MFMA block: S^T of tile (ts_s in stage st_s) and O^T += V^T P^T for the tile in st_p.
+  auto mfma_block = [&](bool do_s, int ts_s, int kend_s, int st_s, int st_p) {
+    __builtin_amdgcn_s_setprio(1);
+    s_valid = false;
+    if (do_s && wave_on && !(ts_s > w_jmax_hi || min(kend_s, a.Skv) - 1 < w_jmin_lo)) {
+      s_valid = true;
+      const char* kt = lds + st_s * C::STAGE + k_off;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk)        // two independent accumulation chains
+      for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 ka = *(const bf16x8*)&kt[k_off + C::KL::rows(32 * mb) + 16 * kk];
+          const bf16x8 ka = *(const bf16x8*)(kt + mb * 32 * 16 * C::KRS + 32 * kk);
           s[mb] = mfma32(ka, qreg[kk], s[mb]);
         }
-      if (!full) {
-        cold_path();
-        // key j = ts + 4lh + koff is visible iff jlo_v <= j <= jhi_v: one unsigned compare
-        const int jlo_v = max(my_jmin, ts), jhi_v = min(my_jmax, tend - 1);
-        const uint32_t span = (uint32_t)(jhi_v - jlo_v);
-        const int base = ts + 4 * lh - jlo_v;
+    }
+    if (p_valid) {
+      const char* vt = lds + st_p * C::STAGE + v_off;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
-            if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-      mx = fmaxf(mx, other_half(mx));
-      const float mt = mx * a.scale_log2;          // this tile's row max (log2 units)
-      m_true = fmaxf(m_true, mt);
-      if (__ballot(mt > m_used + kRescaleThreshold)) {
-        cold_path();
-        const float m_new = fmaxf(m_used, mt);
-        const float alpha = fast_exp2(m_used - (m_new == -INFINITY ? 0.f : m_new));
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-        m_used = m_new;
-      }
-      const float m_ref = (m_used == -INFINITY) ? 0.f : m_used;
-      float rs = 0.f;
+        for (int db = 0; db < C::DB; ++db) {
+          const char* vp0 = vt + c * 16 * 16 * C::VRS + 64 * db;
+          const bf16x8 va = join_bf16x8(lds_read_tr16((const __bf16*)vp0),
+                                        lds_read_tr16((const __bf16*)(vp0 + 8 * 16 * C::VRS)));
+          acc[db] = mfma32(va, pb[c], acc[db]);
+        }
+      p_valid = false;
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // VALU block: mask, max, (lazy) rescale of the carry, P = exp2(S - m), row sums.
+  auto softmax_block = [&](int ts, int kend) {
+    if (!s_valid) return;
+    const int tend = min(kend, a.Skv);            // keys >= tend are not in this visit
+    const bool full = ts >= w_jmin_hi && ts + C::BN - 1 <= w_jmax_lo && ts + C::BN <= tend;
+    if (!full) {
+      cold_path();
+      // key j = ts + 4lh + koff is visible iff jlo_v <= j <= jhi_v: one unsigned compare
+      const int jlo_v = max(my_jmin, ts), jhi_v = min(my_jmax, tend - 1);
+      const uint32_t span = (uint32_t)(jhi_v - jlo_v);
+      const int base = ts + 4 * lh - jlo_v;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[mb][r], a.scale_log2, -m_ref));
-          s[mb][r] = p;
-          rs += p;
-        }
-      l_part += rs;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          u32x4 pb;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(s[mb][8 * ks + 2 * w], s[mb][8 * ks + 2 * w + 1]);
-          const bf16x8 pbf = as_bf16x8(pb);
-          const int c = 2 * mb + ks;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const __bf16* vp0 = &vt[tr_off + C::VL::rows(16 * c) + 32 * db];
-            const bf16x8 va = join_bf16x8(lds_read_tr16(vp0), lds_read_tr16(vp0 + C::VL::rows(8)));
-            acc[db] = mfma32(va, pbf, acc[db]);
-          }
+          const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
+          if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
         }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    mx = fmaxf(mx, other_half(mx));
+    const float mt = mx * a.scale_log2;            // this tile's row max (log2 units)
+    m_true = fmaxf(m_true, mt);
+    if (__ballot(mt > m_used + kRescaleThreshold)) {
+      cold_path();
+      const float m_new = fmaxf(m_used, mt);
+      const float alpha = fast_exp2(m_used - (m_new == -INFINITY ? 0.f : m_new));
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m_used = m_new;
+    }
+    const float m_ref = (m_used == -INFINITY) ? 0.f : m_used;
+    float rs = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 w4;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float p0 = fast_exp2(fmaf(s[mb][8 * ks + 2 * w], a.scale_log2, -m_ref));
+          const float p1 = fast_exp2(fmaf(s[mb][8 * ks + 2 * w + 1], a.scale_log2, -m_ref));
+          rs += p0 + p1;
+          w4[w] = pack_bf16x2(p0, p1);
+        }
+        pb[2 * mb + ks] = as_bf16x8(w4);
+      }
+    l_part += rs;
+    p_valid = true;
+  };
 
-    if (nhave) store_tile(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
-    ts = nts;
-    kend = nkend;
-    have = nhave;
+  // Pipeline.  Step t has two halves separated by workgroup barriers:
+  //   group 0: [mfma_block: S of t, PV of t-1] | [softmax of t]
+  //   group 1: [softmax of t-1]                | [mfma_block: S of t, PV of t-1]
+  // Tile t+1 is copied into its stage during step t (the stage last held tile t-2).
+  // Both groups run the same number of steps, hence of barriers.
+  int ts_c = 0, ke_c = 0, ts_p = 0, ke_p = 0;
+  bool have_c = it.next(ts_c, ke_c), have_p = false;
+  if (have_c) issue(ts_c, 0);
+  wait_vmcnt0();
+  __syncthreads();
+  int st_c = 0, st_p = 0;
+  if (grp == 0) {
+    while (have_c || have_p) {
+      int ts_n = 0, ke_n = 0;
+      const bool have_n = have_c && it.next(ts_n, ke_n);
+      const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
+      if (have_n) issue(ts_n, st_n);
+      mfma_block(have_c, ts_c, ke_c, st_c, st_p);
+      __syncthreads();
+      softmax_block(ts_c, ke_c);
+      wait_vmcnt0();
+      __syncthreads();
+      have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
+      have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+    }
+  } else {
+    while (have_c || have_p) {
+      int ts_n = 0, ke_n = 0;
+      const bool have_n = have_c && it.next(ts_n, ke_n);
+      const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
+      if (have_n) issue(ts_n, st_n);
+      softmax_block(ts_p, ke_p);
+      __syncthreads();
+      mfma_block(have_c, ts_c, ke_c, st_c, st_p);
+      wait_vmcnt0();
+      __syncthreads();
+      have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
+      have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+    }
   }
 
   // Normalise the statistics to the exact max: l_true = l_used * 2^(m_used - m_true).
@@ -381,18 +439,30 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
   }
 }
 
-int fwd_tile_rows(int dtype) { return dtype == 0 ? FwdCfg<128>::BM : 128; }
+// Smallest number of query rows a workgroup covers (for the host-side size checks).
+int fwd_tile_rows(int dtype) { return dtype == 0 ? 32 : 128; }
 
-hipError_t launch_fwd(int dtype, const FwdArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.n_qtiles * a.B * a.Hq), block256(256), block128(128);
+hipError_t launch_fwd(int dtype, const FwdArgs& args, hipStream_t stream) {
+  const dim3 block128(128);
   if (dtype == 0) {
+    // gh = q heads per workgroup: the largest power of two <= 8 dividing the GQA group.
+    FwdArgs a = args;
+    a.gh_shift = 0;
+    while (a.gh_shift < 3 && a.G % (2 << a.gh_shift) == 0) ++a.gh_shift;
+    a.gh = 1 << a.gh_shift;
+    a.rows_wg = 256 >> a.gh_shift;
+    a.n_hg = a.Hq >> a.gh_shift;
+    a.n_qtiles = (a.Sq + a.rows_wg - 1) / a.rows_wg;
+    const dim3 grid((unsigned)a.n_qtiles * a.B * a.n_hg), block(512);
     switch (a.D) {
-      case 32: hipLaunchKernelGGL(fwd_bf16_kernel<32>, grid, block256, 0, stream, a); break;
-      case 64: hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block256, 0, stream, a); break;
-      case 128: hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block256, 0, stream, a); break;
+      case 32: hipLaunchKernelGGL(fwd_bf16_kernel<32>, grid, block, 0, stream, a); break;
+      case 64: hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
+    const FwdArgs& a = args;
+    const dim3 grid((unsigned)a.n_qtiles * a.B * a.Hq);
     switch (a.D) {
       case 32: hipLaunchKernelGGL(fwd_f32_kernel<32>, grid, block128, 0, stream, a); break;
       case 64: hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block128, 0, stream, a); break;
