@@ -220,14 +220,12 @@ def main():
     ws = torch.empty(max(rea.bwd_workspace_bytes(qd, kd, **kw), 256), dtype=torch.uint8, device=dev)
 
     # One step, split into its kernels so each can be timed on the launch stream:
-    # forward | D/LSE pre-pass | dq | dk,dv.
+    # forward | dq (which also computes D and the LSE for the dk/dv pass) | dk,dv.
     def segments():
         yield "attn_fwd", lambda: rea.attn_fwd(qd, kd, vd, out=o, m=m, l=l, **kw)
         if w.backward:
-            yield "bwd_pre", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
-                                                  skip_dq=True, skip_dkdv=True, **kw)
             yield "bwd_dq", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
-                                                 skip_dkdv=True, reuse_stats=True, **kw)
+                                                 skip_dkdv=True, **kw)
             yield "bwd_dkdv", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
                                                    skip_dq=True, reuse_stats=True, **kw)
 
@@ -240,13 +238,12 @@ def main():
     # Algorithmic flops per kernel launch: the dk/dv kernel does the recompute of S and
     # dP plus dV and dK (8D per pair); the dq kernel's share is dQ (2D per pair), its own
     # recompute being the cost of computing dq without atomics.
-    alg = {"attn_fwd": f_fwd, "bwd_dq": 2.0 * D * pairs, "bwd_dkdv": 8.0 * D * pairs, "bwd_pre": 0.0}
+    alg = {"attn_fwd": f_fwd, "bwd_dq": 2.0 * D * pairs, "bwd_dkdv": 8.0 * D * pairs}
     # Compulsory HBM bytes per launch (bf16 tensors read or written once, fp32 stats).
     esz = 2 if w.dtype == "bf16" else 4
     qbytes, kvbytes, stat = B * S * Hq * D * esz, B * S * Hkv * D * esz, B * Hq * S * 4
     hbm = {"attn_fwd": 2 * qbytes + 2 * kvbytes + 2 * stat,
-           "bwd_pre": 2 * qbytes + 4 * stat,
-           "bwd_dq": 3 * qbytes + 2 * kvbytes + 2 * stat,
+           "bwd_dq": 4 * qbytes + 2 * kvbytes + 4 * stat,
            "bwd_dkdv": 2 * qbytes + 4 * kvbytes + 2 * stat}
     kernels = {}
     for n, t in seg_ms.items():

@@ -60,36 +60,51 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ dq (bf16)
-// One workgroup = 128 query rows of one (batch, q head), 32 per wavefront, walking the
-// key tiles in ring order.  Transposed form, so each lane owns one query row:
-//   S^T = K Q^T, dP^T = V dO^T (A operands: row-major K, V tiles; B: Q, dO in registers),
+// One workgroup = 8 wavefronts (one per CU, two per SIMD), each owning 32 query rows of
+// one q head; the workgroup covers gh heads of one GQA group x 256/gh rows and walks
+// their key tiles in ring order.  Transposed form, so each lane owns one query row:
+//   S^T = K Q^T, dP^T = V dO^T (A operands: K, V tiles in LDS; B: Q, dO in registers),
 //   P^T = exp2(S^T scale log2e - lse2_i), dS^T = P^T (dP^T - D_i) (lane-local stats),
 //   dQ^T += K^T dS^T with the transposed K operand read by ds_read_b64_tr_b16.
+// K/V tiles are copied straight into LDS, three stages deep.  K is read both as rows
+// and transposed, so its rows go in groups of four at the transposed-read pitch with one
+// extra 16-byte slot per group; V is read as rows only (odd slot pitch).  As in the
+// forward kernel, waves 0-3 and 4-7 alternate between the MFMA block (S, dP of tile t;
+// dQ of tile t-1) and the VALU block (P and dS of tile t) at every barrier.
+// With fused_stats the kernel also computes D_i = rowsum(dO * O) and lse2_i from m, l
+// and stores them for the dk/dv pass.
 template <int D>
 struct BwdQCfg {
-  static constexpr int BM = 128;
+  static constexpr int NW = 8;
   static constexpr int BN = 64;
+  static constexpr int NS = 3;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  using KL = TileLayout<D, kBothRead>;             // K tile: row operands and transposed
-  using VL = TileLayout<D, kRowRead>;              // V tile: row operands
   static constexpr int DC = D / 8;
-  static constexpr int LPT = BN * DC / 256;
+  static constexpr int P4 = DC == 4 ? 4 : (DC == 8 ? 12 : 20);    // K row pitch in a group (slots)
+  static constexpr int G4 = 4 * P4 + 1;                            // K group pitch (slots)
+  static constexpr int VRS = DC + 1;                               // V row pitch (slots)
+  static constexpr int KI = ((BN / 4) * G4 + 63) / 64;             // copy instructions per K tile
+  static constexpr int VI = (BN * VRS + 63) / 64;
+  static constexpr int NI = (KI + VI + NW - 1) / NW;
+  static constexpr int STAGE = (KI + VI) * 1024;
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   using C = BwdQCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][C::KL::elems(C::BN)];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][C::VL::elems(C::BN)];
+  __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE];
 
-  int b, hq, qt;
-  map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, a.xcd_groups, a.hi_off < kPosInf, b, hq, qt);
-  const int hkv = hq / a.G;
+  int b, hg, qt;
+  map_task(blockIdx.x, a.n_qtiles, a.B, a.n_hg, a.Hkv, a.G >> a.gh_shift, a.xcd_groups, a.hi_off < kPosInf,
+           b, hg, qt);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
-  const int wg_row0 = qt * C::BM;
-  const int row0 = wg_row0 + wave * 32;
+  const int grp = wave >> 2;
+  const int hq = (hg << a.gh_shift) + (wave & (a.gh - 1));
+  const int hkv = hq / a.G;
+  const int wg_row0 = qt * a.rows_wg;
+  const int row0 = wg_row0 + 32 * (wave >> a.gh_shift);
   const int row = row0 + li;
   const bool row_ok = row < a.Sq;
   const size_t q_rs = (size_t)a.Hq * D;
@@ -112,8 +127,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
     doreg[kk] = as_bf16x8(g);
   }
   const size_t stat = ((size_t)b * a.Hq + hq) * a.Sq + row;
-  const float lse2 = row_ok ? a.lse2[stat] : INFINITY;
-  const float Di = row_ok ? a.Dvec[stat] : 0.f;
+  float lse2, Di;
+  if (a.fused_stats) {
+    // D_i = sum_d dO[i][d] O[i][d]: this lane holds half of the row's d.
+    float part = 0.f;
+    if (row_ok) {
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk) {
+        const u32x4 ou = *(const u32x4*)((const __bf16*)a.o + qoff + 16 * kk + 8 * lh);
+        const u32x4 gu = __builtin_bit_cast(u32x4, doreg[kk]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          part = fmaf(bf16_lo(ou[w]), bf16_lo(gu[w]), part);
+          part = fmaf(bf16_hi(ou[w]), bf16_hi(gu[w]), part);
+        }
+      }
+    }
+    Di = part + other_half(part);
+    const float l = row_ok ? a.l[stat] : 0.f, m = row_ok ? a.m[stat] : 0.f;
+    lse2 = (l > 0.f) ? fmaf(m, kLog2e, log2f(l)) : INFINITY;
+    if (row_ok && lh == 0) {
+      a.Dvec[stat] = Di;
+      a.lse2[stat] = lse2;
+    }
+  } else {
+    lse2 = row_ok ? a.lse2[stat] : INFINITY;
+    Di = row_ok ? a.Dvec[stat] : 0.f;
+  }
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -121,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  const int r_last_wg = min(wg_row0 + C::BM, a.Sq) - 1;
+  const int r_last_wg = min(wg_row0 + a.rows_wg, a.Sq) - 1;
   const int jlo = max(0, wg_row0 - a.delta + a.lo_off);
   const int jhi = min(a.Skv - 1, r_last_wg - a.delta + a.hi_off);
   int diag = wg_row0 - a.delta;
@@ -136,56 +176,64 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
   const int w_jmax_lo = row0 - a.delta + a.hi_off, w_jmax_hi = w_last - a.delta + a.hi_off;
   const int my_jmin = row - a.delta + a.lo_off, my_jmax = row - a.delta + a.hi_off;
 
-  u32x4 kbuf[C::LPT], vbuf[C::LPT];
-  uint32_t goff[C::LPT];
-  constexpr int RPU = 256 / C::DC;                  // rows per staging round (multiple of 4)
+  // Tile copies: instruction n of a stage fills bytes [1024n, 1024n + 1024); lane l of it
+  // carries slot 64n' + l of the K tile (n' = n; grouped rows) or the V tile (n' = n - KI).
+  uint32_t voff[C::NI];
+  bool vld[C::NI];
 #pragma unroll
-  for (int u = 0; u < C::LPT; ++u) goff[u] = (uint32_t)(tid / C::DC + RPU * u) * kv_rs_b + 16u * (tid % C::DC);
-  const int kl0 = C::KL::idx(tid / C::DC, 8 * (tid % C::DC));
-  const int vl0 = C::VL::idx(tid / C::DC, 8 * (tid % C::DC));
-  auto load_tile = [&](int ts) {
-    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)ts * kv_rs_b);   // uniform
+  for (int i = 0; i < C::NI; ++i) {
+    const int n = wave + C::NW * i;
+    int r, ch;
+    bool ok;
+    if (n < C::KI) {
+      const int slot = 64 * n + lane;
+      const int q4 = slot / C::G4, rem = slot - q4 * C::G4;
+      const int k4 = rem / C::P4;
+      ch = rem - k4 * C::P4;
+      r = 4 * q4 + k4;
+      ok = k4 < 4;
+    } else {
+      const int slot = 64 * (n - C::KI) + lane;
+      r = slot / C::VRS;
+      ch = slot - r * C::VRS;
+      ok = true;
+    }
+    vld[i] = ok && n < C::KI + C::VI && ch < C::DC && r < C::BN;
+    voff[i] = (uint32_t)r * kv_rs_b + 16u * ch;
+  }
+  auto issue = [&](int ts, int stage) {
+    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)ts * kv_rs_b);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc_at(kbase, kv_bytes, so);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc_at(vbase, kv_bytes, so);
+    char* sb = lds + stage * C::STAGE;
 #pragma unroll
-    for (int u = 0; u < C::LPT; ++u) {
-      kbuf[u] = buf_load16(rk, goff[u], 0);
-      vbuf[u] = buf_load16(rv, goff[u], 0);
+    for (int i = 0; i < C::NI; ++i) {
+      const int n = wave + C::NW * i;
+      if (n < C::KI + C::VI) {
+        if (vld[i]) dma16(n < C::KI ? rk : rv, sb + 1024 * n, voff[i]);
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::LPT; ++u) {
-      *(u32x4*)&sK[buf][kl0 + C::KL::rows(RPU * u)] = kbuf[u];
-      *(u32x4*)&sV[buf][vl0 + C::VL::rows(RPU * u)] = vbuf[u];
-    }
-  };
-  // Operand offsets: per-lane base + constants.  Transposed reads: lane (g = lane/16,
-  // j = lane%16) points at K[16c + 4(g>>1) + j/4 (+8)][32db + 16(g&1) + 4(j%4) ..+3].
-  const int tg = lane >> 4, tj = lane & 15;
-  const int tr_off = C::KL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
-  const int k_off = C::KL::idx(li, 8 * lh);
-  const int v_off = C::VL::idx(li, 8 * lh);
 
-  int ts = 0, kend = 0;
-  bool have = it.next(ts, kend);
-  if (have) {
-    load_tile(ts);
-    store_tile(0);
-  }
-  __syncthreads();
-  int cur = 0;
-  while (have) {
-    int nts = 0, nkend = 0;
-    const bool nhave = it.next(nts, nkend);
-    if (nhave) load_tile(nts);
-    const int tend = min(kend, a.Skv);
-    const bool empty = !wave_on || ts > w_jmax_hi || tend - 1 < w_jmin_lo;
-    if (!empty) {
-      const bool full = ts >= w_jmin_hi && ts + C::BN - 1 <= w_jmax_lo && ts + C::BN <= tend;
-      const __bf16* kt = sK[cur];
-      const __bf16* vt = sV[cur];
-      f32x16 s[2], dp[2];
+  // Operand offsets (bytes within a stage).  K row (li, 8lh..) for S^T; transposed K:
+  // lane (g = lane/16, j = lane%16) points at K[16c + 4(g>>1) + j/4 (+8)][32db + 16(g&1) + 4(j%4)];
+  // V row (li, 8lh..) for dP^T.
+  const int tg = lane >> 4, tj = lane & 15;
+  const int k_off = (li >> 2) * (16 * C::G4) + (li & 3) * (16 * C::P4) + 16 * lh;
+  const int kt_off = (tg >> 1) * (16 * C::G4) + (tj >> 2) * (16 * C::P4) + 32 * (tg & 1) + 8 * (tj & 3);
+  const int v_off = C::KI * 1024 + li * (16 * C::VRS) + 16 * lh;
+
+  f32x16 s[2], dp[2];
+  bf16x8 dsb[4];                                   // dS^T of the last VALU block, B operands
+  bool s_valid = false, ds_valid = false;
+
+  auto mfma_block = [&](bool do_s, int ts_s, int kend_s, int st_s, int st_p) {
+    __builtin_amdgcn_s_setprio(1);
+    s_valid = false;
+    if (do_s && wave_on && !(ts_s > w_jmax_hi || min(kend_s, a.Skv) - 1 < w_jmin_lo)) {
+      s_valid = true;
+      const char* kt = lds + st_s * C::STAGE + k_off;
+      const char* vt = lds + st_s * C::STAGE + v_off;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -194,53 +242,98 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs a) {
           dp[mb][r] = 0.f;
         }
 #pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk)        // four independent accumulation chains
+      for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          s[mb] = mfma32(*(const bf16x8*)&kt[k_off + C::KL::rows(32 * mb) + 16 * kk], qreg[kk], s[mb]);
-          dp[mb] = mfma32(*(const bf16x8*)&vt[v_off + C::VL::rows(32 * mb) + 16 * kk], doreg[kk], dp[mb]);
+          s[mb] = mfma32(*(const bf16x8*)(kt + mb * 8 * 16 * C::G4 + 32 * kk), qreg[kk], s[mb]);
+          dp[mb] = mfma32(*(const bf16x8*)(vt + mb * 32 * 16 * C::VRS + 32 * kk), doreg[kk], dp[mb]);
         }
-      if (!full) {
-        cold_path();
-        const int jlo_v = max(my_jmin, ts), jhi_v = min(my_jmax, tend - 1);
-        const uint32_t span = (uint32_t)(jhi_v - jlo_v);
-        const int base = ts + 4 * lh - jlo_v;
+    }
+    if (ds_valid) {
+      const char* kp = lds + st_p * C::STAGE + kt_off;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
-            if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
-          }
-      }
+        for (int db = 0; db < C::DB; ++db) {
+          const char* kp0 = kp + c * 4 * 16 * C::G4 + 64 * db;
+          const bf16x8 ka = join_bf16x8(lds_read_tr16((const __bf16*)kp0),
+                                        lds_read_tr16((const __bf16*)(kp0 + 2 * 16 * C::G4)));
+          acc[db] = mfma32(ka, dsb[c], acc[db]);
+        }
+      ds_valid = false;
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto valu_block = [&](int ts, int kend) {
+    if (!s_valid) return;
+    const int tend = min(kend, a.Skv);
+    const bool full = ts >= w_jmin_hi && ts + C::BN - 1 <= w_jmax_lo && ts + C::BN <= tend;
+    if (!full) {
+      cold_path();
+      const int jlo_v = max(my_jmin, ts), jhi_v = min(my_jmax, tend - 1);
+      const uint32_t span = (uint32_t)(jhi_v - jlo_v);
+      const int base = ts + 4 * lh - jlo_v;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[mb][r], a.scale_log2, -lse2));
-          s[mb][r] = p * (dp[mb][r] - Di);
+          const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
+          if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
         }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int mb = c >> 1, ks = c & 1;
-        u32x4 pb;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(s[mb][8 * ks + 2 * w], s[mb][8 * ks + 2 * w + 1]);
-        const bf16x8 pbf = as_bf16x8(pb);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const __bf16* kp0 = &kt[tr_off + C::KL::rows(16 * c) + 32 * db];
-          const bf16x8 ka = join_bf16x8(lds_read_tr16(kp0), lds_read_tr16(kp0 + C::KL::rows(8)));
-          acc[db] = mfma32(ka, pbf, acc[db]);
-        }
-      }
     }
-    if (nhave) store_tile(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
-    ts = nts;
-    kend = nkend;
-    have = nhave;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 w4;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int r0 = 8 * ks + 2 * w;
+          const float p0 = fast_exp2(fmaf(s[mb][r0], a.scale_log2, -lse2));
+          const float p1 = fast_exp2(fmaf(s[mb][r0 + 1], a.scale_log2, -lse2));
+          w4[w] = pack_bf16x2(p0 * (dp[mb][r0] - Di), p1 * (dp[mb][r0 + 1] - Di));
+        }
+        dsb[2 * mb + ks] = as_bf16x8(w4);
+      }
+    ds_valid = true;
+  };
+
+  // Same two-group pipeline as the forward kernel.
+  int ts_c = 0, ke_c = 0, ts_p = 0, ke_p = 0;
+  bool have_c = it.next(ts_c, ke_c), have_p = false;
+  if (have_c) issue(ts_c, 0);
+  wait_vmcnt0();
+  __syncthreads();
+  int st_c = 0, st_p = 0;
+  if (grp == 0) {
+    while (have_c || have_p) {
+      int ts_n = 0, ke_n = 0;
+      const bool have_n = have_c && it.next(ts_n, ke_n);
+      const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
+      if (have_n) issue(ts_n, st_n);
+      mfma_block(have_c, ts_c, ke_c, st_c, st_p);
+      __syncthreads();
+      valu_block(ts_c, ke_c);
+      wait_vmcnt0();
+      __syncthreads();
+      have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
+      have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+    }
+  } else {
+    while (have_c || have_p) {
+      int ts_n = 0, ke_n = 0;
+      const bool have_n = have_c && it.next(ts_n, ke_n);
+      const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
+      if (have_n) issue(ts_n, st_n);
+      valu_block(ts_p, ke_p);
+      __syncthreads();
+      mfma_block(have_c, ts_c, ke_c, st_c, st_p);
+      wait_vmcnt0();
+      __syncthreads();
+      have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
+      have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+    }
   }
 
   if (row_ok) {
@@ -650,7 +743,8 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
   }
 }
 
-int bwd_q_tile_rows(int dtype) { return dtype == 0 ? BwdQCfg<128>::BM : 128; }
+// Smallest number of query rows a dq workgroup covers (for the host-side size checks).
+int bwd_q_tile_rows(int dtype) { return dtype == 0 ? 32 : 128; }
 int bwd_k_tile_rows(int dtype) { return dtype == 0 ? BwdKVCfg<128>::BK : 128; }
 
 template <typename T, int D>
@@ -662,16 +756,31 @@ static void launch_pre(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, a);
 }
 
-hipError_t launch_bwd(int dtype, const BwdArgs& a, hipStream_t stream) {
-  const dim3 gq((unsigned)a.n_qtiles * a.B * a.Hq), gk((unsigned)a.n_ktiles * a.B * a.Hkv);
+hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
+  BwdArgs a = args;
+  dim3 gq((unsigned)a.n_qtiles * a.B * a.Hq), bq(128);
+  if (dtype == 0) {
+    // dq workgroups: gh q heads of one GQA group x 256/gh rows (as in the forward pass).
+    a.gh_shift = 0;
+    while (a.gh_shift < 3 && a.G % (2 << a.gh_shift) == 0) ++a.gh_shift;
+    a.gh = 1 << a.gh_shift;
+    a.rows_wg = 256 >> a.gh_shift;
+    a.n_hg = a.Hq >> a.gh_shift;
+    a.n_qtiles = (a.Sq + a.rows_wg - 1) / a.rows_wg;
+    gq = dim3((unsigned)a.n_qtiles * a.B * a.n_hg);
+    bq = dim3(512);
+  }
+  const dim3 gk((unsigned)a.n_ktiles * a.B * a.Hkv), bk(dtype == 0 ? 256 : 128);
   const bool has_q = gq.x > 0, has_k = gk.x > 0;
-  const bool pre = has_q && (a.stages & 1), dq = has_q && (a.stages & 2), dkdv = has_k && (a.stages & 4);
-  const dim3 bb(dtype == 0 ? 256 : 128);
+  const bool want_pre = has_q && (a.stages & 1), dq = has_q && (a.stages & 2), dkdv = has_k && (a.stages & 4);
+  // The bf16 dq kernel computes D and the LSE itself when they are needed.
+  a.fused_stats = (dtype == 0 && want_pre && dq) ? 1 : 0;
+  const bool pre = want_pre && !a.fused_stats;
 #define REA_BWD(T, DD, DQ, DKV)                                                  \
   do {                                                                          \
     if (pre) launch_pre<T, DD>(a, stream);                                      \
-    if (dq) hipLaunchKernelGGL(DQ<DD>, gq, bb, 0, stream, a);                   \
-    if (dkdv) hipLaunchKernelGGL(DKV<DD>, gk, bb, 0, stream, a);                \
+    if (dq) hipLaunchKernelGGL(DQ<DD>, gq, bq, 0, stream, a);                   \
+    if (dkdv) hipLaunchKernelGGL(DKV<DD>, gk, bk, 0, stream, a);                \
   } while (0)
   if (dtype == 0) {
     switch (a.D) {

@@ -73,6 +73,9 @@ struct BwdArgs {
   int xcd_groups;              // (B*Hkv)/8 for the XCD-aware dq order, else 0
   int xcd_kv_groups;           // same for the dk/dv grid
   int stages;                  // bit 0: D/LSE pre-pass, bit 1: dq, bit 2: dk/dv
+  // bf16 dq workgroup shape (set by the launcher), as in FwdArgs; fused_stats: the dq
+  // kernel computes D and the LSE itself (and stores them for the dk/dv pass).
+  int gh, gh_shift, rows_wg, n_hg, fused_stats;
 };
 
 struct SelectArgs {
