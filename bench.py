@@ -30,6 +30,37 @@ PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 
 
+def kernel_source_sha():
+    """sha1 over the kernel sources (csrc/* and include/attn.h, sorted by name)."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(root, "ring_exact_attention_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(root, "include", "attn.h")]
+    h = hashlib.sha1()
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs summarised in profiles/kernels_<workload>.md (each counter scaled by
+    its reading for a plain copy of known size).  None when the file has no figure for
+    it or the kernel sources have changed since the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"kernels_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    sha = kernel_source_sha()
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic: "):
+                rec = json.loads(line[len("traffic: "):])
+                if rec.get("kernel") == kernel and rec.get("source_sha1") == sha:
+                    return rec["hbm_bytes_per_launch"]
+    return None
+
+
 def visible_pairs(Sq, Skv, causal, window, q_pos0=0, kv_pos0=0):
     """Visible (query, key) pairs per (batch, q head) for the causal / window mask."""
     import numpy as np
@@ -169,7 +200,7 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
            "roofline": {"kernel": "attn_fwd_sparse", "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                         "avg_us": round(seg_ms["attn_fwd_sparse"] * 1e3, 2), "alg_bytes_per_launch": gathered,
-                        "traffic": None}}
+                        "traffic": measured_traffic(w.name, "attn_fwd_sparse")}}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = sparse_cpu_baseline(w, q, k, v, idx.cpu().numpy(), args.cpu_budget)
     print(json.dumps(out), flush=True)
@@ -262,7 +293,8 @@ def main():
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(alg[dom] / (seg_ms[dom] * 1e-3) / 1e12, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(alg[dom] / (seg_ms[dom] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "avg_us": round(seg_ms[dom] * 1e3, 2), "alg_flop_per_launch": alg[dom], "traffic": None}
+            "avg_us": round(seg_ms[dom] * 1e3, 2), "alg_flop_per_launch": alg[dom],
+            "traffic": measured_traffic(w.name, dom)}
     if w.window[0] >= 0:        # sliding window: the kernels are HBM-bound
         roof.update({"bound": "hbm", "achieved": round(hbm[dom] / (seg_ms[dom] * 1e-3) / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
