@@ -105,7 +105,8 @@ typedef struct attn_params {
   /* Gathered block-sparse mode ("AnnAttention", faiss_block_attention): when sel_idx
    * is non-NULL, attn_fwd attends each token to a zero-padded window of
    * sparse_window keys ending at the token, followed by the sel_block rows of each of
-   * its top_n selected blocks (an index of -1 reads token 0 for every row), with one
+   * its top_n selected blocks (an index of -1 reads token 0 for every row; an index
+   * >= Sq / sel_block, which block_select never produces, reads zero rows), with one
    * softmax over all slots and no mask.  Requires bf16, Hq = Hkv = 1, head_dim = the
    * joint embedding (512), Sq = Skv, causal/window/flags/kv_block unused.           */
   const int32_t* sel_idx;      /* [B, Sq, top_n] device, from block_select             */

@@ -139,17 +139,6 @@ __device__ __forceinline__ void map_kv_task(int bid, int n_tiles, int B, int Hkv
   if (reverse) t = n_tiles - 1 - t;
 }
 
-// Slot of key `kk` (0..BN-1) in a transposed LDS row, so that the eight keys one lane
-// needs for a 32x32x16 MFMA k-step sit in 16 contiguous bytes.  Within each group of
-// 16 keys the lanes of half h (0/1) hold keys {4h..4h+3, 8+4h..8+4h+3} (the row order
-// of the 32x32 MFMA accumulator); slot = 8h + position.
-__device__ __forceinline__ int perm_slot(int kk) {
-  const int c = kk & ~15, r = kk & 15;
-  const int h = (r >> 2) & 1;
-  const int pos = (r & 3) | ((r >> 3) << 2);
-  return c | (h << 3) | pos;
-}
-
 // LDS layouts of a row-major bf16 tile with D columns, chosen per access pattern so that
 // no pattern has bank conflicts (64 banks x 4 bytes; measured on gfx950):
 //   kRowRead:  rows read as 16-byte MFMA operands (16 lanes = 16 rows, same column) ->
