@@ -74,20 +74,14 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   const size_t q_rs = (size_t)a.Hq * D;
   const uint32_t kv_rs_b = (uint32_t)a.Hkv * D * 2;           // bytes between key rows
-  const __bf16* qp = (const __bf16*)a.q + (size_t)b * a.Sq * q_rs + (size_t)hq * D;
   const size_t kv_base = ((size_t)b * a.Skv * a.Hkv + hkv) * D;
   const uint32_t kv_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * kv_rs_b + D * 2 : 0;
   const __bf16* kbase = (const __bf16*)a.k + kv_base;
   const __bf16* vbase = (const __bf16*)a.v + kv_base;
 
-  // Q^T as B operands: lane (li, lh) holds q[row][16kk + 8lh .. +7].
+  // Q^T as B operands: lane (li, lh) holds q[row][16kk + 8lh .. +7]; loaded through LDS
+  // (see the prologue) so that the HBM reads cover whole rows.
   bf16x8 qreg[C::KS];
-#pragma unroll
-  for (int kk = 0; kk < C::KS; ++kk) {
-    u32x4 u = {0u, 0u, 0u, 0u};
-    if (row_ok) u = *(const u32x4*)(qp + (size_t)row * q_rs + 16 * kk + 8 * lh);
-    qreg[kk] = as_bf16x8(u);
-  }
 
   // O^T accumulators: acc[db][r] = O[row][32db + 8(r>>2) + 4lh + (r&3)], unnormalised,
   // relative to m_used.  m_true is the exact running max.
@@ -274,9 +268,24 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // Both groups run the same number of steps, hence of barriers.
   int ts_c = 0, ke_c = 0, ts_p = 0, ke_p = 0;
   bool have_c = it.next(ts_c, ke_c), have_p = false;
+  // Prologue: this wave's 32 Q rows are copied whole (16 lanes per row) into stages 1-2
+  // and read back in the operand layout; tile 0 goes to stage 0.
+  constexpr int RPI = 64 / C::DC;                  // Q rows per copy instruction
+  char* const qs = lds + C::STAGE + wave * (32 * 2 * D);
+  {
+    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (uint32_t)(q_rs * 2) + (uint32_t)hq * D * 2);
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc_at((const __bf16*)a.q + (size_t)b * a.Sq * q_rs, (uint32_t)a.Sq * (uint32_t)(q_rs * 2), so);
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i)
+      dma16(rq, qs + 1024 * i, (uint32_t)(RPI * i + lane / C::DC) * (uint32_t)(q_rs * 2) + 16u * (lane % C::DC));
+  }
   if (have_c) issue(ts_c, 0);
   wait_vmcnt0();
   __syncthreads();
+#pragma unroll
+  for (int kk = 0; kk < C::KS; ++kk) qreg[kk] = *(const bf16x8*)(qs + li * (2 * D) + 32 * kk + 16 * lh);
+  __syncthreads();                                 // stages 1-2 are refilled from step 0 on
   int st_c = 0, st_p = 0;
   if (grp == 0) {
     while (have_c || have_p) {
@@ -311,20 +320,31 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   // Normalise the statistics to the exact max: l_true = l_used * 2^(m_used - m_true).
   const float l_used = l_part + other_half(l_part);
   const float corr = (m_true == -INFINITY) ? 0.f : fast_exp2(m_used - m_true);
+  if (a.finalize) {
+    // O through LDS (this wave's 32 rows at 2D + 16 bytes, in the now idle stages; all
+    // reads of the stages ended at the loop's last barrier), then stored as whole rows.
+    const float inv = l_used > 0.f ? 1.f / l_used : 0.f;
+    constexpr int OP = 2 * D + 16;
+    char* const os = lds + wave * (32 * OP);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+        *(u32x2*)(os + li * OP + 2 * (32 * db + 8 * g + 4 * lh)) = w;
+      }
+    __bf16* ob = (__bf16*)a.o + ((size_t)b * a.Sq + row0) * q_rs + (size_t)hq * D;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + lane / C::DC, ch = lane % C::DC;
+      const u32x4 v = *(const u32x4*)(os + r * OP + 16 * ch);
+      if (row0 + r < a.Sq) *(u32x4*)(ob + (size_t)r * q_rs + 8 * ch) = v;
+    }
+  }
   if (row_ok) {
-    if (a.finalize) {
-      const float inv = l_used > 0.f ? 1.f / l_used : 0.f;
-      __bf16* op = (__bf16*)a.o + ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
-          w[1] = pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-          *(u32x2*)(op + 32 * db + 8 * g + 4 * lh) = w;
-        }
-    } else {
+    if (!a.finalize) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
