@@ -93,7 +93,7 @@ struct BwdQCfg {
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   using C = BwdQCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE + C::NW * 32 * 4];
 
   int b, hg, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.n_hg, a.Hkv, a.G >> a.gh_shift, a.xcd_groups, a.hi_off < kPosInf,
@@ -109,51 +109,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
   const bool row_ok = row < a.Sq;
   const size_t q_rs = (size_t)a.Hq * D;
   const uint32_t kv_rs_b = (uint32_t)a.Hkv * D * 2;
-  const size_t qoff = ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D;
   const size_t kv_base = ((size_t)b * a.Skv * a.Hkv + hkv) * D;
   const uint32_t kv_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * kv_rs_b + D * 2 : 0;
   const __bf16* kbase = (const __bf16*)a.k + kv_base;
   const __bf16* vbase = (const __bf16*)a.v + kv_base;
 
+  // Q^T and dO^T as B operands (lane (li, lh) holds x[row][16kk + 8lh .. +7]) and the row
+  // statistics; filled in the prologue below.
   bf16x8 qreg[C::KS], doreg[C::KS];
-#pragma unroll
-  for (int kk = 0; kk < C::KS; ++kk) {
-    u32x4 u = {0u, 0u, 0u, 0u}, g = {0u, 0u, 0u, 0u};
-    if (row_ok) {
-      u = *(const u32x4*)((const __bf16*)a.q + qoff + 16 * kk + 8 * lh);
-      g = *(const u32x4*)((const __bf16*)a.dout + qoff + 16 * kk + 8 * lh);
-    }
-    qreg[kk] = as_bf16x8(u);
-    doreg[kk] = as_bf16x8(g);
-  }
   const size_t stat = ((size_t)b * a.Hq + hq) * a.Sq + row;
-  float lse2, Di;
-  if (a.fused_stats) {
-    // D_i = sum_d dO[i][d] O[i][d]: this lane holds half of the row's d.
-    float part = 0.f;
-    if (row_ok) {
-#pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk) {
-        const u32x4 ou = *(const u32x4*)((const __bf16*)a.o + qoff + 16 * kk + 8 * lh);
-        const u32x4 gu = __builtin_bit_cast(u32x4, doreg[kk]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          part = fmaf(bf16_lo(ou[w]), bf16_lo(gu[w]), part);
-          part = fmaf(bf16_hi(ou[w]), bf16_hi(gu[w]), part);
-        }
-      }
-    }
-    Di = part + other_half(part);
-    const float l = row_ok ? a.l[stat] : 0.f, m = row_ok ? a.m[stat] : 0.f;
-    lse2 = (l > 0.f) ? fmaf(m, kLog2e, log2f(l)) : INFINITY;
-    if (row_ok && lh == 0) {
-      a.Dvec[stat] = Di;
-      a.lse2[stat] = lse2;
-    }
-  } else {
-    lse2 = row_ok ? a.lse2[stat] : INFINITY;
-    Di = row_ok ? a.Dvec[stat] : 0.f;
-  }
+  float lse2 = INFINITY, Di = 0.f;
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -299,12 +264,74 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
     ds_valid = true;
   };
 
-  // Same two-group pipeline as the forward kernel.
+  // Prologue.  Q, dO (and O for D) rows are read whole, 16 lanes per row, so that every
+  // HBM access covers full cache lines: Q and then dO pass through LDS (stages 1-2) into
+  // the operand layout; O stays in registers in the row layout for the dot product.
   int ts_c = 0, ke_c = 0, ts_p = 0, ke_p = 0;
   bool have_c = it.next(ts_c, ke_c), have_p = false;
-  if (have_c) issue(ts_c, 0);
-  wait_vmcnt0();
-  __syncthreads();
+  {
+    constexpr int RPI = 64 / C::DC;                // rows per copy instruction
+    constexpr int NQ = 32 / RPI;                   // copy instructions for 32 rows
+    char* const qs = lds + C::STAGE + wave * (32 * 2 * D);
+    const uint32_t q_rs_b = (uint32_t)q_rs * 2;
+    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)row0 * q_rs_b + (uint32_t)hq * D * 2);
+    const uint32_t q_bytes = (uint32_t)a.Sq * q_rs_b;
+    const size_t batch0 = (size_t)b * a.Sq * q_rs;
+    const int rr = lane / C::DC, rc = lane % C::DC;
+    auto copy_rows = [&](const void* tensor) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc_at((const __bf16*)tensor + batch0, q_bytes, so);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) dma16(r, qs + 1024 * i, (uint32_t)(RPI * i + rr) * q_rs_b + 16u * rc);
+    };
+    const bool fused = a.fused_stats != 0;
+    u32x4 orow[NQ];                                // O: row RPI*i + lane/DC, chunk lane%DC
+    if (fused) {
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc_at((const __bf16*)a.o + batch0, q_bytes, so);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) orow[i] = buf_load16(ro, (uint32_t)(RPI * i + rr) * q_rs_b + 16u * rc, 0);
+    }
+    copy_rows(a.q);
+    if (have_c) issue(ts_c, 0);
+    wait_vmcnt0();
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) qreg[kk] = *(const bf16x8*)(qs + li * (2 * D) + 32 * kk + 16 * lh);
+    __syncthreads();                               // (this wave's rows only, but keep the copies ordered)
+    copy_rows(a.dout);
+    wait_vmcnt0();
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) doreg[kk] = *(const bf16x8*)(qs + li * (2 * D) + 32 * kk + 16 * lh);
+    if (fused) {
+      // D_i = sum_d dO[i][d] O[i][d] over the DC lanes holding row i, then moved to lane i.
+      float* const sd = (float*)(lds + C::NS * C::STAGE) + wave * 32;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const u32x4 gu = *(const u32x4*)(qs + (RPI * i + rr) * (2 * D) + 16 * rc);
+        float part = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          part = fmaf(bf16_lo(orow[i][w]), bf16_lo(gu[w]), part);
+          part = fmaf(bf16_hi(orow[i][w]), bf16_hi(gu[w]), part);
+        }
+#pragma unroll
+        for (int off = C::DC / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+        if (rc == 0) sd[RPI * i + rr] = part;
+      }
+      Di = sd[li];
+      const float l = row_ok ? a.l[stat] : 0.f, m = row_ok ? a.m[stat] : 0.f;
+      lse2 = (l > 0.f) ? fmaf(m, kLog2e, log2f(l)) : INFINITY;
+      if (row_ok && lh == 0) {
+        a.Dvec[stat] = Di;
+        a.lse2[stat] = lse2;
+      }
+    } else if (row_ok) {
+      lse2 = a.lse2[stat];
+      Di = a.Dvec[stat];
+    }
+    if (!row_ok) Di = 0.f;
+    __syncthreads();                               // stages 1-2 are refilled from step 0 on
+  }
   int st_c = 0, st_p = 0;
   if (grp == 0) {
     while (have_c || have_p) {
@@ -336,8 +363,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
     }
   }
 
-  if (row_ok) {
-    __bf16* op = (__bf16*)a.dq + qoff;
+  // dQ through LDS (this wave's rows at 2D + 16 bytes in the idle stages; all reads of the
+  // stages ended at the loop's last barrier), then stored as whole rows.
+  {
+    constexpr int OP = 2 * D + 16, RPI = 64 / C::DC;
+    char* const os = lds + wave * (32 * OP);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -345,8 +375,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
         u32x2 w;
         w[0] = pack_bf16x2(acc[db][4 * g] * a.scale, acc[db][4 * g + 1] * a.scale);
         w[1] = pack_bf16x2(acc[db][4 * g + 2] * a.scale, acc[db][4 * g + 3] * a.scale);
-        *(u32x2*)(op + 32 * db + 8 * g + 4 * lh) = w;
+        *(u32x2*)(os + li * OP + 2 * (32 * db + 8 * g + 4 * lh)) = w;
       }
+    __bf16* ob = (__bf16*)a.dq + ((size_t)b * a.Sq + row0) * q_rs + (size_t)hq * D;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + lane / C::DC, ch = lane % C::DC;
+      const u32x4 v = *(const u32x4*)(os + r * OP + 16 * ch);
+      if (row0 + r < a.Sq) *(u32x4*)(ob + (size_t)r * q_rs + 8 * ch) = v;
+    }
   }
 }
 
