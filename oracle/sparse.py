@@ -17,6 +17,8 @@ Follows ``faiss_block_attention`` of the "AnnAttention" page ("Core code"):
 The window helper and the block-to-item helper are not shown on the page; the
 readings above (window ends at t inclusive, zero padding; block c -> rows c*bs ..
 c*bs+bs-1) are pinned only to themselves -- parity unpinned against the originals.
+A block index past the last block (never produced by the selection) is read as zero
+rows, like the window padding.
 """
 from __future__ import annotations
 
@@ -34,8 +36,9 @@ def _flat(x):
     return x
 
 
-def candidate_positions(t: int, sel_row, *, window: int, block_size: int):
-    """(positions, is_zero_pad) of token t's candidate slots, in list order."""
+def candidate_positions(t: int, sel_row, *, window: int, block_size: int, seqlen=None):
+    """(positions, is_zero_pad) of token t's candidate slots, in list order.  With
+    ``seqlen`` given, rows at or past it (a block index past the last block) are zero pads."""
     pos, pad = [], []
     for w in range(window):
         p = t - window + 1 + w
@@ -44,8 +47,9 @@ def candidate_positions(t: int, sel_row, *, window: int, block_size: int):
     for c in sel_row:
         for r in range(block_size):
             p = int(c) * block_size + r
-            pos.append(p if p >= 0 else 0)
-            pad.append(False)
+            past = seqlen is not None and p >= seqlen
+            pos.append(0 if (p < 0 or past) else p)
+            pad.append(past)
     return np.asarray(pos, dtype=np.int64), np.asarray(pad, dtype=bool)
 
 
@@ -65,7 +69,7 @@ def sparse_attention(q, k, v, sel, *, window: int, block_size: int, scale=None, 
     toks = range(S) if tokens is None else tokens
     for b in range(B):
         for t in toks:
-            pos, pad = candidate_positions(t, sel[b, t], window=window, block_size=block_size)
+            pos, pad = candidate_positions(t, sel[b, t], window=window, block_size=block_size, seqlen=S)
             K = np.where(pad[:, None], 0.0, k[b, pos])
             V = np.where(pad[:, None], 0.0, v[b, pos])
             s = sc * (K @ q[b, t])

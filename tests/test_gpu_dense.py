@@ -41,6 +41,10 @@ SMALL = [
     ("bf16_d128_ring_swa", "bf16", 1, 768, 768, 4, 1, 128, True, (100, 0), 0, 0, 128),
     ("bf16_d128_right_window", "bf16", 1, 190, 190, 2, 1, 128, False, (-1, 20), 0, 0, 0),
     ("bf16_d64_ring_tiny_blocks", "bf16", 1, 256, 256, 2, 2, 64, True, (-1, -1), 0, 0, 32),
+    ("bf16_d128_gqa8_ragged", "bf16", 2, 97, 97, 16, 2, 128, True, (-1, -1), 0, 0, 0),
+    ("bf16_d64_gqa16_swa", "bf16", 1, 260, 260, 16, 1, 64, True, (50, 0), 0, 0, 0),
+    ("bf16_d128_cross_len_offsets", "bf16", 1, 200, 520, 4, 4, 128, False, (-1, -1), 320, 0, 130),
+    ("bf16_d32_gqa4_causal_offsets", "bf16", 1, 150, 300, 8, 2, 32, True, (-1, -1), 150, 0, 0),
     ("f32_d32_causal_gqa2", "f32", 1, 256, 256, 4, 2, 32, True, (-1, -1), 0, 0, 64),
     ("f32_d64_swa_ragged", "f32", 2, 77, 77, 2, 1, 64, True, (9, 0), 0, 0, 0),
 ]

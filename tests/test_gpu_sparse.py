@@ -100,3 +100,24 @@ def test_sparse_full_size_sampled(gpu):
     check_close("o", oo[:, toks], o_r[:, toks], "bf16")
     np.testing.assert_allclose(m.cpu().numpy()[:, toks], m_r[:, toks], atol=1e-3, rtol=0)
     np.testing.assert_allclose(l.cpu().numpy()[:, toks], l_r[:, toks], rtol=1e-3, atol=0)
+
+
+def test_sparse_handmade_selection(gpu):
+    """Selections block_select never produces: duplicates within a token's list, several
+    -1 entries (token 0 for every row), indices past the last block (zero rows), random
+    order, shared and unshared blocks across the 32-token groups."""
+    B, S, E, bs, n, W = 2, 224, 512, 32, 6, 20
+    q, k, v = rnd((B, S, E), 41), rnd((B, S, E), 42), rnd((B, S, E), 43)
+    g = np.random.default_rng(44)
+    nblk = S // bs
+    sel = g.integers(-1, nblk + 3, size=(B, S, n)).astype(np.int32)
+    sel[:, ::5, 1] = sel[:, ::5, 0]                 # duplicates
+    sel[:, ::7, :3] = -1                            # several -1
+    sel[:, 3::11, 4] = nblk + 7                     # past the end
+    o, m, l = gpu.attn_fwd_sparse(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(sel).to(DEV),
+                                  window=W, block_size=bs)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = sparse.sparse_attention(q, k, v, sel, window=W, block_size=bs)
+    check_close("o", o, o_r, "bf16")
+    np.testing.assert_allclose(m.cpu().numpy(), m_r, atol=1e-3, rtol=0)
+    np.testing.assert_allclose(l.cpu().numpy(), l_r, rtol=1e-3, atol=0)

@@ -67,16 +67,16 @@ def _mut_ties_to_higher_index(monkeypatch):
 def _mut_window_off_by_one(monkeypatch):
     orig = sparse.candidate_positions
 
-    def cand(t, sel_row, *, window, block_size):
-        return orig(t - 1, sel_row, window=window, block_size=block_size)
+    def cand(t, sel_row, *, window, block_size, seqlen=None):
+        return orig(t - 1, sel_row, window=window, block_size=block_size, seqlen=seqlen)
     monkeypatch.setattr(sparse, "candidate_positions", cand)
 
 
 def _mut_clamp_to_last(monkeypatch):
     orig = sparse.candidate_positions
 
-    def cand(t, sel_row, *, window, block_size):
-        pos, pad = orig(t, sel_row, window=window, block_size=block_size)
+    def cand(t, sel_row, *, window, block_size, seqlen=None):
+        pos, pad = orig(t, sel_row, window=window, block_size=block_size, seqlen=seqlen)
         n_w = window
         fixed = [p if (i < n_w or c >= 0) else block_size - 1
                  for i, (p, c) in enumerate(zip(pos, [0] * n_w + [c for c in sel_row for _ in range(block_size)]))]
