@@ -221,7 +221,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
+              "the kernels run on one GPU's share and no multi-GPU path is provided.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -6,9 +6,6 @@
 
 namespace rea {
 
-// Number of compute units of the current device (cached per device).
-int device_cu_count();
-
 // dtype: 0 = bf16, 1 = fp32.
 hipError_t launch_fwd(int dtype, const FwdArgs& a, hipStream_t stream);
 int fwd_tile_rows(int dtype);
