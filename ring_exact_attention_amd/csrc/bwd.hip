@@ -73,11 +73,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // dQ of tile t-1) and the VALU block (P and dS of tile t) at every barrier.
 // With fused_stats the kernel also computes D_i = rowsum(dO * O) and lse2_i from m, l
 // and stores them for the dk/dv pass.
-template <int D>
+template <int D, int NW_>
 struct BwdQCfg {
-  static constexpr int NW = 8;
+  static constexpr int NW = NW_;                  // 8: ping-pong, one workgroup per CU; 4: two per CU
+  static constexpr bool PP = NW == 8;
   static constexpr int BN = 64;
-  static constexpr int NS = 3;
+  static constexpr int NS = PP ? 3 : 2;           // stages of (K, V) tiles
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int DC = D / 8;
@@ -90,9 +91,9 @@ struct BwdQCfg {
   static constexpr int STAGE = (KI + VI) * 1024;
 };
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
-  using C = BwdQCfg<D>;
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a) {
+  using C = BwdQCfg<D, NW>;
   __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE + C::NW * 32 * 4];
 
   int b, hg, qt;
@@ -332,34 +333,53 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_bf16_kernel(BwdArgs a) {
     if (!row_ok) Di = 0.f;
     __syncthreads();                               // stages 1-2 are refilled from step 0 on
   }
-  int st_c = 0, st_p = 0;
-  if (grp == 0) {
-    while (have_c || have_p) {
+  if constexpr (!C::PP) {
+    // 4 waves, one per SIMD (the other workgroup on the CU supplies the second wave):
+    // step t runs S, dP of tile t, then dS, then dQ += K^T dS of the same tile, while tile
+    // t+1 is copied into the other stage (which held tile t-1).
+    int st = 0;
+    while (have_c) {
       int ts_n = 0, ke_n = 0;
-      const bool have_n = have_c && it.next(ts_n, ke_n);
-      const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
-      if (have_n) issue(ts_n, st_n);
-      mfma_block(have_c, ts_c, ke_c, st_c, st_p);
-      __syncthreads();
+      const bool have_n = it.next(ts_n, ke_n);
+      if (have_n) issue(ts_n, st ^ 1);
+      mfma_block(true, ts_c, ke_c, st, st);
       valu_block(ts_c, ke_c);
+      mfma_block(false, ts_c, ke_c, st, st);
       wait_vmcnt0();
       __syncthreads();
-      have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
-      have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+      have_c = have_n; ts_c = ts_n; ke_c = ke_n;
+      st ^= 1;
     }
   } else {
-    while (have_c || have_p) {
-      int ts_n = 0, ke_n = 0;
-      const bool have_n = have_c && it.next(ts_n, ke_n);
-      const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
-      if (have_n) issue(ts_n, st_n);
-      valu_block(ts_p, ke_p);
-      __syncthreads();
-      mfma_block(have_c, ts_c, ke_c, st_c, st_p);
-      wait_vmcnt0();
-      __syncthreads();
-      have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
-      have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+    int st_c = 0, st_p = 0;
+    if (grp == 0) {
+      while (have_c || have_p) {
+        int ts_n = 0, ke_n = 0;
+        const bool have_n = have_c && it.next(ts_n, ke_n);
+        const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
+        if (have_n) issue(ts_n, st_n);
+        mfma_block(have_c, ts_c, ke_c, st_c, st_p);
+        __syncthreads();
+        valu_block(ts_c, ke_c);
+        wait_vmcnt0();
+        __syncthreads();
+        have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
+        have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+      }
+    } else {
+      while (have_c || have_p) {
+        int ts_n = 0, ke_n = 0;
+        const bool have_n = have_c && it.next(ts_n, ke_n);
+        const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
+        if (have_n) issue(ts_n, st_n);
+        valu_block(ts_p, ke_p);
+        __syncthreads();
+        mfma_block(have_c, ts_c, ke_c, st_c, st_p);
+        wait_vmcnt0();
+        __syncthreads();
+        have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
+        have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+      }
     }
   }
 
@@ -793,19 +813,31 @@ static void launch_pre(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, a);
 }
 
+static bool dq_use_w4(const BwdArgs& a) {
+#ifdef REA_DQ_WAVES
+  return REA_DQ_WAVES == 4;
+#else
+  return a.lo_off > -kPosInf && a.hi_off < kPosInf && (long long)a.hi_off - a.lo_off < 512;
+#endif
+}
+
 hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
   BwdArgs a = args;
   dim3 gq((unsigned)a.n_qtiles * a.B * a.Hq), bq(128);
+  // bf16 dq workgroups, as in the forward pass: 8 waves (ping-pong, one per CU) when a
+  // query tile sees many keys, 4 waves (two per CU) when every row sees a short window;
+  // gh q heads of one GQA group x 32 * waves / gh rows.
+  const bool w4 = dq_use_w4(a);
   if (dtype == 0) {
-    // dq workgroups: gh q heads of one GQA group x 256/gh rows (as in the forward pass).
+    const int nw = w4 ? 4 : 8, max_shift = w4 ? 2 : 3;
     a.gh_shift = 0;
-    while (a.gh_shift < 3 && a.G % (2 << a.gh_shift) == 0) ++a.gh_shift;
+    while (a.gh_shift < max_shift && a.G % (2 << a.gh_shift) == 0) ++a.gh_shift;
     a.gh = 1 << a.gh_shift;
-    a.rows_wg = 256 >> a.gh_shift;
+    a.rows_wg = (32 * nw) >> a.gh_shift;
     a.n_hg = a.Hq >> a.gh_shift;
     a.n_qtiles = (a.Sq + a.rows_wg - 1) / a.rows_wg;
     gq = dim3((unsigned)a.n_qtiles * a.B * a.n_hg);
-    bq = dim3(512);
+    bq = dim3(64 * nw);
   }
   const dim3 gk((unsigned)a.n_ktiles * a.B * a.Hkv), bk(dtype == 0 ? 256 : 128);
   const bool has_q = gq.x > 0, has_k = gk.x > 0;
@@ -813,26 +845,32 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
   // The bf16 dq kernel computes D and the LSE itself when they are needed.
   a.fused_stats = (dtype == 0 && want_pre && dq) ? 1 : 0;
   const bool pre = want_pre && !a.fused_stats;
-#define REA_BWD(T, DD, DQ, DKV)                                                  \
+#define REA_BWD(T, DD, DQ_LAUNCH, DKV)                                           \
   do {                                                                          \
     if (pre) launch_pre<T, DD>(a, stream);                                      \
-    if (dq) hipLaunchKernelGGL(DQ<DD>, gq, bq, 0, stream, a);                   \
+    if (dq) DQ_LAUNCH;                                                          \
     if (dkdv) hipLaunchKernelGGL(DKV<DD>, gk, bk, 0, stream, a);                \
+  } while (0)
+#define REA_DQ_BF16(DD)                                                          \
+  do {                                                                          \
+    if (w4) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, 4>), gq, bq, 0, stream, a); \
+    else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, 8>), gq, bq, 0, stream, a);    \
   } while (0)
   if (dtype == 0) {
     switch (a.D) {
-      case 32: REA_BWD(__bf16, 32, bwd_dq_bf16_kernel, bwd_dkdv_bf16_kernel); break;
-      case 64: REA_BWD(__bf16, 64, bwd_dq_bf16_kernel, bwd_dkdv_bf16_kernel); break;
-      case 128: REA_BWD(__bf16, 128, bwd_dq_bf16_kernel, bwd_dkdv_bf16_kernel); break;
+      case 32: REA_BWD(__bf16, 32, REA_DQ_BF16(32), bwd_dkdv_bf16_kernel); break;
+      case 64: REA_BWD(__bf16, 64, REA_DQ_BF16(64), bwd_dkdv_bf16_kernel); break;
+      case 128: REA_BWD(__bf16, 128, REA_DQ_BF16(128), bwd_dkdv_bf16_kernel); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (a.D) {
-      case 32: REA_BWD(float, 32, bwd_dq_f32_kernel, bwd_dkdv_f32_kernel); break;
-      case 64: REA_BWD(float, 64, bwd_dq_f32_kernel, bwd_dkdv_f32_kernel); break;
+      case 32: REA_BWD(float, 32, hipLaunchKernelGGL(bwd_dq_f32_kernel<32>, gq, bq, 0, stream, a), bwd_dkdv_f32_kernel); break;
+      case 64: REA_BWD(float, 64, hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, gq, bq, 0, stream, a), bwd_dkdv_f32_kernel); break;
       default: return hipErrorInvalidValue;
     }
   }
+#undef REA_DQ_BF16
 #undef REA_BWD
   return hipGetLastError();
 }

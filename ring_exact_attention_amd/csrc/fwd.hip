@@ -35,11 +35,11 @@
 
 namespace rea {
 
-template <int D>
+template <int D, int NW_>
 struct FwdCfg {
-  static constexpr int NW = 8;                     // wavefronts per workgroup
+  static constexpr int NW = NW_;                   // wavefronts per workgroup (8 or 4)
+  static constexpr bool PP = NW == 8;              // ping-pong between the two waves of a SIMD
   static constexpr int BN = 64;                    // keys per tile
-  static constexpr int NS = 3;                     // LDS stages
   static constexpr int KS = D / 16;                // k-steps of S^T over d
   static constexpr int DB = D / 32;                // 32-row blocks of O^T
   static constexpr int DC = D / 8;                 // 16-byte chunks per row
@@ -48,16 +48,23 @@ struct FwdCfg {
   static constexpr int KI = (BN * KRS + 63) / 64;  // 64-lane copy instructions per K tile
   static constexpr int VI = (BN * VRS + 63) / 64;  // ... per V tile
   static constexpr int NI = (KI + VI + NW - 1) / NW;   // per wave per tile
-  static constexpr int STAGE = (KI + VI) * 1024;   // bytes per stage (K then V)
+  static constexpr int KB = KI * 1024, VB = VI * 1024;
+  // 8 waves: three stages, each holding K and V of one tile.  4 waves (two workgroups
+  // per CU, so at most 80 KB each): two K slots and two V slots, V copied one tile
+  // behind K (K of tile t+1 and V of tile t are copied during step t).
+  static constexpr int STAGE = KB + VB;
+  static constexpr int LDS = PP ? 3 * STAGE : 2 * STAGE;
+  static constexpr int kaddr(int slot) { return PP ? slot * STAGE : slot * KB; }
+  static constexpr int vaddr(int slot) { return PP ? slot * STAGE + KB : 2 * KB + slot * VB; }
 };
 
 // Rows of the scores may grow by this much (log2 units) before the carry is rescaled.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
-  using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE];
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
+  using C = FwdCfg<D, NW>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
 
   int b, hg, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.n_hg, a.Hkv, a.G >> a.gh_shift, a.xcd_groups, a.hi_off < kPosInf,
@@ -127,10 +134,11 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int my_jmin = row - a.delta + a.lo_off;
   const int my_jmax = row - a.delta + a.hi_off;
 
-  // Tile copies: instruction n (0 <= n < KI + VI) of a stage fills bytes [1024n, 1024n+1024);
-  // lane l of it carries 16-byte slot 64n' + l of the K (n' = n) or V (n' = n - KI) tile,
-  // i.e. row slot / pitch, chunk slot % pitch (padding slots are skipped).  Wave w issues
-  // instructions w, w + 8, ...
+  // Tile copies: instruction n (0 <= n < KI + VI) fills bytes [1024n', 1024n' + 1024) of
+  // a K slot (n' = n < KI) or a V slot (n' = n - KI); lane l of it carries 16-byte slot
+  // 64n' + l of the tile, i.e. row slot / pitch, chunk slot % pitch (padding slots are
+  // skipped).  Wave w issues instructions w, w + NW, ...  One call copies K of tile ts_k
+  // (when do_k) into K slot sk and V of tile ts_v (when do_v) into V slot sv.
   uint32_t voff[C::NI];
   bool vld[C::NI];
 #pragma unroll
@@ -143,38 +151,43 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     vld[i] = n < C::KI + C::VI && ch < C::DC && r < C::BN;
     voff[i] = (uint32_t)r * kv_rs_b + 16u * ch;
   }
-  auto issue = [&](int ts, int stage) {
-    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)ts * kv_rs_b);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc_at(kbase, kv_bytes, so);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc_at(vbase, kv_bytes, so);
-    char* sb = lds + stage * C::STAGE;
+  auto issue = [&](bool do_k, int ts_k, int sk, bool do_v, int ts_v, int sv) {
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc_at(kbase, kv_bytes, __builtin_amdgcn_readfirstlane((uint32_t)ts_k * kv_rs_b));
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc_at(vbase, kv_bytes, __builtin_amdgcn_readfirstlane((uint32_t)ts_v * kv_rs_b));
+    char* const kb = lds + C::kaddr(sk);
+    char* const vb = lds + C::vaddr(sv) - C::KB;
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) {
       const int n = wave + C::NW * i;
-      if (n < C::KI + C::VI) {
-        if (vld[i]) dma16(n < C::KI ? rk : rv, sb + 1024 * n, voff[i]);
+      if (n < C::KI) {
+        if (do_k && vld[i]) dma16(rk, kb + 1024 * n, voff[i]);
+      } else if (n < C::KI + C::VI) {
+        if (do_v && vld[i]) dma16(rv, vb + 1024 * n, voff[i]);
       }
     }
   };
 
-  // Operand offsets (bytes within a stage).  K rows as A operands of S^T; V^T by
+  // Operand offsets (bytes within a slot).  K rows as A operands of S^T; V^T by
   // transposed reads: lane (g = lane/16, j = lane%16) points at
   // V[16c + 4(g>>1) + j/4 (+8)][32db + 16(g&1) + 4(j%4) ..+3].
   const int tg = lane >> 4, tj = lane & 15;
   const int k_off = li * (16 * C::KRS) + 16 * lh;
-  const int v_off = C::KI * 1024 + (4 * (tg >> 1) + (tj >> 2)) * (16 * C::VRS) + 32 * (tg & 1) + 8 * (tj & 3);
+  const int v_off = (4 * (tg >> 1) + (tj >> 2)) * (16 * C::VRS) + 32 * (tg & 1) + 8 * (tj & 3);
 
   f32x16 s[2];
   bf16x8 pb[4];                                    // P^T of the last softmax, B operands
   bool s_valid = false, p_valid = false;
 
-  // MFMA block: S^T of tile (ts_s in stage st_s) and O^T += V^T P^T for the tile in st_p.
+  // MFMA block: S^T of tile ts_s (K in slot st_s) and O^T += V^T P^T for the tile whose
+  // V is in slot st_p.
   auto mfma_block = [&](bool do_s, int ts_s, int kend_s, int st_s, int st_p) {
     __builtin_amdgcn_s_setprio(1);
     s_valid = false;
     if (do_s && wave_on && !(ts_s > w_jmax_hi || min(kend_s, a.Skv) - 1 < w_jmin_lo)) {
       s_valid = true;
-      const char* kt = lds + st_s * C::STAGE + k_off;
+      const char* kt = lds + C::kaddr(st_s) + k_off;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
         }
     }
     if (p_valid) {
-      const char* vt = lds + st_p * C::STAGE + v_off;
+      const char* vt = lds + C::vaddr(st_p) + v_off;
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -261,17 +274,18 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     p_valid = true;
   };
 
-  // Pipeline.  Step t has two halves separated by workgroup barriers:
+  // Pipeline (8 waves).  Step t has two halves separated by workgroup barriers:
   //   group 0: [mfma_block: S of t, PV of t-1] | [softmax of t]
   //   group 1: [softmax of t-1]                | [mfma_block: S of t, PV of t-1]
   // Tile t+1 is copied into its stage during step t (the stage last held tile t-2).
   // Both groups run the same number of steps, hence of barriers.
   int ts_c = 0, ke_c = 0, ts_p = 0, ke_p = 0;
   bool have_c = it.next(ts_c, ke_c), have_p = false;
-  // Prologue: this wave's 32 Q rows are copied whole (16 lanes per row) into stages 1-2
-  // and read back in the operand layout; tile 0 goes to stage 0.
+  // Prologue: this wave's 32 Q rows are copied whole (16 lanes per row) into LDS that no
+  // copy of step 0 touches and read back in the operand layout; K (and V, with 8 waves)
+  // of tile 0 go to slot 0.
   constexpr int RPI = 64 / C::DC;                  // Q rows per copy instruction
-  char* const qs = lds + C::STAGE + wave * (32 * 2 * D);
+  char* const qs = lds + (C::PP ? C::STAGE : C::KB) + wave * (32 * 2 * D);
   {
     const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (uint32_t)(q_rs * 2) + (uint32_t)hq * D * 2);
     const __amdgpu_buffer_rsrc_t rq =
@@ -280,40 +294,59 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a) {
     for (int i = 0; i < 32 / RPI; ++i)
       dma16(rq, qs + 1024 * i, (uint32_t)(RPI * i + lane / C::DC) * (uint32_t)(q_rs * 2) + 16u * (lane % C::DC));
   }
-  if (have_c) issue(ts_c, 0);
+  if (have_c) issue(true, ts_c, 0, C::PP, ts_c, 0);
   wait_vmcnt0();
   __syncthreads();
 #pragma unroll
   for (int kk = 0; kk < C::KS; ++kk) qreg[kk] = *(const bf16x8*)(qs + li * (2 * D) + 32 * kk + 16 * lh);
-  __syncthreads();                                 // stages 1-2 are refilled from step 0 on
-  int st_c = 0, st_p = 0;
-  if (grp == 0) {
+  __syncthreads();                                 // the Q rows' LDS is refilled from step 0 on
+  if constexpr (!C::PP) {
+    // 4 waves, one per SIMD (the other workgroup on the CU supplies the second wave):
+    // step t runs [S of t, PV of t-1] then the softmax of t, while K of t+1 and V of t
+    // are copied (K slot (t+1)&1 last held tile t-1, V slot t&1 tile t-2).
+    int sk = 0;                                    // K slot of the current tile
     while (have_c || have_p) {
       int ts_n = 0, ke_n = 0;
       const bool have_n = have_c && it.next(ts_n, ke_n);
-      const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
-      if (have_n) issue(ts_n, st_n);
-      mfma_block(have_c, ts_c, ke_c, st_c, st_p);
-      __syncthreads();
+      issue(have_n, ts_n, sk ^ 1, have_c, ts_c, sk);
+      mfma_block(have_c, ts_c, ke_c, sk, sk ^ 1);
       softmax_block(ts_c, ke_c);
       wait_vmcnt0();
       __syncthreads();
-      have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
-      have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+      have_p = have_c; ts_p = ts_c; ke_p = ke_c;
+      have_c = have_n; ts_c = ts_n; ke_c = ke_n;
+      sk ^= 1;
     }
   } else {
-    while (have_c || have_p) {
-      int ts_n = 0, ke_n = 0;
-      const bool have_n = have_c && it.next(ts_n, ke_n);
-      const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
-      if (have_n) issue(ts_n, st_n);
-      softmax_block(ts_p, ke_p);
-      __syncthreads();
-      mfma_block(have_c, ts_c, ke_c, st_c, st_p);
-      wait_vmcnt0();
-      __syncthreads();
-      have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
-      have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+    int st_c = 0, st_p = 0;
+    if (grp == 0) {
+      while (have_c || have_p) {
+        int ts_n = 0, ke_n = 0;
+        const bool have_n = have_c && it.next(ts_n, ke_n);
+        const int st_n = st_c == 2 ? 0 : st_c + 1;
+        if (have_n) issue(true, ts_n, st_n, true, ts_n, st_n);
+        mfma_block(have_c, ts_c, ke_c, st_c, st_p);
+        __syncthreads();
+        softmax_block(ts_c, ke_c);
+        wait_vmcnt0();
+        __syncthreads();
+        have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
+        have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+      }
+    } else {
+      while (have_c || have_p) {
+        int ts_n = 0, ke_n = 0;
+        const bool have_n = have_c && it.next(ts_n, ke_n);
+        const int st_n = st_c == 2 ? 0 : st_c + 1;
+        if (have_n) issue(true, ts_n, st_n, true, ts_n, st_n);
+        softmax_block(ts_p, ke_p);
+        __syncthreads();
+        mfma_block(have_c, ts_c, ke_c, st_c, st_p);
+        wait_vmcnt0();
+        __syncthreads();
+        have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
+        have_c = have_n; ts_c = ts_n; ke_c = ke_n; st_c = st_n;
+      }
     }
   }
 
@@ -462,22 +495,43 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
 // Smallest number of query rows a workgroup covers (for the host-side size checks).
 int fwd_tile_rows(int dtype) { return dtype == 0 ? 32 : 128; }
 
+// Workgroup shape of the bf16 forward: 8 waves (ping-pong, one workgroup per CU) when
+// a query tile sees many keys; 4 waves (two workgroups per CU) when every row sees a
+// short window, where a work item is only a few tiles long and the second workgroup
+// hides the load of one item's Q and the store of its O behind the other's tiles.
+static bool fwd_use_w4(const FwdArgs& a) {
+#ifdef REA_FWD_WAVES
+  return REA_FWD_WAVES == 4;
+#else
+  return a.lo_off > -kPosInf && a.hi_off < kPosInf && (long long)a.hi_off - a.lo_off < 512;
+#endif
+}
+
+template <int D>
+static void launch_fwd_bf16(FwdArgs a, bool w4, hipStream_t stream) {
+  // gh = q heads per workgroup: the largest power of two <= NW dividing the GQA group.
+  const int nw = w4 ? 4 : 8, max_shift = w4 ? 2 : 3;
+  a.gh_shift = 0;
+  while (a.gh_shift < max_shift && a.G % (2 << a.gh_shift) == 0) ++a.gh_shift;
+  a.gh = 1 << a.gh_shift;
+  a.rows_wg = (32 * nw) >> a.gh_shift;
+  a.n_hg = a.Hq >> a.gh_shift;
+  a.n_qtiles = (a.Sq + a.rows_wg - 1) / a.rows_wg;
+  const dim3 grid((unsigned)a.n_qtiles * a.B * a.n_hg), block(64 * nw);
+  if (w4)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 4>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 8>), grid, block, 0, stream, a);
+}
+
 hipError_t launch_fwd(int dtype, const FwdArgs& args, hipStream_t stream) {
   const dim3 block128(128);
   if (dtype == 0) {
-    // gh = q heads per workgroup: the largest power of two <= 8 dividing the GQA group.
-    FwdArgs a = args;
-    a.gh_shift = 0;
-    while (a.gh_shift < 3 && a.G % (2 << a.gh_shift) == 0) ++a.gh_shift;
-    a.gh = 1 << a.gh_shift;
-    a.rows_wg = 256 >> a.gh_shift;
-    a.n_hg = a.Hq >> a.gh_shift;
-    a.n_qtiles = (a.Sq + a.rows_wg - 1) / a.rows_wg;
-    const dim3 grid((unsigned)a.n_qtiles * a.B * a.n_hg), block(512);
-    switch (a.D) {
-      case 32: hipLaunchKernelGGL(fwd_bf16_kernel<32>, grid, block, 0, stream, a); break;
-      case 64: hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, stream, a); break;
-      case 128: hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, stream, a); break;
+    const bool w4 = fwd_use_w4(args);
+    switch (args.D) {
+      case 32: launch_fwd_bf16<32>(args, w4, stream); break;
+      case 64: launch_fwd_bf16<64>(args, w4, stream); break;
+      case 128: launch_fwd_bf16<128>(args, w4, stream); break;
       default: return hipErrorInvalidValue;
     }
   } else {
