@@ -92,7 +92,8 @@ def cpu_baseline(w, q, k, v, do, budget_s):
         if w.backward:
             dense.backward(q[:1], k[:1], v[:1], do[:1], causal=w.causal, window=w.window, heads=[h])
         heads_done += 1
-        flops += (14.0 if w.backward else 4.0) * w.head_dim * pairs
+        D, Dv = w.head_dim, w.dv
+        flops += ((8.0 * D + 6.0 * Dv) if w.backward else (2.0 * D + 2.0 * Dv)) * pairs
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
@@ -243,12 +244,13 @@ def main():
     dod = do.to(dev) if do is not None else None
     kw = dict(causal=w.causal, window=w.window, query_chunk=w.query_chunk, key_chunk=w.key_chunk,
               kv_block=w.kv_block)
-    B, S, Hq, Hkv, D = w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim
-    o = torch.empty_like(qd)
+    B, S, Hq, Hkv, D, Dv = w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, w.dv
+    o = torch.empty((B, S, Hq, Dv), dtype=qd.dtype, device=dev)
     m = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     l = torch.empty_like(m)
     grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
-    ws = torch.empty(max(rea.bwd_workspace_bytes(qd, kd, **kw), 256), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(rea.bwd_workspace_bytes(qd, kd, head_dim_v=Dv, **kw), 256), dtype=torch.uint8,
+                     device=dev)
 
     # One step, split into its kernels so each can be timed on the launch stream:
     # forward | dq (which also computes D and the LSE for the dk/dv pass) | dk,dv.
@@ -264,18 +266,22 @@ def main():
     seg_ms, wall = time_segments(torch, segs, args.steps, args.warmup, torch.cuda.current_stream(dev))
 
     pairs = visible_pairs(S, S, w.causal, w.window) * B * Hq
-    f_fwd = 4.0 * D * pairs
-    f_bwd = 10.0 * D * pairs if w.backward else 0.0
+    # Per visible pair: S = Q K^T costs 2D flops and each product with V or dO 2Dv
+    # (D = Dv except for the MLA head dims): forward 2D + 2Dv (= 4D); backward recompute
+    # of S (2D) and dP (2Dv), dV (2Dv), dK (2D), dQ (2D) = 6D + 4Dv (= 10D).
+    f_fwd = (2.0 * D + 2.0 * Dv) * pairs
+    f_bwd = (6.0 * D + 4.0 * Dv) * pairs if w.backward else 0.0
     # Algorithmic flops per kernel launch: the dk/dv kernel does the recompute of S and
-    # dP plus dV and dK (8D per pair); the dq kernel's share is dQ (2D per pair), its own
-    # recompute being the cost of computing dq without atomics.
-    alg = {"attn_fwd": f_fwd, "bwd_dq": 2.0 * D * pairs, "bwd_dkdv": 8.0 * D * pairs}
+    # dP plus dV and dK (4D + 4Dv per pair); the dq kernel's share is dQ (2D per pair),
+    # its own recompute being the cost of computing dq without atomics.
+    alg = {"attn_fwd": f_fwd, "bwd_dq": 2.0 * D * pairs, "bwd_dkdv": (4.0 * D + 4.0 * Dv) * pairs}
     # Compulsory HBM bytes per launch (bf16 tensors read or written once, fp32 stats).
     esz = 2 if w.dtype == "bf16" else 4
-    qbytes, kvbytes, stat = B * S * Hq * D * esz, B * S * Hkv * D * esz, B * Hq * S * 4
-    hbm = {"attn_fwd": 2 * qbytes + 2 * kvbytes + 2 * stat,
-           "bwd_dq": 4 * qbytes + 2 * kvbytes + 4 * stat,
-           "bwd_dkdv": 2 * qbytes + 4 * kvbytes + 2 * stat}
+    qbytes, kbytes, stat = B * S * Hq * D * esz, B * S * Hkv * D * esz, B * Hq * S * 4
+    obytes, vbytes = B * S * Hq * Dv * esz, B * S * Hkv * Dv * esz
+    hbm = {"attn_fwd": qbytes + obytes + kbytes + vbytes + 2 * stat,
+           "bwd_dq": 2 * qbytes + 2 * obytes + kbytes + vbytes + 4 * stat,
+           "bwd_dkdv": qbytes + obytes + 2 * kbytes + 2 * vbytes + 2 * stat}
     kernels = {}
     for n, t in seg_ms.items():
         kernels[n] = {"avg_us": round(t * 1e3, 2), "alg_gflop": round(alg[n] / 1e9, 3),
@@ -315,7 +321,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv,
-                   "head_dim": D, "causal": w.causal, "window": list(w.window),
+                   "head_dim": D, "head_dim_v": Dv, "causal": w.causal, "window": list(w.window),
                    "virtual_blocks": (S // w.kv_block) if w.kv_block else 1,
                    "query_chunk": w.query_chunk, "key_chunk": w.key_chunk, "parallelism": "none (1 GPU)"},
         "fwd_tflops": round(fwd_tflops, 2),

@@ -18,8 +18,10 @@
  *   * All tensor arguments are DEVICE pointers (memory of the current HIP device),
  *     dense and row-major, allocated and owned by the caller.  The library allocates
  *     no device memory and keeps no pointer after a call returns.
- *   * BSHD layout: q, o, dout, dq are [B, Sq, Hq, D]; k, v, dk, dv are [B, Skv, Hkv, D].
- *     Statistics m, l are fp32 [B, Hq, Sq].  The carry ``acc`` is fp32 [B, Sq, Hq, D].
+ *   * BSHD layout: q, dq are [B, Sq, Hq, D]; k, dk are [B, Skv, Hkv, D]; v, dv are
+ *     [B, Skv, Hkv, Dv]; o, dout are [B, Sq, Hq, Dv], with Dv = head_dim_v (= D unless
+ *     set).  Statistics m, l are fp32 [B, Hq, Sq].  The carry ``acc`` is fp32
+ *     [B, Sq, Hq, Dv].
  *   * ``stream`` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; nothing is synchronised.  Buffers must stay alive until the
  *     stream work completes.
@@ -113,7 +115,13 @@ typedef struct attn_params {
   int32_t top_n;               /* 1..16                                                */
   int32_t sel_block;           /* rows per selected block (32)                         */
   int32_t sparse_window;       /* 1..64                                                */
-  int32_t reserved;            /* must be 0                                            */
+  /* Head dim of v (and so of o, dout, dv and the carry acc) when it differs from the
+   * q/k head dim: the DeepSeek-style MLA case of "JAX: Single-GPU Attention with
+   * TransformerEngine", section 4 (q/k 128, v 64).  0 = head_dim.  Pairs built:
+   * bf16 32/32, 64/64, 128/128, 128/64; f32 32/32, 64/64, 64/32; others return
+   * ATTN_ERR_UNSUPPORTED.  The default scale stays 1/sqrt(head_dim).  Sparse mode
+   * requires 0.                                                                     */
+  int32_t head_dim_v;
 } attn_params;
 
 typedef struct select_params {

@@ -51,7 +51,8 @@ def blockwise_pass(q, k, v, carry, *, q_pos0: int, kv_pos0: int, query_chunk: in
                    key_chunk: int, causal: bool, window=(-1, -1), scale=None):
     """One blockwise pass of a query block over one kv block, updating the carry.
 
-    q [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D]; carry as ``init_carry``.  Returns the new
+    q [B, Sq, Hq, D]; k [B, Skv, Hkv, D]; v [B, Skv, Hkv, Dv]; carry as ``init_carry``
+    (numerator with Dv columns).  Returns the new
     carry (numerator, denominator, max_score).
     """
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
@@ -99,15 +100,16 @@ def ring_forward(q, k, v, *, n_blocks: int, query_chunk: int, key_chunk: int, ca
                  window=(-1, -1), scale=None):
     """Ring schedule simulated on one host; returns (o, m, l) like ``dense.forward``."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
-    B, S, Hq, D = q.shape
+    B, S, Hq, _ = q.shape
+    Dv = v.shape[3]                                 # value head dim (may differ from q/k's)
     assert S % n_blocks == 0 and k.shape[1] == S
     blk = S // n_blocks
-    o = np.zeros((B, S, Hq, D))
+    o = np.zeros((B, S, Hq, Dv))
     m = np.zeros((B, Hq, S))
     l = np.zeros((B, Hq, S))
     for i in range(n_blocks):                       # ring member i holds query block i
         qi = slice(i * blk, (i + 1) * blk)
-        carry = init_carry(B, blk, Hq, D)
+        carry = init_carry(B, blk, Hq, Dv)
         for idx in range(n_blocks):                 # ring step idx
             j = (i - idx) % n_blocks                # kv block held at this step
             kj = slice(j * blk, (j + 1) * blk)

@@ -31,6 +31,11 @@ blockwise body of ``_blockwise_attention_bwd`` in "bpt.py"):
 with dK and dV summed over the G q heads that share a kv head (the gradient of the
 repeat in the GQA mapping).
 
+The value head dim Dv may differ from the q/k head dim D (the DeepSeek-style MLA case
+of the TransformerEngine page, section 4: q/k 128, v 64); nothing above needs them
+equal: O, dO and dV have Dv columns, Q, K, dQ and dK have D, and the default scale
+stays 1/sqrt(D).
+
 Rows are processed in slices only to bound memory; every row's softmax is computed
 over that row's complete visible key range, so this is the plain definition.
 """
@@ -108,8 +113,8 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
             kv_pos0: int = 0, rows=None, heads=None, row_block: int = 256):
     """Attention forward from the definition.
 
-    q: [B, Sq, Hq, D]; k, v: [B, Skv, Hkv, D] (torch or numpy, any float dtype).
-    Returns (o [B, Sq, Hq, D], m [B, Hq, Sq], l [B, Hq, Sq]) in fp64, with m in the
+    q: [B, Sq, Hq, D]; k: [B, Skv, Hkv, D]; v: [B, Skv, Hkv, Dv] (torch or numpy, any
+    float dtype).  Returns (o [B, Sq, Hq, Dv], m [B, Hq, Sq], l [B, Hq, Sq]) in fp64, with m in the
     natural-log units of the scaled logits.  ``rows`` / ``heads`` restrict the
     evaluation to sampled query rows / q heads; entries not evaluated are NaN.
     """
@@ -121,7 +126,7 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
     sc = _default_scale(D, scale)
     wl, wr = window
     fill = np.nan if (rows is not None or heads is not None) else 0.0
-    o = np.full((B, Sq, Hq, D), fill)
+    o = np.full((B, Sq, Hq, v.shape[3]), fill)
     m = np.full((B, Hq, Sq), np.nan if fill != 0.0 else -np.inf)
     l = np.full((B, Hq, Sq), fill)
     rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -168,7 +173,7 @@ def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: 
              kv_pos0: int = 0, row_block: int = 256, heads=None, batches=None):
     """Analytic gradient of ``forward`` contracted with dO.
 
-    Returns (dq [B, Sq, Hq, D], dk [B, Skv, Hkv, D], dv [B, Skv, Hkv, D]) in fp64.
+    Returns (dq [B, Sq, Hq, D], dk [B, Skv, Hkv, D], dv [B, Skv, Hkv, Dv]) in fp64.
     D_i uses this function's own fp64 output O.  ``heads`` / ``batches`` restrict the
     evaluation to some q heads / batch entries: dq of the others is NaN, and dk, dv
     only collect the contributions of the evaluated q heads (complete for a kv head

@@ -54,7 +54,7 @@ class AttnParams(ctypes.Structure):
         ("top_n", ctypes.c_int32),
         ("sel_block", ctypes.c_int32),
         ("sparse_window", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
     ]
 
 
@@ -143,7 +143,7 @@ def _need(t, name, dtype=None, device=None):
 
 
 def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
-                kv_block=0, q_pos0=0, kv_pos0=0, flags=0) -> AttnParams:
+                kv_block=0, q_pos0=0, kv_pos0=0, flags=0, head_dim_v=0) -> AttnParams:
     B, Sq, Hq, D = q.shape
     Bk, Skv, Hkv, Dk = k.shape
     if Bk != B or Dk != D:
@@ -153,6 +153,7 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     p.dtype = _dtype_code(q)
     p.batch, p.seqlen_q, p.seqlen_kv = B, Sq, Skv
     p.num_q_heads, p.num_kv_heads, p.head_dim = Hq, Hkv, D
+    p.head_dim_v = 0 if head_dim_v in (0, D) else int(head_dim_v)
     p.q_pos0, p.kv_pos0 = int(q_pos0), int(kv_pos0)
     p.causal = 1 if causal else 0
     p.window_left, p.window_right = int(window[0]), int(window[1])
@@ -165,20 +166,24 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
 def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
              kv_block=0, q_pos0=0, kv_pos0=0, m=None, l=None, acc=None, carry_in=False,
              finalize=True, out=None):
-    """Forward attention.  q [B, Sq, Hq, D], k/v [B, Skv, Hkv, D] on the GPU.
+    """Forward attention.  q [B, Sq, Hq, D], k [B, Skv, Hkv, D], v [B, Skv, Hkv, Dv] on the GPU
+    (Dv = D, or the MLA pair D 128 / Dv 64).
 
-    Returns (o, m, l); with ``finalize=False`` returns (acc, m, l) where acc is the
-    fp32 unnormalised numerator.  ``carry_in=True`` resumes from the given m, l, acc.
+    Returns (o, m, l) with o [B, Sq, Hq, Dv]; with ``finalize=False`` returns (acc, m, l)
+    where acc is the fp32 unnormalised numerator.  ``carry_in=True`` resumes from the
+    given m, l, acc.
     """
     _need(q, "q")
     _need(k, "k", q.dtype, q.device)
     _need(v, "v", q.dtype, q.device)
-    if v.shape != k.shape:
-        raise ValueError("k and v must have the same shape")
+    if v.shape[:3] != k.shape[:3]:
+        raise ValueError("k and v must agree on batch, length and heads")
     B, Sq, Hq, D = q.shape
+    Dv = v.shape[3]
     flags = (ATTN_CARRY_IN if carry_in else 0) | (0 if finalize else ATTN_NO_FINALIZE)
     p = make_params(q, k, causal=causal, window=window, scale=scale, query_chunk=query_chunk,
-                    key_chunk=key_chunk, kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, flags=flags)
+                    key_chunk=key_chunk, kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, flags=flags,
+                    head_dim_v=Dv)
     dev = q.device
     if m is None:
         m = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
@@ -187,13 +192,17 @@ def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     _need(m, "m", torch.float32, dev)
     _need(l, "l", torch.float32, dev)
     if (carry_in or not finalize) and acc is None:
-        acc = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=dev)
+        acc = torch.empty((B, Sq, Hq, Dv), dtype=torch.float32, device=dev)
     if acc is not None:
         _need(acc, "acc", torch.float32, dev)
+    if acc is not None and acc.shape != (B, Sq, Hq, Dv):
+        raise ValueError(f"acc must be [B, Sq, Hq, Dv] = {(B, Sq, Hq, Dv)}")
     o = None
     if finalize:
-        o = out if out is not None else torch.empty_like(q)
+        o = out if out is not None else torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=dev)
         _need(o, "o", q.dtype, dev)
+        if o.shape != (B, Sq, Hq, Dv):
+            raise ValueError(f"o must be [B, Sq, Hq, Dv] = {(B, Sq, Hq, Dv)}")
     _check(lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l),
                           _ptr(acc), _stream(q)))
     return (o, m, l) if finalize else (acc, m, l)
@@ -217,8 +226,12 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
         _need(t, n, q.dtype, q.device)
     _need(m, "m", torch.float32, q.device)
     _need(l, "l", torch.float32, q.device)
+    B, Sq, Hq, _ = q.shape
+    Dv = v.shape[3]
+    if v.shape[:3] != k.shape[:3] or o.shape != (B, Sq, Hq, Dv) or dout.shape != o.shape:
+        raise ValueError("v must match k except in its head dim, and o, dout must be [B, Sq, Hq, Dv]")
     kw = dict(causal=causal, window=window, scale=scale, query_chunk=query_chunk, key_chunk=key_chunk,
-              kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0)
+              kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, head_dim_v=Dv)
     flags = ((ATTN_BWD_SKIP_DQ if skip_dq else 0) | (ATTN_BWD_SKIP_DKDV if skip_dkdv else 0) |
              (ATTN_BWD_REUSE_STATS if reuse_stats else 0))
     p = make_params(q, k, flags=flags, **kw)

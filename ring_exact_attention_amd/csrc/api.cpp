@@ -41,7 +41,7 @@ std::string fmt(const char* f, long long a, long long b = 0) {
 
 // A validated dense (or sparse) problem.
 struct Problem {
-  int dtype = 0, B = 0, Sq = 0, Skv = 0, Hq = 0, Hkv = 0, D = 0, G = 1;
+  int dtype = 0, B = 0, Sq = 0, Skv = 0, Hq = 0, Hkv = 0, D = 0, Dv = 0, G = 1;
   int delta = 0, lo_off = -rea::kPosInf, hi_off = rea::kPosInf;
   float scale = 1.f;
   int kv_block = 1, n_vblocks = 0, q_vblock = 1, n_qvblocks = 0;
@@ -53,7 +53,6 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   if (p->struct_size != sizeof(attn_params))
     return fail(ATTN_ERR_INVALID_ARG, fmt("params->struct_size is %lld, this library expects %lld",
                                           (long long)p->struct_size, (long long)sizeof(attn_params)));
-  if (p->reserved != 0) return fail(ATTN_ERR_INVALID_ARG, "params->reserved must be 0");
   if (p->dtype != ATTN_BF16 && p->dtype != ATTN_F32)
     return fail(ATTN_ERR_UNSUPPORTED, fmt("dtype %lld is not supported (ATTN_BF16 or ATTN_F32)", p->dtype));
   if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_kv < 0)
@@ -66,10 +65,12 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
     return fail(ATTN_ERR_INVALID_ARG, fmt("num_q_heads (%lld) must be a multiple of num_kv_heads (%lld)",
                                           p->num_q_heads, p->num_kv_heads));
   const int D = p->head_dim;
-  const bool d_ok = p->dtype == ATTN_BF16 ? (D == 32 || D == 64 || D == 128) : (D == 32 || D == 64);
-  if (!d_ok)
-    return fail(ATTN_ERR_UNSUPPORTED, fmt("head_dim %lld is not supported for this dtype "
-                                          "(bf16: 32, 64, 128; f32: 32, 64)", D));
+  if (p->head_dim_v < 0) return fail(ATTN_ERR_INVALID_ARG, "head_dim_v must be >= 0 (0 = head_dim)");
+  const int Dv = p->head_dim_v > 0 ? p->head_dim_v : D;
+  if (!rea::head_dims_supported(p->dtype == ATTN_BF16 ? 0 : 1, D, Dv))
+    return fail(ATTN_ERR_UNSUPPORTED, fmt("head_dim %lld / head_dim_v %lld are not supported for this dtype "
+                                          "(bf16: 32/32, 64/64, 128/128, 128/64; f32: 32/32, 64/64, 64/32)",
+                                          D, Dv));
   if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (p->window_left < -1 || p->window_right < -1)
     return fail(ATTN_ERR_INVALID_ARG, "window_left and window_right must be >= -1 (-1 = unbounded)");
@@ -104,6 +105,7 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   r.Hq = p->num_q_heads;
   r.Hkv = p->num_kv_heads;
   r.D = D;
+  r.Dv = Dv;
   r.G = r.Hq / r.Hkv;
   r.delta = (int)(p->kv_pos0 - p->q_pos0);
   // A window wider than any distance between rows is the same as no window.
@@ -122,6 +124,7 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   const long long esize = r.dtype == ATTN_BF16 ? 2 : 4;
   if ((long long)r.Sq * r.Hq * D * esize > kMaxSlice || (long long)r.Skv * r.Hkv * D * esize > kMaxSlice)
     return fail(ATTN_ERR_UNSUPPORTED, fmt("one batch element of q or k/v exceeds %lld bytes", kMaxSlice));
+  // (head_dim_v <= head_dim for every supported pair, so o, dout and v are no larger.)
   r.carry_in = (p->flags & ATTN_CARRY_IN) != 0;
   r.finalize = (p->flags & ATTN_NO_FINALIZE) == 0;
   return ATTN_OK;
@@ -135,6 +138,21 @@ int check_ptr(const void* ptr, const char* name) {
 
 int xcd_groups(int B, int Hkv) { return ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0; }
 
+// dk/dv workgroups per (key tile, kv head).  With a causal (or right-window) mask and no
+// left window, the key tiles near the start of the sequence see many more query rows
+// than those near the end; when there are few workgroups (B * Hkv * key tiles well under
+// a few per CU), the longest ones set the kernel time.  Sharing a group's q heads out
+// over ns workgroups (fp32 partials, summed by a small reduction) evens this out.
+int dkdv_splits(const Problem& r) {
+  if (r.dtype != ATTN_BF16 || r.G < 2) return 1;
+  if (!(r.lo_off == -rea::kPosInf && r.hi_off < rea::kPosInf)) return 1;
+  const int bk = rea::bwd_k_tile_rows(r.dtype);
+  const long long wgs = (long long)((r.Skv + bk - 1) / bk) * r.B * r.Hkv;
+  int ns = 1;
+  while (ns < r.G && r.G % (2 * ns) == 0 && wgs * ns < 2048) ns *= 2;
+  return ns;
+}
+
 int hip_status(hipError_t e) {
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, std::string("HIP error: ") + hipGetErrorString(e));
   return ok();
@@ -145,7 +163,8 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
                float* l, void* stream) {
   if (p->struct_size != sizeof(attn_params))
     return fail(ATTN_ERR_INVALID_ARG, "params->struct_size does not match this library");
-  if (p->reserved != 0) return fail(ATTN_ERR_INVALID_ARG, "params->reserved must be 0");
+  if (p->head_dim_v != 0 && p->head_dim_v != p->head_dim)
+    return fail(ATTN_ERR_UNSUPPORTED, "sparse mode needs head_dim_v = 0 (the joint embedding)");
   if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode supports bf16 only");
   if (p->num_q_heads != 1 || p->num_kv_heads != 1)
     return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes the joint embedding: num_q_heads = num_kv_heads = 1");
@@ -220,6 +239,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.Hkv = r.Hkv;
   a.G = r.G;
   a.D = r.D;
+  a.Dv = r.Dv;
   a.delta = r.delta;
   a.lo_off = r.lo_off;
   a.hi_off = r.hi_off;
@@ -243,7 +263,9 @@ size_t attn_bwd_workspace_bytes(const attn_params* p) {
   if (!p || check_dense(p, true, r) != ATTN_OK) return 0;
   g_err = saved;
   const size_t n = (size_t)r.B * r.Hq * r.Sq * sizeof(float);
-  return 2 * align_up(n > 0 ? n : 1);
+  const int ns = dkdv_splits(r);
+  const size_t part = ns > 1 ? (size_t)ns * r.B * r.Skv * r.Hkv * (r.D + r.Dv) * sizeof(float) : 0;
+  return 2 * align_up(n > 0 ? n : 1) + (part ? align_up(part) : 0);
 }
 
 int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
@@ -291,6 +313,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.Hkv = r.Hkv;
   a.G = r.G;
   a.D = r.D;
+  a.Dv = r.Dv;
   a.delta = r.delta;
   a.lo_off = r.lo_off;
   a.hi_off = r.hi_off;
@@ -304,7 +327,9 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.n_qtiles = (r.Sq + bq - 1) / bq;
   a.n_ktiles = (r.Skv + bk - 1) / bk;
   a.xcd_groups = r.dtype == ATTN_BF16 ? xcd_groups(r.B, r.Hkv) : 0;
-  a.xcd_kv_groups = a.xcd_groups;
+  a.kv_splits = dkdv_splits(r);
+  a.xcd_kv_groups = r.dtype == ATTN_BF16 ? xcd_groups(r.B, r.Hkv * a.kv_splits) : 0;
+  a.dkv_part = a.kv_splits > 1 ? (float*)((char*)workspace + 2 * align_up(n > 0 ? n : 1)) : nullptr;
   a.stages = (do_pre ? 1 : 0) | (do_dq ? 2 : 0) | (do_dkdv ? 4 : 0);
   if ((long long)a.n_qtiles * r.B * r.Hq >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large");
   return hip_status(rea::launch_bwd(r.dtype, a, (hipStream_t)stream));

@@ -73,28 +73,36 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // dQ of tile t-1) and the VALU block (P and dS of tile t) at every barrier.
 // With fused_stats the kernel also computes D_i = rowsum(dO * O) and lse2_i from m, l
 // and stores them for the dk/dv pass.
-template <int D, int NW_>
+template <int D, int DV, int NW_>
 struct BwdQCfg {
   static constexpr int NW = NW_;                  // 8: ping-pong, one workgroup per CU; 4: two per CU
   static constexpr bool PP = NW == 8;
   static constexpr int BN = 64;
   static constexpr int NS = PP ? 3 : 2;           // stages of (K, V) tiles
-  static constexpr int KS = D / 16;
+  static constexpr int KS = D / 16;               // k-steps of S^T (over the q/k head dim)
+  static constexpr int KSV = DV / 16;             // k-steps of dP^T (over the v head dim)
   static constexpr int DB = D / 32;
-  static constexpr int DC = D / 8;
+  static constexpr int DC = D / 8;                // 16-byte chunks per Q / K / dQ row
+  static constexpr int DCV = DV / 8;              // ... per V / O / dO row
   static constexpr int P4 = DC == 4 ? 4 : (DC == 8 ? 12 : 20);    // K row pitch in a group (slots)
   static constexpr int G4 = 4 * P4 + 1;                            // K group pitch (slots)
-  static constexpr int VRS = DC + 1;                               // V row pitch (slots)
+  static constexpr int VRS = DCV + 1;                              // V row pitch (slots)
   static constexpr int KI = ((BN / 4) * G4 + 63) / 64;             // copy instructions per K tile
   static constexpr int VI = (BN * VRS + 63) / 64;
   static constexpr int NI = (KI + VI + NW - 1) / NW;
   static constexpr int STAGE = (KI + VI) * 1024;
+  // LDS: NS stages, enough room from STAGE on for each wave's 32 Q (or dO) rows in the
+  // prologue and from 0 for its 32 dQ rows (2D + 16 bytes each) in the epilogue, then the
+  // per-row D values.
+  static constexpr int cmax(int x, int y) { return x > y ? x : y; }
+  static constexpr int MAIN = cmax(cmax(NS * STAGE, STAGE + NW * 32 * 2 * D), NW * 32 * (2 * D + 16));
 };
 
-template <int D, int NW>
+template <int D, int DV, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a) {
-  using C = BwdQCfg<D, NW>;
-  __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE + C::NW * 32 * 4];
+  using C = BwdQCfg<D, DV, NW>;
+  static_assert(DV <= D, "the v head dim may not exceed the q/k head dim");
+  __shared__ __attribute__((aligned(1024))) char lds[C::MAIN + C::NW * 32 * 4];
 
   int b, hg, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.n_hg, a.Hkv, a.G >> a.gh_shift, a.xcd_groups, a.hi_off < kPosInf,
@@ -108,16 +116,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
   const int row0 = wg_row0 + 32 * (wave >> a.gh_shift);
   const int row = row0 + li;
   const bool row_ok = row < a.Sq;
-  const size_t q_rs = (size_t)a.Hq * D;
-  const uint32_t kv_rs_b = (uint32_t)a.Hkv * D * 2;
-  const size_t kv_base = ((size_t)b * a.Skv * a.Hkv + hkv) * D;
-  const uint32_t kv_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * kv_rs_b + D * 2 : 0;
-  const __bf16* kbase = (const __bf16*)a.k + kv_base;
-  const __bf16* vbase = (const __bf16*)a.v + kv_base;
+  const size_t q_rs = (size_t)a.Hq * D;            // elements between q / dq rows
+  const size_t o_rs = (size_t)a.Hq * DV;           // ... between o / dout rows
+  const uint32_t k_rs_b = (uint32_t)a.Hkv * D * 2, v_rs_b = (uint32_t)a.Hkv * DV * 2;
+  const size_t kv_row0 = (size_t)b * a.Skv * a.Hkv + hkv;
+  const uint32_t k_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * k_rs_b + D * 2 : 0;
+  const uint32_t v_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * v_rs_b + DV * 2 : 0;
+  const __bf16* kbase = (const __bf16*)a.k + kv_row0 * D;
+  const __bf16* vbase = (const __bf16*)a.v + kv_row0 * DV;
 
   // Q^T and dO^T as B operands (lane (li, lh) holds x[row][16kk + 8lh .. +7]) and the row
   // statistics; filled in the prologue below.
-  bf16x8 qreg[C::KS], doreg[C::KS];
+  bf16x8 qreg[C::KS], doreg[C::KSV];
   const size_t stat = ((size_t)b * a.Hq + hq) * a.Sq + row;
   float lse2 = INFINITY, Di = 0.f;
 
@@ -162,15 +172,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
       const int slot = 64 * (n - C::KI) + lane;
       r = slot / C::VRS;
       ch = slot - r * C::VRS;
-      ok = true;
+      ok = ch < C::DCV;
     }
     vld[i] = ok && n < C::KI + C::VI && ch < C::DC && r < C::BN;
-    voff[i] = (uint32_t)r * kv_rs_b + 16u * ch;
+    voff[i] = (uint32_t)r * (n < C::KI ? k_rs_b : v_rs_b) + 16u * ch;
   }
   auto issue = [&](int ts, int stage) {
-    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)ts * kv_rs_b);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc_at(kbase, kv_bytes, so);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc_at(vbase, kv_bytes, so);
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc_at(kbase, k_bytes, __builtin_amdgcn_readfirstlane((uint32_t)ts * k_rs_b));
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc_at(vbase, v_bytes, __builtin_amdgcn_readfirstlane((uint32_t)ts * v_rs_b));
     char* sb = lds + stage * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) {
@@ -212,7 +223,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           s[mb] = mfma32(*(const bf16x8*)(kt + mb * 8 * 16 * C::G4 + 32 * kk), qreg[kk], s[mb]);
-          dp[mb] = mfma32(*(const bf16x8*)(vt + mb * 32 * 16 * C::VRS + 32 * kk), doreg[kk], dp[mb]);
+          if (kk < C::KSV)
+            dp[mb] = mfma32(*(const bf16x8*)(vt + mb * 32 * 16 * C::VRS + 32 * kk), doreg[kk], dp[mb]);
         }
     }
     if (ds_valid) {
@@ -266,49 +278,57 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
   };
 
   // Prologue.  Q, dO (and O for D) rows are read whole, 16 lanes per row, so that every
-  // HBM access covers full cache lines: Q and then dO pass through LDS (stages 1-2) into
+  // HBM access covers full cache lines: Q and then dO pass through LDS (from stage 1 on) into
   // the operand layout; O stays in registers in the row layout for the dot product.
   int ts_c = 0, ke_c = 0, ts_p = 0, ke_p = 0;
   bool have_c = it.next(ts_c, ke_c), have_p = false;
   {
-    constexpr int RPI = 64 / C::DC;                // rows per copy instruction
-    constexpr int NQ = 32 / RPI;                   // copy instructions for 32 rows
+    // Q rows: RPI per copy instruction (DC lanes each), NQ instructions for 32 rows;
+    // dO and O rows likewise with the v head dim (RPO, NO).
+    constexpr int RPI = 64 / C::DC, NQ = 32 / RPI;
+    constexpr int RPO = 64 / C::DCV, NO = 32 / RPO;
     char* const qs = lds + C::STAGE + wave * (32 * 2 * D);
-    const uint32_t q_rs_b = (uint32_t)q_rs * 2;
-    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)row0 * q_rs_b + (uint32_t)hq * D * 2);
-    const uint32_t q_bytes = (uint32_t)a.Sq * q_rs_b;
-    const size_t batch0 = (size_t)b * a.Sq * q_rs;
+    const uint32_t q_rs_b = (uint32_t)q_rs * 2, o_rs_b = (uint32_t)o_rs * 2;
     const int rr = lane / C::DC, rc = lane % C::DC;
-    auto copy_rows = [&](const void* tensor) {
-      const __amdgpu_buffer_rsrc_t r = make_rsrc_at((const __bf16*)tensor + batch0, q_bytes, so);
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) dma16(r, qs + 1024 * i, (uint32_t)(RPI * i + rr) * q_rs_b + 16u * rc);
+    const int orr = lane / C::DCV, orc = lane % C::DCV;
+    auto rsrc_rows = [&](const void* tensor, size_t rs) {
+      const uint32_t rs_b = (uint32_t)rs * 2;
+      const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)row0 * rs_b + (uint32_t)(rs / a.Hq) * hq * 2);
+      return make_rsrc_at((const __bf16*)tensor + (size_t)b * a.Sq * rs, (uint32_t)a.Sq * rs_b, so);
     };
     const bool fused = a.fused_stats != 0;
-    u32x4 orow[NQ];                                // O: row RPI*i + lane/DC, chunk lane%DC
+    u32x4 orow[NO];                                // O: row RPO*i + lane/DCV, chunk lane%DCV
     if (fused) {
-      const __amdgpu_buffer_rsrc_t ro = make_rsrc_at((const __bf16*)a.o + batch0, q_bytes, so);
+      const __amdgpu_buffer_rsrc_t ro = rsrc_rows(a.o, o_rs);
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) orow[i] = buf_load16(ro, (uint32_t)(RPI * i + rr) * q_rs_b + 16u * rc, 0);
+      for (int i = 0; i < NO; ++i) orow[i] = buf_load16(ro, (uint32_t)(RPO * i + orr) * o_rs_b + 16u * orc, 0);
     }
-    copy_rows(a.q);
+    {
+      const __amdgpu_buffer_rsrc_t rq = rsrc_rows(a.q, q_rs);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) dma16(rq, qs + 1024 * i, (uint32_t)(RPI * i + rr) * q_rs_b + 16u * rc);
+    }
     if (have_c) issue(ts_c, 0);
     wait_vmcnt0();
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) qreg[kk] = *(const bf16x8*)(qs + li * (2 * D) + 32 * kk + 16 * lh);
     __syncthreads();                               // (this wave's rows only, but keep the copies ordered)
-    copy_rows(a.dout);
+    {
+      const __amdgpu_buffer_rsrc_t rg = rsrc_rows(a.dout, o_rs);
+#pragma unroll
+      for (int i = 0; i < NO; ++i) dma16(rg, qs + 1024 * i, (uint32_t)(RPO * i + orr) * o_rs_b + 16u * orc);
+    }
     wait_vmcnt0();
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk) doreg[kk] = *(const bf16x8*)(qs + li * (2 * D) + 32 * kk + 16 * lh);
+    for (int kk = 0; kk < C::KSV; ++kk) doreg[kk] = *(const bf16x8*)(qs + li * (2 * DV) + 32 * kk + 16 * lh);
     if (fused) {
-      // D_i = sum_d dO[i][d] O[i][d] over the DC lanes holding row i, then moved to lane i.
-      float* const sd = (float*)(lds + C::NS * C::STAGE) + wave * 32;
+      // D_i = sum_d dO[i][d] O[i][d] over the DCV lanes holding row i, then moved to lane i.
+      float* const sd = (float*)(lds + C::MAIN) + wave * 32;
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const u32x4 gu = *(const u32x4*)(qs + (RPI * i + rr) * (2 * D) + 16 * rc);
+      for (int i = 0; i < NO; ++i) {
+        const u32x4 gu = *(const u32x4*)(qs + (RPO * i + orr) * (2 * DV) + 16 * orc);
         float part = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -316,8 +336,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
           part = fmaf(bf16_hi(orow[i][w]), bf16_hi(gu[w]), part);
         }
 #pragma unroll
-        for (int off = C::DC / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
-        if (rc == 0) sd[RPI * i + rr] = part;
+        for (int off = C::DCV / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+        if (orc == 0) sd[RPO * i + orr] = part;
       }
       Di = sd[li];
       const float l = row_ok ? a.l[stat] : 0.f, m = row_ok ? a.m[stat] : 0.f;
@@ -331,7 +351,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
       Di = a.Dvec[stat];
     }
     if (!row_ok) Di = 0.f;
-    __syncthreads();                               // stages 1-2 are refilled from step 0 on
+    __syncthreads();                               // stage 1 on is refilled from step 0 on
   }
   if constexpr (!C::PP) {
     // 4 waves, one per SIMD (the other workgroup on the CU supplies the second wave):
@@ -414,44 +434,56 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
 //   S = Q K^T, dP = dO V^T (A operands: row-major Q, dO tiles; B: K, V in registers),
 //   P = exp2(S scale log2e - lse2_i), dS = P (dP - D_i),
 //   dV^T += dO^T P, dK^T += Q^T dS with transposed dO / Q operands via ds_read_b64_tr_b16.
-template <int D>
+template <int D, int DV>
 struct BwdKVCfg {
   static constexpr int BK = 128;                  // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 32;                   // query rows per step
-  static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
-  using QL = TileLayout<D, kBothRead>;            // Q, dO tiles: row operands and transposed
-  using VL = TileLayout<D, kRowRead>;             // V tile: row operands
-  static constexpr int DC = D / 8;
-  static constexpr int NCH = BQ * DC;             // 16-byte chunks per tensor per step
-  static constexpr int CPT = (NCH + 255) / 256;   // chunks per thread
-  static constexpr int VCPT = BK * DC / 256;      // 16-byte chunks of the V tile per thread
+  static constexpr int KS = D / 16;               // k-steps of S (q/k head dim)
+  static constexpr int KSV = DV / 16;             // k-steps of dP (v head dim)
+  static constexpr int DB = D / 32;               // 32-column blocks of dK
+  static constexpr int DBV = DV / 32;             // ... of dV
+  using QL = TileLayout<D, kBothRead>;            // Q tile: row operands and transposed
+  using GL = TileLayout<DV, kBothRead>;           // dO tile: the same with the v head dim
+  using VL = TileLayout<DV, kRowRead>;            // V tile: row operands
+  static constexpr int DC = D / 8, DCV = DV / 8;  // 16-byte chunks per Q / dO row
+  static constexpr int NCH = BQ * DC;             // 16-byte chunks of Q per step
+  static constexpr int NCHV = BQ * DCV;           // ... of dO
+  static constexpr int CPT = (NCH + 255) / 256;   // Q chunks per thread
+  static constexpr int CPTV = (NCHV + 255) / 256; // dO chunks per thread
+  static constexpr int VCPT = BK * DCV / 256;     // 16-byte chunks of the V tile per thread
 };
 
-template <int D>
+template <int D, int DV>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
-  using C = BwdKVCfg<D>;
+  using C = BwdKVCfg<D, DV>;
+  static_assert(DV <= D, "the v head dim may not exceed the q/k head dim");
   __shared__ __attribute__((aligned(16))) __bf16 sQ[2][C::QL::elems(C::BQ)];
-  __shared__ __attribute__((aligned(16))) __bf16 sG[2][C::QL::elems(C::BQ)];
+  __shared__ __attribute__((aligned(16))) __bf16 sG[2][C::GL::elems(C::BQ)];
   __shared__ __attribute__((aligned(16))) __bf16 sVk[C::VL::elems(C::BK)];   // this workgroup's V rows
   __shared__ __attribute__((aligned(16))) float sLse[2][C::BQ];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BQ];
 
-  int b, hkv, kt;
-  map_kv_task(blockIdx.x, a.n_ktiles, a.B, a.Hkv, a.xcd_kv_groups, false, b, hkv, kt);
+  // Workgroup id -> (batch, kv head, key tile) and the split: with kv_splits = ns > 1 the
+  // G q heads of the group are shared out over ns workgroups (G / ns heads each), which
+  // write fp32 partial dk, dv that bwd_dkdv_reduce_kernel sums.
+  int b, hv, kt;
+  map_kv_task(blockIdx.x, a.n_ktiles, a.B, a.Hkv * a.kv_splits, a.xcd_kv_groups, false, b, hv, kt);
+  const int hkv = hv / a.kv_splits, split = hv - hkv * a.kv_splits;
+  const int g_per = a.G / a.kv_splits;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int k0 = kt * C::BK;
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + li;
   const bool key_ok = key < a.Skv;
-  const size_t kv_rs = (size_t)a.Hkv * D;
-  const uint32_t q_rs_b = (uint32_t)a.Hq * D * 2;
-  const size_t koff = ((size_t)b * a.Skv + key) * kv_rs + (size_t)hkv * D;
-  const size_t q_base = (size_t)b * a.Sq * a.Hq * D;
+  const size_t k_rs = (size_t)a.Hkv * D, v_rs = (size_t)a.Hkv * DV;
+  const uint32_t q_rs_b = (uint32_t)a.Hq * D * 2, g_rs_b = (uint32_t)a.Hq * DV * 2;
+  const size_t koff = ((size_t)b * a.Skv + key) * k_rs + (size_t)hkv * D;
+  const size_t voff = ((size_t)b * a.Skv + key) * v_rs + (size_t)hkv * DV;
   const uint32_t q_bytes = a.Sq > 0 ? (uint32_t)a.Sq * q_rs_b : 0;
-  const __bf16* qbase = (const __bf16*)a.q + q_base;
-  const __bf16* gbase = (const __bf16*)a.dout + q_base;
+  const uint32_t g_bytes = a.Sq > 0 ? (uint32_t)a.Sq * g_rs_b : 0;
+  const __bf16* qbase = (const __bf16*)a.q + (size_t)b * a.Sq * a.Hq * D;
+  const __bf16* gbase = (const __bf16*)a.dout + (size_t)b * a.Sq * a.Hq * DV;
 
   // K stays in registers (B operand of S = Q K^T); V goes to LDS once (B operand of
   // dP = dO V^T, re-read every step) to keep the register count within two waves per SIMD.
@@ -463,25 +495,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     kreg[kk] = as_bf16x8(u);
   }
   {
-    const uint32_t kv_rs_b = (uint32_t)kv_rs * 2;
-    const size_t v_base = ((size_t)b * a.Skv + k0) * kv_rs + (size_t)hkv * D;
+    const uint32_t v_rs_b = (uint32_t)v_rs * 2;
+    const size_t v_base = ((size_t)b * a.Skv + k0) * v_rs + (size_t)hkv * DV;
     const int rows = min(C::BK, a.Skv - k0);
     const __amdgpu_buffer_rsrc_t rvk =
-        make_rsrc((const __bf16*)a.v + v_base, (uint32_t)(rows - 1) * kv_rs_b + D * 2);
+        make_rsrc((const __bf16*)a.v + v_base, (uint32_t)(rows - 1) * v_rs_b + DV * 2);
 #pragma unroll
     for (int u = 0; u < C::VCPT; ++u) {
-      const int c = tid + 256 * u, r = c / C::DC, ch = c % C::DC;
-      *(u32x4*)&sVk[C::VL::idx(r, 8 * ch)] = buf_load16(rvk, (uint32_t)r * kv_rs_b + 16u * ch, 0);
+      const int c = tid + 256 * u, r = c / C::DCV, ch = c % C::DCV;
+      *(u32x4*)&sVk[C::VL::idx(r, 8 * ch)] = buf_load16(rvk, (uint32_t)r * v_rs_b + 16u * ch, 0);
     }
   }
-  f32x16 dk[C::DB], dv[C::DB];
+  f32x16 dk[C::DB], dv[C::DBV];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[db][r] = 0.f;
-      dv[db][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) dk[db][r] = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::DBV; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[db][r] = 0.f;
 
   // Rows that can see some key of this workgroup: i in [j + delta - hi_off, j + delta - lo_off].
   const int k_last = min(k0 + C::BK, a.Skv) - 1;
@@ -492,10 +525,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int nqvb = a.n_qvblocks;
   if (diag >= nqvb) diag = nqvb - 1;
   QueryTileIter<C::BQ> qit;
-  int hh = 0;
+  int hh = split * g_per;
+  const int hh_end = hh + g_per;
   qit.init(nqvb, a.q_vblock, diag, ilo, ihi);
   auto next_step = [&](int& hq_o, int& qs, int& rend) -> bool {
-    while (hh < a.G) {
+    while (hh < hh_end) {
       if (qit.next(qs, rend)) {
         hq_o = hkv * a.G + hh;
         return true;
@@ -509,25 +543,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const bool wave_on = kw0 < a.Skv;
   const int w_klast = kw0 + 31;
 
-  u32x4 qbuf[C::CPT], gbuf[C::CPT];
-  uint32_t goff[C::CPT];
-  int loff[C::CPT];
+  u32x4 qbuf[C::CPT], gbuf[C::CPTV];
+  uint32_t qgo[C::CPT], ggo[C::CPTV];              // global byte offsets within a step's rows
+  int qlo[C::CPT], glo[C::CPTV];                   // LDS element offsets
 #pragma unroll
   for (int u = 0; u < C::CPT; ++u) {
     const int c = min(tid + 256 * u, C::NCH - 1), i = c / C::DC, ch = c % C::DC;
-    goff[u] = (uint32_t)i * q_rs_b + 16u * ch;
-    loff[u] = C::QL::idx(i, 8 * ch);
+    qgo[u] = (uint32_t)i * q_rs_b + 16u * ch;
+    qlo[u] = C::QL::idx(i, 8 * ch);
+  }
+#pragma unroll
+  for (int u = 0; u < C::CPTV; ++u) {
+    const int c = min(tid + 256 * u, C::NCHV - 1), i = c / C::DCV, ch = c % C::DCV;
+    ggo[u] = (uint32_t)i * g_rs_b + 16u * ch;
+    glo[u] = C::GL::idx(i, 8 * ch);
   }
   float lbuf = 0.f;
   auto load_step = [&](int hq_, int qs) {
-    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)qs * q_rs_b + (uint32_t)hq_ * D * 2);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc_at(qbase, q_bytes, so);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc_at(gbase, q_bytes, so);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc_at(
+        qbase, q_bytes, __builtin_amdgcn_readfirstlane((uint32_t)qs * q_rs_b + (uint32_t)hq_ * D * 2));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc_at(
+        gbase, g_bytes, __builtin_amdgcn_readfirstlane((uint32_t)qs * g_rs_b + (uint32_t)hq_ * DV * 2));
 #pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      qbuf[u] = buf_load16(rq, goff[u], 0);
-      gbuf[u] = buf_load16(rg, goff[u], 0);
-    }
+    for (int u = 0; u < C::CPT; ++u) qbuf[u] = buf_load16(rq, qgo[u], 0);
+#pragma unroll
+    for (int u = 0; u < C::CPTV; ++u) gbuf[u] = buf_load16(rg, ggo[u], 0);
     if (tid < 2 * C::BQ) {
       const int i = tid & (C::BQ - 1), row = qs + i;
       const size_t st = ((size_t)b * a.Hq + hq_) * a.Sq + row;
@@ -536,18 +576,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   };
   auto store_step = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      if (tid + 256 * u < C::NCH) {
-        *(u32x4*)&sQ[buf][loff[u]] = qbuf[u];
-        *(u32x4*)&sG[buf][loff[u]] = gbuf[u];
-      }
-    }
+    for (int u = 0; u < C::CPT; ++u)
+      if (tid + 256 * u < C::NCH) *(u32x4*)&sQ[buf][qlo[u]] = qbuf[u];
+#pragma unroll
+    for (int u = 0; u < C::CPTV; ++u)
+      if (tid + 256 * u < C::NCHV) *(u32x4*)&sG[buf][glo[u]] = gbuf[u];
     if (tid < C::BQ) sLse[buf][tid] = lbuf;
     else if (tid < 2 * C::BQ) sD[buf][tid - C::BQ] = lbuf;
   };
   const int tg = lane >> 4, tj = lane & 15;
   const int tr_off = C::QL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
+  const int gtr_off = C::GL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
   const int q_off = C::QL::idx(li, 8 * lh);
+  const int g_off = C::GL::idx(li, 8 * lh);
   const int v_off = C::VL::idx(wave * 32 + li, 8 * lh);
 
   int hq = 0, qs = 0, rend = 0;
@@ -580,9 +621,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk) {
-        const bf16x8 vb = *(const bf16x8*)&sVk[v_off + 16 * kk];
         s = mfma32(*(const bf16x8*)&qt_[q_off + 16 * kk], kreg[kk], s);
-        dp = mfma32(*(const bf16x8*)&gt_[q_off + 16 * kk], vb, dp);
+        if (kk < C::KSV) {
+          const bf16x8 vb = *(const bf16x8*)&sVk[v_off + 16 * kk];
+          dp = mfma32(*(const bf16x8*)&gt_[g_off + 16 * kk], vb, dp);
+        }
       }
       if (!full) {
         cold_path();
@@ -621,10 +664,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         const bf16x8 pbf = as_bf16x8(pb), sbf = as_bf16x8(sb);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
+          if (db < C::DBV) {
+            const int o0 = gtr_off + C::GL::rows(16 * ks) + 32 * db, o1 = o0 + C::GL::rows(8);
+            const bf16x8 ga = join_bf16x8(lds_read_tr16(&gt_[o0]), lds_read_tr16(&gt_[o1]));
+            dv[db] = mfma32(ga, pbf, dv[db]);
+          }
           const int o0 = tr_off + C::QL::rows(16 * ks) + 32 * db, o1 = o0 + C::QL::rows(8);
-          const bf16x8 ga = join_bf16x8(lds_read_tr16(&gt_[o0]), lds_read_tr16(&gt_[o1]));
           const bf16x8 qa = join_bf16x8(lds_read_tr16(&qt_[o0]), lds_read_tr16(&qt_[o1]));
-          dv[db] = mfma32(ga, pbf, dv[db]);
           dk[db] = mfma32(qa, sbf, dk[db]);
         }
       }
@@ -638,47 +684,101 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     have = nhave;
   }
 
-  if (key_ok) {
-    __bf16* kop = (__bf16*)a.dk + koff;
-    __bf16* vop = (__bf16*)a.dv + koff;
+  if (key_ok && a.kv_splits > 1) {
+    // fp32 partials of this split: [ns, B, Skv, Hkv, D] then [ns, B, Skv, Hkv, Dv]
+    const size_t nk = (size_t)a.B * a.Skv * k_rs, nv = (size_t)a.B * a.Skv * v_rs;
+    float* pk = a.dkv_part + split * nk + koff;
+    float* pv = a.dkv_part + a.kv_splits * nk + split * nv + voff;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 wk, wv;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = dk[db][4 * g + e] * a.scale;
+        *(f32x4*)(pk + 32 * db + 8 * g + 4 * lh) = w;
+      }
+#pragma unroll
+    for (int db = 0; db < C::DBV; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = dv[db][4 * g + e];
+        *(f32x4*)(pv + 32 * db + 8 * g + 4 * lh) = w;
+      }
+  } else if (key_ok) {
+    __bf16* kop = (__bf16*)a.dk + koff;
+    __bf16* vop = (__bf16*)a.dv + voff;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 wk;
         wk[0] = pack_bf16x2(dk[db][4 * g] * a.scale, dk[db][4 * g + 1] * a.scale);
         wk[1] = pack_bf16x2(dk[db][4 * g + 2] * a.scale, dk[db][4 * g + 3] * a.scale);
+        *(u32x2*)(kop + 32 * db + 8 * g + 4 * lh) = wk;
+      }
+#pragma unroll
+    for (int db = 0; db < C::DBV; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 wv;
         wv[0] = pack_bf16x2(dv[db][4 * g], dv[db][4 * g + 1]);
         wv[1] = pack_bf16x2(dv[db][4 * g + 2], dv[db][4 * g + 3]);
-        *(u32x2*)(kop + 32 * db + 8 * g + 4 * lh) = wk;
         *(u32x2*)(vop + 32 * db + 8 * g + 4 * lh) = wv;
       }
   }
 }
 
+// Sum of the kv_splits fp32 partials of dk (n_k elements) and dv (n_v elements), in split
+// order (so the result is bitwise reproducible), rounded once to bf16.  4 elements per
+// thread; n_k and n_v are multiples of 4 (head dims are multiples of 32).
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* part, int ns, long long n_k,
+                                                              long long n_v, __bf16* dk, __bf16* dv) {
+  const long long i = 4 * ((long long)blockIdx.x * 256 + threadIdx.x);
+  if (i >= n_k + n_v) return;
+  const bool is_k = i < n_k;
+  const float* src = is_k ? part + i : part + ns * n_k + (i - n_k);
+  const long long stride = is_k ? n_k : n_v;
+  f32x4 s = *(const f32x4*)src;
+  for (int j = 1; j < ns; ++j) {
+    const f32x4 t = *(const f32x4*)(src + j * stride);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += t[e];
+  }
+  u32x2 w;
+  w[0] = pack_bf16x2(s[0], s[1]);
+  w[1] = pack_bf16x2(s[2], s[3]);
+  *(u32x2*)(is_k ? dk + i : dv + (i - n_k)) = w;
+}
+
 // ------------------------------------------------------------------ fp32 path
 // Plain fp32 kernels (small head dims): one thread per query row for dq, one thread
 // per key row for dk/dv; tiles of the other side staged in LDS.
-template <int D>
+template <int D, int DV>
 __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
   constexpr int BM = 128, BN = 32;
-  __shared__ float sK[BN][D + 1], sV[BN][D + 1];
+  __shared__ float sK[BN][D + 1], sV[BN][DV + 1];
   int b, hq, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, 0, false, b, hq, qt);
   const int hkv = hq / a.G, tid = threadIdx.x;
   const int row = qt * BM + tid;
   const bool row_ok = row < a.Sq;
-  const size_t q_rs = (size_t)a.Hq * D, kv_rs = (size_t)a.Hkv * D;
+  const size_t q_rs = (size_t)a.Hq * D, k_rs = (size_t)a.Hkv * D;
+  const size_t o_rs = (size_t)a.Hq * DV, v_rs = (size_t)a.Hkv * DV;
   const size_t qoff = ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D;
-  const float* kp = (const float*)a.k + (size_t)b * a.Skv * kv_rs + (size_t)hkv * D;
-  const float* vp = (const float*)a.v + (size_t)b * a.Skv * kv_rs + (size_t)hkv * D;
-  float qr[D], gr[D], acc[D];
+  const size_t goff = ((size_t)b * a.Sq + row) * o_rs + (size_t)hq * DV;
+  const float* kp = (const float*)a.k + (size_t)b * a.Skv * k_rs + (size_t)hkv * D;
+  const float* vp = (const float*)a.v + (size_t)b * a.Skv * v_rs + (size_t)hkv * DV;
+  float qr[D], gr[DV], acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     qr[d] = row_ok ? ((const float*)a.q)[qoff + d] : 0.f;
-    gr[d] = row_ok ? ((const float*)a.dout)[qoff + d] : 0.f;
     acc[d] = 0.f;
   }
+#pragma unroll
+  for (int d = 0; d < DV; ++d) gr[d] = row_ok ? ((const float*)a.dout)[goff + d] : 0.f;
   const size_t stat = ((size_t)b * a.Hq + hq) * a.Sq + row;
   const float lse2 = row_ok ? a.lse2[stat] : INFINITY;
   const float Di = row_ok ? a.Dvec[stat] : 0.f;
@@ -696,8 +796,11 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
     const int tend = min(kend, a.Skv);
     for (int c = tid; c < BN * D; c += BM) {
       const int r = c / D, d = c % D, j = ts + r;
-      sK[r][d] = j < a.Skv ? kp[(size_t)j * kv_rs + d] : 0.f;
-      sV[r][d] = j < a.Skv ? vp[(size_t)j * kv_rs + d] : 0.f;
+      sK[r][d] = j < a.Skv ? kp[(size_t)j * k_rs + d] : 0.f;
+    }
+    for (int c = tid; c < BN * DV; c += BM) {
+      const int r = c / DV, d = c % DV, j = ts + r;
+      sV[r][d] = j < a.Skv ? vp[(size_t)j * v_rs + d] : 0.f;
     }
     __syncthreads();
     for (int r = 0; r < BN; ++r) {
@@ -705,10 +808,9 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
       if (j < my_jmin || j > my_jmax || j >= tend) continue;
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        s = fmaf(qr[d], sK[r][d], s);
-        dp = fmaf(gr[d], sV[r][d], dp);
-      }
+      for (int d = 0; d < D; ++d) s = fmaf(qr[d], sK[r][d], s);
+#pragma unroll
+      for (int d = 0; d < DV; ++d) dp = fmaf(gr[d], sV[r][d], dp);
       const float p = fast_exp2(fmaf(s, a.scale_log2, -lse2));
       const float ds = p * (dp - Di);
 #pragma unroll
@@ -723,23 +825,28 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
   }
 }
 
-template <int D>
+template <int D, int DV>
 __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
   constexpr int BK = 128, BQ = 32;
-  __shared__ float sQ[BQ][D + 1], sG[BQ][D + 1], sL[BQ], sDv[BQ];
+  __shared__ float sQ[BQ][D + 1], sG[BQ][DV + 1], sL[BQ], sDv[BQ];
   int b, hkv, kt;
   map_kv_task(blockIdx.x, a.n_ktiles, a.B, a.Hkv, 0, false, b, hkv, kt);
   const int tid = threadIdx.x;
   const int key = kt * BK + tid;
   const bool key_ok = key < a.Skv;
-  const size_t q_rs = (size_t)a.Hq * D, kv_rs = (size_t)a.Hkv * D;
-  const size_t koff = ((size_t)b * a.Skv + key) * kv_rs + (size_t)hkv * D;
-  float kr[D], vr[D], dk[D], dv[D];
+  const size_t q_rs = (size_t)a.Hq * D, k_rs = (size_t)a.Hkv * D;
+  const size_t o_rs = (size_t)a.Hq * DV, v_rs = (size_t)a.Hkv * DV;
+  const size_t koff = ((size_t)b * a.Skv + key) * k_rs + (size_t)hkv * D;
+  const size_t voff = ((size_t)b * a.Skv + key) * v_rs + (size_t)hkv * DV;
+  float kr[D], vr[DV], dk[D], dv[DV];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     kr[d] = key_ok ? ((const float*)a.k)[koff + d] : 0.f;
-    vr[d] = key_ok ? ((const float*)a.v)[koff + d] : 0.f;
     dk[d] = 0.f;
+  }
+#pragma unroll
+  for (int d = 0; d < DV; ++d) {
+    vr[d] = key_ok ? ((const float*)a.v)[voff + d] : 0.f;
     dv[d] = 0.f;
   }
   const int k0 = kt * BK, k_last = min(k0 + BK, a.Skv) - 1;
@@ -752,7 +859,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
   for (int hh = 0; hh < a.G; ++hh) {
     const int hq = hkv * a.G + hh;
     const float* qp = (const float*)a.q + (size_t)b * a.Sq * q_rs + (size_t)hq * D;
-    const float* gp = (const float*)a.dout + (size_t)b * a.Sq * q_rs + (size_t)hq * D;
+    const float* gp = (const float*)a.dout + (size_t)b * a.Sq * o_rs + (size_t)hq * DV;
     QueryTileIter<BQ> qit;
     qit.init(nqvb, a.q_vblock, diag, ilo, ihi);
     int qs, rend;
@@ -761,7 +868,10 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
       for (int c = tid; c < BQ * D; c += BK) {
         const int r = c / D, d = c % D, row = qs + r;
         sQ[r][d] = row < a.Sq ? qp[(size_t)row * q_rs + d] : 0.f;
-        sG[r][d] = row < a.Sq ? gp[(size_t)row * q_rs + d] : 0.f;
+      }
+      for (int c = tid; c < BQ * DV; c += BK) {
+        const int r = c / DV, d = c % DV, row = qs + r;
+        sG[r][d] = row < a.Sq ? gp[(size_t)row * o_rs + d] : 0.f;
       }
       if (tid < BQ) {
         const int row = qs + tid;
@@ -776,33 +886,30 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
         if (i >= qe || dd < a.lo_off || dd > a.hi_off) continue;
         float s = 0.f, dp = 0.f;
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-          s = fmaf(sQ[r][d], kr[d], s);
-          dp = fmaf(sG[r][d], vr[d], dp);
-        }
+        for (int d = 0; d < D; ++d) s = fmaf(sQ[r][d], kr[d], s);
+#pragma unroll
+        for (int d = 0; d < DV; ++d) dp = fmaf(sG[r][d], vr[d], dp);
         const float p = fast_exp2(fmaf(s, a.scale_log2, -sL[r]));
         const float ds = p * (dp - sDv[r]);
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-          dk[d] = fmaf(ds, sQ[r][d], dk[d]);
-          dv[d] = fmaf(p, sG[r][d], dv[d]);
-        }
+        for (int d = 0; d < D; ++d) dk[d] = fmaf(ds, sQ[r][d], dk[d]);
+#pragma unroll
+        for (int d = 0; d < DV; ++d) dv[d] = fmaf(p, sG[r][d], dv[d]);
       }
       __syncthreads();
     }
   }
   if (key_ok) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      ((float*)a.dk)[koff + d] = dk[d] * a.scale;
-      ((float*)a.dv)[koff + d] = dv[d];
-    }
+    for (int d = 0; d < D; ++d) ((float*)a.dk)[koff + d] = dk[d] * a.scale;
+#pragma unroll
+    for (int d = 0; d < DV; ++d) ((float*)a.dv)[voff + d] = dv[d];
   }
 }
 
 // Smallest number of query rows a dq workgroup covers (for the host-side size checks).
 int bwd_q_tile_rows(int dtype) { return dtype == 0 ? 32 : 128; }
-int bwd_k_tile_rows(int dtype) { return dtype == 0 ? BwdKVCfg<128>::BK : 128; }
+int bwd_k_tile_rows(int dtype) { return dtype == 0 ? BwdKVCfg<128, 128>::BK : 128; }
 
 template <typename T, int D>
 static void launch_pre(const BwdArgs& a, hipStream_t stream) {
@@ -839,37 +946,54 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
     gq = dim3((unsigned)a.n_qtiles * a.B * a.n_hg);
     bq = dim3(64 * nw);
   }
-  const dim3 gk((unsigned)a.n_ktiles * a.B * a.Hkv), bk(dtype == 0 ? 256 : 128);
+  const dim3 gk((unsigned)a.n_ktiles * a.B * a.Hkv * a.kv_splits), bk(dtype == 0 ? 256 : 128);
   const bool has_q = gq.x > 0, has_k = gk.x > 0;
   const bool want_pre = has_q && (a.stages & 1), dq = has_q && (a.stages & 2), dkdv = has_k && (a.stages & 4);
   // The bf16 dq kernel computes D and the LSE itself when they are needed.
   a.fused_stats = (dtype == 0 && want_pre && dq) ? 1 : 0;
   const bool pre = want_pre && !a.fused_stats;
-#define REA_BWD(T, DD, DQ_LAUNCH, DKV)                                           \
+  // D and the LSE: rows of o and dout have the v head dim.
+#define REA_BWD(T, DD, DDV, DQ_LAUNCH, DKV)                                       \
   do {                                                                          \
-    if (pre) launch_pre<T, DD>(a, stream);                                      \
+    if (pre) launch_pre<T, DDV>(a, stream);                                     \
     if (dq) DQ_LAUNCH;                                                          \
-    if (dkdv) hipLaunchKernelGGL(DKV<DD>, gk, bk, 0, stream, a);                \
+    if (dkdv) {                                                                 \
+      hipLaunchKernelGGL((DKV<DD, DDV>), gk, bk, 0, stream, a);                 \
+      if (a.kv_splits > 1) {                                                    \
+        const long long nk = (long long)a.B * a.Skv * a.Hkv * a.D;              \
+        const long long nv = (long long)a.B * a.Skv * a.Hkv * a.Dv;             \
+        const unsigned blocks = (unsigned)((nk + nv + 1023) / 1024);            \
+        hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3(blocks), dim3(256), 0,  \
+                           stream, a.dkv_part, a.kv_splits, nk, nv,             \
+                           (__bf16*)a.dk, (__bf16*)a.dv);                       \
+      }                                                                         \
+    }                                                                           \
   } while (0)
-#define REA_DQ_BF16(DD)                                                          \
+#define REA_DQ_BF16(DD, DDV)                                                     \
   do {                                                                          \
-    if (w4) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, 4>), gq, bq, 0, stream, a); \
-    else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, 8>), gq, bq, 0, stream, a);    \
+    if (w4) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 4>), gq, bq, 0, stream, a); \
+    else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 8>), gq, bq, 0, stream, a);    \
   } while (0)
+#define REA_DQ_F32(DD, DDV) hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, DDV>), gq, bq, 0, stream, a)
+  if (!head_dims_supported(dtype, a.D, a.Dv)) return hipErrorInvalidValue;
+  const int dd = a.D * 1000 + a.Dv;
   if (dtype == 0) {
-    switch (a.D) {
-      case 32: REA_BWD(__bf16, 32, REA_DQ_BF16(32), bwd_dkdv_bf16_kernel); break;
-      case 64: REA_BWD(__bf16, 64, REA_DQ_BF16(64), bwd_dkdv_bf16_kernel); break;
-      case 128: REA_BWD(__bf16, 128, REA_DQ_BF16(128), bwd_dkdv_bf16_kernel); break;
+    switch (dd) {
+      case 32032: REA_BWD(__bf16, 32, 32, REA_DQ_BF16(32, 32), bwd_dkdv_bf16_kernel); break;
+      case 64064: REA_BWD(__bf16, 64, 64, REA_DQ_BF16(64, 64), bwd_dkdv_bf16_kernel); break;
+      case 128128: REA_BWD(__bf16, 128, 128, REA_DQ_BF16(128, 128), bwd_dkdv_bf16_kernel); break;
+      case 128064: REA_BWD(__bf16, 128, 64, REA_DQ_BF16(128, 64), bwd_dkdv_bf16_kernel); break;
       default: return hipErrorInvalidValue;
     }
   } else {
-    switch (a.D) {
-      case 32: REA_BWD(float, 32, hipLaunchKernelGGL(bwd_dq_f32_kernel<32>, gq, bq, 0, stream, a), bwd_dkdv_f32_kernel); break;
-      case 64: REA_BWD(float, 64, hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, gq, bq, 0, stream, a), bwd_dkdv_f32_kernel); break;
+    switch (dd) {
+      case 32032: REA_BWD(float, 32, 32, REA_DQ_F32(32, 32), bwd_dkdv_f32_kernel); break;
+      case 64064: REA_BWD(float, 64, 64, REA_DQ_F32(64, 64), bwd_dkdv_f32_kernel); break;
+      case 64032: REA_BWD(float, 64, 32, REA_DQ_F32(64, 32), bwd_dkdv_f32_kernel); break;
       default: return hipErrorInvalidValue;
     }
   }
+#undef REA_DQ_F32
 #undef REA_DQ_BF16
 #undef REA_BWD
   return hipGetLastError();

@@ -32,6 +32,7 @@ struct FwdArgs {
   float* l;
   float* acc;
   int B, Sq, Skv, Hq, Hkv, G, D;
+  int Dv;             // head dim of v and o (may differ from D, the q/k head dim)
   // Visibility of (row i, key j): lo_off <= (j - i) + delta <= hi_off, with
   // delta = kv_pos0 - q_pos0 and j < Skv.
   int delta;
@@ -65,13 +66,17 @@ struct BwdArgs {
   float* Dvec;        // [B, Hq, Sq] workspace: rowsum(dO * o)
   float* lse2;        // [B, Hq, Sq] workspace: m*log2(e) + log2(l)  (log2 units)
   int B, Sq, Skv, Hq, Hkv, G, D;
+  int Dv;             // head dim of v, o, dout, dv
   int delta, lo_off, hi_off;
   float scale, scale_log2;
   int kv_block, n_vblocks;     // virtual key blocks (ring order of the dq pass)
   int q_vblock, n_qvblocks;    // virtual query blocks (ring order of the dk/dv pass)
   int n_qtiles, n_ktiles;      // grid sizes: query tiles (dq), key tiles (dk/dv)
   int xcd_groups;              // (B*Hkv)/8 for the XCD-aware dq order, else 0
-  int xcd_kv_groups;           // same for the dk/dv grid
+  int xcd_kv_groups;           // same for the dk/dv grid (over B * Hkv * kv_splits)
+  int kv_splits;               // dk/dv workgroups per (key tile, kv head), each taking
+                               // G / kv_splits q heads (bf16 only; 1 = no split)
+  float* dkv_part;             // kv_splits > 1: fp32 partials [ns,B,Skv,Hkv,D] ++ [ns,B,Skv,Hkv,Dv]
   int stages;                  // bit 0: D/LSE pre-pass, bit 1: dq, bit 2: dk/dv
   // bf16 dq workgroup shape (set by the launcher), as in FwdArgs; fused_stats: the dq
   // kernel computes D and the LSE itself (and stores them for the dk/dv pass).

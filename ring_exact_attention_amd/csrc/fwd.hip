@@ -35,16 +35,17 @@
 
 namespace rea {
 
-template <int D, int NW_>
+template <int D, int DV, int NW_>
 struct FwdCfg {
   static constexpr int NW = NW_;                   // wavefronts per workgroup (8 or 4)
   static constexpr bool PP = NW == 8;              // ping-pong between the two waves of a SIMD
   static constexpr int BN = 64;                    // keys per tile
   static constexpr int KS = D / 16;                // k-steps of S^T over d
-  static constexpr int DB = D / 32;                // 32-row blocks of O^T
-  static constexpr int DC = D / 8;                 // 16-byte chunks per row
+  static constexpr int DB = DV / 32;               // 32-row blocks of O^T
+  static constexpr int DC = D / 8;                 // 16-byte chunks per Q / K row
+  static constexpr int DCV = DV / 8;               // ... per V / O row
   static constexpr int KRS = DC + 1;               // K row pitch in 16-byte slots (odd)
-  static constexpr int VRS = DC == 4 ? 4 : (DC == 8 ? 12 : 20);   // V row pitch, slots
+  static constexpr int VRS = DCV == 4 ? 4 : (DCV == 8 ? 12 : 20);   // V row pitch, slots
   static constexpr int KI = (BN * KRS + 63) / 64;  // 64-lane copy instructions per K tile
   static constexpr int VI = (BN * VRS + 63) / 64;  // ... per V tile
   static constexpr int NI = (KI + VI + NW - 1) / NW;   // per wave per tile
@@ -53,7 +54,11 @@ struct FwdCfg {
   // per CU, so at most 80 KB each): two K slots and two V slots, V copied one tile
   // behind K (K of tile t+1 and V of tile t are copied during step t).
   static constexpr int STAGE = KB + VB;
-  static constexpr int LDS = PP ? 3 * STAGE : 2 * STAGE;
+  // The prologue stages each wave's 32 Q rows (2D bytes each) from QOFF on, past what
+  // step 0's copies touch; the epilogue stages O rows (2DV + 16 bytes) from 0.
+  static constexpr int QOFF = PP ? STAGE : KB;
+  static constexpr int cmax(int x, int y) { return x > y ? x : y; }
+  static constexpr int LDS = cmax(cmax((PP ? 3 : 2) * STAGE, QOFF + NW * 32 * 2 * D), NW * 32 * (2 * DV + 16));
   static constexpr int kaddr(int slot) { return PP ? slot * STAGE : slot * KB; }
   static constexpr int vaddr(int slot) { return PP ? slot * STAGE + KB : 2 * KB + slot * VB; }
 };
@@ -61,9 +66,9 @@ struct FwdCfg {
 // Rows of the scores may grow by this much (log2 units) before the carry is rescaled.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int NW>
+template <int D, int DV, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
-  using C = FwdCfg<D, NW>;
+  using C = FwdCfg<D, DV, NW>;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
 
   int b, hg, qt;
@@ -79,12 +84,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int row = row0 + li;
   const bool row_ok = row < a.Sq;
 
-  const size_t q_rs = (size_t)a.Hq * D;
-  const uint32_t kv_rs_b = (uint32_t)a.Hkv * D * 2;           // bytes between key rows
-  const size_t kv_base = ((size_t)b * a.Skv * a.Hkv + hkv) * D;
-  const uint32_t kv_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * kv_rs_b + D * 2 : 0;
-  const __bf16* kbase = (const __bf16*)a.k + kv_base;
-  const __bf16* vbase = (const __bf16*)a.v + kv_base;
+  const size_t q_rs = (size_t)a.Hq * D;            // elements between q rows
+  const size_t o_rs = (size_t)a.Hq * DV;           // ... between o (and carry) rows
+  const uint32_t k_rs_b = (uint32_t)a.Hkv * D * 2;            // bytes between key rows
+  const uint32_t v_rs_b = (uint32_t)a.Hkv * DV * 2;           // bytes between value rows
+  const size_t kv_row0 = (size_t)b * a.Skv * a.Hkv + hkv;
+  const uint32_t k_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * k_rs_b + D * 2 : 0;
+  const uint32_t v_bytes = a.Skv > 0 ? (uint32_t)(a.Skv - 1) * v_rs_b + DV * 2 : 0;
+  const __bf16* kbase = (const __bf16*)a.k + kv_row0 * D;
+  const __bf16* vbase = (const __bf16*)a.v + kv_row0 * DV;
 
   // Q^T as B operands: lane (li, lh) holds q[row][16kk + 8lh .. +7]; loaded through LDS
   // (see the prologue) so that the HBM reads cover whole rows.
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   float m_used = -INFINITY, m_true = -INFINITY;   // log2 units of the scaled logits
   float l_part = 0.f;                              // this lane's half of the denominator
   const size_t stat = ((size_t)b * a.Hq + hq) * a.Sq + row;
-  float* accp = a.acc ? a.acc + ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D : nullptr;
+  float* accp = a.acc ? a.acc + ((size_t)b * a.Sq + row) * o_rs + (size_t)hq * DV : nullptr;
   if (a.carry_in && row_ok) {
     const float mi = a.m[stat];
     m_used = m_true = mi * kLog2e;
@@ -148,14 +156,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     const int pitch = is_k ? C::KRS : C::VRS;
     const int slot = 64 * (is_k ? n : n - C::KI) + lane;
     const int r = slot / pitch, ch = slot - r * pitch;
-    vld[i] = n < C::KI + C::VI && ch < C::DC && r < C::BN;
-    voff[i] = (uint32_t)r * kv_rs_b + 16u * ch;
+    vld[i] = n < C::KI + C::VI && ch < (is_k ? C::DC : C::DCV) && r < C::BN;
+    voff[i] = (uint32_t)r * (is_k ? k_rs_b : v_rs_b) + 16u * ch;
   }
   auto issue = [&](bool do_k, int ts_k, int sk, bool do_v, int ts_v, int sv) {
     const __amdgpu_buffer_rsrc_t rk =
-        make_rsrc_at(kbase, kv_bytes, __builtin_amdgcn_readfirstlane((uint32_t)ts_k * kv_rs_b));
+        make_rsrc_at(kbase, k_bytes, __builtin_amdgcn_readfirstlane((uint32_t)ts_k * k_rs_b));
     const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc_at(vbase, kv_bytes, __builtin_amdgcn_readfirstlane((uint32_t)ts_v * kv_rs_b));
+        make_rsrc_at(vbase, v_bytes, __builtin_amdgcn_readfirstlane((uint32_t)ts_v * v_rs_b));
     char* const kb = lds + C::kaddr(sk);
     char* const vb = lds + C::vaddr(sv) - C::KB;
 #pragma unroll
@@ -285,7 +293,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   // copy of step 0 touches and read back in the operand layout; K (and V, with 8 waves)
   // of tile 0 go to slot 0.
   constexpr int RPI = 64 / C::DC;                  // Q rows per copy instruction
-  char* const qs = lds + (C::PP ? C::STAGE : C::KB) + wave * (32 * 2 * D);
+  char* const qs = lds + C::QOFF + wave * (32 * 2 * D);
   {
     const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (uint32_t)(q_rs * 2) + (uint32_t)hq * D * 2);
     const __amdgpu_buffer_rsrc_t rq =
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     // O through LDS (this wave's 32 rows at 2D + 16 bytes, in the now idle stages; all
     // reads of the stages ended at the loop's last barrier), then stored as whole rows.
     const float inv = l_used > 0.f ? 1.f / l_used : 0.f;
-    constexpr int OP = 2 * D + 16;
+    constexpr int OP = 2 * DV + 16, RPO = 64 / C::DCV;
     char* const os = lds + wave * (32 * OP);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -368,12 +376,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
         w[1] = pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
         *(u32x2*)(os + li * OP + 2 * (32 * db + 8 * g + 4 * lh)) = w;
       }
-    __bf16* ob = (__bf16*)a.o + ((size_t)b * a.Sq + row0) * q_rs + (size_t)hq * D;
+    __bf16* ob = (__bf16*)a.o + ((size_t)b * a.Sq + row0) * o_rs + (size_t)hq * DV;
 #pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = RPI * i + lane / C::DC, ch = lane % C::DC;
+    for (int i = 0; i < 32 / RPO; ++i) {
+      const int r = RPO * i + lane / C::DCV, ch = lane % C::DCV;
       const u32x4 v = *(const u32x4*)(os + r * OP + 16 * ch);
-      if (row0 + r < a.Sq) *(u32x4*)(ob + (size_t)r * q_rs + 8 * ch) = v;
+      if (row0 + r < a.Sq) *(u32x4*)(ob + (size_t)r * o_rs + 8 * ch) = v;
     }
   }
   if (row_ok) {
@@ -399,36 +407,36 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 // A plain, exact-in-fp32 kernel for float32 inputs (small head dims): one thread per
 // query row, key tiles staged in LDS, per-tile online softmax.  Same masking,
 // ring order and carry conventions as the bf16 kernel.
-template <int D>
+template <int D, int DV>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
   constexpr int BM = 128, BN = 32;
   __shared__ float sK[BN][D + 1];
-  __shared__ float sV[BN][D + 1];
+  __shared__ float sV[BN][DV + 1];
   int b, hq, qt;
   map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, 0, false, b, hq, qt);
   const int hkv = hq / a.G;
   const int tid = threadIdx.x;
   const int row = qt * BM + tid;
   const bool row_ok = row < a.Sq;
-  const size_t q_rs = (size_t)a.Hq * D, kv_rs = (size_t)a.Hkv * D;
+  const size_t q_rs = (size_t)a.Hq * D, k_rs = (size_t)a.Hkv * D;
+  const size_t o_rs = (size_t)a.Hq * DV, v_rs = (size_t)a.Hkv * DV;
   const float* qp = (const float*)a.q + (size_t)b * a.Sq * q_rs + (size_t)hq * D;
-  const float* kp = (const float*)a.k + (size_t)b * a.Skv * kv_rs + (size_t)hkv * D;
-  const float* vp = (const float*)a.v + (size_t)b * a.Skv * kv_rs + (size_t)hkv * D;
+  const float* kp = (const float*)a.k + (size_t)b * a.Skv * k_rs + (size_t)hkv * D;
+  const float* vp = (const float*)a.v + (size_t)b * a.Skv * v_rs + (size_t)hkv * DV;
 
-  float qr[D], acc[D];
+  float qr[D], acc[DV];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    qr[d] = row_ok ? qp[(size_t)row * q_rs + d] : 0.f;
-    acc[d] = 0.f;
-  }
+  for (int d = 0; d < D; ++d) qr[d] = row_ok ? qp[(size_t)row * q_rs + d] : 0.f;
+#pragma unroll
+  for (int d = 0; d < DV; ++d) acc[d] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const size_t stat = ((size_t)b * a.Hq + hq) * a.Sq + row;
-  float* accp = a.acc ? a.acc + ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D : nullptr;
+  float* accp = a.acc ? a.acc + ((size_t)b * a.Sq + row) * o_rs + (size_t)hq * DV : nullptr;
   if (a.carry_in && row_ok) {
     m_run = a.m[stat] * kLog2e;
     l_run = a.l[stat];
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] = accp[d];
+    for (int d = 0; d < DV; ++d) acc[d] = accp[d];
   }
   const int wg_row0 = qt * BM;
   const int r_last = min(wg_row0 + BM, a.Sq) - 1;
@@ -446,8 +454,11 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
     const int tend = min(kend, a.Skv);
     for (int c = tid; c < BN * D; c += BM) {
       const int r = c / D, d = c % D, j = ts + r;
-      sK[r][d] = j < a.Skv ? kp[(size_t)j * kv_rs + d] : 0.f;
-      sV[r][d] = j < a.Skv ? vp[(size_t)j * kv_rs + d] : 0.f;
+      sK[r][d] = j < a.Skv ? kp[(size_t)j * k_rs + d] : 0.f;
+    }
+    for (int c = tid; c < BN * DV; c += BM) {
+      const int r = c / DV, d = c % DV, j = ts + r;
+      sV[r][d] = j < a.Skv ? vp[(size_t)j * v_rs + d] : 0.f;
     }
     __syncthreads();
     float s[BN];
@@ -466,13 +477,13 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
     const float alpha = fast_exp2(m_run - m_ref);
     l_run *= alpha;
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] *= alpha;
+    for (int d = 0; d < DV; ++d) acc[d] *= alpha;
 #pragma unroll
     for (int r = 0; r < BN; ++r) {
       const float p = fast_exp2(s[r] - m_ref);
       l_run += p;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, sV[r][d], acc[d]);
+      for (int d = 0; d < DV; ++d) acc[d] = fmaf(p, sV[r][d], acc[d]);
     }
     m_run = m_new;
     __syncthreads();
@@ -480,12 +491,12 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
   if (row_ok) {
     if (a.finalize) {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      float* op = (float*)a.o + ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D;
+      float* op = (float*)a.o + ((size_t)b * a.Sq + row) * o_rs + (size_t)hq * DV;
 #pragma unroll
-      for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
+      for (int d = 0; d < DV; ++d) op[d] = acc[d] * inv;
     } else {
 #pragma unroll
-      for (int d = 0; d < D; ++d) accp[d] = acc[d];
+      for (int d = 0; d < DV; ++d) accp[d] = acc[d];
     }
     a.m[stat] = m_run == -INFINITY ? -INFINITY : m_run * kLn2;
     a.l[stat] = l_run;
@@ -507,7 +518,7 @@ static bool fwd_use_w4(const FwdArgs& a) {
 #endif
 }
 
-template <int D>
+template <int D, int DV>
 static void launch_fwd_bf16(FwdArgs a, bool w4, hipStream_t stream) {
   // gh = q heads per workgroup: the largest power of two <= NW dividing the GQA group.
   const int nw = w4 ? 4 : 8, max_shift = w4 ? 2 : 3;
@@ -519,27 +530,35 @@ static void launch_fwd_bf16(FwdArgs a, bool w4, hipStream_t stream) {
   a.n_qtiles = (a.Sq + a.rows_wg - 1) / a.rows_wg;
   const dim3 grid((unsigned)a.n_qtiles * a.B * a.n_hg), block(64 * nw);
   if (w4)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 4>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, 8>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 8>), grid, block, 0, stream, a);
+}
+
+bool head_dims_supported(int dtype, int D, int Dv) {
+  if (dtype == 0) return (D == Dv && (D == 32 || D == 64 || D == 128)) || (D == 128 && Dv == 64);
+  return (D == Dv && (D == 32 || D == 64)) || (D == 64 && Dv == 32);
 }
 
 hipError_t launch_fwd(int dtype, const FwdArgs& args, hipStream_t stream) {
-  const dim3 block128(128);
+  if (!head_dims_supported(dtype, args.D, args.Dv)) return hipErrorInvalidValue;
+  const int dd = args.D * 1000 + args.Dv;
   if (dtype == 0) {
     const bool w4 = fwd_use_w4(args);
-    switch (args.D) {
-      case 32: launch_fwd_bf16<32>(args, w4, stream); break;
-      case 64: launch_fwd_bf16<64>(args, w4, stream); break;
-      case 128: launch_fwd_bf16<128>(args, w4, stream); break;
+    switch (dd) {
+      case 32032: launch_fwd_bf16<32, 32>(args, w4, stream); break;
+      case 64064: launch_fwd_bf16<64, 64>(args, w4, stream); break;
+      case 128128: launch_fwd_bf16<128, 128>(args, w4, stream); break;
+      case 128064: launch_fwd_bf16<128, 64>(args, w4, stream); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     const FwdArgs& a = args;
-    const dim3 grid((unsigned)a.n_qtiles * a.B * a.Hq);
-    switch (a.D) {
-      case 32: hipLaunchKernelGGL(fwd_f32_kernel<32>, grid, block128, 0, stream, a); break;
-      case 64: hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block128, 0, stream, a); break;
+    const dim3 grid((unsigned)a.n_qtiles * a.B * a.Hq), block(128);
+    switch (dd) {
+      case 32032: hipLaunchKernelGGL((fwd_f32_kernel<32, 32>), grid, block, 0, stream, a); break;
+      case 64064: hipLaunchKernelGGL((fwd_f32_kernel<64, 64>), grid, block, 0, stream, a); break;
+      case 64032: hipLaunchKernelGGL((fwd_f32_kernel<64, 32>), grid, block, 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
   }

@@ -6,7 +6,8 @@
 
 namespace rea {
 
-// dtype: 0 = bf16, 1 = fp32.
+// dtype: 0 = bf16, 1 = fp32.  Head dims (q/k D, v Dv) with kernels built for them.
+bool head_dims_supported(int dtype, int D, int Dv);
 hipError_t launch_fwd(int dtype, const FwdArgs& a, hipStream_t stream);
 int fwd_tile_rows(int dtype);
 

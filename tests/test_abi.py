@@ -87,11 +87,23 @@ def test_struct_layout(lib):
     (dict(causal=2), rea.ATTN_ERR_INVALID_ARG, b"causal"),
     (dict(q_pos0=1 << 40), rea.ATTN_ERR_UNSUPPORTED, b"q_pos0"),
     (dict(scale=float("inf")), rea.ATTN_ERR_INVALID_ARG, b"scale"),
-    (dict(reserved=1), rea.ATTN_ERR_INVALID_ARG, b"reserved"),
+    (dict(head_dim_v=-1), rea.ATTN_ERR_INVALID_ARG, b"head_dim_v"),
+    (dict(head_dim_v=32), rea.ATTN_ERR_UNSUPPORTED, b"head_dim_v"),
+    (dict(head_dim=64, head_dim_v=128), rea.ATTN_ERR_UNSUPPORTED, b"head_dim_v"),
+    (dict(dtype=1, head_dim=64, head_dim_v=48), rea.ATTN_ERR_UNSUPPORTED, b"head_dim_v"),
 ])
 def test_forward_argument_checks(lib, kw, status, msg):
     assert fwd_status(lib, params(**kw)) == status
     assert msg in lib.attn_last_error()
+
+
+@pytest.mark.parametrize("dtype,d,dv", [(rea.ATTN_BF16, 128, 64), (rea.ATTN_BF16, 128, 128),
+                                         (rea.ATTN_BF16, 64, 0), (rea.ATTN_F32, 64, 32)])
+def test_head_dim_pairs_accepted(lib, dtype, d, dv):
+    """Every built (head_dim, head_dim_v) pair passes the argument checks (and then stops at
+    the NULL q pointer, so nothing is launched)."""
+    assert fwd_status(lib, params(dtype=dtype, head_dim=d, head_dim_v=dv)) == rea.ATTN_ERR_INVALID_ARG
+    assert b"q is NULL" in lib.attn_last_error()
 
 
 def test_null_and_misaligned_pointers(lib):
@@ -111,7 +123,12 @@ def test_no_finalize_needs_acc(lib):
 def test_backward_checks(lib):
     p = params()
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(p))
-    assert need == 2 * 2048                           # D and LSE: 4*128 floats each, 256-aligned
+    # D and LSE (4*128 floats each, 256-aligned), then fp32 partial dk, dv of the two dk/dv
+    # workgroups that share the GQA group's 2 q heads (causal without a left window)
+    assert need == 2 * 2048 + 2 * 128 * 2 * (128 + 128) * 4
+    # a left window (or a single q head per kv head) keeps one dk/dv workgroup per key tile
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(params(window_left=16))) == 2 * 2048
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(params(num_kv_heads=4))) == 2 * 2048
     d = ctypes.c_void_p(0x1000)
     st = lib.attn_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, need - 1, None)
     assert st == rea.ATTN_ERR_WORKSPACE
@@ -142,6 +159,9 @@ def test_sparse_mode_checks(lib):
     p.top_n = 17
     assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_ERR_INVALID_ARG
     p.top_n = 8
+    p.head_dim_v = 64
+    assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_ERR_UNSUPPORTED
+    p.head_dim_v = 0
     p.batch = 0
     assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_OK
 

@@ -6,7 +6,10 @@ fp64 oracle, on seeded inputs.
   virtual ring blocks, bf16 head dims 32/64/128 and the fp32 path;
 * every workload at its full size, in the launch configuration bench.py times, checked
   on sampled heads / rows the oracle can compute;
-* the step API (carry in / no finalize), determinism and the degenerate cases.
+* the step API (carry in / no finalize), determinism and the degenerate cases;
+* a value head dim of its own (the TransformerEngine page's DeepSeek-style MLA case,
+  q/k 128 and v 64): small shapes through every mask kind and both workgroup shapes,
+  the step API, and the page's full-size shape on one sampled GQA group.
 """
 import zlib
 
@@ -85,6 +88,44 @@ def test_small_backward(gpu, case):
     check_close("dv", dv, dv_r, dt)
 
 
+MLA_SMALL = [
+    # id, dtype, B, Sq, Skv, Hq, Hkv, D, Dv, causal, window, q_pos0, kv_pos0, kv_block
+    ("mla_bf16_causal_gqa4_ragged", "bf16", 2, 300, 300, 8, 2, 128, 64, True, (-1, -1), 0, 0, 0),
+    ("mla_bf16_swa37_gqa16", "bf16", 1, 515, 515, 16, 1, 128, 64, True, (37, 0), 0, 0, 0),
+    ("mla_bf16_ring_offsets", "bf16", 1, 512, 768, 4, 4, 128, 64, True, (-1, -1), 256, 0, 128),
+    ("mla_bf16_right_window", "bf16", 1, 190, 190, 2, 1, 128, 64, False, (-1, 20), 0, 0, 0),
+    ("mla_f32_d64_v32", "f32", 1, 200, 200, 4, 2, 64, 32, True, (-1, -1), 0, 0, 0),
+]
+
+
+def mla_inputs(case):
+    _, dt, B, Sq, Skv, Hq, Hkv, D, Dv, *_ = case
+    t = tdtype(dt)
+    seed = zlib.crc32(case[0].encode()) % 10000
+    return (rnd((B, Sq, Hq, D), seed, t), rnd((B, Skv, Hkv, D), seed + 1, t),
+            rnd((B, Skv, Hkv, Dv), seed + 2, t), rnd((B, Sq, Hq, Dv), seed + 3, t))
+
+
+@pytest.mark.parametrize("case", MLA_SMALL, ids=[c[0] for c in MLA_SMALL])
+def test_mla_head_dims(gpu, case):
+    name, dt, B, Sq, Skv, Hq, Hkv, D, Dv, causal, window, qp0, kp0, kvb = case
+    q, k, v, do = mla_inputs(case)
+    kw = dict(causal=causal, window=window, q_pos0=qp0, kv_pos0=kp0, kv_block=kvb)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **kw)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **kw)
+    torch.cuda.synchronize()
+    assert o.shape == (B, Sq, Hq, Dv) and dv.shape == (B, Skv, Hkv, Dv) and dk.shape == (B, Skv, Hkv, D)
+    okw = dict(causal=causal, window=window, q_pos0=qp0, kv_pos0=kp0)
+    o_r, m_r, l_r = dense.forward(q, k, v, **okw)
+    check_close("o", o, o_r, dt)
+    check_stats(m, l, m_r, l_r, dt)
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, **okw)
+    check_close("dq", dq, dq_r, dt)
+    check_close("dk", dk, dk_r, dt)
+    check_close("dv", dv, dv_r, dt)
+
+
 def full_inputs(name, with_dout=True):
     w = workloads.WORKLOADS[name]
     q, k, v, do = workloads.generate(w, with_dout=with_dout)
@@ -151,6 +192,25 @@ def test_gqa_swa_full_size(gpu):
     check_close("dv", dv[b:b + 1, :, group], dv_r[:, :, group], "bf16")
 
 
+def test_mla_full_size(gpu):
+    """B2 S4096 Hq128 Hkv8, q/k 128, v 64, causal: one full GQA group checked fwd and bwd."""
+    w, q, k, v, do = full_inputs("mla_qk128_v64_s4096")
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **launch_kw(w))
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **launch_kw(w))
+    torch.cuda.synchronize()
+    group, b = 3, 0
+    heads = list(range(16 * group, 16 * group + 16))
+    qs, ks, vs, dos = q[b:b + 1], k[b:b + 1], v[b:b + 1], do[b:b + 1]
+    o_r, m_r, l_r = dense.forward(qs, ks, vs, heads=heads[::5], **oracle_kw(w))
+    check_close("o", o[b:b + 1, :, heads[::5]], o_r[:, :, heads[::5]], "bf16")
+    check_stats(m[b:b + 1, heads[::5]], l[b:b + 1, heads[::5]], m_r[:, heads[::5]], l_r[:, heads[::5]], "bf16")
+    dq_r, dk_r, dv_r = dense.backward(qs, ks, vs, dos, heads=heads, **oracle_kw(w))
+    check_close("dq", dq[b:b + 1, :, heads], dq_r[:, :, heads], "bf16")
+    check_close("dk", dk[b:b + 1, :, group], dk_r[:, :, group], "bf16")
+    check_close("dv", dv[b:b + 1, :, group], dv_r[:, :, group], "bf16")
+
+
 def test_long_context_sampled_rows(gpu):
     """B1 S131072 Hq32 Hkv8 D128 causal, 32 virtual blocks of 4096: sampled rows."""
     w, q, k, v, _ = full_inputs("long_causal_s131072", with_dout=False)
@@ -188,6 +248,23 @@ def test_step_api_carry_equals_single_call(gpu, dt):
     check_close("o (one call)", o1, o_r, dt)
 
 
+def test_step_api_carry_mla(gpu):
+    """The ring step API with a value head dim of its own: the carry acc has Dv columns."""
+    B, S, Hq, Hkv, D, Dv = 1, 384, 4, 1, 128, 64
+    t = torch.bfloat16
+    q, k, v = rnd((B, S, Hq, D), 41, t), rnd((B, 2 * S, Hkv, D), 42, t), rnd((B, 2 * S, Hkv, Dv), 43, t)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    acc, m, l = gpu.attn_fwd(qd, kd[:, S:].contiguous(), vd[:, S:].contiguous(), causal=True,
+                             q_pos0=S, kv_pos0=S, finalize=False)
+    assert acc.shape == (B, S, Hq, Dv)
+    o, m, l = gpu.attn_fwd(qd, kd[:, :S].contiguous(), vd[:, :S].contiguous(), causal=True,
+                           q_pos0=S, kv_pos0=0, carry_in=True, m=m, l=l, acc=acc)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=True, q_pos0=S, kv_pos0=0)
+    check_close("o (two steps)", o, o_r, "bf16")
+    check_stats(m, l, m_r, l_r, "bf16")
+
+
 def test_no_finalize_carry_matches_oracle(gpu):
     B, S, H, D = 1, 256, 2, 64
     q, k, v = rnd((B, S, H, D), 21, torch.bfloat16), rnd((B, S, H, D), 22, torch.bfloat16), \
@@ -200,14 +277,18 @@ def test_no_finalize_carry_matches_oracle(gpu):
     check_close("acc/l", acc / l.transpose(1, 2)[..., None], o_r, "bf16")
 
 
-def test_backward_is_deterministic(gpu):
+@pytest.mark.parametrize("window,Dv", [((200, 0), 128), ((-1, -1), 128), ((-1, -1), 64)])
+def test_backward_is_deterministic(gpu, window, Dv):
+    """Bitwise repeatable: a windowed case (one dk/dv workgroup per key tile) and causal
+    GQA cases whose q heads are shared out over several dk/dv workgroups (fp32 partials
+    summed in a fixed order)."""
     B, S, Hq, Hkv, D = 1, 640, 8, 2, 128
     q, k, v, do = (rnd((B, S, Hq, D), 31, torch.bfloat16).to(DEV), rnd((B, S, Hkv, D), 32, torch.bfloat16).to(DEV),
-                   rnd((B, S, Hkv, D), 33, torch.bfloat16).to(DEV), rnd((B, S, Hq, D), 34, torch.bfloat16).to(DEV))
-    o, m, l = gpu.attn_fwd(q, k, v, causal=True, window=(200, 0))
-    a = gpu.attn_bwd(q, k, v, o, do, m, l, causal=True, window=(200, 0))
-    b = gpu.attn_bwd(q, k, v, o, do, m, l, causal=True, window=(200, 0))
-    o2, _, _ = gpu.attn_fwd(q, k, v, causal=True, window=(200, 0))
+                   rnd((B, S, Hkv, Dv), 33, torch.bfloat16).to(DEV), rnd((B, S, Hq, Dv), 34, torch.bfloat16).to(DEV))
+    o, m, l = gpu.attn_fwd(q, k, v, causal=True, window=window)
+    a = gpu.attn_bwd(q, k, v, o, do, m, l, causal=True, window=window)
+    b = gpu.attn_bwd(q, k, v, o, do, m, l, causal=True, window=window)
+    o2, _, _ = gpu.attn_fwd(q, k, v, causal=True, window=window)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)

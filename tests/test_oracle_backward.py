@@ -25,12 +25,14 @@ def loss(q, k, v, do, **kw):
     return float((o * do).sum())
 
 
-@pytest.mark.parametrize("causal,window,qp0,kp0", [
-    (True, (-1, -1), 0, 0), (True, (3, 0), 0, 0), (False, (2, 1), 0, 0), (True, (-1, -1), 4, 0)])
-def test_finite_differences(causal, window, qp0, kp0):
+@pytest.mark.parametrize("causal,window,qp0,kp0,Dv", [
+    (True, (-1, -1), 0, 0, 4), (True, (3, 0), 0, 0, 4), (False, (2, 1), 0, 0, 4), (True, (-1, -1), 4, 0, 4),
+    (True, (-1, -1), 0, 0, 2), (False, (2, 1), 3, 0, 6)])
+def test_finite_differences(causal, window, qp0, kp0, Dv):
+    """Dv != D covers a value head dim of its own (the MLA case)."""
     B, Sq, Skv, Hq, Hkv, D = 1, 9, 11, 2, 1, 4
     q, k, v, do = (rnd((B, Sq, Hq, D), 1).numpy(), rnd((B, Skv, Hkv, D), 2).numpy(),
-                   rnd((B, Skv, Hkv, D), 3).numpy(), rnd((B, Sq, Hq, D), 4).numpy())
+                   rnd((B, Skv, Hkv, Dv), 3).numpy(), rnd((B, Sq, Hq, Dv), 4).numpy())
     kw = dict(causal=causal, window=window, q_pos0=qp0, kv_pos0=kp0)
     dq, dk, dv = dense.backward(q, k, v, do, **kw)
     h = 1e-6
@@ -50,11 +52,12 @@ def test_finite_differences(causal, window, qp0, kp0):
         assert err < 1e-6, (name, err)
 
 
-@pytest.mark.parametrize("Hq,Hkv,causal,window", [(4, 2, True, (-1, -1)), (6, 3, True, (5, 0)),
-                                                    (2, 2, False, (-1, -1))])
-def test_matches_torch_autograd(Hq, Hkv, causal, window):
+@pytest.mark.parametrize("Hq,Hkv,causal,window,Dv", [(4, 2, True, (-1, -1), 8), (6, 3, True, (5, 0), 8),
+                                                       (2, 2, False, (-1, -1), 8), (8, 2, True, (-1, -1), 4),
+                                                       (4, 1, True, (7, 0), 4)])
+def test_matches_torch_autograd(Hq, Hkv, causal, window, Dv):
     B, S, D = 2, 23, 8
-    q, k, v, do = rnd((B, S, Hq, D), 5), rnd((B, S, Hkv, D), 6), rnd((B, S, Hkv, D), 7), rnd((B, S, Hq, D), 8)
+    q, k, v, do = rnd((B, S, Hq, D), 5), rnd((B, S, Hkv, D), 6), rnd((B, S, Hkv, Dv), 7), rnd((B, S, Hq, Dv), 8)
     mask = np.zeros((S, S), dtype=bool)
     for i in range(S):
         for j in range(S):

@@ -17,16 +17,17 @@ def rnd(shape, seed):
     return torch.randn(shape, generator=g, dtype=torch.float64)
 
 
-@pytest.mark.parametrize("n_blocks,qc,kc,causal,window", [
-    (4, 8, 8, True, (-1, -1)),
-    (4, 4, 16, True, (-1, -1)),       # query and key chunks of different sizes
-    (2, 16, 8, False, (-1, -1)),
-    (8, 4, 4, True, (5, 0)),
-    (1, 32, 32, True, (-1, -1)),      # one block: plain blockwise attention
+@pytest.mark.parametrize("n_blocks,qc,kc,causal,window,Dv", [
+    (4, 8, 8, True, (-1, -1), 8),
+    (4, 4, 16, True, (-1, -1), 8),    # query and key chunks of different sizes
+    (2, 16, 8, False, (-1, -1), 8),
+    (8, 4, 4, True, (5, 0), 8),
+    (1, 32, 32, True, (-1, -1), 8),   # one block: plain blockwise attention
+    (4, 8, 8, True, (-1, -1), 4),     # value head dim of its own (MLA)
 ])
-def test_ring_carry_equals_definition(n_blocks, qc, kc, causal, window):
+def test_ring_carry_equals_definition(n_blocks, qc, kc, causal, window, Dv):
     B, S, Hq, Hkv, D = 2, 64, 4, 2, 8
-    q, k, v = rnd((B, S, Hq, D), 1), rnd((B, S, Hkv, D), 2), rnd((B, S, Hkv, D), 3)
+    q, k, v = rnd((B, S, Hq, D), 1), rnd((B, S, Hkv, D), 2), rnd((B, S, Hkv, Dv), 3)
     o_r, m_r, l_r = blockwise.ring_forward(q, k, v, n_blocks=n_blocks, query_chunk=qc,
                                            key_chunk=kc, causal=causal, window=window)
     o_d, m_d, l_d = dense.forward(q, k, v, causal=causal, window=window)

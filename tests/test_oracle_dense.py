@@ -84,6 +84,23 @@ def test_forward_matches_torch_sdpa(case):
     np.testing.assert_allclose(m + np.log(l), lse_ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal,window,G", [(True, (-1, -1), 2), (True, (6, 0), 4), (False, (-1, 3), 1)])
+def test_value_head_dim_differs_matches_torch_sdpa(causal, window, G):
+    """v (and so o) with its own head dim (the TransformerEngine page's DeepSeek-style
+    MLA case, section 4); torch's SDPA accepts Ev != E."""
+    B, S, Hkv, D, Dv = 2, 33, 2, 16, 8
+    q, k, v = rnd((B, S, Hkv * G, D), 21), rnd((B, S, Hkv, D), 22), rnd((B, S, Hkv, Dv), 23)
+    mask = loop_mask(S, S, causal, *window)
+    assert mask.any(axis=1).all()
+    scale = 1 / math.sqrt(D)                       # the q/k head dim, not Dv
+    o_ref, m_ref, lse_ref = sdpa_reference(q, k, v, mask, scale)
+    o, m, l = dense.forward(q, k, v, causal=causal, window=window)
+    assert o.shape == (B, S, Hkv * G, Dv)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m, m_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m + np.log(l), lse_ref, rtol=0, atol=1e-12)
+
+
 def test_default_scale_is_inverse_sqrt_d():
     q, k, v = rnd((1, 16, 2, 8), 4), rnd((1, 16, 2, 8), 5), rnd((1, 16, 2, 8), 6)
     mask = loop_mask(16, 16, True, -1, -1)

@@ -90,9 +90,9 @@ MUTATIONS = [
     (_mut_transposed_scores, lambda: td.test_forward_matches_torch_sdpa(td.CASES[1])),
     (_mut_strict_causal, td.test_window_zero_left_returns_own_value),
     (_mut_window_exclusive, td.test_zero_queries_average_visible_values),
-    (_mut_grad_sign, lambda: tb.test_finite_differences(True, (-1, -1), 0, 0)),
+    (_mut_grad_sign, lambda: tb.test_finite_differences(True, (-1, -1), 0, 0, 4)),
     (_mut_grad_drop_d, tb.test_gradient_sums),
-    (_mut_correction_inverted, lambda: tw.test_ring_carry_equals_definition(4, 8, 8, True, (-1, -1))),
+    (_mut_correction_inverted, lambda: tw.test_ring_carry_equals_definition(4, 8, 8, True, (-1, -1), 8)),
     (_mut_ties_to_higher_index, ts.test_select_ties_go_to_lower_index),
     (_mut_window_off_by_one, ts.test_sparse_equals_materialised_candidate_list),
     (_mut_clamp_to_last, ts.test_sparse_zero_keys_closed_form),

@@ -10,7 +10,8 @@ Recipe (the same for every workload):
   * an optional multiplier (0.5 for the long-context workload);
   * a round-to-nearest-even cast to the workload's element type (bf16 or fp32).
 
-Shapes are BSHD: q, o, dout are [B, S, Hq, D]; k, v are [B, S, Hkv, D].  The
+Shapes are BSHD: q is [B, S, Hq, D], k is [B, S, Hkv, D], v is [B, S, Hkv, Dv] and o,
+dout are [B, S, Hq, Dv], where Dv = D except in the MLA workload (q/k 128, v 64).  The
 block-sparse workload stores 8 heads of 64 as one joint embedding of 512 per token
 (the AnnAttention page flattens heads into one vector before attending), so its
 tensors are viewed as [B, S, 1, 512].
@@ -45,7 +46,12 @@ class Workload:
     block_size: int = 0
     top_n: int = 0
     sparse_window: int = 0
+    head_dim_v: int = 0             # 0 -> head_dim
     note: str = ""
+
+    @property
+    def dv(self) -> int:
+        return self.head_dim_v or self.head_dim
 
     @property
     def scale(self) -> float:
@@ -81,6 +87,12 @@ WORKLOADS = {
         head_dim=128, dtype="bf16", seed=3, causal=True, query_chunk=4096, key_chunk=4096,
         kv_block=4096, input_scale=0.5, backward=False,
         note="B1 S131072 Hq32 Hkv8 D128 bf16 causal, 32 virtual blocks of 4096, fwd"),
+    # DeepSeek-style MLA head dims behind the projections: q/k 128, v 64, causal, GQA 16
+    # (the TransformerEngine page, section 4, on its section-1 shape).
+    "mla_qk128_v64_s4096": Workload(
+        "mla_qk128_v64_s4096", batch=2, seqlen=4096, num_q_heads=128, num_kv_heads=8,
+        head_dim=128, head_dim_v=64, dtype="bf16", seed=2027, causal=True,
+        note="B2 S4096 Hq128 Hkv8 q/k 128 v 64 bf16 causal"),
     # Block-sparse: per-token exact top-8 over earlier 32-token block means + window 32.
     "block_sparse_top8_s8192": Workload(
         "block_sparse_top8_s8192", batch=4, seqlen=8192, num_q_heads=1, num_kv_heads=1,
@@ -95,16 +107,16 @@ def generate(w: Workload, *, with_dout: bool | None = None):
     if with_dout is None:
         with_dout = w.backward
     g = torch.Generator().manual_seed(w.seed)
-    B, S, Hq, Hkv, D = w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim
+    B, S, Hq, Hkv, D, Dv = w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, w.dv
     out = []
-    for shape in ((B, S, Hq, D), (B, S, Hkv, D), (B, S, Hkv, D)):
+    for shape in ((B, S, Hq, D), (B, S, Hkv, D), (B, S, Hkv, Dv)):
         t = torch.randn(shape, generator=g, dtype=torch.float32)
         if w.input_scale != 1.0:
             t.mul_(w.input_scale)
         out.append(t.to(w.torch_dtype))
     dout = None
     if with_dout:
-        t = torch.randn((B, S, Hq, D), generator=g, dtype=torch.float32)
+        t = torch.randn((B, S, Hq, Dv), generator=g, dtype=torch.float32)
         if w.input_scale != 1.0:
             t.mul_(w.input_scale)
         dout = t.to(w.torch_dtype)
