@@ -31,6 +31,18 @@ blockwise body of ``_blockwise_attention_bwd`` in "bpt.py"):
 with dK and dV summed over the G q heads that share a kv head (the gradient of the
 repeat in the GQA mapping).
 
+Sink softmax ("JAX: Single-GPU Attention with TransformerEngine", "Other attention
+knobs": ``softmax_type="off_by_one"`` or ``"learnable"``; the page names the options only,
+so this is the plain reading of their names): every row's softmax gets one more term in
+its denominator, exp(z_h) for a per-q-head sink logit z_h in the units of the scaled
+logits, with nothing added to the numerator -- as if each row also saw one extra key
+with logit z_h and a zero value vector.  "off_by_one" is z_h = 0 (the 1 + sum exp form);
+"learnable" takes z_h as an input and has a gradient:
+  P_ij = exp(s_ij) / (exp(z_h) + sum_k exp(s_ik)),  P_sink,i = exp(z_h) / (same),
+  dS_ij = P_ij (dP_ij - D_i) as before, and dz_h = -sum_{b,i} P_sink,i D_i.
+The statistics m, l stay those of the keys alone (the sink enters only when the output
+is normalised), so the blockwise carry is unchanged.
+
 The value head dim Dv may differ from the q/k head dim D (the DeepSeek-style MLA case
 of the TransformerEngine page, section 4: q/k 128, v 64); nothing above needs them
 equal: O, dO and dV have Dv columns, Q, K, dQ and dK have D, and the default scale
@@ -109,14 +121,34 @@ def _softmax_rows(s: np.ndarray, vis: np.ndarray):
     return p, m, l
 
 
+def _sink_logits(sink, Hq: int):
+    """None (plain softmax) or the per-q-head sink logits z as an fp64 array [Hq]."""
+    if sink is None:
+        return None
+    z = as_f64(sink).reshape(-1)
+    if z.shape[0] == 1:
+        z = np.full(Hq, z[0])
+    assert z.shape[0] == Hq
+    return z
+
+
+def _sink_weight(z, m, l):
+    """exp(z - m) for the rows' key statistics (m, l); 0 without a sink, and 0 for rows
+    that see no key (their output is 0 whatever the sink)."""
+    if z is None:
+        return np.zeros_like(l)
+    return np.where(np.isfinite(m), np.exp(z - np.where(np.isfinite(m), m, 0.0)), 0.0)
+
+
 def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0,
-            kv_pos0: int = 0, rows=None, heads=None, row_block: int = 256):
+            kv_pos0: int = 0, rows=None, heads=None, row_block: int = 256, sink=None):
     """Attention forward from the definition.
 
     q: [B, Sq, Hq, D]; k: [B, Skv, Hkv, D]; v: [B, Skv, Hkv, Dv] (torch or numpy, any
     float dtype).  Returns (o [B, Sq, Hq, Dv], m [B, Hq, Sq], l [B, Hq, Sq]) in fp64, with m in the
     natural-log units of the scaled logits.  ``rows`` / ``heads`` restrict the
-    evaluation to sampled query rows / q heads; entries not evaluated are NaN.
+    evaluation to sampled query rows / q heads; entries not evaluated are NaN.  ``sink``:
+    None, or the sink logits z [Hq] (zeros for "off_by_one"); m and l exclude the sink.
     """
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     B, Sq, Hq, D = q.shape
@@ -125,6 +157,7 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
     G = Hq // Hkv
     sc = _default_scale(D, scale)
     wl, wr = window
+    z = _sink_logits(sink, Hq)
     fill = np.nan if (rows is not None or heads is not None) else 0.0
     o = np.full((B, Sq, Hq, v.shape[3]), fill)
     m = np.full((B, Hq, Sq), np.nan if fill != 0.0 else -np.inf)
@@ -146,7 +179,8 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
                     continue
                 c0, c1 = rng
                 p, mr, lr = _softmax_rows(scores(q[b, r, hq, :], K[c0:c1], sc), vis[:, c0:c1])
-                denom = np.where(lr > 0, lr, 1.0)
+                denom = lr + _sink_weight(None if z is None else z[hq], mr, lr)
+                denom = np.where(denom > 0, denom, 1.0)
                 o[b, r, hq] = (p @ V[c0:c1]) / denom[:, None]
                 m[b, hq, r] = mr
                 l[b, hq, r] = lr
@@ -170,14 +204,15 @@ def probs(q, k, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0, k
 
 
 def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0,
-             kv_pos0: int = 0, row_block: int = 256, heads=None, batches=None):
+             kv_pos0: int = 0, row_block: int = 256, heads=None, batches=None, sink=None):
     """Analytic gradient of ``forward`` contracted with dO.
 
     Returns (dq [B, Sq, Hq, D], dk [B, Skv, Hkv, D], dv [B, Skv, Hkv, Dv]) in fp64.
     D_i uses this function's own fp64 output O.  ``heads`` / ``batches`` restrict the
     evaluation to some q heads / batch entries: dq of the others is NaN, and dk, dv
     only collect the contributions of the evaluated q heads (complete for a kv head
-    when all q heads of its group are listed).
+    when all q heads of its group are listed).  With ``sink`` (logits z [Hq]) the
+    gradient of z is returned too: (dq, dk, dv, dz [Hq]).
     """
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, Sq, Hq, D = q.shape
@@ -185,6 +220,8 @@ def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: 
     G = Hq // Hkv
     sc = _default_scale(D, scale)
     wl, wr = window
+    z = _sink_logits(sink, Hq)
+    dz = np.zeros(Hq)
     partial = heads is not None or batches is not None
     dq = np.full_like(q, np.nan) if partial else np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -202,17 +239,21 @@ def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: 
                 if rng is None:
                     continue
                 c0, c1 = rng
-                p, _, lr = _softmax_rows(scores(q[b, r, hq], K[c0:c1], sc), vis[:, c0:c1])
-                P = p / np.where(lr > 0, lr, 1.0)[:, None]
+                p, mr, lr = _softmax_rows(scores(q[b, r, hq], K[c0:c1], sc), vis[:, c0:c1])
+                w_sink = _sink_weight(None if z is None else z[hq], mr, lr)
+                denom = lr + w_sink
+                denom = np.where(denom > 0, denom, 1.0)
+                P = p / denom[:, None]
                 O = P @ V[c0:c1]
                 dO = do[b, r, hq]
                 Di = (dO * O).sum(axis=1)
+                dz[hq] -= float(((w_sink / denom) * Di).sum())
                 dP = dO @ V[c0:c1].T
                 dS = grad_scores(P, dP, Di)
                 dq[b, r, hq] = sc * (dS @ K[c0:c1])
                 dk[b, c0:c1, g] += sc * (dS.T @ q[b, r, hq])
                 dv[b, c0:c1, g] += P.T @ dO
-    return dq, dk, dv
+    return (dq, dk, dv) if z is None else (dq, dk, dv, dz)
 
 
 def visible_pairs(Sq: int, Skv: int, *, causal: bool, window=(-1, -1), q_pos0: int = 0,

@@ -13,6 +13,7 @@ import test_oracle_backward as tb
 import test_oracle_blockwise as tw
 import test_oracle_dense as td
 import test_oracle_select_sparse as ts
+import test_oracle_sink as tk
 
 
 def _mut_gqa_modulo(monkeypatch):
@@ -84,6 +85,17 @@ def _mut_clamp_to_last(monkeypatch):
     monkeypatch.setattr(sparse, "candidate_positions", cand)
 
 
+def _mut_sink_sign(monkeypatch):
+    orig = dense._sink_weight
+    monkeypatch.setattr(dense, "_sink_weight", lambda z, m, l: orig(None if z is None else -z, m, l))
+
+
+def _mut_sink_in_log2_units(monkeypatch):
+    orig = dense._sink_weight
+    monkeypatch.setattr(dense, "_sink_weight",
+                        lambda z, m, l: orig(None if z is None else z * 1.4426950408889634, m, l))
+
+
 MUTATIONS = [
     (_mut_gqa_modulo, lambda: td.test_forward_matches_torch_sdpa(td.CASES[0])),
     (_mut_drop_scale, lambda: td.test_forward_matches_torch_sdpa(td.CASES[1])),
@@ -96,6 +108,8 @@ MUTATIONS = [
     (_mut_ties_to_higher_index, ts.test_select_ties_go_to_lower_index),
     (_mut_window_off_by_one, ts.test_sparse_equals_materialised_candidate_list),
     (_mut_clamp_to_last, ts.test_sparse_zero_keys_closed_form),
+    (_mut_sink_sign, tk.test_sink_with_zero_left_window_closed_form),
+    (_mut_sink_in_log2_units, lambda: tk.test_sink_forward_and_backward_match_torch(True, (-1, -1), 2, 8)),
 ]
 
 
