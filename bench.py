@@ -213,6 +213,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ring_sim_causal_s8192")
+    ap.add_argument("--softmax", default="vanilla", choices=["vanilla", "off_by_one", "learnable"],
+                    help="sink softmax variant of the dense workloads (learnable: seeded N(0,1) logits)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -245,12 +247,17 @@ def main():
     kw = dict(causal=w.causal, window=w.window, query_chunk=w.query_chunk, key_chunk=w.key_chunk,
               kv_block=w.kv_block)
     B, S, Hq, Hkv, D, Dv = w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, w.dv
+    sink = None
+    if args.softmax == "learnable":
+        sink = workloads.random_tensor((Hq,), w.seed + 100).to(dev)
+    kw.update(softmax_type=args.softmax, sink=sink)
     o = torch.empty((B, S, Hq, Dv), dtype=qd.dtype, device=dev)
     m = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     l = torch.empty_like(m)
     grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
     ws = torch.empty(max(rea.bwd_workspace_bytes(qd, kd, head_dim_v=Dv, **kw), 256), dtype=torch.uint8,
                      device=dev)
+    bkw = dict(kw, dsink=torch.empty((Hq,), dtype=torch.float32, device=dev)) if sink is not None else kw
 
     # One step, split into its kernels so each can be timed on the launch stream:
     # forward | dq (which also computes D and the LSE for the dk/dv pass) | dk,dv.
@@ -258,9 +265,9 @@ def main():
         yield "attn_fwd", lambda: rea.attn_fwd(qd, kd, vd, out=o, m=m, l=l, **kw)
         if w.backward:
             yield "bwd_dq", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
-                                                 skip_dkdv=True, **kw)
+                                                 skip_dkdv=True, **bkw)
             yield "bwd_dkdv", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
-                                                   skip_dq=True, reuse_stats=True, **kw)
+                                                   skip_dq=True, reuse_stats=True, **bkw)
 
     segs = list(segments())
     seg_ms, wall = time_segments(torch, segs, args.steps, args.warmup, torch.cuda.current_stream(dev))
@@ -320,7 +327,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv,
+        "config": {"workload": w.name if args.softmax == "vanilla" else f"{w.name}+{args.softmax}_sink",
+                   "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "head_dim_v": Dv, "causal": w.causal, "window": list(w.window),
                    "virtual_blocks": (S // w.kv_block) if w.kv_block else 1,
                    "query_chunk": w.query_chunk, "key_chunk": w.key_chunk, "parallelism": "none (1 GPU)"},

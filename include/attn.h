@@ -76,7 +76,24 @@ enum {
                                   params, o, dout, m and l: do not recompute them     */
 };
 
-#define ATTN_PARAMS_VERSION 1u
+/* attn_params.softmax_type ("JAX: Single-GPU Attention with TransformerEngine", "Other
+ * attention knobs": softmax_type "off_by_one" or "learnable").  A sink adds exp(z_h) to
+ * the denominator of every row's softmax of q head h and nothing to its numerator (as
+ * one more key with logit z_h, in the units of the scaled logits, and a zero value):
+ *   o_i = sum_j exp(s_ij) v_j / (exp(z_h) + sum_j exp(s_ij)).
+ * OFF_BY_ONE is z_h = 0 (the "1 + sum" softmax); LEARNABLE reads z_h from params.sink and
+ * attn_bwd can return dL/dz_h.  m and l stay the statistics of the keys alone; the sink
+ * enters only when the output is finalised, so carried ring steps are unchanged. */
+enum {
+  ATTN_SOFTMAX_VANILLA = 0,
+  ATTN_SOFTMAX_OFF_BY_ONE = 1,
+  ATTN_SOFTMAX_LEARNABLE = 2
+};
+
+/* 2: softmax_type, sink, dsink appended (a version-1 struct of ATTN_PARAMS_V1_SIZE bytes,
+ * without them, is still accepted and means ATTN_SOFTMAX_VANILLA). */
+#define ATTN_PARAMS_VERSION 2u
+#define ATTN_PARAMS_V1_SIZE 104u
 
 typedef struct attn_params {
   uint32_t struct_size;        /* = sizeof(attn_params); versioning of the ABI        */
@@ -122,6 +139,12 @@ typedef struct attn_params {
    * ATTN_ERR_UNSUPPORTED.  The default scale stays 1/sqrt(head_dim).  Sparse mode
    * requires 0.                                                                     */
   int32_t head_dim_v;
+  int32_t softmax_type;        /* ATTN_SOFTMAX_*; sparse mode requires VANILLA          */
+  const float* sink;           /* LEARNABLE: [Hq] fp32 device, sink logits z_h          */
+  float* dsink;                /* attn_bwd with LEARNABLE: [Hq] fp32 device output
+                                  dL/dz_h summed over the batch and this call's query
+                                  rows, written (not accumulated) by calls that compute
+                                  dq; NULL = not wanted                                 */
 } attn_params;
 
 typedef struct select_params {

@@ -28,6 +28,9 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ER
 ATTN_BF16, ATTN_F32 = 0, 1
 ATTN_CARRY_IN, ATTN_NO_FINALIZE = 1, 2
 ATTN_BWD_SKIP_DQ, ATTN_BWD_SKIP_DKDV, ATTN_BWD_REUSE_STATS = 8, 16, 32
+ATTN_SOFTMAX_VANILLA, ATTN_SOFTMAX_OFF_BY_ONE, ATTN_SOFTMAX_LEARNABLE = 0, 1, 2
+_SOFTMAX_TYPES = {"vanilla": ATTN_SOFTMAX_VANILLA, "off_by_one": ATTN_SOFTMAX_OFF_BY_ONE,
+                  "learnable": ATTN_SOFTMAX_LEARNABLE}
 
 
 class AttnParams(ctypes.Structure):
@@ -55,6 +58,9 @@ class AttnParams(ctypes.Structure):
         ("sel_block", ctypes.c_int32),
         ("sparse_window", ctypes.c_int32),
         ("head_dim_v", ctypes.c_int32),
+        ("softmax_type", ctypes.c_int32),
+        ("sink", ctypes.c_void_p),
+        ("dsink", ctypes.c_void_p),
     ]
 
 
@@ -142,8 +148,18 @@ def _need(t, name, dtype=None, device=None):
         raise ValueError(f"{name} must be on {device}")
 
 
+def _softmax_code(softmax_type, sink):
+    if softmax_type not in _SOFTMAX_TYPES:
+        raise ValueError(f"softmax_type must be one of {sorted(_SOFTMAX_TYPES)}")
+    code = _SOFTMAX_TYPES[softmax_type]
+    if (code == ATTN_SOFTMAX_LEARNABLE) != (sink is not None):
+        raise ValueError("sink (fp32 [num_q_heads]) is given exactly when softmax_type='learnable'")
+    return code
+
+
 def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
-                kv_block=0, q_pos0=0, kv_pos0=0, flags=0, head_dim_v=0) -> AttnParams:
+                kv_block=0, q_pos0=0, kv_pos0=0, flags=0, head_dim_v=0, softmax_type="vanilla",
+                sink=None) -> AttnParams:
     B, Sq, Hq, D = q.shape
     Bk, Skv, Hkv, Dk = k.shape
     if Bk != B or Dk != D:
@@ -154,6 +170,12 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     p.batch, p.seqlen_q, p.seqlen_kv = B, Sq, Skv
     p.num_q_heads, p.num_kv_heads, p.head_dim = Hq, Hkv, D
     p.head_dim_v = 0 if head_dim_v in (0, D) else int(head_dim_v)
+    p.softmax_type = _softmax_code(softmax_type, sink)
+    if sink is not None:
+        _need(sink, "sink", torch.float32, q.device)
+        if sink.shape != (Hq,):
+            raise ValueError(f"sink must be [num_q_heads] = [{Hq}]")
+        p.sink = sink.data_ptr()
     p.q_pos0, p.kv_pos0 = int(q_pos0), int(kv_pos0)
     p.causal = 1 if causal else 0
     p.window_left, p.window_right = int(window[0]), int(window[1])
@@ -165,13 +187,14 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
 
 def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
              kv_block=0, q_pos0=0, kv_pos0=0, m=None, l=None, acc=None, carry_in=False,
-             finalize=True, out=None):
+             finalize=True, out=None, softmax_type="vanilla", sink=None):
     """Forward attention.  q [B, Sq, Hq, D], k [B, Skv, Hkv, D], v [B, Skv, Hkv, Dv] on the GPU
     (Dv = D, or the MLA pair D 128 / Dv 64).
 
     Returns (o, m, l) with o [B, Sq, Hq, Dv]; with ``finalize=False`` returns (acc, m, l)
     where acc is the fp32 unnormalised numerator.  ``carry_in=True`` resumes from the
-    given m, l, acc.
+    given m, l, acc.  ``softmax_type`` "off_by_one" / "learnable" (with ``sink``, fp32
+    [Hq] logits) adds exp(z_h) to each row's denominator when the output is finalised.
     """
     _need(q, "q")
     _need(k, "k", q.dtype, q.device)
@@ -183,7 +206,7 @@ def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     flags = (ATTN_CARRY_IN if carry_in else 0) | (0 if finalize else ATTN_NO_FINALIZE)
     p = make_params(q, k, causal=causal, window=window, scale=scale, query_chunk=query_chunk,
                     key_chunk=key_chunk, kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, flags=flags,
-                    head_dim_v=Dv)
+                    head_dim_v=Dv, softmax_type=softmax_type, sink=sink)
     dev = q.device
     if m is None:
         m = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
@@ -215,12 +238,15 @@ def bwd_workspace_bytes(q, k, **kw) -> int:
 
 def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None, query_chunk=0,
              key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, workspace=None, out=None,
-             skip_dq=False, skip_dkdv=False, reuse_stats=False):
+             skip_dq=False, skip_dkdv=False, reuse_stats=False, softmax_type="vanilla", sink=None,
+             dsink=None):
     """Gradients (dq, dk, dv) of attn_fwd's output for upstream gradient dout.
 
     ``skip_dq`` / ``skip_dkdv`` compute only part of them (the skipped outputs are left
     untouched); ``reuse_stats`` takes D and the log-sum-exp from ``workspace`` as left
-    by an earlier call with the same inputs.
+    by an earlier call with the same inputs.  With ``softmax_type="learnable"`` the
+    gradient of the sink logits is returned as a fourth tensor (fp32 [Hq]; written by
+    calls that compute dq).
     """
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _need(t, n, q.dtype, q.device)
@@ -231,7 +257,8 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
     if v.shape[:3] != k.shape[:3] or o.shape != (B, Sq, Hq, Dv) or dout.shape != o.shape:
         raise ValueError("v must match k except in its head dim, and o, dout must be [B, Sq, Hq, Dv]")
     kw = dict(causal=causal, window=window, scale=scale, query_chunk=query_chunk, key_chunk=key_chunk,
-              kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, head_dim_v=Dv)
+              kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, head_dim_v=Dv, softmax_type=softmax_type,
+              sink=sink)
     flags = ((ATTN_BWD_SKIP_DQ if skip_dq else 0) | (ATTN_BWD_SKIP_DKDV if skip_dkdv else 0) |
              (ATTN_BWD_REUSE_STATS if reuse_stats else 0))
     p = make_params(q, k, flags=flags, **kw)
@@ -240,11 +267,17 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
         if reuse_stats:
             raise ValueError("reuse_stats needs the workspace of the earlier call")
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    learnable = softmax_type == "learnable"
+    if learnable:
+        if dsink is None:
+            dsink = torch.zeros((Hq,), dtype=torch.float32, device=q.device)
+        _need(dsink, "dsink", torch.float32, q.device)
+        p.dsink = dsink.data_ptr()
     dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     _check(lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(m),
                           _ptr(l), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(q)))
-    return dq, dk, dv
+    return (dq, dk, dv, dsink) if learnable else (dq, dk, dv)
 
 
 def _joint(x):

@@ -6,8 +6,10 @@
 #include "attn.h"
 
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "launch.h"
@@ -46,7 +48,23 @@ struct Problem {
   float scale = 1.f;
   int kv_block = 1, n_vblocks = 0, q_vblock = 1, n_qvblocks = 0;
   bool carry_in = false, finalize = true;
+  int has_sink = 0;
+  const float* sink = nullptr;
+  float* dsink = nullptr;
 };
+
+static_assert(offsetof(attn_params, softmax_type) == ATTN_PARAMS_V1_SIZE,
+              "a version-1 attn_params is the current one without its softmax fields");
+
+// The caller's params in the current layout: a version-1 struct (without the softmax
+// fields) reads as ATTN_SOFTMAX_VANILLA.  Other sizes pass through for the size check.
+const attn_params* current_layout(const attn_params* p, attn_params& tmp) {
+  if (!p || p->struct_size != ATTN_PARAMS_V1_SIZE) return p;
+  memset(&tmp, 0, sizeof tmp);
+  memcpy(&tmp, p, ATTN_PARAMS_V1_SIZE);
+  tmp.struct_size = sizeof(attn_params);
+  return &tmp;
+}
 
 int check_dense(const attn_params* p, bool bwd, Problem& r) {
   if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
@@ -90,6 +108,13 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   if (p->kv_block > 0 && p->seqlen_kv % p->kv_block != 0)
     return fail(ATTN_ERR_INVALID_ARG, fmt("kv_block (%lld) must divide seqlen_kv (%lld)",
                                           p->kv_block, p->seqlen_kv));
+  if (p->softmax_type != ATTN_SOFTMAX_VANILLA && p->softmax_type != ATTN_SOFTMAX_OFF_BY_ONE &&
+      p->softmax_type != ATTN_SOFTMAX_LEARNABLE)
+    return fail(ATTN_ERR_INVALID_ARG, fmt("softmax_type %lld is not one of the ATTN_SOFTMAX_* values",
+                                          p->softmax_type));
+  if (p->softmax_type == ATTN_SOFTMAX_LEARNABLE && (!p->sink || ((uintptr_t)p->sink & 3u)))
+    return fail(ATTN_ERR_INVALID_ARG, "ATTN_SOFTMAX_LEARNABLE needs sink: [num_q_heads] fp32 on the device");
+  if (p->dsink && ((uintptr_t)p->dsink & 3u)) return fail(ATTN_ERR_INVALID_ARG, "dsink must be 4-byte aligned");
   const uint32_t fwd_flags = ATTN_CARRY_IN | ATTN_NO_FINALIZE;
   const uint32_t bwd_flags = ATTN_BWD_SKIP_DQ | ATTN_BWD_SKIP_DKDV | ATTN_BWD_REUSE_STATS;
   if (p->flags & ~(fwd_flags | bwd_flags)) return fail(ATTN_ERR_INVALID_ARG, "unknown bits in flags");
@@ -127,6 +152,9 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   // (head_dim_v <= head_dim for every supported pair, so o, dout and v are no larger.)
   r.carry_in = (p->flags & ATTN_CARRY_IN) != 0;
   r.finalize = (p->flags & ATTN_NO_FINALIZE) == 0;
+  r.has_sink = p->softmax_type != ATTN_SOFTMAX_VANILLA;
+  r.sink = p->softmax_type == ATTN_SOFTMAX_LEARNABLE ? p->sink : nullptr;
+  r.dsink = p->softmax_type == ATTN_SOFTMAX_LEARNABLE ? p->dsink : nullptr;
   return ATTN_OK;
 }
 
@@ -165,6 +193,8 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
     return fail(ATTN_ERR_INVALID_ARG, "params->struct_size does not match this library");
   if (p->head_dim_v != 0 && p->head_dim_v != p->head_dim)
     return fail(ATTN_ERR_UNSUPPORTED, "sparse mode needs head_dim_v = 0 (the joint embedding)");
+  if (p->softmax_type != ATTN_SOFTMAX_VANILLA)
+    return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no sink softmax");
   if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode supports bf16 only");
   if (p->num_q_heads != 1 || p->num_kv_heads != 1)
     return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes the joint embedding: num_q_heads = num_kv_heads = 1");
@@ -212,8 +242,10 @@ const char* attn_last_error(void) { return g_err.c_str(); }
 
 uint32_t attn_abi_version(void) { return ATTN_PARAMS_VERSION; }
 
-int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o, float* m,
+int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* v, void* o, float* m,
              float* l, float* acc, void* stream) {
+  attn_params tmp;
+  const attn_params* p = current_layout(p_in, tmp);
   if (p && p->sel_idx) return sparse_fwd(p, q, k, v, o, m, l, stream);
   Problem r;
   int st = check_dense(p, false, r);
@@ -240,6 +272,8 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.G = r.G;
   a.D = r.D;
   a.Dv = r.Dv;
+  a.has_sink = r.has_sink;
+  a.sink = r.sink;
   a.delta = r.delta;
   a.lo_off = r.lo_off;
   a.hi_off = r.hi_off;
@@ -257,7 +291,9 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   return hip_status(rea::launch_fwd(r.dtype, a, (hipStream_t)stream));
 }
 
-size_t attn_bwd_workspace_bytes(const attn_params* p) {
+size_t attn_bwd_workspace_bytes(const attn_params* p_in) {
+  attn_params tmp;
+  const attn_params* p = current_layout(p_in, tmp);
   Problem r;
   const std::string saved = g_err;
   if (!p || check_dense(p, true, r) != ATTN_OK) return 0;
@@ -268,9 +304,11 @@ size_t attn_bwd_workspace_bytes(const attn_params* p) {
   return 2 * align_up(n > 0 ? n : 1) + (part ? align_up(part) : 0);
 }
 
-int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* v, const void* o,
              const void* dout, const float* m, const float* l, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes, void* stream) {
+  attn_params tmp;
+  const attn_params* p = current_layout(p_in, tmp);
   if (p && p->sel_idx) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd has no sparse mode");
   Problem r;
   int st = check_dense(p, true, r);
@@ -314,6 +352,8 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.G = r.G;
   a.D = r.D;
   a.Dv = r.Dv;
+  a.has_sink = r.has_sink;
+  a.sink = r.sink;
   a.delta = r.delta;
   a.lo_off = r.lo_off;
   a.hi_off = r.hi_off;
@@ -331,6 +371,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.xcd_kv_groups = r.dtype == ATTN_BF16 ? xcd_groups(r.B, r.Hkv * a.kv_splits) : 0;
   a.dkv_part = a.kv_splits > 1 ? (float*)((char*)workspace + 2 * align_up(n > 0 ? n : 1)) : nullptr;
   a.stages = (do_pre ? 1 : 0) | (do_dq ? 2 : 0) | (do_dkdv ? 4 : 0);
+  a.dsink = r.Sq > 0 ? r.dsink : nullptr;
   if ((long long)a.n_qtiles * r.B * r.Hq >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large");
   return hip_status(rea::launch_bwd(r.dtype, a, (hipStream_t)stream));
 }

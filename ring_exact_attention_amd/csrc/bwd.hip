@@ -55,7 +55,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const size_t st = ((size_t)b * a.Hq + h) * a.Sq + s;
     a.Dvec[st] = part;
     const float l = a.l[st], m = a.m[st];
-    a.lse2[st] = (l > 0.f) ? fmaf(m, kLog2e, log2f(l)) : INFINITY;
+    if (a.has_sink)
+      a.lse2[st] = lse2_with_sink(m * kLog2e, l, (a.sink ? a.sink[h] : 0.f) * kLog2e);
+    else
+      a.lse2[st] = (l > 0.f) ? fmaf(m, kLog2e, log2f(l)) : INFINITY;
   }
 }
 
@@ -341,7 +344,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
       }
       Di = sd[li];
       const float l = row_ok ? a.l[stat] : 0.f, m = row_ok ? a.m[stat] : 0.f;
-      lse2 = (l > 0.f) ? fmaf(m, kLog2e, log2f(l)) : INFINITY;
+      if (a.has_sink)
+        lse2 = lse2_with_sink(m * kLog2e, l, (a.sink ? a.sink[hq] : 0.f) * kLog2e);
+      else
+        lse2 = (l > 0.f) ? fmaf(m, kLog2e, log2f(l)) : INFINITY;
       if (row_ok && lh == 0) {
         a.Dvec[stat] = Di;
         a.lse2[stat] = lse2;
@@ -753,6 +759,28 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* part,
   *(u32x2*)(is_k ? dk + i : dv + (i - n_k)) = w;
 }
 
+// Gradient of the learnable sink logits: dz_h = -sum over (b, i) of P_sink,i * D_i, with
+// P_sink,i = exp(z_h - LSE_i) (the LSE includes the sink) and D_i = rowsum(dO * O), both
+// left in the workspace by the D / LSE pass.  One workgroup per q head; each thread sums
+// a fixed strided subset and the workgroup a fixed tree, so the result is reproducible.
+__global__ __launch_bounds__(256) void bwd_sink_grad_kernel(BwdArgs a) {
+  __shared__ float red[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float zz = a.sink[h] * kLog2e;
+  float acc = 0.f;
+  for (int b = 0; b < a.B; ++b) {
+    const size_t base = ((size_t)b * a.Hq + h) * a.Sq;
+    for (int i = tid; i < a.Sq; i += 256) acc -= exp2f(zz - a.lse2[base + i]) * a.Dvec[base + i];
+  }
+  red[tid] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) a.dsink[h] = red[0];
+}
+
 // ------------------------------------------------------------------ fp32 path
 // Plain fp32 kernels (small head dims): one thread per query row for dq, one thread
 // per key row for dk/dv; tiles of the other side staged in LDS.
@@ -994,6 +1022,9 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
     }
   }
 #undef REA_DQ_F32
+  // The sink gradient needs D and the LSE of every row: after the pass that wrote them.
+  if (a.dsink && a.sink && has_q && (want_pre || dq))
+    hipLaunchKernelGGL(bwd_sink_grad_kernel, dim3(a.Hq), dim3(256), 0, stream, a);
 #undef REA_DQ_BF16
 #undef REA_BWD
   return hipGetLastError();

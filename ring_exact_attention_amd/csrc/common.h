@@ -33,6 +33,8 @@ struct FwdArgs {
   float* acc;
   int B, Sq, Skv, Hq, Hkv, G, D;
   int Dv;             // head dim of v and o (may differ from D, the q/k head dim)
+  int has_sink;       // softmax with a sink term exp(z_h) in each row's denominator
+  const float* sink;  // [Hq] sink logits z_h (natural units); NULL with has_sink: z = 0
   // Visibility of (row i, key j): lo_off <= (j - i) + delta <= hi_off, with
   // delta = kv_pos0 - q_pos0 and j < Skv.
   int delta;
@@ -67,6 +69,9 @@ struct BwdArgs {
   float* lse2;        // [B, Hq, Sq] workspace: m*log2(e) + log2(l)  (log2 units)
   int B, Sq, Skv, Hq, Hkv, G, D;
   int Dv;             // head dim of v, o, dout, dv
+  int has_sink;       // as in FwdArgs: the LSE includes exp(z_h)
+  const float* sink;  // [Hq] or NULL (z = 0)
+  float* dsink;       // [Hq] output dL/dz_h (learnable sink), or NULL
   int delta, lo_off, hi_off;
   float scale, scale_log2;
   int kv_block, n_vblocks;     // virtual key blocks (ring order of the dq pass)
@@ -110,6 +115,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// log2 of (l * 2^mm + 2^zz) for a row's key statistics (mm = m * log2 e, l relative to
+// m) and a sink logit zz in log2 units, without overflow; +inf when the row sees no key.
+__device__ __forceinline__ float lse2_with_sink(float mm, float l, float zz) {
+  if (!(l > 0.f)) return INFINITY;
+  const float M = fmaxf(mm, zz);
+  return M + log2f(l * exp2f(mm - M) + exp2f(zz - M));
+}
 
 // Value held by the lane in the other half of the wavefront (lane ^ 32).
 __device__ __forceinline__ float other_half(float x) {

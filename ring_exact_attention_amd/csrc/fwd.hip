@@ -364,7 +364,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   if (a.finalize) {
     // O through LDS (this wave's 32 rows at 2D + 16 bytes, in the now idle stages; all
     // reads of the stages ended at the loop's last barrier), then stored as whole rows.
-    const float inv = l_used > 0.f ? 1.f / l_used : 0.f;
+    // A sink adds exp(z) to the denominator (relative to m_used, like l_used); a row with
+    // no visible key keeps O = 0.
+    float den = l_used;
+    if (a.has_sink && m_used != -INFINITY) den += fast_exp2(fmaf(a.sink ? a.sink[hq] : 0.f, kLog2e, -m_used));
+    const float inv = den > 0.f ? 1.f / den : 0.f;
     constexpr int OP = 2 * DV + 16, RPO = 64 / C::DCV;
     char* const os = lds + wave * (32 * OP);
 #pragma unroll
@@ -490,7 +494,9 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
   }
   if (row_ok) {
     if (a.finalize) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      float den = l_run;
+      if (a.has_sink && m_run != -INFINITY) den += fast_exp2(fmaf(a.sink ? a.sink[hq] : 0.f, kLog2e, -m_run));
+      const float inv = den > 0.f ? 1.f / den : 0.f;
       float* op = (float*)a.o + ((size_t)b * a.Sq + row) * o_rs + (size_t)hq * DV;
 #pragma unroll
       for (int d = 0; d < DV; ++d) op[d] = acc[d] * inv;

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
 
 
 def params(**kw):
@@ -61,7 +61,8 @@ def fwd_status(lib, p, ptr=None):
 
 
 def test_struct_layout(lib):
-    assert ctypes.sizeof(rea.AttnParams) == 104
+    assert ctypes.sizeof(rea.AttnParams) == 128
+    assert rea.AttnParams.softmax_type.offset == 104          # ATTN_PARAMS_V1_SIZE
     assert ctypes.sizeof(rea.SelectParams) == 32
     # a zero batch is a successful no-op only when the struct size matches
     assert fwd_status(lib, params(batch=0)) == rea.ATTN_OK
@@ -88,6 +89,9 @@ def test_struct_layout(lib):
     (dict(q_pos0=1 << 40), rea.ATTN_ERR_UNSUPPORTED, b"q_pos0"),
     (dict(scale=float("inf")), rea.ATTN_ERR_INVALID_ARG, b"scale"),
     (dict(head_dim_v=-1), rea.ATTN_ERR_INVALID_ARG, b"head_dim_v"),
+    (dict(softmax_type=3), rea.ATTN_ERR_INVALID_ARG, b"softmax_type"),
+    (dict(softmax_type=2), rea.ATTN_ERR_INVALID_ARG, b"sink"),
+    (dict(softmax_type=2, sink=0x1002), rea.ATTN_ERR_INVALID_ARG, b"sink"),
     (dict(head_dim_v=32), rea.ATTN_ERR_UNSUPPORTED, b"head_dim_v"),
     (dict(head_dim=64, head_dim_v=128), rea.ATTN_ERR_UNSUPPORTED, b"head_dim_v"),
     (dict(dtype=1, head_dim=64, head_dim_v=48), rea.ATTN_ERR_UNSUPPORTED, b"head_dim_v"),
@@ -103,6 +107,21 @@ def test_head_dim_pairs_accepted(lib, dtype, d, dv):
     """Every built (head_dim, head_dim_v) pair passes the argument checks (and then stops at
     the NULL q pointer, so nothing is launched)."""
     assert fwd_status(lib, params(dtype=dtype, head_dim=d, head_dim_v=dv)) == rea.ATTN_ERR_INVALID_ARG
+    assert b"q is NULL" in lib.attn_last_error()
+
+
+def test_version1_struct_is_accepted(lib):
+    """A caller built against the 104-byte struct (no softmax fields) is read as a plain
+    softmax; the bytes after it are not looked at."""
+    class Big(ctypes.Structure):
+        _fields_ = [("p", rea.AttnParams), ("junk", ctypes.c_char * 64)]
+    big = Big()
+    big.p = params(batch=0)
+    big.p.struct_size = 104
+    big.p.softmax_type = 77                      # beyond a version-1 struct: ignored
+    assert lib.attn_fwd(ctypes.byref(big.p), None, None, None, None, None, None, None, None) == rea.ATTN_OK
+    big.p.batch = 1
+    assert fwd_status(lib, big.p) == rea.ATTN_ERR_INVALID_ARG
     assert b"q is NULL" in lib.attn_last_error()
 
 
@@ -162,6 +181,9 @@ def test_sparse_mode_checks(lib):
     p.head_dim_v = 64
     assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_ERR_UNSUPPORTED
     p.head_dim_v = 0
+    p.softmax_type = rea.ATTN_SOFTMAX_OFF_BY_ONE
+    assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_ERR_UNSUPPORTED
+    p.softmax_type = 0
     p.batch = 0
     assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_OK
 

@@ -19,7 +19,7 @@ import torch
 
 import workloads
 from oracle import dense
-from parity import check_close, check_stats
+from parity import check_close, check_stats, check_sum
 
 pytestmark = pytest.mark.gpu
 
@@ -124,6 +124,65 @@ def test_mla_head_dims(gpu, case):
     check_close("dq", dq, dq_r, dt)
     check_close("dk", dk, dk_r, dt)
     check_close("dv", dv, dv_r, dt)
+
+
+SINK_CASES = [
+    # id, dtype, B, S, Hq, Hkv, D, Dv, causal, window, kv_block, softmax_type
+    ("sink_learnable_bf16_causal_gqa4", "bf16", 2, 300, 8, 2, 128, 128, True, (-1, -1), 0, "learnable"),
+    ("sink_off_by_one_bf16_swa37_gqa16", "bf16", 1, 515, 16, 1, 128, 128, True, (37, 0), 0, "off_by_one"),
+    ("sink_learnable_bf16_mla_ring", "bf16", 1, 512, 4, 4, 128, 64, True, (-1, -1), 128, "learnable"),
+    ("sink_learnable_bf16_d64_window", "bf16", 1, 333, 4, 1, 64, 64, False, (20, 5), 0, "learnable"),
+    ("sink_learnable_f32_d64", "f32", 1, 200, 4, 2, 64, 64, True, (-1, -1), 0, "learnable"),
+]
+
+
+@pytest.mark.parametrize("case", SINK_CASES, ids=[c[0] for c in SINK_CASES])
+def test_sink_softmax(gpu, case):
+    """softmax_type off_by_one / learnable: output, statistics (of the keys alone),
+    gradients and the sink-logit gradient against the oracle."""
+    name, dt, B, S, Hq, Hkv, D, Dv, causal, window, kvb, stype = case
+    t = tdtype(dt)
+    seed = zlib.crc32(name.encode()) % 10000
+    q, k, v, do = (rnd((B, S, Hq, D), seed, t), rnd((B, S, Hkv, D), seed + 1, t),
+                   rnd((B, S, Hkv, Dv), seed + 2, t), rnd((B, S, Hq, Dv), seed + 3, t))
+    z = 1.5 * rnd((Hq,), seed + 4, torch.float32) if stype == "learnable" else torch.zeros(Hq)
+    sk = dict(softmax_type=stype, sink=z.to(DEV) if stype == "learnable" else None)
+    kw = dict(causal=causal, window=window, kv_block=kvb)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **kw, **sk)
+    grads = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **kw, **sk)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=causal, window=window, sink=z)
+    check_close("o", o, o_r, dt)
+    check_stats(m, l, m_r, l_r, dt)
+    dq_r, dk_r, dv_r, dz_r = dense.backward(q, k, v, do, causal=causal, window=window, sink=z)
+    for nm, g_, r_ in (("dq", grads[0], dq_r), ("dk", grads[1], dk_r), ("dv", grads[2], dv_r)):
+        check_close(nm, g_, r_, dt)
+    if stype == "learnable":
+        # sum over rows of |P_sink,i D_i|, from the oracle's own output and statistics
+        zn = z.double().numpy()[None, :, None]
+        w = np.exp(zn - np.where(np.isfinite(m_r), m_r, 0.0)) * np.isfinite(m_r)
+        p_sink = w / np.where(l_r + w > 0, l_r + w, 1.0)
+        d_row = np.einsum("bshd,bshd->bhs", do.double().numpy(), o_r)
+        check_sum("dsink", grads[3], dz_r, np.abs(p_sink * d_row).sum(axis=(0, 2)), dt)
+
+
+def test_sink_carry_is_applied_once(gpu):
+    """Two ring steps with the carry handed over: the sink enters only when the output is
+    finalised, so the result equals one call and the oracle."""
+    B, S, Hq, Hkv, D = 1, 384, 4, 2, 128
+    t = torch.bfloat16
+    q, k, v = rnd((B, S, Hq, D), 51, t), rnd((B, 2 * S, Hkv, D), 52, t), rnd((B, 2 * S, Hkv, D), 53, t)
+    z = rnd((Hq,), 54, torch.float32)
+    qd, kd, vd, zd = q.to(DEV), k.to(DEV), v.to(DEV), z.to(DEV)
+    acc, m, l = gpu.attn_fwd(qd, kd[:, S:].contiguous(), vd[:, S:].contiguous(), causal=True, q_pos0=S,
+                             kv_pos0=S, finalize=False, softmax_type="learnable", sink=zd)
+    o, m, l = gpu.attn_fwd(qd, kd[:, :S].contiguous(), vd[:, :S].contiguous(), causal=True, q_pos0=S,
+                           kv_pos0=0, carry_in=True, m=m, l=l, acc=acc, softmax_type="learnable", sink=zd)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=True, q_pos0=S, kv_pos0=0, sink=z)
+    check_close("o (two steps)", o, o_r, "bf16")
+    check_stats(m, l, m_r, l_r, "bf16")
 
 
 def full_inputs(name, with_dout=True):
