@@ -80,3 +80,37 @@ def sparse_attention(q, k, v, sel, *, window: int, block_size: int, scale=None, 
             m[b, t] = mt
             l[b, t] = lt
     return o, m, l
+
+
+def sparse_attention_backward(q, k, v, sel, do, *, window: int, block_size: int, scale=None):
+    """Gradient of ``sparse_attention`` contracted with dO: (dq, dk, dv), each [B, S, E] fp64.
+
+    Per token t, with its candidate slots j (keys K_j, values V_j; zero pads are
+    constants): P = softmax(s), D_t = dO_t . O_t, dP_j = dO_t . V_j,
+    dS_j = P_j (dP_j - D_t), dq_t = scale sum_j dS_j K_j, and every slot that reads
+    a sequence row p passes dk_p += scale dS_j q_t, dv_p += P_j dO_t back to it (a
+    row read by several slots -- duplicates, the -1 clamp to token 0 -- collects all of
+    them; zero pads collect nothing).
+    """
+    q, k, v, do = _flat(q), _flat(k), _flat(v), _flat(do)
+    sel = np.asarray(sel.cpu() if hasattr(sel, "cpu") else sel)
+    B, S, E = q.shape
+    sc = 1.0 / math.sqrt(E) if (scale is None or scale <= 0) else float(scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for t in range(S):
+            pos, pad = candidate_positions(t, sel[b, t], window=window, block_size=block_size, seqlen=S)
+            K = np.where(pad[:, None], 0.0, k[b, pos])
+            V = np.where(pad[:, None], 0.0, v[b, pos])
+            s = sc * (K @ q[b, t])
+            p = np.exp(s - s.max())
+            P = p / p.sum()
+            O = P @ V
+            Dt = do[b, t] @ O
+            dP = V @ do[b, t]
+            dS = P * (dP - Dt)
+            dq[b, t] = sc * (dS @ K)
+            live = ~pad
+            np.add.at(dk[b], pos[live], sc * dS[live, None] * q[b, t][None, :])
+            np.add.at(dv[b], pos[live], P[live, None] * do[b, t][None, :])
+    return dq, dk, dv

@@ -96,6 +96,17 @@ def _mut_sink_in_log2_units(monkeypatch):
                         lambda z, m, l: orig(None if z is None else z * 1.4426950408889634, m, l))
 
 
+def _mut_clamped_slots_pass_no_gradient(monkeypatch):
+    """The -1 clamp reads token 0, so token 0 must also collect those slots' gradients."""
+    orig = sparse.candidate_positions
+
+    def cand(t, sel_row, *, window, block_size, seqlen=None):
+        pos, pad = orig(t, sel_row, window=window, block_size=block_size, seqlen=seqlen)
+        neg = np.concatenate([np.zeros(window, bool), np.repeat(np.asarray(sel_row) < 0, block_size)])
+        return pos, pad | neg
+    monkeypatch.setattr(sparse, "candidate_positions", cand)
+
+
 MUTATIONS = [
     (_mut_gqa_modulo, lambda: td.test_forward_matches_torch_sdpa(td.CASES[0])),
     (_mut_drop_scale, lambda: td.test_forward_matches_torch_sdpa(td.CASES[1])),
@@ -109,6 +120,7 @@ MUTATIONS = [
     (_mut_window_off_by_one, ts.test_sparse_equals_materialised_candidate_list),
     (_mut_clamp_to_last, ts.test_sparse_zero_keys_closed_form),
     (_mut_sink_sign, tk.test_sink_with_zero_left_window_closed_form),
+    (_mut_clamped_slots_pass_no_gradient, lambda: ts.test_sparse_backward_matches_autograd_of_materialised_list(8, 3)),
     (_mut_sink_in_log2_units, lambda: tk.test_sink_forward_and_backward_match_torch(True, (-1, -1), 2, 8)),
 ]
 

@@ -5,6 +5,10 @@ exact ties on integer inputs, closed forms for the first blocks, exact means.
 sparse_attention: K = 0 closed form (uniform weights over all slots, which pins the
 zero padding, the duplicates and the -1 clamp together), constant V, and equality
 with attention over an explicitly materialised candidate list built with torch ops.
+sparse_attention_backward: torch autograd through that materialised list (its gather
+scatters the gradients back to the sequence rows), central finite differences on a tiny
+case, and the K = 0 closed forms (dq = 0; dv of a row = the sum of dO / L over the slots
+that read it).
 """
 import math
 
@@ -124,6 +128,10 @@ def test_sparse_constant_values():
 
 
 def materialised_route(q, k, v, sel, W, bs):
+    return materialised_route_t(q, k, v, sel, W, bs).detach().numpy()
+
+
+def materialised_route_t(q, k, v, sel, W, bs):
     """Candidate list built with tensor ops, as the page's function does: zero-padded
     windows via unfold, selected rows via index arithmetic with negatives clamped to 0,
     concatenation, einsum, softmax."""
@@ -140,7 +148,7 @@ def materialised_route(q, k, v, sel, W, bs):
     V = torch.cat([vw, vs], 2)
     s = torch.einsum("bqd,bqwd->bqw", q, K) / math.sqrt(E)
     p = torch.softmax(s, -1)
-    return torch.einsum("bqw,bqwd->bqd", p, V).numpy()
+    return torch.einsum("bqw,bqwd->bqd", p, V)
 
 
 def test_sparse_equals_materialised_candidate_list():
@@ -173,3 +181,66 @@ def test_sparse_block_past_the_end_reads_zero_rows():
     o2, m2, l2 = sparse.sparse_attention(q2, k2, v2, sel2, window=W, block_size=bs)
     np.testing.assert_allclose(o, o2[:, :S], atol=1e-14, rtol=0)
     np.testing.assert_allclose(l, l2[:, :S], rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("W,n", [(8, 3), (5, 2)])
+def test_sparse_backward_matches_autograd_of_materialised_list(W, n):
+    B, S, E, bs = 2, 72, 16, 8
+    q, k, v, do = rnd((B, S, E), 21), rnd((B, S, E), 22), rnd((B, S, E), 23), rnd((B, S, E), 24)
+    sel = select.block_select(q, k, block_size=bs, top_n=n)     # has -1 entries early on
+    assert (sel < 0).any()
+    qt, kt, vt = (x.clone().requires_grad_(True) for x in (q, k, v))
+    materialised_route_t(qt, kt, vt, sel, W, bs).backward(do)
+    dq, dk, dv = sparse.sparse_attention_backward(q, k, v, sel, do, window=W, block_size=bs)
+    np.testing.assert_allclose(dq, qt.grad.numpy(), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-12, rtol=0)
+
+
+def test_sparse_backward_finite_differences():
+    B, S, E, bs, n, W = 1, 24, 4, 4, 2, 3
+    q, k, v, do = (rnd((B, S, E), s).numpy() for s in (25, 26, 27, 28))
+    sel = select.block_select(q, k, block_size=bs, top_n=n)
+    grads = sparse.sparse_attention_backward(q, k, v, sel, do, window=W, block_size=bs)
+    h = 1e-6
+    for x, g in zip((q, k, v), grads):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = x[i]
+            x[i] = old + h
+            lp = float((sparse.sparse_attention(q, k, v, sel, window=W, block_size=bs)[0] * do).sum())
+            x[i] = old - h
+            lm = float((sparse.sparse_attention(q, k, v, sel, window=W, block_size=bs)[0] * do).sum())
+            x[i] = old
+            num[i] = (lp - lm) / (2 * h)
+        assert np.abs(num - g).max() < 1e-6 * max(1.0, np.abs(g).max())
+
+
+def test_sparse_backward_zero_keys_closed_form():
+    """K = 0: every logit is 0, so P = 1/L on each of the L = W + n*bs slots.  Then
+    dq = scale sum_j dS_j K_j = 0, and a row p collects dv_p = sum over the slots that read
+    it of dO_t / L (window slots of tokens p..p+W-1, selected slots, and for row 0 every
+    slot of a -1 block)."""
+    B, S, E, bs, n, W = 1, 48, 8, 8, 2, 4
+    q, v, do = rnd((B, S, E), 29), rnd((B, S, E), 30), rnd((B, S, E), 31)
+    k = torch.zeros((B, S, E), dtype=torch.float64)
+    sel = np.full((B, S, n), -1, dtype=np.int64)
+    for t in range(S):
+        i = t // bs
+        chosen = list(range(max(0, i - n), i))
+        sel[0, t, n - len(chosen):] = chosen
+    dq, dk, dv = sparse.sparse_attention_backward(q, k, v, sel, do, window=W, block_size=bs)
+    L = W + n * bs
+    np.testing.assert_allclose(dq, 0.0, atol=1e-15)
+    ref = np.zeros((S, E))
+    dO = do.numpy()[0]
+    for t in range(S):
+        for p in range(t - W + 1, t + 1):
+            if p >= 0:
+                ref[p] += dO[t] / L
+        for c in sel[0, t]:
+            for r in range(bs):
+                ref[0 if c < 0 else c * bs + r] += dO[t] / L
+    np.testing.assert_allclose(dv[0], ref, atol=1e-13, rtol=0)
