@@ -168,20 +168,36 @@ def sparse_cpu_baseline(w, q, k, v, sel, budget_s):
 
 
 def bench_sparse(torch, rea, workloads, w, dev, args):
-    """Block selection + gathered sparse attention (one step = both)."""
+    """Block selection + gathered sparse attention (one step = both), and with
+    --sparse-backward its gradient too."""
     q, k, v, _ = workloads.generate(w, with_dout=False)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     B, S, E = w.batch, w.seqlen, w.head_dim
     idx = torch.empty((B, S, w.top_n), dtype=torch.int32, device=dev)
     o = torch.empty_like(qd)
+    m = torch.empty((B, S), dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    state = {}
+
+    def fwd():
+        state["o"], state["m"], state["l"] = rea.attn_fwd_sparse(qd, kd, vd, idx, window=w.sparse_window,
+                                                                 block_size=w.block_size, out=o)
     segs = [("block_select", lambda: rea.block_select(qd, kd, block_size=w.block_size, top_n=w.top_n, out=idx)),
-            ("attn_fwd_sparse", lambda: rea.attn_fwd_sparse(qd, kd, vd, idx, window=w.sparse_window,
-                                                            block_size=w.block_size, out=o))]
+            ("attn_fwd_sparse", fwd)]
+    if args.sparse_backward:
+        dod = workloads.random_tensor(q.shape, w.seed + 50, dtype=torch.bfloat16).to(dev)
+        grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
+        segs.append(("attn_bwd_sparse", lambda: rea.attn_bwd_sparse(
+            qd, kd, vd, idx, o, dod, state["m"], state["l"], window=w.sparse_window, block_size=w.block_size,
+            out=grads)))
     seg_ms, wall = time_segments(torch, segs, args.steps, args.warmup, torch.cuda.current_stream(dev))
     slots = w.sparse_window + w.top_n * w.block_size
     gathered = B * S * slots * E * 2 * 2
     f_sparse = B * S * slots * E * 4.0
     f_select = B * 2.0 * E * w.block_size * sum(range(S // w.block_size))
+    # backward per (token, slot): S and dP recomputed, dQ, dK, dV (10 E flops); it gathers
+    # K, V for dq and Q, dO for dk, dv: twice the forward's gathered bytes
+    f_bwd = B * S * slots * E * 10.0 if args.sparse_backward else 0.0
     ms = wall / args.steps * 1e3
     kernels = {"block_select": {"avg_us": round(seg_ms["block_select"] * 1e3, 2),
                                 "fp64_gflop": round(f_select / 1e9, 3),
@@ -190,18 +206,27 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
                                    "gathered_gb": round(gathered / 1e9, 3),
                                    "gathered_gbs": round(gathered / (seg_ms["attn_fwd_sparse"] * 1e-3) / 1e9, 1),
                                    "tflops": round(f_sparse / (seg_ms["attn_fwd_sparse"] * 1e-3) / 1e12, 2)}}
-    ach = gathered / (seg_ms["attn_fwd_sparse"] * 1e-3) / 1e9
-    out = {"metric": METRIC, "value": round((f_sparse + f_select) / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+    if args.sparse_backward:
+        tb = seg_ms["attn_bwd_sparse"] * 1e-3
+        kernels["attn_bwd_sparse"] = {"avg_us": round(tb * 1e6, 2), "gathered_gb": round(2 * gathered / 1e9, 3),
+                                      "gathered_gbs": round(2 * gathered / tb / 1e9, 1),
+                                      "tflops": round(f_bwd / tb / 1e12, 2)}
+    # roofline of the dominant attention kernel (the gradient's when it is timed)
+    rk = "attn_bwd_sparse" if args.sparse_backward else "attn_fwd_sparse"
+    rbytes = 2 * gathered if args.sparse_backward else gathered
+    ach = rbytes / (seg_ms[rk] * 1e-3) / 1e9
+    out = {"metric": METRIC, "value": round((f_sparse + f_select + f_bwd) / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
-           "config": {"workload": w.name, "batch": B, "seq_len": S, "embed": E, "block_size": w.block_size,
+           "config": {"workload": w.name + ("+backward" if args.sparse_backward else ""), "batch": B,
+                      "seq_len": S, "embed": E, "block_size": w.block_size,
                       "top_n": w.top_n, "window": w.sparse_window, "parallelism": "none (1 GPU)"},
            "kernels": kernels,
-           "roofline": {"kernel": "attn_fwd_sparse", "bound": "hbm", "achieved": round(ach, 1),
+           "roofline": {"kernel": rk, "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                        "avg_us": round(seg_ms["attn_fwd_sparse"] * 1e3, 2), "alg_bytes_per_launch": gathered,
-                        "traffic": measured_traffic(w.name, "attn_fwd_sparse")}}
+                        "avg_us": round(seg_ms[rk] * 1e3, 2), "alg_bytes_per_launch": rbytes,
+                        "traffic": measured_traffic(w.name, rk)}}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = sparse_cpu_baseline(w, q, k, v, idx.cpu().numpy(), args.cpu_budget)
     print(json.dumps(out), flush=True)
@@ -213,6 +238,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ring_sim_causal_s8192")
+    ap.add_argument("--sparse-backward", action="store_true",
+                    help="block-sparse workload: also time the gradient (attn_bwd with sel_idx)")
     ap.add_argument("--softmax", default="vanilla", choices=["vanilla", "off_by_one", "learnable"],
                     help="sink softmax variant of the dense workloads (learnable: seeded N(0,1) logits)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")

@@ -196,8 +196,17 @@ int attn_fwd(const attn_params* params, const void* q, const void* k, const void
  *   dq [out] [B, Sq, Hq, D]; dk, dv [out] [B, Skv, Hkv, D] (element type of q).
  *   workspace        device scratch of at least attn_bwd_workspace_bytes(params)
  *                    bytes (256-byte aligned); its contents are overwritten.
- * flags: 0 or a combination of the ATTN_BWD_* flags; sel_idx must be NULL.  The
- * result is bitwise reproducible run to run.
+ * flags: 0 or a combination of the ATTN_BWD_* flags.  The result is bitwise
+ * reproducible run to run.
+ *
+ * Gathered block-sparse mode (params->sel_idx != NULL, the same params as the sparse
+ * attn_fwd call, sel_block 32): the gradient of "AnnAttention"'s
+ * faiss_block_attention.  Per token t with slots j (window ++ selected blocks),
+ * dS_tj = P_tj (dO_t . v_j - D_t) and dq_t = scale sum_j dS_tj k_j; every slot that
+ * reads a sequence row p passes scale dS_tj q_t to dk_p and P_tj dO_t to dv_p (the -1
+ * clamp makes row 0 collect those slots; zero pads and rows past the end pass nothing).
+ * q, k, v, o, dout, dq, dk, dv are bf16 [B, S, 512]; m, l fp32 [B, S] from the sparse
+ * forward; flags must be 0.
  */
 int attn_bwd(const attn_params* params, const void* q, const void* k, const void* v,
              const void* o, const void* dout, const float* m, const float* l,

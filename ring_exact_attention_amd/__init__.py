@@ -12,6 +12,7 @@ Entry points (names as in the C ABI):
   attn_bwd(q, k, v, o, dout, m, l, ...)  -> (dq, dk, dv)
   block_select(q, k, block_size, top_n)  -> idx int32 [B, S, top_n]
   attn_fwd_sparse(q, k, v, idx, ...)     -> (o, m, l)      (attn_fwd with sel_idx)
+  attn_bwd_sparse(q, k, v, idx, o, dout, m, l, ...) -> (dq, dk, dv)  (attn_bwd with sel_idx)
 """
 from __future__ import annotations
 
@@ -331,6 +332,38 @@ def attn_fwd_sparse(q, k, v, idx, *, window=32, block_size=32, scale=None, out=N
     _check(lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l), None,
                           _stream(q)))
     return o, m, l
+
+
+def attn_bwd_sparse(q, k, v, idx, o, dout, m, l, *, window=32, block_size=32, scale=None,
+                    workspace=None, out=None):
+    """Gradients (dq, dk, dv) of attn_fwd_sparse's output o for upstream gradient dout."""
+    q, k, v, o, dout = _joint(q), _joint(k), _joint(v), _joint(o), _joint(dout)
+    for t, nme in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, nme, torch.bfloat16, q.device)
+    _need(idx, "idx", torch.int32, q.device)
+    _need(m, "m", torch.float32, q.device)
+    _need(l, "l", torch.float32, q.device)
+    B, S, E = q.shape
+    top_n = idx.shape[-1]
+    if idx.shape != (B, S, top_n) or m.shape != (B, S) or l.shape != (B, S):
+        raise ValueError("idx must be [B, S, top_n] and m, l [B, S]")
+    p = AttnParams()
+    p.struct_size = ctypes.sizeof(AttnParams)
+    p.dtype = ATTN_BF16
+    p.batch, p.seqlen_q, p.seqlen_kv = B, S, S
+    p.num_q_heads = p.num_kv_heads = 1
+    p.head_dim = E
+    p.scale = 0.0 if scale is None else float(scale)
+    p.sel_idx = idx.data_ptr()
+    p.top_n, p.sel_block, p.sparse_window = int(top_n), int(block_size), int(window)
+    need = int(lib().attn_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    _check(lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(m), _ptr(l),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq, dk, dv
 
 
 def flops_fwd(visible_pairs_per_head: int, heads: int, batch: int, head_dim: int) -> float:

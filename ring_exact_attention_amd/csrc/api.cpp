@@ -186,9 +186,8 @@ int hip_status(hipError_t e) {
   return ok();
 }
 
-// Gathered block-sparse forward (sel_idx != NULL).
-int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o, float* m,
-               float* l, void* stream) {
+// Checks shared by the gathered block-sparse forward and backward (sel_idx != NULL).
+int check_sparse(const attn_params* p) {
   if (p->struct_size != sizeof(attn_params))
     return fail(ATTN_ERR_INVALID_ARG, "params->struct_size does not match this library");
   if (p->head_dim_v != 0 && p->head_dim_v != p->head_dim)
@@ -210,6 +209,14 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
     return fail(ATTN_ERR_INVALID_ARG, "sparse_window must be in 1..64");
   if (p->flags) return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes no flags");
   if (std::isinf(p->scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  return ATTN_OK;
+}
+
+// Gathered block-sparse forward (sel_idx != NULL).
+int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o, float* m,
+               float* l, void* stream) {
+  int st0 = check_sparse(p);
+  if (st0) return st0;
   if (p->batch == 0 || p->seqlen_q == 0) return ok();
   int st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
@@ -232,6 +239,57 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
   a.scale = p->scale > 0.f ? p->scale : 1.f / std::sqrt((float)a.E);
   a.scale_log2 = a.scale * rea::kLog2e;
   return hip_status(rea::launch_sparse(a, (hipStream_t)stream));
+}
+
+size_t sparse_bwd_workspace(const attn_params* p) {
+  const size_t n = (size_t)(p->batch > 0 ? p->batch : 0) * (p->seqlen_q > 0 ? p->seqlen_q : 0) * sizeof(float);
+  return 2 * align_up(n > 0 ? n : 1);
+}
+
+// Gradient of the gathered block-sparse attention (sel_idx != NULL).
+int sparse_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* m, const float* l, void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_sparse(p);
+  if (st) return st;
+  if (p->sel_block != 32)
+    return fail(ATTN_ERR_UNSUPPORTED, "the sparse backward supports sel_block 32");
+  if (p->batch == 0 || p->seqlen_q == 0) return ok();
+  const size_t need = sparse_bwd_workspace(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, fmt("workspace of %lld bytes needed, %lld given", (long long)need,
+                                        (long long)(workspace ? workspace_bytes : 0)));
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")) || (st = check_ptr(dout, "dout")) || (st = check_ptr(m, "m")) ||
+      (st = check_ptr(l, "l")) || (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) ||
+      (st = check_ptr(dv, "dv")))
+    return st;
+  rea::SparseBwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sel = p->sel_idx;
+  a.o = o;
+  a.dout = dout;
+  a.m = m;
+  a.l = l;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const size_t n = (size_t)p->batch * p->seqlen_q * sizeof(float);
+  a.Dvec = (float*)workspace;
+  a.lse2 = (float*)((char*)workspace + align_up(n));
+  a.B = p->batch;
+  a.S = p->seqlen_q;
+  a.E = p->head_dim;
+  a.top_n = p->top_n;
+  a.sel_block = p->sel_block;
+  a.window = p->sparse_window;
+  a.scale = p->scale > 0.f ? p->scale : 1.f / std::sqrt((float)a.E);
+  a.scale_log2 = a.scale * rea::kLog2e;
+  return hip_status(rea::launch_sparse_bwd(a, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -294,6 +352,12 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
 size_t attn_bwd_workspace_bytes(const attn_params* p_in) {
   attn_params tmp;
   const attn_params* p = current_layout(p_in, tmp);
+  if (p && p->sel_idx) {
+    const std::string saved = g_err;
+    if (p->struct_size != sizeof(attn_params) || check_sparse(p) != ATTN_OK) return 0;
+    g_err = saved;
+    return sparse_bwd_workspace(p);
+  }
   Problem r;
   const std::string saved = g_err;
   if (!p || check_dense(p, true, r) != ATTN_OK) return 0;
@@ -309,7 +373,8 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
              void* workspace, size_t workspace_bytes, void* stream) {
   attn_params tmp;
   const attn_params* p = current_layout(p_in, tmp);
-  if (p && p->sel_idx) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd has no sparse mode");
+  if (p && p->sel_idx)
+    return sparse_bwd(p, q, k, v, o, dout, m, l, dq, dk, dv, workspace, workspace_bytes, stream);
   Problem r;
   int st = check_dense(p, true, r);
   if (st) return st;

@@ -108,6 +108,25 @@ struct SparseArgs {
   float scale_log2, scale;
 };
 
+// Backward of the gathered block-sparse attention.
+struct SparseBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* sel;
+  const void* o;
+  const void* dout;
+  const float* m;
+  const float* l;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* Dvec;        // [B, S] workspace: rowsum(dO * o)
+  float* lse2;        // [B, S] workspace: m*log2(e) + log2(l)
+  int B, S, E, top_n, sel_block, window;
+  float scale_log2, scale;
+};
+
 // ---------------------------------------------------------------- device helpers
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {

@@ -17,5 +17,6 @@ int bwd_k_tile_rows(int dtype);
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
+hipError_t launch_sparse_bwd(const SparseBwdArgs& a, hipStream_t stream);
 
 }  // namespace rea

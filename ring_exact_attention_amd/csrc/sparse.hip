@@ -7,10 +7,10 @@
 //
 #include "common.h"
 #include "launch.h"
+#include "sparse_common.h"
 
 namespace rea {
 
-constexpr int kSpE = 512;            // joint embedding (8 bf16 per lane)
 // ---------------------------------------------------------------------------------
 // Block-shared form (E = 512, bs in {16, 32, 64}): one workgroup per 32 consecutive
 // tokens.  The tokens' selected block indices are sorted and deduplicated in LDS; each
@@ -24,11 +24,6 @@ constexpr int kSpE = 512;            // joint embedding (8 bf16 per lane)
 //   O^T += V^T P^T on the wave's embedding slice (V staged row-major in LDS, read
 //   transposed with ds_read_b64_tr_b16).
 // A block shared by several tokens is read once for all of them.
-constexpr int kUQ = 32;              // tokens per workgroup
-constexpr int kUDW = 128;            // embedding slice per wavefront
-constexpr int kUPITCH = kUDW + 32;   // V slice row pitch (elements): conflict-free tr reads
-constexpr int kUMaxEnt = 512;        // 32 tokens x top_n (<= 16)
-constexpr int kUSentinel = 0x7fffffff;
 
 __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   // LDS: partial scores 16 KiB | V slices 40 KiB (setup scratch reuses it) | counts 16 KiB
@@ -43,66 +38,9 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const int nqb = (a.S + kUQ - 1) / kUQ;
   const int b = blockIdx.x / nqb, t0 = (blockIdx.x % nqb) * kUQ;
   const int n = a.top_n, bs = a.sel_block, W = a.window;
-  const int ne = kUQ * n;
 
   // ---- setup: sort (block, token) pairs, deduplicate, count per token
-  int* skey = (int*)&sV[0][0];
-  int* stok = skey + kUMaxEnt;
-  for (int k = tid; k < kUMaxEnt; k += 256) {
-    int key = kUSentinel, tok = 0;
-    if (k < ne) {
-      const int t = k / n, j = k % n;
-      if (t0 + t < a.S) {
-        const int c = a.sel[((size_t)b * a.S + t0 + t) * n + j];
-        key = c < 0 ? -1 : c;
-        tok = t;
-      }
-    }
-    skey[k] = key;
-    stok[k] = tok;
-  }
-  __syncthreads();
-  for (int size = 2; size <= kUMaxEnt; size <<= 1) {          // bitonic sort by key
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int k = tid; k < kUMaxEnt / 2; k += 256) {
-        const int lo = 2 * k - (k & (stride - 1)), hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const int ka = skey[lo], kb = skey[hi];
-        if ((ka > kb) == up) {
-          skey[lo] = kb;
-          skey[hi] = ka;
-          const int ta = stok[lo];
-          stok[lo] = stok[hi];
-          stok[hi] = ta;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  if (wave == 0) {                                             // union index of each entry
-    int* suid = stok + kUMaxEnt;
-    int running = 0;
-    for (int c0 = 0; c0 < kUMaxEnt; c0 += 64) {
-      const int k = c0 + lane;
-      const int key = skey[k];
-      const bool first = key != kUSentinel && (k == 0 || skey[k - 1] != key);
-      const uint64_t mask = __ballot(first);
-      const int before = __popcll(mask & ((1ull << lane) - 1));
-      suid[k] = running + before + (first ? 0 : -1);
-      if (first) ublk[running + before] = key;
-      running += __popcll(mask);
-    }
-    if (lane == 0) s_nu = running;
-  }
-  for (int k = tid; k < kUMaxEnt * (kUQ / 4); k += 256) ((uint32_t*)ucnt)[k] = 0u;
-  __syncthreads();
-  {
-    const int* suid = stok + kUMaxEnt;
-    for (int k = tid; k < kUMaxEnt; k += 256)
-      if (skey[k] != kUSentinel) atomicAdd(&ucnt[suid[k]][stok[k] >> 2], 1u << (8 * (stok[k] & 3)));
-  }
-  __syncthreads();
-  const int nu = s_nu;
+  const int nu = build_union(a.sel, a.S, n, b, t0, (int*)&sV[0][0], ucnt, ublk, &s_nu);
 
   // ---- main loop over 32-row blocks: window blocks, then union blocks
   const int nwin = (W + kUQ - 1 + 31) / 32;

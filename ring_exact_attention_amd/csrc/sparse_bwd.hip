@@ -1,0 +1,502 @@
+// Backward pass of the attention over gathered candidates ("AnnAttention",
+// faiss_block_attention: the model trains through it).
+//
+// Token t attends to its slots j (window of W keys ending at t, zero vectors before
+// position 0; then the bs rows of each selected block, -1 reading token 0).  With the
+// forward's statistics, P(t, j) = exp(s_tj - LSE_t) and
+//   D_t = dO_t . O_t,  dP(t, j) = dO_t . v_j,  dS(t, j) = P(t, j) (dP(t, j) - D_t),
+//   dq_t = scale sum_j dS(t, j) k_j,
+// and every slot j that reads sequence row p passes scale dS(t, j) q_t to dk_p and
+// P(t, j) dO_t to dv_p (duplicates and the -1 clamp to token 0 add up; zero pads pass
+// nothing).  Slots of one token that read the same row have the same logit, so they are
+// handled together with a weight w(t, row) = the number of such slots.
+//
+// Two kernels, both owner-computes (no atomics, bitwise reproducible):
+//  * sparse_bwd_dq_kernel -- one workgroup per 32 consecutive tokens, walking the same
+//    deduplicated union of selected blocks and window blocks as the forward kernel,
+//    twice: the first walk computes D_t = sum_j P(t, j) dP(t, j) (equal to dO_t . O_t,
+//    but from the fp32 probabilities instead of the stored bf16 output: a row that many
+//    slots read, such as row 0 under the -1 clamp, sums P (dP - D) over hundreds of
+//    tokens, and the rounding of the stored output would show there), the second dS and
+//    dq; D_t and the LSE go to the workspace for the dk/dv kernel;
+//  * sparse_bwd_dkdv_kernel -- one workgroup per 32-row key tile (one selection block,
+//    bs = 32): the tokens whose window covers the tile, then every token that selected
+//    the block (found by scanning the selections in token order), and for the tile at
+//    position 0 the tokens with -1 entries, whose bs clamped slots all read row 0.
+// Both split the embedding E = 512 over their four waves (128 each) and sum the partial
+// score tiles through LDS, as the forward kernel does.
+#include "common.h"
+#include "launch.h"
+#include "sparse_common.h"
+#include "tiles.h"
+
+namespace rea {
+
+__global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sS[4][64 * 16];   // partial scores per wave
+  __shared__ __attribute__((aligned(16))) float sP[4][64 * 16];   // partial dP per wave
+  __shared__ __attribute__((aligned(16))) __bf16 sK[4][32 * kUPITCH];   // K slices (setup scratch)
+  __shared__ uint32_t ucnt[kUMaxEnt][kUQ / 4];
+  __shared__ int ublk[kUMaxEnt];
+  __shared__ int s_nu;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int li = lane & 31, lh = lane >> 5;
+  const int nqb = (a.S + kUQ - 1) / kUQ;
+  const int b = blockIdx.x / nqb, t0 = (blockIdx.x % nqb) * kUQ;
+  const int n = a.top_n, bs = a.sel_block, W = a.window;
+
+  const int nu = build_union(a.sel, a.S, n, b, t0, (int*)&sK[0][0], ucnt, ublk, &s_nu);
+
+  const int nwin = (W + kUQ - 1 + 31) / 32;
+  const int nsub = (bs + 31) / 32;
+  const int nsteps = nwin + nu * nsub;
+  const int wstart = t0 - W + 1;
+  const uint32_t row_b = (uint32_t)kSpE * 2;
+  const size_t bbase = (size_t)b * a.S * kSpE;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + bbase, (uint32_t)a.S * row_b);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + bbase, (uint32_t)a.S * row_b);
+  const int e0 = kUDW * wave;
+  const int tok = t0 + li;
+  const bool tok_ok = tok < a.S;
+
+  // Q^T and dO^T slices as B operands (lane (li, lh): token li, e0 + 16kk + 8lh ..+7).
+  bf16x8 qreg[kUDW / 16], doreg[kUDW / 16];
+#pragma unroll
+  for (int kk = 0; kk < kUDW / 16; ++kk) {
+    u32x4 uq = {0u, 0u, 0u, 0u}, ug = uq;
+    if (tok_ok) {
+      const size_t off = bbase + (size_t)tok * kSpE + e0 + 16 * kk + 8 * lh;
+      uq = *(const u32x4*)((const __bf16*)a.q + off);
+      ug = *(const u32x4*)((const __bf16*)a.dout + off);
+    }
+    qreg[kk] = as_bf16x8(uq);
+    doreg[kk] = as_bf16x8(ug);
+  }
+  const size_t st = (size_t)b * a.S + (tok_ok ? tok : 0);
+  float lse2 = INFINITY;
+  if (tok_ok) {
+    const float l = a.l[st];
+    lse2 = l > 0.f ? fmaf(a.m[st], kLog2e, log2f(l)) : INFINITY;
+  }
+
+  auto row_pos = [&](int step, int r) -> int {      // sequence row of row r of a step
+    if (step < nwin) return wstart + 32 * step + r;    // negative: zero pad (reads 0)
+    const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;
+    const int c = ublk[u];
+    return c < 0 ? 0 : c * bs + 32 * h + r;
+  };
+  // K and V rows as A operands: lane (li, lh) holds row li, e0 + 16kk + 8lh ..+7.
+  u32x4 kbuf[kUDW / 16], vbuf[kUDW / 16];
+  auto load_step = [&](int step) {
+    const int pk = row_pos(step, li);
+#pragma unroll
+    for (int kk = 0; kk < kUDW / 16; ++kk) {
+      const uint32_t off = (uint32_t)pk * row_b + 2u * (e0 + 16 * kk + 8 * lh);
+      kbuf[kk] = buf_load16(rk, off, 0);
+      vbuf[kk] = buf_load16(rv, off, 0);
+    }
+  };
+
+  f32x16 acc[kUDW / 32];                             // dQ^T slice: 4 blocks of 32 e x 32 tokens
+#pragma unroll
+  for (int db = 0; db < kUDW / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  const int tg = lane >> 4, tj = lane & 15;
+  const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * kUPITCH + 16 * (tg & 1) + 4 * (tj & 3);
+
+  // Two walks over the steps: pass 0 accumulates D_t, pass 1 uses it for dS and dQ.
+  float Dt = 0.f, dsum = 0.f;
+  for (int pass = 0; pass < 2; ++pass) {
+    if (nsteps > 0) load_step(0);
+    for (int step = 0; step < nsteps; ++step) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < kUDW / 16; ++kk) {
+        s = mfma32(as_bf16x8(kbuf[kk]), qreg[kk], s);
+        dp = mfma32(as_bf16x8(vbuf[kk]), doreg[kk], dp);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 s4 = {s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
+        const f32x4 p4 = {dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3]};
+        *(f32x4*)&sS[wave][lane * 16 + 4 * g] = s4;
+        *(f32x4*)&sP[wave][lane * 16 + 4 * g] = p4;
+      }
+      if (pass == 1) {
+#pragma unroll
+        for (int kk = 0; kk < kUDW / 16; ++kk) *(u32x4*)&sK[wave][li * kUPITCH + 16 * kk + 8 * lh] = kbuf[kk];
+      }
+      __syncthreads();
+      if (step + 1 < nsteps) load_step(step + 1);
+
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 s4 = *(const f32x4*)&sS[w2][lane * 16 + 4 * g];
+          const f32x4 p4 = *(const f32x4*)&sP[w2][lane * 16 + 4 * g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[4 * g + e] += s4[e];
+            dp[4 * g + e] += p4[e];
+          }
+        }
+      // weights of (token li, row 8(r>>2) + 4lh + (r&3)), as in the forward kernel
+      float wt[16];
+      if (step < nwin) {
+        const int p0 = wstart + 32 * step + 4 * lh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = p0 + 8 * (r >> 2) + (r & 3);
+          wt[r] = (tok_ok && p >= tok - W + 1 && p <= tok) ? 1.f : 0.f;
+        }
+      } else {
+        const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;
+        const float cnt = (float)((ucnt[u][li >> 2] >> (8 * (li & 3))) & 0xffu);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * h + 8 * (r >> 2) + 4 * lh + (r & 3);
+          wt[r] = row < bs ? cnt : 0.f;
+        }
+      }
+      if (pass == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsum = fmaf(wt[r] * fast_exp2(fmaf(s[r], a.scale_log2, -lse2)), dp[r], dsum);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = wt[r] * fast_exp2(fmaf(s[r], a.scale_log2, -lse2));
+          dp[r] = p * (dp[r] - Dt);                    // dS
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4 pb;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(dp[8 * ks + 2 * w], dp[8 * ks + 2 * w + 1]);
+          const bf16x8 dsb = as_bf16x8(pb);
+#pragma unroll
+          for (int db = 0; db < kUDW / 32; ++db) {
+            const __bf16* kp0 = &sK[wave][tr_off + 16 * ks * kUPITCH + 32 * db];
+            const bf16x8 ka = join_bf16x8(lds_read_tr16(kp0), lds_read_tr16(kp0 + 8 * kUPITCH));
+            acc[db] = mfma32(ka, dsb, acc[db]);
+          }
+        }
+      }
+      __syncthreads();                                 // sS / sP / sK are rewritten next step
+    }
+    if (pass == 0) {
+      // the two half-waves hold different rows of each step; every wave has the full sums
+      Dt = tok_ok ? dsum + other_half(dsum) : 0.f;
+      if (tok_ok && wave == 0 && lh == 0) {
+        a.Dvec[st] = Dt;
+        a.lse2[st] = lse2;
+      }
+    }
+  }
+
+  if (tok_ok) {
+    __bf16* op = (__bf16*)a.dq + bbase + (size_t)tok * kSpE + e0;
+#pragma unroll
+    for (int db = 0; db < kUDW / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][4 * g] * a.scale, acc[db][4 * g + 1] * a.scale);
+        w[1] = pack_bf16x2(acc[db][4 * g + 2] * a.scale, acc[db][4 * g + 3] * a.scale);
+        *(u32x2*)(op + 32 * db + 8 * g + 4 * lh) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// dk, dv: one workgroup per 32-row key tile (selection block c = tile index, bs = 32).
+// A lane owns one key row (B operand of S = Q K^T and dP = dO V^T, K and V slices in
+// registers); tiles of 32 tokens are gathered into LDS (row-major Q and dO slices, read
+// as rows for S / dP and transposed for dV^T += dO^T P and dK^T += Q^T dS).
+constexpr int kSpList = 512;         // pending token list (a scan chunk of 256 + leftover)
+
+__global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a) {
+  using QL = TileLayout<kUDW, kBothRead>;
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[4][QL::elems(kUQ)];
+  __shared__ __attribute__((aligned(16))) __bf16 sG[4][QL::elems(kUQ)];
+  __shared__ __attribute__((aligned(16))) float sS[4][64 * 16];
+  __shared__ __attribute__((aligned(16))) float sP[4][64 * 16];
+  __shared__ __attribute__((aligned(16))) float sLse[kUQ];
+  __shared__ __attribute__((aligned(16))) float sD[kUQ];
+  __shared__ float sWa[kUQ], sWb[kUQ];               // per token: weight of every row / extra on row 0
+  __shared__ int sTok[kUQ];
+  __shared__ int lstT[kSpList];
+  __shared__ int lstC[kSpList];                      // count | (count of -1 entries) << 8
+  __shared__ int sWaveN[4];
+  __shared__ int s_npend;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int li = lane & 31, lh = lane >> 5;
+  const int nkt = (a.S + 31) / 32;
+  const int b = blockIdx.x / nkt, c = blockIdx.x % nkt;
+  const int r0 = 32 * c;
+  const int n = a.top_n, W = a.window;
+  const int e0 = kUDW * wave;
+  const uint32_t row_b = (uint32_t)kSpE * 2;
+  const size_t bbase = (size_t)b * a.S * kSpE;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const __bf16*)a.q + bbase, (uint32_t)a.S * row_b);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const __bf16*)a.dout + bbase, (uint32_t)a.S * row_b);
+  const int key = r0 + li;
+  const bool key_ok = key < a.S;
+
+  bf16x8 kreg[kUDW / 16], vreg[kUDW / 16];
+#pragma unroll
+  for (int kk = 0; kk < kUDW / 16; ++kk) {
+    u32x4 uk = {0u, 0u, 0u, 0u}, uv = uk;
+    if (key_ok) {
+      const size_t off = bbase + (size_t)key * kSpE + e0 + 16 * kk + 8 * lh;
+      uk = *(const u32x4*)((const __bf16*)a.k + off);
+      uv = *(const u32x4*)((const __bf16*)a.v + off);
+    }
+    kreg[kk] = as_bf16x8(uk);
+    vreg[kk] = as_bf16x8(uv);
+  }
+  f32x16 dk[kUDW / 32], dv[kUDW / 32];
+#pragma unroll
+  for (int db = 0; db < kUDW / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.f;
+      dv[db][r] = 0.f;
+    }
+  const int tg = lane >> 4, tj = lane & 15;
+  const int tr_off = QL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
+  const int q_off = QL::idx(li, 8 * lh);
+
+  // One tile of up to 32 tokens: tokfn(i) -> (token or -1, weight of every row, extra
+  // weight on row 0); with `win` the weight is instead 1 for the rows in the token's
+  // window.  Gathers the tokens' Q / dO slices and statistics, then accumulates this
+  // tile's part of dK^T and dV^T.  Outside the window pass a weight stands for several
+  // slots (up to bs * top_n on row 0 under the -1 clamp), so P and dS enter the MFMAs as
+  // a bf16 pair hi + lo: one bf16 rounding of the merged weight would cost as much as
+  // that many roundings of the separate slots.
+  auto tile = [&](auto tokfn, bool win) {
+    // gather: 32 tokens x 16 chunks of 16 bytes per tensor per wave -> 8 per lane
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int cidx = lane + 64 * u, i = cidx >> 4, ch = cidx & 15;
+      float wa, wb;
+      const int t = tokfn(i, wa, wb);
+      const uint32_t off = t >= 0 ? (uint32_t)t * row_b + 2u * (e0 + 8 * ch) : 0xffffffffu;
+      *(u32x4*)&sQ[wave][QL::idx(i, 8 * ch)] = buf_load16(rq, off, 0);
+      *(u32x4*)&sG[wave][QL::idx(i, 8 * ch)] = buf_load16(rg, off, 0);
+    }
+    if (tid < kUQ) {
+      float wa, wb;
+      const int t = tokfn(tid, wa, wb);
+      const size_t st = (size_t)b * a.S + (t >= 0 ? t : 0);
+      sLse[tid] = t >= 0 ? a.lse2[st] : INFINITY;
+      sD[tid] = t >= 0 ? a.Dvec[st] : 0.f;
+      sWa[tid] = t >= 0 ? wa : 0.f;
+      sWb[tid] = t >= 0 ? wb : 0.f;
+      sTok[tid] = t;
+    }
+    __syncthreads();
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < kUDW / 16; ++kk) {
+      s = mfma32(*(const bf16x8*)&sQ[wave][q_off + 16 * kk], kreg[kk], s);
+      dp = mfma32(*(const bf16x8*)&sG[wave][q_off + 16 * kk], vreg[kk], dp);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 s4 = {s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
+      const f32x4 p4 = {dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3]};
+      *(f32x4*)&sS[wave][lane * 16 + 4 * g] = s4;
+      *(f32x4*)&sP[wave][lane * 16 + 4 * g] = p4;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 s4 = *(const f32x4*)&sS[w2][lane * 16 + 4 * g];
+        const f32x4 p4 = *(const f32x4*)&sP[w2][lane * 16 + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[4 * g + e] += s4[e];
+          dp[4 * g + e] += p4[e];
+        }
+      }
+    // lane = key row li; register r = token 8(r>>2) + 4lh + (r&3) of the tile
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 lse4 = *(const f32x4*)&sLse[8 * g + 4 * lh];
+      const f32x4 d4 = *(const f32x4*)&sD[8 * g + 4 * lh];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 8 * g + 4 * lh + e, r = 4 * g + e;
+        const int t = sTok[i];
+        const float w = win ? ((t >= 0 && key >= t - W + 1 && key <= t) ? 1.f : 0.f)
+                            : sWa[i] + (li == 0 ? sWb[i] : 0.f);
+        const float p = key_ok ? w * fast_exp2(fmaf(s[r], a.scale_log2, -lse4[e])) : 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - d4[e]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 pb, sb, pl, sl;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = s[8 * ks + 2 * w], p1 = s[8 * ks + 2 * w + 1];
+        const float d0 = dp[8 * ks + 2 * w], d1 = dp[8 * ks + 2 * w + 1];
+        pb[w] = pack_bf16x2(p0, p1);
+        sb[w] = pack_bf16x2(d0, d1);
+        pl[w] = pack_bf16x2(p0 - bf16_lo(pb[w]), p1 - bf16_hi(pb[w]));
+        sl[w] = pack_bf16x2(d0 - bf16_lo(sb[w]), d1 - bf16_hi(sb[w]));
+      }
+      const bf16x8 pbf = as_bf16x8(pb), sbf = as_bf16x8(sb), plf = as_bf16x8(pl), slf = as_bf16x8(sl);
+#pragma unroll
+      for (int db = 0; db < kUDW / 32; ++db) {
+        const int o0 = tr_off + QL::rows(16 * ks) + 32 * db, o1 = o0 + QL::rows(8);
+        const bf16x8 ga = join_bf16x8(lds_read_tr16(&sG[wave][o0]), lds_read_tr16(&sG[wave][o1]));
+        const bf16x8 qa = join_bf16x8(lds_read_tr16(&sQ[wave][o0]), lds_read_tr16(&sQ[wave][o1]));
+        dv[db] = mfma32(ga, pbf, dv[db]);
+        dk[db] = mfma32(qa, sbf, dk[db]);
+        if (!win) {
+          dv[db] = mfma32(ga, plf, dv[db]);
+          dk[db] = mfma32(qa, slf, dk[db]);
+        }
+      }
+    }
+    __syncthreads();                                   // LDS tiles are rewritten by the next tile
+  };
+
+  // 1. Window slots: token t reads rows t - W + 1 .. t, so the tile's rows are read by
+  //    tokens r0 .. r0 + 31 + W - 1, one slot per (token, row) pair in its window.
+  const int wend = min(a.S, r0 + 32 + W - 1);
+  for (int tw = r0; tw < wend; tw += kUQ) {
+    tile([&](int i, float& wa, float& wb) -> int {
+      const int t = tw + i;
+      wa = 0.f;
+      wb = 0.f;
+      return t < wend ? t : -1;
+    }, true);
+  }
+
+  // 2. Selected slots: tokens that list block c (each listing = bs slots, one per row),
+  //    and for the tile at position 0 the -1 entries (bs slots that all read row 0).
+  //    Every token is scanned, in order, so any selection (not only block_select's,
+  //    which lists strictly earlier blocks) is handled, and the order is fixed.
+  if (tid == 0) s_npend = 0;
+  __syncthreads();
+  for (int base = 0; base < a.S; base += 256) {
+    const int t = base + tid;
+    int cnt = 0, neg = 0;
+    if (t < a.S && c < a.S / a.sel_block) {
+      const int32_t* row = a.sel + ((size_t)b * a.S + t) * n;
+      for (int j = 0; j < n; ++j) {
+        const int e = row[j];
+        cnt += e == c;
+        neg += e < 0;
+      }
+    }
+    if (c != 0) neg = 0;
+    const bool keep = cnt > 0 || neg > 0;
+    const uint64_t mask = __ballot(keep);
+    if (lane == 0) sWaveN[wave] = __popcll(mask);
+    __syncthreads();
+    const int npend = s_npend;
+    int before = npend;
+    for (int w2 = 0; w2 < wave; ++w2) before += sWaveN[w2];
+    const int total = sWaveN[0] + sWaveN[1] + sWaveN[2] + sWaveN[3];
+    if (keep) {
+      const int pos = before + __popcll(mask & ((1ull << lane) - 1));
+      lstT[pos] = t;
+      lstC[pos] = cnt | (neg << 8);
+    }
+    __syncthreads();
+    int have = npend + total;
+    int head = 0;
+    while (have - head >= kUQ) {
+      tile([&](int i, float& wa, float& wb) -> int {
+        const int e = lstC[head + i];
+        wa = (float)(e & 0xff);
+        wb = (float)(32 * (e >> 8));
+        return lstT[head + i];
+      }, false);
+      head += kUQ;
+    }
+    // move the leftover (< 32 entries) to the front
+    int lt = 0, lc = 0;
+    if (tid < have - head) {
+      lt = lstT[head + tid];
+      lc = lstC[head + tid];
+    }
+    __syncthreads();
+    if (tid < have - head) {
+      lstT[tid] = lt;
+      lstC[tid] = lc;
+    }
+    if (tid == 0) s_npend = have - head;
+    __syncthreads();
+  }
+  const int rest = s_npend;
+  if (rest > 0) {
+    tile([&](int i, float& wa, float& wb) -> int {
+      if (i >= rest) {
+        wa = 0.f;
+        wb = 0.f;
+        return -1;
+      }
+      const int e = lstC[i];
+      wa = (float)(e & 0xff);
+      wb = (float)(32 * (e >> 8));
+      return lstT[i];
+    }, false);
+  }
+
+  if (key_ok) {
+    __bf16* kop = (__bf16*)a.dk + bbase + (size_t)key * kSpE + e0;
+    __bf16* vop = (__bf16*)a.dv + bbase + (size_t)key * kSpE + e0;
+#pragma unroll
+    for (int db = 0; db < kUDW / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dk[db][4 * g] * a.scale, dk[db][4 * g + 1] * a.scale);
+        wk[1] = pack_bf16x2(dk[db][4 * g + 2] * a.scale, dk[db][4 * g + 3] * a.scale);
+        wv[0] = pack_bf16x2(dv[db][4 * g], dv[db][4 * g + 1]);
+        wv[1] = pack_bf16x2(dv[db][4 * g + 2], dv[db][4 * g + 3]);
+        *(u32x2*)(kop + 32 * db + 8 * g + 4 * lh) = wk;
+        *(u32x2*)(vop + 32 * db + 8 * g + 4 * lh) = wv;
+      }
+  }
+}
+
+hipError_t launch_sparse_bwd(const SparseBwdArgs& a, hipStream_t stream) {
+  const unsigned nqb = (unsigned)((a.S + kUQ - 1) / kUQ);
+  hipLaunchKernelGGL(sparse_bwd_dq_kernel, dim3((unsigned)a.B * nqb), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(sparse_bwd_dkdv_kernel, dim3((unsigned)a.B * nqb), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rea

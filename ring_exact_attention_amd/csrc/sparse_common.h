@@ -1,0 +1,84 @@
+// Shared pieces of the gathered block-sparse kernels ("AnnAttention",
+// faiss_block_attention): the joint embedding, the 32-token work unit and the per-unit
+// union of selected blocks.
+#pragma once
+
+#include "common.h"
+
+namespace rea {
+
+constexpr int kSpE = 512;            // joint embedding (8 bf16 per lane)
+constexpr int kUQ = 32;              // tokens per workgroup
+constexpr int kUDW = 128;            // embedding slice per wavefront
+constexpr int kUPITCH = kUDW + 32;   // slice row pitch (elements): conflict-free tr reads
+constexpr int kUMaxEnt = 512;        // 32 tokens x top_n (<= 16)
+constexpr int kUSentinel = 0x7fffffff;
+
+// The selections of tokens t0 .. t0 + 31 of sequence b: their (block, token) pairs are
+// sorted by block in LDS, the distinct blocks go to ublk[0 .. nu) in ascending order
+// (-1 first), and ucnt[u][t / 4] byte t % 4 counts how often token t lists block u.
+// scratch: 3 * kUMaxEnt ints of LDS.  Called by all 256 threads; returns nu.
+__device__ __forceinline__ int build_union(const int32_t* sel, int S, int n, int b, int t0, int* scratch,
+                                           uint32_t (*ucnt)[kUQ / 4], int* ublk, int* s_nu) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int ne = kUQ * n;
+  int* skey = scratch;
+  int* stok = skey + kUMaxEnt;
+  for (int k = tid; k < kUMaxEnt; k += 256) {
+    int key = kUSentinel, tok = 0;
+    if (k < ne) {
+      const int t = k / n, j = k % n;
+      if (t0 + t < S) {
+        const int c = sel[((size_t)b * S + t0 + t) * n + j];
+        key = c < 0 ? -1 : c;
+        tok = t;
+      }
+    }
+    skey[k] = key;
+    stok[k] = tok;
+  }
+  __syncthreads();
+  for (int size = 2; size <= kUMaxEnt; size <<= 1) {          // bitonic sort by key
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int k = tid; k < kUMaxEnt / 2; k += 256) {
+        const int lo = 2 * k - (k & (stride - 1)), hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const int ka = skey[lo], kb = skey[hi];
+        if ((ka > kb) == up) {
+          skey[lo] = kb;
+          skey[hi] = ka;
+          const int ta = stok[lo];
+          stok[lo] = stok[hi];
+          stok[hi] = ta;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (wave == 0) {                                             // union index of each entry
+    int* suid = stok + kUMaxEnt;
+    int running = 0;
+    for (int c0 = 0; c0 < kUMaxEnt; c0 += 64) {
+      const int k = c0 + lane;
+      const int key = skey[k];
+      const bool first = key != kUSentinel && (k == 0 || skey[k - 1] != key);
+      const uint64_t mask = __ballot(first);
+      const int before = __popcll(mask & ((1ull << lane) - 1));
+      suid[k] = running + before + (first ? 0 : -1);
+      if (first) ublk[running + before] = key;
+      running += __popcll(mask);
+    }
+    if (lane == 0) *s_nu = running;
+  }
+  for (int k = tid; k < kUMaxEnt * (kUQ / 4); k += 256) ((uint32_t*)ucnt)[k] = 0u;
+  __syncthreads();
+  {
+    const int* suid = stok + kUMaxEnt;
+    for (int k = tid; k < kUMaxEnt; k += 256)
+      if (skey[k] != kUSentinel) atomicAdd(&ucnt[suid[k]][stok[k] >> 2], 1u << (8 * (stok[k] & 3)));
+  }
+  __syncthreads();
+  return *s_nu;
+}
+
+}  // namespace rea

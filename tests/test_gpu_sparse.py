@@ -1,7 +1,8 @@
-"""GPU parity of block_select (bit-exact indices) and the gathered block-sparse forward
-(attn_fwd with sel_idx) against the fp64 oracle, on seeded inputs: small ragged shapes,
-engineered exact ties, the degenerate first blocks, and the full-size workload
-(B4 S8192, 8 heads x 64 as a joint embedding of 512, top-8 of 32-token blocks, window 32)."""
+"""GPU parity of block_select (bit-exact indices), the gathered block-sparse forward
+(attn_fwd with sel_idx) and its gradient (attn_bwd with sel_idx) against the fp64
+oracle, on seeded inputs: small ragged shapes, engineered exact ties, hand-made
+selections, the degenerate first blocks, and the full-size workload (B4 S8192, 8 heads
+x 64 as a joint embedding of 512, top-8 of 32-token blocks, window 32)."""
 import numpy as np
 import pytest
 import torch
@@ -121,3 +122,76 @@ def test_sparse_handmade_selection(gpu):
     check_close("o", o, o_r, "bf16")
     np.testing.assert_allclose(m.cpu().numpy(), m_r, atol=1e-3, rtol=0)
     np.testing.assert_allclose(l.cpu().numpy(), l_r, rtol=1e-3, atol=0)
+
+
+# ---------------------------------------------------------------- backward (sel_block 32)
+def sparse_grads(gpu, q, k, v, do, sel, W, bs=32):
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    idx = torch.from_numpy(np.ascontiguousarray(sel)).to(DEV) if isinstance(sel, np.ndarray) else sel
+    o, m, l = gpu.attn_fwd_sparse(qd, kd, vd, idx, window=W, block_size=bs)
+    grads = gpu.attn_bwd_sparse(qd, kd, vd, idx, o, dod, m, l, window=W, block_size=bs)
+    torch.cuda.synchronize()
+    return grads
+
+
+@pytest.mark.parametrize("B,S,n,W", [(1, 200, 4, 32), (2, 160, 8, 7), (1, 96, 8, 1), (1, 300, 8, 64),
+                                     (2, 256, 16, 32)])
+def test_sparse_backward_small(gpu, B, S, n, W):
+    E, bs = 512, 32
+    q, k, v, do = rnd((B, S, E), 60 + S), rnd((B, S, E), 61 + S), rnd((B, S, E), 62 + S), rnd((B, S, E), 63 + S)
+    sel = select.block_select(q, k, block_size=bs, top_n=n)
+    dq, dk, dv = sparse_grads(gpu, q, k, v, do, sel, W)
+    dq_r, dk_r, dv_r = sparse.sparse_attention_backward(q, k, v, sel, do, window=W, block_size=bs)
+    check_close("dq", dq, dq_r, "bf16")
+    check_close("dk", dk, dk_r, "bf16")
+    check_close("dv", dv, dv_r, "bf16")
+
+
+def test_sparse_backward_handmade_selection(gpu):
+    """Duplicates, several -1 entries (all collected by row 0), indices past the last
+    block (no gradient), tokens listing blocks at or after their own."""
+    B, S, E, bs, n, W = 2, 224, 512, 32, 6, 20
+    q, k, v, do = rnd((B, S, E), 45), rnd((B, S, E), 46), rnd((B, S, E), 47), rnd((B, S, E), 48)
+    g = np.random.default_rng(49)
+    nblk = S // bs
+    sel = g.integers(-1, nblk + 3, size=(B, S, n)).astype(np.int32)
+    sel[:, ::5, 1] = sel[:, ::5, 0]
+    sel[:, ::7, :3] = -1
+    sel[:, 3::11, 4] = nblk + 7
+    dq, dk, dv = sparse_grads(gpu, q, k, v, do, sel, W)
+    dq_r, dk_r, dv_r = sparse.sparse_attention_backward(q, k, v, sel, do, window=W, block_size=bs)
+    check_close("dq", dq, dq_r, "bf16")
+    check_close("dk", dk, dk_r, "bf16")
+    check_close("dv", dv, dv_r, "bf16")
+
+
+def test_sparse_backward_zero_keys(gpu):
+    B, S, E, bs, n, W = 1, 160, 512, 32, 8, 32
+    q, v, do = rnd((B, S, E), 50), rnd((B, S, E), 51), rnd((B, S, E), 52)
+    k = torch.zeros((B, S, E), dtype=torch.bfloat16)
+    sel = select.block_select(q, k, block_size=bs, top_n=n)
+    dq, dk, dv = sparse_grads(gpu, q, k, v, do, sel, W)
+    dq_r, dk_r, dv_r = sparse.sparse_attention_backward(q, k, v, sel, do, window=W, block_size=bs)
+    assert float(dq.abs().max()) == 0.0                       # K = 0: dq is exactly zero
+    check_close("dk", dk, dk_r, "bf16")
+    check_close("dv", dv, dv_r, "bf16")
+
+
+def test_sparse_backward_full_size_batch0(gpu):
+    """The full workload (B4 S8192 E512, top-8 of 32-token blocks, window 32) on the GPU;
+    batch 0 checked completely against the oracle (its dk, dv depend on batch 0 only)."""
+    w = workloads.WORKLOADS["block_sparse_top8_s8192"]
+    q, k, v, _ = workloads.generate(w)
+    do = workloads.random_tensor(q.shape, w.seed + 50, dtype=torch.bfloat16)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    idx = gpu.block_select(qd, kd, block_size=w.block_size, top_n=w.top_n)
+    dq, dk, dv = sparse_grads(gpu, q, k, v, do, idx, w.sparse_window)
+    dq2, dk2, dv2 = sparse_grads(gpu, q, k, v, do, idx, w.sparse_window)
+    for a_, b_ in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a_, b_)                           # bitwise reproducible
+    sel = idx.cpu().numpy()
+    dq_r, dk_r, dv_r = sparse.sparse_attention_backward(q[:1], k[:1], v[:1], sel[:1], do[:1],
+                                                        window=w.sparse_window, block_size=w.block_size)
+    check_close("dq", dq[:1], dq_r, "bf16")
+    check_close("dk", dk[:1], dk_r, "bf16")
+    check_close("dv", dv[:1], dv_r, "bf16")
