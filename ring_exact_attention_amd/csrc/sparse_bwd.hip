@@ -13,12 +13,13 @@
 //
 // Two kernels, both owner-computes (no atomics, bitwise reproducible):
 //  * sparse_bwd_dq_kernel -- one workgroup per 32 consecutive tokens, walking the same
-//    deduplicated union of selected blocks and window blocks as the forward kernel,
-//    twice: the first walk computes D_t = sum_j P(t, j) dP(t, j) (equal to dO_t . O_t,
-//    but from the fp32 probabilities instead of the stored bf16 output: a row that many
-//    slots read, such as row 0 under the -1 clamp, sums P (dP - D) over hundreds of
-//    tokens, and the rounding of the stored output would show there), the second dS and
-//    dq; D_t and the LSE go to the workspace for the dk/dv kernel;
+//    deduplicated union of selected blocks and window blocks as the forward kernel.
+//    D_t = dO_t . O_t from the stored output, except in a unit whose tokens have -1
+//    entries: there the bs clamped slots of each entry all pass their gradient to row 0,
+//    so row 0 collects P (dP - D) with weights up to bs * top_n, and the rounding of the
+//    stored bf16 output would show; such a unit first walks its blocks once to form
+//    D_t = sum_j P(t, j) dP(t, j) from fp32 values (equal in exact arithmetic).  D_t and
+//    the LSE go to the workspace for the dk/dv kernel;
 //  * sparse_bwd_dkdv_kernel -- one workgroup per 32-row key tile (one selection block,
 //    bs = 32): the tokens whose window covers the tile, then every token that selected
 //    the block (found by scanning the selections in token order), and for the tile at
@@ -39,6 +40,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   __shared__ uint32_t ucnt[kUMaxEnt][kUQ / 4];
   __shared__ int ublk[kUMaxEnt];
   __shared__ int s_nu;
+  __shared__ float sDp[4][kUQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
@@ -60,20 +62,33 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   const int tok = t0 + li;
   const bool tok_ok = tok < a.S;
 
-  // Q^T and dO^T slices as B operands (lane (li, lh): token li, e0 + 16kk + 8lh ..+7).
+  // Q^T and dO^T slices as B operands (lane (li, lh): token li, e0 + 16kk + 8lh ..+7);
+  // dO . O over this wave's slice for D_t.
   bf16x8 qreg[kUDW / 16], doreg[kUDW / 16];
+  float dpart = 0.f;
 #pragma unroll
   for (int kk = 0; kk < kUDW / 16; ++kk) {
-    u32x4 uq = {0u, 0u, 0u, 0u}, ug = uq;
+    u32x4 uq = {0u, 0u, 0u, 0u}, ug = uq, uo = uq;
     if (tok_ok) {
       const size_t off = bbase + (size_t)tok * kSpE + e0 + 16 * kk + 8 * lh;
       uq = *(const u32x4*)((const __bf16*)a.q + off);
       ug = *(const u32x4*)((const __bf16*)a.dout + off);
+      uo = *(const u32x4*)((const __bf16*)a.o + off);
     }
     qreg[kk] = as_bf16x8(uq);
     doreg[kk] = as_bf16x8(ug);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      dpart = fmaf(bf16_lo(ug[w]), bf16_lo(uo[w]), dpart);
+      dpart = fmaf(bf16_hi(ug[w]), bf16_hi(uo[w]), dpart);
+    }
   }
+  dpart += other_half(dpart);
+  if (lh == 0) sDp[wave][li] = dpart;
+  __syncthreads();
   const size_t st = (size_t)b * a.S + (tok_ok ? tok : 0);
+  // union blocks are sorted ascending, so a -1 entry in this unit shows as ublk[0] = -1
+  const bool exact_d = nu > 0 && ublk[0] < 0;
   float lse2 = INFINITY;
   if (tok_ok) {
     const float l = a.l[st];
@@ -106,9 +121,14 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   const int tg = lane >> 4, tj = lane & 15;
   const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * kUPITCH + 16 * (tg & 1) + 4 * (tj & 3);
 
-  // Two walks over the steps: pass 0 accumulates D_t, pass 1 uses it for dS and dQ.
-  float Dt = 0.f, dsum = 0.f;
-  for (int pass = 0; pass < 2; ++pass) {
+  // pass 0 (units with -1 entries only) accumulates D_t from P and dP; pass 1 uses D_t
+  // for dS and dQ.
+  float Dt = tok_ok ? (sDp[0][li] + sDp[1][li]) + (sDp[2][li] + sDp[3][li]) : 0.f, dsum = 0.f;
+  if (!exact_d && tok_ok && wave == 0 && lh == 0) {
+    a.Dvec[st] = Dt;
+    a.lse2[st] = lse2;
+  }
+  for (int pass = exact_d ? 0 : 1; pass < 2; ++pass) {
     if (nsteps > 0) load_step(0);
     for (int step = 0; step < nsteps; ++step) {
       f32x16 s, dp;
