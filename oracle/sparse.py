@@ -19,6 +19,11 @@ readings above (window ends at t inclusive, zero padding; block c -> rows c*bs .
 c*bs+bs-1) are pinned only to themselves -- parity unpinned against the originals.
 A block index past the last block (never produced by the selection) is read as zero
 rows, like the window padding.
+
+Decoding (the page's inference mode trims the windows to the last position and attends
+the new tokens against the whole key cache): ``q_pos0`` places the query rows at
+positions q_pos0 .. q_pos0 + Sq - 1 of a key / value cache of Skv rows; every token's
+slots are as above, taken from the cache.
 """
 from __future__ import annotations
 
@@ -53,14 +58,17 @@ def candidate_positions(t: int, sel_row, *, window: int, block_size: int, seqlen
     return np.asarray(pos, dtype=np.int64), np.asarray(pad, dtype=bool)
 
 
-def sparse_attention(q, k, v, sel, *, window: int, block_size: int, scale=None, tokens=None):
-    """o [B, S, E], m [B, S], l [B, S] in fp64 (m, l: max logit and sum of exp(logit - m)).
+def sparse_attention(q, k, v, sel, *, window: int, block_size: int, scale=None, tokens=None,
+                     q_pos0: int = 0):
+    """o [B, Sq, E], m [B, Sq], l [B, Sq] in fp64 (m, l: max logit and sum of exp(logit - m))
+    for query rows at positions q_pos0 + i of the key / value sequence (length Skv).
 
-    ``tokens`` restricts the evaluation to sampled token indices (others are NaN).
+    ``tokens`` restricts the evaluation to sampled query rows (others are NaN).
     """
     q, k, v = _flat(q), _flat(k), _flat(v)
     sel = np.asarray(sel.cpu() if hasattr(sel, "cpu") else sel)
     B, S, E = q.shape
+    Skv = k.shape[1]
     sc = 1.0 / math.sqrt(E) if (scale is None or scale <= 0) else float(scale)
     fill = np.nan if tokens is not None else 0.0
     o = np.full((B, S, E), fill)
@@ -69,7 +77,8 @@ def sparse_attention(q, k, v, sel, *, window: int, block_size: int, scale=None, 
     toks = range(S) if tokens is None else tokens
     for b in range(B):
         for t in toks:
-            pos, pad = candidate_positions(t, sel[b, t], window=window, block_size=block_size, seqlen=S)
+            pos, pad = candidate_positions(q_pos0 + t, sel[b, t], window=window, block_size=block_size,
+                                           seqlen=Skv)
             K = np.where(pad[:, None], 0.0, k[b, pos])
             V = np.where(pad[:, None], 0.0, v[b, pos])
             s = sc * (K @ q[b, t])

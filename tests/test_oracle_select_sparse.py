@@ -244,3 +244,30 @@ def test_sparse_backward_zero_keys_closed_form():
             for r in range(bs):
                 ref[0 if c < 0 else c * bs + r] += dO[t] / L
     np.testing.assert_allclose(dv[0], ref, atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("T,S", [(1, 200), (3, 200), (37, 200), (1, 192), (5, 97)])
+def test_decode_equals_full_sequence(T, S):
+    """Decoding the last T tokens against the whole cache (q_pos0 = S - T) gives the same
+    selections and outputs as the full-sequence call on those rows."""
+    B, E, bs, n, W = 2, 16, 8, 3, 6
+    q, k, v = rnd((B, S, E), 30 + T), rnd((B, S, E), 31 + T), rnd((B, S, E), 32 + T)
+    sel_full = select.block_select(q, k, block_size=bs, top_n=n)
+    sel_dec = select.block_select(q[:, S - T:], k, block_size=bs, top_n=n, q_pos0=S - T)
+    np.testing.assert_array_equal(sel_dec, sel_full[:, S - T:])
+    o_full, m_full, l_full = sparse.sparse_attention(q, k, v, sel_full, window=W, block_size=bs)
+    o_dec, m_dec, l_dec = sparse.sparse_attention(q[:, S - T:], k, v, sel_dec, window=W, block_size=bs,
+                                                  q_pos0=S - T)
+    np.testing.assert_allclose(o_dec, o_full[:, S - T:], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(l_dec, l_full[:, S - T:], rtol=1e-13, atol=0)
+
+
+def test_decode_in_the_middle_of_the_cache_brute_force():
+    """Query rows at positions 45..60 of a cache of 96 (not the end): brute-force selection
+    over the full blocks before each token's block."""
+    B, S, E, bs, n = 1, 96, 8, 8, 3
+    q, k = rnd((B, 16, E), 40), rnd((B, S, E), 41)
+    q_full = torch.zeros((B, S, E), dtype=torch.float64)
+    q_full[:, 45:61] = q
+    ref = brute_select(q_full.numpy(), k.numpy(), bs, n)[:, 45:61]
+    np.testing.assert_array_equal(select.block_select(q, k, block_size=bs, top_n=n, q_pos0=45), ref)
