@@ -206,6 +206,22 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
                                    "gathered_gb": round(gathered / 1e9, 3),
                                    "gathered_gbs": round(gathered / (seg_ms["attn_fwd_sparse"] * 1e-3) / 1e9, 1),
                                    "tflops": round(f_sparse / (seg_ms["attn_fwd_sparse"] * 1e-3) / 1e12, 2)}}
+    if args.decode_tokens > 0:
+        # decoding: T new tokens at the end of the S-row cache (selection + attention)
+        T = args.decode_tokens
+        qn = qd[:, S - T:].contiguous()
+        idn = torch.empty((B, T, w.top_n), dtype=torch.int32, device=dev)
+        on = torch.empty_like(qn)
+        dsegs = [("decode_select", lambda: rea.block_select(qn, kd, block_size=w.block_size, top_n=w.top_n,
+                                                            out=idn, q_pos0=S - T)),
+                 ("decode_attn", lambda: rea.attn_fwd_sparse(qn, kd, vd, idn, window=w.sparse_window,
+                                                             block_size=w.block_size, out=on, q_pos0=S - T))]
+        dms, _ = time_segments(torch, dsegs, args.steps, args.warmup, torch.cuda.current_stream(dev))
+        step_us = (dms["decode_select"] + dms["decode_attn"]) * 1e3
+        kernels["decode_step"] = {"new_tokens_per_sequence": T, "cache_rows": S,
+                                  "select_us": round(dms["decode_select"] * 1e3, 2),
+                                  "attn_us": round(dms["decode_attn"] * 1e3, 2), "step_us": round(step_us, 2),
+                                  "tokens_per_s": round(B * T / (step_us * 1e-6), 1)}
     if args.sparse_backward:
         tb = seg_ms["attn_bwd_sparse"] * 1e-3
         kernels["attn_bwd_sparse"] = {"avg_us": round(tb * 1e6, 2), "gathered_gb": round(2 * gathered / 1e9, 3),
@@ -238,6 +254,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ring_sim_causal_s8192")
+    ap.add_argument("--decode-tokens", type=int, default=0,
+                    help="block-sparse workload: also time decoding this many new tokens per sequence "
+                         "against the full cache (selection + attention)")
     ap.add_argument("--sparse-backward", action="store_true",
                     help="block-sparse workload: also time the gradient (attn_bwd with sel_idx)")
     ap.add_argument("--softmax", default="vanilla", choices=["vanilla", "off_by_one", "learnable"],

@@ -125,9 +125,12 @@ typedef struct attn_params {
    * is non-NULL, attn_fwd attends each token to a zero-padded window of
    * sparse_window keys ending at the token, followed by the sel_block rows of each of
    * its top_n selected blocks (an index of -1 reads token 0 for every row; an index
-   * >= Sq / sel_block, which block_select never produces, reads zero rows), with one
+   * >= Skv / sel_block, which block_select never produces, reads zero rows), with one
    * softmax over all slots and no mask.  Requires bf16, Hq = Hkv = 1, head_dim = the
-   * joint embedding (512), Sq = Skv, causal/window/flags/kv_block unused.           */
+   * joint embedding (512), causal/window/flags/kv_block unused.  Query row r sits at
+   * position q_pos0 + r of the Skv key / value rows (q_pos0 >= 0, q_pos0 + Sq <= Skv):
+   * the whole sequence (Sq = Skv, q_pos0 = 0) or new tokens against a cache.  The
+   * backward requires Sq = Skv and q_pos0 = 0.                                       */
   const int32_t* sel_idx;      /* [B, Sq, top_n] device, from block_select             */
   int32_t top_n;               /* 1..16                                                */
   int32_t sel_block;           /* rows per selected block (32)                         */
@@ -147,15 +150,24 @@ typedef struct attn_params {
                                   dq; NULL = not wanted                                 */
 } attn_params;
 
+/* 2: seqlen_kv and q_pos0 appended (a version-1 struct of SELECT_PARAMS_V1_SIZE bytes
+ * means seqlen_kv = seqlen, q_pos0 = 0). */
+#define SELECT_PARAMS_V1_SIZE 32u
+
 typedef struct select_params {
   uint32_t struct_size;        /* = sizeof(select_params)                              */
   int32_t dtype;               /* ATTN_BF16                                            */
   int32_t batch;               /* B >= 0                                               */
-  int32_t seqlen;              /* S >= 0                                               */
+  int32_t seqlen;              /* Sq >= 0: query rows                                  */
   int32_t embed;               /* E = heads * head_dim, multiple of 64, <= 1024        */
   int32_t block_size;          /* 16, 32 or 64                                         */
   int32_t top_n;               /* 1..16                                                */
   int32_t reserved;            /* must be 0                                            */
+  /* Decoding ("AnnAttention" in inference mode: new tokens against the key cache).
+   * Query row r sits at position q_pos0 + r of a key sequence of seqlen_kv rows;
+   * 0 = seqlen (the whole sequence, q_pos0 = 0).  q_pos0 + seqlen <= seqlen_kv.      */
+  int32_t seqlen_kv;
+  int32_t q_pos0;              /* >= 0                                                 */
 } select_params;
 
 /*
@@ -224,8 +236,12 @@ size_t attn_bwd_workspace_bytes(const attn_params* params);
  *   keeps the top min(top_n, i) by (score descending, block index ascending), pads
  *   with -1 and sorts ascending (so -1 entries come first).
  *
- *   q, k       [in]  bf16 [B, S, E] (BSHD with the heads flattened: E = H * D).
- *   idx        [out] int32 [B, S, top_n].
+ *   q          [in]  bf16 [B, Sq, E] (BSHD with the heads flattened: E = H * D), row r at
+ *                    position q_pos0 + r.
+ *   k          [in]  bf16 [B, Skv, E] (Skv = seqlen_kv, or Sq when 0).
+ *   idx        [out] int32 [B, Sq, top_n].
+ * A block's mean is a function of its rows, so recomputing the means from the key cache
+ * at every decoding step equals the page's index that gains one mean per completed block.
  *   workspace  device scratch of at least block_select_workspace_bytes(params) bytes.
  */
 int block_select(const select_params* params, const void* q, const void* k, int32_t* idx,

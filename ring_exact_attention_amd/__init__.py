@@ -75,6 +75,8 @@ class SelectParams(ctypes.Structure):
         ("block_size", ctypes.c_int32),
         ("top_n", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+        ("seqlen_kv", ctypes.c_int32),
+        ("q_pos0", ctypes.c_int32),
     ]
 
 
@@ -286,16 +288,22 @@ def _joint(x):
     return x.reshape(x.shape[0], x.shape[1], -1) if x.dim() == 4 else x
 
 
-def block_select(q, k, *, block_size=32, top_n=8, workspace=None, out=None):
-    """Exact top-n earlier-block selection by block-mean inner product -> int32 [B, S, top_n]."""
+def block_select(q, k, *, block_size=32, top_n=8, workspace=None, out=None, q_pos0=0):
+    """Exact top-n earlier-block selection by block-mean inner product -> int32 [B, Sq, top_n].
+
+    Query row r sits at position q_pos0 + r of the key sequence k [B, Skv, E] (decoding:
+    new tokens against the key cache)."""
     q, k = _joint(q), _joint(k)
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16, q.device)
     B, S, E = q.shape
+    if k.shape[0] != B or k.shape[2] != E:
+        raise ValueError("q and k must agree on batch and embedding")
     p = SelectParams()
     p.struct_size = ctypes.sizeof(SelectParams)
     p.dtype = ATTN_BF16
     p.batch, p.seqlen, p.embed = B, S, E
+    p.seqlen_kv, p.q_pos0 = k.shape[1], int(q_pos0)
     p.block_size, p.top_n = int(block_size), int(top_n)
     need = int(lib().block_select_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
@@ -306,8 +314,10 @@ def block_select(q, k, *, block_size=32, top_n=8, workspace=None, out=None):
     return idx
 
 
-def attn_fwd_sparse(q, k, v, idx, *, window=32, block_size=32, scale=None, out=None):
-    """Attention of every token over its zero-padded window ++ selected blocks."""
+def attn_fwd_sparse(q, k, v, idx, *, window=32, block_size=32, scale=None, out=None, q_pos0=0):
+    """Attention of every token over its zero-padded window ++ selected blocks.  Query row r
+    sits at position q_pos0 + r of the key / value sequence (decoding: new tokens against
+    the cache, with idx from block_select(..., q_pos0=q_pos0))."""
     q, k, v = _joint(q), _joint(k), _joint(v)
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16, q.device)
@@ -317,10 +327,13 @@ def attn_fwd_sparse(q, k, v, idx, *, window=32, block_size=32, scale=None, out=N
     top_n = idx.shape[-1]
     if idx.shape != (B, S, top_n):
         raise ValueError("idx must be [B, S, top_n]")
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != E:
+        raise ValueError("k, v must be [B, Skv, E] with q's batch and embedding")
     p = AttnParams()
     p.struct_size = ctypes.sizeof(AttnParams)
     p.dtype = ATTN_BF16
-    p.batch, p.seqlen_q, p.seqlen_kv = B, S, S
+    p.batch, p.seqlen_q, p.seqlen_kv = B, S, k.shape[1]
+    p.q_pos0 = int(q_pos0)
     p.num_q_heads = p.num_kv_heads = 1
     p.head_dim = E
     p.scale = 0.0 if scale is None else float(scale)

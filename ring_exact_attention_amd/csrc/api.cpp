@@ -198,9 +198,9 @@ int check_sparse(const attn_params* p) {
   if (p->num_q_heads != 1 || p->num_kv_heads != 1)
     return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes the joint embedding: num_q_heads = num_kv_heads = 1");
   if (p->head_dim != 512) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode supports head_dim (embed) 512");
-  if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_kv != p->seqlen_q)
-    return fail(ATTN_ERR_INVALID_ARG, "sparse mode needs seqlen_q == seqlen_kv >= 0");
-  if (p->seqlen_q > kMaxLen || (long long)p->seqlen_q * 512 * 2 > kMaxSlice)
+  if (p->batch < 0 || p->seqlen_q < 0 || p->q_pos0 < 0 || p->q_pos0 + p->seqlen_q > p->seqlen_kv)
+    return fail(ATTN_ERR_INVALID_ARG, "sparse mode needs 0 <= q_pos0 and q_pos0 + seqlen_q <= seqlen_kv");
+  if (p->seqlen_kv > kMaxLen || (long long)p->seqlen_kv * 512 * 2 > kMaxSlice)
     return fail(ATTN_ERR_UNSUPPORTED, "sequence too long");
   if (p->top_n < 1 || p->top_n > 16) return fail(ATTN_ERR_INVALID_ARG, "top_n must be in 1..16");
   if (p->sel_block != 16 && p->sel_block != 32 && p->sel_block != 64)
@@ -232,6 +232,8 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
   a.l = l;
   a.B = p->batch;
   a.S = p->seqlen_q;
+  a.Skv = p->seqlen_kv;
+  a.q_pos0 = (int)p->q_pos0;
   a.E = p->head_dim;
   a.top_n = p->top_n;
   a.sel_block = p->sel_block;
@@ -254,6 +256,8 @@ int sparse_bwd(const attn_params* p, const void* q, const void* k, const void* v
   if (st) return st;
   if (p->sel_block != 32)
     return fail(ATTN_ERR_UNSUPPORTED, "the sparse backward supports sel_block 32");
+  if (p->seqlen_kv != p->seqlen_q || p->q_pos0 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "the sparse backward needs seqlen_q == seqlen_kv and q_pos0 == 0");
   if (p->batch == 0 || p->seqlen_q == 0) return ok();
   const size_t need = sparse_bwd_workspace(p);
   if (!workspace || workspace_bytes < need)
@@ -441,24 +445,45 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
   return hip_status(rea::launch_bwd(r.dtype, a, (hipStream_t)stream));
 }
 
-size_t block_select_workspace_bytes(const select_params* p) {
-  if (!p || p->struct_size != sizeof(select_params) || p->batch < 0 || p->seqlen < 0 || p->embed <= 0 ||
-      p->block_size <= 0)
+// The caller's select params in the current layout (version 1: seqlen_kv = seqlen,
+// q_pos0 = 0).  Other sizes pass through for the size check.
+const select_params* current_select_layout(const select_params* p, select_params& tmp) {
+  if (!p || p->struct_size != SELECT_PARAMS_V1_SIZE) return p;
+  memset(&tmp, 0, sizeof tmp);
+  memcpy(&tmp, p, SELECT_PARAMS_V1_SIZE);
+  tmp.struct_size = sizeof(select_params);
+  return &tmp;
+}
+
+// Key rows of a select call (seqlen_kv, or seqlen when 0).
+int select_kv_rows(const select_params* p) { return p->seqlen_kv > 0 ? p->seqlen_kv : p->seqlen; }
+
+size_t block_select_workspace_bytes(const select_params* p_in) {
+  select_params tmp;
+  const select_params* p = current_select_layout(p_in, tmp);
+  if (!p || p->struct_size != sizeof(select_params) || p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 ||
+      p->embed <= 0 || p->block_size <= 0)
     return 0;
-  const size_t nblk = (size_t)(p->seqlen / p->block_size);
+  const size_t nblk = (size_t)(select_kv_rows(p) / p->block_size);
   const size_t n = (size_t)p->batch * nblk * p->embed * sizeof(double);
   return align_up(n > 0 ? n : 1);
 }
 
-int block_select(const select_params* p, const void* q, const void* k, int32_t* idx, void* workspace,
+int block_select(const select_params* p_in, const void* q, const void* k, int32_t* idx, void* workspace,
                  size_t workspace_bytes, void* stream) {
+  select_params tmp;
+  const select_params* p = current_select_layout(p_in, tmp);
   if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
   if (p->struct_size != sizeof(select_params))
     return fail(ATTN_ERR_INVALID_ARG, "params->struct_size does not match this library");
   if (p->reserved != 0) return fail(ATTN_ERR_INVALID_ARG, "params->reserved must be 0");
   if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "block_select supports bf16 inputs");
-  if (p->batch < 0 || p->seqlen < 0) return fail(ATTN_ERR_INVALID_ARG, "batch and seqlen must be >= 0");
-  if (p->seqlen > kMaxLen) return fail(ATTN_ERR_UNSUPPORTED, "sequence too long");
+  if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 || p->q_pos0 < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "batch, seqlen, seqlen_kv and q_pos0 must be >= 0");
+  const int skv = select_kv_rows(p);
+  if ((long long)p->q_pos0 + p->seqlen > skv)
+    return fail(ATTN_ERR_INVALID_ARG, "q_pos0 + seqlen must not exceed seqlen_kv");
+  if (skv > kMaxLen) return fail(ATTN_ERR_UNSUPPORTED, "sequence too long");
   if (p->embed <= 0 || p->embed % 64 != 0 || p->embed > 1024)
     return fail(ATTN_ERR_UNSUPPORTED, "embed must be a multiple of 64 up to 1024");
   if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
@@ -482,10 +507,12 @@ int block_select(const select_params* p, const void* q, const void* k, int32_t* 
   a.means = (double*)workspace;
   a.B = p->batch;
   a.S = p->seqlen;
+  a.Skv = skv;
+  a.q_pos0 = p->q_pos0;
   a.E = p->embed;
   a.bs = p->block_size;
   a.top_n = p->top_n;
-  a.nblk = p->seqlen / p->block_size;
+  a.nblk = skv / p->block_size;
   return hip_status(rea::launch_select(a, (hipStream_t)stream));
 }
 

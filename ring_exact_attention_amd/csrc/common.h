@@ -93,7 +93,8 @@ struct SelectArgs {
   const void* k;
   int32_t* idx;
   double* means;      // [B, nblk, E] workspace
-  int B, S, E, bs, top_n, nblk;
+  int B, S, E, bs, top_n, nblk;   // S: query rows; nblk = Skv / bs full key blocks
+  int Skv, q_pos0;    // key rows; position of query row 0 in the key sequence
 };
 
 struct SparseArgs {
@@ -106,6 +107,7 @@ struct SparseArgs {
   float* l;
   int B, S, E, top_n, sel_block, window;
   float scale_log2, scale;
+  int Skv, q_pos0;    // key / value rows; position of query row 0 among them
 };
 
 // Backward of the gathered block-sparse attention.

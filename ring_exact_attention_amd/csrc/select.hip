@@ -2,8 +2,10 @@
 // in place of the approximate index).
 //
 // block_means: mean of each full block of bs key rows, in fp64 (exact for bf16 rows).
-// block_select: one workgroup per (batch, query block i).  The bs tokens of the block
-// score the candidate blocks c < i in chunks of 64 (16 per wavefront) with fp64 MFMA
+// block_select: one workgroup per (batch, block i of query positions; query row r sits
+// at position q_pos0 + r of the key sequence, so decoding a few new tokens against a
+// key cache is the same call).  The block's tokens score the candidate blocks
+// c < i in chunks of 64 (16 per wavefront) with fp64 MFMA
 // (bf16 queries are exact in fp64), the chunk's scores go to LDS, and one thread per
 // token merges them into its running top-n list kept in LDS (score descending; on
 // equal scores the earlier, lower index stays ahead).  The list is written sorted
@@ -15,7 +17,7 @@ namespace rea {
 
 __global__ __launch_bounds__(256) void block_means_kernel(SelectArgs a) {
   const int c = blockIdx.x % a.nblk, b = blockIdx.x / a.nblk;
-  const __bf16* kp = (const __bf16*)a.k + ((size_t)b * a.S + (size_t)c * a.bs) * a.E;
+  const __bf16* kp = (const __bf16*)a.k + ((size_t)b * a.Skv + (size_t)c * a.bs) * a.E;
   double* mp = a.means + ((size_t)b * a.nblk + c) * a.E;
   for (int e = threadIdx.x; e < a.E; e += 256) {
     double s = 0.0;
@@ -40,11 +42,13 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
   __shared__ double best_s[BS][NMAX];
   __shared__ int best_c[BS][NMAX];
 
-  const int nqb = (a.S + BS - 1) / BS;
-  const int i = blockIdx.x % nqb, b = blockIdx.x / nqb;
+  const int first = a.q_pos0 / BS;
+  const int nqb = (a.q_pos0 + a.S - 1) / BS - first + 1;
+  const int i = first + blockIdx.x % nqb, b = blockIdx.x / nqb;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int t0 = i * BS;
-  const int ntok = min(BS, a.S - t0);
+  const int p0 = max(i * BS, a.q_pos0);                      // first query position of the block
+  const int t0 = p0 - a.q_pos0;                               // its query row
+  const int ntok = min((i + 1) * BS, a.q_pos0 + a.S) - p0;
   const int ncand = min(i, a.nblk);
   int kept = 0;                           // list length of token `tid` (threads < BS)
 
@@ -125,7 +129,8 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (a.nblk > 0)
     hipLaunchKernelGGL(block_means_kernel, dim3((unsigned)(a.B * a.nblk)), dim3(256), 0, stream, a);
-  const int nqb = (a.S + a.bs - 1) / a.bs;
+  if (a.S == 0) return hipGetLastError();
+  const int nqb = (a.q_pos0 + a.S - 1) / a.bs - a.q_pos0 / a.bs + 1;
   const dim3 grid((unsigned)(a.B * nqb));
   const size_t lds = (size_t)a.bs * a.E * sizeof(__bf16);
   switch (a.bs) {

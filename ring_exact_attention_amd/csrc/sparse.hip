@@ -46,13 +46,17 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const int nwin = (W + kUQ - 1 + 31) / 32;
   const int nsub = (bs + 31) / 32;
   const int nsteps = nwin + nu * nsub;
-  const int wstart = t0 - W + 1;
+  // Query row r sits at position q_pos0 + r of the key / value sequence (Skv rows): the
+  // whole sequence when q_pos0 = 0 and Skv = S, or a few new tokens against a cache.
+  const int wstart = a.q_pos0 + t0 - W + 1;
   const uint32_t row_b = (uint32_t)kSpE * 2;
-  const size_t bbase = (size_t)b * a.S * kSpE;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + bbase, (uint32_t)a.S * row_b);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + bbase, (uint32_t)a.S * row_b);
+  const size_t bbase = (size_t)b * a.S * kSpE;                 // query / output rows
+  const size_t kvbase = (size_t)b * a.Skv * kSpE;              // key / value rows
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const __bf16*)a.k + kvbase, (uint32_t)a.Skv * row_b);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + kvbase, (uint32_t)a.Skv * row_b);
   const int e0 = kUDW * wave;                                  // this wave's embedding slice
   const int tok = t0 + li;                                     // this lane's token (B / C column)
+  const int tpos = a.q_pos0 + tok;                             // its position
 
   bf16x8 qreg[kUDW / 16];
 #pragma unroll
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int p = p0 + 8 * (r >> 2) + (r & 3);
-        wt[r] = (tok < a.S && p >= tok - W + 1 && p <= tok) ? 1.f : 0.f;
+        wt[r] = (tok < a.S && p >= tpos - W + 1 && p <= tpos) ? 1.f : 0.f;
       }
     } else {
       const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;

@@ -63,7 +63,8 @@ def fwd_status(lib, p, ptr=None):
 def test_struct_layout(lib):
     assert ctypes.sizeof(rea.AttnParams) == 128
     assert rea.AttnParams.softmax_type.offset == 104          # ATTN_PARAMS_V1_SIZE
-    assert ctypes.sizeof(rea.SelectParams) == 32
+    assert ctypes.sizeof(rea.SelectParams) == 40
+    assert rea.SelectParams.seqlen_kv.offset == 32          # SELECT_PARAMS_V1_SIZE
     # a zero batch is a successful no-op only when the struct size matches
     assert fwd_status(lib, params(batch=0)) == rea.ATTN_OK
     p = params(batch=0)
@@ -123,6 +124,45 @@ def test_version1_struct_is_accepted(lib):
     big.p.batch = 1
     assert fwd_status(lib, big.p) == rea.ATTN_ERR_INVALID_ARG
     assert b"q is NULL" in lib.attn_last_error()
+
+
+def test_select_decode_checks(lib):
+    """block_select with query rows at q_pos0 of a longer key sequence, and the 32-byte
+    version-1 select struct (no decode fields)."""
+    def sp(**kw):
+        p = rea.SelectParams()
+        p.struct_size = ctypes.sizeof(rea.SelectParams)
+        for k_, v_ in dict(dtype=rea.ATTN_BF16, batch=1, seqlen=4, embed=512, block_size=32, top_n=8,
+                           seqlen_kv=256, q_pos0=252).items():
+            setattr(p, k_, v_)
+        for k_, v_ in kw.items():
+            setattr(p, k_, v_)
+        return p
+    d = ctypes.c_void_p(0x1000)
+    call = lambda p: lib.block_select(ctypes.byref(p), d, d, None, d, 1 << 30, None)
+    assert call(sp()) == rea.ATTN_ERR_INVALID_ARG and b"idx is NULL" in lib.attn_last_error()
+    assert call(sp(q_pos0=253)) == rea.ATTN_ERR_INVALID_ARG and b"q_pos0" in lib.attn_last_error()
+    assert call(sp(q_pos0=-1)) == rea.ATTN_ERR_INVALID_ARG
+    # workspace: the means of the key sequence's full blocks
+    assert lib.block_select_workspace_bytes(ctypes.byref(sp())) == 8 * 512 * 8
+    v1 = sp(seqlen=256, seqlen_kv=77, q_pos0=99)
+    v1.struct_size = 32                                      # fields past 32 bytes ignored
+    assert lib.block_select_workspace_bytes(ctypes.byref(v1)) == 8 * 512 * 8
+    assert call(v1) == rea.ATTN_ERR_INVALID_ARG and b"idx is NULL" in lib.attn_last_error()
+
+
+def test_sparse_decode_checks(lib):
+    d = ctypes.c_void_p(0x1000)
+    p = params(num_q_heads=1, num_kv_heads=1, head_dim=512, seqlen_q=2, seqlen_kv=64, causal=0, q_pos0=62)
+    p.sel_idx = 0x1000
+    p.top_n, p.sel_block, p.sparse_window = 8, 32, 32
+    assert lib.attn_fwd(ctypes.byref(p), None, d, d, d, d, d, None, None) == rea.ATTN_ERR_INVALID_ARG
+    assert b"q is NULL" in lib.attn_last_error()               # decoding shape accepted
+    p.q_pos0 = 63
+    assert lib.attn_fwd(ctypes.byref(p), d, d, d, d, d, d, None, None) == rea.ATTN_ERR_INVALID_ARG
+    assert b"q_pos0" in lib.attn_last_error()
+    p.q_pos0 = 62                                              # the gradient needs the whole sequence
+    assert lib.attn_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, 1 << 30, None) == rea.ATTN_ERR_UNSUPPORTED
 
 
 def test_null_and_misaligned_pointers(lib):

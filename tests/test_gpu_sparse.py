@@ -195,3 +195,44 @@ def test_sparse_backward_full_size_batch0(gpu):
     check_close("dq", dq[:1], dq_r, "bf16")
     check_close("dk", dk[:1], dk_r, "bf16")
     check_close("dv", dv[:1], dv_r, "bf16")
+
+
+# ---------------------------------------------------------------- decoding against a cache
+@pytest.mark.parametrize("S,T,pos0", [(1000, 1, 999), (1000, 4, 996), (1000, 33, 967), (1000, 20, 500),
+                                      (256, 32, 224)])
+def test_decode_against_cache(gpu, S, T, pos0):
+    """New tokens at positions pos0 .. pos0 + T - 1 against a key / value cache of S rows:
+    selection bit-exact and output within tolerance of the oracle, and the same
+    selection as the full-sequence call on those rows."""
+    B, E, bs, n, W = 2, 512, 32, 8, 32
+    q, k, v = rnd((B, S, E), 70 + T), rnd((B, S, E), 71 + T), rnd((B, S, E), 72 + T)
+    qn = q[:, pos0:pos0 + T].contiguous()
+    qd, kd, vd = qn.to(DEV), k.to(DEV), v.to(DEV)
+    idx = gpu.block_select(qd, kd, block_size=bs, top_n=n, q_pos0=pos0)
+    o, m, l = gpu.attn_fwd_sparse(qd, kd, vd, idx, window=W, block_size=bs, q_pos0=pos0)
+    idx_full = gpu.block_select(q.to(DEV), kd, block_size=bs, top_n=n)
+    torch.cuda.synchronize()
+    sel = select.block_select(qn, k, block_size=bs, top_n=n, q_pos0=pos0)
+    np.testing.assert_array_equal(idx.cpu().numpy(), sel)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_full.cpu().numpy()[:, pos0:pos0 + T])
+    o_r, m_r, l_r = sparse.sparse_attention(qn, k, v, sel, window=W, block_size=bs, q_pos0=pos0)
+    check_close("o", o, o_r, "bf16")
+    np.testing.assert_allclose(m.cpu().numpy(), m_r, atol=1e-3, rtol=0)
+    np.testing.assert_allclose(l.cpu().numpy(), l_r, rtol=1e-3, atol=0)
+
+
+def test_decode_full_size_cache(gpu):
+    """One new token per sequence at the end of the full workload's 8192-row cache."""
+    w = workloads.WORKLOADS["block_sparse_top8_s8192"]
+    q, k, v, _ = workloads.generate(w)
+    S = w.seqlen
+    qn = q[:, S - 1:].contiguous()
+    qd, kd, vd = qn.to(DEV), k.to(DEV), v.to(DEV)
+    idx = gpu.block_select(qd, kd, block_size=w.block_size, top_n=w.top_n, q_pos0=S - 1)
+    o, m, l = gpu.attn_fwd_sparse(qd, kd, vd, idx, window=w.sparse_window, block_size=w.block_size, q_pos0=S - 1)
+    torch.cuda.synchronize()
+    sel = select.block_select(qn, k, block_size=w.block_size, top_n=w.top_n, q_pos0=S - 1)
+    np.testing.assert_array_equal(idx.cpu().numpy(), sel)
+    o_r, _, _ = sparse.sparse_attention(qn, k, v, sel, window=w.sparse_window, block_size=w.block_size,
+                                        q_pos0=S - 1)
+    check_close("o", o, o_r, "bf16")
