@@ -31,6 +31,12 @@ blockwise body of ``_blockwise_attention_bwd`` in "bpt.py"):
 with dK and dV summed over the G q heads that share a kv head (the gradient of the
 repeat in the GQA mapping).
 
+Additive bias ("bpt.py": ``ring_attention`` / ``blockwise_attn`` take a bias that
+broadcasts to (batch, heads, q_len, kv_len) and is added to the scaled logits of each
+chunk, ``_chunk_attention_bias``; the page returns no gradient for it): s_ij gains
+bias[b, h, i, j] (natural units) before the mask and the softmax.  A bias of -inf removes
+a pair like the mask does.
+
 Sink softmax ("JAX: Single-GPU Attention with TransformerEngine", "Other attention
 knobs": ``softmax_type="off_by_one"`` or ``"learnable"``; the page names the options only,
 so this is the plain reading of their names): every row's softmax gets one more term in
@@ -140,8 +146,17 @@ def _sink_weight(z, m, l):
     return np.where(np.isfinite(m), np.exp(z - np.where(np.isfinite(m), m, 0.0)), 0.0)
 
 
+def _bias_rows(bias, b, h, rows, c0, c1):
+    """bias[b, h, rows, c0:c1] of a broadcastable [B|1, H|1, Sq|1, Skv|1] array, or 0."""
+    if bias is None:
+        return 0.0
+    bb = bias[min(b, bias.shape[0] - 1), min(h, bias.shape[1] - 1)]
+    r = bb[rows] if bb.shape[0] > 1 else bb[np.zeros_like(rows)]
+    return r[:, c0:c1] if r.shape[1] > 1 else r
+
+
 def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0,
-            kv_pos0: int = 0, rows=None, heads=None, row_block: int = 256, sink=None):
+            kv_pos0: int = 0, rows=None, heads=None, row_block: int = 256, sink=None, bias=None):
     """Attention forward from the definition.
 
     q: [B, Sq, Hq, D]; k: [B, Skv, Hkv, D]; v: [B, Skv, Hkv, Dv] (torch or numpy, any
@@ -149,6 +164,7 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
     natural-log units of the scaled logits.  ``rows`` / ``heads`` restrict the
     evaluation to sampled query rows / q heads; entries not evaluated are NaN.  ``sink``:
     None, or the sink logits z [Hq] (zeros for "off_by_one"); m and l exclude the sink.
+    ``bias``: None, or an additive logit bias broadcastable to [B, Hq, Sq, Skv].
     """
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     B, Sq, Hq, D = q.shape
@@ -158,6 +174,7 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
     sc = _default_scale(D, scale)
     wl, wr = window
     z = _sink_logits(sink, Hq)
+    bias = None if bias is None else as_f64(bias)
     fill = np.nan if (rows is not None or heads is not None) else 0.0
     o = np.full((B, Sq, Hq, v.shape[3]), fill)
     m = np.full((B, Hq, Sq), np.nan if fill != 0.0 else -np.inf)
@@ -171,6 +188,8 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
             K, V = k[b, :, g, :], v[b, :, g, :]
             for r in _row_slices(rows, row_block):
                 vis = visible(q_pos0 + r, kpos, causal, wl, wr)
+                if bias is not None:
+                    vis = vis & (_bias_rows(bias, b, hq, r, 0, Skv) > -np.inf)
                 rng = _visible_range(vis)
                 if rng is None:
                     o[b, r, hq] = 0.0
@@ -178,7 +197,8 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
                     l[b, hq, r] = 0.0
                     continue
                 c0, c1 = rng
-                p, mr, lr = _softmax_rows(scores(q[b, r, hq, :], K[c0:c1], sc), vis[:, c0:c1])
+                s = scores(q[b, r, hq, :], K[c0:c1], sc) + _bias_rows(bias, b, hq, r, c0, c1)
+                p, mr, lr = _softmax_rows(s, vis[:, c0:c1])
                 denom = lr + _sink_weight(None if z is None else z[hq], mr, lr)
                 denom = np.where(denom > 0, denom, 1.0)
                 o[b, r, hq] = (p @ V[c0:c1]) / denom[:, None]
@@ -204,7 +224,7 @@ def probs(q, k, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0, k
 
 
 def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0,
-             kv_pos0: int = 0, row_block: int = 256, heads=None, batches=None, sink=None):
+             kv_pos0: int = 0, row_block: int = 256, heads=None, batches=None, sink=None, bias=None):
     """Analytic gradient of ``forward`` contracted with dO.
 
     Returns (dq [B, Sq, Hq, D], dk [B, Skv, Hkv, D], dv [B, Skv, Hkv, Dv]) in fp64.
@@ -222,6 +242,7 @@ def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: 
     wl, wr = window
     z = _sink_logits(sink, Hq)
     dz = np.zeros(Hq)
+    bias = None if bias is None else as_f64(bias)
     partial = heads is not None or batches is not None
     dq = np.full_like(q, np.nan) if partial else np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -235,11 +256,14 @@ def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: 
             K, V = k[b, :, g, :], v[b, :, g, :]
             for r in _row_slices(rows, row_block):
                 vis = visible(q_pos0 + r, kpos, causal, wl, wr)
+                if bias is not None:
+                    vis = vis & (_bias_rows(bias, b, hq, r, 0, Skv) > -np.inf)
                 rng = _visible_range(vis)
                 if rng is None:
                     continue
                 c0, c1 = rng
-                p, mr, lr = _softmax_rows(scores(q[b, r, hq], K[c0:c1], sc), vis[:, c0:c1])
+                s = scores(q[b, r, hq], K[c0:c1], sc) + _bias_rows(bias, b, hq, r, c0, c1)
+                p, mr, lr = _softmax_rows(s, vis[:, c0:c1])
                 w_sink = _sink_weight(None if z is None else z[hq], mr, lr)
                 denom = lr + w_sink
                 denom = np.where(denom > 0, denom, 1.0)

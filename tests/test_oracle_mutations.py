@@ -14,6 +14,7 @@ import test_oracle_blockwise as tw
 import test_oracle_dense as td
 import test_oracle_select_sparse as ts
 import test_oracle_sink as tk
+import test_oracle_bias as tbias
 
 
 def _mut_gqa_modulo(monkeypatch):
@@ -107,6 +108,12 @@ def _mut_clamped_slots_pass_no_gradient(monkeypatch):
     monkeypatch.setattr(sparse, "candidate_positions", cand)
 
 
+def _mut_bias_scaled_with_logits(monkeypatch):
+    """The bias is added to the scaled logits, not scaled with them."""
+    orig = dense._bias_rows
+    monkeypatch.setattr(dense, "_bias_rows", lambda *a: orig(*a) / np.sqrt(8.0))
+
+
 MUTATIONS = [
     (_mut_gqa_modulo, lambda: td.test_forward_matches_torch_sdpa(td.CASES[0])),
     (_mut_drop_scale, lambda: td.test_forward_matches_torch_sdpa(td.CASES[1])),
@@ -120,6 +127,7 @@ MUTATIONS = [
     (_mut_window_off_by_one, ts.test_sparse_equals_materialised_candidate_list),
     (_mut_clamp_to_last, ts.test_sparse_zero_keys_closed_form),
     (_mut_sink_sign, tk.test_sink_with_zero_left_window_closed_form),
+    (_mut_bias_scaled_with_logits, lambda: tbias.test_bias_matches_torch_sdpa_and_autograd((2, 4, 19, 19), True, (-1, -1))),
     (_mut_clamped_slots_pass_no_gradient, lambda: ts.test_sparse_backward_matches_autograd_of_materialised_list(8, 3)),
     (_mut_sink_in_log2_units, lambda: tk.test_sink_forward_and_backward_match_torch(True, (-1, -1), 2, 8)),
 ]
