@@ -261,6 +261,9 @@ def main():
                     help="block-sparse workload: also time the gradient (attn_bwd with sel_idx)")
     ap.add_argument("--softmax", default="vanilla", choices=["vanilla", "off_by_one", "learnable"],
                     help="sink softmax variant of the dense workloads (learnable: seeded N(0,1) logits)")
+    ap.add_argument("--bias", default="none", choices=["none", "keypad", "shared"],
+                    help="additive logit bias: keypad = [B,1,1,S] with the last S/16 keys at -inf, "
+                         "shared = one random [1,1,S,S] fp32 matrix")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -297,6 +300,12 @@ def main():
     if args.softmax == "learnable":
         sink = workloads.random_tensor((Hq,), w.seed + 100).to(dev)
     kw.update(softmax_type=args.softmax, sink=sink)
+    if args.bias == "keypad":
+        bias = torch.zeros((B, 1, 1, S), dtype=torch.float32, device=dev)
+        bias[..., S - S // 16:] = float("-inf")
+        kw.update(bias=bias)
+    elif args.bias == "shared":
+        kw.update(bias=workloads.random_tensor((1, 1, S, S), w.seed + 101).to(dev))
     o = torch.empty((B, S, Hq, Dv), dtype=qd.dtype, device=dev)
     m = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     l = torch.empty_like(m)
@@ -373,7 +382,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name if args.softmax == "vanilla" else f"{w.name}+{args.softmax}_sink",
+        "config": {"workload": w.name + ("" if args.softmax == "vanilla" else f"+{args.softmax}_sink")
+                               + ("" if args.bias == "none" else f"+{args.bias}_bias"),
                    "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "head_dim_v": Dv, "causal": w.causal, "window": list(w.window),
                    "virtual_blocks": (S // w.kv_block) if w.kv_block else 1,

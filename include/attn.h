@@ -90,10 +90,12 @@ enum {
   ATTN_SOFTMAX_LEARNABLE = 2
 };
 
-/* 2: softmax_type, sink, dsink appended (a version-1 struct of ATTN_PARAMS_V1_SIZE bytes,
- * without them, is still accepted and means ATTN_SOFTMAX_VANILLA). */
-#define ATTN_PARAMS_VERSION 2u
+/* 2: softmax_type, sink, dsink appended; 3: bias, bias_stride appended.  Structs of the
+ * earlier sizes are still accepted: the missing fields read as zero (ATTN_SOFTMAX_VANILLA,
+ * no bias). */
+#define ATTN_PARAMS_VERSION 3u
 #define ATTN_PARAMS_V1_SIZE 104u
+#define ATTN_PARAMS_V2_SIZE 128u
 
 typedef struct attn_params {
   uint32_t struct_size;        /* = sizeof(attn_params); versioning of the ABI        */
@@ -148,6 +150,15 @@ typedef struct attn_params {
                                   dL/dz_h summed over the batch and this call's query
                                   rows, written (not accumulated) by calls that compute
                                   dq; NULL = not wanted                                 */
+  /* Additive logit bias ("bpt.py": ring_attention / blockwise_attn take a bias that
+   * broadcasts to (batch, heads, q_len, kv_len) and is added to the scaled logits;
+   * the page passes no gradient to it, and neither does attn_bwd).  fp32 device, in the
+   * units of the scaled logits; element (b, hq, i, j) -- this call's query row i and
+   * key row j -- is bias[b*s0 + hq*s1 + i*s2 + j*s3] with s = bias_stride (elements,
+   * >= 0; 0 broadcasts that dimension).  -inf removes a pair like the mask.  NULL = none.
+   * Dense mode only.                                                                   */
+  const float* bias;
+  int64_t bias_stride[4];
 } attn_params;
 
 /* 2: seqlen_kv and q_pos0 appended (a version-1 struct of SELECT_PARAMS_V1_SIZE bytes

@@ -62,6 +62,8 @@ class AttnParams(ctypes.Structure):
         ("softmax_type", ctypes.c_int32),
         ("sink", ctypes.c_void_p),
         ("dsink", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("bias_stride", ctypes.c_int64 * 4),
     ]
 
 
@@ -162,7 +164,7 @@ def _softmax_code(softmax_type, sink):
 
 def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
                 kv_block=0, q_pos0=0, kv_pos0=0, flags=0, head_dim_v=0, softmax_type="vanilla",
-                sink=None) -> AttnParams:
+                sink=None, bias=None) -> AttnParams:
     B, Sq, Hq, D = q.shape
     Bk, Skv, Hkv, Dk = k.shape
     if Bk != B or Dk != D:
@@ -179,6 +181,16 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
         if sink.shape != (Hq,):
             raise ValueError(f"sink must be [num_q_heads] = [{Hq}]")
         p.sink = sink.data_ptr()
+    if bias is not None:
+        # additive logit bias broadcastable to [B, Hq, Sq, Skv]: strides of the expanded view
+        if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or bias.device != q.device:
+            raise TypeError("bias must be a float32 tensor on q's device")
+        if bias.dim() != 4:
+            raise ValueError("bias must have 4 dims broadcastable to [B, Hq, Sq, Skv]")
+        view = bias.expand(B, Hq, Sq, Skv)
+        p.bias = bias.data_ptr()
+        for d in range(4):
+            p.bias_stride[d] = view.stride(d) if view.shape[d] > 1 else 0
     p.q_pos0, p.kv_pos0 = int(q_pos0), int(kv_pos0)
     p.causal = 1 if causal else 0
     p.window_left, p.window_right = int(window[0]), int(window[1])
@@ -190,7 +202,7 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
 
 def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
              kv_block=0, q_pos0=0, kv_pos0=0, m=None, l=None, acc=None, carry_in=False,
-             finalize=True, out=None, softmax_type="vanilla", sink=None):
+             finalize=True, out=None, softmax_type="vanilla", sink=None, bias=None):
     """Forward attention.  q [B, Sq, Hq, D], k [B, Skv, Hkv, D], v [B, Skv, Hkv, Dv] on the GPU
     (Dv = D, or the MLA pair D 128 / Dv 64).
 
@@ -198,6 +210,7 @@ def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     where acc is the fp32 unnormalised numerator.  ``carry_in=True`` resumes from the
     given m, l, acc.  ``softmax_type`` "off_by_one" / "learnable" (with ``sink``, fp32
     [Hq] logits) adds exp(z_h) to each row's denominator when the output is finalised.
+    ``bias``: fp32 additive logit bias broadcastable to [B, Hq, Sq, Skv] (-inf masks).
     """
     _need(q, "q")
     _need(k, "k", q.dtype, q.device)
@@ -209,7 +222,7 @@ def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     flags = (ATTN_CARRY_IN if carry_in else 0) | (0 if finalize else ATTN_NO_FINALIZE)
     p = make_params(q, k, causal=causal, window=window, scale=scale, query_chunk=query_chunk,
                     key_chunk=key_chunk, kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, flags=flags,
-                    head_dim_v=Dv, softmax_type=softmax_type, sink=sink)
+                    head_dim_v=Dv, softmax_type=softmax_type, sink=sink, bias=bias)
     dev = q.device
     if m is None:
         m = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
@@ -242,7 +255,7 @@ def bwd_workspace_bytes(q, k, **kw) -> int:
 def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None, query_chunk=0,
              key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, workspace=None, out=None,
              skip_dq=False, skip_dkdv=False, reuse_stats=False, softmax_type="vanilla", sink=None,
-             dsink=None):
+             dsink=None, bias=None):
     """Gradients (dq, dk, dv) of attn_fwd's output for upstream gradient dout.
 
     ``skip_dq`` / ``skip_dkdv`` compute only part of them (the skipped outputs are left
@@ -261,7 +274,7 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
         raise ValueError("v must match k except in its head dim, and o, dout must be [B, Sq, Hq, Dv]")
     kw = dict(causal=causal, window=window, scale=scale, query_chunk=query_chunk, key_chunk=key_chunk,
               kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, head_dim_v=Dv, softmax_type=softmax_type,
-              sink=sink)
+              sink=sink, bias=bias)
     flags = ((ATTN_BWD_SKIP_DQ if skip_dq else 0) | (ATTN_BWD_SKIP_DKDV if skip_dkdv else 0) |
              (ATTN_BWD_REUSE_STATS if reuse_stats else 0))
     p = make_params(q, k, flags=flags, **kw)

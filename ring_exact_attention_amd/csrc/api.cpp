@@ -51,17 +51,23 @@ struct Problem {
   int has_sink = 0;
   const float* sink = nullptr;
   float* dsink = nullptr;
+  const float* bias = nullptr;
+  long long bias_stride[4] = {0, 0, 0, 0};
 };
 
 static_assert(offsetof(attn_params, softmax_type) == ATTN_PARAMS_V1_SIZE,
               "a version-1 attn_params is the current one without its softmax fields");
+static_assert(offsetof(attn_params, bias) == ATTN_PARAMS_V2_SIZE,
+              "a version-2 attn_params is the current one without its bias fields");
 
-// The caller's params in the current layout: a version-1 struct (without the softmax
-// fields) reads as ATTN_SOFTMAX_VANILLA.  Other sizes pass through for the size check.
+// The caller's params in the current layout: an earlier version's struct reads with its
+// missing fields zero (ATTN_SOFTMAX_VANILLA, no bias).  Other sizes pass through for the
+// size check.
 const attn_params* current_layout(const attn_params* p, attn_params& tmp) {
-  if (!p || p->struct_size != ATTN_PARAMS_V1_SIZE) return p;
+  if (!p || (p->struct_size != ATTN_PARAMS_V1_SIZE && p->struct_size != ATTN_PARAMS_V2_SIZE)) return p;
+  const size_t n = p->struct_size;
   memset(&tmp, 0, sizeof tmp);
-  memcpy(&tmp, p, ATTN_PARAMS_V1_SIZE);
+  memcpy(&tmp, p, n);
   tmp.struct_size = sizeof(attn_params);
   return &tmp;
 }
@@ -115,6 +121,12 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   if (p->softmax_type == ATTN_SOFTMAX_LEARNABLE && (!p->sink || ((uintptr_t)p->sink & 3u)))
     return fail(ATTN_ERR_INVALID_ARG, "ATTN_SOFTMAX_LEARNABLE needs sink: [num_q_heads] fp32 on the device");
   if (p->dsink && ((uintptr_t)p->dsink & 3u)) return fail(ATTN_ERR_INVALID_ARG, "dsink must be 4-byte aligned");
+  if (p->bias) {
+    if ((uintptr_t)p->bias & 3u) return fail(ATTN_ERR_INVALID_ARG, "bias must be 4-byte aligned");
+    for (int d = 0; d < 4; ++d)
+      if (p->bias_stride[d] < 0 || p->bias_stride[d] > (1LL << 40))
+        return fail(ATTN_ERR_INVALID_ARG, "bias_stride entries must be in [0, 2^40]");
+  }
   const uint32_t fwd_flags = ATTN_CARRY_IN | ATTN_NO_FINALIZE;
   const uint32_t bwd_flags = ATTN_BWD_SKIP_DQ | ATTN_BWD_SKIP_DKDV | ATTN_BWD_REUSE_STATS;
   if (p->flags & ~(fwd_flags | bwd_flags)) return fail(ATTN_ERR_INVALID_ARG, "unknown bits in flags");
@@ -155,6 +167,8 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   r.has_sink = p->softmax_type != ATTN_SOFTMAX_VANILLA;
   r.sink = p->softmax_type == ATTN_SOFTMAX_LEARNABLE ? p->sink : nullptr;
   r.dsink = p->softmax_type == ATTN_SOFTMAX_LEARNABLE ? p->dsink : nullptr;
+  r.bias = p->bias;
+  for (int d = 0; d < 4; ++d) r.bias_stride[d] = p->bias_stride[d];
   return ATTN_OK;
 }
 
@@ -194,6 +208,7 @@ int check_sparse(const attn_params* p) {
     return fail(ATTN_ERR_UNSUPPORTED, "sparse mode needs head_dim_v = 0 (the joint embedding)");
   if (p->softmax_type != ATTN_SOFTMAX_VANILLA)
     return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no sink softmax");
+  if (p->bias) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no bias");
   if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode supports bf16 only");
   if (p->num_q_heads != 1 || p->num_kv_heads != 1)
     return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes the joint embedding: num_q_heads = num_kv_heads = 1");
@@ -336,6 +351,12 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
   a.Dv = r.Dv;
   a.has_sink = r.has_sink;
   a.sink = r.sink;
+  a.bias = r.bias;
+  a.bs_b = r.bias_stride[0];
+  a.bs_h = r.bias_stride[1];
+  a.bs_i = r.bias_stride[2];
+  a.bs_j = r.bias_stride[3];
+  a.inv_scale = 1.f / r.scale;
   a.delta = r.delta;
   a.lo_off = r.lo_off;
   a.hi_off = r.hi_off;
@@ -423,6 +444,12 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
   a.Dv = r.Dv;
   a.has_sink = r.has_sink;
   a.sink = r.sink;
+  a.bias = r.bias;
+  a.bs_b = r.bias_stride[0];
+  a.bs_h = r.bias_stride[1];
+  a.bs_i = r.bias_stride[2];
+  a.bs_j = r.bias_stride[3];
+  a.inv_scale = 1.f / r.scale;
   a.delta = r.delta;
   a.lo_off = r.lo_off;
   a.hi_off = r.hi_off;

@@ -263,6 +263,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
           if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
         }
     }
+    if (a.bias) {
+      cold_path();
+      const float* bp = a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) add_bias16(s[mb], bp, a.bs_j, ts + 32 * mb + 4 * lh, tend, a.inv_scale);
+    }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -646,6 +652,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
           if (ihi_v < ilo_v || (uint32_t)(base + ioff) > span) s[r] = -INFINITY;
         }
       }
+      if (a.bias) {
+        cold_path();
+        const float* bp = a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(key, a.Skv - 1) * a.bs_j;
+        add_bias16(s, bp, a.bs_i, qs + 4 * lh, qe, a.inv_scale);
+      }
       // lane (key li) holds query rows i = 8g + 4lh + e, r = 4g + e
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -839,6 +850,8 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
       for (int d = 0; d < D; ++d) s = fmaf(qr[d], sK[r][d], s);
 #pragma unroll
       for (int d = 0; d < DV; ++d) dp = fmaf(gr[d], sV[r][d], dp);
+      if (a.bias)
+        s = fmaf(a.bias[b * a.bs_b + hq * a.bs_h + (long long)row * a.bs_i + (long long)j * a.bs_j], a.inv_scale, s);
       const float p = fast_exp2(fmaf(s, a.scale_log2, -lse2));
       const float ds = p * (dp - Di);
 #pragma unroll
@@ -917,6 +930,8 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
         for (int d = 0; d < D; ++d) s = fmaf(sQ[r][d], kr[d], s);
 #pragma unroll
         for (int d = 0; d < DV; ++d) dp = fmaf(sG[r][d], vr[d], dp);
+        if (a.bias)
+          s = fmaf(a.bias[b * a.bs_b + hq * a.bs_h + (long long)i * a.bs_i + (long long)key * a.bs_j], a.inv_scale, s);
         const float p = fast_exp2(fmaf(s, a.scale_log2, -sL[r]));
         const float ds = p * (dp - sDv[r]);
 #pragma unroll

@@ -35,6 +35,12 @@ struct FwdArgs {
   int Dv;             // head dim of v and o (may differ from D, the q/k head dim)
   int has_sink;       // softmax with a sink term exp(z_h) in each row's denominator
   const float* sink;  // [Hq] sink logits z_h (natural units); NULL with has_sink: z = 0
+  // Additive logit bias (natural units) or NULL: element (b, hq, i, j) at
+  // bias[b*bs_b + hq*bs_h + i*bs_i + j*bs_j] (a zero stride broadcasts).  It enters the
+  // raw dot products as bias / scale.
+  const float* bias;
+  long long bs_b, bs_h, bs_i, bs_j;
+  float inv_scale;
   // Visibility of (row i, key j): lo_off <= (j - i) + delta <= hi_off, with
   // delta = kv_pos0 - q_pos0 and j < Skv.
   int delta;
@@ -72,6 +78,9 @@ struct BwdArgs {
   int has_sink;       // as in FwdArgs: the LSE includes exp(z_h)
   const float* sink;  // [Hq] or NULL (z = 0)
   float* dsink;       // [Hq] output dL/dz_h (learnable sink), or NULL
+  const float* bias;  // as in FwdArgs
+  long long bs_b, bs_h, bs_i, bs_j;
+  float inv_scale;
   int delta, lo_off, hi_off;
   float scale, scale_log2;
   int kv_block, n_vblocks;     // virtual key blocks (ring order of the dq pass)
@@ -136,6 +145,20 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Additive logit bias on the 16 score registers of one lane of a 32x32 MFMA tile:
+// register r holds the pair at index first + 8(r>>2) + (r&3) along the tile's register
+// dimension (keys in the forward and dq kernels, query rows in dk/dv); p points at the
+// bias of the lane's own row (or key) and st is the stride along the register dimension.
+// Indices >= limit are skipped (their scores are already masked).
+__device__ __forceinline__ void add_bias16(f32x16& s, const float* p, long long st, int first, int limit,
+                                           float inv_scale) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int x = first + 8 * (r >> 2) + (r & 3);
+    if (x < limit) s[r] = fmaf(p[(long long)x * st], inv_scale, s[r]);
+  }
+}
 
 // log2 of (l * 2^mm + 2^zz) for a row's key statistics (mm = m * log2 e, l relative to
 // m) and a sink logit zz in log2 units, without overflow; +inf when the row sees no key.

@@ -243,6 +243,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
           if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
         }
     }
+    if (a.bias) {
+      cold_path();
+      const float* bp = a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) add_bias16(s[mb], bp, a.bs_j, ts + 32 * mb + 4 * lh, tend, a.inv_scale);
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -473,6 +479,8 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
       float dot = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) dot = fmaf(qr[d], sK[r][d], dot);
+      if (a.bias && j < tend) dot = fmaf(a.bias[b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i +
+                                                (long long)j * a.bs_j], a.inv_scale, dot);
       s[r] = (j < my_jmin || j > my_jmax || j >= tend) ? -INFINITY : dot * a.scale_log2;
       mx = fmaxf(mx, s[r]);
     }

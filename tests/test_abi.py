@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
 
 
 def params(**kw):
@@ -61,8 +61,9 @@ def fwd_status(lib, p, ptr=None):
 
 
 def test_struct_layout(lib):
-    assert ctypes.sizeof(rea.AttnParams) == 128
+    assert ctypes.sizeof(rea.AttnParams) == 168
     assert rea.AttnParams.softmax_type.offset == 104          # ATTN_PARAMS_V1_SIZE
+    assert rea.AttnParams.bias.offset == 128                  # ATTN_PARAMS_V2_SIZE
     assert ctypes.sizeof(rea.SelectParams) == 40
     assert rea.SelectParams.seqlen_kv.offset == 32          # SELECT_PARAMS_V1_SIZE
     # a zero batch is a successful no-op only when the struct size matches
@@ -91,6 +92,7 @@ def test_struct_layout(lib):
     (dict(scale=float("inf")), rea.ATTN_ERR_INVALID_ARG, b"scale"),
     (dict(head_dim_v=-1), rea.ATTN_ERR_INVALID_ARG, b"head_dim_v"),
     (dict(softmax_type=3), rea.ATTN_ERR_INVALID_ARG, b"softmax_type"),
+    (dict(bias=0x1002), rea.ATTN_ERR_INVALID_ARG, b"bias"),
     (dict(softmax_type=2), rea.ATTN_ERR_INVALID_ARG, b"sink"),
     (dict(softmax_type=2, sink=0x1002), rea.ATTN_ERR_INVALID_ARG, b"sink"),
     (dict(head_dim_v=32), rea.ATTN_ERR_UNSUPPORTED, b"head_dim_v"),
@@ -109,6 +111,21 @@ def test_head_dim_pairs_accepted(lib, dtype, d, dv):
     the NULL q pointer, so nothing is launched)."""
     assert fwd_status(lib, params(dtype=dtype, head_dim=d, head_dim_v=dv)) == rea.ATTN_ERR_INVALID_ARG
     assert b"q is NULL" in lib.attn_last_error()
+
+
+def test_bias_stride_checks(lib):
+    p = params(bias=0x1000)
+    p.bias_stride[2] = -1
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"bias_stride" in lib.attn_last_error()
+    p.bias_stride[2] = 0
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"q is NULL" in lib.attn_last_error()
+
+
+def test_version2_struct_is_accepted(lib):
+    """A 128-byte struct (before the bias fields) reads as having no bias."""
+    p = params(batch=1, bias=0x1002)                 # misaligned bias past the v2 size: ignored
+    p.struct_size = 128
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"q is NULL" in lib.attn_last_error()
 
 
 def test_version1_struct_is_accepted(lib):

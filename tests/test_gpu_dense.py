@@ -167,6 +167,57 @@ def test_sink_softmax(gpu, case):
         check_sum("dsink", grads[3], dz_r, np.abs(p_sink * d_row).sum(axis=(0, 2)), dt)
 
 
+BIAS_CASES = [
+    # id, dtype, B, S, Hq, Hkv, D, Dv, causal, window, kv_block, bias shape, kind
+    ("bias_full_bf16_causal_gqa2", "bf16", 2, 300, 4, 2, 128, 128, True, (-1, -1), 0, "bhij", "randn"),
+    ("bias_keypad_bf16_full", "bf16", 2, 260, 4, 4, 64, 64, False, (-1, -1), 0, "b11j", "keypad"),
+    ("bias_row_bf16_swa_gqa16", "bf16", 1, 515, 16, 1, 128, 128, True, (37, 0), 0, "1hi1", "randn"),
+    ("bias_dead_rows_bf16_ring", "bf16", 1, 512, 4, 2, 128, 128, True, (-1, -1), 128, "b1ij", "deadrows"),
+    ("bias_full_bf16_mla", "bf16", 1, 333, 4, 1, 128, 64, True, (-1, -1), 0, "bhij", "randn"),
+    ("bias_full_f32_d64", "f32", 1, 200, 4, 2, 64, 64, True, (-1, -1), 0, "bhij", "randn"),
+]
+
+
+def make_bias(kind, shape_code, B, Hq, S, seed):
+    dims = {"b": B, "h": Hq, "i": S, "j": S, "1": 1}
+    shape = tuple(dims[c] for c in shape_code)
+    if kind == "randn":
+        return 2.0 * workloads.random_tensor(shape, seed, dtype=torch.float32)
+    bias = torch.zeros(shape, dtype=torch.float32)
+    if kind == "keypad":                       # the last 37 keys of every sequence are padding
+        bias[..., S - 37:] = float("-inf")
+    else:                                      # random -inf pairs and a few rows with no key at all
+        g = torch.Generator().manual_seed(seed)
+        bias[torch.rand(shape, generator=g) < 0.2] = float("-inf")
+        bias[..., 5, :] = float("-inf")
+        bias[..., 200:203, :] = float("-inf")
+    return bias
+
+
+@pytest.mark.parametrize("case", BIAS_CASES, ids=[c[0] for c in BIAS_CASES])
+def test_additive_bias(gpu, case):
+    """bpt.py's additive logit bias (broadcast shapes, -inf padding, rows with no key left)
+    through the forward and backward kernels (both workgroup shapes, MLA dims, fp32)."""
+    name, dt, B, S, Hq, Hkv, D, Dv, causal, window, kvb, shape_code, kind = case
+    t = tdtype(dt)
+    seed = zlib.crc32(name.encode()) % 10000
+    q, k, v, do = (rnd((B, S, Hq, D), seed, t), rnd((B, S, Hkv, D), seed + 1, t),
+                   rnd((B, S, Hkv, Dv), seed + 2, t), rnd((B, S, Hq, Dv), seed + 3, t))
+    bias = make_bias(kind, shape_code, B, Hq, S, seed + 4)
+    kw = dict(causal=causal, window=window, kv_block=kvb)
+    qd, kd, vd, dod, bd = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), bias.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, bias=bd, **kw)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, bias=bd, **kw)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=causal, window=window, bias=bias)
+    check_close("o", o, o_r, dt)
+    check_stats(m, l, m_r, l_r, dt)
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, causal=causal, window=window, bias=bias)
+    check_close("dq", dq, dq_r, dt)
+    check_close("dk", dk, dk_r, dt)
+    check_close("dv", dv, dv_r, dt)
+
+
 def test_sink_carry_is_applied_once(gpu):
     """Two ring steps with the carry handed over: the sink enters only when the output is
     finalised, so the result equals one call and the oracle."""
