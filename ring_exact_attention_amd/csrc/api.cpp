@@ -53,6 +53,7 @@ struct Problem {
   float* dsink = nullptr;
   const float* bias = nullptr;
   long long bias_stride[4] = {0, 0, 0, 0};
+  bool bias_vec4 = false;
 };
 
 static_assert(offsetof(attn_params, softmax_type) == ATTN_PARAMS_V1_SIZE,
@@ -169,6 +170,11 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   r.dsink = p->softmax_type == ATTN_SOFTMAX_LEARNABLE ? p->dsink : nullptr;
   r.bias = p->bias;
   for (int d = 0; d < 4; ++d) r.bias_stride[d] = p->bias_stride[d];
+  // Rows of the bias read as 16-byte vectors by the bf16 kernels: unit key stride, every
+  // row start 16-byte aligned, and key tiles that start at multiples of 4 keys.
+  r.bias_vec4 = r.bias && r.bias_stride[3] == 1 && ((uintptr_t)r.bias & 15u) == 0 &&
+                r.bias_stride[0] % 4 == 0 && r.bias_stride[1] % 4 == 0 && r.bias_stride[2] % 4 == 0 &&
+                r.Skv % 4 == 0 && r.kv_block % 4 == 0;
   return ATTN_OK;
 }
 
@@ -356,6 +362,7 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
   a.bs_h = r.bias_stride[1];
   a.bs_i = r.bias_stride[2];
   a.bs_j = r.bias_stride[3];
+  a.bias_vec4 = r.bias_vec4 ? 1 : 0;
   a.inv_scale = 1.f / r.scale;
   a.delta = r.delta;
   a.lo_off = r.lo_off;
@@ -449,6 +456,7 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
   a.bs_h = r.bias_stride[1];
   a.bs_i = r.bias_stride[2];
   a.bs_j = r.bias_stride[3];
+  a.bias_vec4 = r.bias_vec4 ? 1 : 0;
   a.inv_scale = 1.f / r.scale;
   a.delta = r.delta;
   a.lo_off = r.lo_off;

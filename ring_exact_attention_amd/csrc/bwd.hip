@@ -101,7 +101,7 @@ struct BwdQCfg {
   static constexpr int MAIN = cmax(cmax(NS * STAGE, STAGE + NW * 32 * 2 * D), NW * 32 * (2 * D + 16));
 };
 
-template <int D, int DV, int NW>
+template <int D, int DV, int NW, bool BIAS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a) {
   using C = BwdQCfg<D, DV, NW>;
   static_assert(DV <= D, "the v head dim may not exceed the q/k head dim");
@@ -207,6 +207,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
   bf16x8 dsb[4];                                   // dS^T of the last VALU block, B operands
   bool s_valid = false, ds_valid = false;
 
+  // With a bias, s holds the raw bias of the next tile whose S is computed (loaded once
+  // the previous scores are consumed); the S MFMAs accumulate onto bias / scale.
+  const float* const brow =
+      BIAS ? a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i : nullptr;
+  auto bias_load = [&](int ts, int kend) {
+    if constexpr (BIAS) {
+      const int last = min(kend, a.Skv) - 1;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        bias_fetch16(s[mb], brow, a.bs_j, ts + 32 * mb + 4 * lh, last, ts, a.bias_vec4 != 0);
+    }
+  };
+
   auto mfma_block = [&](bool do_s, int ts_s, int kend_s, int st_s, int st_p) {
     __builtin_amdgcn_s_setprio(1);
     s_valid = false;
@@ -218,7 +231,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[mb][r] = 0.f;
+          s[mb][r] = BIAS ? s[mb][r] * a.inv_scale : 0.f;
           dp[mb][r] = 0.f;
         }
 #pragma unroll
@@ -262,12 +275,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
           const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
           if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
         }
-    }
-    if (a.bias) {
-      cold_path();
-      const float* bp = a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) add_bias16(s[mb], bp, a.bs_j, ts + 32 * mb + 4 * lh, tend, a.inv_scale);
     }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -370,12 +377,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
     // step t runs S, dP of tile t, then dS, then dQ += K^T dS of the same tile, while tile
     // t+1 is copied into the other stage (which held tile t-1).
     int st = 0;
+    if (have_c) bias_load(ts_c, ke_c);
     while (have_c) {
       int ts_n = 0, ke_n = 0;
       const bool have_n = it.next(ts_n, ke_n);
       if (have_n) issue(ts_n, st ^ 1);
       mfma_block(true, ts_c, ke_c, st, st);
       valu_block(ts_c, ke_c);
+      if (have_n) bias_load(ts_n, ke_n);
       mfma_block(false, ts_c, ke_c, st, st);
       wait_vmcnt0();
       __syncthreads();
@@ -385,6 +394,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
   } else {
     int st_c = 0, st_p = 0;
     if (grp == 0) {
+      if (have_c) bias_load(ts_c, ke_c);
       while (have_c || have_p) {
         int ts_n = 0, ke_n = 0;
         const bool have_n = have_c && it.next(ts_n, ke_n);
@@ -393,6 +403,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
         mfma_block(have_c, ts_c, ke_c, st_c, st_p);
         __syncthreads();
         valu_block(ts_c, ke_c);
+        if (have_n) bias_load(ts_n, ke_n);
         wait_vmcnt0();
         __syncthreads();
         have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
@@ -405,6 +416,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
         const int st_n = st_c == C::NS - 1 ? 0 : st_c + 1;
         if (have_n) issue(ts_n, st_n);
         valu_block(ts_p, ke_p);
+        if (have_c) bias_load(ts_c, ke_c);
         __syncthreads();
         mfma_block(have_c, ts_c, ke_c, st_c, st_p);
         wait_vmcnt0();
@@ -465,7 +477,7 @@ struct BwdKVCfg {
   static constexpr int VCPT = BK * DCV / 256;     // 16-byte chunks of the V tile per thread
 };
 
-template <int D, int DV>
+template <int D, int DV, bool BIAS>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdKVCfg<D, DV>;
   static_assert(DV <= D, "the v head dim may not exceed the q/k head dim");
@@ -603,32 +615,53 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int g_off = C::GL::idx(li, 8 * lh);
   const int v_off = C::VL::idx(wave * 32 + li, 8 * lh);
 
+  // With a bias, S accumulates onto bias / scale.  A bias without a row stride (bs_i == 0,
+  // e.g. key padding) is one value per lane and q head, fetched a step ahead (bkey);
+  // otherwise the step's 16 row values are read into s at the top of the step, before the
+  // next step's copies are issued.  Rows past the step's end read row qs and are masked.
+  const bool bias_rows = BIAS && a.bs_i != 0;
+  auto bias_ptr = [&](int hq_) {
+    return a.bias + b * a.bs_b + hq_ * a.bs_h + (long long)min(key, a.Skv - 1) * a.bs_j;
+  };
+  float bkey = 0.f;
+
   int hq = 0, qs = 0, rend = 0;
   bool have = next_step(hq, qs, rend);
   if (have) {
     load_step(hq, qs);
     store_step(0);
+    if (BIAS && !bias_rows) bkey = *bias_ptr(hq);
   }
   __syncthreads();
   int cur = 0;
   while (have) {
     int nhq = 0, nqs = 0, nrend = 0;
     const bool nhave = next_step(nhq, nqs, nrend);
-    if (nhave) load_step(nhq, nqs);
 
     const int qe = min(rend, a.Sq);   // rows >= qe are not part of this step
     // pair (i, j) visible iff lo_off <= j - i + delta <= hi_off
     const int dmin = kw0 - (qs + C::BQ - 1) + a.delta;   // smallest j - i + delta in the step
     const int dmax = w_klast - qs + a.delta;             // largest
     const bool empty = !wave_on || dmax < a.lo_off || dmin > a.hi_off || qs >= qe;
+    f32x16 s;
+    if (BIAS && !empty) {
+      if (bias_rows) {
+        bias_fetch16(s, bias_ptr(hq), a.bs_i, qs + 4 * lh, qe - 1, qs, false);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = bkey;
+      }
+    }
+    if (nhave) load_step(nhq, nqs);
+    if (BIAS && !bias_rows && nhave) bkey = *bias_ptr(nhq);
     if (!empty) {
       const bool full = dmin >= a.lo_off && dmax <= a.hi_off && qs + C::BQ <= qe;
       const __bf16* qt_ = sQ[cur];
       const __bf16* gt_ = sG[cur];
-      f32x16 s, dp;
+      f32x16 dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
+        s[r] = BIAS ? s[r] * a.inv_scale : 0.f;
         dp[r] = 0.f;
       }
 #pragma unroll
@@ -652,11 +685,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
           if (ihi_v < ilo_v || (uint32_t)(base + ioff) > span) s[r] = -INFINITY;
         }
       }
-      if (a.bias) {
-        cold_path();
-        const float* bp = a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(key, a.Skv - 1) * a.bs_j;
-        add_bias16(s, bp, a.bs_i, qs + 4 * lh, qe, a.inv_scale);
-      }
       // lane (key li) holds query rows i = 8g + 4lh + e, r = 4g + e
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -670,15 +698,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
           dp[r] = p * (dp[r] - d4[e]);
         }
       }
+      u32x4 pb[2], sb[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 pb, sb;
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          pb[w] = pack_bf16x2(s[8 * ks + 2 * w], s[8 * ks + 2 * w + 1]);
-          sb[w] = pack_bf16x2(dp[8 * ks + 2 * w], dp[8 * ks + 2 * w + 1]);
+          pb[ks][w] = pack_bf16x2(s[8 * ks + 2 * w], s[8 * ks + 2 * w + 1]);
+          sb[ks][w] = pack_bf16x2(dp[8 * ks + 2 * w], dp[8 * ks + 2 * w + 1]);
         }
-        const bf16x8 pbf = as_bf16x8(pb), sbf = as_bf16x8(sb);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pbf = as_bf16x8(pb[ks]), sbf = as_bf16x8(sb[ks]);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           if (db < C::DBV) {
@@ -866,7 +896,7 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
   }
 }
 
-template <int D, int DV>
+template <int D, int DV, bool BIAS>
 __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
   constexpr int BK = 128, BQ = 32;
   __shared__ float sQ[BQ][D + 1], sG[BQ][DV + 1], sL[BQ], sDv[BQ];
@@ -930,7 +960,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
         for (int d = 0; d < D; ++d) s = fmaf(sQ[r][d], kr[d], s);
 #pragma unroll
         for (int d = 0; d < DV; ++d) dp = fmaf(sG[r][d], vr[d], dp);
-        if (a.bias)
+        if (BIAS)
           s = fmaf(a.bias[b * a.bs_b + hq * a.bs_h + (long long)i * a.bs_i + (long long)key * a.bs_j], a.inv_scale, s);
         const float p = fast_exp2(fmaf(s, a.scale_log2, -sL[r]));
         const float ds = p * (dp - sDv[r]);
@@ -1001,7 +1031,8 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
     if (pre) launch_pre<T, DDV>(a, stream);                                     \
     if (dq) DQ_LAUNCH;                                                          \
     if (dkdv) {                                                                 \
-      hipLaunchKernelGGL((DKV<DD, DDV>), gk, bk, 0, stream, a);                 \
+      if (a.bias) hipLaunchKernelGGL((DKV<DD, DDV, true>), gk, bk, 0, stream, a); \
+      else hipLaunchKernelGGL((DKV<DD, DDV, false>), gk, bk, 0, stream, a);       \
       if (a.kv_splits > 1) {                                                    \
         const long long nk = (long long)a.B * a.Skv * a.Hkv * a.D;              \
         const long long nv = (long long)a.B * a.Skv * a.Hkv * a.Dv;             \
@@ -1012,10 +1043,15 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
       }                                                                         \
     }                                                                           \
   } while (0)
-#define REA_DQ_BF16(DD, DDV)                                                     \
-  do {                                                                          \
-    if (w4) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 4>), gq, bq, 0, stream, a); \
-    else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 8>), gq, bq, 0, stream, a);    \
+#define REA_DQ_BF16(DD, DDV)                                                                    \
+  do {                                                                                         \
+    if (a.bias) {                                                                              \
+      if (w4) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 4, true>), gq, bq, 0, stream, a); \
+      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 8, true>), gq, bq, 0, stream, a);    \
+    } else {                                                                                   \
+      if (w4) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 4, false>), gq, bq, 0, stream, a); \
+      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 8, false>), gq, bq, 0, stream, a);    \
+    }                                                                                          \
   } while (0)
 #define REA_DQ_F32(DD, DDV) hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, DDV>), gq, bq, 0, stream, a)
   if (!head_dims_supported(dtype, a.D, a.Dv)) return hipErrorInvalidValue;

@@ -41,6 +41,7 @@ struct FwdArgs {
   const float* bias;
   long long bs_b, bs_h, bs_i, bs_j;
   float inv_scale;
+  int bias_vec4;      // rows readable as 16-byte vectors (unit key stride, aligned)
   // Visibility of (row i, key j): lo_off <= (j - i) + delta <= hi_off, with
   // delta = kv_pos0 - q_pos0 and j < Skv.
   int delta;
@@ -81,6 +82,7 @@ struct BwdArgs {
   const float* bias;  // as in FwdArgs
   long long bs_b, bs_h, bs_i, bs_j;
   float inv_scale;
+  int bias_vec4;
   int delta, lo_off, hi_off;
   float scale, scale_log2;
   int kv_block, n_vblocks;     // virtual key blocks (ring order of the dq pass)
@@ -146,17 +148,30 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Additive logit bias on the 16 score registers of one lane of a 32x32 MFMA tile:
-// register r holds the pair at index first + 8(r>>2) + (r&3) along the tile's register
-// dimension (keys in the forward and dq kernels, query rows in dk/dv); p points at the
-// bias of the lane's own row (or key) and st is the stride along the register dimension.
-// Indices >= limit are skipped (their scores are already masked).
-__device__ __forceinline__ void add_bias16(f32x16& s, const float* p, long long st, int first, int limit,
-                                           float inv_scale) {
+// Raw additive bias (without the 1/scale factor) for the 16 score registers of one lane
+// of a 32x32 MFMA tile: register r holds index x = first + 8(r>>2) + (r&3) along the
+// register dimension (keys in the forward and dq kernels, query rows in dk/dv); p points
+// at the bias of the lane's own row (or key), st is the stride along x.  An x beyond
+// `last` reads element `safe` instead (an in-range index; the caller masks those scores),
+// so the loads carry no branches and are waited for together where d is first used.
+// vec4 (st == 1, p 16-byte aligned, first and safe multiples of 4 and every in-range
+// group of 4 whole): four 16-byte loads instead of 16 scalar ones.
+__device__ __forceinline__ void bias_fetch16(f32x16& d, const float* p, long long st, int first, int last,
+                                             int safe, bool vec4) {
+  if (vec4) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int x = first + 8 * (r >> 2) + (r & 3);
-    if (x < limit) s[r] = fmaf(p[(long long)x * st], inv_scale, s[r]);
+    for (int g = 0; g < 4; ++g) {
+      const int x0 = first + 8 * g;
+      const f32x4 v = *(const f32x4*)(p + (x0 <= last ? x0 : safe));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[4 * g + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int x = first + 8 * (r >> 2) + (r & 3);
+      d[r] = p[(long long)(x <= last ? x : safe) * st];
+    }
   }
 }
 

@@ -66,7 +66,7 @@ struct FwdCfg {
 // Rows of the scores may grow by this much (log2 units) before the carry is rescaled.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int DV, int NW>
+template <int D, int DV, int NW, bool BIAS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D, DV, NW>;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
@@ -188,6 +188,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   bf16x8 pb[4];                                    // P^T of the last softmax, B operands
   bool s_valid = false, p_valid = false;
 
+  // With a bias, s holds the raw bias of the next tile whose S is computed (loaded as
+  // soon as the previous scores are consumed, so the loads overlap other work); the S
+  // MFMAs accumulate onto bias / scale.  Keys past the tile's end read key ts instead
+  // and are masked with the rest.
+  const float* const brow =
+      BIAS ? a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i : nullptr;
+  auto bias_load = [&](int ts, int kend) {
+    if constexpr (BIAS) {
+      const int last = min(kend, a.Skv) - 1;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        bias_fetch16(s[mb], brow, a.bs_j, ts + 32 * mb + 4 * lh, last, ts, a.bias_vec4 != 0);
+    }
+  };
+
   // MFMA block: S^T of tile ts_s (K in slot st_s) and O^T += V^T P^T for the tile whose
   // V is in slot st_p.
   auto mfma_block = [&](bool do_s, int ts_s, int kend_s, int st_s, int st_p) {
@@ -199,7 +214,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[mb][r] = BIAS ? s[mb][r] * a.inv_scale : 0.f;
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
@@ -242,12 +257,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
           const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
           if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
         }
-    }
-    if (a.bias) {
-      cold_path();
-      const float* bp = a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) add_bias16(s[mb], bp, a.bs_j, ts + 32 * mb + 4 * lh, tend, a.inv_scale);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -319,12 +328,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     // step t runs [S of t, PV of t-1] then the softmax of t, while K of t+1 and V of t
     // are copied (K slot (t+1)&1 last held tile t-1, V slot t&1 tile t-2).
     int sk = 0;                                    // K slot of the current tile
+    if (have_c) bias_load(ts_c, ke_c);
     while (have_c || have_p) {
       int ts_n = 0, ke_n = 0;
       const bool have_n = have_c && it.next(ts_n, ke_n);
       issue(have_n, ts_n, sk ^ 1, have_c, ts_c, sk);
       mfma_block(have_c, ts_c, ke_c, sk, sk ^ 1);
       softmax_block(ts_c, ke_c);
+      if (have_n) bias_load(ts_n, ke_n);
       wait_vmcnt0();
       __syncthreads();
       have_p = have_c; ts_p = ts_c; ke_p = ke_c;
@@ -334,6 +345,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   } else {
     int st_c = 0, st_p = 0;
     if (grp == 0) {
+      if (have_c) bias_load(ts_c, ke_c);
       while (have_c || have_p) {
         int ts_n = 0, ke_n = 0;
         const bool have_n = have_c && it.next(ts_n, ke_n);
@@ -342,6 +354,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
         mfma_block(have_c, ts_c, ke_c, st_c, st_p);
         __syncthreads();
         softmax_block(ts_c, ke_c);
+        if (have_n) bias_load(ts_n, ke_n);
         wait_vmcnt0();
         __syncthreads();
         have_p = have_c; ts_p = ts_c; ke_p = ke_c; st_p = st_c;
@@ -354,6 +367,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
         const int st_n = st_c == 2 ? 0 : st_c + 1;
         if (have_n) issue(true, ts_n, st_n, true, ts_n, st_n);
         softmax_block(ts_p, ke_p);
+        if (have_c) bias_load(ts_c, ke_c);
         __syncthreads();
         mfma_block(have_c, ts_c, ke_c, st_c, st_p);
         wait_vmcnt0();
@@ -543,10 +557,17 @@ static void launch_fwd_bf16(FwdArgs a, bool w4, hipStream_t stream) {
   a.n_hg = a.Hq >> a.gh_shift;
   a.n_qtiles = (a.Sq + a.rows_wg - 1) / a.rows_wg;
   const dim3 grid((unsigned)a.n_qtiles * a.B * a.n_hg), block(64 * nw);
-  if (w4)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 4>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 8>), grid, block, 0, stream, a);
+  if (a.bias) {
+    if (w4)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 4, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 8, true>), grid, block, 0, stream, a);
+  } else {
+    if (w4)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 4, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 8, false>), grid, block, 0, stream, a);
+  }
 }
 
 bool head_dims_supported(int dtype, int D, int Dv) {
