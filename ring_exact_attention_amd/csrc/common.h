@@ -119,6 +119,7 @@ struct SparseArgs {
   int B, S, E, top_n, sel_block, window;
   float scale_log2, scale;
   int Skv, q_pos0;    // key / value rows; position of query row 0 among them
+  int tpw;            // tokens per workgroup (power of two <= 32; set by the launcher)
 };
 
 // Backward of the gathered block-sparse attention.

@@ -5,11 +5,12 @@
 // block_select: one workgroup per (batch, block i of query positions; query row r sits
 // at position q_pos0 + r of the key sequence, so decoding a few new tokens against a
 // key cache is the same call).  The block's tokens score the candidate blocks
-// c < i in chunks of 64 (16 per wavefront) with fp64 MFMA
-// (bf16 queries are exact in fp64), the chunk's scores go to LDS, and one thread per
-// token merges them into its running top-n list kept in LDS (score descending; on
-// equal scores the earlier, lower index stays ahead).  The list is written sorted
-// ascending with -1 padding first.
+// c < i in chunks of 64 (16 per wavefront) with fp64 MFMA (bf16 queries are exact in
+// fp64), the chunk's scores go to LDS, and each token's running top-n list (in LDS,
+// score descending; on equal scores the lower index ahead) absorbs the chunk in one
+// parallel step: a wavefront per token ranks the candidates that beat the list's last
+// entry against the list and each other and writes every survivor to its rank.  The
+// list is written sorted ascending with -1 padding first.
 #include "common.h"
 #include "launch.h"
 
@@ -28,6 +29,18 @@ __global__ __launch_bounds__(256) void block_means_kernel(SelectArgs a) {
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
+// Lane y's value of x (y uniform across the wavefront).
+__device__ __forceinline__ double read_lane_f64(double x, int y) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, y);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), y);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Row pitch (elements) of the queries staged in LDS: padded by 8 so that the 16 rows one
+// MFMA operand read touches fall in different banks, unless that would pass 64 KiB.
+__host__ __device__ inline int sq_pitch(int bs, int E) { return bs * (E + 8) * 2 <= 65536 ? E + 8 : E; }
+
 // Scores by v_mfma_f64_16x16x4_f64 (A: lane l holds A[l % 16][l / 16]; B: B[l / 16][l % 16];
 // D: lane l, register r holds D[l / 16 + 4r][l % 16]).  The contraction index of the
 // 4 MFMAs of one 16-wide slice is e = 16m + 4(l / 16) + s, so each lane reads 4
@@ -37,7 +50,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
   constexpr int TB = BS / 16;             // 16-token blocks
   constexpr int CH = 64;                  // candidates per chunk (16 per wave)
   constexpr int NMAX = 16;                // largest top_n
-  extern __shared__ __attribute__((aligned(16))) __bf16 sq[];   // BS * E (dynamic, <= 64 KiB)
+  extern __shared__ __attribute__((aligned(16))) __bf16 sq[];   // BS rows of sq_pitch (dynamic)
   __shared__ double ssc[BS][CH + 1];
   __shared__ double best_s[BS][NMAX];
   __shared__ int best_c[BS][NMAX];
@@ -50,14 +63,16 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
   const int t0 = p0 - a.q_pos0;                               // its query row
   const int ntok = min((i + 1) * BS, a.q_pos0 + a.S) - p0;
   const int ncand = min(i, a.nblk);
-  int kept = 0;                           // list length of token `tid` (threads < BS)
 
   if (ncand > 0) {
     const __bf16* qp = (const __bf16*)a.q + ((size_t)b * a.S + t0) * a.E;
-    const int chunks = ntok * a.E / 8;
-    for (int c = tid; c < chunks; c += 256)
-      *(u32x4*)&sq[c * 8] = *(const u32x4*)(qp + (size_t)c * 8);
-    for (int c = chunks + tid; c < BS * a.E / 8; c += 256) *(u32x4*)&sq[c * 8] = u32x4{0u, 0u, 0u, 0u};
+    const int pitch = sq_pitch(BS, a.E), cpr = a.E / 8;
+    for (int c = tid; c < BS * cpr; c += 256) {
+      const int t = c / cpr, ch = c - t * cpr;
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (t < ntok) u = *(const u32x4*)(qp + (size_t)t * a.E + 8 * ch);
+      *(u32x4*)&sq[t * pitch + 8 * ch] = u;
+    }
     __syncthreads();
 
     const double* mbase = a.means + (size_t)b * a.nblk * a.E;
@@ -68,16 +83,29 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
       f64x4 acc[TB];
 #pragma unroll
       for (int x = 0; x < TB; ++x) acc[x] = f64x4{0.0, 0.0, 0.0, 0.0};
-      for (int e0 = 0; e0 < a.E; e0 += 16) {
-        const f64x4 mv = *(const f64x4*)(mrow + e0);
+      // The candidate's means stream through a ring of PF 16-wide slices loaded PF slices
+      // ahead (a past-the-end slice rereads slice 0), so the L2 latency overlaps the MFMAs.
+      constexpr int PF = 8;
+      f64x4 mv[PF];
 #pragma unroll
-        for (int x = 0; x < TB; ++x) {
-          const u32x2 qu = *(const u32x2*)&sq[(16 * x + col) * a.E + e0 + 4 * grp];
-          const double q0 = bf16_lo(qu[0]), q1 = bf16_hi(qu[0]), q2 = bf16_lo(qu[1]), q3 = bf16_hi(qu[1]);
-          acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(q0, mv[0], acc[x], 0, 0, 0);
-          acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(q1, mv[1], acc[x], 0, 0, 0);
-          acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(q2, mv[2], acc[x], 0, 0, 0);
-          acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(q3, mv[3], acc[x], 0, 0, 0);
+      for (int u = 0; u < PF; ++u) mv[u] = *(const f64x4*)(mrow + (16 * u < a.E ? 16 * u : 0));
+      for (int e0 = 0; e0 < a.E; e0 += 16 * PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          const int e = e0 + 16 * u, en = e + 16 * PF;
+          const f64x4 m4 = mv[u];
+          mv[u] = *(const f64x4*)(mrow + (en < a.E ? en : 0));
+          if (e < a.E) {
+#pragma unroll
+            for (int x = 0; x < TB; ++x) {
+              const u32x2 qu = *(const u32x2*)&sq[(16 * x + col) * pitch + e + 4 * grp];
+              const double q0 = bf16_lo(qu[0]), q1 = bf16_hi(qu[0]), q2 = bf16_lo(qu[1]), q3 = bf16_hi(qu[1]);
+              acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(q0, m4[0], acc[x], 0, 0, 0);
+              acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(q1, m4[1], acc[x], 0, 0, 0);
+              acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(q2, m4[2], acc[x], 0, 0, 0);
+              acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(q3, m4[3], acc[x], 0, 0, 0);
+            }
+          }
         }
       }
 #pragma unroll
@@ -85,23 +113,37 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) ssc[16 * x + grp + 4 * r][16 * wave + col] = acc[x][r];
       __syncthreads();
-      if (tid < ntok) {
-        const int nc = min(CH, ncand - c0);
-        for (int y = 0; y < nc; ++y) {
-          const double sc = ssc[tid][y];
-          const int c = c0 + y;
-          // insert (sc, c) if it beats the last kept entry; candidates arrive in
-          // ascending index order, so an equal score never displaces an entry.
-          if (kept < a.top_n || sc > best_s[tid][a.top_n - 1]) {
-            int pos = kept < a.top_n ? kept : a.top_n - 1;
-            while (pos > 0 && sc > best_s[tid][pos - 1]) {
-              best_s[tid][pos] = best_s[tid][pos - 1];
-              best_c[tid][pos] = best_c[tid][pos - 1];
-              --pos;
-            }
-            best_s[tid][pos] = sc;
-            best_c[tid][pos] = c;
-            if (kept < a.top_n) ++kept;
+      // Merge the chunk into each token's list.  Before the chunk the list holds
+      // kept0 = min(n, c0) entries.  Lane y carries candidate c0 + y; those not above
+      // the last entry of a full list cannot place (ties go to the lower index).  A
+      // survivor's rank counts the list entries >= it and the survivors above it (or
+      // equal with a lower index); list entry e moves down by the survivors above it.
+      {
+        const int n = a.top_n, nc = min(CH, ncand - c0), kept0 = min(n, c0);
+        for (int t = wave; t < ntok; t += 4) {
+          const bool cval = lane < nc;
+          const double v = cval ? ssc[t][lane] : 0.0;
+          const double thr = kept0 < n ? -INFINITY : best_s[t][n - 1];
+          const bool surv = cval && v > thr;
+          const uint64_t P = __ballot(surv);
+          const bool is_l = lane < kept0;
+          const double ls = is_l ? best_s[t][lane] : 0.0;
+          const int lc = is_l ? best_c[t][lane] : 0;
+          int rc = 0, rl = lane;
+          for (int e = 0; e < kept0; ++e) rc += read_lane_f64(ls, e) >= v ? 1 : 0;
+          for (uint64_t m = P; m; m &= m - 1) {
+            const int y = __builtin_ctzll(m);
+            const double w = read_lane_f64(v, y);
+            rc += (w > v || (w == v && y < lane)) ? 1 : 0;
+            rl += w > ls ? 1 : 0;
+          }
+          if (surv && rc < n) {
+            best_s[t][rc] = v;
+            best_c[t][rc] = c0 + lane;
+          }
+          if (is_l && rl < n) {
+            best_s[t][rl] = ls;
+            best_c[t][rl] = lc;
           }
         }
       }
@@ -110,6 +152,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
   }
 
   if (tid < ntok) {
+    const int kept = min(a.top_n, ncand);
     // sort the kept indices ascending (insertion sort on <= 16 entries)
     for (int x = 1; x < kept; ++x) {
       const int v = best_c[tid][x];
@@ -132,7 +175,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (a.S == 0) return hipGetLastError();
   const int nqb = (a.q_pos0 + a.S - 1) / a.bs - a.q_pos0 / a.bs + 1;
   const dim3 grid((unsigned)(a.B * nqb));
-  const size_t lds = (size_t)a.bs * a.E * sizeof(__bf16);
+  const size_t lds = (size_t)a.bs * sq_pitch(a.bs, a.E) * sizeof(__bf16);
   switch (a.bs) {
     case 16: hipLaunchKernelGGL(block_select_kernel<16>, grid, dim3(256), lds, stream, a); break;
     case 32: hipLaunchKernelGGL(block_select_kernel<32>, grid, dim3(256), lds, stream, a); break;

@@ -12,8 +12,9 @@
 namespace rea {
 
 // ---------------------------------------------------------------------------------
-// Block-shared form (E = 512, bs in {16, 32, 64}): one workgroup per 32 consecutive
-// tokens.  The tokens' selected block indices are sorted and deduplicated in LDS; each
+// Block-shared form (E = 512, bs in {16, 32, 64}): one workgroup per tpw <= 32
+// consecutive tokens (32 unless the grid would be small, as when decoding a few
+// tokens).  The tokens' selected block indices are sorted and deduplicated in LDS; each
 // distinct block u gets a per-token multiplicity cnt(u, t) (a token lists a block at
 // most once in a valid selection; -1 entries are one block whose rows are all token 0,
 // counted once per entry).  The window is covered by up to three 32-row blocks with a
@@ -35,15 +36,16 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
-  const int nqb = (a.S + kUQ - 1) / kUQ;
-  const int b = blockIdx.x / nqb, t0 = (blockIdx.x % nqb) * kUQ;
+  const int nqb = (a.S + a.tpw - 1) / a.tpw;
+  const int b = blockIdx.x / nqb, t0 = (blockIdx.x % nqb) * a.tpw;
+  const int tend = min(t0 + a.tpw, a.S);                      // this workgroup's tokens: [t0, tend)
   const int n = a.top_n, bs = a.sel_block, W = a.window;
 
   // ---- setup: sort (block, token) pairs, deduplicate, count per token
-  const int nu = build_union(a.sel, a.S, n, b, t0, (int*)&sV[0][0], ucnt, ublk, &s_nu);
+  const int nu = build_union(a.sel, a.S, tend, n, b, t0, (int*)&sV[0][0], ucnt, ublk, &s_nu);
 
   // ---- main loop over 32-row blocks: window blocks, then union blocks
-  const int nwin = (W + kUQ - 1 + 31) / 32;
+  const int nwin = (W + a.tpw - 1 + 31) / 32;
   const int nsub = (bs + 31) / 32;
   const int nsteps = nwin + nu * nsub;
   // Query row r sits at position q_pos0 + r of the key / value sequence (Skv rows): the
@@ -56,13 +58,14 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const __bf16*)a.v + kvbase, (uint32_t)a.Skv * row_b);
   const int e0 = kUDW * wave;                                  // this wave's embedding slice
   const int tok = t0 + li;                                     // this lane's token (B / C column)
+  const bool tok_ok = tok < tend;
   const int tpos = a.q_pos0 + tok;                             // its position
 
   bf16x8 qreg[kUDW / 16];
 #pragma unroll
   for (int kk = 0; kk < kUDW / 16; ++kk) {
     u32x4 u = {0u, 0u, 0u, 0u};
-    if (tok < a.S) u = *(const u32x4*)((const __bf16*)a.q + bbase + (size_t)tok * kSpE + e0 + 16 * kk + 8 * lh);
+    if (tok_ok) u = *(const u32x4*)((const __bf16*)a.q + bbase + (size_t)tok * kSpE + e0 + 16 * kk + 8 * lh);
     qreg[kk] = as_bf16x8(u);
   }
 
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int p = p0 + 8 * (r >> 2) + (r & 3);
-        wt[r] = (tok < a.S && p >= tpos - W + 1 && p <= tpos) ? 1.f : 0.f;
+        wt[r] = (tok_ok && p >= tpos - W + 1 && p <= tpos) ? 1.f : 0.f;
       }
     } else {
       const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
 
   const float l_used = l_part + other_half(l_part);
   const float corr = (m_true == -INFINITY) ? 0.f : fast_exp2(m_used - m_true);
-  if (tok < a.S) {
+  if (tok_ok) {
     const float inv = l_used > 0.f ? 1.f / l_used : 0.f;
     __bf16* op = (__bf16*)a.o + bbase + (size_t)tok * kSpE + e0;
 #pragma unroll
@@ -212,8 +215,13 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   }
 }
 
-hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
-  const long long nqb = (a.S + kUQ - 1) / kUQ;
+hipError_t launch_sparse(const SparseArgs& args, hipStream_t stream) {
+  // Fewer tokens per workgroup while the grid would leave most of the chip idle (few
+  // tokens, e.g. decoding): each workgroup then walks a smaller union of blocks.
+  SparseArgs a = args;
+  a.tpw = kUQ;
+  while (a.tpw > 1 && (long long)a.B * ((a.S + a.tpw - 1) / a.tpw) < 512) a.tpw >>= 1;
+  const long long nqb = (a.S + a.tpw - 1) / a.tpw;
   hipLaunchKernelGGL(sparse_union_kernel, dim3((unsigned)(a.B * nqb)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

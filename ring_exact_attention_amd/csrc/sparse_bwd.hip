@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   const int b = blockIdx.x / nqb, t0 = (blockIdx.x % nqb) * kUQ;
   const int n = a.top_n, bs = a.sel_block, W = a.window;
 
-  const int nu = build_union(a.sel, a.S, n, b, t0, (int*)&sK[0][0], ucnt, ublk, &s_nu);
+  const int nu = build_union(a.sel, a.S, a.S, n, b, t0, (int*)&sK[0][0], ucnt, ublk, &s_nu);
 
   const int nwin = (W + kUQ - 1 + 31) / 32;
   const int nsub = (bs + 31) / 32;

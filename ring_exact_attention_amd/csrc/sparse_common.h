@@ -14,12 +14,13 @@ constexpr int kUPITCH = kUDW + 32;   // slice row pitch (elements): conflict-fre
 constexpr int kUMaxEnt = 512;        // 32 tokens x top_n (<= 16)
 constexpr int kUSentinel = 0x7fffffff;
 
-// The selections of tokens t0 .. t0 + 31 of sequence b: their (block, token) pairs are
-// sorted by block in LDS, the distinct blocks go to ublk[0 .. nu) in ascending order
-// (-1 first), and ucnt[u][t / 4] byte t % 4 counts how often token t lists block u.
-// scratch: 3 * kUMaxEnt ints of LDS.  Called by all 256 threads; returns nu.
-__device__ __forceinline__ int build_union(const int32_t* sel, int S, int n, int b, int t0, int* scratch,
-                                           uint32_t (*ucnt)[kUQ / 4], int* ublk, int* s_nu) {
+// The selections of tokens t0 .. min(t0 + 32, tend) - 1 of sequence b (S tokens): their
+// (block, token) pairs are sorted by block in LDS, the distinct blocks go to
+// ublk[0 .. nu) in ascending order (-1 first), and ucnt[u][t / 4] byte t % 4 counts how
+// often token t0 + t lists block u.  scratch: 3 * kUMaxEnt ints of LDS.  Called by all
+// 256 threads; returns nu.
+__device__ __forceinline__ int build_union(const int32_t* sel, int S, int tend, int n, int b, int t0,
+                                           int* scratch, uint32_t (*ucnt)[kUQ / 4], int* ublk, int* s_nu) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int ne = kUQ * n;
   int* skey = scratch;
@@ -28,7 +29,7 @@ __device__ __forceinline__ int build_union(const int32_t* sel, int S, int n, int
     int key = kUSentinel, tok = 0;
     if (k < ne) {
       const int t = k / n, j = k % n;
-      if (t0 + t < S) {
+      if (t0 + t < tend) {
         const int c = sel[((size_t)b * S + t0 + t) * n + j];
         key = c < 0 ? -1 : c;
         tok = t;

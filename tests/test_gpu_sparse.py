@@ -21,7 +21,8 @@ def rnd(shape, seed):
 
 
 @pytest.mark.parametrize("B,S,E,bs,n", [(2, 256, 64, 16, 3), (1, 300, 512, 32, 8), (2, 200, 128, 64, 2),
-                                         (1, 1000, 512, 32, 16), (3, 64, 64, 32, 1)])
+                                         (1, 1000, 512, 32, 16), (3, 64, 64, 32, 1), (1, 700, 512, 64, 5),
+                                         (1, 520, 1024, 16, 16)])
 def test_select_small(gpu, B, S, E, bs, n):
     q, k = rnd((B, S, E), S + E), rnd((B, S, E), S + E + 1)
     idx = gpu.block_select(q.to(DEV), k.to(DEV), block_size=bs, top_n=n)
@@ -60,6 +61,23 @@ def test_select_full_size(gpu):
 def test_sparse_small(gpu, B, S, bs, n, W):
     E = 512
     q, k, v = rnd((B, S, E), 7 + S), rnd((B, S, E), 8 + S), rnd((B, S, E), 9 + S)
+    sel = select.block_select(q, k, block_size=bs, top_n=n)
+    o, m, l = gpu.attn_fwd_sparse(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(sel).to(DEV),
+                                  window=W, block_size=bs)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = sparse.sparse_attention(q, k, v, sel, window=W, block_size=bs)
+    check_close("o", o, o_r, "bf16")
+    np.testing.assert_allclose(m.cpu().numpy(), m_r, atol=1e-3, rtol=0)
+    np.testing.assert_allclose(l.cpu().numpy(), l_r, rtol=1e-3, atol=0)
+
+
+@pytest.mark.parametrize("B,S", [(1, 2048), (2, 4100)])
+def test_sparse_tokens_per_workgroup(gpu, B, S):
+    """Grids where a workgroup takes 4 (S 2048) or 16 (S 4100, ragged tail) tokens and
+    their shared union of blocks, between the one-token workgroups of small inputs and
+    the 32-token ones of the full workload."""
+    E, bs, n, W = 512, 32, 8, 32
+    q, k, v = rnd((B, S, E), 17 + S), rnd((B, S, E), 18 + S), rnd((B, S, E), 19 + S)
     sel = select.block_select(q, k, block_size=bs, top_n=n)
     o, m, l = gpu.attn_fwd_sparse(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(sel).to(DEV),
                                   window=W, block_size=bs)
