@@ -16,14 +16,37 @@
 
 namespace rea {
 
+// One workgroup per (batch, block): a thread sums 8 consecutive columns over every
+// RG-th row of the block (16-byte loads; RG = 256 / (E / 8) row groups), the row groups
+// are added in LDS.  All partial sums of bf16 values are exact in fp64, so the order
+// does not change the mean.
 __global__ __launch_bounds__(256) void block_means_kernel(SelectArgs a) {
+  __shared__ double part[256 * 8];
   const int c = blockIdx.x % a.nblk, b = blockIdx.x / a.nblk;
   const __bf16* kp = (const __bf16*)a.k + ((size_t)b * a.Skv + (size_t)c * a.bs) * a.E;
   double* mp = a.means + ((size_t)b * a.nblk + c) * a.E;
-  for (int e = threadIdx.x; e < a.E; e += 256) {
-    double s = 0.0;
-    for (int r = 0; r < a.bs; ++r) s += (double)(float)kp[(size_t)r * a.E + e];
-    mp[e] = s / (double)a.bs;
+  const int cpr = a.E / 8;                               // 16-byte chunks per row (8 .. 128)
+  const int rg = 256 / cpr;                               // row groups (2 .. 32)
+  const int tid = threadIdx.x, g = tid / cpr, ch = tid - g * cpr;
+  double s[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  if (g < rg) {
+    for (int r = g; r < a.bs; r += rg) {
+      const u32x4 u = *(const u32x4*)(kp + (size_t)r * a.E + 8 * ch);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        s[2 * w] += (double)bf16_lo(u[w]);
+        s[2 * w + 1] += (double)bf16_hi(u[w]);
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) part[x * 256 + tid] = s[x];
+  __syncthreads();
+  for (int e = tid; e < a.E; e += 256) {
+    const int ch2 = e / 8, x = e % 8;
+    double t = 0.0;
+    for (int g2 = 0; g2 < rg; ++g2) t += part[x * 256 + g2 * cpr + ch2];
+    mp[e] = t / (double)a.bs;
   }
 }
 
@@ -98,6 +121,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
           if (e < a.E) {
 #pragma unroll
             for (int x = 0; x < TB; ++x) {
+              if (16 * x >= ntok) break;                   // no token in this 16-row tile
               const u32x2 qu = *(const u32x2*)&sq[(16 * x + col) * pitch + e + 4 * grp];
               const double q0 = bf16_lo(qu[0]), q1 = bf16_hi(qu[0]), q2 = bf16_lo(qu[1]), q3 = bf16_hi(qu[1]);
               acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(q0, m4[0], acc[x], 0, 0, 0);
