@@ -44,8 +44,9 @@ def kernel_source_sha():
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3 FETCH_SIZE and
-    WRITE_SIZE runs summarised in profiles/kernels_<workload>.md (each counter scaled by
+    """HBM bytes per launch of `kernel` on `workload` (the config's workload label, '+'
+    written '_') from the rocprofv3 FETCH_SIZE and WRITE_SIZE runs summarised in
+    profiles/kernels_<workload>.md (each counter scaled by
     its reading for a plain copy of known size).  None when the file has no figure for
     it or the kernel sources have changed since the counters were taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"kernels_{workload}.md")
@@ -357,12 +358,14 @@ def main():
     bwd_ms = step_ms - seg_ms["attn_fwd"]
     bwd_tflops = f_bwd / (bwd_ms * 1e-3) / 1e12 if w.backward else None
 
+    label = (w.name + ("" if args.softmax == "vanilla" else f"+{args.softmax}_sink")
+             + ("" if args.bias == "none" else f"+{args.bias}_bias"))
     dom = max(seg_ms, key=seg_ms.get)
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(alg[dom] / (seg_ms[dom] * 1e-3) / 1e12, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(alg[dom] / (seg_ms[dom] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "avg_us": round(seg_ms[dom] * 1e3, 2), "alg_flop_per_launch": alg[dom],
-            "traffic": measured_traffic(w.name, dom)}
+            "traffic": measured_traffic(label.replace("+", "_"), dom)}
     if w.window[0] >= 0:        # sliding window: the kernels are HBM-bound
         roof.update({"bound": "hbm", "achieved": round(hbm[dom] / (seg_ms[dom] * 1e-3) / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -382,8 +385,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name + ("" if args.softmax == "vanilla" else f"+{args.softmax}_sink")
-                               + ("" if args.bias == "none" else f"+{args.bias}_bias"),
+        "config": {"workload": label,
                    "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "head_dim_v": Dv, "causal": w.causal, "window": list(w.window),
                    "virtual_blocks": (S // w.kv_block) if w.kv_block else 1,
