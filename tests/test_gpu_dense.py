@@ -358,6 +358,53 @@ def test_step_api_carry_equals_single_call(gpu, dt):
     check_close("o (one call)", o1, o_r, dt)
 
 
+def test_step_api_carry_with_bias(gpu):
+    """Ring steps with a bias: each step gets the slice of the bias for its key block
+    (a strided view), and the carried result equals one call with the whole bias, and
+    the oracle (full [B, Hq, Sq, Skv] bias with -inf entries)."""
+    B, S, Hq, Hkv, D = 1, 512, 4, 2, 128
+    t = torch.bfloat16
+    q, k, v = rnd((B, S, Hq, D), 21, t), rnd((B, 2 * S, Hkv, D), 22, t), rnd((B, 2 * S, Hkv, D), 23, t)
+    bias = 2.0 * workloads.random_tensor((B, Hq, S, 2 * S), 24, dtype=torch.float32)
+    bias[workloads.random_tensor((B, Hq, S, 2 * S), 25) > 1.5] = float("-inf")
+    qd, kd, vd, bd = q.to(DEV), k.to(DEV), v.to(DEV), bias.to(DEV)
+    acc, m, l = gpu.attn_fwd(qd, kd[:, S:].contiguous(), vd[:, S:].contiguous(), causal=True,
+                             q_pos0=S, kv_pos0=S, finalize=False, bias=bd[..., S:])
+    o, m, l = gpu.attn_fwd(qd, kd[:, :S].contiguous(), vd[:, :S].contiguous(), causal=True,
+                           q_pos0=S, kv_pos0=0, carry_in=True, m=m, l=l, acc=acc, bias=bd[..., :S])
+    o1, m1, l1 = gpu.attn_fwd(qd, kd, vd, causal=True, q_pos0=S, kv_pos0=0, bias=bd)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=True, q_pos0=S, kv_pos0=0, bias=bias)
+    check_close("o (two steps)", o, o_r, "bf16")
+    check_stats(m, l, m_r, l_r, "bf16")
+    check_close("o (one call)", o1, o_r, "bf16")
+    check_stats(m1, l1, m_r, l_r, "bf16")
+
+
+def test_bias_with_learnable_sink(gpu):
+    """Bias and a learnable sink together: the sink joins the denominator of the biased
+    logits; forward, gradients and the sink gradient against the oracle."""
+    B, S, Hq, Hkv, D = 1, 300, 8, 2, 128
+    t = torch.bfloat16
+    q, k, v, do = (rnd((B, S, Hq, D), 31, t), rnd((B, S, Hkv, D), 32, t), rnd((B, S, Hkv, D), 33, t),
+                   rnd((B, S, Hq, D), 34, t))
+    z = 1.5 * rnd((Hq,), 35, torch.float32)
+    bias = make_bias("keypad", "b11j", B, Hq, S, 36)
+    kw = dict(causal=True, softmax_type="learnable", sink=z.to(DEV), bias=bias.to(DEV))
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **kw)
+    dq, dk, dv, dz = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **kw)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=True, sink=z, bias=bias)
+    check_close("o", o, o_r, "bf16")
+    check_stats(m, l, m_r, l_r, "bf16")
+    dq_r, dk_r, dv_r, dz_r = dense.backward(q, k, v, do, causal=True, sink=z, bias=bias)
+    check_close("dq", dq, dq_r, "bf16")
+    check_close("dk", dk, dk_r, "bf16")
+    check_close("dv", dv, dv_r, "bf16")
+    np.testing.assert_allclose(dz.cpu().numpy(), dz_r, atol=2e-2, rtol=2e-2)
+
+
 def test_step_api_carry_mla(gpu):
     """The ring step API with a value head dim of its own: the carry acc has Dv columns."""
     B, S, Hq, Hkv, D, Dv = 1, 384, 4, 1, 128, 64
