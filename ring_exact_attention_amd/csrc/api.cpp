@@ -501,7 +501,10 @@ size_t block_select_workspace_bytes(const select_params* p_in) {
     return 0;
   const size_t nblk = (size_t)(select_kv_rows(p) / p->block_size);
   const size_t n = (size_t)p->batch * nblk * p->embed * sizeof(double);
-  return align_up(n > 0 ? n : 1);
+  // block means, then (split selection) the partial top-n lists
+  const int ns = rea::select_splits(p->batch, p->seqlen, p->q_pos0, p->block_size, (int)nblk, p->top_n);
+  const size_t parts = ns > 1 ? (size_t)p->batch * p->seqlen * ns * p->top_n : 0;
+  return align_up(n > 0 ? n : 1) + (parts ? align_up(parts * sizeof(double)) + align_up(parts * sizeof(int32_t)) : 0);
 }
 
 int block_select(const select_params* p_in, const void* q, const void* k, int32_t* idx, void* workspace,
@@ -548,6 +551,13 @@ int block_select(const select_params* p_in, const void* q, const void* k, int32_
   a.bs = p->block_size;
   a.top_n = p->top_n;
   a.nblk = skv / p->block_size;
+  a.nsplit = rea::select_splits(a.B, a.S, a.q_pos0, a.bs, a.nblk, a.top_n);
+  if (a.nsplit > 1) {
+    const size_t nm = (size_t)a.B * a.nblk * a.E * sizeof(double);
+    const size_t parts = (size_t)a.B * a.S * a.nsplit * a.top_n;
+    a.part_s = (double*)((char*)workspace + align_up(nm > 0 ? nm : 1));
+    a.part_c = (int32_t*)((char*)a.part_s + align_up(parts * sizeof(double)));
+  }
   return hip_status(rea::launch_select(a, (hipStream_t)stream));
 }
 

@@ -106,6 +106,9 @@ struct SelectArgs {
   double* means;      // [B, nblk, E] workspace
   int B, S, E, bs, top_n, nblk;   // S: query rows; nblk = Skv / bs full key blocks
   int Skv, q_pos0;    // key rows; position of query row 0 in the key sequence
+  int nsplit;         // workgroups per query block, each over a share of the candidates
+  double* part_s;     // nsplit > 1: [B, S, nsplit, top_n] partial lists (score, index;
+  int32_t* part_c;    //   index -1 = empty), combined by block_select_merge_kernel
 };
 
 struct SparseArgs {

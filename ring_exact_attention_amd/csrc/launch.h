@@ -16,6 +16,22 @@ int bwd_q_tile_rows(int dtype);
 int bwd_k_tile_rows(int dtype);
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+// Workgroups per query block of block_select.  While the grid would have fewer than 256
+// workgroups (a few tokens, e.g. decoding), each query block's chunks of 64 candidate
+// blocks are shared out over several workgroups whose top-n lists a merge kernel
+// combines (at most 64 list entries per token).
+inline int select_splits(int B, int S, int q_pos0, int bs, int nblk, int top_n) {
+  if (B <= 0 || S <= 0 || bs <= 0 || top_n < 1 || top_n > 16) return 1;
+  const long long nqb = (long long)(q_pos0 + S - 1) / bs - q_pos0 / bs + 1;
+  const long long wg = (long long)B * nqb;
+  if (wg >= 256) return 1;
+  long long ns = 256 / wg;
+  const long long chunks = (nblk + 63) / 64;
+  if (ns > chunks) ns = chunks;
+  if (ns > 64 / top_n) ns = 64 / top_n;
+  return ns < 1 ? 1 : (int)ns;
+}
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
 hipError_t launch_sparse_bwd(const SparseBwdArgs& a, hipStream_t stream);
 

@@ -80,14 +80,18 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
 
   const int first = a.q_pos0 / BS;
   const int nqb = (a.q_pos0 + a.S - 1) / BS - first + 1;
-  const int i = first + blockIdx.x % nqb, b = blockIdx.x / nqb;
+  const int ns = a.nsplit, split = blockIdx.x % ns, qb = blockIdx.x / ns;
+  const int i = first + qb % nqb, b = qb / nqb;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int p0 = max(i * BS, a.q_pos0);                      // first query position of the block
   const int t0 = p0 - a.q_pos0;                               // its query row
   const int ntok = min((i + 1) * BS, a.q_pos0 + a.S) - p0;
   const int ncand = min(i, a.nblk);
+  // this workgroup's share of the candidates: whole chunks [c_begin, c_end)
+  const int nch = (ncand + CH - 1) / CH, cps = (nch + ns - 1) / ns;
+  const int c_begin = min(ncand, split * cps * CH), c_end = min(ncand, (split + 1) * cps * CH);
 
-  if (ncand > 0) {
+  if (c_begin < c_end) {
     const __bf16* qp = (const __bf16*)a.q + ((size_t)b * a.S + t0) * a.E;
     const int pitch = sq_pitch(BS, a.E), cpr = a.E / 8;
     for (int c = tid; c < BS * cpr; c += 256) {
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
 
     const double* mbase = a.means + (size_t)b * a.nblk * a.E;
     const int col = lane & 15, grp = lane >> 4;
-    for (int c0 = 0; c0 < ncand; c0 += CH) {
+    for (int c0 = c_begin; c0 < c_end; c0 += CH) {
       const int cand = min(c0 + 16 * wave + col, ncand - 1);
       const double* mrow = mbase + (size_t)cand * a.E + 4 * grp;
       f64x4 acc[TB];
@@ -138,12 +142,12 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
         for (int r = 0; r < 4; ++r) ssc[16 * x + grp + 4 * r][16 * wave + col] = acc[x][r];
       __syncthreads();
       // Merge the chunk into each token's list.  Before the chunk the list holds
-      // kept0 = min(n, c0) entries.  Lane y carries candidate c0 + y; those not above
+      // kept0 = min(n, c0 - c_begin) entries.  Lane y carries candidate c0 + y; those not above
       // the last entry of a full list cannot place (ties go to the lower index).  A
       // survivor's rank counts the list entries >= it and the survivors above it (or
       // equal with a lower index); list entry e moves down by the survivors above it.
       {
-        const int n = a.top_n, nc = min(CH, ncand - c0), kept0 = min(n, c0);
+        const int n = a.top_n, nc = min(CH, c_end - c0), kept0 = min(n, c0 - c_begin);
         for (int t = wave; t < ntok; t += 4) {
           const bool cval = lane < nc;
           const double v = cval ? ssc[t][lane] : 0.0;
@@ -175,7 +179,15 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
     }
   }
 
-  if (tid < ntok) {
+  if (ns > 1 && tid < ntok) {
+    // a share of the candidates: the list as ranked (index -1 = empty) for the merge
+    const int kept = min(a.top_n, c_end - c_begin);
+    const size_t base = ((size_t)(b * a.S + t0 + tid) * ns + split) * a.top_n;
+    for (int j = 0; j < a.top_n; ++j) {
+      a.part_s[base + j] = j < kept ? best_s[tid][j] : -INFINITY;
+      a.part_c[base + j] = j < kept ? best_c[tid][j] : -1;
+    }
+  } else if (tid < ntok) {
     const int kept = min(a.top_n, ncand);
     // sort the kept indices ascending (insertion sort on <= 16 entries)
     for (int x = 1; x < kept; ++x) {
@@ -193,18 +205,55 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
   }
 }
 
+// Combines the nsplit partial lists of each token (disjoint candidate ranges), one
+// wavefront per token: an entry's rank counts the entries that beat it (a higher score,
+// or an equal one with a lower index -- the order one workgroup's merge keeps); ranks
+// below top_n are kept and written ascending by index after the -1 padding.
+__global__ __launch_bounds__(256) void block_select_merge_kernel(SelectArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long tok = (long long)blockIdx.x * 4 + wave_id();
+  if (tok >= (long long)a.B * a.S) return;               // the whole wavefront
+  const int n = a.top_n, ne = a.nsplit * n;
+  double s = -INFINITY;
+  int c = -1;
+  if (lane < ne) {
+    s = a.part_s[tok * ne + lane];
+    c = a.part_c[tok * ne + lane];
+  }
+  const bool valid = c >= 0;
+  int rank = 0;
+  for (uint64_t m = __ballot(valid); m; m &= m - 1) {
+    const int y = __builtin_ctzll(m);
+    const double w = read_lane_f64(s, y);
+    const int cy = __builtin_amdgcn_readlane(c, y);
+    rank += (w > s || (w == s && cy < c)) ? 1 : 0;
+  }
+  const bool keep = valid && rank < n;
+  const uint64_t K = __ballot(keep);
+  int pos = 0;                                            // among the kept, by index
+  for (uint64_t m = K; m; m &= m - 1) pos += __builtin_amdgcn_readlane(c, __builtin_ctzll(m)) < c ? 1 : 0;
+  int32_t* out = a.idx + tok * n;
+  const int pad = n - __popcll(K);
+  if (keep) out[pad + pos] = c;
+  if (lane < pad) out[lane] = -1;
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (a.nblk > 0)
     hipLaunchKernelGGL(block_means_kernel, dim3((unsigned)(a.B * a.nblk)), dim3(256), 0, stream, a);
   if (a.S == 0) return hipGetLastError();
   const int nqb = (a.q_pos0 + a.S - 1) / a.bs - a.q_pos0 / a.bs + 1;
-  const dim3 grid((unsigned)(a.B * nqb));
+  const dim3 grid((unsigned)(a.B * nqb * a.nsplit));
   const size_t lds = (size_t)a.bs * sq_pitch(a.bs, a.E) * sizeof(__bf16);
   switch (a.bs) {
     case 16: hipLaunchKernelGGL(block_select_kernel<16>, grid, dim3(256), lds, stream, a); break;
     case 32: hipLaunchKernelGGL(block_select_kernel<32>, grid, dim3(256), lds, stream, a); break;
     case 64: hipLaunchKernelGGL(block_select_kernel<64>, grid, dim3(256), lds, stream, a); break;
     default: return hipErrorInvalidValue;
+  }
+  if (a.nsplit > 1) {
+    const long long toks = (long long)a.B * a.S;
+    hipLaunchKernelGGL(block_select_merge_kernel, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }

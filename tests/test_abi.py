@@ -166,6 +166,12 @@ def test_select_decode_checks(lib):
     v1.struct_size = 32                                      # fields past 32 bytes ignored
     assert lib.block_select_workspace_bytes(ctypes.byref(v1)) == 8 * 512 * 8
     assert call(v1) == rea.ATTN_ERR_INVALID_ARG and b"idx is NULL" in lib.attn_last_error()
+    # few query blocks (decoding): the candidates of a block are shared out over
+    # workgroups (here 4: 256 blocks = 4 chunks of 64), whose partial top-n lists
+    # (fp64 score + int32 index per entry) follow the means
+    dec = sp(seqlen=4, seqlen_kv=8192, q_pos0=8188)
+    parts = 1 * 4 * 4 * 8
+    assert lib.block_select_workspace_bytes(ctypes.byref(dec)) == 256 * 512 * 8 + parts * 8 + parts * 4
 
 
 def test_sparse_decode_checks(lib):

@@ -46,6 +46,28 @@ def test_select_exact_ties(gpu):
     np.testing.assert_array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("n", [3, 8, 16])
+def test_select_split_candidates_ties(gpu, n):
+    """Few query blocks against a long cache: each block's candidates are shared out over
+    several workgroups and their lists merged.  Integer-valued inputs with repeated key
+    blocks put exact ties across the shares; the indices must equal the oracle's and the
+    single-workgroup path's (the full-sequence call)."""
+    B, S, E, bs, T, pos0 = 2, 8192, 64, 32, 100, 8000
+    g = torch.Generator().manual_seed(40 + n)
+    k = torch.randint(-2, 3, (B, S, E), generator=g).to(torch.bfloat16)
+    for b in range(B):
+        for c in range(70, S // bs, 67):
+            k[b, c * bs:(c + 1) * bs] = k[b, (c - 69) * bs:(c - 68) * bs]   # block c repeats block c-69
+    q = torch.randint(-2, 3, (B, S, E), generator=g).to(torch.bfloat16)
+    qn = q[:, pos0:pos0 + T].contiguous()
+    idx = gpu.block_select(qn.to(DEV), k.to(DEV), block_size=bs, top_n=n, q_pos0=pos0)
+    idx_full = gpu.block_select(q.to(DEV), k.to(DEV), block_size=bs, top_n=n)
+    torch.cuda.synchronize()
+    ref = select.block_select(qn, k, block_size=bs, top_n=n, q_pos0=pos0)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_full.cpu().numpy()[:, pos0:pos0 + T])
+
+
 def test_select_full_size(gpu):
     w = workloads.WORKLOADS["block_sparse_top8_s8192"]
     q, k, v, _ = workloads.generate(w)
