@@ -253,7 +253,10 @@ size_t attn_bwd_workspace_bytes(const attn_params* params);
  *   idx        [out] int32 [B, Sq, top_n].
  * A block's mean is a function of its rows, so recomputing the means from the key cache
  * at every decoding step equals the page's index that gains one mean per completed block.
- *   workspace  device scratch of at least block_select_workspace_bytes(params) bytes.
+ *   workspace  device scratch of at least block_select_workspace_bytes(params) bytes
+ *              (256-byte aligned; contents overwritten): the fp64 block means and, when
+ *              only a few query blocks are selected for (decoding), the partial top-n
+ *              lists of the workgroups that share a block's candidates.
  */
 int block_select(const select_params* params, const void* q, const void* k, int32_t* idx,
                  void* workspace, size_t workspace_bytes, void* stream);
