@@ -213,10 +213,14 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
         qn = qd[:, S - T:].contiguous()
         idn = torch.empty((B, T, w.top_n), dtype=torch.int32, device=dev)
         on = torch.empty_like(qn)
+        wsd = torch.empty(max(rea.fwd_sparse_workspace_bytes(B, T, top_n=w.top_n, window=w.sparse_window,
+                                                             block_size=w.block_size, seqlen_kv=S,
+                                                             q_pos0=S - T), 256), dtype=torch.uint8, device=dev)
         dsegs = [("decode_select", lambda: rea.block_select(qn, kd, block_size=w.block_size, top_n=w.top_n,
                                                             out=idn, q_pos0=S - T)),
                  ("decode_attn", lambda: rea.attn_fwd_sparse(qn, kd, vd, idn, window=w.sparse_window,
-                                                             block_size=w.block_size, out=on, q_pos0=S - T))]
+                                                             block_size=w.block_size, out=on, q_pos0=S - T,
+                                                             workspace=wsd))]
         dms, _ = time_segments(torch, dsegs, args.steps, args.warmup, torch.cuda.current_stream(dev))
         step_us = (dms["decode_select"] + dms["decode_attn"]) * 1e3
         kernels["decode_step"] = {"new_tokens_per_sequence": T, "cache_rows": S,

@@ -202,10 +202,17 @@ typedef struct select_params {
  *             With ATTN_NO_FINALIZE the stored (m, l, acc) satisfy
  *             acc_i = sum_j exp(s_ij - m_i) v_j over all blocks seen so far.
  * In sparse mode (sel_idx != NULL) m and l hold the max logit and the softmax sum
- * over the token's slots.
+ * over the token's slots, and acc is NULL or the workspace of attn_fwd_workspace_bytes.
  */
 int attn_fwd(const attn_params* params, const void* q, const void* k, const void* v,
              void* o, float* m, float* l, float* acc, void* stream);
+
+/* Bytes of optional device workspace the sparse forward (params->sel_idx != NULL) can
+ * use, passed as attn_fwd's acc argument (256-byte aligned, contents overwritten): with
+ * it, a call with few tokens (decoding) shares each token group's 32-row steps out over
+ * several workgroups and combines their partial results; acc = NULL runs without the
+ * split.  0 when the call would not split, for dense params, and for invalid params. */
+size_t attn_fwd_workspace_bytes(const attn_params* params);
 
 /*
  * attn_bwd -- gradients of attn_fwd's output, recomputing the probabilities from the

@@ -96,6 +96,7 @@ _SIGNATURES = {
     "attn_bwd": (ctypes.c_int, [ctypes.POINTER(AttnParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P, ctypes.c_size_t, _P]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AttnParams)]),
+    "attn_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AttnParams)]),
     "block_select": (ctypes.c_int, [ctypes.POINTER(SelectParams), _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "block_select_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SelectParams)]),
     "attn_last_error": (ctypes.c_char_p, []),
@@ -327,10 +328,13 @@ def block_select(q, k, *, block_size=32, top_n=8, workspace=None, out=None, q_po
     return idx
 
 
-def attn_fwd_sparse(q, k, v, idx, *, window=32, block_size=32, scale=None, out=None, q_pos0=0):
+def attn_fwd_sparse(q, k, v, idx, *, window=32, block_size=32, scale=None, out=None, q_pos0=0,
+                    workspace=None):
     """Attention of every token over its zero-padded window ++ selected blocks.  Query row r
     sits at position q_pos0 + r of the key / value sequence (decoding: new tokens against
-    the cache, with idx from block_select(..., q_pos0=q_pos0))."""
+    the cache, with idx from block_select(..., q_pos0=q_pos0)).  ``workspace``: a uint8
+    device tensor of at least attn_fwd_workspace_bytes (allocated here when None and the
+    call would use it), or False to run without the split over steps."""
     q, k, v = _joint(q), _joint(k), _joint(v)
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16, q.device)
@@ -355,9 +359,30 @@ def attn_fwd_sparse(q, k, v, idx, *, window=32, block_size=32, scale=None, out=N
     o = out if out is not None else torch.empty_like(q)
     m = torch.empty((B, S), dtype=torch.float32, device=q.device)
     l = torch.empty((B, S), dtype=torch.float32, device=q.device)
-    _check(lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l), None,
+    need = int(lib().attn_fwd_workspace_bytes(ctypes.byref(p))) if workspace is not False else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if need and (workspace.numel() * workspace.element_size() < need or workspace.device != q.device):
+        raise ValueError(f"workspace of {need} bytes on q's device needed")
+    ws = _ptr(workspace) if need else None
+    _check(lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l), ws,
                           _stream(q)))
     return o, m, l
+
+
+def fwd_sparse_workspace_bytes(B, S, *, top_n, window=32, block_size=32, seqlen_kv=None, q_pos0=0):
+    """attn_fwd_workspace_bytes for a sparse forward of B x S query rows (embed 512)."""
+    p = AttnParams()
+    p.struct_size = ctypes.sizeof(AttnParams)
+    p.dtype = ATTN_BF16
+    p.batch, p.seqlen_q = int(B), int(S)
+    p.seqlen_kv = int(seqlen_kv if seqlen_kv is not None else S)
+    p.q_pos0 = int(q_pos0)
+    p.num_q_heads = p.num_kv_heads = 1
+    p.head_dim = 512
+    p.sel_idx = 1
+    p.top_n, p.sel_block, p.sparse_window = int(top_n), int(block_size), int(window)
+    return int(lib().attn_fwd_workspace_bytes(ctypes.byref(p)))
 
 
 def attn_bwd_sparse(q, k, v, idx, o, dout, m, l, *, window=32, block_size=32, scale=None,

@@ -235,7 +235,7 @@ int check_sparse(const attn_params* p) {
 
 // Gathered block-sparse forward (sel_idx != NULL).
 int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o, float* m,
-               float* l, void* stream) {
+               float* l, float* work, void* stream) {
   int st0 = check_sparse(p);
   if (st0) return st0;
   if (p->batch == 0 || p->seqlen_q == 0) return ok();
@@ -243,7 +243,10 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")) || (st = check_ptr(m, "m")) || (st = check_ptr(l, "l")))
     return st;
+  if (work && ((uintptr_t)work & (kAlign - 1)) != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "the sparse forward's workspace (acc) must be 256-byte aligned");
   rea::SparseArgs a{};
+  a.part = work;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -329,7 +332,7 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
              float* l, float* acc, void* stream) {
   attn_params tmp;
   const attn_params* p = current_layout(p_in, tmp);
-  if (p && p->sel_idx) return sparse_fwd(p, q, k, v, o, m, l, stream);
+  if (p && p->sel_idx) return sparse_fwd(p, q, k, v, o, m, l, acc, stream);
   Problem r;
   int st = check_dense(p, false, r);
   if (st) return st;
@@ -379,6 +382,19 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
   if ((long long)a.n_qtiles * r.B * r.Hq >= (1LL << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
   return hip_status(rea::launch_fwd(r.dtype, a, (hipStream_t)stream));
+}
+
+size_t attn_fwd_workspace_bytes(const attn_params* p_in) {
+  attn_params tmp;
+  const attn_params* p = current_layout(p_in, tmp);
+  if (!p || !p->sel_idx) return 0;
+  const std::string saved = g_err;
+  if (check_sparse(p) != ATTN_OK) return 0;
+  g_err = saved;
+  int tpw = 0, ks = 1;
+  rea::sparse_plan(p->batch, p->seqlen_q, p->sparse_window, p->sel_block, p->top_n, true, tpw, ks);
+  if (ks <= 1) return 0;
+  return align_up((size_t)p->batch * p->seqlen_q * ks * (512 + 4) * sizeof(float));
 }
 
 size_t attn_bwd_workspace_bytes(const attn_params* p_in) {

@@ -123,6 +123,8 @@ struct SparseArgs {
   float scale_log2, scale;
   int Skv, q_pos0;    // key / value rows; position of query row 0 among them
   int tpw;            // tokens per workgroup (power of two <= 32; set by the launcher)
+  int ksplit;         // workgroups per token group, each over a share of its 32-row steps
+  float* part;        // ksplit > 1: [B, S, ksplit, 512 + 4] partial numerator, max, sum, pad
 };
 
 // Backward of the gathered block-sparse attention.

@@ -17,6 +17,24 @@ int bwd_k_tile_rows(int dtype);
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
+// Work split of the gathered sparse forward: tokens per workgroup (32, halved while the
+// grid would have fewer than 512 workgroups, down to 1) and, when the grid is still
+// below 256 workgroups and a workspace is given, workgroups per token group over the
+// group's 32-row steps (window blocks, then the union of selected blocks).
+inline void sparse_plan(int B, int S, int window, int sel_block, int top_n, bool workspace, int& tpw,
+                        int& ksplit) {
+  tpw = 32;
+  while (tpw > 1 && (long long)B * ((S + tpw - 1) / tpw) < 512) tpw >>= 1;
+  ksplit = 1;
+  const long long wg = (long long)B * ((S + tpw - 1) / tpw);
+  if (!workspace || wg <= 0 || wg >= 256) return;
+  const long long nwin = (window + tpw - 1 + 31) / 32, nsub = (sel_block + 31) / 32;
+  const long long ent = (long long)tpw * top_n < 512 ? (long long)tpw * top_n : 512;
+  long long ks = 256 / wg;
+  if (ks > nwin + ent * nsub) ks = nwin + ent * nsub;
+  ksplit = ks < 1 ? 1 : (int)ks;
+}
+
 // Workgroups per query block of block_select.  While the grid would have fewer than 256
 // workgroups (a few tokens, e.g. decoding), each query block's chunks of 64 candidate
 // blocks are shared out over several workgroups whose top-n lists a merge kernel

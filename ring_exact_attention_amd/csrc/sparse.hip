@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int nqb = (a.S + a.tpw - 1) / a.tpw;
-  const int b = blockIdx.x / nqb, t0 = (blockIdx.x % nqb) * a.tpw;
+  const int split = blockIdx.x % a.ksplit, grp_id = blockIdx.x / a.ksplit;
+  const int b = grp_id / nqb, t0 = (grp_id % nqb) * a.tpw;
   const int tend = min(t0 + a.tpw, a.S);                      // this workgroup's tokens: [t0, tend)
   const int n = a.top_n, bs = a.sel_block, W = a.window;
 
@@ -48,6 +49,9 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const int nwin = (W + a.tpw - 1 + 31) / 32;
   const int nsub = (bs + 31) / 32;
   const int nsteps = nwin + nu * nsub;
+  // this workgroup's share of the steps (all of them unless split)
+  const int sps = (nsteps + a.ksplit - 1) / a.ksplit;
+  const int s_begin = min(nsteps, split * sps), s_end = min(nsteps, s_begin + sps);
   // Query row r sits at position q_pos0 + r of the key / value sequence (Skv rows): the
   // whole sequence when q_pos0 = 0 and Skv = S, or a few new tokens against a cache.
   const int wstart = a.q_pos0 + t0 - W + 1;
@@ -101,8 +105,8 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const int tg = lane >> 4, tj = lane & 15;
   const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * kUPITCH + 16 * (tg & 1) + 4 * (tj & 3);
 
-  if (nsteps > 0) load_step(0);
-  for (int step = 0; step < nsteps; ++step) {
+  if (s_begin < s_end) load_step(s_begin);
+  for (int step = s_begin; step < s_end; ++step) {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
       *(u32x4*)&sV[wave][r * kUPITCH + 8 * ch] = vbuf[u];
     }
     __syncthreads();
-    if (step + 1 < nsteps) load_step(step + 1);              // registers are free again
+    if (step + 1 < s_end) load_step(step + 1);               // registers are free again
 
     // full scores (sum of the four embedding slices), identical in every wave
 #pragma unroll
@@ -195,6 +199,26 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
 
   const float l_used = l_part + other_half(l_part);
   const float corr = (m_true == -INFINITY) ? 0.f : fast_exp2(m_used - m_true);
+  if (a.ksplit > 1) {
+    // partial result of this share, relative to its exact max: numerator, max, sum
+    if (tok_ok) {
+      float* pp = a.part + (((size_t)b * a.S + tok) * a.ksplit + split) * (kSpE + 4);
+#pragma unroll
+      for (int db = 0; db < kUDW / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * g + e] * corr;
+          *(f32x4*)(pp + e0 + 32 * db + 8 * g + 4 * lh) = w;
+        }
+      if (wave == 0 && lh == 0) {
+        pp[kSpE] = m_true;
+        pp[kSpE + 1] = l_used * corr;
+      }
+    }
+    return;
+  }
   if (tok_ok) {
     const float inv = l_used > 0.f ? 1.f / l_used : 0.f;
     __bf16* op = (__bf16*)a.o + bbase + (size_t)tok * kSpE + e0;
@@ -215,14 +239,38 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   }
 }
 
+// Combines the ksplit partial results of each token (one workgroup per token, two
+// embedding columns per thread): O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s; a token whose shares saw nothing keeps O = 0, m = -inf, l = 0.
+__global__ __launch_bounds__(256) void sparse_combine_kernel(SparseArgs a) {
+  const size_t tok = blockIdx.x;                               // b * S + token
+  const float* pp = a.part + tok * a.ksplit * (kSpE + 4);
+  float M = -INFINITY;
+  for (int s = 0; s < a.ksplit; ++s) M = fmaxf(M, pp[s * (kSpE + 4) + kSpE]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  const int e = 2 * threadIdx.x;
+  for (int s = 0; s < a.ksplit; ++s) {
+    const float* ps = pp + s * (kSpE + 4);
+    const float w = ps[kSpE] == -INFINITY ? 0.f : fast_exp2(ps[kSpE] - M);
+    L = fmaf(w, ps[kSpE + 1], L);
+    o0 = fmaf(w, ps[e], o0);
+    o1 = fmaf(w, ps[e + 1], o1);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *(uint32_t*)((__bf16*)a.o + tok * kSpE + e) = pack_bf16x2(o0 * inv, o1 * inv);
+  if (threadIdx.x == 0) {
+    a.m[tok] = M == -INFINITY ? -INFINITY : M * kLn2;
+    a.l[tok] = L;
+  }
+}
+
 hipError_t launch_sparse(const SparseArgs& args, hipStream_t stream) {
-  // Fewer tokens per workgroup while the grid would leave most of the chip idle (few
-  // tokens, e.g. decoding): each workgroup then walks a smaller union of blocks.
   SparseArgs a = args;
-  a.tpw = kUQ;
-  while (a.tpw > 1 && (long long)a.B * ((a.S + a.tpw - 1) / a.tpw) < 512) a.tpw >>= 1;
+  sparse_plan(a.B, a.S, a.window, a.sel_block, a.top_n, a.part != nullptr, a.tpw, a.ksplit);
   const long long nqb = (a.S + a.tpw - 1) / a.tpw;
-  hipLaunchKernelGGL(sparse_union_kernel, dim3((unsigned)(a.B * nqb)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(sparse_union_kernel, dim3((unsigned)(a.B * nqb * a.ksplit)), dim3(256), 0, stream, a);
+  if (a.ksplit > 1)
+    hipLaunchKernelGGL(sparse_combine_kernel, dim3((unsigned)((long long)a.B * a.S)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -23,9 +23,13 @@ __device__ __forceinline__ int build_union(const int32_t* sel, int S, int tend, 
                                            int* scratch, uint32_t (*ucnt)[kUQ / 4], int* ublk, int* s_nu) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int ne = kUQ * n;
+  // entries sorted: the group's tokens x n, rounded up to a power of two (>= 64)
+  const int cnt = max(0, min(kUQ, tend - t0));
+  int SZ = 64;
+  while (SZ < cnt * n) SZ <<= 1;
   int* skey = scratch;
   int* stok = skey + kUMaxEnt;
-  for (int k = tid; k < kUMaxEnt; k += 256) {
+  for (int k = tid; k < SZ; k += 256) {
     int key = kUSentinel, tok = 0;
     if (k < ne) {
       const int t = k / n, j = k % n;
@@ -39,9 +43,9 @@ __device__ __forceinline__ int build_union(const int32_t* sel, int S, int tend, 
     stok[k] = tok;
   }
   __syncthreads();
-  for (int size = 2; size <= kUMaxEnt; size <<= 1) {          // bitonic sort by key
+  for (int size = 2; size <= SZ; size <<= 1) {                // bitonic sort by key
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int k = tid; k < kUMaxEnt / 2; k += 256) {
+      for (int k = tid; k < SZ / 2; k += 256) {
         const int lo = 2 * k - (k & (stride - 1)), hi = lo + stride;
         const bool up = (lo & size) == 0;
         const int ka = skey[lo], kb = skey[hi];
@@ -59,7 +63,7 @@ __device__ __forceinline__ int build_union(const int32_t* sel, int S, int tend, 
   if (wave == 0) {                                             // union index of each entry
     int* suid = stok + kUMaxEnt;
     int running = 0;
-    for (int c0 = 0; c0 < kUMaxEnt; c0 += 64) {
+    for (int c0 = 0; c0 < SZ; c0 += 64) {
       const int k = c0 + lane;
       const int key = skey[k];
       const bool first = key != kUSentinel && (k == 0 || skey[k - 1] != key);
@@ -71,11 +75,11 @@ __device__ __forceinline__ int build_union(const int32_t* sel, int S, int tend, 
     }
     if (lane == 0) *s_nu = running;
   }
-  for (int k = tid; k < kUMaxEnt * (kUQ / 4); k += 256) ((uint32_t*)ucnt)[k] = 0u;
+  for (int k = tid; k < SZ * (kUQ / 4); k += 256) ((uint32_t*)ucnt)[k] = 0u;
   __syncthreads();
   {
     const int* suid = stok + kUMaxEnt;
-    for (int k = tid; k < kUMaxEnt; k += 256)
+    for (int k = tid; k < SZ; k += 256)
       if (skey[k] != kUSentinel) atomicAdd(&ucnt[suid[k]][stok[k] >> 2], 1u << (8 * (stok[k] & 3)));
   }
   __syncthreads();

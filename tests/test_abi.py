@@ -174,6 +174,24 @@ def test_select_decode_checks(lib):
     assert lib.block_select_workspace_bytes(ctypes.byref(dec)) == 256 * 512 * 8 + parts * 8 + parts * 4
 
 
+def test_sparse_forward_workspace(lib):
+    """attn_fwd_workspace_bytes: 0 for dense params and for sparse calls with a full grid;
+    the per-token partial results (512 + 4 floats per share) when decoding."""
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(params())) == 0
+    p = params(num_q_heads=1, num_kv_heads=1, head_dim=512, seqlen_q=16, seqlen_kv=8192, causal=0, q_pos0=8176,
+               batch=4)
+    p.sel_idx = 0x1000
+    p.top_n, p.sel_block, p.sparse_window = 8, 32, 32
+    # one token per workgroup (64 groups), 4 shares of at most 1 + 8 steps
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(p)) == 4 * 16 * 4 * 516 * 4
+    full = params(num_q_heads=1, num_kv_heads=1, head_dim=512, seqlen_q=8192, seqlen_kv=8192, causal=0, batch=4)
+    full.sel_idx = 0x1000
+    full.top_n, full.sel_block, full.sparse_window = 8, 32, 32
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(full)) == 0
+    p.top_n = 0                                              # invalid: 0
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(p)) == 0
+
+
 def test_sparse_decode_checks(lib):
     d = ctypes.c_void_p(0x1000)
     p = params(num_q_heads=1, num_kv_heads=1, head_dim=512, seqlen_q=2, seqlen_kv=64, causal=0, q_pos0=62)

@@ -261,6 +261,29 @@ def test_decode_against_cache(gpu, S, T, pos0):
     np.testing.assert_allclose(l.cpu().numpy(), l_r, rtol=1e-3, atol=0)
 
 
+@pytest.mark.parametrize("B,T,pos0", [(2, 1, 999), (1, 5, 700), (3, 2, 64)])
+def test_decode_split_over_steps(gpu, B, T, pos0):
+    """Decoding with the workspace: each token's steps are shared out over several
+    workgroups and combined; equal (within rounding) to the unsplit call and to the
+    oracle."""
+    S, E, bs, n, W = 1000, 512, 32, 8, 32
+    q, k, v = rnd((B, S, E), 90 + T), rnd((B, S, E), 91 + T), rnd((B, S, E), 92 + T)
+    qn = q[:, pos0:pos0 + T].contiguous()
+    qd, kd, vd = qn.to(DEV), k.to(DEV), v.to(DEV)
+    assert gpu.fwd_sparse_workspace_bytes(B, T, top_n=n, seqlen_kv=S, q_pos0=pos0) > 0
+    idx = gpu.block_select(qd, kd, block_size=bs, top_n=n, q_pos0=pos0)
+    o, m, l = gpu.attn_fwd_sparse(qd, kd, vd, idx, window=W, block_size=bs, q_pos0=pos0)
+    o1, m1, l1 = gpu.attn_fwd_sparse(qd, kd, vd, idx, window=W, block_size=bs, q_pos0=pos0, workspace=False)
+    torch.cuda.synchronize()
+    sel = idx.cpu().numpy()
+    o_r, m_r, l_r = sparse.sparse_attention(qn, k, v, sel, window=W, block_size=bs, q_pos0=pos0)
+    check_close("o (split)", o, o_r, "bf16")
+    check_close("o (unsplit)", o1, o_r, "bf16")
+    np.testing.assert_allclose(m.cpu().numpy(), m_r, atol=1e-3, rtol=0)
+    np.testing.assert_allclose(l.cpu().numpy(), l_r, rtol=1e-3, atol=0)
+    np.testing.assert_allclose(m.cpu().numpy(), m1.cpu().numpy(), atol=1e-5, rtol=0)
+
+
 def test_decode_full_size_cache(gpu):
     """One new token per sequence at the end of the full workload's 8192-row cache."""
     w = workloads.WORKLOADS["block_sparse_top8_s8192"]
