@@ -37,6 +37,13 @@ chunk, ``_chunk_attention_bias``; the page returns no gradient for it): s_ij gai
 bias[b, h, i, j] (natural units) before the mask and the softmax.  A bias of -inf removes
 a pair like the mask does.
 
+Dropout ("bpt.py": ``_blockwise_attention_fwd`` / ``_blockwise_attention_bwd`` draw a
+Bernoulli(attn_pdrop) array over (batch, heads, q_len, kv_len) and
+``_chunk_attention_bias`` adds it times the dtype's most negative value to the logits):
+a dropped pair leaves the softmax like a masked one, and the other weights are not
+rescaled.  The array is an input here (the page draws it from a JAX key; any source of
+the same Bernoulli draws will do), True = dropped, broadcastable like the bias.
+
 Sink softmax ("JAX: Single-GPU Attention with TransformerEngine", "Other attention
 knobs": ``softmax_type="off_by_one"`` or ``"learnable"``; the page names the options only,
 so this is the plain reading of their names): every row's softmax gets one more term in
@@ -155,8 +162,18 @@ def _bias_rows(bias, b, h, rows, c0, c1):
     return r[:, c0:c1] if r.shape[1] > 1 else r
 
 
+def _drop_rows(drop, b, h, rows, Skv):
+    """Dropped pairs drop[b, h, rows, :] of a broadcastable boolean array, or none."""
+    if drop is None:
+        return np.zeros((len(rows), Skv), dtype=bool)
+    dd = drop[min(b, drop.shape[0] - 1), min(h, drop.shape[1] - 1)]
+    r = dd[rows] if dd.shape[0] > 1 else dd[np.zeros_like(rows)]
+    return np.broadcast_to(r, (len(rows), Skv))
+
+
 def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0,
-            kv_pos0: int = 0, rows=None, heads=None, row_block: int = 256, sink=None, bias=None):
+            kv_pos0: int = 0, rows=None, heads=None, row_block: int = 256, sink=None, bias=None,
+            dropout=None):
     """Attention forward from the definition.
 
     q: [B, Sq, Hq, D]; k: [B, Skv, Hkv, D]; v: [B, Skv, Hkv, Dv] (torch or numpy, any
@@ -165,6 +182,7 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
     evaluation to sampled query rows / q heads; entries not evaluated are NaN.  ``sink``:
     None, or the sink logits z [Hq] (zeros for "off_by_one"); m and l exclude the sink.
     ``bias``: None, or an additive logit bias broadcastable to [B, Hq, Sq, Skv].
+    ``dropout``: None, or a boolean array broadcastable to [B, Hq, Sq, Skv], True = dropped.
     """
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     B, Sq, Hq, D = q.shape
@@ -175,6 +193,7 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
     wl, wr = window
     z = _sink_logits(sink, Hq)
     bias = None if bias is None else as_f64(bias)
+    drop = None if dropout is None else np.asarray(dropout, dtype=bool)
     fill = np.nan if (rows is not None or heads is not None) else 0.0
     o = np.full((B, Sq, Hq, v.shape[3]), fill)
     m = np.full((B, Hq, Sq), np.nan if fill != 0.0 else -np.inf)
@@ -190,6 +209,7 @@ def forward(q, k, v, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int =
                 vis = visible(q_pos0 + r, kpos, causal, wl, wr)
                 if bias is not None:
                     vis = vis & (_bias_rows(bias, b, hq, r, 0, Skv) > -np.inf)
+                vis = vis & ~_drop_rows(drop, b, hq, r, Skv)
                 rng = _visible_range(vis)
                 if rng is None:
                     o[b, r, hq] = 0.0
@@ -224,7 +244,8 @@ def probs(q, k, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0, k
 
 
 def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: int = 0,
-             kv_pos0: int = 0, row_block: int = 256, heads=None, batches=None, sink=None, bias=None):
+             kv_pos0: int = 0, row_block: int = 256, heads=None, batches=None, sink=None, bias=None,
+             dropout=None):
     """Analytic gradient of ``forward`` contracted with dO.
 
     Returns (dq [B, Sq, Hq, D], dk [B, Skv, Hkv, D], dv [B, Skv, Hkv, Dv]) in fp64.
@@ -243,6 +264,7 @@ def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: 
     z = _sink_logits(sink, Hq)
     dz = np.zeros(Hq)
     bias = None if bias is None else as_f64(bias)
+    drop = None if dropout is None else np.asarray(dropout, dtype=bool)
     partial = heads is not None or batches is not None
     dq = np.full_like(q, np.nan) if partial else np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -258,6 +280,7 @@ def backward(q, k, v, do, *, causal: bool, window=(-1, -1), scale=None, q_pos0: 
                 vis = visible(q_pos0 + r, kpos, causal, wl, wr)
                 if bias is not None:
                     vis = vis & (_bias_rows(bias, b, hq, r, 0, Skv) > -np.inf)
+                vis = vis & ~_drop_rows(drop, b, hq, r, Skv)
                 rng = _visible_range(vis)
                 if rng is None:
                     continue

@@ -15,6 +15,7 @@ import test_oracle_dense as td
 import test_oracle_select_sparse as ts
 import test_oracle_sink as tk
 import test_oracle_bias as tbias
+import test_oracle_dropout as tdrop
 
 
 def _mut_gqa_modulo(monkeypatch):
@@ -114,6 +115,19 @@ def _mut_bias_scaled_with_logits(monkeypatch):
     monkeypatch.setattr(dense, "_bias_rows", lambda *a: orig(*a) / np.sqrt(8.0))
 
 
+def _mut_dropout_ignored(monkeypatch):
+    """The dropout array is read but never applied."""
+    orig = dense._drop_rows
+    monkeypatch.setattr(dense, "_drop_rows", lambda drop, b, h, rows, Skv: orig(None, b, h, rows, Skv))
+
+
+def _mut_dropout_inverted(monkeypatch):
+    """True read as kept instead of dropped."""
+    orig = dense._drop_rows
+    monkeypatch.setattr(dense, "_drop_rows", lambda drop, b, h, rows, Skv:
+                        ~orig(drop, b, h, rows, Skv) if drop is not None else orig(drop, b, h, rows, Skv))
+
+
 MUTATIONS = [
     (_mut_gqa_modulo, lambda: td.test_forward_matches_torch_sdpa(td.CASES[0])),
     (_mut_drop_scale, lambda: td.test_forward_matches_torch_sdpa(td.CASES[1])),
@@ -128,6 +142,8 @@ MUTATIONS = [
     (_mut_clamp_to_last, ts.test_sparse_zero_keys_closed_form),
     (_mut_sink_sign, tk.test_sink_with_zero_left_window_closed_form),
     (_mut_bias_scaled_with_logits, lambda: tbias.test_bias_matches_torch_sdpa_and_autograd((2, 4, 19, 19), True, (-1, -1))),
+    (_mut_dropout_ignored, lambda: tdrop.test_dropout_matches_torch_sdpa_and_autograd((2, 4, 19, 19), True, (-1, -1))),
+    (_mut_dropout_inverted, lambda: tdrop.test_dropout_matches_torch_sdpa_and_autograd((2, 4, 19, 19), True, (-1, -1))),
     (_mut_clamped_slots_pass_no_gradient, lambda: ts.test_sparse_backward_matches_autograd_of_materialised_list(8, 3)),
     (_mut_sink_in_log2_units, lambda: tk.test_sink_forward_and_backward_match_torch(True, (-1, -1), 2, 8)),
 ]
