@@ -269,6 +269,9 @@ def main():
     ap.add_argument("--bias", default="none", choices=["none", "keypad", "shared"],
                     help="additive logit bias: keypad = [B,1,1,S] with the last S/16 keys at -inf, "
                          "shared = one random [1,1,S,S] fp32 matrix")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability: a seeded Bernoulli array [1, Hq, S, S], packed, "
+                         "removes the dropped pairs from the softmax")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -311,6 +314,13 @@ def main():
         kw.update(bias=bias)
     elif args.bias == "shared":
         kw.update(bias=workloads.random_tensor((1, 1, S, S), w.seed + 101).to(dev))
+    if args.dropout > 0.0:
+        # drawn on the GPU head by head (the [S, S] draws of all heads would be large)
+        g = torch.Generator(device=dev).manual_seed(w.seed + 102)
+        words = torch.empty((1, Hq, S, (S + 31) // 32), dtype=torch.int32, device=dev)
+        for h in range(Hq):
+            words[0, h] = workloads.pack_bits(torch.rand((S, S), generator=g, device=dev) < args.dropout)
+        kw.update(dropout=words)
     o = torch.empty((B, S, Hq, Dv), dtype=qd.dtype, device=dev)
     m = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     l = torch.empty_like(m)
@@ -363,7 +373,8 @@ def main():
     bwd_tflops = f_bwd / (bwd_ms * 1e-3) / 1e12 if w.backward else None
 
     label = (w.name + ("" if args.softmax == "vanilla" else f"+{args.softmax}_sink")
-             + ("" if args.bias == "none" else f"+{args.bias}_bias"))
+             + ("" if args.bias == "none" else f"+{args.bias}_bias")
+             + ("" if args.dropout <= 0.0 else f"+dropout{args.dropout:g}"))
     dom = max(seg_ms, key=seg_ms.get)
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(alg[dom] / (seg_ms[dom] * 1e-3) / 1e12, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -90,12 +90,13 @@ enum {
   ATTN_SOFTMAX_LEARNABLE = 2
 };
 
-/* 2: softmax_type, sink, dsink appended; 3: bias, bias_stride appended.  Structs of the
- * earlier sizes are still accepted: the missing fields read as zero (ATTN_SOFTMAX_VANILLA,
- * no bias). */
-#define ATTN_PARAMS_VERSION 3u
+/* 2: softmax_type, sink, dsink appended; 3: bias, bias_stride appended; 4: drop_mask,
+ * drop_stride appended.  Structs of the earlier sizes are still accepted: the missing
+ * fields read as zero (ATTN_SOFTMAX_VANILLA, no bias, no dropout). */
+#define ATTN_PARAMS_VERSION 4u
 #define ATTN_PARAMS_V1_SIZE 104u
 #define ATTN_PARAMS_V2_SIZE 128u
+#define ATTN_PARAMS_V3_SIZE 168u
 
 typedef struct attn_params {
   uint32_t struct_size;        /* = sizeof(attn_params); versioning of the ABI        */
@@ -159,6 +160,16 @@ typedef struct attn_params {
    * Dense mode only.                                                                   */
   const float* bias;
   int64_t bias_stride[4];
+  /* Dropout ("bpt.py": _blockwise_attention_fwd / _bwd draw a Bernoulli(attn_pdrop) array
+   * over (batch, heads, q_len, kv_len) that _chunk_attention_bias adds to the logits times
+   * the dtype's most negative value): a dropped pair leaves the softmax like a masked one
+   * and the others are not rescaled.  The caller draws the array and passes it packed:
+   * pair (i, j) of (b, hq) -- this call's query row i and key row j -- is dropped iff
+   * bit j % 32 of word drop_mask[b*d0 + hq*d1 + i*d2 + j/32] is set, d = drop_stride
+   * (32-bit words, >= 0; 0 broadcasts that dimension).  The same array must be given to
+   * attn_fwd and attn_bwd.  NULL = no dropout.  Dense mode only.                         */
+  const uint32_t* drop_mask;
+  int64_t drop_stride[3];
 } attn_params;
 
 /* 2: seqlen_kv and q_pos0 appended (a version-1 struct of SELECT_PARAMS_V1_SIZE bytes

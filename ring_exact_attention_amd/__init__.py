@@ -64,6 +64,8 @@ class AttnParams(ctypes.Structure):
         ("dsink", ctypes.c_void_p),
         ("bias", ctypes.c_void_p),
         ("bias_stride", ctypes.c_int64 * 4),
+        ("drop_mask", ctypes.c_void_p),
+        ("drop_stride", ctypes.c_int64 * 3),
     ]
 
 
@@ -165,7 +167,7 @@ def _softmax_code(softmax_type, sink):
 
 def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
                 kv_block=0, q_pos0=0, kv_pos0=0, flags=0, head_dim_v=0, softmax_type="vanilla",
-                sink=None, bias=None) -> AttnParams:
+                sink=None, bias=None, dropout=None) -> AttnParams:
     B, Sq, Hq, D = q.shape
     Bk, Skv, Hkv, Dk = k.shape
     if Bk != B or Dk != D:
@@ -192,6 +194,18 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
         p.bias = bias.data_ptr()
         for d in range(4):
             p.bias_stride[d] = view.stride(d) if view.shape[d] > 1 else 0
+    if dropout is not None:
+        # packed dropout bits [B|1, Hq|1, Sq|1, W >= ceil(Skv / 32)] int32 words, bit j % 32 of
+        # word j / 32 = pair (i, j) dropped (workloads.pack_bits builds them)
+        if not isinstance(dropout, torch.Tensor) or dropout.dtype != torch.int32 or dropout.device != q.device:
+            raise TypeError("dropout must be an int32 tensor of packed bits on q's device")
+        W = (Skv + 31) // 32
+        if dropout.dim() != 4 or dropout.shape[3] < W or dropout.stride(3) != 1:
+            raise ValueError(f"dropout must be [B|1, Hq|1, Sq|1, >= {W}] words, contiguous in the last dim")
+        view = dropout.expand(B, Hq, Sq, dropout.shape[3])
+        p.drop_mask = dropout.data_ptr()
+        for d in range(3):
+            p.drop_stride[d] = view.stride(d) if view.shape[d] > 1 else 0
     p.q_pos0, p.kv_pos0 = int(q_pos0), int(kv_pos0)
     p.causal = 1 if causal else 0
     p.window_left, p.window_right = int(window[0]), int(window[1])
@@ -203,7 +217,7 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
 
 def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
              kv_block=0, q_pos0=0, kv_pos0=0, m=None, l=None, acc=None, carry_in=False,
-             finalize=True, out=None, softmax_type="vanilla", sink=None, bias=None):
+             finalize=True, out=None, softmax_type="vanilla", sink=None, bias=None, dropout=None):
     """Forward attention.  q [B, Sq, Hq, D], k [B, Skv, Hkv, D], v [B, Skv, Hkv, Dv] on the GPU
     (Dv = D, or the MLA pair D 128 / Dv 64).
 
@@ -212,6 +226,9 @@ def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     given m, l, acc.  ``softmax_type`` "off_by_one" / "learnable" (with ``sink``, fp32
     [Hq] logits) adds exp(z_h) to each row's denominator when the output is finalised.
     ``bias``: fp32 additive logit bias broadcastable to [B, Hq, Sq, Skv] (-inf masks).
+    ``dropout``: packed int32 dropout bits [B|1, Hq|1, Sq|1, ceil(Skv/32)] (see
+    workloads.pack_bits); a set bit drops the pair from the softmax.  Pass the same
+    tensor to attn_bwd.
     """
     _need(q, "q")
     _need(k, "k", q.dtype, q.device)
@@ -223,7 +240,7 @@ def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     flags = (ATTN_CARRY_IN if carry_in else 0) | (0 if finalize else ATTN_NO_FINALIZE)
     p = make_params(q, k, causal=causal, window=window, scale=scale, query_chunk=query_chunk,
                     key_chunk=key_chunk, kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, flags=flags,
-                    head_dim_v=Dv, softmax_type=softmax_type, sink=sink, bias=bias)
+                    head_dim_v=Dv, softmax_type=softmax_type, sink=sink, bias=bias, dropout=dropout)
     dev = q.device
     if m is None:
         m = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
@@ -256,7 +273,7 @@ def bwd_workspace_bytes(q, k, **kw) -> int:
 def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None, query_chunk=0,
              key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, workspace=None, out=None,
              skip_dq=False, skip_dkdv=False, reuse_stats=False, softmax_type="vanilla", sink=None,
-             dsink=None, bias=None):
+             dsink=None, bias=None, dropout=None):
     """Gradients (dq, dk, dv) of attn_fwd's output for upstream gradient dout.
 
     ``skip_dq`` / ``skip_dkdv`` compute only part of them (the skipped outputs are left
@@ -275,7 +292,7 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
         raise ValueError("v must match k except in its head dim, and o, dout must be [B, Sq, Hq, Dv]")
     kw = dict(causal=causal, window=window, scale=scale, query_chunk=query_chunk, key_chunk=key_chunk,
               kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, head_dim_v=Dv, softmax_type=softmax_type,
-              sink=sink, bias=bias)
+              sink=sink, bias=bias, dropout=dropout)
     flags = ((ATTN_BWD_SKIP_DQ if skip_dq else 0) | (ATTN_BWD_SKIP_DKDV if skip_dkdv else 0) |
              (ATTN_BWD_REUSE_STATS if reuse_stats else 0))
     p = make_params(q, k, flags=flags, **kw)

@@ -54,18 +54,24 @@ struct Problem {
   const float* bias = nullptr;
   long long bias_stride[4] = {0, 0, 0, 0};
   bool bias_vec4 = false;
+  const uint32_t* drop = nullptr;
+  long long drop_stride[3] = {0, 0, 0};
 };
 
 static_assert(offsetof(attn_params, softmax_type) == ATTN_PARAMS_V1_SIZE,
               "a version-1 attn_params is the current one without its softmax fields");
 static_assert(offsetof(attn_params, bias) == ATTN_PARAMS_V2_SIZE,
               "a version-2 attn_params is the current one without its bias fields");
+static_assert(offsetof(attn_params, drop_mask) == ATTN_PARAMS_V3_SIZE,
+              "a version-3 attn_params is the current one without its dropout fields");
 
 // The caller's params in the current layout: an earlier version's struct reads with its
-// missing fields zero (ATTN_SOFTMAX_VANILLA, no bias).  Other sizes pass through for the
+// missing fields zero (ATTN_SOFTMAX_VANILLA, no bias, no dropout).  Other sizes pass through for the
 // size check.
 const attn_params* current_layout(const attn_params* p, attn_params& tmp) {
-  if (!p || (p->struct_size != ATTN_PARAMS_V1_SIZE && p->struct_size != ATTN_PARAMS_V2_SIZE)) return p;
+  if (!p || (p->struct_size != ATTN_PARAMS_V1_SIZE && p->struct_size != ATTN_PARAMS_V2_SIZE &&
+             p->struct_size != ATTN_PARAMS_V3_SIZE))
+    return p;
   const size_t n = p->struct_size;
   memset(&tmp, 0, sizeof tmp);
   memcpy(&tmp, p, n);
@@ -128,6 +134,12 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
       if (p->bias_stride[d] < 0 || p->bias_stride[d] > (1LL << 40))
         return fail(ATTN_ERR_INVALID_ARG, "bias_stride entries must be in [0, 2^40]");
   }
+  if (p->drop_mask) {
+    if ((uintptr_t)p->drop_mask & 3u) return fail(ATTN_ERR_INVALID_ARG, "drop_mask must be 4-byte aligned");
+    for (int d = 0; d < 3; ++d)
+      if (p->drop_stride[d] < 0 || p->drop_stride[d] > (1LL << 40))
+        return fail(ATTN_ERR_INVALID_ARG, "drop_stride entries must be in [0, 2^40]");
+  }
   const uint32_t fwd_flags = ATTN_CARRY_IN | ATTN_NO_FINALIZE;
   const uint32_t bwd_flags = ATTN_BWD_SKIP_DQ | ATTN_BWD_SKIP_DKDV | ATTN_BWD_REUSE_STATS;
   if (p->flags & ~(fwd_flags | bwd_flags)) return fail(ATTN_ERR_INVALID_ARG, "unknown bits in flags");
@@ -170,6 +182,8 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   r.dsink = p->softmax_type == ATTN_SOFTMAX_LEARNABLE ? p->dsink : nullptr;
   r.bias = p->bias;
   for (int d = 0; d < 4; ++d) r.bias_stride[d] = p->bias_stride[d];
+  r.drop = p->drop_mask;
+  for (int d = 0; d < 3; ++d) r.drop_stride[d] = p->drop_stride[d];
   // Rows of the bias read as 16-byte vectors by the bf16 kernels: unit key stride, every
   // row start 16-byte aligned, and key tiles that start at multiples of 4 keys.
   r.bias_vec4 = r.bias && r.bias_stride[3] == 1 && ((uintptr_t)r.bias & 15u) == 0 &&
@@ -215,6 +229,7 @@ int check_sparse(const attn_params* p) {
   if (p->softmax_type != ATTN_SOFTMAX_VANILLA)
     return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no sink softmax");
   if (p->bias) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no bias");
+  if (p->drop_mask) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no dropout mask");
   if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode supports bf16 only");
   if (p->num_q_heads != 1 || p->num_kv_heads != 1)
     return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes the joint embedding: num_q_heads = num_kv_heads = 1");
@@ -366,6 +381,10 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
   a.bs_i = r.bias_stride[2];
   a.bs_j = r.bias_stride[3];
   a.bias_vec4 = r.bias_vec4 ? 1 : 0;
+  a.drop = r.drop;
+  a.ds_b = r.drop_stride[0];
+  a.ds_h = r.drop_stride[1];
+  a.ds_i = r.drop_stride[2];
   a.inv_scale = 1.f / r.scale;
   a.delta = r.delta;
   a.lo_off = r.lo_off;
@@ -473,6 +492,10 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
   a.bs_i = r.bias_stride[2];
   a.bs_j = r.bias_stride[3];
   a.bias_vec4 = r.bias_vec4 ? 1 : 0;
+  a.drop = r.drop;
+  a.ds_b = r.drop_stride[0];
+  a.ds_h = r.drop_stride[1];
+  a.ds_i = r.drop_stride[2];
   a.inv_scale = 1.f / r.scale;
   a.delta = r.delta;
   a.lo_off = r.lo_off;

@@ -101,9 +101,11 @@ struct BwdQCfg {
   static constexpr int MAIN = cmax(cmax(NS * STAGE, STAGE + NW * 32 * 2 * D), NW * 32 * (2 * D + 16));
 };
 
-template <int D, int DV, int NW, bool BIAS>
+// EX: extra logit terms compiled in -- bit 0 an additive bias, bit 1 a dropout mask.
+template <int D, int DV, int NW, int EX>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a) {
   using C = BwdQCfg<D, DV, NW>;
+  constexpr bool BIAS = (EX & 1) != 0, DROP = (EX & 2) != 0;
   static_assert(DV <= D, "the v head dim may not exceed the q/k head dim");
   __shared__ __attribute__((aligned(1024))) char lds[C::MAIN + C::NW * 32 * 4];
 
@@ -211,6 +213,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
   // the previous scores are consumed); the S MFMAs accumulate onto bias / scale.
   const float* const brow =
       BIAS ? a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i : nullptr;
+  // Dropout bits of the same tile (dwl), fetched with it and applied before the row max.
+  const uint32_t* const drow =
+      DROP ? a.drop + b * a.ds_b + hq * a.ds_h + (long long)min(row, a.Sq - 1) * a.ds_i : nullptr;
+  const int drop_nw = (a.Skv + 31) >> 5;
+  uint32_t dwr[3] = {0u, 0u, 0u};
   auto bias_load = [&](int ts, int kend) {
     if constexpr (BIAS) {
       const int last = min(kend, a.Skv) - 1;
@@ -218,6 +225,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
       for (int mb = 0; mb < 2; ++mb)
         bias_fetch16(s[mb], brow, a.bs_j, ts + 32 * mb + 4 * lh, last, ts, a.bias_vec4 != 0);
     }
+    if constexpr (DROP) drop_fetch_tile(dwr, drow, drop_nw, ts);
   };
 
   auto mfma_block = [&](bool do_s, int ts_s, int kend_s, int st_s, int st_p) {
@@ -263,6 +271,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
     if (!s_valid) return;
     const int tend = min(kend, a.Skv);
     const bool full = ts >= w_jmin_hi && ts + C::BN - 1 <= w_jmax_lo && ts + C::BN <= tend;
+    if constexpr (DROP) {
+      uint32_t dwl[2];
+      drop_bits_tile(dwl, dwr, ts, lh);
+      drop_apply16(s[0], dwl[0]);
+      drop_apply16(s[1], dwl[1]);
+    }
     if (!full) {
       cold_path();
       const int jlo_v = max(my_jmin, ts), jhi_v = min(my_jmax, tend - 1);
@@ -477,15 +491,19 @@ struct BwdKVCfg {
   static constexpr int VCPT = BK * DCV / 256;     // 16-byte chunks of the V tile per thread
 };
 
-template <int D, int DV, bool BIAS>
+// EX: extra logit terms compiled in -- bit 0 an additive bias, bit 1 a dropout mask.
+template <int D, int DV, int EX>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdKVCfg<D, DV>;
+  constexpr bool BIAS = (EX & 1) != 0, DROP = (EX & 2) != 0;
   static_assert(DV <= D, "the v head dim may not exceed the q/k head dim");
   __shared__ __attribute__((aligned(16))) __bf16 sQ[2][C::QL::elems(C::BQ)];
   __shared__ __attribute__((aligned(16))) __bf16 sG[2][C::GL::elems(C::BQ)];
   __shared__ __attribute__((aligned(16))) __bf16 sVk[C::VL::elems(C::BK)];   // this workgroup's V rows
   __shared__ __attribute__((aligned(16))) float sLse[2][C::BQ];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BQ];
+  // dropout words of a step: [wave][row], one 32-key word per wave (staged like Q, dO)
+  __shared__ __attribute__((aligned(16))) uint32_t sDrop[2][DROP ? 4 * C::BQ : 1];
 
   // Workgroup id -> (batch, kv head, key tile) and the split: with kv_splits = ns > 1 the
   // G q heads of the group are shared out over ns workgroups (G / ns heads each), which
@@ -583,6 +601,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     glo[u] = C::GL::idx(i, 8 * ch);
   }
   float lbuf = 0.f;
+  uint32_t dbuf = 0u;
   auto load_step = [&](int hq_, int qs) {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc_at(
         qbase, q_bytes, __builtin_amdgcn_readfirstlane((uint32_t)qs * q_rs_b + (uint32_t)hq_ * D * 2));
@@ -597,6 +616,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       const size_t st = ((size_t)b * a.Hq + hq_) * a.Sq + row;
       lbuf = row < a.Sq ? (tid < C::BQ ? a.lse2[st] : a.Dvec[st]) : (tid < C::BQ ? INFINITY : 0.f);
     }
+    if constexpr (DROP) {
+      if (tid < 4 * C::BQ) {   // word of row qs + tid % BQ for the keys of wave tid / BQ
+        const int i = min(qs + (tid % C::BQ), a.Sq - 1);
+        const int kw = min(k0 + 32 * (tid / C::BQ), a.Skv - 1) >> 5;
+        dbuf = a.drop[b * a.ds_b + hq_ * a.ds_h + (long long)i * a.ds_i + kw];
+      }
+    }
   };
   auto store_step = [&](int buf) {
 #pragma unroll
@@ -607,6 +633,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       if (tid + 256 * u < C::NCHV) *(u32x4*)&sG[buf][glo[u]] = gbuf[u];
     if (tid < C::BQ) sLse[buf][tid] = lbuf;
     else if (tid < 2 * C::BQ) sD[buf][tid - C::BQ] = lbuf;
+    if constexpr (DROP) {
+      if (tid < 4 * C::BQ) sDrop[buf][tid] = dbuf;
+    }
   };
   const int tg = lane >> 4, tj = lane & 15;
   const int tr_off = C::QL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
@@ -624,7 +653,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     return a.bias + b * a.bs_b + hq_ * a.bs_h + (long long)min(key, a.Skv - 1) * a.bs_j;
   };
   float bkey = 0.f;
-
   int hq = 0, qs = 0, rend = 0;
   bool have = next_step(hq, qs, rend);
   if (have) {
@@ -644,12 +672,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     const int dmax = w_klast - qs + a.delta;             // largest
     const bool empty = !wave_on || dmax < a.lo_off || dmin > a.hi_off || qs >= qe;
     f32x16 s;
-    if (BIAS && !empty) {
+    if ((BIAS || DROP) && !empty) {
       if (bias_rows) {
         bias_fetch16(s, bias_ptr(hq), a.bs_i, qs + 4 * lh, qe - 1, qs, false);
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = bkey;
+        for (int r = 0; r < 16; ++r) s[r] = BIAS ? bkey : 0.f;
+      }
+      if constexpr (DROP) {
+        // dropped pairs start the S accumulation at -inf: lane (key li) holds rows
+        // 8g + 4lh + e of the step, bit li of their words
+        const uint32_t* dw = &sDrop[cur][wave * C::BQ];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 w4 = *(const u32x4*)(dw + 8 * g + 4 * lh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[4 * g + e] = drop_if(s[4 * g + e], w4[e], li);
+        }
       }
     }
     if (nhave) load_step(nhq, nqs);
@@ -661,7 +700,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       f32x16 dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[r] = BIAS ? s[r] * a.inv_scale : 0.f;
+        s[r] = (BIAS || DROP) ? s[r] * a.inv_scale : 0.f;
         dp[r] = 0.f;
       }
 #pragma unroll
@@ -880,8 +919,11 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
       for (int d = 0; d < D; ++d) s = fmaf(qr[d], sK[r][d], s);
 #pragma unroll
       for (int d = 0; d < DV; ++d) dp = fmaf(gr[d], sV[r][d], dp);
+      // rows past the end (not stored) read the last row's bias / dropout bits
+      const int rc = min(row, a.Sq - 1);
       if (a.bias)
-        s = fmaf(a.bias[b * a.bs_b + hq * a.bs_h + (long long)row * a.bs_i + (long long)j * a.bs_j], a.inv_scale, s);
+        s = fmaf(a.bias[b * a.bs_b + hq * a.bs_h + (long long)rc * a.bs_i + (long long)j * a.bs_j], a.inv_scale, s);
+      if (a.drop && dropped(a.drop, b * a.ds_b + hq * a.ds_h, a.ds_i, rc, j)) s = -INFINITY;
       const float p = fast_exp2(fmaf(s, a.scale_log2, -lse2));
       const float ds = p * (dp - Di);
 #pragma unroll
@@ -896,7 +938,7 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
   }
 }
 
-template <int D, int DV, bool BIAS>
+template <int D, int DV, int EX>
 __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
   constexpr int BK = 128, BQ = 32;
   __shared__ float sQ[BQ][D + 1], sG[BQ][DV + 1], sL[BQ], sDv[BQ];
@@ -960,8 +1002,11 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
         for (int d = 0; d < D; ++d) s = fmaf(sQ[r][d], kr[d], s);
 #pragma unroll
         for (int d = 0; d < DV; ++d) dp = fmaf(sG[r][d], vr[d], dp);
-        if (BIAS)
-          s = fmaf(a.bias[b * a.bs_b + hq * a.bs_h + (long long)i * a.bs_i + (long long)key * a.bs_j], a.inv_scale, s);
+        // keys past the end (not stored) read the last key's bias / dropout bits
+        const int kc = min(key, a.Skv - 1);
+        if ((EX & 1) && a.bias)
+          s = fmaf(a.bias[b * a.bs_b + hq * a.bs_h + (long long)i * a.bs_i + (long long)kc * a.bs_j], a.inv_scale, s);
+        if ((EX & 2) && a.drop && dropped(a.drop, b * a.ds_b + hq * a.ds_h, a.ds_i, i, kc)) s = -INFINITY;
         const float p = fast_exp2(fmaf(s, a.scale_log2, -sL[r]));
         const float ds = p * (dp - sDv[r]);
 #pragma unroll
@@ -1025,14 +1070,19 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
   // The bf16 dq kernel computes D and the LSE itself when they are needed.
   a.fused_stats = (dtype == 0 && want_pre && dq) ? 1 : 0;
   const bool pre = want_pre && !a.fused_stats;
+  const int ex = (a.bias ? 1 : 0) | (a.drop ? 2 : 0);   // extra logit terms compiled in
   // D and the LSE: rows of o and dout have the v head dim.
 #define REA_BWD(T, DD, DDV, DQ_LAUNCH, DKV)                                       \
   do {                                                                          \
     if (pre) launch_pre<T, DDV>(a, stream);                                     \
     if (dq) DQ_LAUNCH;                                                          \
     if (dkdv) {                                                                 \
-      if (a.bias) hipLaunchKernelGGL((DKV<DD, DDV, true>), gk, bk, 0, stream, a); \
-      else hipLaunchKernelGGL((DKV<DD, DDV, false>), gk, bk, 0, stream, a);       \
+      switch (ex) {                                                             \
+        case 1: hipLaunchKernelGGL((DKV<DD, DDV, 1>), gk, bk, 0, stream, a); break; \
+        case 2: hipLaunchKernelGGL((DKV<DD, DDV, 2>), gk, bk, 0, stream, a); break; \
+        case 3: hipLaunchKernelGGL((DKV<DD, DDV, 3>), gk, bk, 0, stream, a); break; \
+        default: hipLaunchKernelGGL((DKV<DD, DDV, 0>), gk, bk, 0, stream, a);      \
+      }                                                                         \
       if (a.kv_splits > 1) {                                                    \
         const long long nk = (long long)a.B * a.Skv * a.Hkv * a.D;              \
         const long long nv = (long long)a.B * a.Skv * a.Hkv * a.Dv;             \
@@ -1043,15 +1093,19 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
       }                                                                         \
     }                                                                           \
   } while (0)
-#define REA_DQ_BF16(DD, DDV)                                                                    \
-  do {                                                                                         \
-    if (a.bias) {                                                                              \
-      if (w4) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 4, true>), gq, bq, 0, stream, a); \
-      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 8, true>), gq, bq, 0, stream, a);    \
-    } else {                                                                                   \
-      if (w4) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 4, false>), gq, bq, 0, stream, a); \
-      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 8, false>), gq, bq, 0, stream, a);    \
-    }                                                                                          \
+#define REA_DQ_BF16_EX(DD, DDV, EXV)                                                          \
+  do {                                                                                     \
+    if (w4) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 4, EXV>), gq, bq, 0, stream, a); \
+    else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, DDV, 8, EXV>), gq, bq, 0, stream, a);    \
+  } while (0)
+#define REA_DQ_BF16(DD, DDV)                                        \
+  do {                                                              \
+    switch (ex) {                                                   \
+      case 1: REA_DQ_BF16_EX(DD, DDV, 1); break;                    \
+      case 2: REA_DQ_BF16_EX(DD, DDV, 2); break;                    \
+      case 3: REA_DQ_BF16_EX(DD, DDV, 3); break;                    \
+      default: REA_DQ_BF16_EX(DD, DDV, 0);                          \
+    }                                                               \
   } while (0)
 #define REA_DQ_F32(DD, DDV) hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, DDV>), gq, bq, 0, stream, a)
   if (!head_dims_supported(dtype, a.D, a.Dv)) return hipErrorInvalidValue;
@@ -1077,6 +1131,7 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
   if (a.dsink && a.sink && has_q && (want_pre || dq))
     hipLaunchKernelGGL(bwd_sink_grad_kernel, dim3(a.Hq), dim3(256), 0, stream, a);
 #undef REA_DQ_BF16
+#undef REA_DQ_BF16_EX
 #undef REA_BWD
   return hipGetLastError();
 }

@@ -42,6 +42,10 @@ struct FwdArgs {
   long long bs_b, bs_h, bs_i, bs_j;
   float inv_scale;
   int bias_vec4;      // rows readable as 16-byte vectors (unit key stride, aligned)
+  // Dropout: pair (i, j) of (b, hq) dropped iff bit j % 32 of word
+  // drop[b*ds_b + hq*ds_h + i*ds_i + j/32] is set; NULL = none.
+  const uint32_t* drop;
+  long long ds_b, ds_h, ds_i;
   // Visibility of (row i, key j): lo_off <= (j - i) + delta <= hi_off, with
   // delta = kv_pos0 - q_pos0 and j < Skv.
   int delta;
@@ -83,6 +87,8 @@ struct BwdArgs {
   long long bs_b, bs_h, bs_i, bs_j;
   float inv_scale;
   int bias_vec4;
+  const uint32_t* drop;  // as in FwdArgs
+  long long ds_b, ds_h, ds_i;
   int delta, lo_off, hi_off;
   float scale, scale_log2;
   int kv_block, n_vblocks;     // virtual key blocks (ring order of the dq pass)
@@ -179,6 +185,38 @@ __device__ __forceinline__ void bias_fetch16(f32x16& d, const float* p, long lon
       d[r] = p[(long long)(x <= last ? x : safe) * st];
     }
   }
+}
+
+// Dropout words of a 64-key tile starting at key ts: the three words of the query row
+// (p, nw of them; words past the row are clamped -- their keys are masked anyway) that
+// cover the tile, loaded ahead; drop_bits_tile() aligns them where they are used (so the
+// loads are not waited for at once).
+__device__ __forceinline__ void drop_fetch_tile(uint32_t (&dwr)[3], const uint32_t* p, int nw, int ts) {
+  const int k0 = ts >> 5;
+  dwr[0] = p[min(k0, nw - 1)];
+  dwr[1] = p[min(k0 + 1, nw - 1)];
+  dwr[2] = p[min(k0 + 2, nw - 1)];
+}
+// Register r of 32-key half mb of a lane holds key ts + 32mb + 8(r>>2) + 4lh + (r&3): bit
+// 8(r>>2) + (r&3) of dwl[mb] set = dropped.
+__device__ __forceinline__ void drop_bits_tile(uint32_t (&dwl)[2], const uint32_t (&dwr)[3], int ts, int lh) {
+  const uint32_t sh = (uint32_t)ts & 31u;
+  dwl[0] = __builtin_amdgcn_alignbit(dwr[1], dwr[0], sh) >> (4 * lh);   // keys ts .. ts + 31
+  dwl[1] = __builtin_amdgcn_alignbit(dwr[2], dwr[1], sh) >> (4 * lh);   // keys ts + 32 .. ts + 63
+}
+// x, or -inf where bit `bit` of w is set: the sign-extended bit selects the bits of -inf
+// (a bitfield extract and a bitfield insert).
+__device__ __forceinline__ float drop_if(float x, uint32_t w, int bit) {
+  const int m = __builtin_amdgcn_sbfe((int)w, bit, 1);           // 0 or -1
+  return __int_as_float((m & (int)0xff800000) | (~m & __float_as_int(x)));
+}
+__device__ __forceinline__ void drop_apply16(f32x16& s, uint32_t w) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = drop_if(s[r], w, 8 * (r >> 2) + (r & 3));
+}
+// Whether pair (row i, key j) is dropped (j < Skv, i < Sq).
+__device__ __forceinline__ bool dropped(const uint32_t* drop, long long base, long long ds_i, int i, int j) {
+  return (drop[base + (long long)i * ds_i + (j >> 5)] >> (j & 31)) & 1u;
 }
 
 // log2 of (l * 2^mm + 2^zz) for a row's key statistics (mm = m * log2 e, l relative to

@@ -66,9 +66,11 @@ struct FwdCfg {
 // Rows of the scores may grow by this much (log2 units) before the carry is rescaled.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int DV, int NW, bool BIAS>
+// EX: extra logit terms compiled in -- bit 0 an additive bias, bit 1 a dropout mask.
+template <int D, int DV, int NW, int EX>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D, DV, NW>;
+  constexpr bool BIAS = (EX & 1) != 0, DROP = (EX & 2) != 0;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
 
   int b, hg, qt;
@@ -194,6 +196,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   // and are masked with the rest.
   const float* const brow =
       BIAS ? a.bias + b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i : nullptr;
+  // Dropout bits of the same tile (dwl), fetched with it and applied before the row max.
+  const uint32_t* const drow =
+      DROP ? a.drop + b * a.ds_b + hq * a.ds_h + (long long)min(row, a.Sq - 1) * a.ds_i : nullptr;
+  const int drop_nw = (a.Skv + 31) >> 5;
+  uint32_t dwr[3] = {0u, 0u, 0u};
   auto bias_load = [&](int ts, int kend) {
     if constexpr (BIAS) {
       const int last = min(kend, a.Skv) - 1;
@@ -201,6 +208,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       for (int mb = 0; mb < 2; ++mb)
         bias_fetch16(s[mb], brow, a.bs_j, ts + 32 * mb + 4 * lh, last, ts, a.bias_vec4 != 0);
     }
+    if constexpr (DROP) drop_fetch_tile(dwr, drow, drop_nw, ts);
   };
 
   // MFMA block: S^T of tile ts_s (K in slot st_s) and O^T += V^T P^T for the tile whose
@@ -257,6 +265,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
           const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
           if (jhi_v < jlo_v || (uint32_t)(base + koff) > span) s[mb][r] = -INFINITY;
         }
+    }
+    if constexpr (DROP) {
+      uint32_t dwl[2];
+      drop_bits_tile(dwl, dwr, ts, lh);
+      drop_apply16(s[0], dwl[0]);
+      drop_apply16(s[1], dwl[1]);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -495,7 +509,8 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
       for (int d = 0; d < D; ++d) dot = fmaf(qr[d], sK[r][d], dot);
       if (a.bias && j < tend) dot = fmaf(a.bias[b * a.bs_b + hq * a.bs_h + (long long)min(row, a.Sq - 1) * a.bs_i +
                                                 (long long)j * a.bs_j], a.inv_scale, dot);
-      s[r] = (j < my_jmin || j > my_jmax || j >= tend) ? -INFINITY : dot * a.scale_log2;
+      const bool drop = a.drop && j < tend && dropped(a.drop, b * a.ds_b + hq * a.ds_h, a.ds_i, min(row, a.Sq - 1), j);
+      s[r] = (j < my_jmin || j > my_jmax || j >= tend || drop) ? -INFINITY : dot * a.scale_log2;
       mx = fmaxf(mx, s[r]);
     }
     const float m_new = fmaxf(m_run, mx);
@@ -546,6 +561,14 @@ static bool fwd_use_w4(const FwdArgs& a) {
 #endif
 }
 
+template <int D, int DV, int EX>
+static void launch_fwd_ex(const FwdArgs& a, bool w4, dim3 grid, dim3 block, hipStream_t stream) {
+  if (w4)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 4, EX>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 8, EX>), grid, block, 0, stream, a);
+}
+
 template <int D, int DV>
 static void launch_fwd_bf16(FwdArgs a, bool w4, hipStream_t stream) {
   // gh = q heads per workgroup: the largest power of two <= NW dividing the GQA group.
@@ -557,16 +580,12 @@ static void launch_fwd_bf16(FwdArgs a, bool w4, hipStream_t stream) {
   a.n_hg = a.Hq >> a.gh_shift;
   a.n_qtiles = (a.Sq + a.rows_wg - 1) / a.rows_wg;
   const dim3 grid((unsigned)a.n_qtiles * a.B * a.n_hg), block(64 * nw);
-  if (a.bias) {
-    if (w4)
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 4, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 8, true>), grid, block, 0, stream, a);
-  } else {
-    if (w4)
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 4, false>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, 8, false>), grid, block, 0, stream, a);
+  // extra logit terms compiled in: bit 0 bias, bit 1 dropout
+  switch ((a.bias ? 1 : 0) | (a.drop ? 2 : 0)) {
+    case 1: launch_fwd_ex<D, DV, 1>(a, w4, grid, block, stream); break;
+    case 2: launch_fwd_ex<D, DV, 2>(a, w4, grid, block, stream); break;
+    case 3: launch_fwd_ex<D, DV, 3>(a, w4, grid, block, stream); break;
+    default: launch_fwd_ex<D, DV, 0>(a, w4, grid, block, stream);
   }
 }
 

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
 
 
 def params(**kw):
@@ -61,9 +61,10 @@ def fwd_status(lib, p, ptr=None):
 
 
 def test_struct_layout(lib):
-    assert ctypes.sizeof(rea.AttnParams) == 168
+    assert ctypes.sizeof(rea.AttnParams) == 200
     assert rea.AttnParams.softmax_type.offset == 104          # ATTN_PARAMS_V1_SIZE
     assert rea.AttnParams.bias.offset == 128                  # ATTN_PARAMS_V2_SIZE
+    assert rea.AttnParams.drop_mask.offset == 168             # ATTN_PARAMS_V3_SIZE
     assert ctypes.sizeof(rea.SelectParams) == 40
     assert rea.SelectParams.seqlen_kv.offset == 32          # SELECT_PARAMS_V1_SIZE
     # a zero batch is a successful no-op only when the struct size matches
@@ -119,6 +120,19 @@ def test_bias_stride_checks(lib):
     assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"bias_stride" in lib.attn_last_error()
     p.bias_stride[2] = 0
     assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"q is NULL" in lib.attn_last_error()
+
+
+def test_version3_struct_is_accepted(lib):
+    """A 168-byte struct (before the dropout fields) reads as having no dropout."""
+    p = params(batch=1)
+    p.drop_mask = 0x1002                              # misaligned, past the v3 size: ignored
+    p.struct_size = 168
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"q is NULL" in lib.attn_last_error()
+    p.struct_size = 200
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"drop_mask" in lib.attn_last_error()
+    p.drop_mask = 0x1000
+    p.drop_stride[1] = -4
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"drop_stride" in lib.attn_last_error()
 
 
 def test_version2_struct_is_accepted(lib):

@@ -218,6 +218,50 @@ def test_additive_bias(gpu, case):
     check_close("dv", dv, dv_r, dt)
 
 
+DROP_CASES = [
+    # id, dtype, B, Sq, Skv, Hq, Hkv, D, Dv, causal, window, q_pos0, kv_block, dropout shape, p, with bias
+    ("drop_bf16_causal_gqa2", "bf16", 2, 300, 300, 4, 2, 128, 128, True, (-1, -1), 0, 0, "bhij", 0.2, False),
+    ("drop_bf16_swa_gqa16_headshared", "bf16", 1, 515, 515, 16, 1, 128, 128, True, (37, 0), 0, 0, "b1ij", 0.3, False),
+    ("drop_bf16_ring_unaligned_blocks", "bf16", 1, 520, 520, 4, 2, 128, 128, True, (-1, -1), 0, 130, "1hij", 0.1, False),
+    ("drop_bf16_cross_offsets", "bf16", 1, 200, 520, 4, 4, 64, 64, False, (-1, -1), 320, 0, "bhij", 0.25, False),
+    ("drop_bf16_mla", "bf16", 1, 333, 333, 4, 1, 128, 64, True, (-1, -1), 0, 0, "bhij", 0.2, False),
+    ("drop_bf16_with_bias", "bf16", 2, 260, 260, 4, 4, 64, 64, True, (-1, -1), 0, 0, "bhij", 0.15, True),
+    ("drop_f32_d64", "f32", 1, 200, 200, 4, 2, 64, 64, True, (-1, -1), 0, 0, "bhij", 0.2, False),
+]
+
+
+@pytest.mark.parametrize("case", DROP_CASES, ids=[c[0] for c in DROP_CASES])
+def test_dropout(gpu, case):
+    """bpt.py's dropout as a packed Bernoulli array (dropped pairs leave the softmax):
+    forward and backward against the oracle, for broadcast shapes, key tiles that start
+    off a 32-key boundary (ring blocks of 130), position offsets, MLA dims, together with
+    a bias, and fp32."""
+    name, dt, B, Sq, Skv, Hq, Hkv, D, Dv, causal, window, qp0, kvb, dshape, pdrop, with_bias = case
+    t = tdtype(dt)
+    seed = zlib.crc32(name.encode()) % 10000
+    q, k, v, do = (rnd((B, Sq, Hq, D), seed, t), rnd((B, Skv, Hkv, D), seed + 1, t),
+                   rnd((B, Skv, Hkv, Dv), seed + 2, t), rnd((B, Sq, Hq, Dv), seed + 3, t))
+    dims = {"b": B, "h": Hq, "i": Sq, "j": Skv, "1": 1}
+    g = torch.Generator().manual_seed(seed + 4)
+    drop = torch.rand(tuple(dims[c] for c in dshape), generator=g) < pdrop
+    bias = 2.0 * workloads.random_tensor((B, Hq, Sq, Skv), seed + 5) if with_bias else None
+    kw = dict(causal=causal, window=window, q_pos0=qp0, kv_block=kvb)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    words = workloads.pack_bits(drop).to(DEV)
+    gk = dict(kw, dropout=words, bias=None if bias is None else bias.to(DEV))
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **gk)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **gk)
+    torch.cuda.synchronize()
+    ok = dict(causal=causal, window=window, q_pos0=qp0, dropout=drop.numpy(), bias=bias)
+    o_r, m_r, l_r = dense.forward(q, k, v, **ok)
+    check_close("o", o, o_r, dt)
+    check_stats(m, l, m_r, l_r, dt)
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, **ok)
+    check_close("dq", dq, dq_r, dt)
+    check_close("dk", dk, dk_r, dt)
+    check_close("dv", dv, dv_r, dt)
+
+
 def test_sink_carry_is_applied_once(gpu):
     """Two ring steps with the carry handed over: the sink enters only when the output is
     finalised, so the result equals one call and the oracle."""

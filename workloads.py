@@ -128,6 +128,18 @@ def small(w: Workload, **kw) -> Workload:
     return w.with_(**kw)
 
 
+def pack_bits(mask: torch.Tensor) -> torch.Tensor:
+    """Boolean [..., N] -> int32 words [..., ceil(N / 32)], bit j % 32 of word j / 32 = mask[..., j]
+    (the packed dropout bits the library reads)."""
+    N = mask.shape[-1]
+    W = (N + 31) // 32
+    m = torch.zeros(mask.shape[:-1] + (W * 32,), dtype=torch.int32, device=mask.device)
+    m[..., :N] = mask.to(torch.int32)
+    # disjoint bits: the int32 sum is their OR (bit 31 wraps to the sign bit)
+    shifts = torch.arange(32, dtype=torch.int32, device=mask.device)
+    return (m.reshape(mask.shape[:-1] + (W, 32)) << shifts).sum(-1, dtype=torch.int32)
+
+
 def random_tensor(shape, seed: int, dtype=torch.float32, scale: float = 1.0):
     """Standalone seeded N(0, scale^2) tensor (used for edge-case shapes in tests)."""
     g = torch.Generator().manual_seed(seed)
