@@ -425,6 +425,36 @@ def test_step_api_carry_with_bias(gpu):
     check_stats(m1, l1, m_r, l_r, "bf16")
 
 
+def test_step_api_carry_with_dropout(gpu):
+    """Ring steps with dropout: each step gets the words of its key block (a slice of the
+    packed array at a word boundary), and the carried result equals one call and the
+    oracle; the backward of the single call too."""
+    B, S, Hq, Hkv, D = 1, 512, 4, 2, 128
+    t = torch.bfloat16
+    q, k, v = rnd((B, S, Hq, D), 41, t), rnd((B, 2 * S, Hkv, D), 42, t), rnd((B, 2 * S, Hkv, D), 43, t)
+    do = rnd((B, S, Hq, D), 44, t)
+    g = torch.Generator().manual_seed(45)
+    drop = torch.rand((B, Hq, S, 2 * S), generator=g) < 0.2
+    words = workloads.pack_bits(drop).to(DEV)                       # [B, Hq, S, 2S / 32]
+    W = S // 32
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    acc, m, l = gpu.attn_fwd(qd, kd[:, S:].contiguous(), vd[:, S:].contiguous(), causal=True,
+                             q_pos0=S, kv_pos0=S, finalize=False, dropout=words[..., W:])
+    o, m, l = gpu.attn_fwd(qd, kd[:, :S].contiguous(), vd[:, :S].contiguous(), causal=True,
+                           q_pos0=S, kv_pos0=0, carry_in=True, m=m, l=l, acc=acc, dropout=words[..., :W])
+    o1, m1, l1 = gpu.attn_fwd(qd, kd, vd, causal=True, q_pos0=S, kv_pos0=0, dropout=words)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o1, dod, m1, l1, causal=True, q_pos0=S, kv_pos0=0, dropout=words)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = dense.forward(q, k, v, causal=True, q_pos0=S, kv_pos0=0, dropout=drop.numpy())
+    check_close("o (two steps)", o, o_r, "bf16")
+    check_stats(m, l, m_r, l_r, "bf16")
+    check_close("o (one call)", o1, o_r, "bf16")
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, causal=True, q_pos0=S, kv_pos0=0, dropout=drop.numpy())
+    check_close("dq", dq, dq_r, "bf16")
+    check_close("dk", dk, dk_r, "bf16")
+    check_close("dv", dv, dv_r, "bf16")
+
+
 def test_bias_with_learnable_sink(gpu):
     """Bias and a learnable sink together: the sink joins the denominator of the biased
     logits; forward, gradients and the sink gradient against the oracle."""
