@@ -326,6 +326,42 @@ def test_ring_sim_full_size(gpu):
     check_close("dv", dv[:, :, bh], dv_r[:, :, bh], "bf16")
 
 
+def unpack_bits(words, n):
+    """int32 words [..., W] -> boolean [..., n] (bit j % 32 of word j / 32)."""
+    u = words.numpy().view(np.uint32)
+    bits = (u[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1
+    return bits.reshape(u.shape[:-1] + (-1,))[..., :n].astype(bool)
+
+
+def test_ring_full_size_bias_dropout(gpu):
+    """The ring workload with the inputs of bench --bias keypad --dropout 0.1 (last S/16 keys
+    at -inf; Bernoulli(0.1) drops drawn on the GPU and packed): two heads checked forward,
+    one backward, against the oracle given the same drops."""
+    w, q, k, v, do = full_inputs("ring_sim_causal_s8192")
+    B, S, H = w.batch, w.seqlen, w.num_q_heads
+    bias = torch.zeros((B, 1, 1, S), dtype=torch.float32)
+    bias[..., S - S // 16:] = float("-inf")
+    g = torch.Generator(device=DEV).manual_seed(w.seed + 102)
+    words = torch.empty((1, H, S, (S + 31) // 32), dtype=torch.int32, device=DEV)
+    for h in range(H):
+        words[0, h] = workloads.pack_bits(torch.rand((S, S), generator=g, device=DEV) < 0.1)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    kw = dict(launch_kw(w), bias=bias.to(DEV), dropout=words)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **kw)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **kw)
+    torch.cuda.synchronize()
+    for h in (2, 9):
+        drop = unpack_bits(words[0, h].cpu(), S)[None, None]
+        o_r, m_r, l_r = dense.forward(q, k, v, heads=[h], bias=bias, dropout=drop, **oracle_kw(w))
+        check_close(f"o head {h}", o[:, :, [h]], o_r[:, :, [h]], "bf16")
+        check_stats(m[:, [h]], l[:, [h]], m_r[:, [h]], l_r[:, [h]], "bf16")
+        if h == 9:
+            dq_r, dk_r, dv_r = dense.backward(q, k, v, do, heads=[h], bias=bias, dropout=drop, **oracle_kw(w))
+            check_close("dq", dq[:, :, [h]], dq_r[:, :, [h]], "bf16")
+            check_close("dk", dk[:, :, [h]], dk_r[:, :, [h]], "bf16")      # G = 1
+            check_close("dv", dv[:, :, [h]], dv_r[:, :, [h]], "bf16")
+
+
 def test_gqa_swa_full_size(gpu):
     """B2 S4096 Hq128 Hkv8 D128, window (128, 0): one full GQA group checked fwd and bwd."""
     w, q, k, v, do = full_inputs("gqa16_swa128_s4096")
