@@ -80,7 +80,8 @@ template <int D, int DV, int NW_>
 struct BwdQCfg {
   static constexpr int NW = NW_;                  // 8: ping-pong, one workgroup per CU; 4: two per CU
   static constexpr bool PP = NW == 8;
-  static constexpr int BN = 64;
+  static constexpr int BN = PP ? 64 : 32;        // keys per tile (32: windowed rows, see the forward)
+  static constexpr int NMB = BN / 32;             // 32-key blocks per tile
   static constexpr int NS = PP ? 3 : 2;           // stages of (K, V) tiles
   static constexpr int KS = D / 16;               // k-steps of S^T (over the q/k head dim)
   static constexpr int KSV = DV / 16;             // k-steps of dP^T (over the v head dim)
@@ -205,8 +206,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
   const int kt_off = (tg >> 1) * (16 * C::G4) + (tj >> 2) * (16 * C::P4) + 32 * (tg & 1) + 8 * (tj & 3);
   const int v_off = C::KI * 1024 + li * (16 * C::VRS) + 16 * lh;
 
-  f32x16 s[2], dp[2];
-  bf16x8 dsb[4];                                   // dS^T of the last VALU block, B operands
+  f32x16 s[C::NMB], dp[C::NMB];
+  bf16x8 dsb[2 * C::NMB];                                   // dS^T of the last VALU block, B operands
   bool s_valid = false, ds_valid = false;
 
   // With a bias, s holds the raw bias of the next tile whose S is computed (loaded once
@@ -217,12 +218,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
   const uint32_t* const drow =
       DROP ? a.drop + b * a.ds_b + hq * a.ds_h + (long long)min(row, a.Sq - 1) * a.ds_i : nullptr;
   const int drop_nw = (a.Skv + 31) >> 5;
-  uint32_t dwr[3] = {0u, 0u, 0u};
+  uint32_t dwr[C::NMB + 1] = {};
   auto bias_load = [&](int ts, int kend) {
     if constexpr (BIAS) {
       const int last = min(kend, a.Skv) - 1;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::NMB; ++mb)
         bias_fetch16(s[mb], brow, a.bs_j, ts + 32 * mb + 4 * lh, last, ts, a.bias_vec4 != 0);
     }
     if constexpr (DROP) drop_fetch_tile(dwr, drow, drop_nw, ts);
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
       const char* kt = lds + st_s * C::STAGE + k_off;
       const char* vt = lds + st_s * C::STAGE + v_off;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           s[mb][r] = BIAS ? s[mb][r] * a.inv_scale : 0.f;
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < C::NMB; ++mb) {
           s[mb] = mfma32(*(const bf16x8*)(kt + mb * 8 * 16 * C::G4 + 32 * kk), qreg[kk], s[mb]);
           if (kk < C::KSV)
             dp[mb] = mfma32(*(const bf16x8*)(vt + mb * 32 * 16 * C::VRS + 32 * kk), doreg[kk], dp[mb]);
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
     if (ds_valid) {
       const char* kp = lds + st_p * C::STAGE + kt_off;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 2 * C::NMB; ++c)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           const char* kp0 = kp + c * 4 * 16 * C::G4 + 64 * db;
@@ -272,10 +273,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
     const int tend = min(kend, a.Skv);
     const bool full = ts >= w_jmin_hi && ts + C::BN - 1 <= w_jmax_lo && ts + C::BN <= tend;
     if constexpr (DROP) {
-      uint32_t dwl[2];
+      uint32_t dwl[C::NMB];
       drop_bits_tile(dwl, dwr, ts, lh);
-      drop_apply16(s[0], dwl[0]);
-      drop_apply16(s[1], dwl[1]);
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) drop_apply16(s[mb], dwl[mb]);
     }
     if (!full) {
       cold_path();
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
       const uint32_t span = (uint32_t)(jhi_v - jlo_v);
       const int base = ts + 4 * lh - jlo_v;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
         }
     }
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32x4 w4;

@@ -187,22 +187,24 @@ __device__ __forceinline__ void bias_fetch16(f32x16& d, const float* p, long lon
   }
 }
 
-// Dropout words of a 64-key tile starting at key ts: the three words of the query row
-// (p, nw of them; words past the row are clamped -- their keys are masked anyway) that
-// cover the tile, loaded ahead; drop_bits_tile() aligns them where they are used (so the
+// Dropout words of a tile of 32(NR - 1) keys starting at key ts: the NR words of the
+// query row (p, nw of them; words past the row are clamped -- their keys are masked
+// anyway) that cover the tile, loaded ahead; drop_bits_tile() aligns them where they are used (so the
 // loads are not waited for at once).
-__device__ __forceinline__ void drop_fetch_tile(uint32_t (&dwr)[3], const uint32_t* p, int nw, int ts) {
+template <int NR>
+__device__ __forceinline__ void drop_fetch_tile(uint32_t (&dwr)[NR], const uint32_t* p, int nw, int ts) {
   const int k0 = ts >> 5;
-  dwr[0] = p[min(k0, nw - 1)];
-  dwr[1] = p[min(k0 + 1, nw - 1)];
-  dwr[2] = p[min(k0 + 2, nw - 1)];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) dwr[i] = p[min(k0 + i, nw - 1)];
 }
 // Register r of 32-key half mb of a lane holds key ts + 32mb + 8(r>>2) + 4lh + (r&3): bit
 // 8(r>>2) + (r&3) of dwl[mb] set = dropped.
-__device__ __forceinline__ void drop_bits_tile(uint32_t (&dwl)[2], const uint32_t (&dwr)[3], int ts, int lh) {
+template <int NL>
+__device__ __forceinline__ void drop_bits_tile(uint32_t (&dwl)[NL], const uint32_t (&dwr)[NL + 1], int ts, int lh) {
   const uint32_t sh = (uint32_t)ts & 31u;
-  dwl[0] = __builtin_amdgcn_alignbit(dwr[1], dwr[0], sh) >> (4 * lh);   // keys ts .. ts + 31
-  dwl[1] = __builtin_amdgcn_alignbit(dwr[2], dwr[1], sh) >> (4 * lh);   // keys ts + 32 .. ts + 63
+#pragma unroll
+  for (int i = 0; i < NL; ++i)                    // keys ts + 32i .. ts + 32i + 31
+    dwl[i] = __builtin_amdgcn_alignbit(dwr[i + 1], dwr[i], sh) >> (4 * lh);
 }
 // x, or -inf where bit `bit` of w is set: the sign-extended bit selects the bits of -inf
 // (a bitfield extract and a bitfield insert).

@@ -39,7 +39,10 @@ template <int D, int DV, int NW_>
 struct FwdCfg {
   static constexpr int NW = NW_;                   // wavefronts per workgroup (8 or 4)
   static constexpr bool PP = NW == 8;              // ping-pong between the two waves of a SIMD
-  static constexpr int BN = 64;                    // keys per tile
+  // keys per tile: 64 with the ping-pong; 32 with 4 waves, whose windowed rows need
+  // about 160 keys per 32-row block (five 32-key tiles instead of three of 64)
+  static constexpr int BN = PP ? 64 : 32;
+  static constexpr int NMB = BN / 32;              // 32-key blocks per tile
   static constexpr int KS = D / 16;                // k-steps of S^T over d
   static constexpr int DB = DV / 32;               // 32-row blocks of O^T
   static constexpr int DC = D / 8;                 // 16-byte chunks per Q / K row
@@ -186,8 +189,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int k_off = li * (16 * C::KRS) + 16 * lh;
   const int v_off = (4 * (tg >> 1) + (tj >> 2)) * (16 * C::VRS) + 32 * (tg & 1) + 8 * (tj & 3);
 
-  f32x16 s[2];
-  bf16x8 pb[4];                                    // P^T of the last softmax, B operands
+  f32x16 s[C::NMB];
+  bf16x8 pb[2 * C::NMB];                           // P^T of the last softmax, B operands
   bool s_valid = false, p_valid = false;
 
   // With a bias, s holds the raw bias of the next tile whose S is computed (loaded as
@@ -200,12 +203,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const uint32_t* const drow =
       DROP ? a.drop + b * a.ds_b + hq * a.ds_h + (long long)min(row, a.Sq - 1) * a.ds_i : nullptr;
   const int drop_nw = (a.Skv + 31) >> 5;
-  uint32_t dwr[3] = {0u, 0u, 0u};
+  uint32_t dwr[C::NMB + 1] = {};
   auto bias_load = [&](int ts, int kend) {
     if constexpr (BIAS) {
       const int last = min(kend, a.Skv) - 1;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::NMB; ++mb)
         bias_fetch16(s[mb], brow, a.bs_j, ts + 32 * mb + 4 * lh, last, ts, a.bias_vec4 != 0);
     }
     if constexpr (DROP) drop_fetch_tile(dwr, drow, drop_nw, ts);
@@ -220,13 +223,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       s_valid = true;
       const char* kt = lds + C::kaddr(st_s) + k_off;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[mb][r] = BIAS ? s[mb][r] * a.inv_scale : 0.f;
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < C::NMB; ++mb) {
           const bf16x8 ka = *(const bf16x8*)(kt + mb * 32 * 16 * C::KRS + 32 * kk);
           s[mb] = mfma32(ka, qreg[kk], s[mb]);
         }
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     if (p_valid) {
       const char* vt = lds + C::vaddr(st_p) + v_off;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 2 * C::NMB; ++c)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           const char* vp0 = vt + c * 16 * 16 * C::VRS + 64 * db;
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       const uint32_t span = (uint32_t)(jhi_v - jlo_v);
       const int base = ts + 4 * lh - jlo_v;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int koff = 32 * mb + 8 * (r >> 2) + (r & 3);
@@ -267,14 +270,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
         }
     }
     if constexpr (DROP) {
-      uint32_t dwl[2];
+      uint32_t dwl[C::NMB];
       drop_bits_tile(dwl, dwr, ts, lh);
-      drop_apply16(s[0], dwl[0]);
-      drop_apply16(s[1], dwl[1]);
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) drop_apply16(s[mb], dwl[mb]);
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
     mx = fmaxf(mx, other_half(mx));
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     const float m_ref = (m_used == -INFINITY) ? 0.f : m_used;
     float rs = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32x4 w4;
