@@ -49,6 +49,10 @@ SMALL = [
     ("bf16_d128_cross_len_offsets", "bf16", 1, 200, 520, 4, 4, 128, False, (-1, -1), 320, 0, 130),
     ("bf16_d32_gqa4_causal_offsets", "bf16", 1, 150, 300, 8, 2, 32, True, (-1, -1), 150, 0, 0),
     ("f32_d32_causal_gqa2", "f32", 1, 256, 256, 4, 2, 32, True, (-1, -1), 0, 0, 64),
+    # windowed (32-key tiles): ring blocks of 130 keys, so tiles start off a 32-key
+    # boundary; a window 509 keys wide, the widest that still takes the windowed kernels
+    ("bf16_d128_swa_unaligned_blocks", "bf16", 1, 650, 650, 4, 2, 128, True, (300, 0), 0, 0, 130),
+    ("bf16_d64_window_509", "bf16", 1, 900, 900, 2, 2, 64, False, (400, 108), 0, 0, 0),
     ("f32_d64_swa_ragged", "f32", 2, 77, 77, 2, 1, 64, True, (9, 0), 0, 0, 0),
 ]
 
@@ -94,6 +98,7 @@ MLA_SMALL = [
     ("mla_bf16_swa37_gqa16", "bf16", 1, 515, 515, 16, 1, 128, 64, True, (37, 0), 0, 0, 0),
     ("mla_bf16_ring_offsets", "bf16", 1, 512, 768, 4, 4, 128, 64, True, (-1, -1), 256, 0, 128),
     ("mla_bf16_right_window", "bf16", 1, 190, 190, 2, 1, 128, 64, False, (-1, 20), 0, 0, 0),
+    ("mla_bf16_swa_ring_blocks", "bf16", 1, 576, 576, 4, 1, 128, 64, True, (77, 0), 0, 0, 96),
     ("mla_f32_d64_v32", "f32", 1, 200, 200, 4, 2, 64, 32, True, (-1, -1), 0, 0, 0),
 ]
 
@@ -175,6 +180,7 @@ BIAS_CASES = [
     ("bias_dead_rows_bf16_ring", "bf16", 1, 512, 4, 2, 128, 128, True, (-1, -1), 128, "b1ij", "deadrows"),
     ("bias_full_bf16_mla", "bf16", 1, 333, 4, 1, 128, 64, True, (-1, -1), 0, "bhij", "randn"),
     ("bias_full_f32_d64", "f32", 1, 200, 4, 2, 64, 64, True, (-1, -1), 0, "bhij", "randn"),
+    ("bias_full_bf16_swa_vec4", "bf16", 1, 300, 4, 2, 128, 128, True, (64, 0), 0, "bhij", "randn"),
 ]
 
 
@@ -227,6 +233,7 @@ DROP_CASES = [
     ("drop_bf16_mla", "bf16", 1, 333, 333, 4, 1, 128, 64, True, (-1, -1), 0, 0, "bhij", 0.2, False),
     ("drop_bf16_with_bias", "bf16", 2, 260, 260, 4, 4, 64, 64, True, (-1, -1), 0, 0, "bhij", 0.15, True),
     ("drop_f32_d64", "f32", 1, 200, 200, 4, 2, 64, 64, True, (-1, -1), 0, 0, "bhij", 0.2, False),
+    ("drop_bf16_swa_unaligned_bias", "bf16", 1, 390, 390, 4, 2, 128, 128, True, (90, 0), 0, 130, "bhij", 0.2, True),
 ]
 
 
