@@ -1039,20 +1039,23 @@ static void launch_pre(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, a);
 }
 
+// Workgroup shape of the bf16 dq kernel.  The 4-wave form (32-key tiles, two workgroups
+// per CU) measured faster for every window tried (128 to 3000 keys wide) and for causal
+// attention with fewer than 8 q heads per kv head; with 8 or more heads sharing each K/V
+// tile the 8-wave ping-pong is ahead.
 static bool dq_use_w4(const BwdArgs& a) {
 #ifdef REA_DQ_WAVES
   return REA_DQ_WAVES == 4;
 #else
-  return a.lo_off > -kPosInf && a.hi_off < kPosInf && (long long)a.hi_off - a.lo_off < 512;
+  return (a.lo_off > -kPosInf && a.hi_off < kPosInf) || a.G < 8;
 #endif
 }
 
 hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
   BwdArgs a = args;
   dim3 gq((unsigned)a.n_qtiles * a.B * a.Hq), bq(128);
-  // bf16 dq workgroups, as in the forward pass: 8 waves (ping-pong, one per CU) when a
-  // query tile sees many keys, 4 waves (two per CU) when every row sees a short window;
-  // gh q heads of one GQA group x 32 * waves / gh rows.
+  // bf16 dq workgroups: 8 waves (ping-pong, one per CU) or 4 waves (two per CU), chosen
+  // by dq_use_w4; gh q heads of one GQA group x 32 * waves / gh rows.
   const bool w4 = dq_use_w4(a);
   if (dtype == 0) {
     const int nw = w4 ? 4 : 8, max_shift = w4 ? 2 : 3;

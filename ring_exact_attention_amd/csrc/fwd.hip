@@ -553,14 +553,15 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
 int fwd_tile_rows(int dtype) { return dtype == 0 ? 32 : 128; }
 
 // Workgroup shape of the bf16 forward: 8 waves (ping-pong, one workgroup per CU) when
-// a query tile sees many keys; 4 waves (two workgroups per CU) when every row sees a
-// short window, where a work item is only a few tiles long and the second workgroup
-// hides the load of one item's Q and the store of its O behind the other's tiles.
+// a query tile sees many keys; 4 waves (two workgroups per CU, 32-key tiles) when every
+// row sees a window under 1024 keys, where a work item is only a few tiles long and the
+// second workgroup hides the load of one item's Q and the store of its O behind the
+// other's tiles (measured ahead up to windows of about 1000 keys, level at 1500-3000).
 static bool fwd_use_w4(const FwdArgs& a) {
 #ifdef REA_FWD_WAVES
   return REA_FWD_WAVES == 4;
 #else
-  return a.lo_off > -kPosInf && a.hi_off < kPosInf && (long long)a.hi_off - a.lo_off < 512;
+  return a.lo_off > -kPosInf && a.hi_off < kPosInf && (long long)a.hi_off - a.lo_off < 1024;
 #endif
 }
 
