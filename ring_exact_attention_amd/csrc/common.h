@@ -191,11 +191,14 @@ __device__ __forceinline__ void bias_fetch16(f32x16& d, const float* p, long lon
 // query row (p, nw of them; words past the row are clamped -- their keys are masked
 // anyway) that cover the tile, loaded ahead; drop_bits_tile() aligns them where they are used (so the
 // loads are not waited for at once).
+// A tile that starts on a 32-key boundary needs only the first NR - 1 words (ts is
+// wave-uniform, so the last load is skipped for the whole wave).
 template <int NR>
 __device__ __forceinline__ void drop_fetch_tile(uint32_t (&dwr)[NR], const uint32_t* p, int nw, int ts) {
   const int k0 = ts >> 5;
 #pragma unroll
-  for (int i = 0; i < NR; ++i) dwr[i] = p[min(k0 + i, nw - 1)];
+  for (int i = 0; i < NR - 1; ++i) dwr[i] = p[min(k0 + i, nw - 1)];
+  dwr[NR - 1] = (ts & 31) ? p[min(k0 + NR - 1, nw - 1)] : 0u;
 }
 // Register r of 32-key half mb of a lane holds key ts + 32mb + 8(r>>2) + 4lh + (r&3): bit
 // 8(r>>2) + (r&3) of dwl[mb] set = dropped.
