@@ -1042,12 +1042,13 @@ static void launch_pre(const BwdArgs& a, hipStream_t stream) {
 // Workgroup shape of the bf16 dq kernel.  The 4-wave form (32-key tiles, two workgroups
 // per CU) measured faster for every window tried (128 to 3000 keys wide) and for causal
 // attention with fewer than 8 q heads per kv head; with 8 or more heads sharing each K/V
-// tile the 8-wave ping-pong is ahead.
+// tile, or with dropout (whose words cost more loads per key in 32-key tiles), the 8-wave
+// ping-pong is ahead.
 static bool dq_use_w4(const BwdArgs& a) {
 #ifdef REA_DQ_WAVES
   return REA_DQ_WAVES == 4;
 #else
-  return (a.lo_off > -kPosInf && a.hi_off < kPosInf) || a.G < 8;
+  return (a.lo_off > -kPosInf && a.hi_off < kPosInf) || (a.G < 8 && a.drop == nullptr);
 #endif
 }
 
