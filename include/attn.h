@@ -127,9 +127,12 @@ typedef struct attn_params {
   /* Gathered block-sparse mode ("AnnAttention", faiss_block_attention): when sel_idx
    * is non-NULL, attn_fwd attends each token to a zero-padded window of
    * sparse_window keys ending at the token, followed by the sel_block rows of each of
-   * its top_n selected blocks (an index of -1 reads token 0 for every row; an index
-   * >= Skv / sel_block, which block_select never produces, reads zero rows), with one
-   * softmax over all slots and no mask.  Requires bf16, Hq = Hkv = 1, head_dim = the
+   * its top_n selected blocks (an index of -1 reads token 0 for every row), with one
+   * softmax over all slots and no mask.  A block whose rows run past the end of the
+   * key sequence is outside the operation (block_select never produces one, and the
+   * page's gather is undefined for it); the kernels' range-checked reads then see zero
+   * rows (logit 0, value 0, no gradient), nothing is read out of bounds and no error is
+   * returned.  Requires bf16, Hq = Hkv = 1, head_dim = the
    * joint embedding (512), causal/window/flags/kv_block unused.  Query row r sits at
    * position q_pos0 + r of the Skv key / value rows (q_pos0 >= 0, q_pos0 + Sq <= Skv):
    * the whole sequence (Sq = Skv, q_pos0 = 0) or new tokens against a cache.  The

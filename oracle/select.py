@@ -26,7 +26,10 @@ block, after the call's search, so a new token at position t still chooses among
 full blocks before its own block -- the same candidates as above.  ``q_pos0`` places the
 query rows at positions q_pos0 .. q_pos0 + Sq - 1 of a key cache of any length Skv; the
 means are those of the cache's full blocks (a mean is a function of its rows, so
-recomputing them equals keeping them in an index).
+recomputing them equals keeping them in an index).  The page's inference-mode loop is
+garbled in the extracted text, so this reading is pinned only to itself (equality with
+the full-sequence rows, brute force on the same reading): parity unpinned against the
+page.
 
 Precision: block means of bf16 inputs are exact in fp64 (a sum of 32 bf16 values fits
 in 53 bits; dividing by 32 is exact), and fp64 dot products leave rounding of ~1e-16

@@ -17,13 +17,16 @@ Follows ``faiss_block_attention`` of the "AnnAttention" page ("Core code"):
 The window helper and the block-to-item helper are not shown on the page; the
 readings above (window ends at t inclusive, zero padding; block c -> rows c*bs ..
 c*bs+bs-1) are pinned only to themselves -- parity unpinned against the originals.
-A block index past the last block (never produced by the selection) is read as zero
-rows, like the window padding.
+A selected block whose rows run past the end of the key sequence is outside what the
+page defines: its selection never returns one, and its gather would fail on it.  The
+functions here raise ValueError for such an index.
 
 Decoding (the page's inference mode trims the windows to the last position and attends
 the new tokens against the whole key cache): ``q_pos0`` places the query rows at
 positions q_pos0 .. q_pos0 + Sq - 1 of a key / value cache of Skv rows; every token's
-slots are as above, taken from the cache.
+slots are as above, taken from the cache.  The page's inference-mode loop is garbled in
+the extracted text, so this reading is pinned only to itself (equality with the
+full-sequence rows): parity unpinned against the page.
 """
 from __future__ import annotations
 
@@ -43,18 +46,21 @@ def _flat(x):
 
 def candidate_positions(t: int, sel_row, *, window: int, block_size: int, seqlen=None):
     """(positions, is_zero_pad) of token t's candidate slots, in list order.  With
-    ``seqlen`` given, rows at or past it (a block index past the last block) are zero pads."""
+    ``seqlen`` given, a selected block with rows at or past it raises ValueError (the
+    page's gather of item indices is only defined inside the sequence)."""
     pos, pad = [], []
     for w in range(window):
         p = t - window + 1 + w
         pos.append(max(p, 0))
         pad.append(p < 0)
     for c in sel_row:
+        c = int(c)
+        if seqlen is not None and c >= 0 and (c + 1) * block_size > seqlen:
+            raise ValueError(f"selected block {c} has rows past the end of the {seqlen}-row key sequence")
         for r in range(block_size):
-            p = int(c) * block_size + r
-            past = seqlen is not None and p >= seqlen
-            pos.append(0 if (p < 0 or past) else p)
-            pad.append(past)
+            p = c * block_size + r
+            pos.append(0 if p < 0 else p)
+            pad.append(False)
     return np.asarray(pos, dtype=np.int64), np.asarray(pad, dtype=bool)
 
 

@@ -143,18 +143,22 @@ def test_sparse_full_size_sampled(gpu):
     np.testing.assert_allclose(l.cpu().numpy()[:, toks], l_r[:, toks], rtol=1e-3, atol=0)
 
 
-def test_sparse_handmade_selection(gpu):
-    """Selections block_select never produces: duplicates within a token's list, several
-    -1 entries (token 0 for every row), indices past the last block (zero rows), random
-    order, shared and unshared blocks across the 32-token groups."""
-    B, S, E, bs, n, W = 2, 224, 512, 32, 6, 20
-    q, k, v = rnd((B, S, E), 41), rnd((B, S, E), 42), rnd((B, S, E), 43)
-    g = np.random.default_rng(44)
+def handmade_selection(B, S, bs, n, seed):
+    """Selections block_select never produces, all inside the sequence: duplicates within a
+    token's list, several -1 entries (token 0 for every row), random order, blocks at or
+    after the token's own, shared and unshared blocks across the 32-token groups."""
+    g = np.random.default_rng(seed)
     nblk = S // bs
-    sel = g.integers(-1, nblk + 3, size=(B, S, n)).astype(np.int32)
+    sel = g.integers(-1, nblk, size=(B, S, n)).astype(np.int32)
     sel[:, ::5, 1] = sel[:, ::5, 0]                 # duplicates
     sel[:, ::7, :3] = -1                            # several -1
-    sel[:, 3::11, 4] = nblk + 7                     # past the end
+    return sel
+
+
+def test_sparse_handmade_selection(gpu):
+    B, S, E, bs, n, W = 2, 224, 512, 32, 6, 20
+    q, k, v = rnd((B, S, E), 41), rnd((B, S, E), 42), rnd((B, S, E), 43)
+    sel = handmade_selection(B, S, bs, n, 44)
     o, m, l = gpu.attn_fwd_sparse(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(sel).to(DEV),
                                   window=W, block_size=bs)
     torch.cuda.synchronize()
@@ -162,6 +166,39 @@ def test_sparse_handmade_selection(gpu):
     check_close("o", o, o_r, "bf16")
     np.testing.assert_allclose(m.cpu().numpy(), m_r, atol=1e-3, rtol=0)
     np.testing.assert_allclose(l.cpu().numpy(), l_r, rtol=1e-3, atol=0)
+
+
+def test_sparse_past_the_end_contract(gpu):
+    """A selected block past the last one is outside the page's definition (its selection
+    never returns one; the oracle rejects it).  The kernels' contract for it: the
+    range-checked reads see zero rows, nothing faults, every output is finite, and the
+    result equals the same call on a sequence extended by one block of zero rows (query
+    and dO rows zero too) with those indices pointing at that block.  Kernel against
+    kernel, no oracle."""
+    B, S, E, bs, n, W = 2, 224, 512, 32, 6, 20
+    nblk = S // bs
+    q, k, v, do = rnd((B, S, E), 141), rnd((B, S, E), 142), rnd((B, S, E), 143), rnd((B, S, E), 144)
+    sel = handmade_selection(B, S, bs, n, 145)
+    sel[:, 3::11, 4] = nblk + 7                     # past the end
+    sel[:, 5::13, 2] = nblk
+    z = torch.zeros((B, bs, E), dtype=torch.bfloat16)
+    q2, k2, v2, do2 = (torch.cat([x, z], 1) for x in (q, k, v, do))
+    sel2 = np.concatenate([np.where(sel >= nblk, nblk, sel), np.full((B, bs, n), -1, np.int32)], 1)
+    sel2 = np.ascontiguousarray(sel2.astype(np.int32))
+    # forward
+    idx, idx2 = torch.from_numpy(sel).to(DEV), torch.from_numpy(sel2).to(DEV)
+    o, m, l = gpu.attn_fwd_sparse(q.to(DEV), k.to(DEV), v.to(DEV), idx, window=W, block_size=bs)
+    o2, m2, l2 = gpu.attn_fwd_sparse(q2.to(DEV), k2.to(DEV), v2.to(DEV), idx2, window=W, block_size=bs)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(m).all() and torch.isfinite(l).all()
+    check_close("o vs zero-extended", o, o2[:, :S], "bf16")
+    np.testing.assert_allclose(l.cpu().numpy(), l2[:, :S].cpu().numpy(), rtol=1e-5, atol=0)
+    # backward: the extra rows have q = dO = 0, so they pass nothing to dk, dv of the rest
+    dq, dk, dv = sparse_grads(gpu, q, k, v, do, sel, W)
+    dq2, dk2, dv2 = sparse_grads(gpu, q2, k2, v2, do2, sel2, W)
+    for nm, a_, b_ in (("dq", dq, dq2), ("dk", dk, dk2), ("dv", dv, dv2)):
+        assert torch.isfinite(a_.float()).all(), nm
+        check_close(f"{nm} vs zero-extended", a_, b_[:, :S], "bf16")
 
 
 # ---------------------------------------------------------------- backward (sel_block 32)
@@ -188,16 +225,11 @@ def test_sparse_backward_small(gpu, B, S, n, W):
 
 
 def test_sparse_backward_handmade_selection(gpu):
-    """Duplicates, several -1 entries (all collected by row 0), indices past the last
-    block (no gradient), tokens listing blocks at or after their own."""
+    """Duplicates, several -1 entries (all collected by row 0), tokens listing blocks at or
+    after their own."""
     B, S, E, bs, n, W = 2, 224, 512, 32, 6, 20
     q, k, v, do = rnd((B, S, E), 45), rnd((B, S, E), 46), rnd((B, S, E), 47), rnd((B, S, E), 48)
-    g = np.random.default_rng(49)
-    nblk = S // bs
-    sel = g.integers(-1, nblk + 3, size=(B, S, n)).astype(np.int32)
-    sel[:, ::5, 1] = sel[:, ::5, 0]
-    sel[:, ::7, :3] = -1
-    sel[:, 3::11, 4] = nblk + 7
+    sel = handmade_selection(B, S, bs, n, 49)
     dq, dk, dv = sparse_grads(gpu, q, k, v, do, sel, W)
     dq_r, dk_r, dv_r = sparse.sparse_attention_backward(q, k, v, sel, do, window=W, block_size=bs)
     check_close("dq", dq, dq_r, "bf16")

@@ -162,25 +162,23 @@ def test_sparse_equals_materialised_candidate_list():
     np.testing.assert_array_equal(o_s[:, toks], o[:, toks])
 
 
-def test_sparse_block_past_the_end_reads_zero_rows():
-    """A block index past the last block reads zero rows: the same result as appending a
-    block of zero keys and values to the sequence and selecting it in range."""
-    B, S, E, bs, W = 1, 64, 8, 8, 4
+def test_sparse_block_past_the_end_is_rejected():
+    """The page's gather reads item indices inside the sequence only (its selection never
+    returns a block past the last one): the oracle raises on such an index, forward and
+    backward, and on a partial last block; the last full block is accepted."""
+    B, S, E, bs, W = 1, 68, 8, 8, 4                # 8 full blocks and 4 rows of a ninth
     q, k, v = rnd((B, S, E), 18), rnd((B, S, E), 19), rnd((B, S, E), 20)
     nblk = S // bs
     sel = np.full((B, S, 3), -1, dtype=np.int64)
     sel[0, :, 1] = 2
-    sel[0, :, 2] = nblk + 5                        # past the end
-    o, m, l = sparse.sparse_attention(q, k, v, sel, window=W, block_size=bs)
-    z = torch.zeros((B, bs, E), dtype=q.dtype)
-    k2, v2 = torch.cat([k, z], 1), torch.cat([v, z], 1)
-    q2 = torch.cat([q, z], 1)
-    sel2 = sel.copy()
-    sel2[0, :, 2] = nblk                           # the appended zero block, in range
-    sel2 = np.concatenate([sel2, np.full((B, bs, 3), -1, dtype=np.int64)], 1)
-    o2, m2, l2 = sparse.sparse_attention(q2, k2, v2, sel2, window=W, block_size=bs)
-    np.testing.assert_allclose(o, o2[:, :S], atol=1e-14, rtol=0)
-    np.testing.assert_allclose(l, l2[:, :S], rtol=1e-14, atol=0)
+    sel[0, :, 2] = nblk - 1                        # the last full block: defined
+    sparse.sparse_attention(q, k, v, sel, window=W, block_size=bs)
+    for bad in (nblk, nblk + 5):                   # partial block, past the end
+        sel[0, 10, 2] = bad
+        with pytest.raises(ValueError, match="past the end"):
+            sparse.sparse_attention(q, k, v, sel, window=W, block_size=bs)
+        with pytest.raises(ValueError, match="past the end"):
+            sparse.sparse_attention_backward(q, k, v, sel, q, window=W, block_size=bs)
 
 
 @pytest.mark.parametrize("W,n", [(8, 3), (5, 2)])
