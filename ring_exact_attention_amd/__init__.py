@@ -339,9 +339,13 @@ def block_select(q, k, *, block_size=32, top_n=8, workspace=None, out=None, q_po
     need = int(lib().block_select_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", device=q.device)
     idx = out if out is not None else torch.empty((B, S, top_n), dtype=torch.int32, device=q.device)
+    _need(idx, "out", torch.int32, q.device)
+    if idx.shape != (B, S, top_n):
+        raise ValueError(f"out must be [B, Sq, top_n] = {(B, S, top_n)}")
     _check(lib().block_select(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(idx), _ptr(workspace),
-                              workspace.numel(), _stream(q)))
+                              workspace.numel() * workspace.element_size(), _stream(q)))
     return idx
 
 

@@ -1045,11 +1045,7 @@ static void launch_pre(const BwdArgs& a, hipStream_t stream) {
 // tile, or with dropout (whose words cost more loads per key in 32-key tiles), the 8-wave
 // ping-pong is ahead.
 static bool dq_use_w4(const BwdArgs& a) {
-#ifdef REA_DQ_WAVES
-  return REA_DQ_WAVES == 4;
-#else
   return (a.lo_off > -kPosInf && a.hi_off < kPosInf) || (a.G < 8 && a.drop == nullptr);
-#endif
 }
 
 hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {

@@ -558,11 +558,7 @@ int fwd_tile_rows(int dtype) { return dtype == 0 ? 32 : 128; }
 // second workgroup hides the load of one item's Q and the store of its O behind the
 // other's tiles (measured ahead up to windows of about 1000 keys, level at 1500-3000).
 static bool fwd_use_w4(const FwdArgs& a) {
-#ifdef REA_FWD_WAVES
-  return REA_FWD_WAVES == 4;
-#else
   return a.lo_off > -kPosInf && a.hi_off < kPosInf && (long long)a.hi_off - a.lo_off < 1024;
-#endif
 }
 
 template <int D, int DV, int EX>

@@ -324,13 +324,14 @@ def test_ring_sim_full_size(gpu):
     torch.cuda.synchronize()
     heads = [0, 7, 15]
     o_r, m_r, l_r = dense.forward(q, k, v, heads=heads, **oracle_kw(w))
-    check_close("o", o[:, :, heads], o_r[:, :, heads], "bf16")
+    blk = w.kv_block
+    check_close("o", o[:, :, heads], o_r[:, :, heads], "bf16", blocks=blk)
     check_stats(m[:, heads], l[:, heads], m_r[:, heads], l_r[:, heads], "bf16")
     bh = [3, 12]
     dq_r, dk_r, dv_r = dense.backward(q, k, v, do, heads=bh, **oracle_kw(w))
-    check_close("dq", dq[:, :, bh], dq_r[:, :, bh], "bf16")
-    check_close("dk", dk[:, :, bh], dk_r[:, :, bh], "bf16")      # G = 1: kv head = q head
-    check_close("dv", dv[:, :, bh], dv_r[:, :, bh], "bf16")
+    check_close("dq", dq[:, :, bh], dq_r[:, :, bh], "bf16", blocks=blk)
+    check_close("dk", dk[:, :, bh], dk_r[:, :, bh], "bf16", blocks=blk)      # G = 1: kv head = q head
+    check_close("dv", dv[:, :, bh], dv_r[:, :, bh], "bf16", blocks=blk)
 
 
 def unpack_bits(words, n):
@@ -409,19 +410,24 @@ def test_mla_full_size(gpu):
 
 
 def test_long_context_sampled_rows(gpu):
-    """B1 S131072 Hq32 Hkv8 D128 causal, 32 virtual blocks of 4096: sampled rows."""
+    """B1 S131072 Hq32 Hkv8 D128 causal, 32 virtual blocks of 4096: 16 rows of every
+    virtual block (its first and last row and 14 drawn at random, 512 in all) on all 32 q
+    heads, with the relative Frobenius bound per (head, virtual block) -- the outputs of
+    late rows are small (inputs x 0.5), so the element bound alone would be vacuous."""
     w, q, k, v, _ = full_inputs("long_causal_s131072", with_dout=False)
     o, m, l = gpu.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), **launch_kw(w))
     torch.cuda.synchronize()
     g = np.random.default_rng(3)
     blk = w.kv_block
-    rows = sorted(set([0, 1, blk - 1, blk, 17 * blk + 5, w.seqlen - 1] +
-                      list(g.integers(0, w.seqlen, 10))))
-    heads = [0, 13, 31]
-    o_r, m_r, l_r = dense.forward(q, k, v, rows=rows, heads=heads, **oracle_kw(w))
-    check_close("o", o[:, rows][:, :, heads], o_r[:, rows][:, :, heads], "bf16")
-    check_stats(m[:, heads][:, :, rows], l[:, heads][:, :, rows], m_r[:, heads][:, :, rows],
-                l_r[:, heads][:, :, rows], "bf16")
+    rows = []
+    for c in range(w.seqlen // blk):
+        rows += [c * blk, c * blk + blk - 1] + list(c * blk + 1 + g.choice(blk - 2, 14, replace=False))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    assert rows.size == 512
+    o_r, m_r, l_r = dense.forward(q, k, v, rows=rows, row_block=16, **oracle_kw(w))
+    ri = torch.from_numpy(rows)
+    check_close("o", o[:, ri.to(o.device)].cpu(), o_r[:, rows], "bf16", blocks=blk, rows=rows)
+    check_stats(m[:, :, ri.to(m.device)], l[:, :, ri.to(l.device)], m_r[:, :, rows], l_r[:, :, rows], "bf16")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
