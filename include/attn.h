@@ -261,6 +261,26 @@ int attn_bwd(const attn_params* params, const void* q, const void* k, const void
 size_t attn_bwd_workspace_bytes(const attn_params* params);
 
 /*
+ * attn_bwd_noalloc -- attn_bwd (dense mode) for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, result and flags as attn_bwd, without the workspace: the
+ * scratch lives in a static device array of ATTN_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds from the library's load until the process ends.  Nothing is
+ * allocated.
+ *   * Params whose attn_bwd_workspace_bytes exceeds ATTN_NOALLOC_SCRATCH_BYTES return
+ *     ATTN_ERR_WORKSPACE (nothing launched); use attn_bwd with a workspace for them.
+ *   * All calls on one GPU share that GPU's array, which keeps the last call's contents
+ *     (nothing in it needs to start at zero: every call writes what it reads, except that
+ *     ATTN_BWD_REUSE_STATS reads the statistics left by the previous call on this GPU).
+ *     Calls that overlap on one GPU (other streams, other threads) race on it.
+ *   * Sparse mode (sel_idx != NULL) returns ATTN_ERR_UNSUPPORTED.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_bwd_noalloc(const attn_params* params, const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* m, const float* l,
+                     void* dq, void* dk, void* dv, void* stream);
+
+/*
  * block_select -- exact top-n block selection ("AnnAttention", select_block, with the
  * approximate index replaced by exact inner products):
  *   mean_c = average of key rows c*bs .. c*bs+bs-1 (full blocks), in fp64;

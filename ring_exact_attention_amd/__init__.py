@@ -10,6 +10,7 @@ call raises.
 Entry points (names as in the C ABI):
   attn_fwd(q, k, v, ...)                 -> (o, m, l)      or (acc, m, l) without finalize
   attn_bwd(q, k, v, o, dout, m, l, ...)  -> (dq, dk, dv)
+  attn_bwd_noalloc(q, k, v, o, dout, m, l, out=(dq, dk, dv), ...)  (static scratch)
   block_select(q, k, block_size, top_n)  -> idx int32 [B, S, top_n]
   attn_fwd_sparse(q, k, v, idx, ...)     -> (o, m, l)      (attn_fwd with sel_idx)
   attn_bwd_sparse(q, k, v, idx, o, dout, m, l, ...) -> (dq, dk, dv)  (attn_bwd with sel_idx)
@@ -97,6 +98,7 @@ _SIGNATURES = {
     "attn_fwd": (ctypes.c_int, [ctypes.POINTER(AttnParams), _P, _P, _P, _P, _P, _P, _P, _P]),
     "attn_bwd": (ctypes.c_int, [ctypes.POINTER(AttnParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P, ctypes.c_size_t, _P]),
+    "attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AttnParams)]),
     "attn_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(AttnParams)]),
     "block_select": (ctypes.c_int, [ctypes.POINTER(SelectParams), _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -312,6 +314,38 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
                           _ptr(l), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(q)))
     return (dq, dk, dv, dsink) if learnable else (dq, dk, dv)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20     # ATTN_NOALLOC_SCRATCH_BYTES of attn.h
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, m, l, *, out, causal=True, window=(-1, -1), scale=None,
+                     query_chunk=0, key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, skip_dq=False,
+                     skip_dkdv=False, reuse_stats=False, softmax_type="vanilla", sink=None, dsink=None,
+                     bias=None, dropout=None):
+    """attn_bwd without a workspace (the library's static scratch; see attn.h): the caller
+    passes the outputs ``out = (dq, dk, dv)`` (and ``dsink`` for a learnable sink), so this
+    call allocates nothing.  Returns ``out``."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, q.dtype, q.device)
+    _need(m, "m", torch.float32, q.device)
+    _need(l, "l", torch.float32, q.device)
+    dq, dk, dv = out
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _need(t, n, q.dtype, q.device)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
+    flags = ((ATTN_BWD_SKIP_DQ if skip_dq else 0) | (ATTN_BWD_SKIP_DKDV if skip_dkdv else 0) |
+             (ATTN_BWD_REUSE_STATS if reuse_stats else 0))
+    p = make_params(q, k, causal=causal, window=window, scale=scale, query_chunk=query_chunk,
+                    key_chunk=key_chunk, kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, flags=flags,
+                    head_dim_v=v.shape[3], softmax_type=softmax_type, sink=sink, bias=bias, dropout=dropout)
+    if dsink is not None:
+        _need(dsink, "dsink", torch.float32, q.device)
+        p.dsink = dsink.data_ptr()
+    _check(lib().attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(m),
+                                  _ptr(l), _ptr(dq), _ptr(dk), _ptr(dv), _stream(q)))
+    return out
 
 
 def _joint(x):

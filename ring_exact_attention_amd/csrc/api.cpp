@@ -337,6 +337,11 @@ int sparse_bwd(const attn_params* p, const void* q, const void* k, const void* v
 
 }  // namespace
 
+namespace rea {
+// Status reporting for entry points defined in other translation units.
+int report_error(int code, const char* msg) { return fail(code, msg); }
+}  // namespace rea
+
 extern "C" {
 
 const char* attn_last_error(void) { return g_err.c_str(); }

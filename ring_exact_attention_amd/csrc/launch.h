@@ -51,6 +51,9 @@ inline int select_splits(int B, int S, int q_pos0, int bs, int nblk, int top_n) 
   return ns < 1 ? 1 : (int)ns;
 }
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
+
+// Sets this thread's attn_last_error() message and returns `code`.
+int report_error(int code, const char* msg);
 hipError_t launch_sparse_bwd(const SparseBwdArgs& a, hipStream_t stream);
 
 }  // namespace rea

@@ -304,3 +304,21 @@ def test_success_clears_error(lib):
     assert lib.attn_last_error() != b""
     assert fwd_status(lib, params(batch=0)) == rea.ATTN_OK
     assert lib.attn_last_error() == b""
+
+
+def test_noalloc_rejects_params_beyond_the_static_scratch(lib):
+    """attn_bwd_noalloc checks the scratch its params need against the static array before
+    it touches the device (so this runs without a GPU)."""
+    p = params(batch=8, seqlen_q=65536, seqlen_kv=65536, num_q_heads=32, num_kv_heads=8)
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(p))
+    assert need > rea.NOALLOC_SCRATCH_BYTES
+    dummy = ctypes.c_void_p(256)
+    st = lib.attn_bwd_noalloc(ctypes.byref(p), *([dummy] * 10), None)
+    assert st == rea.ATTN_ERR_WORKSPACE
+    assert b"static" in lib.attn_last_error()
+    bad = params(num_q_heads=6, num_kv_heads=4)                 # invalid params: attn_bwd's message
+    assert lib.attn_bwd_noalloc(ctypes.byref(bad), *([dummy] * 10), None) == rea.ATTN_ERR_INVALID_ARG
+    assert b"multiple" in lib.attn_last_error()
+    sp = params()
+    sp.sel_idx = 256
+    assert lib.attn_bwd_noalloc(ctypes.byref(sp), *([dummy] * 10), None) == rea.ATTN_ERR_UNSUPPORTED
