@@ -32,6 +32,9 @@
  *   * One batch element's slice of any tensor (S x H x D elements) must stay under
  *     4 GiB: the kernels address each slice with 32-bit byte offsets.  Larger slices
  *     return ATTN_ERR_UNSUPPORTED.
+ *   * Testing knob: with ATTN_REVERSE_WORKGROUPS=1 in the environment (read at every
+ *     call), every kernel takes the tasks of its grid in reverse order.  Results are
+ *     bitwise the same: no workgroup depends on another's progress or write order.
  */
 #ifndef RING_EXACT_ATTENTION_ATTN_H_
 #define RING_EXACT_ATTENTION_ATTN_H_

@@ -9,6 +9,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -68,11 +69,20 @@ static_assert(offsetof(attn_params, drop_mask) == ATTN_PARAMS_V3_SIZE,
 // The caller's params in the current layout: an earlier version's struct reads with its
 // missing fields zero (ATTN_SOFTMAX_VANILLA, no bias, no dropout).  Other sizes pass through for the
 // size check.
+// First field of every params struct: read with memcpy, since a caller's struct of an
+// unknown or older version may be shorter than the current type.
+uint32_t struct_size_of(const void* p) {
+  uint32_t n = 0;
+  memcpy(&n, p, sizeof n);
+  return n;
+}
+
+// The size field is read with memcpy: an older caller's struct is shorter than
+// attn_params, so no member of it is accessed through the current type.
 const attn_params* current_layout(const attn_params* p, attn_params& tmp) {
-  if (!p || (p->struct_size != ATTN_PARAMS_V1_SIZE && p->struct_size != ATTN_PARAMS_V2_SIZE &&
-             p->struct_size != ATTN_PARAMS_V3_SIZE))
-    return p;
-  const size_t n = p->struct_size;
+  if (!p) return p;
+  const uint32_t n = struct_size_of(p);
+  if (n != ATTN_PARAMS_V1_SIZE && n != ATTN_PARAMS_V2_SIZE && n != ATTN_PARAMS_V3_SIZE) return p;
   memset(&tmp, 0, sizeof tmp);
   memcpy(&tmp, p, n);
   tmp.struct_size = sizeof(attn_params);
@@ -81,9 +91,9 @@ const attn_params* current_layout(const attn_params* p, attn_params& tmp) {
 
 int check_dense(const attn_params* p, bool bwd, Problem& r) {
   if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
-  if (p->struct_size != sizeof(attn_params))
+  if (struct_size_of(p) != sizeof(attn_params))
     return fail(ATTN_ERR_INVALID_ARG, fmt("params->struct_size is %lld, this library expects %lld",
-                                          (long long)p->struct_size, (long long)sizeof(attn_params)));
+                                          (long long)struct_size_of(p), (long long)sizeof(attn_params)));
   if (p->dtype != ATTN_BF16 && p->dtype != ATTN_F32)
     return fail(ATTN_ERR_UNSUPPORTED, fmt("dtype %lld is not supported (ATTN_BF16 or ATTN_F32)", p->dtype));
   if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_kv < 0)
@@ -192,6 +202,13 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   return ATTN_OK;
 }
 
+// Testing knob: with ATTN_REVERSE_WORKGROUPS=1 in the environment every kernel takes its
+// grid's tasks in reverse order (results must not change; see wg_index in common.h).
+int reverse_order() {
+  const char* e = getenv("ATTN_REVERSE_WORKGROUPS");
+  return e && e[0] == '1' ? 1 : 0;
+}
+
 int check_ptr(const void* ptr, const char* name) {
   if (!ptr) return fail(ATTN_ERR_INVALID_ARG, std::string(name) + " is NULL");
   if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, std::string(name) + " must be 16-byte aligned");
@@ -222,7 +239,7 @@ int hip_status(hipError_t e) {
 
 // Checks shared by the gathered block-sparse forward and backward (sel_idx != NULL).
 int check_sparse(const attn_params* p) {
-  if (p->struct_size != sizeof(attn_params))
+  if (struct_size_of(p) != sizeof(attn_params))
     return fail(ATTN_ERR_INVALID_ARG, "params->struct_size does not match this library");
   if (p->head_dim_v != 0 && p->head_dim_v != p->head_dim)
     return fail(ATTN_ERR_UNSUPPORTED, "sparse mode needs head_dim_v = 0 (the joint embedding)");
@@ -261,6 +278,7 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
   if (work && ((uintptr_t)work & (kAlign - 1)) != 0)
     return fail(ATTN_ERR_INVALID_ARG, "the sparse forward's workspace (acc) must be 256-byte aligned");
   rea::SparseArgs a{};
+  a.rev_order = reverse_order();
   a.part = work;
   a.q = q;
   a.k = k;
@@ -310,6 +328,7 @@ int sparse_bwd(const attn_params* p, const void* q, const void* k, const void* v
       (st = check_ptr(dv, "dv")))
     return st;
   rea::SparseBwdArgs a{};
+  a.rev_order = reverse_order();
   a.q = q;
   a.k = k;
   a.v = v;
@@ -352,7 +371,8 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
              float* l, float* acc, void* stream) {
   attn_params tmp;
   const attn_params* p = current_layout(p_in, tmp);
-  if (p && p->sel_idx) return sparse_fwd(p, q, k, v, o, m, l, acc, stream);
+  if (p && struct_size_of(p) == sizeof(attn_params) && p->sel_idx)
+    return sparse_fwd(p, q, k, v, o, m, l, acc, stream);
   Problem r;
   int st = check_dense(p, false, r);
   if (st) return st;
@@ -363,6 +383,7 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
   if ((r.carry_in || !r.finalize) && (st = check_ptr(acc, "acc (needed by ATTN_CARRY_IN / ATTN_NO_FINALIZE)")))
     return st;
   rea::FwdArgs a{};
+  a.rev_order = reverse_order();
   a.q = q;
   a.k = k;
   a.v = v;
@@ -411,7 +432,7 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
 size_t attn_fwd_workspace_bytes(const attn_params* p_in) {
   attn_params tmp;
   const attn_params* p = current_layout(p_in, tmp);
-  if (!p || !p->sel_idx) return 0;
+  if (!p || struct_size_of(p) != sizeof(attn_params) || !p->sel_idx) return 0;
   const std::string saved = g_err;
   if (check_sparse(p) != ATTN_OK) return 0;
   g_err = saved;
@@ -424,9 +445,9 @@ size_t attn_fwd_workspace_bytes(const attn_params* p_in) {
 size_t attn_bwd_workspace_bytes(const attn_params* p_in) {
   attn_params tmp;
   const attn_params* p = current_layout(p_in, tmp);
-  if (p && p->sel_idx) {
+  if (p && struct_size_of(p) == sizeof(attn_params) && p->sel_idx) {
     const std::string saved = g_err;
-    if (p->struct_size != sizeof(attn_params) || check_sparse(p) != ATTN_OK) return 0;
+    if (struct_size_of(p) != sizeof(attn_params) || check_sparse(p) != ATTN_OK) return 0;
     g_err = saved;
     return sparse_bwd_workspace(p);
   }
@@ -445,7 +466,7 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
              void* workspace, size_t workspace_bytes, void* stream) {
   attn_params tmp;
   const attn_params* p = current_layout(p_in, tmp);
-  if (p && p->sel_idx)
+  if (p && struct_size_of(p) == sizeof(attn_params) && p->sel_idx)
     return sparse_bwd(p, q, k, v, o, dout, m, l, dq, dk, dv, workspace, workspace_bytes, stream);
   Problem r;
   int st = check_dense(p, true, r);
@@ -468,6 +489,7 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
   if (r.Skv > 0 && ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")))) return st;
   if (r.Skv > 0 && do_dkdv && ((st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))) return st;
   rea::BwdArgs a{};
+  a.rev_order = reverse_order();
   a.q = q;
   a.k = k;
   a.v = v;
@@ -527,7 +549,8 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
 // The caller's select params in the current layout (version 1: seqlen_kv = seqlen,
 // q_pos0 = 0).  Other sizes pass through for the size check.
 const select_params* current_select_layout(const select_params* p, select_params& tmp) {
-  if (!p || p->struct_size != SELECT_PARAMS_V1_SIZE) return p;
+  if (!p) return p;
+  if (struct_size_of(p) != SELECT_PARAMS_V1_SIZE) return p;
   memset(&tmp, 0, sizeof tmp);
   memcpy(&tmp, p, SELECT_PARAMS_V1_SIZE);
   tmp.struct_size = sizeof(select_params);
@@ -540,7 +563,7 @@ int select_kv_rows(const select_params* p) { return p->seqlen_kv > 0 ? p->seqlen
 size_t block_select_workspace_bytes(const select_params* p_in) {
   select_params tmp;
   const select_params* p = current_select_layout(p_in, tmp);
-  if (!p || p->struct_size != sizeof(select_params) || p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 ||
+  if (!p || struct_size_of(p) != sizeof(select_params) || p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 ||
       p->embed <= 0 || p->block_size <= 0)
     return 0;
   const size_t nblk = (size_t)(select_kv_rows(p) / p->block_size);
@@ -556,7 +579,7 @@ int block_select(const select_params* p_in, const void* q, const void* k, int32_
   select_params tmp;
   const select_params* p = current_select_layout(p_in, tmp);
   if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
-  if (p->struct_size != sizeof(select_params))
+  if (struct_size_of(p) != sizeof(select_params))
     return fail(ATTN_ERR_INVALID_ARG, "params->struct_size does not match this library");
   if (p->reserved != 0) return fail(ATTN_ERR_INVALID_ARG, "params->reserved must be 0");
   if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "block_select supports bf16 inputs");
@@ -583,6 +606,7 @@ int block_select(const select_params* p_in, const void* q, const void* k, int32_
   if (((uintptr_t)workspace & (kAlign - 1)) != 0)
     return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   rea::SelectArgs a{};
+  a.rev_order = reverse_order();
   a.q = q;
   a.k = k;
   a.idx = idx;

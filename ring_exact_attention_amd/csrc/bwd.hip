@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int LPR = D / EPC;               // lanes per row
   constexpr int RPB = 256 / LPR;             // rows per block
   const int tid = threadIdx.x;
-  const long long rowg = (long long)blockIdx.x * RPB + tid / LPR;   // row of [B, Sq, Hq]
+  const long long rowg = (long long)wg_index(a.rev_order) * RPB + tid / LPR;   // row of [B, Sq, Hq]
   const int sub = tid % LPR;
   const long long nrows = (long long)a.B * a.Sq * a.Hq;
   float part = 0.f;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
   __shared__ __attribute__((aligned(1024))) char lds[C::MAIN + C::NW * 32 * 4];
 
   int b, hg, qt;
-  map_task(blockIdx.x, a.n_qtiles, a.B, a.n_hg, a.Hkv, a.G >> a.gh_shift, a.xcd_groups, a.hi_off < kPosInf,
+  map_task(wg_index(a.rev_order), a.n_qtiles, a.B, a.n_hg, a.Hkv, a.G >> a.gh_shift, a.xcd_groups, a.hi_off < kPosInf,
            b, hg, qt);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   // G q heads of the group are shared out over ns workgroups (G / ns heads each), which
   // write fp32 partial dk, dv that bwd_dkdv_reduce_kernel sums.
   int b, hv, kt;
-  map_kv_task(blockIdx.x, a.n_ktiles, a.B, a.Hkv * a.kv_splits, a.xcd_kv_groups, false, b, hv, kt);
+  map_kv_task(wg_index(a.rev_order), a.n_ktiles, a.B, a.Hkv * a.kv_splits, a.xcd_kv_groups, false, b, hv, kt);
   const int hkv = hv / a.kv_splits, split = hv - hkv * a.kv_splits;
   const int g_per = a.G / a.kv_splits;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -822,8 +822,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 // order (so the result is bitwise reproducible), rounded once to bf16.  4 elements per
 // thread; n_k and n_v are multiples of 4 (head dims are multiples of 32).
 __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* part, int ns, long long n_k,
-                                                              long long n_v, __bf16* dk, __bf16* dv) {
-  const long long i = 4 * ((long long)blockIdx.x * 256 + threadIdx.x);
+                                                              long long n_v, __bf16* dk, __bf16* dv, int rev) {
+  const long long i = 4 * ((long long)wg_index(rev) * 256 + threadIdx.x);
   if (i >= n_k + n_v) return;
   const bool is_k = i < n_k;
   const float* src = is_k ? part + i : part + ns * n_k + (i - n_k);
@@ -846,7 +846,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* part,
 // a fixed strided subset and the workgroup a fixed tree, so the result is reproducible.
 __global__ __launch_bounds__(256) void bwd_sink_grad_kernel(BwdArgs a) {
   __shared__ float red[256];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int h = wg_index(a.rev_order), tid = threadIdx.x;
   const float zz = a.sink[h] * kLog2e;
   float acc = 0.f;
   for (int b = 0; b < a.B; ++b) {
@@ -870,7 +870,7 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
   constexpr int BM = 128, BN = 32;
   __shared__ float sK[BN][D + 1], sV[BN][DV + 1];
   int b, hq, qt;
-  map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, 0, false, b, hq, qt);
+  map_task(wg_index(a.rev_order), a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, 0, false, b, hq, qt);
   const int hkv = hq / a.G, tid = threadIdx.x;
   const int row = qt * BM + tid;
   const bool row_ok = row < a.Sq;
@@ -944,7 +944,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
   constexpr int BK = 128, BQ = 32;
   __shared__ float sQ[BQ][D + 1], sG[BQ][DV + 1], sL[BQ], sDv[BQ];
   int b, hkv, kt;
-  map_kv_task(blockIdx.x, a.n_ktiles, a.B, a.Hkv, 0, false, b, hkv, kt);
+  map_kv_task(wg_index(a.rev_order), a.n_ktiles, a.B, a.Hkv, 0, false, b, hkv, kt);
   const int tid = threadIdx.x;
   const int key = kt * BK + tid;
   const bool key_ok = key < a.Skv;
@@ -1090,7 +1090,7 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
         const unsigned blocks = (unsigned)((nk + nv + 1023) / 1024);            \
         hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3(blocks), dim3(256), 0,  \
                            stream, a.dkv_part, a.kv_splits, nk, nv,             \
-                           (__bf16*)a.dk, (__bf16*)a.dv);                       \
+                           (__bf16*)a.dk, (__bf16*)a.dv, a.rev_order);          \
       }                                                                         \
     }                                                                           \
   } while (0)

@@ -24,6 +24,7 @@ constexpr int kPosInf = 1 << 30;   // "unbounded" key offset (positions are vali
 
 // Forward kernel arguments (dense path).
 struct FwdArgs {
+  int rev_order;      // nonzero: workgroups take the grid's tasks in reverse order (see wg_index)
   const void* q;
   const void* k;
   const void* v;
@@ -66,6 +67,7 @@ struct FwdArgs {
 
 // Backward kernel arguments (dense path).
 struct BwdArgs {
+  int rev_order;      // nonzero: workgroups take the grid's tasks in reverse order (see wg_index)
   const void* q;
   const void* k;
   const void* v;
@@ -106,6 +108,7 @@ struct BwdArgs {
 };
 
 struct SelectArgs {
+  int rev_order;      // nonzero: workgroups take the grid's tasks in reverse order (see wg_index)
   const void* q;
   const void* k;
   int32_t* idx;
@@ -118,6 +121,7 @@ struct SelectArgs {
 };
 
 struct SparseArgs {
+  int rev_order;      // nonzero: workgroups take the grid's tasks in reverse order (see wg_index)
   const void* q;
   const void* k;
   const void* v;
@@ -135,6 +139,7 @@ struct SparseArgs {
 
 // Backward of the gathered block-sparse attention.
 struct SparseBwdArgs {
+  int rev_order;      // nonzero: workgroups take the grid's tasks in reverse order (see wg_index)
   const void* q;
   const void* k;
   const void* v;
@@ -153,6 +158,14 @@ struct SparseBwdArgs {
 };
 
 // ---------------------------------------------------------------- device helpers
+
+// Task index of this workgroup: its id in dispatch order, or (rev != 0) counted from the
+// end of the grid.  No workgroup depends on another's progress or on the order of their
+// writes, so a launch with the order reversed must give bitwise the same results; tests
+// run both (the host sets rev from the ATTN_REVERSE_WORKGROUPS environment variable).
+__device__ __forceinline__ int wg_index(int rev) {
+  return rev ? (int)(gridDim.x - 1u - blockIdx.x) : (int)blockIdx.x;
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
 
   int b, hg, qt;
-  map_task(blockIdx.x, a.n_qtiles, a.B, a.n_hg, a.Hkv, a.G >> a.gh_shift, a.xcd_groups, a.hi_off < kPosInf,
+  map_task(wg_index(a.rev_order), a.n_qtiles, a.B, a.n_hg, a.Hkv, a.G >> a.gh_shift, a.xcd_groups, a.hi_off < kPosInf,
            b, hg, qt);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdArgs a) {
   __shared__ float sK[BN][D + 1];
   __shared__ float sV[BN][DV + 1];
   int b, hq, qt;
-  map_task(blockIdx.x, a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, 0, false, b, hq, qt);
+  map_task(wg_index(a.rev_order), a.n_qtiles, a.B, a.Hq, a.Hkv, a.G, 0, false, b, hq, qt);
   const int hkv = hq / a.G;
   const int tid = threadIdx.x;
   const int row = qt * BM + tid;
@@ -587,11 +587,6 @@ static void launch_fwd_bf16(FwdArgs a, bool w4, hipStream_t stream) {
     case 3: launch_fwd_ex<D, DV, 3>(a, w4, grid, block, stream); break;
     default: launch_fwd_ex<D, DV, 0>(a, w4, grid, block, stream);
   }
-}
-
-bool head_dims_supported(int dtype, int D, int Dv) {
-  if (dtype == 0) return (D == Dv && (D == 32 || D == 64 || D == 128)) || (D == 128 && Dv == 64);
-  return (D == Dv && (D == 32 || D == 64)) || (D == 64 && Dv == 32);
 }
 
 hipError_t launch_fwd(int dtype, const FwdArgs& args, hipStream_t stream) {

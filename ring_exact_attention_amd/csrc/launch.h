@@ -7,7 +7,10 @@
 namespace rea {
 
 // dtype: 0 = bf16, 1 = fp32.  Head dims (q/k D, v Dv) with kernels built for them.
-bool head_dims_supported(int dtype, int D, int Dv);
+inline bool head_dims_supported(int dtype, int D, int Dv) {
+  if (dtype == 0) return (D == Dv && (D == 32 || D == 64 || D == 128)) || (D == 128 && Dv == 64);
+  return (D == Dv && (D == 32 || D == 64)) || (D == 64 && Dv == 32);
+}
 hipError_t launch_fwd(int dtype, const FwdArgs& a, hipStream_t stream);
 int fwd_tile_rows(int dtype);
 

@@ -22,7 +22,7 @@ namespace rea {
 // does not change the mean.
 __global__ __launch_bounds__(256) void block_means_kernel(SelectArgs a) {
   __shared__ double part[256 * 8];
-  const int c = blockIdx.x % a.nblk, b = blockIdx.x / a.nblk;
+  const int wg = wg_index(a.rev_order), c = wg % a.nblk, b = wg / a.nblk;
   const __bf16* kp = (const __bf16*)a.k + ((size_t)b * a.Skv + (size_t)c * a.bs) * a.E;
   double* mp = a.means + ((size_t)b * a.nblk + c) * a.E;
   const int cpr = a.E / 8;                               // 16-byte chunks per row (8 .. 128)
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
 
   const int first = a.q_pos0 / BS;
   const int nqb = (a.q_pos0 + a.S - 1) / BS - first + 1;
-  const int ns = a.nsplit, split = blockIdx.x % ns, qb = blockIdx.x / ns;
+  const int ns = a.nsplit, wg = wg_index(a.rev_order), split = wg % ns, qb = wg / ns;
   const int i = first + qb % nqb, b = qb / nqb;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int p0 = max(i * BS, a.q_pos0);                      // first query position of the block
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
 // below top_n are kept and written ascending by index after the -1 padding.
 __global__ __launch_bounds__(256) void block_select_merge_kernel(SelectArgs a) {
   const int lane = threadIdx.x & 63;
-  const long long tok = (long long)blockIdx.x * 4 + wave_id();
+  const long long tok = (long long)wg_index(a.rev_order) * 4 + wave_id();
   if (tok >= (long long)a.B * a.S) return;               // the whole wavefront
   const int n = a.top_n, ne = a.nsplit * n;
   double s = -INFINITY;

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int nqb = (a.S + a.tpw - 1) / a.tpw;
-  const int split = blockIdx.x % a.ksplit, grp_id = blockIdx.x / a.ksplit;
+  const int wg = wg_index(a.rev_order), split = wg % a.ksplit, grp_id = wg / a.ksplit;
   const int b = grp_id / nqb, t0 = (grp_id % nqb) * a.tpw;
   const int tend = min(t0 + a.tpw, a.S);                      // this workgroup's tokens: [t0, tend)
   const int n = a.top_n, bs = a.sel_block, W = a.window;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
 // embedding columns per thread): O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
 // M = max_s m_s; a token whose shares saw nothing keeps O = 0, m = -inf, l = 0.
 __global__ __launch_bounds__(256) void sparse_combine_kernel(SparseArgs a) {
-  const size_t tok = blockIdx.x;                               // b * S + token
+  const size_t tok = wg_index(a.rev_order);                    // b * S + token
   const float* pp = a.part + tok * a.ksplit * (kSpE + 4);
   float M = -INFINITY;
   for (int s = 0; s < a.ksplit; ++s) M = fmaxf(M, pp[s * (kSpE + 4) + kSpE]);
