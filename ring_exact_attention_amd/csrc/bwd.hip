@@ -485,11 +485,14 @@ struct BwdKVCfg {
   using GL = TileLayout<DV, kBothRead>;           // dO tile: the same with the v head dim
   using VL = TileLayout<DV, kRowRead>;            // V tile: row operands
   static constexpr int DC = D / 8, DCV = DV / 8;  // 16-byte chunks per Q / dO row
-  static constexpr int NCH = BQ * DC;             // 16-byte chunks of Q per step
-  static constexpr int NCHV = BQ * DCV;           // ... of dO
-  static constexpr int CPT = (NCH + 255) / 256;   // Q chunks per thread
-  static constexpr int CPTV = (NCHV + 255) / 256; // dO chunks per thread
   static constexpr int VCPT = BK * DCV / 256;     // 16-byte chunks of the V tile per thread
+  // Step tiles are copied straight into LDS: 16-byte slot s of a tile is row
+  // 4 (s / GS) + (s % GS) / PS, chunk (s % GS) % PS; padding slots are skipped.
+  static constexpr int QPS = QL::PITCH / 8, QGS = QL::GROUP / 8, QSL = QL::elems(BQ) / 8;
+  static constexpr int GPS = GL::PITCH / 8, GGS = GL::GROUP / 8, GSL = GL::elems(BQ) / 8;
+  static constexpr int QI = (QSL + 63) / 64, GI = (GSL + 63) / 64;   // 64-lane copies per tile
+  static constexpr int NI = (QI + GI + 3) / 4;                       // per wave
+  static constexpr int QB = QI * 1024, GB = GI * 1024;               // bytes per tile buffer
 };
 
 // EX: extra logit terms compiled in -- bit 0 an additive bias, bit 1 a dropout mask.
@@ -498,8 +501,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   using C = BwdKVCfg<D, DV>;
   constexpr bool BIAS = (EX & 1) != 0, DROP = (EX & 2) != 0;
   static_assert(DV <= D, "the v head dim may not exceed the q/k head dim");
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][C::QL::elems(C::BQ)];
-  __shared__ __attribute__((aligned(16))) __bf16 sG[2][C::GL::elems(C::BQ)];
+  // Q and dO tiles of a step, two buffers each (the next step's rows are copied in while
+  // the current step runs)
+  __shared__ __attribute__((aligned(1024))) char sQG[2 * C::QB + 2 * C::GB];
   __shared__ __attribute__((aligned(16))) __bf16 sVk[C::VL::elems(C::BK)];   // this workgroup's V rows
   __shared__ __attribute__((aligned(16))) float sLse[2][C::BQ];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BQ];
@@ -586,32 +590,38 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const bool wave_on = kw0 < a.Skv;
   const int w_klast = kw0 + 31;
 
-  u32x4 qbuf[C::CPT], gbuf[C::CPTV];
-  uint32_t qgo[C::CPT], ggo[C::CPTV];              // global byte offsets within a step's rows
-  int qlo[C::CPT], glo[C::CPTV];                   // LDS element offsets
+  // Step tile copies: instruction n fills bytes [1024n, 1024n + 1024) of the Q buffer
+  // (n < QI) or of the dO buffer (n - QI); lane l carries 16-byte slot 64n' + l.  Wave w
+  // issues instructions w, w + 4, ...
+  uint32_t cpo[C::NI];
+  bool cpv[C::NI];
 #pragma unroll
-  for (int u = 0; u < C::CPT; ++u) {
-    const int c = min(tid + 256 * u, C::NCH - 1), i = c / C::DC, ch = c % C::DC;
-    qgo[u] = (uint32_t)i * q_rs_b + 16u * ch;
-    qlo[u] = C::QL::idx(i, 8 * ch);
-  }
-#pragma unroll
-  for (int u = 0; u < C::CPTV; ++u) {
-    const int c = min(tid + 256 * u, C::NCHV - 1), i = c / C::DCV, ch = c % C::DCV;
-    ggo[u] = (uint32_t)i * g_rs_b + 16u * ch;
-    glo[u] = C::GL::idx(i, 8 * ch);
+  for (int i = 0; i < C::NI; ++i) {
+    const int n = wave + 4 * i;
+    const bool is_q = n < C::QI;
+    const int sl = 64 * (is_q ? n : n - C::QI) + lane;
+    const int gs = is_q ? C::QGS : C::GGS, ps = is_q ? C::QPS : C::GPS;
+    const int grp = sl / gs, rem = sl - grp * gs, k4 = rem / ps, ch = rem - k4 * ps;
+    const int r = 4 * grp + k4;
+    cpv[i] = n < C::QI + C::GI && k4 < 4 && ch < (is_q ? C::DC : C::DCV) && r < C::BQ;
+    cpo[i] = (uint32_t)r * (is_q ? q_rs_b : g_rs_b) + 16u * ch;
   }
   float lbuf = 0.f;
   uint32_t dbuf = 0u;
-  auto load_step = [&](int hq_, int qs) {
+  auto load_step = [&](int hq_, int qs, int buf) {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc_at(
         qbase, q_bytes, __builtin_amdgcn_readfirstlane((uint32_t)qs * q_rs_b + (uint32_t)hq_ * D * 2));
     const __amdgpu_buffer_rsrc_t rg = make_rsrc_at(
         gbase, g_bytes, __builtin_amdgcn_readfirstlane((uint32_t)qs * g_rs_b + (uint32_t)hq_ * DV * 2));
 #pragma unroll
-    for (int u = 0; u < C::CPT; ++u) qbuf[u] = buf_load16(rq, qgo[u], 0);
-#pragma unroll
-    for (int u = 0; u < C::CPTV; ++u) gbuf[u] = buf_load16(rg, ggo[u], 0);
+    for (int i = 0; i < C::NI; ++i) {
+      const int n = wave + 4 * i;
+      if (n < C::QI) {
+        if (cpv[i]) dma16(rq, sQG + buf * C::QB + 1024 * n, cpo[i]);
+      } else if (n < C::QI + C::GI) {
+        if (cpv[i]) dma16(rg, sQG + 2 * C::QB + buf * C::GB + 1024 * (n - C::QI), cpo[i]);
+      }
+    }
     if (tid < 2 * C::BQ) {
       const int i = tid & (C::BQ - 1), row = qs + i;
       const size_t st = ((size_t)b * a.Hq + hq_) * a.Sq + row;
@@ -625,13 +635,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       }
     }
   };
+  // After this wave's copies of a step have landed: its row statistics (and dropout words).
   auto store_step = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u)
-      if (tid + 256 * u < C::NCH) *(u32x4*)&sQ[buf][qlo[u]] = qbuf[u];
-#pragma unroll
-    for (int u = 0; u < C::CPTV; ++u)
-      if (tid + 256 * u < C::NCHV) *(u32x4*)&sG[buf][glo[u]] = gbuf[u];
     if (tid < C::BQ) sLse[buf][tid] = lbuf;
     else if (tid < 2 * C::BQ) sD[buf][tid - C::BQ] = lbuf;
     if constexpr (DROP) {
@@ -657,7 +662,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   int hq = 0, qs = 0, rend = 0;
   bool have = next_step(hq, qs, rend);
   if (have) {
-    load_step(hq, qs);
+    load_step(hq, qs, 0);
+    wait_vmcnt0();
     store_step(0);
     if (BIAS && !bias_rows) bkey = *bias_ptr(hq);
   }
@@ -692,12 +698,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         }
       }
     }
-    if (nhave) load_step(nhq, nqs);
+    if (nhave) load_step(nhq, nqs, cur ^ 1);
     if (BIAS && !bias_rows && nhave) bkey = *bias_ptr(nhq);
     if (!empty) {
       const bool full = dmin >= a.lo_off && dmax <= a.hi_off && qs + C::BQ <= qe;
-      const __bf16* qt_ = sQ[cur];
-      const __bf16* gt_ = sG[cur];
+      const __bf16* qt_ = (const __bf16*)(sQG + cur * C::QB);
+      const __bf16* gt_ = (const __bf16*)(sQG + 2 * C::QB + cur * C::GB);
       f32x16 dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -762,7 +768,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         }
       }
     }
-    if (nhave) store_step(cur ^ 1);
+    if (nhave) {
+      wait_vmcnt0();                 // this wave's copies of the next step have landed
+      store_step(cur ^ 1);
+    }
     __syncthreads();
     cur ^= 1;
     hq = nhq;
