@@ -74,9 +74,17 @@ enum {
    * and passes dk, dv along the ring), so an owner may want only its share. */
   ATTN_BWD_SKIP_DQ = 8u,       /* do not compute dq (dq may be NULL)                  */
   ATTN_BWD_SKIP_DKDV = 16u,    /* do not compute dk, dv (both may be NULL)            */
-  ATTN_BWD_REUSE_STATS = 32u   /* the workspace already holds D and the log-sum-exp
+  ATTN_BWD_REUSE_STATS = 32u,  /* the workspace already holds D and the log-sum-exp
                                   written by an earlier attn_bwd call with the same
                                   params, o, dout, m and l: do not recompute them     */
+  /* attn_bwd only: dq, dk, dv are fp32 buffers (same shapes, whatever the element type of
+   * q) and this call adds its gradients into them, as does dsink.  One ring step of the
+   * backward pass ("bpt.py", _ring_attention_bwd carries fp32 dq, dk, dv through its scan:
+   * dq stays with the query block while dk, dv travel with the key block and gather the
+   * contributions of every query block they meet): call attn_bwd once per (query block,
+   * key block) pair with that pair's q_pos0 / kv_pos0, adding into the query block's dq and
+   * the key block's dk, dv. */
+  ATTN_BWD_ACCUMULATE = 64u
 };
 
 /* attn_params.softmax_type ("JAX: Single-GPU Attention with TransformerEngine", "Other
@@ -126,7 +134,7 @@ typedef struct attn_params {
                                   own position and descending (mod the block count).  */
   uint32_t flags;              /* attn_fwd: ATTN_CARRY_IN | ATTN_NO_FINALIZE;
                                   attn_bwd: ATTN_BWD_SKIP_DQ | ATTN_BWD_SKIP_DKDV |
-                                  ATTN_BWD_REUSE_STATS                                  */
+                                  ATTN_BWD_REUSE_STATS | ATTN_BWD_ACCUMULATE            */
   /* Gathered block-sparse mode ("AnnAttention", faiss_block_attention): when sel_idx
    * is non-NULL, attn_fwd attends each token to a zero-padded window of
    * sparse_window keys ending at the token, followed by the sel_block rows of each of
@@ -155,8 +163,10 @@ typedef struct attn_params {
   const float* sink;           /* LEARNABLE: [Hq] fp32 device, sink logits z_h          */
   float* dsink;                /* attn_bwd with LEARNABLE: [Hq] fp32 device output
                                   dL/dz_h summed over the batch and this call's query
-                                  rows, written (not accumulated) by calls that compute
-                                  dq; NULL = not wanted                                 */
+                                  rows, written by calls that compute dq (added into
+                                  with ATTN_BWD_ACCUMULATE; it depends on the query
+                                  rows only, so pass it on one call per query block);
+                                  NULL = not wanted                                     */
   /* Additive logit bias ("bpt.py": ring_attention / blockwise_attn take a bias that
    * broadcasts to (batch, heads, q_len, kv_len) and is added to the scaled logits;
    * the page passes no gradient to it, and neither does attn_bwd).  fp32 device, in the
@@ -240,7 +250,8 @@ size_t attn_fwd_workspace_bytes(const attn_params* params);
  *
  *   q, k, v, o, dout [in] as in attn_fwd (o = attn_fwd's output, dout = dL/do).
  *   m, l             [in] fp32 [B, Hq, Sq] written by attn_fwd.
- *   dq [out] [B, Sq, Hq, D]; dk, dv [out] [B, Skv, Hkv, D] (element type of q).
+ *   dq [out] [B, Sq, Hq, D]; dk, dv [out] [B, Skv, Hkv, D] (element type of q; fp32 and
+ *                    added into with ATTN_BWD_ACCUMULATE).
  *   workspace        device scratch of at least attn_bwd_workspace_bytes(params)
  *                    bytes (256-byte aligned); its contents are overwritten.
  * flags: 0 or a combination of the ATTN_BWD_* flags.  The result is bitwise

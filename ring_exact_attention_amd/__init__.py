@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, -1, -2, -3, -4
 ATTN_BF16, ATTN_F32 = 0, 1
 ATTN_CARRY_IN, ATTN_NO_FINALIZE = 1, 2
-ATTN_BWD_SKIP_DQ, ATTN_BWD_SKIP_DKDV, ATTN_BWD_REUSE_STATS = 8, 16, 32
+ATTN_BWD_SKIP_DQ, ATTN_BWD_SKIP_DKDV, ATTN_BWD_REUSE_STATS, ATTN_BWD_ACCUMULATE = 8, 16, 32, 64
 ATTN_SOFTMAX_VANILLA, ATTN_SOFTMAX_OFF_BY_ONE, ATTN_SOFTMAX_LEARNABLE = 0, 1, 2
 _SOFTMAX_TYPES = {"vanilla": ATTN_SOFTMAX_VANILLA, "off_by_one": ATTN_SOFTMAX_OFF_BY_ONE,
                   "learnable": ATTN_SOFTMAX_LEARNABLE}
@@ -275,14 +275,16 @@ def bwd_workspace_bytes(q, k, **kw) -> int:
 def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None, query_chunk=0,
              key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, workspace=None, out=None,
              skip_dq=False, skip_dkdv=False, reuse_stats=False, softmax_type="vanilla", sink=None,
-             dsink=None, bias=None, dropout=None):
+             dsink=None, bias=None, dropout=None, accumulate=False):
     """Gradients (dq, dk, dv) of attn_fwd's output for upstream gradient dout.
 
     ``skip_dq`` / ``skip_dkdv`` compute only part of them (the skipped outputs are left
     untouched); ``reuse_stats`` takes D and the log-sum-exp from ``workspace`` as left
     by an earlier call with the same inputs.  With ``softmax_type="learnable"`` the
     gradient of the sink logits is returned as a fourth tensor (fp32 [Hq]; written by
-    calls that compute dq).
+    calls that compute dq).  ``accumulate``: one ring step of the backward pass -- ``out``
+    holds fp32 dq, dk, dv (and ``dsink`` fp32) that this call adds its gradients into
+    (zeros are allocated when they are not given).
     """
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _need(t, n, q.dtype, q.device)
@@ -296,7 +298,7 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
               kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, head_dim_v=Dv, softmax_type=softmax_type,
               sink=sink, bias=bias, dropout=dropout)
     flags = ((ATTN_BWD_SKIP_DQ if skip_dq else 0) | (ATTN_BWD_SKIP_DKDV if skip_dkdv else 0) |
-             (ATTN_BWD_REUSE_STATS if reuse_stats else 0))
+             (ATTN_BWD_REUSE_STATS if reuse_stats else 0) | (ATTN_BWD_ACCUMULATE if accumulate else 0))
     p = make_params(q, k, flags=flags, **kw)
     need = int(lib().attn_bwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
@@ -309,7 +311,16 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
             dsink = torch.zeros((Hq,), dtype=torch.float32, device=q.device)
         _need(dsink, "dsink", torch.float32, q.device)
         p.dsink = dsink.data_ptr()
-    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    if accumulate:
+        f32 = torch.float32
+        dq, dk, dv = out if out is not None else (torch.zeros_like(q, dtype=f32), torch.zeros_like(k, dtype=f32),
+                                                  torch.zeros_like(v, dtype=f32))
+        for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+            _need(t, n, f32, q.device)
+            if t.shape != ref.shape:
+                raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
+    else:
+        dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     _check(lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(m),
                           _ptr(l), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(q)))

@@ -151,7 +151,7 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
         return fail(ATTN_ERR_INVALID_ARG, "drop_stride entries must be in [0, 2^40]");
   }
   const uint32_t fwd_flags = ATTN_CARRY_IN | ATTN_NO_FINALIZE;
-  const uint32_t bwd_flags = ATTN_BWD_SKIP_DQ | ATTN_BWD_SKIP_DKDV | ATTN_BWD_REUSE_STATS;
+  const uint32_t bwd_flags = ATTN_BWD_SKIP_DQ | ATTN_BWD_SKIP_DKDV | ATTN_BWD_REUSE_STATS | ATTN_BWD_ACCUMULATE;
   if (p->flags & ~(fwd_flags | bwd_flags)) return fail(ATTN_ERR_INVALID_ARG, "unknown bits in flags");
   if (bwd && (p->flags & fwd_flags))
     return fail(ATTN_ERR_INVALID_ARG, "attn_bwd flags: only the ATTN_BWD_* flags apply");
@@ -541,6 +541,7 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
   a.xcd_kv_groups = r.dtype == ATTN_BF16 ? xcd_groups(r.B, r.Hkv * a.kv_splits) : 0;
   a.dkv_part = a.kv_splits > 1 ? (float*)((char*)workspace + 2 * align_up(n > 0 ? n : 1)) : nullptr;
   a.stages = (do_pre ? 1 : 0) | (do_dq ? 2 : 0) | (do_dkdv ? 4 : 0);
+  a.accumulate = (p->flags & ATTN_BWD_ACCUMULATE) ? 1 : 0;
   a.dsink = r.Sq > 0 ? r.dsink : nullptr;
   if ((long long)a.n_qtiles * r.B * r.Hq >= (1LL << 31)) return fail(ATTN_ERR_UNSUPPORTED, "problem too large");
   return hip_status(rea::launch_bwd(r.dtype, a, (hipStream_t)stream));

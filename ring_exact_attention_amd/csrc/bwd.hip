@@ -442,6 +442,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
     }
   }
 
+  if (a.accumulate) {
+    // fp32 dq of the caller, added into: lane (li, lh) holds dq[row][32db + 8g + 4lh .. +3]
+    if (row_ok) {
+      float* dqp = (float*)a.dq + ((size_t)b * a.Sq + row) * q_rs + (size_t)hq * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4* p = (f32x4*)(dqp + 32 * db + 8 * g + 4 * lh);
+          f32x4 v = *p;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += acc[db][4 * g + e] * a.scale;
+          *p = v;
+        }
+    }
+    return;
+  }
   // dQ through LDS (this wave's rows at 2D + 16 bytes in the idle stages; all reads of the
   // stages ended at the loop's last barrier), then stored as whole rows.
   {
@@ -803,6 +820,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) w[e] = dv[db][4 * g + e];
         *(f32x4*)(pv + 32 * db + 8 * g + 4 * lh) = w;
       }
+  } else if (key_ok && a.accumulate) {
+    // fp32 dk, dv of the caller, added into
+    float* kop = (float*)a.dk + koff;
+    float* vop = (float*)a.dv + voff;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4* p = (f32x4*)(kop + 32 * db + 8 * g + 4 * lh);
+        f32x4 w = *p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] += dk[db][4 * g + e] * a.scale;
+        *p = w;
+      }
+#pragma unroll
+    for (int db = 0; db < C::DBV; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4* p = (f32x4*)(vop + 32 * db + 8 * g + 4 * lh);
+        f32x4 w = *p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] += dv[db][4 * g + e];
+        *p = w;
+      }
   } else if (key_ok) {
     __bf16* kop = (__bf16*)a.dk + koff;
     __bf16* vop = (__bf16*)a.dv + voff;
@@ -828,10 +869,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 }
 
 // Sum of the kv_splits fp32 partials of dk (n_k elements) and dv (n_v elements), in split
-// order (so the result is bitwise reproducible), rounded once to bf16.  4 elements per
-// thread; n_k and n_v are multiples of 4 (head dims are multiples of 32).
+// order (so the result is bitwise reproducible), rounded once to bf16 (or, accumulating,
+// added into the caller's fp32 dk, dv).  4 elements per thread; n_k and n_v are multiples
+// of 4 (head dims are multiples of 32).
 __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* part, int ns, long long n_k,
-                                                              long long n_v, __bf16* dk, __bf16* dv, int rev) {
+                                                              long long n_v, void* dk, void* dv, int rev,
+                                                              int accumulate) {
   const long long i = 4 * ((long long)wg_index(rev) * 256 + threadIdx.x);
   if (i >= n_k + n_v) return;
   const bool is_k = i < n_k;
@@ -843,10 +886,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* part,
 #pragma unroll
     for (int e = 0; e < 4; ++e) s[e] += t[e];
   }
+  if (accumulate) {          // fp32 outputs of the caller, added into
+    f32x4* p = (f32x4*)(is_k ? (float*)dk + i : (float*)dv + (i - n_k));
+    f32x4 o = *p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] += s[e];
+    *p = o;
+    return;
+  }
   u32x2 w;
   w[0] = pack_bf16x2(s[0], s[1]);
   w[1] = pack_bf16x2(s[2], s[3]);
-  *(u32x2*)(is_k ? dk + i : dv + (i - n_k)) = w;
+  *(u32x2*)(is_k ? (__bf16*)dk + i : (__bf16*)dv + (i - n_k)) = w;
 }
 
 // Gradient of the learnable sink logits: dz_h = -sum over (b, i) of P_sink,i * D_i, with
@@ -868,7 +919,7 @@ __global__ __launch_bounds__(256) void bwd_sink_grad_kernel(BwdArgs a) {
     if (tid < s) red[tid] += red[tid + s];
     __syncthreads();
   }
-  if (tid == 0) a.dsink[h] = red[0];
+  if (tid == 0) a.dsink[h] = a.accumulate ? a.dsink[h] + red[0] : red[0];
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -944,7 +995,7 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a) {
   if (row_ok) {
     float* op = (float*)a.dq + qoff;
 #pragma unroll
-    for (int d = 0; d < D; ++d) op[d] = acc[d] * a.scale;
+    for (int d = 0; d < D; ++d) op[d] = (a.accumulate ? op[d] : 0.f) + acc[d] * a.scale;
   }
 }
 
@@ -1029,9 +1080,9 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdArgs a) {
   }
   if (key_ok) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) ((float*)a.dk)[koff + d] = dk[d] * a.scale;
+    for (int d = 0; d < D; ++d) ((float*)a.dk)[koff + d] = (a.accumulate ? ((float*)a.dk)[koff + d] : 0.f) + dk[d] * a.scale;
 #pragma unroll
-    for (int d = 0; d < DV; ++d) ((float*)a.dv)[voff + d] = dv[d];
+    for (int d = 0; d < DV; ++d) ((float*)a.dv)[voff + d] = (a.accumulate ? ((float*)a.dv)[voff + d] : 0.f) + dv[d];
   }
 }
 
@@ -1099,7 +1150,7 @@ hipError_t launch_bwd(int dtype, const BwdArgs& args, hipStream_t stream) {
         const unsigned blocks = (unsigned)((nk + nv + 1023) / 1024);            \
         hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3(blocks), dim3(256), 0,  \
                            stream, a.dkv_part, a.kv_splits, nk, nv,             \
-                           (__bf16*)a.dk, (__bf16*)a.dv, a.rev_order);          \
+                           a.dk, a.dv, a.rev_order, a.accumulate);              \
       }                                                                         \
     }                                                                           \
   } while (0)

@@ -102,6 +102,7 @@ struct BwdArgs {
                                // G / kv_splits q heads (bf16 only; 1 = no split)
   float* dkv_part;             // kv_splits > 1: fp32 partials [ns,B,Skv,Hkv,D] ++ [ns,B,Skv,Hkv,Dv]
   int stages;                  // bit 0: D/LSE pre-pass, bit 1: dq, bit 2: dk/dv
+  int accumulate;              // dq, dk, dv (and dsink) are fp32 and this call adds into them
   // bf16 dq workgroup shape (set by the launcher), as in FwdArgs; fused_stats: the dq
   // kernel computes D and the LSE itself (and stores them for the dk/dv pass).
   int gh, gh_shift, rows_wg, n_hg, fused_stats;

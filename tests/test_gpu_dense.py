@@ -451,6 +451,58 @@ def test_step_api_carry_equals_single_call(gpu, dt):
     check_close("o (one call)", o1, o_r, dt)
 
 
+RING_BWD = [
+    # id, dtype, S per block, Hq, Hkv, D, Dv, softmax
+    ("bf16_d128_gqa2", "bf16", 192, 4, 2, 128, 128, "vanilla"),
+    ("bf16_mla_split_dkdv_sink", "bf16", 160, 8, 2, 128, 64, "learnable"),
+    ("f32_d64", "f32", 96, 4, 2, 64, 64, "vanilla"),
+]
+
+
+@pytest.mark.parametrize("case", RING_BWD, ids=[c[0] for c in RING_BWD])
+def test_ring_backward_steps_accumulate(gpu, case):
+    """The backward ring on one GPU ("bpt.py", _ring_attention_bwd): two query blocks and
+    two key blocks of a causal sequence, one attn_bwd call per (query block, key block) pair
+    in ring order with ATTN_BWD_ACCUMULATE, adding into the query block's fp32 dq and the key
+    block's fp32 dk, dv (the sink gradient once per query block).  Equal to the oracle and
+    to the single call over the whole sequence."""
+    name, dt, S, Hq, Hkv, D, Dv, softmax = case
+    t = tdtype(dt)
+    seed = zlib.crc32(name.encode()) % 10000
+    B, N = 1, 2
+    q, k, v, do = (rnd((B, N * S, Hq, D), seed, t), rnd((B, N * S, Hkv, D), seed + 1, t),
+                   rnd((B, N * S, Hkv, Dv), seed + 2, t), rnd((B, N * S, Hq, Dv), seed + 3, t))
+    z = rnd((Hq,), seed + 4, torch.float32) if softmax == "learnable" else None
+    sk = dict(softmax_type=softmax, sink=z.to(DEV) if z is not None else None)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, causal=True, **sk)
+    single = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, causal=True, **sk)
+    blk = lambda x, i: x[:, i * S:(i + 1) * S].contiguous()
+    f32 = torch.float32
+    dq = [torch.zeros((B, S, Hq, D), dtype=f32, device=DEV) for _ in range(N)]
+    dk = [torch.zeros((B, S, Hkv, D), dtype=f32, device=DEV) for _ in range(N)]
+    dv = [torch.zeros((B, S, Hkv, Dv), dtype=f32, device=DEV) for _ in range(N)]
+    dz = torch.zeros((Hq,), dtype=f32, device=DEV)
+    for i in range(N):                                   # query block i = ring member i
+        mi, li = m[:, :, i * S:(i + 1) * S].contiguous(), l[:, :, i * S:(i + 1) * S].contiguous()
+        for idx in range(N):                             # ring step: key block (i - idx) mod N
+            j = (i - idx) % N
+            extra = dict(dsink=dz) if (z is not None and idx == 0) else {}
+            gpu.attn_bwd(blk(qd, i), blk(kd, j), blk(vd, j), blk(o, i), blk(dod, i), mi, li, causal=True,
+                         q_pos0=i * S, kv_pos0=j * S, accumulate=True, out=(dq[i], dk[j], dv[j]), **sk, **extra)
+    torch.cuda.synchronize()
+    dq_all, dk_all, dv_all = torch.cat(dq, 1), torch.cat(dk, 1), torch.cat(dv, 1)
+    ref = dense.backward(q, k, v, do, causal=True, sink=z)
+    check_close("dq (ring steps)", dq_all, ref[0], dt, blocks=S)
+    check_close("dk (ring steps)", dk_all, ref[1], dt, blocks=S)
+    check_close("dv (ring steps)", dv_all, ref[2], dt, blocks=S)
+    for nm, a_, b_ in (("dq", dq_all, single[0]), ("dk", dk_all, single[1]), ("dv", dv_all, single[2])):
+        check_close(f"{nm} (ring steps vs one call)", a_, b_.double().cpu(), dt)
+    if z is not None:
+        np.testing.assert_allclose(dz.cpu().numpy(), ref[3], atol=2e-2, rtol=2e-2)
+        np.testing.assert_allclose(dz.cpu().numpy(), single[3].cpu().numpy(), atol=1e-4, rtol=1e-4)
+
+
 def test_step_api_carry_with_bias(gpu):
     """Ring steps with a bias: each step gets the slice of the bias for its key block
     (a strided view), and the carried result equals one call with the whole bias, and
