@@ -7,9 +7,13 @@ A step is one forward and one backward pass of the whole attention over one batc
 synthetic seeded input resident in HBM.  The default workload is one GPU's share of a
 causal ring: B1, S8192, 16 heads of 128, bf16, 8 virtual key blocks of 1024 visited
 in ring order.  Prints ONE JSON line: whole-step TFLOP/s over the algorithmic flops
-(4*D per visible pair forward, 10*D backward), per-kernel HIP-event timings, the
-roofline of the dominant kernel, and the oracle timed on a bounded sample on the host
-cores as a CPU baseline.
+(4*D per visible pair forward, 10*D backward), per-kernel HIP-event timings (mean,
+median, min), the rooflines of the dominant kernel, of the forward and of the whole
+backward, and the oracle timed on a bounded sample on the host cores as a CPU baseline.
+The default run also measures the other workloads under "workloads", each with its own
+rooflines: GQA-16 + sliding window (fwd + bwd, HBM-bound; the 256 MiB MALL is flushed by
+writing 512 MiB before every step, outside the timed events), the long-context causal
+forward, and the block-sparse selection + gathered attention (MALL flushed too).
 
 Only one GPU is used: a run asking for more exits with a message.
 """
@@ -28,6 +32,8 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 + % of MFMA peak at 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+PEAK_FP64_TFLOPS = 78.6          # MI355X fp64 (MFMA), published
+DEFAULT_WORKLOAD = "ring_sim_causal_s8192"
 
 
 def kernel_source_sha():
@@ -105,15 +111,22 @@ def cpu_baseline(w, q, k, v, do, budget_s):
                       f"at full length S={w.seqlen}; TFLOP/s over the same algorithmic flops as the GPU"}
 
 
-def time_segments(torch, segs, steps, warmup, stream):
-    """Run warmup + timed steps of the segment list; per-segment mean ms from HIP events."""
+def time_segments(torch, segs, steps, warmup, stream, flush=None):
+    """Run warmup + timed steps of the segment list (each step runs every segment in order).
+    Returns per-segment mean ms (HIP events on the launch stream), the wall time of the timed
+    steps, and per-segment lists of per-step ms.  ``flush`` (the MALL flush of HBM-bound
+    workloads) runs before every step, outside the events."""
     for _ in range(warmup):
+        if flush is not None:
+            flush()
         for _, fn in segs:
             fn()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(segs) + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
     for s in range(steps):
+        if flush is not None:
+            flush()
         ev = events[s]
         ev[0].record(stream)
         for i, (_, fn) in enumerate(segs):
@@ -121,11 +134,24 @@ def time_segments(torch, segs, steps, warmup, stream):
             ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    seg_ms = {name: 0.0 for name, _ in segs}
-    for ev in events:
-        for i, (name, _) in enumerate(segs):
-            seg_ms[name] += ev[i].elapsed_time(ev[i + 1])
-    return {n: t / steps for n, t in seg_ms.items()}, wall
+    per = {name: [ev[i].elapsed_time(ev[i + 1]) for ev in events] for i, (name, _) in enumerate(segs)}
+    seg_ms = {n: sum(v) / len(v) for n, v in per.items()}
+    return seg_ms, wall, per
+
+
+def stats_us(ms_list):
+    """mean / median / min of per-step times (ms) in microseconds."""
+    v = sorted(ms_list)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"mean": round(sum(v) / n * 1e3, 2), "median": round(med * 1e3, 2), "min": round(v[0] * 1e3, 2)}
+
+
+def mall_flusher(torch, dev, nbytes=512 << 20):
+    """Writes a 512 MiB buffer: evicts the inputs of the previous step from the 256 MiB MALL
+    (and the L2s) so that an HBM-bound step reads them from HBM again."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return lambda: buf.zero_()
 
 
 def copy_calibration(torch, dev, args):
@@ -133,8 +159,8 @@ def copy_calibration(torch, dev, args):
     n = args.copy_bytes
     a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
-    seg_ms, _ = time_segments(torch, [("copy", lambda: b.copy_(a))], args.steps, args.warmup,
-                              torch.cuda.current_stream(dev))
+    seg_ms, _, _ = time_segments(torch, [("copy", lambda: b.copy_(a))], args.steps, args.warmup,
+                                 torch.cuda.current_stream(dev))
     print(json.dumps({"copy_bytes": n, "avg_us": round(seg_ms["copy"] * 1e3, 2),
                       "gbs": round(2 * n / (seg_ms["copy"] * 1e-3) / 1e9, 1)}), flush=True)
 
@@ -191,7 +217,9 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
         segs.append(("attn_bwd_sparse", lambda: rea.attn_bwd_sparse(
             qd, kd, vd, idx, o, dod, state["m"], state["l"], window=w.sparse_window, block_size=w.block_size,
             out=grads)))
-    seg_ms, wall = time_segments(torch, segs, args.steps, args.warmup, torch.cuda.current_stream(dev))
+    flush = mall_flusher(torch, dev)
+    seg_ms, wall, per = time_segments(torch, segs, args.steps, args.warmup, torch.cuda.current_stream(dev),
+                                      flush=flush)
     slots = w.sparse_window + w.top_n * w.block_size
     gathered = B * S * slots * E * 2 * 2
     f_sparse = B * S * slots * E * 4.0
@@ -221,7 +249,7 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
                  ("decode_attn", lambda: rea.attn_fwd_sparse(qn, kd, vd, idn, window=w.sparse_window,
                                                              block_size=w.block_size, out=on, q_pos0=S - T,
                                                              workspace=wsd))]
-        dms, _ = time_segments(torch, dsegs, args.steps, args.warmup, torch.cuda.current_stream(dev))
+        dms, _, _ = time_segments(torch, dsegs, args.steps, args.warmup, torch.cuda.current_stream(dev))
         step_us = (dms["decode_select"] + dms["decode_attn"]) * 1e3
         kernels["decode_step"] = {"new_tokens_per_sequence": T, "cache_rows": S,
                                   "select_us": round(dms["decode_select"] * 1e3, 2),
@@ -232,10 +260,15 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
         kernels["attn_bwd_sparse"] = {"avg_us": round(tb * 1e6, 2), "gathered_gb": round(2 * gathered / 1e9, 3),
                                       "gathered_gbs": round(2 * gathered / tb / 1e9, 1),
                                       "tflops": round(f_bwd / tb / 1e12, 2)}
-    # roofline of the dominant attention kernel (the gradient's when it is timed)
+    for n in per:
+        kernels.setdefault(n, {})["us"] = stats_us(per[n])
+    # roofline of the dominant attention kernel (the gradient's when it is timed): the
+    # forward on the MFMA work it executes (one 32-row step per window block and distinct
+    # selected block of each 32-token group), the gradient on its gathered bytes
     rk = "attn_bwd_sparse" if args.sparse_backward else "attn_fwd_sparse"
     rbytes = 2 * gathered if args.sparse_backward else gathered
     ach = rbytes / (seg_ms[rk] * 1e-3) / 1e9
+    f_exec, nsteps = sparse_union_flops(idx.cpu().numpy(), 32, w.sparse_window, w.block_size, E)
     out = {"metric": METRIC, "value": round((f_sparse + f_select + f_bwd) / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -247,10 +280,207 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
            "roofline": {"kernel": rk, "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                         "avg_us": round(seg_ms[rk] * 1e3, 2), "alg_bytes_per_launch": rbytes,
-                        "traffic": measured_traffic(w.name, rk)}}
+                        "traffic": measured_traffic(w.name, rk), "mall_flush": True}}
+    if not args.sparse_backward:
+        tf = f_exec / (seg_ms[rk] * 1e-3) / 1e12
+        traffic = measured_traffic(w.name, rk)
+        out["roofline"] = {"kernel": rk, "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                           "avg_us": round(seg_ms[rk] * 1e3, 2), "executed_flop_per_launch": f_exec,
+                           "union_steps": nsteps, "traffic": traffic, "mall_flush": True,
+                           "gathered_gbs_logical": round(ach, 1)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = sparse_cpu_baseline(w, q, k, v, idx.cpu().numpy(), args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def dense_measure(torch, rea, workloads, w, dev, steps, warmup, softmax="vanilla", bias="none", dropout=0.0,
+                  flush=None):
+    """Time one dense workload: forward, then (with a backward) dq with SKIP_DKDV and dk, dv
+    with SKIP_DQ | REUSE_STATS, each on the launch stream.  Returns timings (mean, median,
+    min per kernel and per step), algorithmic flops and compulsory bytes per launch, and the
+    rooflines of the forward, of the whole backward and of the dominant kernel."""
+    q, k, v, do = workloads.generate(w, with_dout=w.backward)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    dod = do.to(dev) if do is not None else None
+    del q, k, v, do
+    kw = dict(causal=w.causal, window=w.window, query_chunk=w.query_chunk, key_chunk=w.key_chunk,
+              kv_block=w.kv_block)
+    B, S, Hq, Hkv, D, Dv = w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, w.dv
+    sink = None
+    if softmax == "learnable":
+        sink = workloads.random_tensor((Hq,), w.seed + 100).to(dev)
+    kw.update(softmax_type=softmax, sink=sink)
+    if bias == "keypad":
+        bt = torch.zeros((B, 1, 1, S), dtype=torch.float32, device=dev)
+        bt[..., S - S // 16:] = float("-inf")
+        kw.update(bias=bt)
+    elif bias == "shared":
+        kw.update(bias=workloads.random_tensor((1, 1, S, S), w.seed + 101).to(dev))
+    if dropout > 0.0:
+        # drawn on the GPU head by head (the [S, S] draws of all heads would be large)
+        g = torch.Generator(device=dev).manual_seed(w.seed + 102)
+        words = torch.empty((1, Hq, S, (S + 31) // 32), dtype=torch.int32, device=dev)
+        for h in range(Hq):
+            words[0, h] = workloads.pack_bits(torch.rand((S, S), generator=g, device=dev) < dropout)
+        kw.update(dropout=words)
+    o = torch.empty((B, S, Hq, Dv), dtype=qd.dtype, device=dev)
+    m = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    segs = [("attn_fwd", lambda: rea.attn_fwd(qd, kd, vd, out=o, m=m, l=l, **kw))]
+    if w.backward:
+        grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
+        ws = torch.empty(max(rea.bwd_workspace_bytes(qd, kd, head_dim_v=Dv, **kw), 256), dtype=torch.uint8,
+                         device=dev)
+        bkw = dict(kw, dsink=torch.empty((Hq,), dtype=torch.float32, device=dev)) if sink is not None else kw
+        # dq also computes D and the LSE, which the dk/dv call takes from the workspace
+        segs.append(("bwd_dq", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
+                                                    skip_dkdv=True, **bkw)))
+        segs.append(("bwd_dkdv", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
+                                                      skip_dq=True, reuse_stats=True, **bkw)))
+    seg_ms, wall, per = time_segments(torch, segs, steps, warmup, torch.cuda.current_stream(dev), flush=flush)
+
+    pairs = visible_pairs(S, S, w.causal, w.window) * B * Hq
+    # Per visible pair: S = Q K^T costs 2D flops and each product with V or dO 2Dv
+    # (D = Dv except for the MLA head dims): forward 2D + 2Dv (= 4D); backward recompute
+    # of S (2D) and dP (2Dv), dV (2Dv), dK (2D), dQ (2D) = 6D + 4Dv (= 10D).
+    f_fwd = (2.0 * D + 2.0 * Dv) * pairs
+    f_bwd = (6.0 * D + 4.0 * Dv) * pairs if w.backward else 0.0
+    # Algorithmic flops per kernel launch: the dk/dv kernel does the recompute of S and
+    # dP plus dV and dK (4D + 4Dv per pair); the dq kernel's share is dQ (2D per pair),
+    # its own recompute being the cost of computing dq without atomics.
+    alg = {"attn_fwd": f_fwd, "bwd_dq": 2.0 * D * pairs, "bwd_dkdv": (4.0 * D + 4.0 * Dv) * pairs}
+    # Compulsory HBM bytes per launch (bf16 tensors read or written once, fp32 stats), and
+    # of the whole backward (q, o, dO, k, v read, dq, dk, dv written, m, l read).
+    esz = 2 if w.dtype == "bf16" else 4
+    qbytes, kbytes, stat = B * S * Hq * D * esz, B * S * Hkv * D * esz, B * Hq * S * 4
+    obytes, vbytes = B * S * Hq * Dv * esz, B * S * Hkv * Dv * esz
+    hbm = {"attn_fwd": qbytes + obytes + kbytes + vbytes + 2 * stat,
+           "bwd_dq": 2 * qbytes + 2 * obytes + kbytes + vbytes + 4 * stat,
+           "bwd_dkdv": qbytes + obytes + 2 * kbytes + 2 * vbytes + 2 * stat}
+    hbm_bwd = 2 * qbytes + 2 * obytes + 2 * kbytes + 2 * vbytes + 2 * stat
+    kernels = {}
+    for n, t in seg_ms.items():
+        kernels[n] = {"avg_us": round(t * 1e3, 2), "us": stats_us(per[n]), "alg_gflop": round(alg[n] / 1e9, 3),
+                      "tflops": round(alg[n] / (t * 1e-3) / 1e12, 2),
+                      "hbm_gbs": round(hbm[n] / (t * 1e-3) / 1e9, 1)}
+    step_per = [sum(per[n][i] for n in per) for i in range(steps)]
+    bwd_ms = sum(seg_ms[n] for n in seg_ms if n != "attn_fwd")
+    label = (w.name + ("" if softmax == "vanilla" else f"+{softmax}_sink")
+             + ("" if bias == "none" else f"+{bias}_bias") + ("" if dropout <= 0.0 else f"+dropout{dropout:g}"))
+    tlabel = label.replace("+", "_")
+    hbm_bound = w.window[0] >= 0        # sliding window: HBM-bound
+
+    def roofline(name, t_ms, flop, nbytes, traffic):
+        r = {"kernel": name, "avg_us": round(t_ms * 1e3, 2), "traffic": traffic}
+        if hbm_bound:
+            ach = nbytes / (t_ms * 1e-3) / 1e9
+            r.update({"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(ach / PEAK_HBM_GBS, 4), "alg_bytes_per_launch": nbytes})
+        else:
+            ach = flop / (t_ms * 1e-3) / 1e12
+            r.update({"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(ach / PEAK_BF16_TFLOPS, 4), "alg_flop_per_launch": flop})
+        return r
+
+    dom = max(seg_ms, key=seg_ms.get)
+    roof = roofline(dom, seg_ms[dom], alg[dom], hbm[dom], measured_traffic(tlabel, dom))
+    roof_fwd = roofline("attn_fwd", seg_ms["attn_fwd"], f_fwd, hbm["attn_fwd"], measured_traffic(tlabel, "attn_fwd"))
+    roof_bwd = None
+    if w.backward:
+        tq, tk = measured_traffic(tlabel, "bwd_dq"), measured_traffic(tlabel, "bwd_dkdv")
+        roof_bwd = roofline("bwd_dq+bwd_dkdv", bwd_ms, f_bwd, hbm_bwd, (tq + tk) if tq and tk else None)
+    return {
+        "ms_per_step": wall / steps * 1e3,
+        "step_us": stats_us(step_per),
+        "total_flop": f_fwd + f_bwd,
+        "fwd_tflops": round(f_fwd / (seg_ms["attn_fwd"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if w.backward else None,
+        "config": {"workload": label, "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "head_dim_v": Dv, "causal": w.causal, "window": list(w.window),
+                   "virtual_blocks": (S // w.kv_block) if w.kv_block else 1,
+                   "query_chunk": w.query_chunk, "key_chunk": w.key_chunk, "parallelism": "none (1 GPU)"},
+        "kernels": kernels,
+        "roofline": roof,
+        "roofline_fwd": roof_fwd,
+        "roofline_bwd": roof_bwd,
+    }
+
+
+def sparse_union_flops(sel, tokens_per_group=32, window=32, block_size=32, embed=512):
+    """MFMA flops the gathered-attention kernel executes: per group of 32 consecutive
+    tokens, every 32-row step (the window's blocks, then each distinct selected block,
+    -1 entries counting as one) costs 32 x 32 x E x 2 for the scores and as much for P V."""
+    import numpy as np
+    B, S, n = sel.shape
+    G = S // tokens_per_group
+    g = sel[:, :G * tokens_per_group].reshape(B, G, tokens_per_group * n)
+    srt = np.sort(g, axis=2)
+    distinct = 1 + (np.diff(srt, axis=2) != 0).sum(axis=2)
+    nwin = (window + tokens_per_group - 1 + 31) // 32
+    steps = int((distinct + nwin).sum()) * ((block_size + 31) // 32)
+    return steps * 32 * 32 * embed * 4.0, steps
+
+
+def extra_workloads(torch, rea, workloads, dev, args):
+    """The other workloads the method is measured on, each with its own roofline: GQA-16 +
+    sliding window (fwd + bwd, HBM-bound, MALL flushed before every step), the long-context
+    causal forward (MFMA-bound) and the block-sparse selection + gathered attention (MALL
+    flushed before every step)."""
+    out = {}
+    flush = mall_flusher(torch, dev)
+    w3 = workloads.WORKLOADS["gqa16_swa128_s4096"]
+    r3 = dense_measure(torch, rea, workloads, w3, dev, args.steps, args.warmup, flush=flush)
+    out[w3.name] = {"mall_flush": True, "step_us": r3["step_us"], "fwd_tflops": r3["fwd_tflops"],
+                    "bwd_tflops": r3["bwd_tflops"],
+                    "fwd_bwd_tflops": round(r3["total_flop"] / (r3["step_us"]["mean"] * 1e-6) / 1e12, 2),
+                    "kernels": r3["kernels"], "roofline_fwd": r3["roofline_fwd"],
+                    "roofline_bwd": r3["roofline_bwd"]}
+    torch.cuda.empty_cache()
+    w4 = workloads.WORKLOADS["long_causal_s131072"]
+    r4 = dense_measure(torch, rea, workloads, w4, dev, max(3, args.steps // 4), max(1, args.warmup // 4))
+    out[w4.name] = {"step_us": r4["step_us"], "fwd_tflops": r4["fwd_tflops"], "kernels": r4["kernels"],
+                    "roofline_fwd": r4["roofline_fwd"]}
+    torch.cuda.empty_cache()
+    out["block_sparse_top8_s8192"] = sparse_measure(torch, rea, workloads, dev, args.steps, args.warmup, flush)
+    torch.cuda.empty_cache()
+    return out
+
+
+def sparse_measure(torch, rea, workloads, dev, steps, warmup, flush):
+    """block_select + gathered sparse forward of the block-sparse workload, MALL flushed."""
+    w = workloads.WORKLOADS["block_sparse_top8_s8192"]
+    q, k, v, _ = workloads.generate(w, with_dout=False)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    B, S, E = w.batch, w.seqlen, w.head_dim
+    idx = torch.empty((B, S, w.top_n), dtype=torch.int32, device=dev)
+    o = torch.empty_like(qd)
+    segs = [("block_select", lambda: rea.block_select(qd, kd, block_size=w.block_size, top_n=w.top_n, out=idx)),
+            ("attn_fwd_sparse", lambda: rea.attn_fwd_sparse(qd, kd, vd, idx, window=w.sparse_window,
+                                                            block_size=w.block_size, out=o))]
+    seg_ms, _, per = time_segments(torch, segs, steps, warmup, torch.cuda.current_stream(dev), flush=flush)
+    f_select = B * 2.0 * E * w.block_size * sum(range(S // w.block_size))
+    slots = w.sparse_window + w.top_n * w.block_size
+    gathered = B * S * slots * E * 2 * 2
+    f_exec, nsteps = sparse_union_flops(idx.cpu().numpy(), 32, w.sparse_window, w.block_size, E)
+    t_sel, t_sp = seg_ms["block_select"] * 1e-3, seg_ms["attn_fwd_sparse"] * 1e-3
+    traffic = measured_traffic(w.name, "attn_fwd_sparse")
+    sel_traffic = measured_traffic(w.name, "block_select")
+    roof_sp = {"kernel": "attn_fwd_sparse", "bound": "mfma", "avg_us": round(t_sp * 1e6, 2),
+               "achieved": round(f_exec / t_sp / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+               "frac": round(f_exec / t_sp / 1e12 / PEAK_BF16_TFLOPS, 4), "executed_flop_per_launch": f_exec,
+               "union_steps": nsteps, "traffic": traffic,
+               "hbm": ({"achieved": round(traffic / t_sp / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(traffic / t_sp / 1e9 / PEAK_HBM_GBS, 4)} if traffic else None),
+               "gathered_gb_logical": round(gathered / 1e9, 3),
+               "gathered_gbs_logical": round(gathered / t_sp / 1e9, 1)}
+    roof_sel = {"kernel": "block_select", "bound": "fp64", "avg_us": round(t_sel * 1e6, 2),
+                "achieved": round(f_select / t_sel / 1e12, 3), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(f_select / t_sel / 1e12 / PEAK_FP64_TFLOPS, 4), "alg_flop_per_launch": f_select,
+                "traffic": sel_traffic}
+    return {"mall_flush": True, "kernels": {n: {"us": stats_us(per[n])} for n in per},
+            "roofline_select": roof_sel, "roofline_sparse": roof_sp}
 
 
 def main():
@@ -258,7 +488,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ring_sim_causal_s8192")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--decode-tokens", type=int, default=0,
                     help="block-sparse workload: also time decoding this many new tokens per sequence "
                          "against the full cache (selection + attention)")
@@ -274,6 +504,8 @@ def main():
                          "removes the dropped pairs from the softmax")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default run only: skip the other workloads (GQA-16 SWA, long context, block-sparse)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter calibration)")
     args = ap.parse_args()
@@ -298,95 +530,9 @@ def main():
         return copy_calibration(torch, dev, args)
     if w.sparse:
         return bench_sparse(torch, rea, workloads, w, dev, args)
-    q, k, v, do = workloads.generate(w, with_dout=w.backward)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    dod = do.to(dev) if do is not None else None
-    kw = dict(causal=w.causal, window=w.window, query_chunk=w.query_chunk, key_chunk=w.key_chunk,
-              kv_block=w.kv_block)
-    B, S, Hq, Hkv, D, Dv = w.batch, w.seqlen, w.num_q_heads, w.num_kv_heads, w.head_dim, w.dv
-    sink = None
-    if args.softmax == "learnable":
-        sink = workloads.random_tensor((Hq,), w.seed + 100).to(dev)
-    kw.update(softmax_type=args.softmax, sink=sink)
-    if args.bias == "keypad":
-        bias = torch.zeros((B, 1, 1, S), dtype=torch.float32, device=dev)
-        bias[..., S - S // 16:] = float("-inf")
-        kw.update(bias=bias)
-    elif args.bias == "shared":
-        kw.update(bias=workloads.random_tensor((1, 1, S, S), w.seed + 101).to(dev))
-    if args.dropout > 0.0:
-        # drawn on the GPU head by head (the [S, S] draws of all heads would be large)
-        g = torch.Generator(device=dev).manual_seed(w.seed + 102)
-        words = torch.empty((1, Hq, S, (S + 31) // 32), dtype=torch.int32, device=dev)
-        for h in range(Hq):
-            words[0, h] = workloads.pack_bits(torch.rand((S, S), generator=g, device=dev) < args.dropout)
-        kw.update(dropout=words)
-    o = torch.empty((B, S, Hq, Dv), dtype=qd.dtype, device=dev)
-    m = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
-    l = torch.empty_like(m)
-    grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
-    ws = torch.empty(max(rea.bwd_workspace_bytes(qd, kd, head_dim_v=Dv, **kw), 256), dtype=torch.uint8,
-                     device=dev)
-    bkw = dict(kw, dsink=torch.empty((Hq,), dtype=torch.float32, device=dev)) if sink is not None else kw
-
-    # One step, split into its kernels so each can be timed on the launch stream:
-    # forward | dq (which also computes D and the LSE for the dk/dv pass) | dk,dv.
-    def segments():
-        yield "attn_fwd", lambda: rea.attn_fwd(qd, kd, vd, out=o, m=m, l=l, **kw)
-        if w.backward:
-            yield "bwd_dq", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
-                                                 skip_dkdv=True, **bkw)
-            yield "bwd_dkdv", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
-                                                   skip_dq=True, reuse_stats=True, **bkw)
-
-    segs = list(segments())
-    seg_ms, wall = time_segments(torch, segs, args.steps, args.warmup, torch.cuda.current_stream(dev))
-
-    pairs = visible_pairs(S, S, w.causal, w.window) * B * Hq
-    # Per visible pair: S = Q K^T costs 2D flops and each product with V or dO 2Dv
-    # (D = Dv except for the MLA head dims): forward 2D + 2Dv (= 4D); backward recompute
-    # of S (2D) and dP (2Dv), dV (2Dv), dK (2D), dQ (2D) = 6D + 4Dv (= 10D).
-    f_fwd = (2.0 * D + 2.0 * Dv) * pairs
-    f_bwd = (6.0 * D + 4.0 * Dv) * pairs if w.backward else 0.0
-    # Algorithmic flops per kernel launch: the dk/dv kernel does the recompute of S and
-    # dP plus dV and dK (4D + 4Dv per pair); the dq kernel's share is dQ (2D per pair),
-    # its own recompute being the cost of computing dq without atomics.
-    alg = {"attn_fwd": f_fwd, "bwd_dq": 2.0 * D * pairs, "bwd_dkdv": (4.0 * D + 4.0 * Dv) * pairs}
-    # Compulsory HBM bytes per launch (bf16 tensors read or written once, fp32 stats).
-    esz = 2 if w.dtype == "bf16" else 4
-    qbytes, kbytes, stat = B * S * Hq * D * esz, B * S * Hkv * D * esz, B * Hq * S * 4
-    obytes, vbytes = B * S * Hq * Dv * esz, B * S * Hkv * Dv * esz
-    hbm = {"attn_fwd": qbytes + obytes + kbytes + vbytes + 2 * stat,
-           "bwd_dq": 2 * qbytes + 2 * obytes + kbytes + vbytes + 4 * stat,
-           "bwd_dkdv": qbytes + obytes + 2 * kbytes + 2 * vbytes + 2 * stat}
-    kernels = {}
-    for n, t in seg_ms.items():
-        kernels[n] = {"avg_us": round(t * 1e3, 2), "alg_gflop": round(alg[n] / 1e9, 3),
-                      "tflops": round(alg[n] / (t * 1e-3) / 1e12, 2),
-                      "hbm_gbs": round(hbm[n] / (t * 1e-3) / 1e9, 1)}
-    step_ms = sum(seg_ms.values())
-    ms_per_step = wall / args.steps * 1e3
-    total = f_fwd + f_bwd
-    value = total / (ms_per_step * 1e-3) / 1e12
-    fwd_tflops = f_fwd / (seg_ms["attn_fwd"] * 1e-3) / 1e12
-    bwd_ms = step_ms - seg_ms["attn_fwd"]
-    bwd_tflops = f_bwd / (bwd_ms * 1e-3) / 1e12 if w.backward else None
-
-    label = (w.name + ("" if args.softmax == "vanilla" else f"+{args.softmax}_sink")
-             + ("" if args.bias == "none" else f"+{args.bias}_bias")
-             + ("" if args.dropout <= 0.0 else f"+dropout{args.dropout:g}"))
-    dom = max(seg_ms, key=seg_ms.get)
-    roof = {"kernel": dom, "bound": "mfma", "achieved": round(alg[dom] / (seg_ms[dom] * 1e-3) / 1e12, 2),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(alg[dom] / (seg_ms[dom] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "avg_us": round(seg_ms[dom] * 1e3, 2), "alg_flop_per_launch": alg[dom],
-            "traffic": measured_traffic(label.replace("+", "_"), dom)}
-    if w.window[0] >= 0:        # sliding window: the kernels are HBM-bound
-        roof.update({"bound": "hbm", "achieved": round(hbm[dom] / (seg_ms[dom] * 1e-3) / 1e9, 1),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(hbm[dom] / (seg_ms[dom] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                     "alg_bytes_per_launch": hbm[dom]})
-
+    res = dense_measure(torch, rea, workloads, w, dev, args.steps, args.warmup, softmax=args.softmax,
+                        bias=args.bias, dropout=args.dropout)
+    value = res["total_flop"] / (res["ms_per_step"] * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -394,26 +540,31 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(res["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": label,
-                   "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv,
-                   "head_dim": D, "head_dim_v": Dv, "causal": w.causal, "window": list(w.window),
-                   "virtual_blocks": (S // w.kv_block) if w.kv_block else 1,
-                   "query_chunk": w.query_chunk, "key_chunk": w.key_chunk, "parallelism": "none (1 GPU)"},
-        "fwd_tflops": round(fwd_tflops, 2),
-        "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
+        "config": res["config"],
+        "step_us": res["step_us"],
+        "fwd_tflops": res["fwd_tflops"],
+        "bwd_tflops": res["bwd_tflops"],
         "fwd_bwd_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd_mfma_frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-        "kernels": kernels,
-        "roofline": roof,
+        "fwd_mfma_frac": round(res["fwd_tflops"] / PEAK_BF16_TFLOPS, 4),
+        "kernels": res["kernels"],
+        "roofline": res["roofline"],
+        "roofline_fwd": res["roofline_fwd"],
+        "roofline_bwd": res["roofline_bwd"],
     }
+    default_run = (args.workload == DEFAULT_WORKLOAD and args.softmax == "vanilla" and args.bias == "none"
+                   and args.dropout <= 0.0)
     if not args.no_cpu_baseline:
+        q, k, v, do = workloads.generate(w, with_dout=w.backward)
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, args.cpu_budget)
+        del q, k, v, do
+    if default_run and not args.no_extras:
+        out["workloads"] = extra_workloads(torch, rea, workloads, dev, args)
     print(json.dumps(out), flush=True)
 
 
