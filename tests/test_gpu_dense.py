@@ -370,6 +370,30 @@ def test_ring_full_size_bias_dropout(gpu):
             check_close("dv", dv[:, :, [h]], dv_r[:, :, [h]], "bf16")
 
 
+def test_ring_full_size_shared_bias(gpu):
+    """The ring workload with the input of bench --bias shared: one N(0,1) fp32 bias matrix
+    [1, 1, S, S] added to the scaled logits of every head.  Two heads forward, one backward,
+    per virtual block, against the oracle given the same bias."""
+    w, q, k, v, do = full_inputs("ring_sim_causal_s8192")
+    S = w.seqlen
+    bias = workloads.random_tensor((1, 1, S, S), w.seed + 101)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    kw = dict(launch_kw(w), bias=bias.to(DEV))
+    o, m, l = gpu.attn_fwd(qd, kd, vd, **kw)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **kw)
+    torch.cuda.synchronize()
+    blk = w.kv_block
+    for h in (4, 11):
+        o_r, m_r, l_r = dense.forward(q, k, v, heads=[h], bias=bias, **oracle_kw(w))
+        check_close(f"o head {h}", o[:, :, [h]], o_r[:, :, [h]], "bf16", blocks=blk)
+        check_stats(m[:, [h]], l[:, [h]], m_r[:, [h]], l_r[:, [h]], "bf16")
+    h = 11
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, heads=[h], bias=bias, **oracle_kw(w))
+    check_close("dq", dq[:, :, [h]], dq_r[:, :, [h]], "bf16", blocks=blk)
+    check_close("dk", dk[:, :, [h]], dk_r[:, :, [h]], "bf16", blocks=blk)      # G = 1
+    check_close("dv", dv[:, :, [h]], dv_r[:, :, [h]], "bf16", blocks=blk)
+
+
 def test_gqa_swa_full_size(gpu):
     """B2 S4096 Hq128 Hkv8 D128, window (128, 0): one full GQA group checked fwd and bwd."""
     w, q, k, v, do = full_inputs("gqa16_swa128_s4096")
