@@ -81,7 +81,9 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
   const int first = a.q_pos0 / BS;
   const int nqb = (a.q_pos0 + a.S - 1) / BS - first + 1;
   const int ns = a.nsplit, wg = wg_index(a.rev_order), split = wg % ns, qb = wg / ns;
-  const int i = first + qb % nqb, b = qb / nqb;
+  // longest first: query block i scores i candidates, so the grid walks i downwards (all
+  // sequences of the batch at each i) and the short blocks fill in behind the long ones
+  const int i = first + (nqb - 1 - qb / a.B), b = qb % a.B;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int p0 = max(i * BS, a.q_pos0);                      // first query position of the block
   const int t0 = p0 - a.q_pos0;                               // its query row
