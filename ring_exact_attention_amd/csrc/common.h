@@ -135,6 +135,7 @@ struct SparseArgs {
   int Skv, q_pos0;    // key / value rows; position of query row 0 among them
   int tpw;            // tokens per workgroup (power of two <= 32; set by the launcher)
   int ksplit;         // workgroups per token group, each over a share of its 32-row steps
+  int xcd_seq;        // > 0: XCDs per sequence of the XCD-aware group order (set by the launcher)
   float* part;        // ksplit > 1: [B, S, ksplit, 512 + 4] partial numerator, max, sum, pad
 };
 

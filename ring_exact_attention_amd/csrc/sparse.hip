@@ -37,7 +37,9 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int nqb = (a.S + a.tpw - 1) / a.tpw;
-  const int wg = wg_index(a.rev_order), split = wg % a.ksplit, grp_id = wg / a.ksplit;
+  const int wg = wg_index(a.rev_order), split = wg % a.ksplit;
+  // token groups of one sequence per XCD (see xcd_unit) when the split is off
+  const int grp_id = a.ksplit == 1 ? xcd_unit(wg, nqb, a.xcd_seq) : wg / a.ksplit;
   const int b = grp_id / nqb, t0 = (grp_id % nqb) * a.tpw;
   const int tend = min(t0 + a.tpw, a.S);                      // this workgroup's tokens: [t0, tend)
   const int n = a.top_n, bs = a.sel_block, W = a.window;
@@ -268,6 +270,7 @@ hipError_t launch_sparse(const SparseArgs& args, hipStream_t stream) {
   SparseArgs a = args;
   sparse_plan(a.B, a.S, a.window, a.sel_block, a.top_n, a.part != nullptr, a.tpw, a.ksplit);
   const long long nqb = (a.S + a.tpw - 1) / a.tpw;
+  a.xcd_seq = a.ksplit == 1 ? xcd_per_seq(a.B, nqb) : 0;
   hipLaunchKernelGGL(sparse_union_kernel, dim3((unsigned)(a.B * nqb * a.ksplit)), dim3(256), 0, stream, a);
   if (a.ksplit > 1)
     hipLaunchKernelGGL(sparse_combine_kernel, dim3((unsigned)((long long)a.B * a.S)), dim3(256), 0, stream, a);

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int nqb = (a.S + kUQ - 1) / kUQ;
-  const int wg = wg_index(a.rev_order), b = wg / nqb, t0 = (wg % nqb) * kUQ;
+  const int u = xcd_unit(wg_index(a.rev_order), nqb, xcd_per_seq(a.B, nqb));
+  const int b = u / nqb, t0 = (u % nqb) * kUQ;
   const int n = a.top_n, bs = a.sel_block, W = a.window;
 
   const int nu = build_union(a.sel, a.S, a.S, n, b, t0, (int*)&sK[0][0], ucnt, ublk, &s_nu);
@@ -265,7 +266,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int nkt = (a.S + 31) / 32;
-  const int wg = wg_index(a.rev_order), b = wg / nkt, c = wg % nkt;
+  const int u = xcd_unit(wg_index(a.rev_order), nkt, xcd_per_seq(a.B, nkt));
+  const int b = u / nkt, c = u % nkt;
   const int r0 = 32 * c;
   const int n = a.top_n, W = a.window;
   const int e0 = kUDW * wave;

@@ -12,6 +12,20 @@ constexpr int kUQ = 32;              // tokens per workgroup
 constexpr int kUDW = 128;            // embedding slice per wavefront
 constexpr int kUPITCH = kUDW + 32;   // slice row pitch (elements): conflict-free tr reads
 constexpr int kUMaxEnt = 512;        // 32 tokens x top_n (<= 16)
+
+// Unit index (b * n_per_seq + unit) of workgroup wg.  Workgroups are dispatched
+// round-robin over the 8 XCDs (wg % 8), each with its own L2; with xcd_seq > 0 every XCD
+// takes the units of one sequence (xcd_seq XCDs share a sequence, taking its units in
+// turn), so the rows a unit gathers on an XCD all come from that sequence.
+__device__ __forceinline__ int xcd_unit(int wg, int n_per_seq, int xcd_seq) {
+  if (xcd_seq <= 0) return wg;
+  const int x = wg & 7, r = wg >> 3;
+  return (x / xcd_seq) * n_per_seq + r * xcd_seq + (x % xcd_seq);
+}
+// XCDs per sequence for B sequences of n_per_seq units each (0 = plain order).
+__host__ __device__ inline int xcd_per_seq(int B, long long n_per_seq) {
+  return (B >= 1 && B <= 8 && 8 % B == 0 && n_per_seq % (8 / B) == 0) ? 8 / B : 0;
+}
 constexpr int kUSentinel = 0x7fffffff;
 
 // The selections of tokens t0 .. min(t0 + 32, tend) - 1 of sequence b (S tokens): their
