@@ -52,6 +52,13 @@ __global__ __launch_bounds__(256) void block_means_kernel(SelectArgs a) {
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
+// Largest value of x over the wavefront (a butterfly of lane exchanges; every lane gets it).
+__device__ __forceinline__ double wave_max_f64(double x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fmax(x, __shfl_xor(x, off));
+  return x;
+}
+
 // Lane y's value of x (y uniform across the wavefront).
 __device__ __forceinline__ double read_lane_f64(double x, int y) {
   const unsigned long long u = (unsigned long long)__double_as_longlong(x);
@@ -153,8 +160,21 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
         for (int t = wave; t < ntok; t += 4) {
           const bool cval = lane < nc;
           const double v = cval ? ssc[t][lane] : 0.0;
-          const double thr = kept0 < n ? -INFINITY : best_s[t][n - 1];
-          const bool surv = cval && v > thr;
+          double thr = kept0 < n ? -INFINITY : best_s[t][n - 1];
+          bool surv = cval && v > thr;
+          if (kept0 == 0 && nc > n) {
+            // Empty list (a share's first chunk): only the chunk's n largest scores can
+            // enter it, so keep the candidates at or above the n-th largest (counted with
+            // multiplicity; ties at it survive and are ranked by index below) instead of
+            // ranking all of them against each other.
+            double cut = INFINITY;
+            int cnt = 0;
+            for (int it = 0; it < n && cnt < n; ++it) {
+              cut = wave_max_f64(cval && v < cut ? v : -INFINITY);
+              cnt += __popcll(__ballot(cval && v == cut));
+            }
+            surv = cval && v >= cut;
+          }
           const uint64_t P = __ballot(surv);
           const bool is_l = lane < kept0;
           const double ls = is_l ? best_s[t][lane] : 0.0;
