@@ -588,10 +588,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   diag = diag < 0 ? 0 : diag / a.q_vblock;
   const int nqvb = a.n_qvblocks;
   if (diag >= nqvb) diag = nqvb - 1;
+  // One row block and a left window: the walk is phased so that neighbouring key tiles
+  // read the query rows they share at about the same time.  With n step tiles, it starts
+  // at the tile whose index (row / BQ) is a multiple of n and wraps round; away from the
+  // sequence ends every key tile has the same n, so a row is reached at the same
+  // position (row / BQ mod n) of every walk that reads it, and the L2 the neighbours share
+  // serves all but its first read.  The walk is presented to the iterator as two row
+  // blocks, [mid, 2 mid) visited before [0, mid).
+  int it_nvb = nqvb, it_qvb = a.q_vblock, it_diag = diag;
+  if (nqvb == 1 && a.lo_off > -kPosInf && ilo <= ihi) {
+    const int t0 = ilo / C::BQ, n = ihi / C::BQ - t0 + 1;
+    const int first = (n - t0 % n) % n;
+    const int mid = (t0 + first) * C::BQ;
+    if (first > 0 && 2 * mid > ihi) {
+      it_nvb = 2;
+      it_qvb = mid;
+      it_diag = 1;
+    }
+  }
   QueryTileIter<C::BQ> qit;
   int hh = split * g_per;
   const int hh_end = hh + g_per;
-  qit.init(nqvb, a.q_vblock, diag, ilo, ihi);
+  qit.init(it_nvb, it_qvb, it_diag, ilo, ihi);
   auto next_step = [&](int& hq_o, int& qs, int& rend) -> bool {
     while (hh < hh_end) {
       if (qit.next(qs, rend)) {
@@ -599,7 +617,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         return true;
       }
       ++hh;
-      qit.init(nqvb, a.q_vblock, diag, ilo, ihi);
+      qit.init(it_nvb, it_qvb, it_diag, ilo, ihi);
     }
     return false;
   };
