@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       f32x4 v4 = {s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
-      *(f32x4*)&sS[wave][lane * 16 + 4 * g] = v4;
+      *(f32x4*)&sS[wave][part_off(lane, g)] = v4;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
     for (int w2 = 0; w2 < 4; ++w2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 v4 = *(const f32x4*)&sS[w2][lane * 16 + 4 * g];
+        const f32x4 v4 = *(const f32x4*)&sS[w2][part_off(lane, g)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[4 * g + e] += v4[e];
       }

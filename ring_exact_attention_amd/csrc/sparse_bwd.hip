@@ -36,7 +36,10 @@ namespace rea {
 __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sS[4][64 * 16];   // partial scores per wave
   __shared__ __attribute__((aligned(16))) float sP[4][64 * 16];   // partial dP per wave
-  __shared__ __attribute__((aligned(16))) __bf16 sK[4][32 * kUPITCH];   // K slices (setup scratch)
+  // K slices, stored by rows (lane = row) and read transposed: the grouped layout keeps
+  // both patterns free of bank conflicts (also the setup scratch)
+  using KL = TileLayout<kUDW, kBothRead>;
+  __shared__ __attribute__((aligned(16))) __bf16 sK[4][KL::elems(kUQ)];
   __shared__ uint32_t ucnt[kUMaxEnt][kUQ / 4];
   __shared__ int ublk[kUMaxEnt];
   __shared__ int s_nu;
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   const int tg = lane >> 4, tj = lane & 15;
-  const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * kUPITCH + 16 * (tg & 1) + 4 * (tj & 3);
+  const int tr_off = KL::idx(4 * (tg >> 1) + (tj >> 2), 16 * (tg & 1) + 4 * (tj & 3));
 
   // pass 0 (units with -1 entries only) accumulates D_t from P and dP; pass 1 uses D_t
   // for dS and dQ.
@@ -147,12 +150,12 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
       for (int g = 0; g < 4; ++g) {
         const f32x4 s4 = {s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
         const f32x4 p4 = {dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3]};
-        *(f32x4*)&sS[wave][lane * 16 + 4 * g] = s4;
-        *(f32x4*)&sP[wave][lane * 16 + 4 * g] = p4;
+        *(f32x4*)&sS[wave][part_off(lane, g)] = s4;
+        *(f32x4*)&sP[wave][part_off(lane, g)] = p4;
       }
       if (pass == 1) {
 #pragma unroll
-        for (int kk = 0; kk < kUDW / 16; ++kk) *(u32x4*)&sK[wave][li * kUPITCH + 16 * kk + 8 * lh] = kbuf[kk];
+        for (int kk = 0; kk < kUDW / 16; ++kk) *(u32x4*)&sK[wave][KL::idx(li, 16 * kk + 8 * lh)] = kbuf[kk];
       }
       __syncthreads();
       if (step + 1 < nsteps) load_step(step + 1);
@@ -166,8 +169,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
       for (int w2 = 0; w2 < 4; ++w2)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 s4 = *(const f32x4*)&sS[w2][lane * 16 + 4 * g];
-          const f32x4 p4 = *(const f32x4*)&sP[w2][lane * 16 + 4 * g];
+          const f32x4 s4 = *(const f32x4*)&sS[w2][part_off(lane, g)];
+          const f32x4 p4 = *(const f32x4*)&sP[w2][part_off(lane, g)];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             s[4 * g + e] += s4[e];
@@ -209,8 +212,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
           const bf16x8 dsb = as_bf16x8(pb);
 #pragma unroll
           for (int db = 0; db < kUDW / 32; ++db) {
-            const __bf16* kp0 = &sK[wave][tr_off + 16 * ks * kUPITCH + 32 * db];
-            const bf16x8 ka = join_bf16x8(lds_read_tr16(kp0), lds_read_tr16(kp0 + 8 * kUPITCH));
+            const __bf16* kp0 = &sK[wave][tr_off + KL::rows(16 * ks) + 32 * db];
+            const bf16x8 ka = join_bf16x8(lds_read_tr16(kp0), lds_read_tr16(kp0 + KL::rows(8)));
             acc[db] = mfma32(ka, dsb, acc[db]);
           }
         }
@@ -346,8 +349,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
     for (int g = 0; g < 4; ++g) {
       const f32x4 s4 = {s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
       const f32x4 p4 = {dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3]};
-      *(f32x4*)&sS[wave][lane * 16 + 4 * g] = s4;
-      *(f32x4*)&sP[wave][lane * 16 + 4 * g] = p4;
+      *(f32x4*)&sS[wave][part_off(lane, g)] = s4;
+      *(f32x4*)&sP[wave][part_off(lane, g)] = p4;
     }
     __syncthreads();
 #pragma unroll
@@ -359,8 +362,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
     for (int w2 = 0; w2 < 4; ++w2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 s4 = *(const f32x4*)&sS[w2][lane * 16 + 4 * g];
-        const f32x4 p4 = *(const f32x4*)&sP[w2][lane * 16 + 4 * g];
+        const f32x4 s4 = *(const f32x4*)&sS[w2][part_off(lane, g)];
+        const f32x4 p4 = *(const f32x4*)&sP[w2][part_off(lane, g)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           s[4 * g + e] += s4[e];

@@ -13,6 +13,12 @@ constexpr int kUDW = 128;            // embedding slice per wavefront
 constexpr int kUPITCH = kUDW + 32;   // slice row pitch (elements): conflict-free tr reads
 constexpr int kUMaxEnt = 512;        // 32 tokens x top_n (<= 16)
 
+// Float offset of group g (four values) of lane `lane` in a wave's partial score tile
+// (an f32x16 per lane) exchanged through LDS.  Consecutive lanes take consecutive
+// 16-byte slots, so 16 lanes cover 256 contiguous bytes: no bank conflicts, where a
+// lane-major layout (16 floats per lane) puts every fourth lane on the same banks.
+__device__ __forceinline__ int part_off(int lane, int g) { return 4 * (64 * g + lane); }
+
 // Unit index (b * n_per_seq + unit) of workgroup wg.  Workgroups are dispatched
 // round-robin over the 8 XCDs (wg % 8), each with its own L2; with xcd_seq > 0 every XCD
 // takes the units of one sequence (xcd_seq XCDs share a sequence, taking its units in
