@@ -49,7 +49,9 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
 
   // ---- main loop over 32-row blocks: window blocks, then union blocks
   const int nwin = (W + a.tpw - 1 + 31) / 32;
-  const int nsub = (bs + 31) / 32;
+  // 32-row steps per selected block: bs is 16, 32 or 64 (checked by the host), so a
+  // step's entry and sub-block come from a shift and a mask rather than a division
+  const int nsub_sh = bs > 32 ? 1 : 0, nsub = 1 << nsub_sh;
   const int nsteps = nwin + nu * nsub;
   // this workgroup's share of the steps (all of them unless split)
   const int sps = (nsteps + a.ksplit - 1) / a.ksplit;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   auto row_pos = [&](int step, int r, bool& valid) -> int {   // position of row r of a step
     valid = true;
     if (step < nwin) return wstart + 32 * step + r;
-    const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;
+    const int u = (step - nwin) >> nsub_sh, h = (step - nwin) & (nsub - 1);
     const int c = ublk[u];
     valid = 32 * h + r < bs;
     return c < 0 ? 0 : c * bs + 32 * h + r;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
         wt[r] = (tok_ok && p >= tpos - W + 1 && p <= tpos) ? 1.f : 0.f;
       }
     } else {
-      const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;
+      const int u = (step - nwin) >> nsub_sh, h = (step - nwin) & (nsub - 1);
       const float cnt = (float)((ucnt[u][li >> 2] >> (8 * (li & 3))) & 0xffu);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

@@ -55,7 +55,9 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   const int nu = build_union(a.sel, a.S, a.S, n, b, t0, (int*)&sK[0][0], ucnt, ublk, &s_nu);
 
   const int nwin = (W + kUQ - 1 + 31) / 32;
-  const int nsub = (bs + 31) / 32;
+  // 32-row steps per selected block: bs is 16, 32 or 64 (checked by the host), so a
+  // step's entry and sub-block come from a shift and a mask rather than a division
+  const int nsub_sh = bs > 32 ? 1 : 0, nsub = 1 << nsub_sh;
   const int nsteps = nwin + nu * nsub;
   const int wstart = t0 - W + 1;
   const uint32_t row_b = (uint32_t)kSpE * 2;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
 
   auto row_pos = [&](int step, int r) -> int {      // sequence row of row r of a step
     if (step < nwin) return wstart + 32 * step + r;    // negative: zero pad (reads 0)
-    const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;
+    const int u = (step - nwin) >> nsub_sh, h = (step - nwin) & (nsub - 1);
     const int c = ublk[u];
     return c < 0 ? 0 : c * bs + 32 * h + r;
   };
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
           wt[r] = (tok_ok && p >= tok - W + 1 && p <= tok) ? 1.f : 0.f;
         }
       } else {
-        const int u = (step - nwin) / nsub, h = (step - nwin) % nsub;
+        const int u = (step - nwin) >> nsub_sh, h = (step - nwin) & (nsub - 1);
         const float cnt = (float)((ucnt[u][li >> 2] >> (8 * (li & 3))) & 0xffu);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
