@@ -26,6 +26,13 @@ namespace rea {
 //   transposed with ds_read_b64_tr_b16).
 // A block shared by several tokens is read once for all of them.
 
+// Workgroup barrier over LDS only: this wave's LDS operations complete, then s_barrier
+// (the memory clobber keeps LDS accesses on their side of it).  __syncthreads also waits
+// for every vector memory load in flight, which here are the next step's gathers.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   // LDS: partial scores 16 KiB | V slices 40 KiB (setup scratch reuses it) | counts 16 KiB
   __shared__ __attribute__((aligned(16))) float sS[4][64 * 16];
@@ -85,18 +92,40 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
     valid = 32 * h + r < bs;
     return c < 0 ? 0 : c * bs + 32 * h + r;
   };
-  u32x4 kbuf[kUDW / 16], vbuf[8];
-  auto load_step = [&](int step) {
+  u32x4 kbuf[kUDW / 16];
+  // Both loaders are issued unconditionally (a step past the end, and the padding slots,
+  // get an out-of-range offset and read zero without a memory access), so the loop body
+  // is straight-line and the compiler's waits count exactly the loads in flight.
+  auto load_k = [&](int step) {
     bool ok;
-    const int pk = row_pos(step, li, ok);                      // K operand row of this lane
+    const int pk = step < s_end ? row_pos(step, li, ok) : -1;  // K operand row of this lane
 #pragma unroll
     for (int kk = 0; kk < kUDW / 16; ++kk)
       kbuf[kk] = buf_load16(rk, (uint32_t)pk * row_b + 2u * (e0 + 16 * kk + 8 * lh), 0);
+  };
+  // The V slice goes straight into this wave's LDS rows (buffer loads with an LDS
+  // destination): instruction n fills bytes [1024 n, 1024 n + 1024) of the slice, lane l
+  // the 16 bytes of slot j = 64 n + l, i.e. row j / 20, chunk j % 20 of the 320-byte
+  // pitch (chunks 16..19 are padding and load nothing).  Only this wave reads the slice,
+  // so it needs no barrier, only this wave's wait before the P V MFMAs.
+  constexpr int kVSlots = kUPITCH / 8;                         // 16-byte slots per row
+  auto dma_v = [&](int step) {
+    const bool live = step < s_end;
+    bool all0 = false;
+    int base = 0;
+    if (live && step < nwin) {
+      base = wstart + 32 * step;
+    } else if (live) {
+      const int c = ublk[(step - nwin) >> nsub_sh];
+      all0 = c < 0;
+      base = c * bs + 32 * ((step - nwin) & (nsub - 1));
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {                              // V slice: row (lane + 64u) / 16
-      const int qc = lane + 64 * u, r = qc >> 4, ch = qc & 15;
-      const int pv = row_pos(step, r, ok);
-      vbuf[u] = buf_load16(rv, (uint32_t)pv * row_b + 2u * (e0 + 8 * ch), 0);
+    for (int n = 0; n < 32 * kVSlots / 64; ++n) {
+      const int j = 64 * n + lane, r = j / kVSlots, ch = j - kVSlots * r;
+      const int pv = all0 ? 0 : base + r;
+      const uint32_t off = live && ch < 16 ? (uint32_t)pv * row_b + 2u * (e0 + 8 * ch) : 0xffffffffu;
+      dma16(rv, &sV[wave][512 * n], off);
     }
   };
 
@@ -109,7 +138,10 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const int tg = lane >> 4, tj = lane & 15;
   const int tr_off = (4 * (tg >> 1) + (tj >> 2)) * kUPITCH + 16 * (tg & 1) + 4 * (tj & 3);
 
-  if (s_begin < s_end) load_step(s_begin);
+  if (s_begin < s_end) {
+    load_k(s_begin);
+    dma_v(s_begin);
+  }
   for (int step = s_begin; step < s_end; ++step) {
     f32x16 s;
 #pragma unroll
@@ -121,13 +153,8 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
       f32x4 v4 = {s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
       *(f32x4*)&sS[wave][part_off(lane, g)] = v4;
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int qc = lane + 64 * u, r = qc >> 4, ch = qc & 15;
-      *(u32x4*)&sV[wave][r * kUPITCH + 8 * ch] = vbuf[u];
-    }
-    __syncthreads();
-    if (step + 1 < s_end) load_step(step + 1);               // registers are free again
+    lds_barrier();                                             // partial tiles written
+    load_k(step + 1);                                          // registers are free again
 
     // full scores (sum of the four embedding slices), identical in every wave
 #pragma unroll
@@ -185,6 +212,9 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
       s[r] = p;
       l_part += p;
     }
+    // this step's V slice has landed: it was issued before the next step's 8 K loads
+    // (the memory clobber keeps the compiler from moving LDS reads above the wait)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 pb;
@@ -198,7 +228,10 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
         acc[db] = mfma32(va, pbf, acc[db]);
       }
     }
-    __syncthreads();                                           // sS / sV are rewritten next step
+    // the P V MFMAs have consumed this wave's transposed reads of its slice, which the
+    // next step's rows may now overwrite
+    dma_v(step + 1);
+    lds_barrier();                                             // sS is rewritten next step
   }
 
   const float l_used = l_part + other_half(l_part);
