@@ -45,8 +45,9 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   const int li = lane & 31, lh = lane >> 5;
   const int nqb = (a.S + a.tpw - 1) / a.tpw;
   const int wg = wg_index(a.rev_order), split = wg % a.ksplit;
-  // token groups of one sequence per XCD (see xcd_unit) when the split is off
-  const int grp_id = a.ksplit == 1 ? xcd_unit(wg, nqb, a.xcd_seq) : wg / a.ksplit;
+  // token groups of one sequence per XCD (see xcd_unit), longest first, when the split
+  // is off
+  const int grp_id = a.ksplit == 1 ? longest_first(xcd_unit(wg, nqb, a.xcd_seq), nqb) : wg / a.ksplit;
   const int b = grp_id / nqb, t0 = (grp_id % nqb) * a.tpw;
   const int tend = min(t0 + a.tpw, a.S);                      // this workgroup's tokens: [t0, tend)
   const int n = a.top_n, bs = a.sel_block, W = a.window;

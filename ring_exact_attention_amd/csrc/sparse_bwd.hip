@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
   const int nqb = (a.S + kUQ - 1) / kUQ;
-  const int u = xcd_unit(wg_index(a.rev_order), nqb, xcd_per_seq(a.B, nqb));
+  const int u = longest_first(xcd_unit(wg_index(a.rev_order), nqb, xcd_per_seq(a.B, nqb)), nqb);
   const int b = u / nqb, t0 = (u % nqb) * kUQ;
   const int n = a.top_n, bs = a.sel_block, W = a.window;
 
@@ -251,7 +251,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
 // A lane owns one key row (B operand of S = Q K^T and dP = dO V^T, K and V slices in
 // registers); tiles of 32 tokens are gathered into LDS (row-major Q and dO slices, read
 // as rows for S / dP and transposed for dV^T += dO^T P and dK^T += Q^T dS).
-constexpr int kSpList = 512;         // pending token list (a scan chunk of 256 + leftover)
+constexpr int kSpScan = 4;           // tokens per thread in one pass of the selection scan
+constexpr int kSpList = 256 * kSpScan + 32;   // pending token list (a scan pass + leftover)
 
 __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a) {
   using QL = TileLayout<kUDW, kBothRead>;
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   __shared__ int sTok[kUQ];
   __shared__ int lstT[kSpList];
   __shared__ int lstC[kSpList];                      // count | (count of -1 entries) << 8
-  __shared__ int sWaveN[4];
+  __shared__ int sWaveN[kSpScan][4];
   __shared__ int s_npend;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -435,33 +436,49 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   //    which lists strictly earlier blocks) is handled, and the order is fixed.
   if (tid == 0) s_npend = 0;
   __syncthreads();
-  for (int base = 0; base < a.S; base += 256) {
-    const int t = base + tid;
-    int cnt = 0, neg = 0;
-    if (t < a.S && c < a.S / a.sel_block) {
-      const int32_t* row = a.sel + ((size_t)b * a.S + t) * n;
-      for (int j = 0; j < n; ++j) {
-        const int e = row[j];
-        cnt += e == c;
-        neg += e < 0;
+  // A pass covers 256 * kSpScan tokens (token base0 + 256 k + tid for k < kSpScan):
+  // every selection load of the pass is issued before the first compare (the top-n loop
+  // is unrolled to its bound of 16), and the pass's entries are appended in token order
+  // with one ballot per 256-token chunk and one prefix over the pass.
+  for (int base0 = 0; base0 < a.S; base0 += 256 * kSpScan) {
+    int code[kSpScan];                                 // count | (count of -1 entries) << 8
+#pragma unroll
+    for (int k = 0; k < kSpScan; ++k) {
+      const int t = base0 + 256 * k + tid;
+      const bool scan = t < a.S && c < a.S / a.sel_block;
+      const int32_t* row = a.sel + ((size_t)b * a.S + (scan ? t : 0)) * n;
+      int e[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) e[j] = scan && j < n ? row[j] : c + 1;
+      int cnt = 0, neg = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        cnt += e[j] == c;
+        neg += e[j] < 0;
       }
+      code[k] = cnt | ((c != 0 ? 0 : neg) << 8);
     }
-    if (c != 0) neg = 0;
-    const bool keep = cnt > 0 || neg > 0;
-    const uint64_t mask = __ballot(keep);
-    if (lane == 0) sWaveN[wave] = __popcll(mask);
+    uint64_t mask[kSpScan];
+#pragma unroll
+    for (int k = 0; k < kSpScan; ++k) {
+      mask[k] = __ballot(code[k] != 0);
+      if (lane == 0) sWaveN[k][wave] = __popcll(mask[k]);
+    }
     __syncthreads();
     const int npend = s_npend;
-    int before = npend;
-    for (int w2 = 0; w2 < wave; ++w2) before += sWaveN[w2];
-    const int total = sWaveN[0] + sWaveN[1] + sWaveN[2] + sWaveN[3];
-    if (keep) {
-      const int pos = before + __popcll(mask & ((1ull << lane) - 1));
-      lstT[pos] = t;
-      lstC[pos] = cnt | (neg << 8);
+    int have = npend;
+#pragma unroll
+    for (int k = 0; k < kSpScan; ++k) {
+      int before = have;
+      for (int w2 = 0; w2 < wave; ++w2) before += sWaveN[k][w2];
+      if (code[k] != 0) {
+        const int pos = before + __popcll(mask[k] & ((1ull << lane) - 1));
+        lstT[pos] = base0 + 256 * k + tid;
+        lstC[pos] = code[k];
+      }
+      have += sWaveN[k][0] + sWaveN[k][1] + sWaveN[k][2] + sWaveN[k][3];
     }
     __syncthreads();
-    int have = npend + total;
     int head = 0;
     while (have - head >= kUQ) {
       tile([&](int i, float& wa, float& wb) -> int {

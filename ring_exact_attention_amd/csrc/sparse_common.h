@@ -28,6 +28,14 @@ __device__ __forceinline__ int xcd_unit(int wg, int n_per_seq, int xcd_seq) {
   const int x = wg & 7, r = wg >> 3;
   return (x / xcd_seq) * n_per_seq + r * xcd_seq + (x % xcd_seq);
 }
+// Token groups later in a sequence see more earlier blocks, so their unions are longer
+// (S 8192, top 8: a few steps for the first group, ~176 for the last), and the walks that
+// go through them in ascending order end on a tail of the longest ones.  This takes each
+// sequence's units from the last one down.
+__device__ __forceinline__ int longest_first(int u, int n_per_seq) {
+  const int b = u / n_per_seq;
+  return b * n_per_seq + (n_per_seq - 1 - (u - b * n_per_seq));
+}
 // XCDs per sequence for B sequences of n_per_seq units each (0 = plain order).
 __host__ __device__ inline int xcd_per_seq(int B, long long n_per_seq) {
   return (B >= 1 && B <= 8 && 8 % B == 0 && n_per_seq % (8 / B) == 0) ? 8 / B : 0;
