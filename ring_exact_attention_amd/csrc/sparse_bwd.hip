@@ -44,6 +44,11 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   __shared__ int ublk[kUMaxEnt];
   __shared__ int s_nu;
   __shared__ float sDp[4][kUQ];
+  // dS of the step as bf16, [token][key] at a 34-word row pitch (conflict-free B-operand
+  // reads), and each token's log2-LSE and D
+  constexpr int kDsPitch = 34;
+  __shared__ __attribute__((aligned(16))) uint32_t sDS[kUQ * kDsPitch];
+  __shared__ float sTokLse[kUQ], sTokD[kUQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int li = lane & 31, lh = lane >> 5;
@@ -129,11 +134,28 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
 
   // pass 0 (units with -1 entries only) accumulates D_t from P and dP; pass 1 uses D_t
   // for dS and dQ.
-  float Dt = tok_ok ? (sDp[0][li] + sDp[1][li]) + (sDp[2][li] + sDp[3][li]) : 0.f, dsum = 0.f;
-  if (!exact_d && tok_ok && wave == 0 && lh == 0) {
-    a.Dvec[st] = Dt;
-    a.lse2[st] = lse2;
+  //
+  // A step: each wave forms partial S and dP tiles over its embedding slice and writes
+  // them to LDS; after a barrier wave w sums the four partials of tokens 8w .. 8w + 7
+  // only (lane: token T = 8w + lane / 8, key rows 4q .. 4q + 3 with q = lane % 8), forms
+  // P and dS for them and writes dS as bf16; after a second barrier every wave reads the
+  // whole dS tile as the B operand of dQ^T += K^T dS^T.  Next step's partials are written
+  // only after every wave has passed the second barrier, i.e. finished its sums; the K
+  // slice in LDS is private to its wave.
+  const float Dt = tok_ok ? (sDp[0][li] + sDp[1][li]) + (sDp[2][li] + sDp[3][li]) : 0.f;
+  if (wave == 0 && lh == 0) {
+    sTokLse[li] = lse2;
+    sTokD[li] = Dt;
+    if (!exact_d && tok_ok) {
+      a.Dvec[st] = Dt;
+      a.lse2[st] = lse2;
+    }
   }
+  const int rT = 8 * wave + (lane >> 3), rq = lane & 7;       // reduce phase: token, key quad
+  const int rtok = t0 + rT;
+  const bool rtok_ok = rtok < a.S;
+  const int rsrc = part_off(rT + 32 * (rq & 1), rq >> 1);      // its four values in a partial tile
+  float dsum = 0.f;
   for (int pass = exact_d ? 0 : 1; pass < 2; ++pass) {
     if (nsteps > 0) load_step(0);
     for (int step = 0; step < nsteps; ++step) {
@@ -162,55 +184,55 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
       __syncthreads();
       if (step + 1 < nsteps) load_step(step + 1);
 
+      // reduce phase: token rT, key rows 4 rq + e of the step
+      f32x4 sr = *(const f32x4*)&sS[0][rsrc], pr = *(const f32x4*)&sP[0][rsrc];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
+      for (int w2 = 1; w2 < 4; ++w2) {
+        const f32x4 s4 = *(const f32x4*)&sS[w2][rsrc];
+        const f32x4 p4 = *(const f32x4*)&sP[w2][rsrc];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sr[e] += s4[e];
+          pr[e] += p4[e];
+        }
       }
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 s4 = *(const f32x4*)&sS[w2][part_off(lane, g)];
-          const f32x4 p4 = *(const f32x4*)&sP[w2][part_off(lane, g)];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            s[4 * g + e] += s4[e];
-            dp[4 * g + e] += p4[e];
-          }
-        }
-      // weights of (token li, row 8(r>>2) + 4lh + (r&3)), as in the forward kernel
-      float wt[16];
+      float wt[4];
       if (step < nwin) {
-        const int p0 = wstart + 32 * step + 4 * lh;
+        const int p0 = wstart + 32 * step + 4 * rq;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int p = p0 + 8 * (r >> 2) + (r & 3);
-          wt[r] = (tok_ok && p >= tok - W + 1 && p <= tok) ? 1.f : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) wt[e] = (rtok_ok && p0 + e >= rtok - W + 1 && p0 + e <= rtok) ? 1.f : 0.f;
       } else {
         const int u = (step - nwin) >> nsub_sh, h = (step - nwin) & (nsub - 1);
-        const float cnt = (float)((ucnt[u][li >> 2] >> (8 * (li & 3))) & 0xffu);
+        const float cnt = (float)((ucnt[u][rT >> 2] >> (8 * (rT & 3))) & 0xffu);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 32 * h + 8 * (r >> 2) + 4 * lh + (r & 3);
-          wt[r] = row < bs ? cnt : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) wt[e] = 32 * h + 4 * rq + e < bs ? cnt : 0.f;
       }
+      const float lseT = sTokLse[rT];
       if (pass == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dsum = fmaf(wt[r] * fast_exp2(fmaf(s[r], a.scale_log2, -lse2)), dp[r], dsum);
+        for (int e = 0; e < 4; ++e) dsum = fmaf(wt[e] * fast_exp2(fmaf(sr[e], a.scale_log2, -lseT)), pr[e], dsum);
       } else {
+        const float DT = sTokD[rT];
+        float ds[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = wt[r] * fast_exp2(fmaf(s[r], a.scale_log2, -lse2));
-          dp[r] = p * (dp[r] - Dt);                    // dS
+        for (int e = 0; e < 4; ++e) {
+          const float pe = wt[e] * fast_exp2(fmaf(sr[e], a.scale_log2, -lseT));
+          ds[e] = pe * (pr[e] - DT);
         }
+        u32x2 w2v;
+        w2v[0] = pack_bf16x2(ds[0], ds[1]);
+        w2v[1] = pack_bf16x2(ds[2], ds[3]);
+        *(u32x2*)&sDS[rT * kDsPitch + 2 * rq] = w2v;
+      }
+      __syncthreads();
+      if (pass == 1) {
+        // B operand for keys 16 ks + {4 lh .. 4 lh + 3, 8 + 4 lh .. 8 + 4 lh + 3} of token
+        // li: the key order of the transposed K reads below
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          u32x4 pb;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(dp[8 * ks + 2 * w], dp[8 * ks + 2 * w + 1]);
+          const uint32_t* dr = &sDS[li * kDsPitch + 8 * ks + 2 * lh];
+          const u32x2 lo = *(const u32x2*)dr, hi = *(const u32x2*)(dr + 4);
+          const u32x4 pb = {lo[0], lo[1], hi[0], hi[1]};
           const bf16x8 dsb = as_bf16x8(pb);
 #pragma unroll
           for (int db = 0; db < kUDW / 32; ++db) {
@@ -220,15 +242,22 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
           }
         }
       }
-      __syncthreads();                                 // sS / sP / sK are rewritten next step
     }
     if (pass == 0) {
-      // the two half-waves hold different rows of each step; every wave has the full sums
-      Dt = tok_ok ? dsum + other_half(dsum) : 0.f;
-      if (tok_ok && wave == 0 && lh == 0) {
-        a.Dvec[st] = Dt;
-        a.lse2[st] = lse2;
+      // D of token rT: the sum over its eight key-quad lanes
+      float d = dsum;
+      d += __shfl_xor(d, 1);
+      d += __shfl_xor(d, 2);
+      d += __shfl_xor(d, 4);
+      if (rq == 0) {
+        sTokD[rT] = rtok_ok ? d : 0.f;
+        if (rtok_ok) {
+          const size_t rst = (size_t)b * a.S + rtok;
+          a.Dvec[rst] = d;
+          a.lse2[rst] = sTokLse[rT];
+        }
       }
+      __syncthreads();
     }
   }
 
