@@ -344,28 +344,63 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   // slots (up to bs * top_n on row 0 under the -1 clamp), so P and dS enter the MFMAs as
   // a bf16 pair hi + lo: one bf16 rounding of the merged weight would cost as much as
   // that many roundings of the separate slots.
-  auto tile = [&](auto tokfn, bool win) {
-    // gather: 32 tokens x 16 chunks of 16 bytes per tensor per wave -> 8 per lane
+  // A tile's gathered rows in registers (32 tokens x 16 chunks of 16 bytes per tensor
+  // per wave: 8 per lane) and the statistics of token tid < 32; gathered one tile ahead
+  // where the next tile's tokens are already listed, so the gather's latency overlaps the
+  // current tile's work.
+  struct Gathered {
+    u32x4 q[8], g[8];
+    float lse, d, wa, wb;
+    int t;
+  };
+  auto gather = [&](auto tokfn, Gathered& G) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int cidx = lane + 64 * u, i = cidx >> 4, ch = cidx & 15;
       float wa, wb;
       const int t = tokfn(i, wa, wb);
       const uint32_t off = t >= 0 ? (uint32_t)t * row_b + 2u * (e0 + 8 * ch) : 0xffffffffu;
-      *(u32x4*)&sQ[wave][QL::idx(i, 8 * ch)] = buf_load16(rq, off, 0);
-      *(u32x4*)&sG[wave][QL::idx(i, 8 * ch)] = buf_load16(rg, off, 0);
+      G.q[u] = buf_load16(rq, off, 0);
+      G.g[u] = buf_load16(rg, off, 0);
     }
+    G.lse = INFINITY;
+    G.d = 0.f;
+    G.wa = 0.f;
+    G.wb = 0.f;
+    G.t = -1;
     if (tid < kUQ) {
       float wa, wb;
       const int t = tokfn(tid, wa, wb);
       const size_t st = (size_t)b * a.S + (t >= 0 ? t : 0);
-      sLse[tid] = t >= 0 ? a.lse2[st] : INFINITY;
-      sD[tid] = t >= 0 ? a.Dvec[st] : 0.f;
-      sWa[tid] = t >= 0 ? wa : 0.f;
-      sWb[tid] = t >= 0 ? wb : 0.f;
-      sTok[tid] = t;
+      if (t >= 0) {
+        G.lse = a.lse2[st];
+        G.d = a.Dvec[st];
+        G.wa = wa;
+        G.wb = wb;
+      }
+      G.t = t;
     }
+  };
+  // Stores a gathered tile to LDS (the previous tile's reads ended at its last barrier).
+  auto store = [&](const Gathered& G) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int cidx = lane + 64 * u, i = cidx >> 4, ch = cidx & 15;
+      *(u32x4*)&sQ[wave][QL::idx(i, 8 * ch)] = G.q[u];
+      *(u32x4*)&sG[wave][QL::idx(i, 8 * ch)] = G.g[u];
+    }
+    if (tid < kUQ) {
+      sLse[tid] = G.lse;
+      sD[tid] = G.d;
+      sWa[tid] = G.wa;
+      sWb[tid] = G.wb;
+      sTok[tid] = G.t;
+    }
+  };
+  // The tile's work once its rows are in LDS; `next` (if any) is gathered meanwhile.
+  auto compute = [&](bool win, auto&& next) {
     __syncthreads();
+    next();
     f32x16 s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -450,13 +485,16 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   // 1. Window slots: token t reads rows t - W + 1 .. t, so the tile's rows are read by
   //    tokens r0 .. r0 + 31 + W - 1, one slot per (token, row) pair in its window.
   const int wend = min(a.S, r0 + 32 + W - 1);
+  Gathered G;
   for (int tw = r0; tw < wend; tw += kUQ) {
-    tile([&](int i, float& wa, float& wb) -> int {
+    gather([&](int i, float& wa, float& wb) -> int {
       const int t = tw + i;
       wa = 0.f;
       wb = 0.f;
       return t < wend ? t : -1;
-    }, true);
+    }, G);
+    store(G);
+    compute(true, [] {});
   }
 
   // 2. Selected slots: tokens that list block c (each listing = bs slots, one per row),
@@ -509,13 +547,21 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
     }
     __syncthreads();
     int head = 0;
-    while (have - head >= kUQ) {
-      tile([&](int i, float& wa, float& wb) -> int {
-        const int e = lstC[head + i];
+    auto listed = [&](int h) {
+      return [&, h](int i, float& wa, float& wb) -> int {
+        const int e = lstC[h + i];
         wa = (float)(e & 0xff);
         wb = (float)(32 * (e >> 8));
-        return lstT[head + i];
-      }, false);
+        return lstT[h + i];
+      };
+    };
+    if (have - head >= kUQ) gather(listed(head), G);
+    while (have - head >= kUQ) {
+      store(G);
+      const bool more = have - head >= 2 * kUQ;
+      compute(false, [&] {
+        if (more) gather(listed(head + kUQ), G);
+      });
       head += kUQ;
     }
     // move the leftover (< 32 entries) to the front
@@ -534,7 +580,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   }
   const int rest = s_npend;
   if (rest > 0) {
-    tile([&](int i, float& wa, float& wb) -> int {
+    gather([&](int i, float& wa, float& wb) -> int {
       if (i >= rest) {
         wa = 0.f;
         wb = 0.f;
@@ -544,7 +590,9 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
       wa = (float)(e & 0xff);
       wb = (float)(32 * (e >> 8));
       return lstT[i];
-    }, false);
+    }, G);
+    store(G);
+    compute(false, [] {});
   }
 
   if (key_ok) {
