@@ -293,6 +293,9 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   __shared__ __attribute__((aligned(16))) float sD[kUQ];
   __shared__ float sWa[kUQ], sWb[kUQ];               // per token: weight of every row / extra on row 0
   __shared__ int sTok[kUQ];
+  // P and dS of the tile as bf16 hi and lo parts, [key][token] at a 34-word row pitch
+  constexpr int kTPitch = 34;
+  __shared__ __attribute__((aligned(16))) uint32_t sPD[4][32 * kTPitch];
   __shared__ int lstT[kSpList];
   __shared__ int lstC[kSpList];                      // count | (count of -1 entries) << 8
   __shared__ int sWaveN[kSpScan][4];
@@ -420,52 +423,72 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
       *(f32x4*)&sP[wave][part_off(lane, g)] = p4;
     }
     __syncthreads();
+    // Reduce-scatter: wave w sums the four partials of keys 8w .. 8w + 7 only (lane: key
+    // rK = 8w + lane / 8, tokens 4 rq .. 4 rq + 3 with rq = lane % 8), forms P and dS as
+    // bf16 hi + lo parts and shares them; after the next barrier every wave reads the
+    // whole tiles as B operands, in the token order of its transposed Q / dO reads.
+    {
+      const int rK = 8 * wave + (lane >> 3), rq = lane & 7;
+      const int rkey = r0 + rK;
+      const int rsrc = part_off(rK + 32 * (rq & 1), rq >> 1);
+      f32x4 sr = *(const f32x4*)&sS[0][rsrc], pr = *(const f32x4*)&sP[0][rsrc];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.f;
-      dp[r] = 0.f;
-    }
-#pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 s4 = *(const f32x4*)&sS[w2][part_off(lane, g)];
-        const f32x4 p4 = *(const f32x4*)&sP[w2][part_off(lane, g)];
+      for (int w2 = 1; w2 < 4; ++w2) {
+        const f32x4 s4 = *(const f32x4*)&sS[w2][rsrc];
+        const f32x4 p4 = *(const f32x4*)&sP[w2][rsrc];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s[4 * g + e] += s4[e];
-          dp[4 * g + e] += p4[e];
+          sr[e] += s4[e];
+          pr[e] += p4[e];
         }
       }
-    // lane = key row li; register r = token 8(r>>2) + 4lh + (r&3) of the tile
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 lse4 = *(const f32x4*)&sLse[8 * g + 4 * lh];
-      const f32x4 d4 = *(const f32x4*)&sD[8 * g + 4 * lh];
+      const f32x4 lse4 = *(const f32x4*)&sLse[4 * rq];
+      const f32x4 d4 = *(const f32x4*)&sD[4 * rq];
+      float pv[4], dv4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 8 * g + 4 * lh + e, r = 4 * g + e;
+        const int i = 4 * rq + e;
         const int t = sTok[i];
-        const float w = win ? ((t >= 0 && key >= t - W + 1 && key <= t) ? 1.f : 0.f)
-                            : sWa[i] + (li == 0 ? sWb[i] : 0.f);
-        const float p = key_ok ? w * fast_exp2(fmaf(s[r], a.scale_log2, -lse4[e])) : 0.f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - d4[e]);
+        const float w = win ? ((t >= 0 && rkey >= t - W + 1 && rkey <= t) ? 1.f : 0.f)
+                            : sWa[i] + (rK == 0 ? sWb[i] : 0.f);
+        const float p = rkey < a.S ? w * fast_exp2(fmaf(sr[e], a.scale_log2, -lse4[e])) : 0.f;
+        pv[e] = p;
+        dv4[e] = p * (pr[e] - d4[e]);
+      }
+      const int o = rK * kTPitch + 2 * rq;
+      u32x2 ph, sh;
+      ph[0] = pack_bf16x2(pv[0], pv[1]);
+      ph[1] = pack_bf16x2(pv[2], pv[3]);
+      sh[0] = pack_bf16x2(dv4[0], dv4[1]);
+      sh[1] = pack_bf16x2(dv4[2], dv4[3]);
+      *(u32x2*)&sPD[0][o] = ph;
+      *(u32x2*)&sPD[1][o] = sh;
+      if (!win) {
+        u32x2 pl, sl;
+        pl[0] = pack_bf16x2(pv[0] - bf16_lo(ph[0]), pv[1] - bf16_hi(ph[0]));
+        pl[1] = pack_bf16x2(pv[2] - bf16_lo(ph[1]), pv[3] - bf16_hi(ph[1]));
+        sl[0] = pack_bf16x2(dv4[0] - bf16_lo(sh[0]), dv4[1] - bf16_hi(sh[0]));
+        sl[1] = pack_bf16x2(dv4[2] - bf16_lo(sh[1]), dv4[3] - bf16_hi(sh[1]));
+        *(u32x2*)&sPD[2][o] = pl;
+        *(u32x2*)&sPD[3][o] = sl;
       }
     }
+    __syncthreads();
+    // B operand of tile k: key li, tokens 16 ks + {4 lh .. 4 lh + 3, 8 + 4 lh .. + 3}
+    auto bop = [&](int k, int ks) -> bf16x8 {
+      const uint32_t* r = &sPD[k][li * kTPitch + 8 * ks + 2 * lh];
+      const u32x2 lo = *(const u32x2*)r, hi = *(const u32x2*)(r + 4);
+      const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+      return as_bf16x8(w);
+    };
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      u32x4 pb, sb, pl, sl;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float p0 = s[8 * ks + 2 * w], p1 = s[8 * ks + 2 * w + 1];
-        const float d0 = dp[8 * ks + 2 * w], d1 = dp[8 * ks + 2 * w + 1];
-        pb[w] = pack_bf16x2(p0, p1);
-        sb[w] = pack_bf16x2(d0, d1);
-        pl[w] = pack_bf16x2(p0 - bf16_lo(pb[w]), p1 - bf16_hi(pb[w]));
-        sl[w] = pack_bf16x2(d0 - bf16_lo(sb[w]), d1 - bf16_hi(sb[w]));
+      const bf16x8 pbf = bop(0, ks), sbf = bop(1, ks);
+      bf16x8 plf = pbf, slf = sbf;
+      if (!win) {
+        plf = bop(2, ks);
+        slf = bop(3, ks);
       }
-      const bf16x8 pbf = as_bf16x8(pb), sbf = as_bf16x8(sb), plf = as_bf16x8(pl), slf = as_bf16x8(sl);
 #pragma unroll
       for (int db = 0; db < kUDW / 32; ++db) {
         const int o0 = tr_off + QL::rows(16 * ks) + 32 * db, o1 = o0 + QL::rows(8);
