@@ -26,13 +26,6 @@ namespace rea {
 //   transposed with ds_read_b64_tr_b16).
 // A block shared by several tokens is read once for all of them.
 
-// Workgroup barrier over LDS only: this wave's LDS operations complete, then s_barrier
-// (the memory clobber keeps LDS accesses on their side of it).  __syncthreads also waits
-// for every vector memory load in flight, which here are the next step's gathers.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
   // LDS: partial scores 16 KiB | V slices 40 KiB (setup scratch reuses it) | counts 16 KiB
   __shared__ __attribute__((aligned(16))) float sS[4][64 * 16];

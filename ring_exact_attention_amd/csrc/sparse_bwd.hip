@@ -40,6 +40,12 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   // both patterns free of bank conflicts (also the setup scratch)
   using KL = TileLayout<kUDW, kBothRead>;
   __shared__ __attribute__((aligned(16))) __bf16 sK[4][KL::elems(kUQ)];
+  // V slices by rows at a 272-byte pitch (conflict-free row reads), copied straight from
+  // the gathered rows: nine 1 KB copies per wave, the last one partly into the padding
+  using VL = TileLayout<kUDW, kRowRead>;
+  constexpr int kVRowSlots = VL::PITCH / 8;                      // 16-byte slots per row
+  constexpr int kVCopies = (kUQ * kVRowSlots + 63) / 64;
+  __shared__ __attribute__((aligned(16))) __bf16 sV[4][kVCopies * 512];
   __shared__ uint32_t ucnt[kUMaxEnt][kUQ / 4];
   __shared__ int ublk[kUMaxEnt];
   __shared__ int s_nu;
@@ -112,15 +118,37 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
     const int c = ublk[u];
     return c < 0 ? 0 : c * bs + 32 * h + r;
   };
-  // K and V rows as A operands: lane (li, lh) holds row li, e0 + 16kk + 8lh ..+7.
-  u32x4 kbuf[kUDW / 16], vbuf[kUDW / 16];
-  auto load_step = [&](int step) {
-    const int pk = row_pos(step, li);
+  // K rows as A operands in registers: lane (li, lh) holds row li, e0 + 16kk + 8lh ..+7.
+  // An A-operand load puts 32 rows in flight, 32 bytes of each, and the load path serves
+  // about one cache line per clock, so issuing these gathers had become the longest part
+  // of a step; V rows therefore go straight into this wave's LDS rows instead (16 lanes
+  // per row: an instruction moves four whole rows) and are read back as A operands.
+  // Both loads are issued unconditionally (a step past the end reads out of range), so a
+  // step's single wait counts exactly.
+  u32x4 kbuf[kUDW / 16];
+  auto load_k = [&](int step) {
+    const int pk = step < nsteps ? row_pos(step, li) : -1;
 #pragma unroll
-    for (int kk = 0; kk < kUDW / 16; ++kk) {
-      const uint32_t off = (uint32_t)pk * row_b + 2u * (e0 + 16 * kk + 8 * lh);
-      kbuf[kk] = buf_load16(rk, off, 0);
-      vbuf[kk] = buf_load16(rv, off, 0);
+    for (int kk = 0; kk < kUDW / 16; ++kk)
+      kbuf[kk] = buf_load16(rk, (uint32_t)pk * row_b + 2u * (e0 + 16 * kk + 8 * lh), 0);
+  };
+  auto dma_v = [&](int step) {
+    const bool live = step < nsteps;
+    bool all0 = false;
+    int base = 0;
+    if (live && step < nwin) {
+      base = wstart + 32 * step;
+    } else if (live) {
+      const int c = ublk[(step - nwin) >> nsub_sh];
+      all0 = c < 0;
+      base = c * bs + 32 * ((step - nwin) & (nsub - 1));
+    }
+#pragma unroll
+    for (int n = 0; n < kVCopies; ++n) {
+      const int j = 64 * n + lane, r = j / kVRowSlots, ch = j - kVRowSlots * r;
+      const int pv = all0 ? 0 : base + r;
+      const bool ok = live && ch < 16 && r < kUQ;
+      dma16(rv, &sV[wave][512 * n], ok ? (uint32_t)pv * row_b + 2u * (e0 + 8 * ch) : 0xffffffffu);
     }
   };
 
@@ -157,7 +185,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
   const int rsrc = part_off(rT + 32 * (rq & 1), rq >> 1);      // its four values in a partial tile
   float dsum = 0.f;
   for (int pass = exact_d ? 0 : 1; pass < 2; ++pass) {
-    if (nsteps > 0) load_step(0);
+    load_k(0);
+    dma_v(0);
     for (int step = 0; step < nsteps; ++step) {
       f32x16 s, dp;
 #pragma unroll
@@ -165,11 +194,15 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
         s[r] = 0.f;
         dp[r] = 0.f;
       }
+      // this step's K rows and V slice have landed (the memory clobber keeps the V reads
+      // below the wait)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
       for (int kk = 0; kk < kUDW / 16; ++kk) {
         s = mfma32(as_bf16x8(kbuf[kk]), qreg[kk], s);
-        dp = mfma32(as_bf16x8(vbuf[kk]), doreg[kk], dp);
+        dp = mfma32(*(const bf16x8*)&sV[wave][VL::idx(li, 16 * kk + 8 * lh)], doreg[kk], dp);
       }
+
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 s4 = {s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
@@ -181,8 +214,12 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
 #pragma unroll
         for (int kk = 0; kk < kUDW / 16; ++kk) *(u32x4*)&sK[wave][KL::idx(li, 16 * kk + 8 * lh)] = kbuf[kk];
       }
-      __syncthreads();
-      if (step + 1 < nsteps) load_step(step + 1);
+      // the dP MFMAs have consumed this wave's reads of its V slice; issued after this
+      // step's other LDS stores, which the compiler would otherwise hold back until the
+      // copies land
+      dma_v(step + 1);
+      lds_barrier();                                   // partial tiles written
+      load_k(step + 1);
 
       // reduce phase: token rT, key rows 4 rq + e of the step
       f32x4 sr = *(const f32x4*)&sS[0][rsrc], pr = *(const f32x4*)&sP[0][rsrc];
@@ -224,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
         w2v[1] = pack_bf16x2(ds[2], ds[3]);
         *(u32x2*)&sDS[rT * kDsPitch + 2 * rq] = w2v;
       }
-      __syncthreads();
+      lds_barrier();                                   // dS tile written
       if (pass == 1) {
         // B operand for keys 16 ks + {4 lh .. 4 lh + 3, 8 + 4 lh .. 8 + 4 lh + 3} of token
         // li: the key order of the transposed K reads below

@@ -19,6 +19,14 @@ constexpr int kUMaxEnt = 512;        // 32 tokens x top_n (<= 16)
 // lane-major layout (16 floats per lane) puts every fourth lane on the same banks.
 __device__ __forceinline__ int part_off(int lane, int g) { return 4 * (64 * g + lane); }
 
+// Workgroup barrier over LDS only: this wave's LDS operations complete, then s_barrier
+// (the memory clobber keeps LDS accesses on their side of it).  __syncthreads also waits
+// for every vector memory load in flight (its release fence covers the loads that write
+// LDS), which in the walks below are the next step's gathers.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Unit index (b * n_per_seq + unit) of workgroup wg.  Workgroups are dispatched
 // round-robin over the 8 XCDs (wg % 8), each with its own L2; with xcd_seq > 0 every XCD
 // takes the units of one sequence (xcd_seq XCDs share a sequence, taking its units in
