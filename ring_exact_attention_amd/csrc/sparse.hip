@@ -223,7 +223,8 @@ __global__ __launch_bounds__(256, 2) void sparse_union_kernel(SparseArgs a) {
       }
     }
     // the P V MFMAs have consumed this wave's transposed reads of its slice, which the
-    // next step's rows may now overwrite
+    // next step's rows may now overwrite (the wait and clobber keep the copies after them)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     dma_v(step + 1);
     lds_barrier();                                             // sS is rewritten next step
   }

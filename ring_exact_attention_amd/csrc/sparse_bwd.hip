@@ -216,7 +216,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(SparseBwdArgs a) 
       }
       // the dP MFMAs have consumed this wave's reads of its V slice; issued after this
       // step's other LDS stores, which the compiler would otherwise hold back until the
-      // copies land
+      // copies land (the wait and clobber keep the copies after the reads)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       dma_v(step + 1);
       lds_barrier();                                   // partial tiles written
       load_k(step + 1);
