@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   __shared__ __attribute__((aligned(16))) uint32_t sPD[4][32 * kTPitch];
   __shared__ int lstT[kSpList];
   __shared__ int lstC[kSpList];                      // count | (count of -1 entries) << 8
-  __shared__ int sWaveN[kSpScan][4];
+  __shared__ int sWaveN[4];
   __shared__ int s_npend;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -564,48 +564,75 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   //    which lists strictly earlier blocks) is handled, and the order is fixed.
   if (tid == 0) s_npend = 0;
   __syncthreads();
-  // A pass covers 256 * kSpScan tokens (token base0 + 256 k + tid for k < kSpScan):
-  // every selection load of the pass is issued before the first compare (the top-n loop
-  // is unrolled to its bound of 16), and the pass's entries are appended in token order
-  // with one ballot per 256-token chunk and one prefix over the pass.
+  // A pass covers 256 * kSpScan tokens: thread tid takes the consecutive tokens
+  // base0 + kSpScan tid + k (k < kSpScan), whose selections are contiguous, so with top_n a
+  // multiple of 4 they come in 16-byte loads (kSpScan top_n / 4 per thread instead of
+  // kSpScan top_n); the entries are appended in token order (lane-major, then k).
+  const bool vec_sel = (n & 3) == 0 && ((uintptr_t)a.sel & 15) == 0;
   for (int base0 = 0; base0 < a.S; base0 += 256 * kSpScan) {
     int code[kSpScan];                                 // count | (count of -1 entries) << 8
+    const int tb = base0 + kSpScan * tid;              // this thread's first token
+    const bool scan_blk = c < a.S / a.sel_block;
+    const int32_t* rowp = a.sel + ((size_t)b * a.S + (tb < a.S ? tb : 0)) * n;
+    if (vec_sel && scan_blk && tb + kSpScan <= a.S) {
+      int cnt[kSpScan], neg[kSpScan];
 #pragma unroll
-    for (int k = 0; k < kSpScan; ++k) {
-      const int t = base0 + 256 * k + tid;
-      const bool scan = t < a.S && c < a.S / a.sel_block;
-      const int32_t* row = a.sel + ((size_t)b * a.S + (scan ? t : 0)) * n;
-      int e[16];
+      for (int k = 0; k < kSpScan; ++k) cnt[k] = neg[k] = 0;
+      // kSpScan * n entries, n / 4 16-byte pieces per token
+      for (int j4 = 0; j4 < n / 4; ++j4) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) e[j] = scan && j < n ? row[j] : c + 1;
-      int cnt = 0, neg = 0;
+        for (int k = 0; k < kSpScan; ++k) {
+          const u32x4 e4 = *(const u32x4*)(rowp + k * n + 4 * j4);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        cnt += e[j] == c;
-        neg += e[j] < 0;
+          for (int x = 0; x < 4; ++x) {
+            cnt[k] += (int)e4[x] == c;
+            neg[k] += (int)e4[x] < 0;
+          }
+        }
       }
-      code[k] = cnt | ((c != 0 ? 0 : neg) << 8);
+#pragma unroll
+      for (int k = 0; k < kSpScan; ++k) code[k] = cnt[k] | ((c != 0 ? 0 : neg[k]) << 8);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSpScan; ++k) {
+        const int t = tb + k;
+        const bool scan = t < a.S && scan_blk;
+        const int32_t* row = rowp + k * n;
+        int e[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) e[j] = scan && j < n ? row[j] : c + 1;
+        int cnt = 0, neg = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          cnt += e[j] == c;
+          neg += e[j] < 0;
+        }
+        code[k] = cnt | ((c != 0 ? 0 : neg) << 8);
+      }
     }
-    uint64_t mask[kSpScan];
+    // position: entries of the lanes below, then of this lane's earlier tokens
+    const uint64_t below = (1ull << lane) - 1;
+    int pre = 0, tot = 0;
 #pragma unroll
     for (int k = 0; k < kSpScan; ++k) {
-      mask[k] = __ballot(code[k] != 0);
-      if (lane == 0) sWaveN[k][wave] = __popcll(mask[k]);
+      const uint64_t mk = __ballot(code[k] != 0);
+      pre += __popcll(mk & below);
+      tot += __popcll(mk);
     }
+    if (lane == 0) sWaveN[wave] = tot;
     __syncthreads();
     const int npend = s_npend;
-    int have = npend;
+    int pos = npend + pre;
+    for (int w2 = 0; w2 < wave; ++w2) pos += sWaveN[w2];
 #pragma unroll
     for (int k = 0; k < kSpScan; ++k) {
-      int before = have;
-      for (int w2 = 0; w2 < wave; ++w2) before += sWaveN[k][w2];
       if (code[k] != 0) {
-        const int pos = before + __popcll(mask[k] & ((1ull << lane) - 1));
-        lstT[pos] = base0 + 256 * k + tid;
+        lstT[pos] = tb + k;
         lstC[pos] = code[k];
+        ++pos;
       }
-      have += sWaveN[k][0] + sWaveN[k][1] + sWaveN[k][2] + sWaveN[k][3];
     }
+    const int have = npend + sWaveN[0] + sWaveN[1] + sWaveN[2] + sWaveN[3];
     __syncthreads();
     int head = 0;
     auto listed = [&](int h) {

@@ -212,7 +212,7 @@ def sparse_grads(gpu, q, k, v, do, sel, W, bs=32):
 
 
 @pytest.mark.parametrize("B,S,n,W", [(1, 200, 4, 32), (2, 160, 8, 7), (1, 96, 8, 1), (1, 300, 8, 64),
-                                     (2, 256, 16, 32)])
+                                     (2, 256, 16, 32), (1, 203, 8, 32), (1, 450, 12, 16)])
 def test_sparse_backward_small(gpu, B, S, n, W):
     E, bs = 512, 32
     q, k, v, do = rnd((B, S, E), 60 + S), rnd((B, S, E), 61 + S), rnd((B, S, E), 62 + S), rnd((B, S, E), 63 + S)
@@ -224,10 +224,12 @@ def test_sparse_backward_small(gpu, B, S, n, W):
     check_close("dv", dv, dv_r, "bf16")
 
 
-def test_sparse_backward_handmade_selection(gpu):
+@pytest.mark.parametrize("S,n", [(224, 6), (203, 8)])
+def test_sparse_backward_handmade_selection(gpu, S, n):
     """Duplicates, several -1 entries (all collected by row 0), tokens listing blocks at or
-    after their own."""
-    B, S, E, bs, n, W = 2, 224, 512, 32, 6, 20
+    after their own; top_n 8 with a token count that is not a multiple of 4 takes the
+    16-byte reads of the selection with a partial last group."""
+    B, E, bs, W = 2, 512, 32, 20
     q, k, v, do = rnd((B, S, E), 45), rnd((B, S, E), 46), rnd((B, S, E), 47), rnd((B, S, E), 48)
     sel = handmade_selection(B, S, bs, n, 49)
     dq, dk, dv = sparse_grads(gpu, q, k, v, do, sel, W)
