@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   };
   // The tile's work once its rows are in LDS; `next` (if any) is gathered meanwhile.
   auto compute = [&](bool win, auto&& next) {
-    __syncthreads();
+    lds_barrier();
     next();
     f32x16 s, dp;
 #pragma unroll
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
       *(f32x4*)&sS[wave][part_off(lane, g)] = s4;
       *(f32x4*)&sP[wave][part_off(lane, g)] = p4;
     }
-    __syncthreads();
+    lds_barrier();
     // Reduce-scatter: wave w sums the four partials of keys 8w .. 8w + 7 only (lane: key
     // rK = 8w + lane / 8, tokens 4 rq .. 4 rq + 3 with rq = lane % 8), forms P and dS as
     // bf16 hi + lo parts and shares them; after the next barrier every wave reads the
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
         *(u32x2*)&sPD[3][o] = sl;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // B operand of tile k: key li, tokens 16 ks + {4 lh .. 4 lh + 3, 8 + 4 lh .. + 3}
     auto bop = [&](int k, int ks) -> bf16x8 {
       const uint32_t* r = &sPD[k][li * kTPitch + 8 * ks + 2 * lh];
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
         }
       }
     }
-    __syncthreads();                                   // LDS tiles are rewritten by the next tile
+    lds_barrier();                                   // LDS tiles are rewritten by the next tile
   };
 
   // 1. Window slots: token t reads rows t - W + 1 .. t, so the tile's rows are read by
@@ -563,18 +563,48 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   //    Every token is scanned, in order, so any selection (not only block_select's,
   //    which lists strictly earlier blocks) is handled, and the order is fixed.
   if (tid == 0) s_npend = 0;
-  __syncthreads();
+  lds_barrier();
   // A pass covers 256 * kSpScan tokens: thread tid takes the consecutive tokens
   // base0 + kSpScan tid + k (k < kSpScan), whose selections are contiguous, so with top_n a
   // multiple of 4 they come in 16-byte loads (kSpScan top_n / 4 per thread instead of
   // kSpScan top_n); the entries are appended in token order (lane-major, then k).
   const bool vec_sel = (n & 3) == 0 && ((uintptr_t)a.sel & 15) == 0;
+  const bool scan_blk = c < a.S / a.sel_block;
+  // With top_n <= 8 the next pass's pieces are loaded into registers before this pass's
+  // tiles run (the barriers are LDS-only, so the loads stay in flight through them).
+  const bool pf_sel = vec_sel && n <= 8;
+  u32x4 selpf[kSpScan][2];
+  bool selpf_ok = false;
+  auto sel_fetch = [&](int base0) {
+    const int tb = base0 + kSpScan * tid;
+    selpf_ok = scan_blk && tb + kSpScan <= a.S;
+    const int32_t* rowp = a.sel + ((size_t)b * a.S + (selpf_ok ? tb : 0)) * n;
+#pragma unroll
+    for (int k = 0; k < kSpScan; ++k)
+#pragma unroll
+      for (int j4 = 0; j4 < 2; ++j4)
+        if (selpf_ok && 4 * j4 < n) selpf[k][j4] = *(const u32x4*)(rowp + k * n + 4 * j4);
+  };
+  if (pf_sel) sel_fetch(0);
   for (int base0 = 0; base0 < a.S; base0 += 256 * kSpScan) {
     int code[kSpScan];                                 // count | (count of -1 entries) << 8
     const int tb = base0 + kSpScan * tid;              // this thread's first token
-    const bool scan_blk = c < a.S / a.sel_block;
     const int32_t* rowp = a.sel + ((size_t)b * a.S + (tb < a.S ? tb : 0)) * n;
-    if (vec_sel && scan_blk && tb + kSpScan <= a.S) {
+    if (pf_sel && selpf_ok) {
+#pragma unroll
+      for (int k = 0; k < kSpScan; ++k) {
+        int cnt = 0, neg = 0;
+#pragma unroll
+        for (int j4 = 0; j4 < 2; ++j4)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int e = 4 * j4 < n ? (int)selpf[k][j4][x] : c + 1;
+            cnt += e == c;
+            neg += e < 0;
+          }
+        code[k] = cnt | ((c != 0 ? 0 : neg) << 8);
+      }
+    } else if (vec_sel && scan_blk && tb + kSpScan <= a.S) {
       int cnt[kSpScan], neg[kSpScan];
 #pragma unroll
       for (int k = 0; k < kSpScan; ++k) cnt[k] = neg[k] = 0;
@@ -610,6 +640,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
         code[k] = cnt | ((c != 0 ? 0 : neg) << 8);
       }
     }
+    if (pf_sel) sel_fetch(base0 + 256 * kSpScan);
     // position: entries of the lanes below, then of this lane's earlier tokens
     const uint64_t below = (1ull << lane) - 1;
     int pre = 0, tot = 0;
@@ -620,7 +651,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
       tot += __popcll(mk);
     }
     if (lane == 0) sWaveN[wave] = tot;
-    __syncthreads();
+    lds_barrier();
     const int npend = s_npend;
     int pos = npend + pre;
     for (int w2 = 0; w2 < wave; ++w2) pos += sWaveN[w2];
@@ -633,7 +664,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
       }
     }
     const int have = npend + sWaveN[0] + sWaveN[1] + sWaveN[2] + sWaveN[3];
-    __syncthreads();
+    lds_barrier();
     int head = 0;
     auto listed = [&](int h) {
       return [&, h](int i, float& wa, float& wb) -> int {
@@ -658,13 +689,13 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
       lt = lstT[head + tid];
       lc = lstC[head + tid];
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < have - head) {
       lstT[tid] = lt;
       lstC[tid] = lc;
     }
     if (tid == 0) s_npend = have - head;
-    __syncthreads();
+    lds_barrier();
   }
   const int rest = s_npend;
   if (rest > 0) {
