@@ -519,8 +519,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr bool BIAS = (EX & 1) != 0, DROP = (EX & 2) != 0;
   static_assert(DV <= D, "the v head dim may not exceed the q/k head dim");
   // Q and dO tiles of a step, two buffers each (the next step's rows are copied in while
-  // the current step runs)
-  __shared__ __attribute__((aligned(1024))) char sQG[2 * C::QB + 2 * C::GB];
+  // the current step runs).  Each buffer is an array of its own and the step loop is
+  // unrolled by two, so the compiler can tell the buffer being read from the one being
+  // copied into and does not hold the step's LDS reads behind the copies.
+  __shared__ __attribute__((aligned(1024))) char sQb0[C::QB];
+  __shared__ __attribute__((aligned(1024))) char sQb1[C::QB];
+  __shared__ __attribute__((aligned(1024))) char sGb0[C::GB];
+  __shared__ __attribute__((aligned(1024))) char sGb1[C::GB];
   __shared__ __attribute__((aligned(16))) __bf16 sVk[C::VL::elems(C::BK)];   // this workgroup's V rows
   __shared__ __attribute__((aligned(16))) float sLse[2][C::BQ];
   __shared__ __attribute__((aligned(16))) float sD[2][C::BQ];
@@ -652,9 +657,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     for (int i = 0; i < C::NI; ++i) {
       const int n = wave + 4 * i;
       if (n < C::QI) {
-        if (cpv[i]) dma16(rq, sQG + buf * C::QB + 1024 * n, cpo[i]);
+        if (cpv[i]) dma16(rq, (buf ? sQb1 : sQb0) + 1024 * n, cpo[i]);
       } else if (n < C::QI + C::GI) {
-        if (cpv[i]) dma16(rg, sQG + 2 * C::QB + buf * C::GB + 1024 * (n - C::QI), cpo[i]);
+        if (cpv[i]) dma16(rg, (buf ? sGb1 : sGb0) + 1024 * (n - C::QI), cpo[i]);
       }
     }
     if (tid < 2 * C::BQ) {
@@ -703,8 +708,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     if (BIAS && !bias_rows) bkey = *bias_ptr(hq);
   }
   __syncthreads();
-  int cur = 0;
-  while (have) {
+  // One query step on buffer CUR (the next step's rows go to the other one).
+  auto step = [&](auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
     int nhq = 0, nqs = 0, nrend = 0;
     const bool nhave = next_step(nhq, nqs, nrend);
 
@@ -737,8 +743,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     if (BIAS && !bias_rows && nhave) bkey = *bias_ptr(nhq);
     if (!empty) {
       const bool full = dmin >= a.lo_off && dmax <= a.hi_off && qs + C::BQ <= qe;
-      const __bf16* qt_ = (const __bf16*)(sQG + cur * C::QB);
-      const __bf16* gt_ = (const __bf16*)(sQG + 2 * C::QB + cur * C::GB);
+      const __bf16* qt_ = (const __bf16*)(cur ? sQb1 : sQb0);
+      const __bf16* gt_ = (const __bf16*)(cur ? sGb1 : sGb0);
       f32x16 dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -808,11 +814,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       store_step(cur ^ 1);
     }
     __syncthreads();
-    cur ^= 1;
     hq = nhq;
     qs = nqs;
     rend = nrend;
     have = nhave;
+  };
+  while (have) {
+    step(IntConst<0>{});
+    if (!have) break;
+    step(IntConst<1>{});
   }
 
   if (key_ok && a.kv_splits > 1) {

@@ -169,6 +169,12 @@ __device__ __forceinline__ int wg_index(int rev) {
   return rev ? (int)(gridDim.x - 1u - blockIdx.x) : (int)blockIdx.x;
 }
 
+// A compile-time int passed to a generic lambda (e.g. the buffer of an unrolled step).
+template <int V>
+struct IntConst {
+  static constexpr int value = V;
+};
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -317,10 +323,12 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 // 16-bit values (row j of a 16 x 4 block); lane i receives column i % 4 of rows
 // i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12.
 typedef short short4v __attribute__((ext_vector_type(4)));
+// The pointer is cast to the LDS address space directly (not through an integer), so
+// the compiler still sees which LDS array it reads: it then does not hold the read
+// behind copies in flight into other arrays.
 __device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
   typedef __attribute__((address_space(3))) short4v lds_s4;
-  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s4*)((__attribute__((address_space(3))) char*)((uintptr_t)p)));
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
   return __builtin_bit_cast(u32x2, r);
 }
 
