@@ -52,10 +52,28 @@ __global__ __launch_bounds__(256) void block_means_kernel(SelectArgs a) {
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// Largest value of x over the wavefront (a butterfly of lane exchanges; every lane gets it).
-__device__ __forceinline__ double wave_max_f64(double x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x = fmax(x, __shfl_xor(x, off));
+// The wavefront's maximum of x, in every lane: DPP within each row of 16 lanes (quad
+// swaps, then the half-row and row mirrors), then the row-swapping permutes; all VALU,
+// where a shuffle through ds_bpermute puts an LDS round trip on each of the six steps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor16_f32(float x) {   // lane i's value from lane i ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32_f32(float x) {   // ... from lane i ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));    // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));    // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_f32<0x141>(x));   // row_half_mirror: the two quads of each 8 lanes
+  x = fmaxf(x, dpp_f32<0x140>(x));   // row_mirror: the two halves of each 16-lane row
+  x = fmaxf(x, xor16_f32(x));
+  x = fmaxf(x, xor32_f32(x));
   return x;
 }
 
@@ -166,16 +184,22 @@ __global__ __launch_bounds__(256) void block_select_kernel(SelectArgs a) {
             // Empty list (a share's first chunk): only the chunk's n largest scores can
             // enter it, so keep the candidates at or above the n-th largest (counted with
             // multiplicity; ties at it survive and are ranked by index below) instead of
-            // ranking all of them against each other.
-            double cut = INFINITY;
+            // ranking all of them against each other.  The cut is taken on the scores
+            // rounded to fp32, which keeps their order (a >= b gives f(a) >= f(b)): the n-th
+            // largest rounded score is the rounding of the n-th largest score, so every
+            // candidate at or above the latter passes; the few more that round to the same
+            // value are ranked exactly below and drop out there.
+            const float vf = (float)v;
+            float cut = INFINITY;
             int cnt = 0;
             for (int it = 0; it < n && cnt < n; ++it) {
-              cut = wave_max_f64(cval && v < cut ? v : -INFINITY);
-              cnt += __popcll(__ballot(cval && v == cut));
+              cut = wave_max_f32(cval && vf < cut ? vf : -INFINITY);
+              cnt += __popcll(__ballot(cval && vf == cut));
             }
-            surv = cval && v >= cut;
+            surv = cval && vf >= cut;
           }
           const uint64_t P = __ballot(surv);
+          if (P == 0) continue;                          // nothing enters: the list stays
           const bool is_l = lane < kept0;
           const double ls = is_l ? best_s[t][lane] : 0.0;
           const int lc = is_l ? best_c[t][lane] : 0;

@@ -46,6 +46,33 @@ def test_select_exact_ties(gpu):
     np.testing.assert_array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("n", [1, 2])
+def test_select_scores_equal_in_fp32(gpu, n):
+    """Scores that differ only below fp32 resolution (block 7 = block 3 plus 2^-30 in one
+    dimension, block 9 = block 3): the first chunk's cut is taken on fp32-rounded scores,
+    so all three pass it and the exact ranking must put 7 first, then 3 before 9."""
+    B, S, E, bs = 1, 384, 64, 32
+    g = torch.Generator().manual_seed(11)
+    k = (torch.randint(-2, 3, (B, S, E), generator=g).float() * 2.0 ** -6).to(torch.bfloat16)
+    base = torch.zeros(E)
+    base[0] = 1.0
+    base[2] = 0.5
+    for c, extra in ((3, 0.0), (7, 2.0 ** -30), (9, 0.0)):
+        row = base.clone()
+        row[1] = extra
+        k[0, c * bs:(c + 1) * bs] = row.to(torch.bfloat16)
+    q = (torch.randint(-2, 3, (B, S, E), generator=g).float() * 2.0 ** -6).to(torch.bfloat16)
+    q[0, :, 0] = 1.0
+    q[0, :, 1] = 1.0
+    q[0, :, 2] = 1.0
+    idx = gpu.block_select(q.to(DEV), k.to(DEV), block_size=bs, top_n=n)
+    torch.cuda.synchronize()
+    ref = select.block_select(q, k, block_size=bs, top_n=n)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+    last = ref[0, -1]                                  # a token of the last query block
+    assert list(last) == ([7] if n == 1 else [3, 7])
+
+
 @pytest.mark.parametrize("n", [3, 8, 16])
 def test_select_split_candidates_ties(gpu, n):
     """Few query blocks against a long cache: each block's candidates are shared out over
