@@ -46,8 +46,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+  part = sum_lanes<LPR>(part);
   if (rowg < nrows && sub == 0) {
     const int h = (int)(rowg % a.Hq);
     const long long bs = rowg / a.Hq;
@@ -366,8 +365,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
           part = fmaf(bf16_lo(orow[i][w]), bf16_lo(gu[w]), part);
           part = fmaf(bf16_hi(orow[i][w]), bf16_hi(gu[w]), part);
         }
-#pragma unroll
-        for (int off = C::DCV / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+        part = sum_lanes<C::DCV>(part);
         if (orc == 0) sd[RPO * i + orr] = part;
       }
       Di = sd[li];

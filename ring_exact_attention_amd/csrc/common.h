@@ -169,6 +169,19 @@ __device__ __forceinline__ int wg_index(int rev) {
   return rev ? (int)(gridDim.x - 1u - blockIdx.x) : (int)blockIdx.x;
 }
 
+// Sum of x over each aligned group of N lanes (N = 2, 4, 8 or 16), in every lane of the
+// group: DPP quad swaps, then the half-row and row mirrors (VALU only; a shuffle goes
+// through an LDS permute).
+template <int N>
+__device__ __forceinline__ float sum_lanes(float x) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "groups of 2 to 16 lanes");
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+  if constexpr (N >= 4) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  if constexpr (N >= 8) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+  if constexpr (N >= 16) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
 // A compile-time int passed to a generic lambda (e.g. the buffer of an unrolled step).
 template <int V>
 struct IntConst {
