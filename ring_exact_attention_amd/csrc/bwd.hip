@@ -327,6 +327,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
       return make_rsrc_at((const __bf16*)tensor + (size_t)b * a.Sq * rs, (uint32_t)a.Sq * rs_b, so);
     };
     const bool fused = a.fused_stats != 0;
+    // the row's statistics are loaded now, with the first copies, rather than after the
+    // dO rows have landed (a third round trip to memory)
+    float l_in = 0.f, m_in = 0.f, lse_in = INFINITY, d_in = 0.f;
+    if (row_ok) {
+      if (fused) {
+        l_in = a.l[stat];
+        m_in = a.m[stat];
+      } else {
+        lse_in = a.lse2[stat];
+        d_in = a.Dvec[stat];
+      }
+    }
     u32x4 orow[NO];                                // O: row RPO*i + lane/DCV, chunk lane%DCV
     if (fused) {
       const __amdgpu_buffer_rsrc_t ro = rsrc_rows(a.o, o_rs);
@@ -369,7 +381,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
         if (orc == 0) sd[RPO * i + orr] = part;
       }
       Di = sd[li];
-      const float l = row_ok ? a.l[stat] : 0.f, m = row_ok ? a.m[stat] : 0.f;
+      const float l = l_in, m = m_in;
       if (a.has_sink)
         lse2 = lse2_with_sink(m * kLog2e, l, (a.sink ? a.sink[hq] : 0.f) * kLog2e);
       else
@@ -379,8 +391,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
         a.lse2[stat] = lse2;
       }
     } else if (row_ok) {
-      lse2 = a.lse2[stat];
-      Di = a.Dvec[stat];
+      lse2 = lse_in;
+      Di = d_in;
     }
     if (!row_ok) Di = 0.f;
     __syncthreads();                               // stage 1 on is refilled from step 0 on
