@@ -270,7 +270,11 @@ size_t attn_fwd_workspace_bytes(const attn_params* params);
  * reads a sequence row p passes scale dS_tj q_t to dk_p and P_tj dO_t to dv_p (the -1
  * clamp makes row 0 collect those slots; zero pads and rows past the end pass nothing).
  * q, k, v, o, dout, dq, dk, dv are bf16 [B, S, 512]; m, l fp32 [B, S] from the sparse
- * forward; flags must be 0.
+ * forward; flags must be 0.  The workspace holds D and the log-sum-exp per token and,
+ * while they take at most 64 MiB and S / 32 <= 1024, two bit masks per (batch, block)
+ * over the tokens (which list the block; which of those need their slots re-read); past
+ * that limit attn_bwd_workspace_bytes leaves them out and the kernels scan every
+ * token's selections instead, with the same result.
  */
 int attn_bwd(const attn_params* params, const void* q, const void* k, const void* v,
              const void* o, const void* dout, const float* m, const float* l,

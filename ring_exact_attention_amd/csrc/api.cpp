@@ -300,9 +300,23 @@ int sparse_fwd(const attn_params* p, const void* q, const void* k, const void* v
   return hip_status(rea::launch_sparse(a, (hipStream_t)stream));
 }
 
+// The two block masks of the sparse dk/dv kernel (which tokens list each block, and which
+// of those with a code other than 1) take 2 * B * (S / 32) * ceil(S / 32) words; past
+// kSparseMaskMax bytes, or past rea::kMaskMaxSel blocks (the LDS of the kernel that
+// builds them), they are left out and that kernel scans every token's selections.
+constexpr size_t kSparseMaskMax = (size_t)64 << 20;
+size_t sparse_mask_bytes(const attn_params* p) {
+  if (p->batch <= 0 || p->seqlen_q <= 0 || p->sel_block <= 0) return 0;
+  const size_t S = (size_t)p->seqlen_q, nsel = S / (size_t)p->sel_block;
+  if (nsel > (size_t)rea::kMaskMaxSel) return 0;
+  const size_t bytes = 2 * (size_t)p->batch * nsel * ((S + 31) / 32) * sizeof(uint32_t);
+  return bytes <= kSparseMaskMax ? bytes : 0;
+}
+
 size_t sparse_bwd_workspace(const attn_params* p) {
   const size_t n = (size_t)(p->batch > 0 ? p->batch : 0) * (p->seqlen_q > 0 ? p->seqlen_q : 0) * sizeof(float);
-  return 2 * align_up(n > 0 ? n : 1);
+  const size_t mask = sparse_mask_bytes(p);
+  return 2 * align_up(n > 0 ? n : 1) + (mask > 0 ? align_up(mask) : 0);
 }
 
 // Gradient of the gathered block-sparse attention (sel_idx != NULL).
@@ -343,6 +357,9 @@ int sparse_bwd(const attn_params* p, const void* q, const void* k, const void* v
   const size_t n = (size_t)p->batch * p->seqlen_q * sizeof(float);
   a.Dvec = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + align_up(n));
+  a.lmask = sparse_mask_bytes(p) > 0 ? (uint32_t*)((char*)workspace + 2 * align_up(n)) : nullptr;
+  a.nsel = p->seqlen_q / p->sel_block;
+  a.nwords = (p->seqlen_q + 31) / 32;
   a.B = p->batch;
   a.S = p->seqlen_q;
   a.E = p->head_dim;

@@ -139,6 +139,10 @@ struct SparseArgs {
   float* part;        // ksplit > 1: [B, S, ksplit, 512 + 4] partial numerator, max, sum, pad
 };
 
+// Most selectable blocks (S / sel_block) for which the sparse backward builds its block
+// masks (the building kernel holds 2 x 8 x that many words of LDS).
+constexpr int kMaskMaxSel = 1024;
+
 // Backward of the gathered block-sparse attention.
 struct SparseBwdArgs {
   int rev_order;      // nonzero: workgroups take the grid's tasks in reverse order (see wg_index)
@@ -155,6 +159,12 @@ struct SparseBwdArgs {
   void* dv;
   float* Dvec;        // [B, S] workspace: rowsum(dO * o)
   float* lse2;        // [B, S] workspace: m*log2(e) + log2(l)
+  // 2 x [B, nsel, nwords] workspace (or null): in the first plane, bit t % 32 of word
+  // (b, c, t / 32) is set when token t lists block c (a -1 entry counts for block 0); in
+  // the second, when its code for c (count | count of -1 entries << 8) is not 1.
+  // nsel = S / sel_block, nwords = ceil(S / 32)
+  uint32_t* lmask;
+  int nsel, nwords;
   int B, S, E, top_n, sel_block, window;
   float scale_log2, scale;
 };

@@ -585,12 +585,54 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
       for (int j4 = 0; j4 < 2; ++j4)
         if (selpf_ok && 4 * j4 < n) selpf[k][j4] = *(const u32x4*)(rowp + k * n + 4 * j4);
   };
-  if (pf_sel) sel_fetch(0);
-  for (int base0 = 0; base0 < a.S; base0 += 256 * kSpScan) {
+  // With the block masks a thread reads two words for its four tokens (listed; listed
+  // with a code other than 1) and the selections of only the tokens in the second; the
+  // next pass's words are loaded before the current pass's tiles run.
+  const size_t mplane = (size_t)a.B * a.nsel * a.nwords;
+  const uint32_t* mrow = a.lmask && scan_blk ? a.lmask + ((size_t)b * a.nsel + c) * a.nwords : nullptr;
+  // pw: word (base0 / 32 + lane % 32) of the pass, so that every wave sees all of the
+  // pass's 32 words and all four skip a pass that lists no token, together
+  uint32_t mw1 = 0u, mw2 = 0u, pw = 0u;
+  auto mask_fetch = [&](int base0) {
+    const int tb = base0 + kSpScan * tid;
+    const int pwi = (base0 >> 5) + (lane & 31);
+    mw1 = mw2 = pw = 0u;
+    if (tb < a.S) {
+      mw1 = mrow[tb >> 5];
+      mw2 = mrow[mplane + (tb >> 5)];
+    }
+    if (pwi < a.nwords) pw = mrow[pwi];
+  };
+  if (mrow) mask_fetch(0);
+  if (pf_sel && !mrow) sel_fetch(0);
+  // (a tile past the last whole block is listed by no token: no pass)
+  for (int base0 = 0; base0 < (scan_blk ? a.S : 0); base0 += 256 * kSpScan) {
     int code[kSpScan];                                 // count | (count of -1 entries) << 8
     const int tb = base0 + kSpScan * tid;              // this thread's first token
     const int32_t* rowp = a.sel + ((size_t)b * a.S + (tb < a.S ? tb : 0)) * n;
-    if (pf_sel && selpf_ok) {
+    if (mrow && __ballot(pw != 0u) == 0) {
+      mask_fetch(base0 + 256 * kSpScan);               // no token of this pass lists the block
+      continue;
+    }
+    if (mrow) {
+      // tb is a multiple of 4, so the four tokens' bits sit in one word of each mask
+      const uint32_t bits = (mw1 >> (tb & 31)) & 0xfu, odd = (mw2 >> (tb & 31)) & 0xfu;
+#pragma unroll
+      for (int k = 0; k < kSpScan; ++k) {
+        code[k] = (bits >> k) & 1u;
+        if ((odd >> k) & 1u) {
+          const int32_t* row = rowp + k * n;
+          int cnt = 0, neg = 0;
+          for (int j = 0; j < n; ++j) {
+            const int e = row[j];
+            cnt += e == c;
+            neg += e < 0;
+          }
+          code[k] = cnt | ((c != 0 ? 0 : neg) << 8);
+        }
+      }
+      mask_fetch(base0 + 256 * kSpScan);
+    } else if (pf_sel && selpf_ok) {
 #pragma unroll
       for (int k = 0; k < kSpScan; ++k) {
         int cnt = 0, neg = 0;
@@ -640,7 +682,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
         code[k] = cnt | ((c != 0 ? 0 : neg) << 8);
       }
     }
-    if (pf_sel) sel_fetch(base0 + 256 * kSpScan);
+    if (pf_sel && !mrow) sel_fetch(base0 + 256 * kSpScan);
     // position: entries of the lanes below, then of this lane's earlier tokens
     const uint64_t below = (1ull << lane) - 1;
     int pre = 0, tot = 0;
@@ -732,8 +774,73 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkdv_kernel(SparseBwdArgs a
   }
 }
 
+// Builds the two block masks, one workgroup per 256 tokens (eight 32-token words per
+// block): each thread marks, for its token, every distinct block c < nsel it lists (a -1
+// entry counting for block 0) in the first mask, and in the second too when its code for
+// c is not 1 (listed twice or more, or block 0 with -1 entries); the workgroup's words,
+// zeros included, are then written out, so no word needs clearing beforehand and none is
+// written twice.  LDS: 2 x 8 x nsel words (dynamic).
+__global__ __launch_bounds__(256) void sparse_mask_kernel(SparseBwdArgs a) {
+  extern __shared__ uint32_t smask[];                // [2][8][nsel]
+  const int tid = threadIdx.x;
+  const int nchunk = (a.S + 255) / 256;
+  const int b = blockIdx.x / nchunk, t0 = (blockIdx.x - b * nchunk) * 256;
+  const int ns = a.nsel, n = a.top_n;
+  for (int i = tid; i < 2 * 8 * ns; i += 256) smask[i] = 0u;
+  __syncthreads();
+  const int t = t0 + tid;
+  if (t < a.S) {
+    const int32_t* row = a.sel + ((size_t)b * a.S + t) * n;
+    int e[16];
+    int neg = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      e[j] = j < n ? row[j] : -2;
+      neg += (j < n && e[j] < 0) ? 1 : 0;
+    }
+    const uint32_t bit = 1u << (tid & 31);
+    uint32_t* w1 = smask + (tid >> 5) * ns;
+    uint32_t* w2 = smask + 8 * ns + (tid >> 5) * ns;
+    bool zero_listed = false;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= n || e[j] < 0 || e[j] >= ns) continue;
+      bool first = true;
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < n && e[i] == e[j]) {
+          first = first && i >= j;
+          ++cnt;
+        }
+      if (!first) continue;
+      if (e[j] == 0) zero_listed = true;
+      atomicOr(&w1[e[j]], bit);
+      if ((cnt | (e[j] == 0 ? neg << 8 : 0)) != 1) atomicOr(&w2[e[j]], bit);
+    }
+    if (neg > 0 && !zero_listed && ns > 0) {
+      atomicOr(&w1[0], bit);
+      atomicOr(&w2[0], bit);
+    }
+  }
+  __syncthreads();
+  // word (plane, g, c) of the workgroup goes to plane * (B nsel nwords) + (b nsel + c) nwords
+  // + t0 / 32 + g; consecutive threads take consecutive g
+  const size_t plane = (size_t)a.B * ns * a.nwords;
+  const int g0 = t0 >> 5;
+  for (int i = tid; i < 2 * 8 * ns; i += 256) {
+    const int g = i & 7, rest = i >> 3, c = rest % ns, pl = rest / ns;
+    if (g0 + g < a.nwords) a.lmask[pl * plane + ((size_t)b * ns + c) * a.nwords + g0 + g] = smask[(pl * 8 + g) * ns + c];
+  }
+}
+
 hipError_t launch_sparse_bwd(const SparseBwdArgs& a, hipStream_t stream) {
   const unsigned nqb = (unsigned)((a.S + kUQ - 1) / kUQ);
+  if (a.lmask && a.nsel > 0) {
+    const unsigned nchunk = (unsigned)((a.S + 255) / 256);
+    hipLaunchKernelGGL(sparse_mask_kernel, dim3((unsigned)a.B * nchunk), dim3(256),
+                       (size_t)2 * 8 * a.nsel * sizeof(uint32_t), stream, a);
+  }
   hipLaunchKernelGGL(sparse_bwd_dq_kernel, dim3((unsigned)a.B * nqb), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(sparse_bwd_dkdv_kernel, dim3((unsigned)a.B * nqb), dim3(256), 0, stream, a);
   return hipGetLastError();
