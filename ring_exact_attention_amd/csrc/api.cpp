@@ -586,10 +586,13 @@ size_t block_select_workspace_bytes(const select_params* p_in) {
     return 0;
   const size_t nblk = (size_t)(select_kv_rows(p) / p->block_size);
   const size_t n = (size_t)p->batch * nblk * p->embed * sizeof(double);
-  // block means, then (split selection) the partial top-n lists
+  // block means, their bf16 parts and norms, then (split selection) the partial top-n lists
+  const size_t nb = (size_t)p->batch * nblk;
   const int ns = rea::select_splits(p->batch, p->seqlen, p->q_pos0, p->block_size, (int)nblk, p->top_n);
   const size_t parts = ns > 1 ? (size_t)p->batch * p->seqlen * ns * p->top_n : 0;
-  return align_up(n > 0 ? n : 1) + (parts ? align_up(parts * sizeof(double)) + align_up(parts * sizeof(int32_t)) : 0);
+  const size_t ns3 = 2 * nb * p->embed * sizeof(uint16_t), nn = nb * sizeof(float);
+  return align_up(n > 0 ? n : 1) + align_up(ns3 > 0 ? ns3 : 1) + align_up(nn > 0 ? nn : 1) +
+         (parts ? align_up(parts * sizeof(double)) + align_up(parts * sizeof(int32_t)) : 0);
 }
 
 int block_select(const select_params* p_in, const void* q, const void* k, int32_t* idx, void* workspace,
@@ -638,11 +641,19 @@ int block_select(const select_params* p_in, const void* q, const void* k, int32_
   a.top_n = p->top_n;
   a.nblk = skv / p->block_size;
   a.nsplit = rea::select_splits(a.B, a.S, a.q_pos0, a.bs, a.nblk, a.top_n);
-  if (a.nsplit > 1) {
-    const size_t nm = (size_t)a.B * a.nblk * a.E * sizeof(double);
-    const size_t parts = (size_t)a.B * a.S * a.nsplit * a.top_n;
-    a.part_s = (double*)((char*)workspace + align_up(nm > 0 ? nm : 1));
-    a.part_c = (int32_t*)((char*)a.part_s + align_up(parts * sizeof(double)));
+  {
+    const size_t nm = (size_t)a.B * a.nblk * a.E * sizeof(double), nb = (size_t)a.B * a.nblk;
+    char* w = (char*)workspace + align_up(nm > 0 ? nm : 1);
+    const size_t ns3 = 2 * nb * a.E * sizeof(uint16_t), nn = nb * sizeof(float);
+    a.msplit = (uint16_t*)w;
+    w += align_up(ns3 > 0 ? ns3 : 1);
+    a.mnorm = (float*)w;
+    w += align_up(nn > 0 ? nn : 1);
+    if (a.nsplit > 1) {
+      const size_t parts = (size_t)a.B * a.S * a.nsplit * a.top_n;
+      a.part_s = (double*)w;
+      a.part_c = (int32_t*)((char*)a.part_s + align_up(parts * sizeof(double)));
+    }
   }
   return hip_status(rea::launch_select(a, (hipStream_t)stream));
 }

@@ -119,6 +119,8 @@ struct SelectArgs {
   int nsplit;         // workgroups per query block, each over a share of the candidates
   double* part_s;     // nsplit > 1: [B, S, nsplit, top_n] partial lists (score, index;
   int32_t* part_c;    //   index -1 = empty), combined by block_select_merge_kernel
+  uint16_t* msplit;   // [2, B, nblk, E] the means as sums of two bf16 parts (hi, lo)
+  float* mnorm;       // [B, nblk] Euclidean norm of each mean, rounded up
 };
 
 struct SparseArgs {

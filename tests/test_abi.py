@@ -174,18 +174,20 @@ def test_select_decode_checks(lib):
     assert call(sp()) == rea.ATTN_ERR_INVALID_ARG and b"idx is NULL" in lib.attn_last_error()
     assert call(sp(q_pos0=253)) == rea.ATTN_ERR_INVALID_ARG and b"q_pos0" in lib.attn_last_error()
     assert call(sp(q_pos0=-1)) == rea.ATTN_ERR_INVALID_ARG
-    # workspace: the means of the key sequence's full blocks
-    assert lib.block_select_workspace_bytes(ctypes.byref(sp())) == 8 * 512 * 8
+    # workspace: the means of the key sequence's full blocks (fp64), their two bf16
+    # parts and their norms (fp32), each part 256-byte aligned
+    means = lambda nb, e: nb * e * 8 + 2 * nb * e * 2 + (nb * 4 + 255) // 256 * 256
+    assert lib.block_select_workspace_bytes(ctypes.byref(sp())) == means(8, 512)
     v1 = sp(seqlen=256, seqlen_kv=77, q_pos0=99)
     v1.struct_size = 32                                      # fields past 32 bytes ignored
-    assert lib.block_select_workspace_bytes(ctypes.byref(v1)) == 8 * 512 * 8
+    assert lib.block_select_workspace_bytes(ctypes.byref(v1)) == means(8, 512)
     assert call(v1) == rea.ATTN_ERR_INVALID_ARG and b"idx is NULL" in lib.attn_last_error()
     # few query blocks (decoding): the candidates of a block are shared out over
     # workgroups (here 4: 256 blocks = 4 chunks of 64), whose partial top-n lists
     # (fp64 score + int32 index per entry) follow the means
     dec = sp(seqlen=4, seqlen_kv=8192, q_pos0=8188)
     parts = 1 * 4 * 4 * 8
-    assert lib.block_select_workspace_bytes(ctypes.byref(dec)) == 256 * 512 * 8 + parts * 8 + parts * 4
+    assert lib.block_select_workspace_bytes(ctypes.byref(dec)) == means(256, 512) + parts * 8 + parts * 4
 
 
 def test_sparse_forward_workspace(lib):
@@ -288,7 +290,7 @@ def test_select_checks(lib):
     p.struct_size = ctypes.sizeof(rea.SelectParams)
     p.dtype, p.batch, p.seqlen, p.embed, p.block_size, p.top_n = rea.ATTN_BF16, 2, 256, 512, 32, 8
     need = lib.block_select_workspace_bytes(ctypes.byref(p))
-    assert need == 2 * 8 * 512 * 8
+    assert need == 16 * 512 * 8 + 2 * 16 * 512 * 2 + 256   # means, their bf16 parts, norms
     d = ctypes.c_void_p(0x1000)
     assert lib.block_select(ctypes.byref(p), d, d, d, d, need - 8, None) == rea.ATTN_ERR_WORKSPACE
     p.block_size = 24

@@ -73,13 +73,15 @@ def test_select_scores_equal_in_fp32(gpu, n):
     assert list(last) == ([7] if n == 1 else [3, 7])
 
 
-@pytest.mark.parametrize("n", [3, 8, 16])
-def test_select_split_candidates_ties(gpu, n):
-    """Few query blocks against a long cache: each block's candidates are shared out over
-    several workgroups and their lists merged.  Integer-valued inputs with repeated key
-    blocks put exact ties across the shares; the indices must equal the oracle's and the
-    single-workgroup path's (the full-sequence call)."""
-    B, S, E, bs, T, pos0 = 2, 8192, 64, 32, 100, 8000
+@pytest.mark.parametrize("n,bs", [(3, 32), (8, 32), (16, 32), (3, 16), (16, 16)])
+def test_select_split_candidates_ties(gpu, n, bs):
+    """Few query blocks against a long cache.  With 32-row blocks (256 candidates) each
+    query block's scores fit one workgroup (approximate scores, exact ones near the cut);
+    with 16-row blocks (512) the candidates are shared out over several workgroups (fp64
+    scores, running lists) and their lists merged.  Integer-valued inputs with repeated
+    key blocks put exact ties across the shares; the indices must equal the oracle's and
+    the full-sequence call's."""
+    B, S, E, T, pos0 = 2, 8192, 64, 100, 8000
     g = torch.Generator().manual_seed(40 + n)
     k = torch.randint(-2, 3, (B, S, E), generator=g).to(torch.bfloat16)
     for b in range(B):
@@ -93,6 +95,34 @@ def test_select_split_candidates_ties(gpu, n):
     ref = select.block_select(qn, k, block_size=bs, top_n=n, q_pos0=pos0)
     np.testing.assert_array_equal(idx.cpu().numpy(), ref)
     np.testing.assert_array_equal(idx.cpu().numpy(), idx_full.cpu().numpy()[:, pos0:pos0 + T])
+
+
+@pytest.mark.parametrize("scale", [0.0, 2.0 ** 70])
+def test_select_degenerate_scores(gpu, scale):
+    """All scores zero (every candidate tied: the lowest indices win), and scores past the
+    fp32 range (inputs of 2^70: the approximate scores overflow, so every candidate is
+    scored exactly in fp64)."""
+    B, S, E, bs, n = 2, 640, 128, 32, 5
+    q, k = rnd((B, S, E), 71), rnd((B, S, E), 72)
+    q = (q.float() * scale).to(torch.bfloat16)
+    k = (k.float() * (scale if scale > 0 else 1.0)).to(torch.bfloat16)
+    idx = gpu.block_select(q.to(DEV), k.to(DEV), block_size=bs, top_n=n)
+    torch.cuda.synchronize()
+    ref = select.block_select(q, k, block_size=bs, top_n=n)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+    if scale == 0.0:
+        assert (ref[:, -1] == np.arange(n)).all()
+
+
+def test_select_many_blocks(gpu):
+    """More than 256 candidate blocks with one workgroup per query block (260 blocks of 16
+    rows): the fp64 running-list path without a candidate split."""
+    B, S, E, bs, n = 1, 4160, 64, 16, 8
+    q, k = rnd((B, S, E), 81), rnd((B, S, E), 82)
+    idx = gpu.block_select(q.to(DEV), k.to(DEV), block_size=bs, top_n=n)
+    torch.cuda.synchronize()
+    ref = select.block_select(q, k, block_size=bs, top_n=n)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
 
 
 def test_select_full_size(gpu):
