@@ -321,11 +321,11 @@ int attn_bwd_noalloc(const attn_params* params, const void* q, const void* k, co
  *   workspace  device scratch of at least block_select_workspace_bytes(params) bytes
  *              (256-byte aligned; contents overwritten): the fp64 block means, each
  *              mean as two bf16 parts and its norm and, when only a few query blocks
- *              are selected for and there are more than 256 key blocks, the partial
- *              top-n lists of the workgroups that share a block's candidates.
- * With up to 256 key blocks the scores are first taken in bf16 (the two parts) and only
- * the candidates that an error bound leaves undecided are scored in fp64; the indices
- * are those of the exact fp64 scores either way.
+ *              are selected for (decoding), the partial top-n lists of the workgroups
+ *              that share a block's candidates.
+ * With up to 256 key blocks and 256 or more query blocks the scores are first taken in
+ * bf16 (the two parts) and only the candidates that an error bound leaves undecided are
+ * scored in fp64; the indices are those of the exact fp64 scores either way.
  */
 int block_select(const select_params* params, const void* q, const void* k, int32_t* idx,
                  void* workspace, size_t workspace_bytes, void* stream);

@@ -5,9 +5,10 @@
 // with its two bf16 parts and its norm.
 // Selection: one workgroup per (batch, block i of query positions; query row r sits at
 // position q_pos0 + r of the key sequence, so decoding a few new tokens against a key
-// cache is the same call).  Up to 256 key blocks, block_select_bf16_kernel scores all
-// candidates c < i in bf16 with an error bound and scores in fp64 only those the bound
-// leaves undecided.  Past that, block_select_kernel scores the candidates in chunks of
+// cache is the same call).  Up to 256 key blocks (and 256 or more query blocks),
+// block_select_bf16_kernel scores all candidates c < i in bf16 with an error bound and
+// scores in fp64 only those the bound leaves undecided.  Otherwise block_select_kernel
+// scores the candidates in chunks of
 // 64 (16 per wavefront) with fp64 MFMA (bf16 queries are exact in fp64), the chunk's
 // scores go to LDS, and each token's running top-n list (in LDS, score descending; on
 // equal scores the lower index ahead) absorbs the chunk in one parallel step: a
@@ -708,8 +709,11 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(block_means_kernel, dim3((unsigned)(a.B * a.nblk)), dim3(256), 0, stream, a);
   if (a.S == 0) return hipGetLastError();
   const int nqb = (a.q_pos0 + a.S - 1) / a.bs - a.q_pos0 / a.bs + 1;
-  if (a.nblk <= kSelFastMax) {
-    // all candidates of a query block fit the LDS score table: one workgroup per block
+  if (a.nblk <= kSelFastMax && a.nsplit == 1) {
+    // all candidates of a query block fit the LDS score table: one workgroup per block.
+    // (A grid of fewer than 256 query blocks -- decoding -- takes the split fp64 path
+    // instead: a few workgroups scoring all candidates each wait on their loads longer
+    // than the split's workgroups take to score their shares.)
     const dim3 grid((unsigned)(a.B * nqb));
     const size_t lds = sel_fast_lds(a.bs, a.E);
     switch (a.bs) {
