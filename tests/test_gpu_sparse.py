@@ -114,6 +114,27 @@ def test_select_degenerate_scores(gpu, scale):
         assert (ref[:, -1] == np.arange(n)).all()
 
 
+@pytest.mark.parametrize("n,step", [(1, 2.0 ** -8), (4, 2.0 ** -8), (8, 2.0 ** -8), (4, 2.0 ** -5), (8, 2.0 ** -5)])
+def test_select_near_ties(gpu, n, step):
+    """Every key block is one base block plus a small offset in one dimension of one row,
+    so the block means differ by multiples of step / 32 and the scores by about 10^-4
+    (step 2^-8: inside the bf16 scores' error bound, every candidate is undecided and the
+    exact fp64 scores rank them all) or 10^-3 (2^-5: some candidates decided, some not)."""
+    B, S, E, bs = 2, 2048, 256, 32
+    g = torch.Generator().manual_seed(90 + n)
+    base = torch.randn((bs, E), generator=g)
+    k = base.repeat(B, S // bs, 1).reshape(B, S, E).clone()
+    for b in range(B):
+        for c in range(S // bs):
+            k[b, c * bs, (c * 7 + b) % E] += ((c * 5 + b) % 9 - 4) * step
+    k = k.to(torch.bfloat16)
+    q = rnd((B, S, E), 95 + n)
+    idx = gpu.block_select(q.to(DEV), k.to(DEV), block_size=bs, top_n=n)
+    torch.cuda.synchronize()
+    ref = select.block_select(q, k, block_size=bs, top_n=n)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+
+
 def test_select_many_blocks(gpu):
     """More than 256 candidate blocks with one workgroup per query block (260 blocks of 16
     rows): the fp64 running-list path without a candidate split."""
