@@ -462,34 +462,41 @@ __global__ __launch_bounds__(256, 4) void block_select_bf16_kernel(SelectArgs a)
   const int ntile = (ncand + 31) / 32, nks = a.E / 16;
   f32x16 acc[NT][TT];
 #pragma unroll
-  for (int it = 0; it < NT; ++it) {
-    const int ct = wave + 4 * it;
+  for (int it = 0; it < NT; ++it)
 #pragma unroll
     for (int x = 0; x < TT; ++x)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[it][x][r] = 0.f;
-    if (ct >= ntile) continue;
-    const int cand = min(32 * ct + li, ncand - 1);
-    const uint16_t* mrow = sp0 + (size_t)cand * a.E + 8 * lh;
-    // the two parts of k-steps ks .. ks + PF - 1 are in flight ahead of their MFMAs
-    constexpr int PF = 8;
-    u32x4 mb[PF][2];
+  // The wavefront's NA active tiles (candidates 32 ct .. of ct = wave, wave + 4) share one
+  // k-step loop, so their loads are in flight together; the two parts of k-steps
+  // ks .. ks + PF - 1 are loaded ahead of their MFMAs (PF = 8 / NA).
+  auto score = [&](auto na_c) __attribute__((always_inline)) {
+    constexpr int NA = decltype(na_c)::value, PF = 8 / NA;
+    const uint16_t* mrow[NA];
+#pragma unroll
+    for (int it = 0; it < NA; ++it)
+      mrow[it] = sp0 + (size_t)min(32 * (wave + 4 * it) + li, ncand - 1) * a.E + 8 * lh;
+    u32x4 mb[PF][NA][2];
 #pragma unroll
     for (int u = 0; u < PF; ++u)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) mb[u][k] = *(const u32x4*)(mrow + k * plane + 16 * (u < nks ? u : 0));
+      for (int it = 0; it < NA; ++it)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) mb[u][it][k] = *(const u32x4*)(mrow[it] + k * plane + 16 * (u < nks ? u : 0));
     // nks is a multiple of 4, not always of PF: k-steps past the end are skipped
     for (int ks0 = 0; ks0 < nks; ks0 += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         const int ks = ks0 + u, kn = ks + PF < nks ? ks + PF : 0;
         if (ks >= nks) break;
-        u32x4 m3[2];
+        u32x4 m3[NA][2];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          m3[k] = mb[u][k];
-          mb[u][k] = *(const u32x4*)(mrow + k * plane + 16 * kn);
-        }
+        for (int it = 0; it < NA; ++it)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            m3[it][k] = mb[u][it][k];
+            mb[u][it][k] = *(const u32x4*)(mrow[it] + k * plane + 16 * kn);
+          }
 #pragma unroll
         for (int x = 0; x < TT; ++x) {
           const int row = 32 * x + li;
@@ -497,11 +504,16 @@ __global__ __launch_bounds__(256, 4) void block_select_bf16_kernel(SelectArgs a)
           if (BS >= 32 || row < BS) qu = *(const u32x4*)&sq[row * pitch + 16 * ks + 8 * lh];
           const bf16x8 qa = as_bf16x8(qu);
 #pragma unroll
-          for (int k = 0; k < 2; ++k) acc[it][x] = mfma32(qa, as_bf16x8(m3[k]), acc[it][x]);
+          for (int it = 0; it < NA; ++it)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) acc[it][x] = mfma32(qa, as_bf16x8(m3[it][k]), acc[it][x]);
         }
       }
     }
-  }
+  };
+  static_assert(NT == 2, "a wavefront scores at most two 32-candidate tiles");
+  if (wave + 4 < ntile) score(IntConst<2>{});
+  else if (wave < ntile) score(IntConst<1>{});
   __syncthreads();                                 // the queries' LDS becomes the scores'
   // lane (candidate li) holds tokens 8g + 4lh + e of each 32-token tile
 #pragma unroll
