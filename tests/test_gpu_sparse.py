@@ -22,7 +22,7 @@ def rnd(shape, seed):
 
 @pytest.mark.parametrize("B,S,E,bs,n", [(2, 256, 64, 16, 3), (1, 300, 512, 32, 8), (2, 200, 128, 64, 2),
                                          (1, 1000, 512, 32, 16), (3, 64, 64, 32, 1), (1, 700, 512, 64, 5),
-                                         (1, 520, 1024, 16, 16)])
+                                         (1, 520, 1024, 16, 16), (1, 600, 1024, 32, 8)])
 def test_select_small(gpu, B, S, E, bs, n):
     q, k = rnd((B, S, E), S + E), rnd((B, S, E), S + E + 1)
     idx = gpu.block_select(q.to(DEV), k.to(DEV), block_size=bs, top_n=n)
@@ -114,13 +114,14 @@ def test_select_degenerate_scores(gpu, scale):
         assert (ref[:, -1] == np.arange(n)).all()
 
 
-@pytest.mark.parametrize("n,step", [(1, 2.0 ** -8), (4, 2.0 ** -8), (8, 2.0 ** -8), (4, 2.0 ** -5), (8, 2.0 ** -5)])
-def test_select_near_ties(gpu, n, step):
+@pytest.mark.parametrize("n,step,E", [(1, 2.0 ** -8, 256), (4, 2.0 ** -8, 256), (8, 2.0 ** -8, 256),
+                                      (4, 2.0 ** -5, 256), (8, 2.0 ** -5, 256), (8, 2.0 ** -8, 1024)])
+def test_select_near_ties(gpu, n, step, E):
     """Every key block is one base block plus a small offset in one dimension of one row,
     so the block means differ by multiples of step / 32 and the scores by about 10^-4
     (step 2^-8: inside the bf16 scores' error bound, every candidate is undecided and the
     exact fp64 scores rank them all) or 10^-3 (2^-5: some candidates decided, some not)."""
-    B, S, E, bs = 2, 2048, 256, 32
+    B, S, bs = 2, 2048, 32
     g = torch.Generator().manual_seed(90 + n)
     base = torch.randn((bs, E), generator=g)
     k = base.repeat(B, S // bs, 1).reshape(B, S, E).clone()
