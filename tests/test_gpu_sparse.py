@@ -136,6 +136,20 @@ def test_select_near_ties(gpu, n, step, E):
     np.testing.assert_array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("bs,pos0", [(32, 69), (16, 3)])
+def test_select_offset_queries_full_grid(gpu, bs, pos0):
+    """Query rows starting at an unaligned position of the key sequence (a partial first
+    query block) with enough query blocks for one workgroup each: the bf16-bound path
+    with q_pos0 > 0."""
+    B, S, E, n = 1, 8192 if bs == 32 else 4096, 256, 8
+    q, k = rnd((B, S, E), 120 + bs), rnd((B, S, E), 121 + bs)
+    qn = q[:, pos0:].contiguous()
+    idx = gpu.block_select(qn.to(DEV), k.to(DEV), block_size=bs, top_n=n, q_pos0=pos0)
+    torch.cuda.synchronize()
+    ref = select.block_select(qn, k, block_size=bs, top_n=n, q_pos0=pos0)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+
+
 def test_select_many_blocks(gpu):
     """More than 256 candidate blocks with one workgroup per query block (260 blocks of 16
     rows): the fp64 running-list path without a candidate split."""
