@@ -286,12 +286,27 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
                  ("decode_attn", lambda: rea.attn_fwd_sparse(qn, kd, vd, idn, window=w.sparse_window,
                                                              block_size=w.block_size, out=on, q_pos0=S - T,
                                                              workspace=wsd))]
+        # the same selection with the cache's block means kept in the workspace from a first
+        # call (the blocks before the new tokens' block; the rest are recomputed each step)
+        wss = torch.empty(max(rea.select_workspace_bytes(B, T, E, block_size=w.block_size, top_n=w.top_n,
+                                                         seqlen_kv=S, q_pos0=S - T), 256),
+                          dtype=torch.uint8, device=dev)
+        rea.block_select(qn, kd, block_size=w.block_size, top_n=w.top_n, out=idn, q_pos0=S - T, workspace=wss)
+        cached = (S - T) // w.block_size
+        dsegs.append(("decode_select_cached", lambda: rea.block_select(
+            qn, kd, block_size=w.block_size, top_n=w.top_n, out=idn, q_pos0=S - T, workspace=wss,
+            means_cached=cached)))
         dms, _, _ = time_segments(torch, dsegs, args.steps, args.warmup, torch.cuda.current_stream(dev))
         step_us = (dms["decode_select"] + dms["decode_attn"]) * 1e3
+        step_c = (dms["decode_select_cached"] + dms["decode_attn"]) * 1e3
         kernels["decode_step"] = {"new_tokens_per_sequence": T, "cache_rows": S,
                                   "select_us": round(dms["decode_select"] * 1e3, 2),
                                   "attn_us": round(dms["decode_attn"] * 1e3, 2), "step_us": round(step_us, 2),
-                                  "tokens_per_s": round(B * T / (step_us * 1e-6), 1)}
+                                  "tokens_per_s": round(B * T / (step_us * 1e-6), 1),
+                                  "means_cached_blocks": cached,
+                                  "select_cached_us": round(dms["decode_select_cached"] * 1e3, 2),
+                                  "step_cached_us": round(step_c, 2),
+                                  "tokens_per_s_cached": round(B * T / (step_c * 1e-6), 1)}
     if args.sparse_backward:
         tb = seg_ms["attn_bwd_sparse"] * 1e-3
         kernels["attn_bwd_sparse"] = {"avg_us": round(tb * 1e6, 2), "gathered_gb": round(2 * gathered / 1e9, 3),

@@ -102,9 +102,10 @@ enum {
 };
 
 /* 2: softmax_type, sink, dsink appended; 3: bias, bias_stride appended; 4: drop_mask,
- * drop_stride appended.  Structs of the earlier sizes are still accepted: the missing
- * fields read as zero (ATTN_SOFTMAX_VANILLA, no bias, no dropout). */
-#define ATTN_PARAMS_VERSION 4u
+ * drop_stride appended; 5: select_params.reserved became means_cached (0, the value it
+ * had to hold, keeps the earlier behaviour).  Structs of the earlier sizes are still
+ * accepted: the missing fields read as zero (ATTN_SOFTMAX_VANILLA, no bias, no dropout). */
+#define ATTN_PARAMS_VERSION 5u
 #define ATTN_PARAMS_V1_SIZE 104u
 #define ATTN_PARAMS_V2_SIZE 128u
 #define ATTN_PARAMS_V3_SIZE 168u
@@ -206,7 +207,13 @@ typedef struct select_params {
   int32_t embed;               /* E = heads * head_dim, multiple of 64, <= 1024        */
   int32_t block_size;          /* 16, 32 or 64                                         */
   int32_t top_n;               /* 1..16                                                */
-  int32_t reserved;            /* must be 0                                            */
+  /* Leading full key blocks whose means the workspace already holds from an earlier call
+   * on the same key rows (same k pointer contents for those rows, batch, embed,
+   * block_size and seqlen_kv), as the page's index keeps the means of completed blocks
+   * across decoding steps: 0 <= means_cached <= seqlen_kv / block_size; those blocks'
+   * means are not recomputed.  0 = compute every mean the call needs.  The caller owns
+   * the promise: means of rows that changed since are used as they are.              */
+  int32_t means_cached;
   /* Decoding ("AnnAttention" in inference mode: new tokens against the key cache).
    * Query row r sits at position q_pos0 + r of a key sequence of seqlen_kv rows;
    * 0 = seqlen (the whole sequence, q_pos0 = 0).  q_pos0 + seqlen <= seqlen_kv.      */

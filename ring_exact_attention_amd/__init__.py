@@ -79,7 +79,7 @@ class SelectParams(ctypes.Structure):
         ("embed", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("top_n", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("means_cached", ctypes.c_int32),
         ("seqlen_kv", ctypes.c_int32),
         ("q_pos0", ctypes.c_int32),
     ]
@@ -364,23 +364,38 @@ def _joint(x):
     return x.reshape(x.shape[0], x.shape[1], -1) if x.dim() == 4 else x
 
 
-def block_select(q, k, *, block_size=32, top_n=8, workspace=None, out=None, q_pos0=0):
+def _select_params(B, S, E, block_size, top_n, seqlen_kv, q_pos0, means_cached=0):
+    p = SelectParams()
+    p.struct_size = ctypes.sizeof(SelectParams)
+    p.dtype = ATTN_BF16
+    p.batch, p.seqlen, p.embed = B, S, E
+    p.seqlen_kv, p.q_pos0 = seqlen_kv, int(q_pos0)
+    p.block_size, p.top_n = int(block_size), int(top_n)
+    p.means_cached = int(means_cached)
+    return p
+
+
+def select_workspace_bytes(B, S, E, *, block_size=32, top_n=8, seqlen_kv=None, q_pos0=0) -> int:
+    """Bytes of device workspace block_select needs for these sizes (keep one of this size
+    to carry the block means across decoding calls)."""
+    p = _select_params(B, S, E, block_size, top_n, S if seqlen_kv is None else seqlen_kv, q_pos0)
+    return int(lib().block_select_workspace_bytes(ctypes.byref(p)))
+
+
+def block_select(q, k, *, block_size=32, top_n=8, workspace=None, out=None, q_pos0=0, means_cached=0):
     """Exact top-n earlier-block selection by block-mean inner product -> int32 [B, Sq, top_n].
 
     Query row r sits at position q_pos0 + r of the key sequence k [B, Skv, E] (decoding:
-    new tokens against the key cache)."""
+    new tokens against the key cache).  ``means_cached``: the first that many blocks'
+    means are already in ``workspace`` from an earlier call on the same key rows (the
+    same workspace tensor, batch, embedding, block size and cache length)."""
     q, k = _joint(q), _joint(k)
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16, q.device)
     B, S, E = q.shape
     if k.shape[0] != B or k.shape[2] != E:
         raise ValueError("q and k must agree on batch and embedding")
-    p = SelectParams()
-    p.struct_size = ctypes.sizeof(SelectParams)
-    p.dtype = ATTN_BF16
-    p.batch, p.seqlen, p.embed = B, S, E
-    p.seqlen_kv, p.q_pos0 = k.shape[1], int(q_pos0)
-    p.block_size, p.top_n = int(block_size), int(top_n)
+    p = _select_params(B, S, E, block_size, top_n, k.shape[1], q_pos0, means_cached)
     need = int(lib().block_select_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)

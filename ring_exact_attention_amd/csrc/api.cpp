@@ -5,6 +5,7 @@
 // this file allocates device memory: scratch comes in through the caller's workspace.
 #include "attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -602,7 +603,8 @@ int block_select(const select_params* p_in, const void* q, const void* k, int32_
   if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
   if (struct_size_of(p) != sizeof(select_params))
     return fail(ATTN_ERR_INVALID_ARG, "params->struct_size does not match this library");
-  if (p->reserved != 0) return fail(ATTN_ERR_INVALID_ARG, "params->reserved must be 0");
+  if (p->means_cached < 0 || (p->block_size > 0 && p->means_cached > select_kv_rows(p) / p->block_size))
+    return fail(ATTN_ERR_INVALID_ARG, "params->means_cached must be in 0 .. seqlen_kv / block_size");
   if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "block_select supports bf16 inputs");
   if (p->batch < 0 || p->seqlen < 0 || p->seqlen_kv < 0 || p->q_pos0 < 0)
     return fail(ATTN_ERR_INVALID_ARG, "batch, seqlen, seqlen_kv and q_pos0 must be >= 0");
@@ -640,6 +642,11 @@ int block_select(const select_params* p_in, const void* q, const void* k, int32_
   a.bs = p->block_size;
   a.top_n = p->top_n;
   a.nblk = skv / p->block_size;
+  // Means needed: candidates of query block i are the blocks c < min(i, nblk), and the
+  // last query block of the call is (q_pos0 + S - 1) / bs; the first means_cached are
+  // already in the workspace.
+  a.mto = std::min(a.nblk, (a.q_pos0 + a.S - 1) / a.bs);
+  a.mfrom = std::min(p->means_cached, a.mto);
   a.nsplit = rea::select_splits(a.B, a.S, a.q_pos0, a.bs, a.nblk, a.top_n);
   {
     const size_t nm = (size_t)a.B * a.nblk * a.E * sizeof(double), nb = (size_t)a.B * a.nblk;

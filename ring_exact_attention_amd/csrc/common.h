@@ -121,6 +121,7 @@ struct SelectArgs {
   int32_t* part_c;    //   index -1 = empty), combined by block_select_merge_kernel
   uint16_t* msplit;   // [2, B, nblk, E] the means as sums of two bf16 parts (hi, lo)
   float* mnorm;       // [B, nblk] Euclidean norm of each mean, rounded up
+  int mfrom, mto;     // blocks whose means this call computes: [mfrom, mto)
 };
 
 struct SparseArgs {

@@ -106,7 +106,8 @@ __device__ __forceinline__ uint16_t bf16_bits_rne(float f) { return __builtin_bi
 // does not change the mean.
 __global__ __launch_bounds__(256) void block_means_kernel(SelectArgs a) {
   __shared__ double part[256 * 8];
-  const int wg = wg_index(a.rev_order), c = wg % a.nblk, b = wg / a.nblk;
+  const int nm = a.mto - a.mfrom;                       // blocks per sequence this call
+  const int wg = wg_index(a.rev_order), c = a.mfrom + wg % nm, b = wg / nm;
   const __bf16* kp = (const __bf16*)a.k + ((size_t)b * a.Skv + (size_t)c * a.bs) * a.E;
   double* mp = a.means + ((size_t)b * a.nblk + c) * a.E;
   const int cpr = a.E / 8;                               // 16-byte chunks per row (8 .. 128)
@@ -717,8 +718,8 @@ __global__ __launch_bounds__(256) void block_select_merge_kernel(SelectArgs a) {
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-  if (a.nblk > 0)
-    hipLaunchKernelGGL(block_means_kernel, dim3((unsigned)(a.B * a.nblk)), dim3(256), 0, stream, a);
+  if (a.mto > a.mfrom)
+    hipLaunchKernelGGL(block_means_kernel, dim3((unsigned)(a.B * (a.mto - a.mfrom))), dim3(256), 0, stream, a);
   if (a.S == 0) return hipGetLastError();
   const int nqb = (a.q_pos0 + a.S - 1) / a.bs - a.q_pos0 / a.bs + 1;
   if (a.nblk <= kSelFastMax && a.nsplit == 1) {

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
 
 
 def params(**kw):
@@ -174,6 +174,10 @@ def test_select_decode_checks(lib):
     assert call(sp()) == rea.ATTN_ERR_INVALID_ARG and b"idx is NULL" in lib.attn_last_error()
     assert call(sp(q_pos0=253)) == rea.ATTN_ERR_INVALID_ARG and b"q_pos0" in lib.attn_last_error()
     assert call(sp(q_pos0=-1)) == rea.ATTN_ERR_INVALID_ARG
+    # means_cached: 0 .. seqlen_kv / block_size (8 blocks here)
+    assert call(sp(means_cached=-1)) == rea.ATTN_ERR_INVALID_ARG and b"means_cached" in lib.attn_last_error()
+    assert call(sp(means_cached=9)) == rea.ATTN_ERR_INVALID_ARG and b"means_cached" in lib.attn_last_error()
+    assert call(sp(means_cached=8)) == rea.ATTN_ERR_INVALID_ARG and b"idx is NULL" in lib.attn_last_error()
     # workspace: the means of the key sequence's full blocks (fp64), their two bf16
     # parts and their norms (fp32), each part 256-byte aligned
     means = lambda nb, e: nb * e * 8 + 2 * nb * e * 2 + (nb * 4 + 255) // 256 * 256

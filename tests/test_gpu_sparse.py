@@ -3,6 +3,8 @@
 oracle, on seeded inputs: small ragged shapes, engineered exact ties, hand-made
 selections, the degenerate first blocks, and the full-size workload (B4 S8192, 8 heads
 x 64 as a joint embedding of 512, top-8 of 32-token blocks, window 32)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -148,6 +150,46 @@ def test_select_offset_queries_full_grid(gpu, bs, pos0):
     torch.cuda.synchronize()
     ref = select.block_select(qn, k, block_size=bs, top_n=n, q_pos0=pos0)
     np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("bs", [32, 16])
+def test_select_means_cached(gpu, bs):
+    """Decoding with the block means kept across calls: a first call computes the means of
+    the cache; the cache then gains rows (its blocks from c0 on change) and a second call
+    with means_cached = c0 on the same workspace recomputes only those.  Both equal the
+    oracle on their cache, and equal a call that computes every mean on a poisoned
+    workspace.  (32-row blocks of 8192 rows: 256 blocks, the bf16-bound path for the full
+    cache; 16-row blocks: 512, the split fp64 path.)"""
+    B, S, E, n, T = 2, 8192, 128, 8, 16
+    q, k = rnd((B, S, E), 130 + bs), rnd((B, S, E), 131 + bs)
+    nblk = S // bs
+    ws = torch.empty(gpu.lib().block_select_workspace_bytes(ctypes.byref(_sel_params(gpu, B, T, E, bs, n, S, S - T))),
+                     dtype=torch.uint8, device=DEV)
+    kd = k.to(DEV)
+    idx_full = gpu.block_select(q.to(DEV), kd, block_size=bs, top_n=n, workspace=ws)   # every mean
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx_full.cpu().numpy(), select.block_select(q, k, block_size=bs, top_n=n))
+    c0 = nblk - 40
+    k2 = k.clone()
+    k2[:, c0 * bs:] = rnd((B, S - c0 * bs, E), 140 + bs)        # rows of blocks >= c0 change
+    qn = q[:, S - T:].contiguous()
+    idx = gpu.block_select(qn.to(DEV), k2.to(DEV), block_size=bs, top_n=n, q_pos0=S - T, workspace=ws,
+                           means_cached=c0)
+    ws_poison = torch.full_like(ws, 0xFF)
+    idx_all = gpu.block_select(qn.to(DEV), k2.to(DEV), block_size=bs, top_n=n, q_pos0=S - T, workspace=ws_poison)
+    torch.cuda.synchronize()
+    ref = select.block_select(qn, k2, block_size=bs, top_n=n, q_pos0=S - T)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+    np.testing.assert_array_equal(idx_all.cpu().numpy(), ref)
+
+
+def _sel_params(gpu, B, S, E, bs, n, skv, pos0):
+    p = gpu.SelectParams()
+    p.struct_size = ctypes.sizeof(gpu.SelectParams)
+    p.dtype = gpu.ATTN_BF16
+    p.batch, p.seqlen, p.embed, p.block_size, p.top_n = B, S, E, bs, n
+    p.seqlen_kv, p.q_pos0 = skv, pos0
+    return p
 
 
 def test_select_many_blocks(gpu):
