@@ -381,12 +381,17 @@ def dense_measure(torch, rea, workloads, w, dev, steps, warmup, softmax="vanilla
     o = torch.empty((B, S, Hq, Dv), dtype=qd.dtype, device=dev)
     m = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     l = torch.empty_like(m)
-    segs = [("attn_fwd", lambda: rea.attn_fwd(qd, kd, vd, out=o, m=m, l=l, **kw))]
+    # A training step keeps the output's low part for the backward's D (the fp32 output,
+    # as the page's backward takes it); a forward-only workload has no use for it.
+    o_lo = torch.empty_like(o) if w.backward else None
+    segs = [("attn_fwd", lambda: rea.attn_fwd(qd, kd, vd, out=o, m=m, l=l, o_lo=o_lo, **kw))]
     if w.backward:
         grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
         ws = torch.empty(max(rea.bwd_workspace_bytes(qd, kd, head_dim_v=Dv, **kw), 256), dtype=torch.uint8,
                          device=dev)
-        bkw = dict(kw, dsink=torch.empty((Hq,), dtype=torch.float32, device=dev)) if sink is not None else kw
+        bkw = dict(kw, o_lo=o_lo)
+        if sink is not None:
+            bkw["dsink"] = torch.empty((Hq,), dtype=torch.float32, device=dev)
         # dq also computes D and the LSE, which the dk/dv call takes from the workspace
         segs.append(("bwd_dq", lambda: rea.attn_bwd(qd, kd, vd, o, dod, m, l, workspace=ws, out=grads,
                                                     skip_dkdv=True, **bkw)))
@@ -409,10 +414,12 @@ def dense_measure(torch, rea, workloads, w, dev, steps, warmup, softmax="vanilla
     esz = 2 if w.dtype == "bf16" else 4
     qbytes, kbytes, stat = B * S * Hq * D * esz, B * S * Hkv * D * esz, B * Hq * S * 4
     obytes, vbytes = B * S * Hq * Dv * esz, B * S * Hkv * Dv * esz
-    hbm = {"attn_fwd": qbytes + obytes + kbytes + vbytes + 2 * stat,
-           "bwd_dq": 2 * qbytes + 2 * obytes + kbytes + vbytes + 4 * stat,
+    # (o_lo, when kept, is one more o-sized write in the forward and read in the dq call.)
+    lo = obytes if o_lo is not None else 0
+    hbm = {"attn_fwd": qbytes + obytes + lo + kbytes + vbytes + 2 * stat,
+           "bwd_dq": 2 * qbytes + 2 * obytes + lo + kbytes + vbytes + 4 * stat,
            "bwd_dkdv": qbytes + obytes + 2 * kbytes + 2 * vbytes + 2 * stat}
-    hbm_bwd = 2 * qbytes + 2 * obytes + 2 * kbytes + 2 * vbytes + 2 * stat
+    hbm_bwd = 2 * qbytes + 2 * obytes + lo + 2 * kbytes + 2 * vbytes + 2 * stat
     kernels = {}
     for n, t in seg_ms.items():
         kernels[n] = {"avg_us": round(t * 1e3, 2), "us": stats_us(per[n]), "alg_gflop": round(alg[n] / 1e9, 3),

@@ -103,12 +103,14 @@ enum {
 
 /* 2: softmax_type, sink, dsink appended; 3: bias, bias_stride appended; 4: drop_mask,
  * drop_stride appended; 5: select_params.reserved became means_cached (0, the value it
- * had to hold, keeps the earlier behaviour).  Structs of the earlier sizes are still
- * accepted: the missing fields read as zero (ATTN_SOFTMAX_VANILLA, no bias, no dropout). */
-#define ATTN_PARAMS_VERSION 5u
+ * had to hold, keeps the earlier behaviour); 6: o_lo appended.  Structs of the earlier
+ * sizes are still accepted: the missing fields read as zero (ATTN_SOFTMAX_VANILLA, no
+ * bias, no dropout, no o_lo). */
+#define ATTN_PARAMS_VERSION 6u
 #define ATTN_PARAMS_V1_SIZE 104u
 #define ATTN_PARAMS_V2_SIZE 128u
 #define ATTN_PARAMS_V3_SIZE 168u
+#define ATTN_PARAMS_V4_SIZE 200u   /* versions 4 and 5 */
 
 typedef struct attn_params {
   uint32_t struct_size;        /* = sizeof(attn_params); versioning of the ABI        */
@@ -193,6 +195,18 @@ typedef struct attn_params {
    * attn_fwd and attn_bwd.  NULL = no dropout.  Dense mode only.                         */
   const uint32_t* drop_mask;
   int64_t drop_stride[3];
+  /* Low part of the output ("bpt.py": the forward keeps the output from before its cast
+   * to the input dtype as a residual, and the backward takes each row's dot product of
+   * dout with that output, D_i).  bf16 [B, Sq, Hq, head_dim_v] device, 16-byte aligned,
+   * laid out like o; caller-owned.  attn_fwd (bf16, dense, a call that finalises) writes
+   * o_lo = bf16(o32 - o) beside o = bf16(o32), o32 being the fp32 output, so o + o_lo
+   * holds o32 to about 16 bits.  attn_bwd forms D_i from o + o_lo.  NULL in attn_fwd:
+   * not written; NULL in attn_bwd: D_i from o alone, which puts the output's bf16
+   * rounding into dq and dk through D (past the bf16 bound by a few percent where a key
+   * collects several hundred (row, head) pairs, e.g. a GQA group of 8 under a causal
+   * window of 100).  Must be NULL for fp32 tensors and in sparse mode (whose backward
+   * forms D_i from its fp32 probabilities).                                            */
+  void* o_lo;
 } attn_params;
 
 /* 2: seqlen_kv and q_pos0 appended (a version-1 struct of SELECT_PARAMS_V1_SIZE bytes

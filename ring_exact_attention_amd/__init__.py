@@ -67,6 +67,7 @@ class AttnParams(ctypes.Structure):
         ("bias_stride", ctypes.c_int64 * 4),
         ("drop_mask", ctypes.c_void_p),
         ("drop_stride", ctypes.c_int64 * 3),
+        ("o_lo", ctypes.c_void_p),
     ]
 
 
@@ -169,7 +170,7 @@ def _softmax_code(softmax_type, sink):
 
 def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
                 kv_block=0, q_pos0=0, kv_pos0=0, flags=0, head_dim_v=0, softmax_type="vanilla",
-                sink=None, bias=None, dropout=None) -> AttnParams:
+                sink=None, bias=None, dropout=None, o_lo=None) -> AttnParams:
     B, Sq, Hq, D = q.shape
     Bk, Skv, Hkv, Dk = k.shape
     if Bk != B or Dk != D:
@@ -208,6 +209,13 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
         p.drop_mask = dropout.data_ptr()
         for d in range(3):
             p.drop_stride[d] = view.stride(d) if view.shape[d] > 1 else 0
+    if o_lo is not None:
+        # the output's low part, bf16 [B, Sq, Hq, Dv] like o (attn_fwd writes it, attn_bwd reads it)
+        Dv = head_dim_v if head_dim_v else D
+        _need(o_lo, "o_lo", torch.bfloat16, q.device)
+        if q.dtype != torch.bfloat16 or o_lo.shape != (B, Sq, Hq, Dv):
+            raise ValueError(f"o_lo applies to bf16 attention and must be [B, Sq, Hq, Dv] = {(B, Sq, Hq, Dv)}")
+        p.o_lo = o_lo.data_ptr()
     p.q_pos0, p.kv_pos0 = int(q_pos0), int(kv_pos0)
     p.causal = 1 if causal else 0
     p.window_left, p.window_right = int(window[0]), int(window[1])
@@ -219,7 +227,8 @@ def make_params(q, k, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
 
 def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0, key_chunk=0,
              kv_block=0, q_pos0=0, kv_pos0=0, m=None, l=None, acc=None, carry_in=False,
-             finalize=True, out=None, softmax_type="vanilla", sink=None, bias=None, dropout=None):
+             finalize=True, out=None, softmax_type="vanilla", sink=None, bias=None, dropout=None,
+             o_lo=None):
     """Forward attention.  q [B, Sq, Hq, D], k [B, Skv, Hkv, D], v [B, Skv, Hkv, Dv] on the GPU
     (Dv = D, or the MLA pair D 128 / Dv 64).
 
@@ -230,7 +239,9 @@ def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     ``bias``: fp32 additive logit bias broadcastable to [B, Hq, Sq, Skv] (-inf masks).
     ``dropout``: packed int32 dropout bits [B|1, Hq|1, Sq|1, ceil(Skv/32)] (see
     workloads.pack_bits); a set bit drops the pair from the softmax.  Pass the same
-    tensor to attn_bwd.
+    tensor to attn_bwd.  ``o_lo``: a bf16 tensor shaped like o that a finalising call
+    fills with the output's low part (fp32 output minus o, rounded); attn_bwd given it
+    forms its row dot products D from the fp32 output instead of the rounded o.
     """
     _need(q, "q")
     _need(k, "k", q.dtype, q.device)
@@ -242,7 +253,8 @@ def attn_fwd(q, k, v, *, causal=True, window=(-1, -1), scale=None, query_chunk=0
     flags = (ATTN_CARRY_IN if carry_in else 0) | (0 if finalize else ATTN_NO_FINALIZE)
     p = make_params(q, k, causal=causal, window=window, scale=scale, query_chunk=query_chunk,
                     key_chunk=key_chunk, kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, flags=flags,
-                    head_dim_v=Dv, softmax_type=softmax_type, sink=sink, bias=bias, dropout=dropout)
+                    head_dim_v=Dv, softmax_type=softmax_type, sink=sink, bias=bias, dropout=dropout,
+                    o_lo=o_lo if finalize else None)
     dev = q.device
     if m is None:
         m = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
@@ -275,7 +287,7 @@ def bwd_workspace_bytes(q, k, **kw) -> int:
 def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None, query_chunk=0,
              key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, workspace=None, out=None,
              skip_dq=False, skip_dkdv=False, reuse_stats=False, softmax_type="vanilla", sink=None,
-             dsink=None, bias=None, dropout=None, accumulate=False):
+             dsink=None, bias=None, dropout=None, accumulate=False, o_lo=None):
     """Gradients (dq, dk, dv) of attn_fwd's output for upstream gradient dout.
 
     ``skip_dq`` / ``skip_dkdv`` compute only part of them (the skipped outputs are left
@@ -284,7 +296,8 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
     gradient of the sink logits is returned as a fourth tensor (fp32 [Hq]; written by
     calls that compute dq).  ``accumulate``: one ring step of the backward pass -- ``out``
     holds fp32 dq, dk, dv (and ``dsink`` fp32) that this call adds its gradients into
-    (zeros are allocated when they are not given).
+    (zeros are allocated when they are not given).  ``o_lo``: the output's low part that
+    attn_fwd wrote, for D from the fp32 output.
     """
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _need(t, n, q.dtype, q.device)
@@ -296,7 +309,7 @@ def attn_bwd(q, k, v, o, dout, m, l, *, causal=True, window=(-1, -1), scale=None
         raise ValueError("v must match k except in its head dim, and o, dout must be [B, Sq, Hq, Dv]")
     kw = dict(causal=causal, window=window, scale=scale, query_chunk=query_chunk, key_chunk=key_chunk,
               kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, head_dim_v=Dv, softmax_type=softmax_type,
-              sink=sink, bias=bias, dropout=dropout)
+              sink=sink, bias=bias, dropout=dropout, o_lo=o_lo)
     flags = ((ATTN_BWD_SKIP_DQ if skip_dq else 0) | (ATTN_BWD_SKIP_DKDV if skip_dkdv else 0) |
              (ATTN_BWD_REUSE_STATS if reuse_stats else 0) | (ATTN_BWD_ACCUMULATE if accumulate else 0))
     p = make_params(q, k, flags=flags, **kw)
@@ -333,7 +346,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20     # ATTN_NOALLOC_SCRATCH_BYTES of attn.h
 def attn_bwd_noalloc(q, k, v, o, dout, m, l, *, out, causal=True, window=(-1, -1), scale=None,
                      query_chunk=0, key_chunk=0, kv_block=0, q_pos0=0, kv_pos0=0, skip_dq=False,
                      skip_dkdv=False, reuse_stats=False, softmax_type="vanilla", sink=None, dsink=None,
-                     bias=None, dropout=None):
+                     bias=None, dropout=None, o_lo=None):
     """attn_bwd without a workspace (the library's static scratch; see attn.h): the caller
     passes the outputs ``out = (dq, dk, dv)`` (and ``dsink`` for a learnable sink), so this
     call allocates nothing.  Returns ``out``."""
@@ -350,7 +363,8 @@ def attn_bwd_noalloc(q, k, v, o, dout, m, l, *, out, causal=True, window=(-1, -1
              (ATTN_BWD_REUSE_STATS if reuse_stats else 0))
     p = make_params(q, k, causal=causal, window=window, scale=scale, query_chunk=query_chunk,
                     key_chunk=key_chunk, kv_block=kv_block, q_pos0=q_pos0, kv_pos0=kv_pos0, flags=flags,
-                    head_dim_v=v.shape[3], softmax_type=softmax_type, sink=sink, bias=bias, dropout=dropout)
+                    head_dim_v=v.shape[3], softmax_type=softmax_type, sink=sink, bias=bias, dropout=dropout,
+                    o_lo=o_lo)
     if dsink is not None:
         _need(dsink, "dsink", torch.float32, q.device)
         p.dsink = dsink.data_ptr()

@@ -58,6 +58,7 @@ struct Problem {
   bool bias_vec4 = false;
   const uint32_t* drop = nullptr;
   long long drop_stride[3] = {0, 0, 0};
+  void* o_lo = nullptr;
 };
 
 static_assert(offsetof(attn_params, softmax_type) == ATTN_PARAMS_V1_SIZE,
@@ -66,9 +67,11 @@ static_assert(offsetof(attn_params, bias) == ATTN_PARAMS_V2_SIZE,
               "a version-2 attn_params is the current one without its bias fields");
 static_assert(offsetof(attn_params, drop_mask) == ATTN_PARAMS_V3_SIZE,
               "a version-3 attn_params is the current one without its dropout fields");
+static_assert(offsetof(attn_params, o_lo) == ATTN_PARAMS_V4_SIZE,
+              "a version-4 (or 5) attn_params is the current one without o_lo");
 
 // The caller's params in the current layout: an earlier version's struct reads with its
-// missing fields zero (ATTN_SOFTMAX_VANILLA, no bias, no dropout).  Other sizes pass through for the
+// missing fields zero (ATTN_SOFTMAX_VANILLA, no bias, no dropout, no o_lo).  Other sizes pass through for the
 // size check.
 // First field of every params struct: read with memcpy, since a caller's struct of an
 // unknown or older version may be shorter than the current type.
@@ -83,7 +86,9 @@ uint32_t struct_size_of(const void* p) {
 const attn_params* current_layout(const attn_params* p, attn_params& tmp) {
   if (!p) return p;
   const uint32_t n = struct_size_of(p);
-  if (n != ATTN_PARAMS_V1_SIZE && n != ATTN_PARAMS_V2_SIZE && n != ATTN_PARAMS_V3_SIZE) return p;
+  if (n != ATTN_PARAMS_V1_SIZE && n != ATTN_PARAMS_V2_SIZE && n != ATTN_PARAMS_V3_SIZE &&
+      n != ATTN_PARAMS_V4_SIZE)
+    return p;
   memset(&tmp, 0, sizeof tmp);
   memcpy(&tmp, p, n);
   tmp.struct_size = sizeof(attn_params);
@@ -151,6 +156,10 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
       if (p->drop_stride[d] < 0 || p->drop_stride[d] > (1LL << 40))
         return fail(ATTN_ERR_INVALID_ARG, "drop_stride entries must be in [0, 2^40]");
   }
+  if (p->o_lo) {
+    if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "o_lo applies to bf16 tensors only (must be NULL)");
+    if (!aligned16(p->o_lo)) return fail(ATTN_ERR_INVALID_ARG, "o_lo must be 16-byte aligned");
+  }
   const uint32_t fwd_flags = ATTN_CARRY_IN | ATTN_NO_FINALIZE;
   const uint32_t bwd_flags = ATTN_BWD_SKIP_DQ | ATTN_BWD_SKIP_DKDV | ATTN_BWD_REUSE_STATS | ATTN_BWD_ACCUMULATE;
   if (p->flags & ~(fwd_flags | bwd_flags)) return fail(ATTN_ERR_INVALID_ARG, "unknown bits in flags");
@@ -195,6 +204,7 @@ int check_dense(const attn_params* p, bool bwd, Problem& r) {
   for (int d = 0; d < 4; ++d) r.bias_stride[d] = p->bias_stride[d];
   r.drop = p->drop_mask;
   for (int d = 0; d < 3; ++d) r.drop_stride[d] = p->drop_stride[d];
+  r.o_lo = p->o_lo;
   // Rows of the bias read as 16-byte vectors by the bf16 kernels: unit key stride, every
   // row start 16-byte aligned, and key tiles that start at multiples of 4 keys.
   r.bias_vec4 = r.bias && r.bias_stride[3] == 1 && ((uintptr_t)r.bias & 15u) == 0 &&
@@ -248,6 +258,7 @@ int check_sparse(const attn_params* p) {
     return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no sink softmax");
   if (p->bias) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no bias");
   if (p->drop_mask) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no dropout mask");
+  if (p->o_lo) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode has no o_lo (its backward forms D from fp32 probabilities)");
   if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "sparse mode supports bf16 only");
   if (p->num_q_heads != 1 || p->num_kv_heads != 1)
     return fail(ATTN_ERR_INVALID_ARG, "sparse mode takes the joint embedding: num_q_heads = num_kv_heads = 1");
@@ -406,6 +417,7 @@ int attn_fwd(const attn_params* p_in, const void* q, const void* k, const void* 
   a.k = k;
   a.v = v;
   a.o = o;
+  a.o_lo = r.finalize ? r.o_lo : nullptr;
   a.m = m;
   a.l = l;
   a.acc = acc;
@@ -512,6 +524,7 @@ int attn_bwd(const attn_params* p_in, const void* q, const void* k, const void* 
   a.k = k;
   a.v = v;
   a.o = o;
+  a.o_lo = r.o_lo;
   a.dout = dout;
   a.m = m;
   a.l = l;

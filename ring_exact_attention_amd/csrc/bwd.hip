@@ -45,6 +45,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
         part = fmaf(__uint_as_float(ou[w]), __uint_as_float(gu[w]), part);
       }
     }
+    if constexpr (sizeof(T) == 2) {
+      if (a.o_lo) {   // the output's low part: D_i from the fp32 output, not its bf16 rounding
+        const u32x4 lu = *(const u32x4*)((const T*)a.o_lo + rowg * D + sub * EPC);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          part = fmaf(bf16_lo(lu[w]), bf16_lo(gu[w]), part);
+          part = fmaf(bf16_hi(lu[w]), bf16_hi(gu[w]), part);
+        }
+      }
+    }
   }
   part = sum_lanes<LPR>(part);
   if (rowg < nrows && sub == 0) {
@@ -361,6 +371,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
 #pragma unroll
       for (int i = 0; i < NO; ++i) dma16(rg, qs + 1024 * i, (uint32_t)(RPO * i + orr) * o_rs_b + 16u * orc);
     }
+    // The output's low part, when given, in the same round trip as dO (O's rows layout).
+    u32x4 lrow[NO];
+    const bool with_lo = fused && a.o_lo != nullptr;
+    if (with_lo) {
+      const __amdgpu_buffer_rsrc_t rl = rsrc_rows(a.o_lo, o_rs);
+#pragma unroll
+      for (int i = 0; i < NO; ++i) lrow[i] = buf_load16(rl, (uint32_t)(RPO * i + orr) * o_rs_b + 16u * orc, 0);
+    }
     wait_vmcnt0();
     __syncthreads();
 #pragma unroll
@@ -376,6 +394,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_bf16_kernel(BwdArgs a)
         for (int w = 0; w < 4; ++w) {
           part = fmaf(bf16_lo(orow[i][w]), bf16_lo(gu[w]), part);
           part = fmaf(bf16_hi(orow[i][w]), bf16_hi(gu[w]), part);
+        }
+        if (with_lo) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            part = fmaf(bf16_lo(lrow[i][w]), bf16_lo(gu[w]), part);
+            part = fmaf(bf16_hi(lrow[i][w]), bf16_hi(gu[w]), part);
+          }
         }
         part = sum_lanes<C::DCV>(part);
         if (orc == 0) sd[RPO * i + orr] = part;

@@ -29,6 +29,7 @@ struct FwdArgs {
   const void* k;
   const void* v;
   void* o;
+  void* o_lo;         // NULL, or bf16 like o: the fp32 output's rounding residual
   float* m;
   float* l;
   float* acc;
@@ -72,6 +73,7 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* o;
+  const void* o_lo;   // NULL, or o's low part (bf16 like o): D_i uses o + o_lo
   const void* dout;
   const float* m;
   const float* l;

@@ -408,16 +408,26 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     const float inv = den > 0.f ? 1.f / den : 0.f;
     constexpr int OP = 2 * DV + 16, RPO = 64 / C::DCV;
     char* const os = lds + wave * (32 * OP);
+    const size_t o_off = ((size_t)b * a.Sq + row0) * o_rs + (size_t)hq * DV;
+    // The low part x - bf16(x) of each output, rounded to bf16, goes straight from the
+    // registers to o_lo (8 bytes per lane, the two lanes of a row 16 contiguous bytes).
+    __bf16* const lrow = a.o_lo ? (__bf16*)a.o_lo + o_off + (size_t)li * o_rs : nullptr;
+    const bool lo_ok = a.o_lo != nullptr && row0 + li < a.Sq;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+        u32x2 w, wl;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float x0 = acc[db][4 * g + 2 * h] * inv, x1 = acc[db][4 * g + 2 * h + 1] * inv;
+          w[h] = pack_bf16x2(x0, x1);
+          wl[h] = pack_bf16x2(x0 - bf16_lo(w[h]), x1 - bf16_hi(w[h]));
+        }
         *(u32x2*)(os + li * OP + 2 * (32 * db + 8 * g + 4 * lh)) = w;
+        if (lo_ok) *(u32x2*)(lrow + 32 * db + 8 * g + 4 * lh) = wl;
       }
-    __bf16* ob = (__bf16*)a.o + ((size_t)b * a.Sq + row0) * o_rs + (size_t)hq * DV;
+    __bf16* ob = (__bf16*)a.o + o_off;
 #pragma unroll
     for (int i = 0; i < 32 / RPO; ++i) {
       const int r = RPO * i + lane / C::DCV, ch = lane % C::DCV;

@@ -113,9 +113,12 @@ int main() {
   bad.drop_mask = (const uint32_t*)fake(13);
   bad.drop_stride[2] = (int64_t)1 << 50;
   expect_status(fwd(&bad), ATTN_ERR_INVALID_ARG, "huge dropout stride");
+  bad = p;
+  bad.o_lo = (char*)fake(14) + 2;
+  expect_status(fwd(&bad), ATTN_ERR_INVALID_ARG, "misaligned o_lo");
 
   // ---- older struct versions as heap blocks of exactly their size
-  const unsigned sizes[3] = {ATTN_PARAMS_V1_SIZE, ATTN_PARAMS_V2_SIZE, ATTN_PARAMS_V3_SIZE};
+  const unsigned sizes[4] = {ATTN_PARAMS_V1_SIZE, ATTN_PARAMS_V2_SIZE, ATTN_PARAMS_V3_SIZE, ATTN_PARAMS_V4_SIZE};
   for (unsigned sz : sizes) {
     unsigned char* blk = (unsigned char*)malloc(sz);
     memcpy(blk, &p, sz);

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
 
 
 def params(**kw):
@@ -61,10 +61,11 @@ def fwd_status(lib, p, ptr=None):
 
 
 def test_struct_layout(lib):
-    assert ctypes.sizeof(rea.AttnParams) == 200
+    assert ctypes.sizeof(rea.AttnParams) == 208
     assert rea.AttnParams.softmax_type.offset == 104          # ATTN_PARAMS_V1_SIZE
     assert rea.AttnParams.bias.offset == 128                  # ATTN_PARAMS_V2_SIZE
     assert rea.AttnParams.drop_mask.offset == 168             # ATTN_PARAMS_V3_SIZE
+    assert rea.AttnParams.o_lo.offset == 200                  # ATTN_PARAMS_V4_SIZE
     assert ctypes.sizeof(rea.SelectParams) == 40
     assert rea.SelectParams.seqlen_kv.offset == 32          # SELECT_PARAMS_V1_SIZE
     # a zero batch is a successful no-op only when the struct size matches
@@ -128,11 +129,40 @@ def test_version3_struct_is_accepted(lib):
     p.drop_mask = 0x1002                              # misaligned, past the v3 size: ignored
     p.struct_size = 168
     assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"q is NULL" in lib.attn_last_error()
-    p.struct_size = 200
+    p.struct_size = 208
     assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"drop_mask" in lib.attn_last_error()
     p.drop_mask = 0x1000
     p.drop_stride[1] = -4
     assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"drop_stride" in lib.attn_last_error()
+
+
+def test_version4_struct_is_accepted(lib):
+    """A 200-byte struct (versions 4 and 5, before o_lo) reads as having no o_lo."""
+    p = params(batch=1)
+    p.o_lo = 0x1002                                   # misaligned, past the v4 size: ignored
+    p.struct_size = 200
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"q is NULL" in lib.attn_last_error()
+    p.struct_size = 208
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"o_lo" in lib.attn_last_error()
+
+
+def test_o_lo_checks(lib):
+    """o_lo: bf16 dense only, 16-byte aligned; rejected in sparse mode."""
+    d = ctypes.c_void_p(0x1000)
+    p = params(dtype=rea.ATTN_F32, head_dim=64, o_lo=0x1000)
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"o_lo" in lib.attn_last_error()
+    p = params(o_lo=0x1000)
+    assert fwd_status(lib, p) == rea.ATTN_ERR_INVALID_ARG and b"q is NULL" in lib.attn_last_error()
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(p))
+    assert need == lib.attn_bwd_workspace_bytes(ctypes.byref(params()))
+    p.o_lo = 0x1008
+    st = lib.attn_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, need, None)
+    assert st == rea.ATTN_ERR_INVALID_ARG and b"o_lo" in lib.attn_last_error()
+    s = params(num_q_heads=1, num_kv_heads=1, head_dim=512, seqlen_q=64, seqlen_kv=64, causal=0, o_lo=0x1000)
+    s.sel_idx = 0x1000
+    s.top_n, s.sel_block, s.sparse_window = 8, 32, 32
+    assert lib.attn_fwd(ctypes.byref(s), d, d, d, d, d, d, None, None) == rea.ATTN_ERR_UNSUPPORTED
+    assert b"o_lo" in lib.attn_last_error()
 
 
 def test_version2_struct_is_accepted(lib):

@@ -11,6 +11,7 @@ the key block), and that bench.py times:
   D / log-sum-exp pass.
 
 Each sequence must give bitwise the gradients of the single call, and match the oracle.
+Every call takes the output's low part (o_lo) as bench.py's training step does.
 """
 import zlib
 
@@ -67,8 +68,9 @@ def test_bench_sequence_small(gpu, case):
         rnd((B, S, Hq, Dv), seed + 3)
     kw = dict(causal=causal, window=window, kv_block=kvb)
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
-    o, m, l = gpu.attn_fwd(qd, kd, vd, **kw)
-    single, seq, kv_only = split_and_single(gpu, qd, kd, vd, o, dod, m, l, **kw)
+    o_lo = torch.empty_like(dod)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, o_lo=o_lo, **kw)
+    single, seq, kv_only = split_and_single(gpu, qd, kd, vd, o, dod, m, l, o_lo=o_lo, **kw)
     for nm, a, b in zip(("dq", "dk", "dv"), single, seq):
         assert torch.equal(a, b), f"{nm}: the split sequence differs from the single call"
     dq_r, dk_r, dv_r = dense.backward(q, k, v, do, causal=causal, window=window)
@@ -90,8 +92,9 @@ def test_bench_sequence_ring_full_size(gpu):
     kw = dict(causal=w.causal, window=w.window, query_chunk=w.query_chunk, key_chunk=w.key_chunk,
               kv_block=w.kv_block)
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
-    o, m, l = gpu.attn_fwd(qd, kd, vd, **kw)
-    single, seq, kv_only = split_and_single(gpu, qd, kd, vd, o, dod, m, l, **kw)
+    o_lo = torch.empty_like(dod)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, o_lo=o_lo, **kw)
+    single, seq, kv_only = split_and_single(gpu, qd, kd, vd, o, dod, m, l, o_lo=o_lo, **kw)
     for nm, a, b in zip(("dq", "dk", "dv"), single, seq):
         assert torch.equal(a, b), f"{nm}: the split sequence differs from the single call"
     bh = [5, 14]

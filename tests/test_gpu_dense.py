@@ -651,6 +651,54 @@ def test_backward_is_deterministic(gpu, window, Dv):
     assert torch.equal(o, o2)
 
 
+LOW_PART = [
+    # id, B, S, Hq, Hkv, D, Dv, causal, window, kv_block, seed
+    ("gqa8_window99_d64", 2, 211, 16, 2, 64, 64, True, (99, 0), 0, 4507),
+    ("mla_gqa4_ring_ragged", 1, 300, 8, 2, 128, 64, True, (-1, -1), 100, 77),
+    ("d128_full_window", 1, 257, 4, 4, 128, 128, False, (60, 20), 0, 91),
+]
+
+
+@pytest.mark.parametrize("case", LOW_PART, ids=[c[0] for c in LOW_PART])
+def test_output_low_part(gpu, case):
+    """o_lo, the output's low part ("bpt.py" keeps the output from before its cast to the
+    input dtype for the backward): o is bitwise the same with and without it; o_lo is at
+    most half a bf16 unit in the last place of o and zero where o is; o + o_lo is nearer
+    the oracle's output than o; and the gradients that take it match the oracle.  The
+    first shape's keys each collect about 800 (row, head) pairs (a GQA group of 8 under a
+    causal window of 99 keys): there o alone puts enough of its rounding into D to leave
+    the bf16 bound on one element of dk."""
+    name, B, S, Hq, Hkv, D, Dv, causal, window, kvb, s = case
+    t = torch.bfloat16
+    q, k, v, do = rnd((B, S, Hq, D), s, t), rnd((B, S, Hkv, D), s + 1, t), rnd((B, S, Hkv, Dv), s + 2, t), \
+        rnd((B, S, Hq, Dv), s + 3, t)
+    kw = dict(causal=causal, window=window, kv_block=kvb)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o_lo = torch.full((B, S, Hq, Dv), float("nan"), dtype=t, device=DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, o_lo=o_lo, **kw)
+    o_plain, _, _ = gpu.attn_fwd(qd, kd, vd, **kw)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, o_lo=o_lo, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain), "o must not depend on whether o_lo is written"
+    hi, lo = o.cpu().double().numpy(), o_lo.cpu().double().numpy()
+    assert np.isfinite(lo).all(), "o_lo must be written everywhere"
+    nz = hi != 0
+    assert (lo[~nz] == 0).all()
+    half_ulp = np.exp2(np.floor(np.log2(np.abs(hi[nz]))) - 8)
+    assert (np.abs(lo[nz]) <= half_ulp).all(), "o_lo exceeds half a bf16 ulp of o"
+    o_r, _, _ = dense.forward(q, k, v, **kw_oracle(kw))
+    rel = lambda x: np.linalg.norm(x - o_r) / np.linalg.norm(o_r)
+    assert rel(hi + lo) < 0.8 * rel(hi), (rel(hi + lo), rel(hi))
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, **kw_oracle(kw))
+    check_close("dq", dq, dq_r, "bf16")
+    check_close("dk", dk, dk_r, "bf16")
+    check_close("dv", dv, dv_r, "bf16")
+
+
+def kw_oracle(kw):
+    return dict(causal=kw["causal"], window=kw["window"])
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_rows_without_visible_keys(gpu, dt):
     t = tdtype(dt)

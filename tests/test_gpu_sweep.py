@@ -6,7 +6,11 @@ two-sided window, right window only, none), query / key position offsets, virtua
 blocks whose length divides Skv (often not a multiple of 32), and optionally an additive
 bias of a broadcast shape and a packed dropout array, then checks the forward outputs,
 the statistics and the three gradients element by element.  The draws cover both
-workgroup shapes of the forward and dq kernels and their tile boundaries.
+workgroup shapes of the forward and dq kernels and their tile boundaries.  The backward
+takes the output's low part (o_lo), so that its row dot products D come from the fp32
+output as in "bpt.py"; the rounded o alone carries its bf16 rounding into dq and dk,
+which in one of these draws (a GQA group of 8 under a causal window of 99 keys) ends up
+2% past the bf16 bound on one element of dk.
 """
 import numpy as np
 import pytest
@@ -19,7 +23,7 @@ from parity import check_close, check_stats
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-N_CASES = 40
+N_CASES = 64
 DIMS = [(32, 32), (64, 64), (128, 128), (128, 64)]
 
 
@@ -89,8 +93,9 @@ def test_random_config(gpu, i):
     gk = dict(mask, kv_block=c["kb"], bias=None if bias is None else bias.to(DEV),
               dropout=None if drop is None else workloads.pack_bits(drop).to(DEV))
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
-    o, m, l = gpu.attn_fwd(qd, kd, vd, **gk)
-    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, **gk)
+    o_lo = torch.empty((B, Sq, Hq, Dv), dtype=t, device=DEV)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, o_lo=o_lo, **gk)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, o_lo=o_lo, **gk)
     torch.cuda.synchronize()
     ok = dict(mask, bias=bias, dropout=None if drop is None else drop.numpy())
     o_r, m_r, l_r = dense.forward(q, k, v, **ok)
