@@ -39,15 +39,21 @@ DEFAULT_WORKLOAD = "ring_sim_causal_s8192"
 
 
 def kernel_source_sha():
-    """sha1 over the kernel sources (csrc/* and include/attn.h, sorted by name)."""
+    """sha1 over the kernel sources (csrc/* and include/attn.h, sorted by name), with
+    their comments and blank space taken out, so that an edit of a comment does not mark
+    the measured counters as stale while any change to the code does."""
     import hashlib
+    import re
     root = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(root, "ring_exact_attention_amd", "csrc")
     files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(root, "include", "attn.h")]
+    # string and character literals are kept whole; // and /* */ comments are dropped
+    tok = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
     h = hashlib.sha1()
     for f in files:
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = tok.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", fh.read())
+        h.update(os.path.basename(f).encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()
 
 
@@ -316,10 +322,16 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
         kernels.setdefault(n, {})["us"] = stats_us(per[n])
     # roofline of the dominant attention kernel (the gradient's when it is timed): the
     # forward on the MFMA work it executes (one 32-row step per window block and distinct
-    # selected block of each 32-token group), the gradient on its gathered bytes
+    # selected block of each 32-token group), the gradient on its compulsory HBM bytes:
+    # q, k, v, o, dO read and dq, dk, dv written once (8 bf16 [B, S, E] tensors), the
+    # indices and m, l read, D and the LSE written and read back (fp32 per token).  Its
+    # gathered bytes (every slot's K and V rows, twice) count blocks shared within a token
+    # group once per token, so they exceed what HBM can move and are reported beside it.
     rk = "attn_bwd_sparse" if args.sparse_backward else "attn_fwd_sparse"
-    rbytes = 2 * gathered if args.sparse_backward else gathered
+    sp = B * S * E * 2
+    rbytes = (8 * sp + B * S * (w.top_n * 4 + 8 + 16)) if args.sparse_backward else gathered
     ach = rbytes / (seg_ms[rk] * 1e-3) / 1e9
+    gathered_logical = (2 * gathered if args.sparse_backward else gathered) / (seg_ms[rk] * 1e-3) / 1e9
     f_exec, nsteps = sparse_union_flops(idx.cpu().numpy(), 32, w.sparse_window, w.block_size, E)
     out = {"metric": METRIC, "value": round((f_sparse + f_select + f_bwd) / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -332,7 +344,8 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
            "roofline": {"kernel": rk, "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                         "avg_us": round(seg_ms[rk] * 1e3, 2), "alg_bytes_per_launch": rbytes,
-                        "traffic": measured_traffic(w.name, rk), "mall_flush": True}}
+                        "traffic": measured_traffic(w.name, rk), "mall_flush": True,
+                        "gathered_gbs_logical": round(gathered_logical, 1)}}
     if not args.sparse_backward:
         tf = f_exec / (seg_ms[rk] * 1e-3) / 1e12
         traffic = measured_traffic(w.name, rk)
@@ -340,7 +353,7 @@ def bench_sparse(torch, rea, workloads, w, dev, args):
                            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                            "avg_us": round(seg_ms[rk] * 1e3, 2), "executed_flop_per_launch": f_exec,
                            "union_steps": nsteps, "traffic": traffic, "mall_flush": True,
-                           "gathered_gbs_logical": round(ach, 1)}
+                           "gathered_gbs_logical": round(gathered_logical, 1)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = sparse_cpu_baseline(w, q, k, v, idx.cpu().numpy(), args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -205,7 +205,8 @@ typedef struct attn_params {
    * rounding into dq and dk through D (past the bf16 bound by a few percent where a key
    * collects several hundred (row, head) pairs, e.g. a GQA group of 8 under a causal
    * window of 100).  Must be NULL for fp32 tensors and in sparse mode (whose backward
-   * forms D_i from its fp32 probabilities).                                            */
+   * forms D_i from o, or from its fp32 probabilities where rows of -1 entries gather
+   * the gradients of many slots).                                                      */
   void* o_lo;
 } attn_params;
 
