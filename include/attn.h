@@ -176,13 +176,14 @@ typedef struct attn_params {
    * units of the scaled logits; element (b, hq, i, j) -- this call's query row i and
    * key row j -- is bias[b*s0 + hq*s1 + i*s2 + j*s3] with s = bias_stride (elements,
    * >= 0; 0 broadcasts that dimension).  -inf removes a pair like the mask.  NULL = none.
-   * Dense mode only.  Gradient accuracy: P and dS enter the bf16 backward's MFMAs rounded
-   * to bf16, so where a few keys take most of the attention of thousands of (row, head)
-   * pairs -- a bias shared by all rows (one value per key) of magnitude 2 or more, with
-   * GQA groups of 8 -- dk and dv can leave the bf16 bound 2e-2 + 2^-8 |ref| by up to 2x.
-   * Checked within that bound: key padding (0 / -inf), key-shared biases up to scale
-   * 0.5 over random shapes, per-row / per-head / full biases, and a dense N(0,1) bias
-   * [1, 1, S, S] on a causal S = 8192 ring of 16 heads.                                  */
+   * Dense mode only.  Gradient accuracy: with a bias, P and dS enter dv and dk as bf16
+   * pairs (high part and rounded low part), since a bias can give a few keys most of the
+   * attention of hundreds of (row, head) pairs; the bias backward's dk/dv kernel runs
+   * two more matrix products per step for that.  A bias shared by all rows (one value
+   * per key) of magnitude 2 with GQA groups of 8 can still take dk up to 1.5x the bf16
+   * bound 2e-2 + 2^-8 |ref|.  Checked within that bound: key padding (0 / -inf), key-
+   * shared N(0,1) biases over random shapes (with o_lo), per-row / per-head / full
+   * biases, and a dense N(0,1) bias [1, 1, S, S] on a causal S = 8192 ring of 16 heads. */
   const float* bias;
   int64_t bias_stride[4];
   /* Dropout ("bpt.py": _blockwise_attention_fwd / _bwd draw a Bernoulli(attn_pdrop) array

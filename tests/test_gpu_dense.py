@@ -224,6 +224,45 @@ def test_additive_bias(gpu, case):
     check_close("dv", dv, dv_r, dt)
 
 
+SHARED_BIAS = [
+    # id, B, S, Hq, Hkv, D, causal, window: one N(0,1) offset per key shared by every row
+    ("g16_causal_d64_s96", 1, 96, 16, 1, 64, True, (-1, -1)),
+    ("g8_causal_d128_s300", 2, 300, 16, 2, 128, True, (-1, -1)),
+    ("g16_window120_d128_s400", 1, 400, 16, 1, 128, True, (120, 0)),
+    ("g8_full_d64_s200", 1, 200, 8, 1, 64, False, (-1, -1)),
+]
+
+
+def shared_bias_inputs(case):
+    name, B, S, Hq, Hkv, D, causal, window = case
+    seed = zlib.crc32(name.encode()) % 10000
+    t = torch.bfloat16
+    q, k, v, do = (rnd((B, S, Hq, D), seed, t), rnd((B, S, Hkv, D), seed + 1, t),
+                   rnd((B, S, Hkv, D), seed + 2, t), rnd((B, S, Hq, D), seed + 3, t))
+    return q, k, v, do, workloads.random_tensor((B, 1, 1, S), seed + 4)
+
+
+@pytest.mark.parametrize("case", SHARED_BIAS, ids=[c[0] for c in SHARED_BIAS])
+def test_key_shared_bias_gradients(gpu, case):
+    """A bias of one N(0,1) value per key, shared by every row and head ("bpt.py"'s bias
+    broadcast over heads and query rows): a few keys take a large share of the attention
+    of every (row, head) pair of a GQA group, so their dv sums hundreds of large P's.
+    With P's low part in dV and D from o + o_lo the gradients stay within the bf16 bound
+    (an fp64 model of P rounded to bf16 in dV puts the first shape's dv past it)."""
+    name, B, S, Hq, Hkv, D, causal, window = case
+    q, k, v, do, bias = shared_bias_inputs(case)
+    kw = dict(causal=causal, window=window)
+    qd, kd, vd, dod, bd = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), bias.to(DEV)
+    o_lo = torch.empty_like(dod)
+    o, m, l = gpu.attn_fwd(qd, kd, vd, bias=bd, o_lo=o_lo, **kw)
+    dq, dk, dv = gpu.attn_bwd(qd, kd, vd, o, dod, m, l, bias=bd, o_lo=o_lo, **kw)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = dense.backward(q, k, v, do, bias=bias, **kw)
+    check_close("dq", dq, dq_r, "bf16")
+    check_close("dk", dk, dk_r, "bf16")
+    check_close("dv", dv, dv_r, "bf16")
+
+
 DROP_CASES = [
     # id, dtype, B, Sq, Skv, Hq, Hkv, D, Dv, causal, window, q_pos0, kv_block, dropout shape, p, with bias
     ("drop_bf16_causal_gqa2", "bf16", 2, 300, 300, 4, 2, 128, 128, True, (-1, -1), 0, 0, "bhij", 0.2, False),
