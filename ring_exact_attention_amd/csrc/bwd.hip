@@ -826,7 +826,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       // (row, head) pairs, and their dV and dK then sum hundreds of large terms whose
       // bf16 roundings alone would leave the bf16 bound.  That form packs each k-step
       // just before its products, which keeps it within the register budget.
-      auto products = [&](int ks, const u32x4& pw, const u32x4& sw, const u32x4* plw, const u32x4* slw) {
+      auto products = [&](int ks, const u32x4& pw, const u32x4& sw) {
         const bf16x8 pbf = as_bf16x8(pw), sbf = as_bf16x8(sw);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
@@ -834,28 +834,44 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
             const int o0 = gtr_off + C::GL::rows(16 * ks) + 32 * db, o1 = o0 + C::GL::rows(8);
             const bf16x8 ga = join_bf16x8(lds_read_tr16(&gt_[o0]), lds_read_tr16(&gt_[o1]));
             dv[db] = mfma32(ga, pbf, dv[db]);
-            if (plw) dv[db] = mfma32(ga, as_bf16x8(*plw), dv[db]);
           }
           const int o0 = tr_off + C::QL::rows(16 * ks) + 32 * db, o1 = o0 + C::QL::rows(8);
           const bf16x8 qa = join_bf16x8(lds_read_tr16(&qt_[o0]), lds_read_tr16(&qt_[o1]));
           dk[db] = mfma32(qa, sbf, dk[db]);
-          if (slw) dk[db] = mfma32(qa, as_bf16x8(*slw), dk[db]);
         }
       };
       if constexpr (BIAS) {
+        // (P's pair and its dV products first, then dS's pair and its dK products: only
+        // one pair is live at a time.)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          u32x4 pw, sw, plw, slw;
+          u32x4 hw, lw;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const float p0 = s[8 * ks + 2 * w], p1 = s[8 * ks + 2 * w + 1];
-            const float d0 = dp[8 * ks + 2 * w], d1 = dp[8 * ks + 2 * w + 1];
-            pw[w] = pack_bf16x2(p0, p1);
-            sw[w] = pack_bf16x2(d0, d1);
-            plw[w] = pack_bf16x2(p0 - bf16_lo(pw[w]), p1 - bf16_hi(pw[w]));
-            slw[w] = pack_bf16x2(d0 - bf16_lo(sw[w]), d1 - bf16_hi(sw[w]));
+            hw[w] = pack_bf16x2(p0, p1);
+            lw[w] = pack_bf16x2(p0 - bf16_lo(hw[w]), p1 - bf16_hi(hw[w]));
           }
-          products(ks, pw, sw, &plw, &slw);
+#pragma unroll
+          for (int db = 0; db < C::DBV; ++db) {
+            const int o0 = gtr_off + C::GL::rows(16 * ks) + 32 * db, o1 = o0 + C::GL::rows(8);
+            const bf16x8 ga = join_bf16x8(lds_read_tr16(&gt_[o0]), lds_read_tr16(&gt_[o1]));
+            dv[db] = mfma32(ga, as_bf16x8(hw), dv[db]);
+            dv[db] = mfma32(ga, as_bf16x8(lw), dv[db]);
+          }
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float d0 = dp[8 * ks + 2 * w], d1 = dp[8 * ks + 2 * w + 1];
+            hw[w] = pack_bf16x2(d0, d1);
+            lw[w] = pack_bf16x2(d0 - bf16_lo(hw[w]), d1 - bf16_hi(hw[w]));
+          }
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const int o0 = tr_off + C::QL::rows(16 * ks) + 32 * db, o1 = o0 + C::QL::rows(8);
+            const bf16x8 qa = join_bf16x8(lds_read_tr16(&qt_[o0]), lds_read_tr16(&qt_[o1]));
+            dk[db] = mfma32(qa, as_bf16x8(hw), dk[db]);
+            dk[db] = mfma32(qa, as_bf16x8(lw), dk[db]);
+          }
         }
       } else {
         u32x4 pb[2], sb[2];
@@ -867,7 +883,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs a) {
             sb[ks][w] = pack_bf16x2(dp[8 * ks + 2 * w], dp[8 * ks + 2 * w + 1]);
           }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) products(ks, pb[ks], sb[ks], nullptr, nullptr);
+        for (int ks = 0; ks < 2; ++ks) products(ks, pb[ks], sb[ks]);
       }
     }
     if (nhave) {
