@@ -179,11 +179,11 @@ typedef struct attn_params {
    * Dense mode only.  Gradient accuracy: with a bias, P and dS enter dv and dk as bf16
    * pairs (high part and rounded low part), since a bias can give a few keys most of the
    * attention of hundreds of (row, head) pairs; the bias backward's dk/dv kernel runs
-   * two more matrix products per step for that.  A bias shared by all rows (one value
-   * per key) of magnitude 2 with GQA groups of 8 can still take dk up to 1.5x the bf16
-   * bound 2e-2 + 2^-8 |ref|.  Checked within that bound: key padding (0 / -inf), key-
-   * shared N(0,1) biases over random shapes (with o_lo), per-row / per-head / full
-   * biases, and a dense N(0,1) bias [1, 1, S, S] on a causal S = 8192 ring of 16 heads. */
+   * two more matrix products per step for that.  Checked within the bf16 bound
+   * 2e-2 + 2^-8 |ref|: key padding (0 / -inf), key-shared N(0,1) biases over random
+   * shapes (with o_lo; at N(0,4) one GQA-16 shape leaves the bound on 3 dk elements by
+   * 2 %), per-row / per-head / full biases, and a dense N(0,1) bias [1, 1, S, S] on a
+   * causal S = 8192 ring of 16 heads.                                                    */
   const float* bias;
   int64_t bias_stride[4];
   /* Dropout ("bpt.py": _blockwise_attention_fwd / _bwd draw a Bernoulli(attn_pdrop) array

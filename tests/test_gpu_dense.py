@@ -242,15 +242,20 @@ def shared_bias_inputs(case):
     return q, k, v, do, workloads.random_tensor((B, 1, 1, S), seed + 4)
 
 
+@pytest.mark.parametrize("scale", [1.0])
 @pytest.mark.parametrize("case", SHARED_BIAS, ids=[c[0] for c in SHARED_BIAS])
-def test_key_shared_bias_gradients(gpu, case):
-    """A bias of one N(0,1) value per key, shared by every row and head ("bpt.py"'s bias
-    broadcast over heads and query rows): a few keys take a large share of the attention
-    of every (row, head) pair of a GQA group, so their dv sums hundreds of large P's.
-    With P's low part in dV and D from o + o_lo the gradients stay within the bf16 bound
-    (an fp64 model of P rounded to bf16 in dV puts the first shape's dv past it)."""
+def test_key_shared_bias_gradients(gpu, case, scale):
+    """A bias of one N(0, scale^2) value per key, shared by every row and head ("bpt.py"'s
+    bias broadcast over heads and query rows): a few keys take a large share of the
+    attention of every (row, head) pair of a GQA group, so their dv and dk sum hundreds of
+    large P and dS terms.  With P and dS as bf16 pairs in dV and dK and D from o + o_lo
+    the gradients stay within the bf16 bound; an fp64 model of P and dS rounded to bf16
+    puts dv past it on the first three shapes.  (At scale 2 the third shape's dk leaves
+    the bound on 3 of 51200 elements, by 2 %, where that model of the kernel's roundings
+    stays at 0.66 of it: an error source the model lacks, not yet found.)"""
     name, B, S, Hq, Hkv, D, causal, window = case
     q, k, v, do, bias = shared_bias_inputs(case)
+    bias = scale * bias
     kw = dict(causal=causal, window=window)
     qd, kd, vd, dod, bd = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), bias.to(DEV)
     o_lo = torch.empty_like(dod)

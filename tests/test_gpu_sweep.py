@@ -78,9 +78,9 @@ def test_random_config(gpu, i):
     dims = {"b": B, "h": Hq, "i": Sq, "j": Skv, "1": 1}
     # Biases of unit scale, also for per-key offsets shared by every row ("b11j"), which
     # give a few keys most of the attention of hundreds of (row, head) pairs.  With D
-    # from the fp32 output (o_lo) and P's low part in dV, an fp64 model of the roundings
-    # left (dS and the result to bf16) stays within 0.9 of 2e-2 + 2^-8 |ref| for such a
-    # bias on every one of these draws; at twice that scale dk reaches 1.5x the bound.
+    # from the fp32 output (o_lo) and P and dS as bf16 pairs in dV and dK, an fp64 model
+    # of the roundings left (the result's) stays within 0.7 of 2e-2 + 2^-8 |ref| for such
+    # a bias on every one of these draws.
     bias = None
     if c["bias"] is not None:
         bias = workloads.random_tensor(tuple(dims[ch] for ch in c["bias"]), s + 4)
